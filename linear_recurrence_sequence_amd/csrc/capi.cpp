@@ -1,0 +1,527 @@
+// capi.cpp -- the C ABI: argument validation, buffer layout inside the
+// caller's saved/workspace memory, kernel sequencing, error text and the
+// per-kernel event profiler.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+#include "samu_scan.h"
+
+namespace lrs {
+
+// ------------------------------------------------------------- errors ---
+static thread_local std::string g_last_error;
+
+static scan_status fail(scan_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+// ----------------------------------------------------------- profiler ---
+namespace {
+struct ProfRecord {
+    int id;
+    hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_records;
+std::vector<hipEvent_t> g_prof_pool;
+hipEvent_t g_prof_pending = nullptr;
+int g_prof_pending_id = -1;
+
+hipEvent_t pool_get() {
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+static const char* const kKernelNames[K_NUM_KERNELS] = {
+    "samu_controller", "samu_chunk_summary", "prefix_group_compose", "prefix_group_outer",
+    "prefix_chunk_entries", "samu_replay", "samu_reverse_summary", "samu_bwd_replay",
+    "samu_controller_bwd", "samu_param_reduce", "samu_param_final", "rglru_chunk_summary",
+    "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha_reduce"};
+
+const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
+
+bool profiler_enabled() { return g_prof_on; }
+
+void profiler_before(int id, hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_pending = pool_get();
+    g_prof_pending_id = id;
+    if (g_prof_pending) (void)hipEventRecord(g_prof_pending, s);
+}
+
+void profiler_after(int id, hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t a = g_prof_pending;
+    g_prof_pending = nullptr;
+    if (!a || g_prof_pending_id != id) return;
+    hipEvent_t b = pool_get();
+    if (!b) { g_prof_pool.push_back(a); return; }
+    (void)hipEventRecord(b, s);
+    g_prof_records.push_back({id, a, b});
+}
+
+// -------------------------------------------------------------- sizes ---
+static constexpr size_t kAlign = 256;
+static size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Bump allocator over a caller-owned base pointer (or a null base for sizing).
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+    template <typename T>
+    T* take(size_t count) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off = align_up(off + count * sizeof(T));
+        return p;
+    }
+};
+
+static bool chunking(int B, int L, int K, int G, int default_G, Chunking* ch) {
+    if (B < 1 || L < 1 || B > 65535 || (K != 16 && K != 32) || G < 0) return false;
+    const int64_t C = ceil_div(L, K);
+    if (C > 65535 || (int64_t)B * L > 0x7fffffff) return false;
+    const int g = G == 0 ? default_G : G;
+    ch->B = B;
+    ch->L = L;
+    ch->K = K;
+    ch->C = (int)C;
+    ch->G = (int)std::min<int64_t>(g, C);
+    ch->NG = (int)ceil_div(C, ch->G);
+    return true;
+}
+
+static constexpr int kSamuDefaultG = 64;
+static constexpr int kRglruDefaultG = 32;
+static constexpr int kParamSegments = 16;
+int samu_ctl_tok_per_blk();
+
+struct SamuSaved {
+    float *p, *r, *ctl, *entries;
+};
+static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t* bytes) {
+    Carver cv(base);
+    SamuSaved s;
+    const size_t BL = (size_t)ch.B * ch.L;
+    s.p = cv.take<float>(BL);
+    s.r = cv.take<float>(BL);
+    s.ctl = cv.take<float>(BL * 4);
+    s.entries = cv.take<float>((size_t)ch.B * ch.C * M * 2);
+    if (bytes) *bytes = cv.off;
+    return s;
+}
+
+struct SamuFwdWs {
+    float *summ, *grp, *grp_in;
+};
+static SamuFwdWs samu_fwd_ws_layout(void* base, const Chunking& ch, int M, size_t* bytes) {
+    Carver cv(base);
+    SamuFwdWs w;
+    w.summ = cv.take<float>((size_t)ch.B * ch.C * M * 4);
+    w.grp = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * M * 4) : nullptr;
+    w.grp_in = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * M * 2) : nullptr;
+    if (bytes) *bytes = cv.off;
+    return w;
+}
+
+struct SamuBwdWs {
+    float *rsumm, *rgrp, *rgrp_in, *carry, *tok_part, *mode_part, *g_part;
+    double *g_seg, *mode_seg;
+    int n_tiles, n_blk, n_seg;
+};
+static SamuBwdWs samu_bwd_ws_layout(void* base, const Chunking& ch, int D, int M, size_t* bytes) {
+    Carver cv(base);
+    SamuBwdWs w;
+    const size_t BCM = (size_t)ch.B * ch.C * M;
+    w.n_tiles = samu_bwd_tiles(M);
+    w.n_blk = (int)ceil_div((int64_t)ch.B * ch.L, samu_ctl_tok_per_blk());
+    w.n_seg = std::min(kParamSegments, std::max(1, std::min(w.n_blk, ch.B * ch.C)));
+    w.rsumm = cv.take<float>(BCM * 4);
+    w.rgrp = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * M * 4) : nullptr;
+    w.rgrp_in = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * M * 2) : nullptr;
+    w.carry = cv.take<float>(BCM * 2);
+    w.tok_part = cv.take<float>((size_t)ch.B * w.n_tiles * ch.L * 2);
+    w.mode_part = cv.take<float>(BCM * 2);
+    w.g_part = cv.take<float>((size_t)w.n_blk * (D + 2) * 2);
+    w.g_seg = cv.take<double>((size_t)w.n_seg * (D + 2) * 2);
+    w.mode_seg = cv.take<double>((size_t)w.n_seg * M * 2);
+    if (bytes) *bytes = cv.off;
+    return w;
+}
+
+struct RgSaved {
+    float* entries;
+};
+static RgSaved rg_saved_layout(void* base, const Chunking& ch, int D, size_t* bytes) {
+    Carver cv(base);
+    RgSaved s;
+    s.entries = cv.take<float>((size_t)ch.B * ch.C * D);
+    if (bytes) *bytes = cv.off;
+    return s;
+}
+
+struct RgWs {
+    float *summ, *grp, *grp_in, *carry, *alpha_part;
+};
+static RgWs rg_ws_layout(void* base, const Chunking& ch, int D, bool backward, size_t* bytes) {
+    Carver cv(base);
+    RgWs w{};
+    const size_t BCD = (size_t)ch.B * ch.C * D;
+    w.summ = cv.take<float>(BCD * 2);
+    w.grp = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * D * 2) : nullptr;
+    w.grp_in = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * D) : nullptr;
+    if (backward) {
+        w.carry = cv.take<float>(BCD);
+        w.alpha_part = cv.take<float>(BCD);
+    }
+    if (bytes) *bytes = cv.off;
+    return w;
+}
+
+// --------------------------------------------------------- validation ---
+struct Span {
+    const void* p;
+    size_t n;
+    const char* name;
+};
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static scan_status check_ptrs(std::initializer_list<Span> req, std::initializer_list<Span> opt) {
+    for (const Span& s : req) {
+        if (!s.p) return fail(SCAN_ERR_NULL, std::string(s.name) + " is NULL");
+        if (!aligned16(s.p)) return fail(SCAN_ERR_ALIGN, std::string(s.name) + " is not 16-byte aligned");
+    }
+    for (const Span& s : opt)
+        if (s.p && !aligned16(s.p)) return fail(SCAN_ERR_ALIGN, std::string(s.name) + " is not 16-byte aligned");
+    return SCAN_OK;
+}
+
+static bool overlap(const Span& a, const Span& b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// outputs must not overlap inputs nor each other
+static scan_status check_alias(const std::vector<Span>& ins, const std::vector<Span>& outs) {
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (const Span& in : ins)
+            if (overlap(outs[i], in))
+                return fail(SCAN_ERR_ALIAS, std::string(outs[i].name) + " overlaps " + in.name);
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlap(outs[i], outs[j]))
+                return fail(SCAN_ERR_ALIAS, std::string(outs[i].name) + " overlaps " + outs[j].name);
+    }
+    return SCAN_OK;
+}
+
+static scan_status device_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return SCAN_OK;
+    return fail(SCAN_ERR_DEVICE, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define LRS_TRY(expr, where)                                    \
+    do {                                                        \
+        scan_status _st = device_status((expr), (where));       \
+        if (_st != SCAN_OK) return _st;                         \
+    } while (0)
+
+static bool samu_shape(int B, int L, int D, int K, int G, Chunking* ch) {
+    if (D < 8 || D % 8 != 0) return false;
+    return chunking(B, L, K, G, kSamuDefaultG, ch);
+}
+
+static bool rglru_shape(int B, int L, int D, int K, int G, Chunking* ch) {
+    if (D < 2 || D % 2 != 0) return false;
+    return chunking(B, L, K, G, kRglruDefaultG, ch);
+}
+
+static std::string shape_text(int B, int L, int D, int K, int G) {
+    return "B=" + std::to_string(B) + " L=" + std::to_string(L) + " D=" + std::to_string(D) +
+           " K=" + std::to_string(K) + " G=" + std::to_string(G);
+}
+
+}  // namespace lrs
+
+using namespace lrs;
+
+extern "C" {
+
+const char* scan_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------- SAMU ---
+size_t samu_scan_saved_bytes(int B, int L, int D, int K) {
+    Chunking ch;
+    if (!samu_shape(B, L, D, K, 0, &ch)) return 0;
+    size_t n = 0;
+    samu_saved_layout(nullptr, ch, D / 2, &n);
+    return n;
+}
+
+size_t samu_scan_workspace_bytes(int B, int L, int D, int K, int G, int backward) {
+    Chunking ch;
+    if (!samu_shape(B, L, D, K, G, &ch)) return 0;
+    size_t n = 0;
+    if (backward) samu_bwd_ws_layout(nullptr, ch, D, D / 2, &n);
+    else samu_fwd_ws_layout(nullptr, ch, D / 2, &n);
+    return n;
+}
+
+size_t scan_prefix_scratch_bytes(int B, int L, int D, int K, int G, int rglru) {
+    Chunking ch;
+    const bool ok = rglru ? rglru_shape(B, L, D, K, G, &ch) : samu_shape(B, L, D, K, G, &ch);
+    if (!ok) return 0;
+    const size_t groups = ch.NG > 1 ? (size_t)ch.NG : 0;
+    return (size_t)12 * B * D * ((size_t)ch.C + groups);
+}
+
+scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, const void* b,
+                          const float* w_phi, const float* w_r, const float* a_phi, const float* a_r,
+                          const float* nu, const float* theta, const float* z0, void* y, int y_dtype,
+                          float* z_final, void* saved, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    Chunking ch;
+    if (!samu_shape(B, L, D, K, G, &ch))
+        return fail(SCAN_ERR_SHAPE, "samu_scan_fwd: unsupported shape " + shape_text(B, L, D, K, G) +
+                                        " (need B, L >= 1, D >= 8 a multiple of 8, K in {16, 32}, G >= 0,"
+                                        " ceil(L/K) <= 65535)");
+    if (y_dtype != SCAN_BF16 && y_dtype != SCAN_F32)
+        return fail(SCAN_ERR_SHAPE, "samu_scan_fwd: y_dtype must be SCAN_BF16 or SCAN_F32");
+    scan_status st = check_ptrs({{x_sel, 0, "x_sel"}, {b, 0, "b"}, {w_phi, 0, "w_phi"}, {w_r, 0, "w_r"},
+                                 {a_phi, 0, "a_phi"}, {a_r, 0, "a_r"}, {nu, 0, "nu"}, {theta, 0, "theta"},
+                                 {y, 0, "y"}, {saved, 0, "saved"}, {workspace, 0, "workspace"}},
+                                {{z0, 0, "z0"}, {z_final, 0, "z_final"}});
+    if (st != SCAN_OK) return st;
+    const int M = D / 2;
+    size_t need = 0, saved_n = 0;
+    samu_fwd_ws_layout(nullptr, ch, M, &need);
+    samu_saved_layout(nullptr, ch, M, &saved_n);
+    if (workspace_bytes < need)
+        return fail(SCAN_ERR_WORKSPACE, "samu_scan_fwd: workspace_bytes " + std::to_string(workspace_bytes) +
+                                            " < " + std::to_string(need));
+    const size_t BL = (size_t)B * L, BLM = BL * M;
+    const size_t ysz = BLM * 2 * (y_dtype == SCAN_F32 ? 4 : 2);
+    st = check_alias({{x_sel, BL * D * 2, "x_sel"}, {b, BLM * 4, "b"}, {w_phi, (size_t)(D + 1) * 4, "w_phi"},
+                      {w_r, (size_t)(D + 1) * 4, "w_r"}, {a_phi, 4, "a_phi"}, {a_r, 4, "a_r"},
+                      {nu, (size_t)M * 4, "nu"}, {theta, (size_t)M * 4, "theta"},
+                      {z0, (size_t)B * M * 8, "z0"}},
+                     {{y, ysz, "y"}, {z_final, (size_t)B * M * 8, "z_final"}, {saved, saved_n, "saved"},
+                      {workspace, need, "workspace"}});
+    if (st != SCAN_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
+    SamuSaved sv = samu_saved_layout(saved, ch, M, nullptr);
+    SamuFwdWs ws = samu_fwd_ws_layout(workspace, ch, M, nullptr);
+    LRS_TRY(launch_samu_controller(p, sv.p, sv.r, sv.ctl, s), "samu controller");
+    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, b, false, ws.summ, s), "samu chunk summary");
+    LRS_TRY(launch_prefix(2, false, ch, M, ws.summ, ws.grp, ws.grp_in, z0, sv.entries, s), "samu prefix");
+    LRS_TRY(launch_samu_replay(p, ch, sv.ctl, sv.entries, y, y_dtype == SCAN_F32, z_final, s), "samu replay");
+    return SCAN_OK;
+}
+
+scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, const void* b,
+                          const float* w_phi, const float* w_r, const float* a_phi, const float* a_r,
+                          const float* nu, const float* theta, const void* saved, const void* dy,
+                          const float* dz_final, void* dx_sel, void* db, int grad_dtype, float* dz0,
+                          float* dw_phi, float* dw_r, float* da_phi, float* da_r, float* dnu,
+                          float* dtheta, void* workspace, size_t workspace_bytes, void* stream) {
+    Chunking ch;
+    if (!samu_shape(B, L, D, K, G, &ch))
+        return fail(SCAN_ERR_SHAPE, "samu_scan_bwd: unsupported shape " + shape_text(B, L, D, K, G));
+    if (grad_dtype != SCAN_BF16 && grad_dtype != SCAN_F32)
+        return fail(SCAN_ERR_SHAPE, "samu_scan_bwd: grad_dtype must be SCAN_BF16 or SCAN_F32");
+    scan_status st = check_ptrs(
+        {{x_sel, 0, "x_sel"}, {b, 0, "b"}, {w_phi, 0, "w_phi"}, {w_r, 0, "w_r"}, {a_phi, 0, "a_phi"},
+         {a_r, 0, "a_r"}, {nu, 0, "nu"}, {theta, 0, "theta"}, {saved, 0, "saved"}, {dy, 0, "dy"},
+         {dx_sel, 0, "dx_sel"}, {db, 0, "db"}, {dw_phi, 0, "dw_phi"}, {dw_r, 0, "dw_r"},
+         {da_phi, 0, "da_phi"}, {da_r, 0, "da_r"}, {dnu, 0, "dnu"}, {dtheta, 0, "dtheta"},
+         {workspace, 0, "workspace"}},
+        {{dz_final, 0, "dz_final"}, {dz0, 0, "dz0"}});
+    if (st != SCAN_OK) return st;
+    const int M = D / 2;
+    size_t need = 0, saved_n = 0;
+    samu_bwd_ws_layout(nullptr, ch, D, M, &need);
+    samu_saved_layout(nullptr, ch, M, &saved_n);
+    if (workspace_bytes < need)
+        return fail(SCAN_ERR_WORKSPACE, "samu_scan_bwd: workspace_bytes " + std::to_string(workspace_bytes) +
+                                            " < " + std::to_string(need));
+    const size_t BL = (size_t)B * L, BLM = BL * M;
+    const size_t gsz = grad_dtype == SCAN_F32 ? 4 : 2;
+    st = check_alias(
+        {{x_sel, BL * D * 2, "x_sel"}, {b, BLM * 4, "b"}, {w_phi, (size_t)(D + 1) * 4, "w_phi"},
+         {w_r, (size_t)(D + 1) * 4, "w_r"}, {a_phi, 4, "a_phi"}, {a_r, 4, "a_r"}, {nu, (size_t)M * 4, "nu"},
+         {theta, (size_t)M * 4, "theta"}, {saved, saved_n, "saved"}, {dy, BLM * 4, "dy"},
+         {dz_final, (size_t)B * M * 8, "dz_final"}},
+        {{dx_sel, BL * D * gsz, "dx_sel"}, {db, BLM * 2 * gsz, "db"}, {dz0, (size_t)B * M * 8, "dz0"},
+         {dw_phi, (size_t)(D + 1) * 4, "dw_phi"}, {dw_r, (size_t)(D + 1) * 4, "dw_r"}, {da_phi, 4, "da_phi"},
+         {da_r, 4, "da_r"}, {dnu, (size_t)M * 4, "dnu"}, {dtheta, (size_t)M * 4, "dtheta"},
+         {workspace, need, "workspace"}});
+    if (st != SCAN_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, nullptr};
+    SamuSaved sv = samu_saved_layout(const_cast<void*>(saved), ch, M, nullptr);
+    SamuBwdWs ws = samu_bwd_ws_layout(workspace, ch, D, M, nullptr);
+    const int f32 = grad_dtype == SCAN_F32;
+    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, dy, true, ws.rsumm, s), "samu reverse summary");
+    LRS_TRY(launch_prefix(2, true, ch, M, ws.rsumm, ws.rgrp, ws.rgrp_in, dz_final, ws.carry, s),
+            "samu reverse prefix");
+    LRS_TRY(launch_samu_bwd_replay(p, ch, sv.ctl, sv.entries, ws.carry, dy, db, f32, dz0, ws.tok_part,
+                                   ws.n_tiles, ws.mode_part, s),
+            "samu backward replay");
+    LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part,
+                                samu_ctl_tok_per_blk(), s),
+            "samu controller backward");
+    LRS_TRY(launch_samu_param_reduce(p, ch, ws.g_part, ws.n_blk, ws.mode_part, ws.g_seg, ws.n_seg,
+                                     ws.mode_seg, s),
+            "samu parameter reduction");
+    LRS_TRY(launch_samu_param_final(p, ch, ws.g_seg, ws.n_seg, ws.mode_seg, ws.n_seg, dw_phi, dw_r, da_phi,
+                                    da_r, dnu, dtheta, s),
+            "samu parameter final");
+    return SCAN_OK;
+}
+
+// -------------------------------------------------------------- RG-LRU ---
+size_t rglru_scan_saved_bytes(int B, int L, int D, int K) {
+    Chunking ch;
+    if (!rglru_shape(B, L, D, K, 0, &ch)) return 0;
+    size_t n = 0;
+    rg_saved_layout(nullptr, ch, D, &n);
+    return n;
+}
+
+size_t rglru_scan_workspace_bytes(int B, int L, int D, int K, int G, int backward) {
+    Chunking ch;
+    if (!rglru_shape(B, L, D, K, G, &ch)) return 0;
+    size_t n = 0;
+    rg_ws_layout(nullptr, ch, D, backward != 0, &n);
+    return n;
+}
+
+scan_status rglru_scan_fwd(int B, int L, int D, int K, int G, const void* x, const void* lx, const void* la,
+                           const float* alpha, const unsigned char* reset, const float* h0, void* y,
+                           int y_dtype, float* h_final, void* saved, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    Chunking ch;
+    if (!rglru_shape(B, L, D, K, G, &ch))
+        return fail(SCAN_ERR_SHAPE, "rglru_scan_fwd: unsupported shape " + shape_text(B, L, D, K, G) +
+                                        " (need B, L >= 1, D >= 2 even, K in {16, 32}, G >= 0,"
+                                        " ceil(L/K) <= 65535)");
+    if (y_dtype != SCAN_BF16 && y_dtype != SCAN_F32)
+        return fail(SCAN_ERR_SHAPE, "rglru_scan_fwd: y_dtype must be SCAN_BF16 or SCAN_F32");
+    scan_status st = check_ptrs({{x, 0, "x"}, {lx, 0, "lx"}, {la, 0, "la"}, {alpha, 0, "alpha"}, {y, 0, "y"},
+                                 {saved, 0, "saved"}, {workspace, 0, "workspace"}},
+                                {{h0, 0, "h0"}, {h_final, 0, "h_final"}});
+    if (st != SCAN_OK) return st;
+    size_t need = 0, saved_n = 0;
+    rg_ws_layout(nullptr, ch, D, false, &need);
+    rg_saved_layout(nullptr, ch, D, &saved_n);
+    if (workspace_bytes < need)
+        return fail(SCAN_ERR_WORKSPACE, "rglru_scan_fwd: workspace_bytes " + std::to_string(workspace_bytes) +
+                                            " < " + std::to_string(need));
+    const size_t BL = (size_t)B * L, BLD = BL * D;
+    st = check_alias({{x, BLD * 2, "x"}, {lx, BLD * 2, "lx"}, {la, BLD * 2, "la"}, {alpha, (size_t)D * 4, "alpha"},
+                      {reset, BL, "reset"}, {h0, (size_t)B * D * 4, "h0"}},
+                     {{y, BLD * (y_dtype == SCAN_F32 ? 4 : 2), "y"}, {h_final, (size_t)B * D * 4, "h_final"},
+                      {saved, saved_n, "saved"}, {workspace, need, "workspace"}});
+    if (st != SCAN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    RglruParams p{B, L, D, x, lx, la, alpha, reset, h0};
+    RgSaved sv = rg_saved_layout(saved, ch, D, nullptr);
+    RgWs ws = rg_ws_layout(workspace, ch, D, false, nullptr);
+    LRS_TRY(launch_rglru_summary(p, ch, ws.summ, s), "rglru chunk summary");
+    LRS_TRY(launch_prefix(1, false, ch, D, ws.summ, ws.grp, ws.grp_in, h0, sv.entries, s), "rglru prefix");
+    LRS_TRY(launch_rglru_replay(p, ch, sv.entries, y, y_dtype == SCAN_F32, h_final, s), "rglru replay");
+    return SCAN_OK;
+}
+
+scan_status rglru_scan_bwd(int B, int L, int D, int K, int G, const void* x, const void* lx, const void* la,
+                           const float* alpha, const unsigned char* reset, const void* saved, const void* dy,
+                           const float* dh_final, void* dx, void* dlx, void* dla, int grad_dtype,
+                           float* dalpha, float* dh0, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    Chunking ch;
+    if (!rglru_shape(B, L, D, K, G, &ch))
+        return fail(SCAN_ERR_SHAPE, "rglru_scan_bwd: unsupported shape " + shape_text(B, L, D, K, G));
+    if (grad_dtype != SCAN_BF16 && grad_dtype != SCAN_F32)
+        return fail(SCAN_ERR_SHAPE, "rglru_scan_bwd: grad_dtype must be SCAN_BF16 or SCAN_F32");
+    scan_status st = check_ptrs({{x, 0, "x"}, {lx, 0, "lx"}, {la, 0, "la"}, {alpha, 0, "alpha"},
+                                 {saved, 0, "saved"}, {dy, 0, "dy"}, {dx, 0, "dx"}, {dlx, 0, "dlx"},
+                                 {dla, 0, "dla"}, {dalpha, 0, "dalpha"}, {workspace, 0, "workspace"}},
+                                {{dh_final, 0, "dh_final"}, {dh0, 0, "dh0"}});
+    if (st != SCAN_OK) return st;
+    size_t need = 0, saved_n = 0;
+    rg_ws_layout(nullptr, ch, D, true, &need);
+    rg_saved_layout(nullptr, ch, D, &saved_n);
+    if (workspace_bytes < need)
+        return fail(SCAN_ERR_WORKSPACE, "rglru_scan_bwd: workspace_bytes " + std::to_string(workspace_bytes) +
+                                            " < " + std::to_string(need));
+    const size_t BL = (size_t)B * L, BLD = BL * D;
+    const size_t gsz = grad_dtype == SCAN_F32 ? 4 : 2;
+    st = check_alias({{x, BLD * 2, "x"}, {lx, BLD * 2, "lx"}, {la, BLD * 2, "la"}, {alpha, (size_t)D * 4, "alpha"},
+                      {reset, BL, "reset"}, {saved, saved_n, "saved"}, {dy, BLD * 2, "dy"},
+                      {dh_final, (size_t)B * D * 4, "dh_final"}},
+                     {{dx, BLD * gsz, "dx"}, {dlx, BLD * gsz, "dlx"}, {dla, BLD * gsz, "dla"},
+                      {dalpha, (size_t)D * 4, "dalpha"}, {dh0, (size_t)B * D * 4, "dh0"},
+                      {workspace, need, "workspace"}});
+    if (st != SCAN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    RglruParams p{B, L, D, x, lx, la, alpha, reset, nullptr};
+    RgSaved sv = rg_saved_layout(const_cast<void*>(saved), ch, D, nullptr);
+    RgWs ws = rg_ws_layout(workspace, ch, D, true, nullptr);
+    const int f32 = grad_dtype == SCAN_F32;
+    LRS_TRY(launch_rglru_rev_summary(p, ch, dy, ws.summ, s), "rglru reverse summary");
+    LRS_TRY(launch_prefix(1, true, ch, D, ws.summ, ws.grp, ws.grp_in, dh_final, ws.carry, s),
+            "rglru reverse prefix");
+    LRS_TRY(launch_rglru_bwd_replay(p, ch, sv.entries, ws.carry, dy, dx, dlx, dla, f32, dh0, ws.alpha_part, s),
+            "rglru backward replay");
+    LRS_TRY(launch_rglru_alpha_reduce(p, ch, ws.alpha_part, dalpha, s), "rglru alpha reduction");
+    return SCAN_OK;
+}
+
+// ------------------------------------------------------------ profiler ---
+void scan_profile_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = on != 0;
+}
+
+int scan_profile_kernel_count(void) { return K_NUM_KERNELS; }
+
+const char* scan_profile_kernel_name(int id) { return kernel_name(id); }
+
+scan_status scan_profile_collect(double* total_ms, int* launches) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (total_ms) std::fill(total_ms, total_ms + K_NUM_KERNELS, 0.0);
+    if (launches) std::fill(launches, launches + K_NUM_KERNELS, 0);
+    scan_status st = SCAN_OK;
+    for (const ProfRecord& r : g_prof_records) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && st == SCAN_OK) st = device_status(e, "scan_profile_collect");
+        if (total_ms) total_ms[r.id] += ms;
+        if (launches) launches[r.id] += 1;
+        g_prof_pool.push_back(r.a);
+        g_prof_pool.push_back(r.b);
+    }
+    g_prof_records.clear();
+    return st;
+}
+
+}  // extern "C"

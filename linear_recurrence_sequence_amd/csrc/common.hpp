@@ -1,0 +1,99 @@
+// common.hpp -- device helpers shared by the gfx950 scan kernels.
+//
+// Storage formats: BF16 tensors travel as packed pairs in 32-bit words (low
+// half = element 2k, high half = element 2k+1), complex values as (Re, Im)
+// pairs, chunk summaries as affine maps (A, B) with h -> A h + B.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "internal.hpp"
+
+namespace lrs {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// ---------------------------------------------------------------- BF16 ---
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even of two FP32 values into one packed BF16 pair
+// (a single v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// -------------------------------------------------------------- complex ---
+struct cf { float re, im; };
+
+__device__ __forceinline__ cf cmul(cf a, cf b) {
+    return {fmaf(a.re, b.re, -a.im * b.im), fmaf(a.re, b.im, a.im * b.re)};
+}
+// a * b + c
+__device__ __forceinline__ cf cfma(cf a, cf b, cf c) {
+    return {fmaf(a.re, b.re, fmaf(-a.im, b.im, c.re)), fmaf(a.re, b.im, fmaf(a.im, b.re, c.im))};
+}
+// conj(a) * b
+__device__ __forceinline__ cf cmulc(cf a, cf b) {
+    return {fmaf(a.re, b.re, a.im * b.im), fmaf(a.re, b.im, -a.im * b.re)};
+}
+// conj(a) * b + c
+__device__ __forceinline__ cf cfmac(cf a, cf b, cf c) {
+    return {fmaf(a.re, b.re, fmaf(a.im, b.im, c.re)), fmaf(a.re, b.im, fmaf(-a.im, b.re, c.im))};
+}
+
+// ------------------------------------------------------- mode constants ---
+// Per-mode static spectrum, prepared once per thread.  The unit phasor
+// e^{i theta} is kept as an unevaluated sum hi + lo of two FP32 pairs
+// (evaluated in FP64, split once) so that its rounding does not act as a
+// fixed per-mode bias repeated at every step of a long recurrence.
+struct ModeConst {
+    float kappa;           // -nu * log2(e): rho_t = 2^(kappa * E_t)
+    float ch, sh, cl, sl;  // cos(theta) = ch + cl, sin(theta) = sh + sl
+};
+
+__device__ __forceinline__ ModeConst mode_const(float nu, float theta) {
+    ModeConst k;
+    double c, s;
+    sincos((double)theta, &s, &c);
+    k.ch = (float)c;
+    k.cl = (float)(c - (double)k.ch);
+    k.sh = (float)s;
+    k.sl = (float)(s - (double)k.sh);
+    k.kappa = (float)(-(double)nu * 1.4426950408889634074);
+    return k;
+}
+
+// Transition of one mode at one token (page section 05, the lambda display):
+//   lambda = exp(-nu E_t) [(cos th C_t - sin th S_t) + i (sin th C_t + cos th S_t)]
+// E, C, S are the token's shared special functions.
+__device__ __forceinline__ cf mode_lambda(const ModeConst& k, float E, float C, float S) {
+    float rho = __builtin_amdgcn_exp2f(k.kappa * E);
+    float rr = fmaf(k.ch, C, fmaf(-k.sh, S, k.cl));
+    float ri = fmaf(k.sh, C, fmaf(k.ch, S, k.sl));
+    return {rho * rr, rho * ri};
+}
+
+// Per-token control record written by the controller kernel.
+struct TokenCtl { float E, C, S, pad; };
+
+// ------------------------------------------------------ wave reductions ---
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+}  // namespace lrs

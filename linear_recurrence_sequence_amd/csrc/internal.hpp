@@ -1,0 +1,133 @@
+// internal.hpp -- host-side plumbing shared by the kernel files and the C ABI:
+// launch geometry, the optional per-kernel event profiler, and the launcher
+// declarations of every kernel family.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lrs {
+
+__host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------ profiler ---
+// When enabled, every kernel launch is bracketed by a pair of HIP events on
+// the launch stream; scan_profile_* in the C ABI read the sums back.
+enum KernelId {
+    K_SAMU_CONTROLLER = 0,
+    K_SAMU_SUMMARY,
+    K_PREFIX_GROUPS,
+    K_PREFIX_OUTER,
+    K_PREFIX_ENTRIES,
+    K_SAMU_REPLAY,
+    K_SAMU_REV_SUMMARY,
+    K_SAMU_BWD_REPLAY,
+    K_SAMU_CTL_BWD,
+    K_SAMU_PARAM_REDUCE,
+    K_SAMU_PARAM_FINAL,
+    K_RGLRU_SUMMARY,
+    K_RGLRU_REPLAY,
+    K_RGLRU_REV_SUMMARY,
+    K_RGLRU_BWD_REPLAY,
+    K_RGLRU_ALPHA_REDUCE,
+    K_NUM_KERNELS
+};
+
+const char* kernel_name(int id);
+bool profiler_enabled();
+void profiler_before(int id, hipStream_t s);
+void profiler_after(int id, hipStream_t s);
+
+#define LRS_LAUNCH(ID, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                        \
+    do {                                                                                 \
+        const bool _prof = ::lrs::profiler_enabled();                                    \
+        if (_prof) ::lrs::profiler_before((ID), (STREAM));                               \
+        hipLaunchKernelGGL(KERNEL, (GRID), (BLOCK), (SHMEM), (STREAM), __VA_ARGS__);     \
+        if (_prof) ::lrs::profiler_after((ID), (STREAM));                                \
+    } while (0)
+
+// ------------------------------------------------------------- layouts ---
+// Chunking of one scan: C chunks of K tokens (last one K_c = L - (C-1)K),
+// grouped G chunks at a time into NG groups for the two-level prefix.
+struct Chunking {
+    int B, L, K, C, G, NG;
+};
+
+// --------------------------------------------------- prefix (all scans) ---
+// Element type of a scan: 1 = real (RG-LRU channels), 2 = complex (SAMU modes).
+// summ:    [B, C, W] affine maps (A, B) in chunk order (2*ELEM floats each)
+// grp:     [B, NG, W] group compositions U_g            (workspace, NG > 1)
+// grp_in:  [B, NG, W] group entry states O_g(init)      (workspace, NG > 1)
+// init:    [B, W] initial state (NULL = 0)
+// entries: [B, C, W] state entering each chunk (ELEM floats each)
+// reverse: chunks are visited from the last to the first (adjoint scans).
+hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W,
+                         const float* summ, float* grp, float* grp_in, const float* init,
+                         float* entries, hipStream_t s);
+
+// ---------------------------------------------------------------- SAMU ---
+struct SamuParams {
+    int B, L, D, M;
+    const void* x_sel;       // bf16 [B, L, D]
+    const void* b;           // bf16 [B, L, M, 2]
+    const float* w_phi;      // [D+1]
+    const float* w_r;        // [D+1]
+    const float* a_phi;      // [1]
+    const float* a_r;        // [1]
+    const float* nu;         // [M]
+    const float* theta;      // [M]
+    const float* z0;         // [B, M, 2] or NULL
+};
+
+hipError_t launch_samu_controller(const SamuParams& p, float* p_out, float* r_out,
+                                  float* ctl, hipStream_t s);
+hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const float* ctl,
+                               const void* drive, bool reverse, float* summ, hipStream_t s);
+hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
+                              const float* entries, void* y, int y_f32, float* z_final,
+                              hipStream_t s);
+hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
+                                  const float* entries, const float* carry_in,
+                                  const void* dy, void* db, int db_f32, float* dz0,
+                                  float* tok_part, int n_tiles, float* mode_part,
+                                  hipStream_t s);
+int samu_bwd_tiles(int M);
+int samu_ctl_tok_per_blk();
+hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const float* r_sv,
+                               const float* tok_part, int n_tiles, void* dx_sel, int dx_f32,
+                               float* g_part, int tok_per_blk, hipStream_t s);
+hipError_t launch_samu_param_reduce(const SamuParams& p, const Chunking& ch,
+                                    const float* g_part, int n_blk, const float* mode_part,
+                                    double* g_seg, int n_seg, double* mode_seg,
+                                    hipStream_t s);
+hipError_t launch_samu_param_final(const SamuParams& p, const Chunking& ch, const double* g_seg,
+                                   int n_seg, const double* mode_seg, int mode_nseg,
+                                   float* dw_phi, float* dw_r, float* da_phi, float* da_r,
+                                   float* dnu, float* dtheta, hipStream_t s);
+
+// -------------------------------------------------------------- RG-LRU ---
+struct RglruParams {
+    int B, L, D;
+    const void* x;                 // bf16 [B, L, D]
+    const void* lx;                // bf16 [B, L, D]
+    const void* la;                // bf16 [B, L, D]
+    const float* alpha;            // [D]
+    const unsigned char* reset;    // [B, L] or NULL
+    const float* h0;               // [B, D] or NULL
+};
+
+hipError_t launch_rglru_summary(const RglruParams& p, const Chunking& ch, float* summ,
+                                hipStream_t s);
+hipError_t launch_rglru_replay(const RglruParams& p, const Chunking& ch, const float* entries,
+                               void* y, int y_f32, float* h_final, hipStream_t s);
+hipError_t launch_rglru_rev_summary(const RglruParams& p, const Chunking& ch, const void* dy,
+                                    float* summ, hipStream_t s);
+hipError_t launch_rglru_bwd_replay(const RglruParams& p, const Chunking& ch,
+                                   const float* entries, const float* carry_in, const void* dy,
+                                   void* dx, void* dlx, void* dla, int g_f32, float* dh0,
+                                   float* alpha_part, hipStream_t s);
+hipError_t launch_rglru_alpha_reduce(const RglruParams& p, const Chunking& ch,
+                                     const float* alpha_part, float* dalpha, hipStream_t s);
+
+}  // namespace lrs
