@@ -1,0 +1,286 @@
+"""Benchmark: SAMU mixer forward+backward at B=1, L=32768, D=2048 on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = samu_scan_fwd + samu_scan_bwd (the whole hot path: controller,
+chunk summary, grouped prefix, replay; reverse summary, reverse prefix,
+backward replay, controller backward, parameter reductions) over one batch of
+seeded synthetic inputs already resident in HBM.  Prints ONE JSON line on
+stdout; progress goes to stderr.
+
+value = algorithmic floor bytes of the mixer F+B (16 B per token x real
+channel: x_sel, b, y forward; dy, b, x_sel, dx_sel, db backward) / F+B time,
+in GB/s.  The roofline object reports the dominant kernel's algorithmic bytes
+per launch over its average launch time, timed with HIP events recorded by the
+library around every launch on the bench stream during the timed steps.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+WORKLOAD = dict(B=1, L=32768, D=2048, K=32, G=64)
+METRIC = "mixer F+B ms and achieved HBM GB/s (% of peak) at B=1,L=32768,D=2048"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_bytes(name, B, L, D, K, G):
+    """Algorithmic bytes one launch of `name` must move at this shape: the
+    streams its job reads and writes, each counted once."""
+    M = D // 2
+    C = -(-L // K)
+    NG = -(-C // min(G, C))
+    BL, BLD, BCM = B * L, B * L * D, B * C * M
+    n_tiles = -(-M // 64)
+    table = {
+        "samu_controller": 2 * BLD + 4 * (D + 1) * 2 + 24 * BL,
+        "samu_chunk_summary": 2 * BLD + 16 * BL + 16 * BCM,
+        "prefix_group_compose": 16 * BCM + 16 * B * NG * M,
+        "prefix_group_outer": 24 * B * NG * M,
+        "prefix_chunk_entries": 16 * BCM + 8 * BCM + 8 * B * NG * M,
+        "samu_replay": 2 * BLD + 16 * BL + 8 * BCM + 2 * BLD,
+        "samu_reverse_summary": 2 * BLD + 16 * BL + 16 * BCM,
+        "samu_bwd_replay": 2 * BLD + 2 * BLD + 16 * BL + 8 * BCM + 8 * BCM + 2 * BLD
+        + 8 * B * n_tiles * L + 8 * BCM,
+        "samu_controller_bwd": 2 * BLD + 8 * BL + 8 * B * n_tiles * L + 2 * BLD
+        + 8 * (-(-BL // 64)) * (D + 2),
+    }
+    return table.get(name)
+
+
+def traffic_record(kernel):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get(kernel)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def copy_probe(torch, nbytes=512 << 20, reps=10):
+    """Device-to-device copy of a 512 MiB buffer: achievable HBM GB/s (read +
+    write bytes), the second denominator of the roofline."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(sample_L):
+    """The FP64 oracle, as it stands, on the host cores: one forward+backward
+    over the first `sample_L` tokens of the same workload."""
+    import oracle
+    from linear_recurrence_sequence_amd import inputs
+    B, D = WORKLOAD["B"], WORKLOAD["D"]
+    inp = inputs.samu_inputs(B, sample_L, D, seed=3002, z0_std=0.1)
+    t0 = time.perf_counter()
+    oracle.samu_fwd(inp["x_sel"], inp["b"], inp["w_phi"], inp["w_r"], inp["a_phi"], inp["a_r"],
+                    inp["nu"], inp["theta"], inp["z0"])
+    oracle.samu_bwd(inp["x_sel"], inp["b"], inp["w_phi"], inp["w_r"], inp["a_phi"], inp["a_r"],
+                    inp["nu"], inp["theta"], inp["z0"], inp["dy"], None)
+    dt = time.perf_counter() - t0
+    floor = 16.0 * B * sample_L * D
+    return {"value": round(floor / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "ms_per_step": round(dt * 1e3, 1),
+            "sample": f"one forward+backward of B={B}, L={sample_L} (of {WORKLOAD['L']}), D={D}; "
+                      f"same seed and distributions; floor bytes / wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample-L", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rglru", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_recurrence_sequence_amd import inputs, scan
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    scan.lib()  # fail loudly if the HIP library is missing
+
+    B, L, D, K, G = (WORKLOAD[k] for k in ("B", "L", "D", "K", "G"))
+    M = D // 2
+    log(f"[bench] generating inputs B={B} L={L} D={D}")
+    inp = inputs.samu_inputs(B, L, D, seed=3002, z0_std=0.1)
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in inp.items()}
+    dev_ = torch.device("cuda")
+    f32 = dict(dtype=torch.float32, device=dev_)
+    y = torch.empty((B, L, M, 2), dtype=torch.bfloat16, device=dev_)
+    zf = torch.empty((B, M, 2), **f32)
+    saved = torch.empty(scan.samu_scan_saved_bytes(B, L, D, K), dtype=torch.uint8, device=dev_)
+    ws_f = torch.empty(scan.samu_scan_workspace_bytes(B, L, D, K, G, False), dtype=torch.uint8, device=dev_)
+    ws_b = torch.empty(scan.samu_scan_workspace_bytes(B, L, D, K, G, True), dtype=torch.uint8, device=dev_)
+    out = dict(dx_sel=torch.empty((B, L, D), dtype=torch.bfloat16, device=dev_),
+               db=torch.empty((B, L, M, 2), dtype=torch.bfloat16, device=dev_),
+               dz0=torch.empty((B, M, 2), **f32), dw_phi=torch.empty(D + 1, **f32),
+               dw_r=torch.empty(D + 1, **f32), da_phi=torch.empty(1, **f32),
+               da_r=torch.empty(1, **f32), dnu=torch.empty(M, **f32), dtheta=torch.empty(M, **f32))
+
+    def samu_step():
+        scan.samu_scan_fwd(d["x_sel"], d["b"], d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"],
+                           d["theta"], d["z0"], K=K, G=G, y=y, z_final=zf, saved=saved, workspace=ws_f)
+        scan.samu_scan_bwd(d["x_sel"], d["b"], d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"],
+                           d["theta"], saved, d["dy"], None, K=K, G=G, out=out, workspace=ws_b)
+
+    def timed(step, steps, warmup, profile):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        scan.scan_profile_collect()
+        scan.scan_profile_enable(profile)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        scan.scan_profile_enable(False)
+        prof = scan.scan_profile_collect()
+        return e0.elapsed_time(e1) / steps, prof
+
+    log(f"[bench] SAMU F+B: warmup {args.warmup}, timing {args.steps} steps")
+    ms, prof = timed(samu_step, args.steps, args.warmup, True)
+    log(f"[bench] SAMU F+B {ms:.4f} ms/step (with per-kernel events)")
+    ms_plain, _ = timed(samu_step, args.steps, 1, False)
+    log(f"[bench] SAMU F+B {ms_plain:.4f} ms/step (no per-kernel events)")
+    launches_per_step = sum(c for _, c in prof.values()) / args.steps
+    for name, (tot, cnt) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
+        log(f"    {name:24s} {tot / cnt * 1e3:9.2f} us/launch  x{cnt // args.steps}/step")
+
+    floor_bytes = 16.0 * B * L * D
+    value = floor_bytes / (ms * 1e-3) / 1e9
+
+    # dominant kernel and its roofline
+    dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
+    dom_ms = prof[dom][0] / prof[dom][1]
+    dom_bytes = kernel_bytes(dom, B, L, D, K, G)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = traffic_record(dom)
+    kernels = {n: {"us_per_launch": round(t / c * 1e3, 2),
+                   "launches_per_step": c // args.steps,
+                   "gbs": (round(kernel_bytes(n, B, L, D, K, G) / (t / c * 1e-3) / 1e9, 1)
+                           if kernel_bytes(n, B, L, D, K, G) else None)}
+               for n, (t, c) in prof.items()}
+
+    log("[bench] copy probe (512 MiB)")
+    copy_gbs = copy_probe(torch)
+
+    rg = None
+    if not args.no_rglru:
+        log("[bench] RG-LRU F+B at the same shape (comparison variant)")
+        ri = inputs.rglru_inputs(B, L, D, seed=3003, h0_std=0.1)
+        rd = {k: dev(v) for k, v in ri.items()}
+        RK, RG = 16, 32
+        ry = torch.empty((B, L, D), dtype=torch.bfloat16, device=dev_)
+        rhf = torch.empty((B, D), **f32)
+        rsv = torch.empty(scan.rglru_scan_saved_bytes(B, L, D, RK), dtype=torch.uint8, device=dev_)
+        rwf = torch.empty(scan.rglru_scan_workspace_bytes(B, L, D, RK, RG, False), dtype=torch.uint8, device=dev_)
+        rwb = torch.empty(scan.rglru_scan_workspace_bytes(B, L, D, RK, RG, True), dtype=torch.uint8, device=dev_)
+        rout = dict(dx=torch.empty((B, L, D), dtype=torch.bfloat16, device=dev_),
+                    dlx=torch.empty((B, L, D), dtype=torch.bfloat16, device=dev_),
+                    dla=torch.empty((B, L, D), dtype=torch.bfloat16, device=dev_),
+                    dalpha=torch.empty(D, **f32), dh0=torch.empty((B, D), **f32))
+
+        def rg_step():
+            scan.rglru_scan_fwd(rd["x"], rd["lx"], rd["la"], rd["alpha"], None, rd["h0"], K=RK, G=RG,
+                                y=ry, h_final=rhf, saved=rsv, workspace=rwf)
+            scan.rglru_scan_bwd(rd["x"], rd["lx"], rd["la"], rd["alpha"], None, rsv, rd["dy"], None,
+                                K=RK, G=RG, out=rout, workspace=rwb)
+
+        rg_ms, rg_prof = timed(rg_step, args.steps, args.warmup, False)
+        rg = {"ms_per_step": round(rg_ms, 4), "K": RK, "G": RG,
+              "gbs_floor": round(22.0 * B * L * D / (rg_ms * 1e-3) / 1e9, 1),
+              "samu_fb_time_reduction": round((rg_ms - ms) / rg_ms, 4)}
+        log(f"[bench] RG-LRU F+B {rg_ms:.4f} ms/step; SAMU reduction {(rg_ms - ms) / rg_ms:.1%}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU baseline: oracle F+B over L={args.cpu_sample_L}")
+        cpu = cpu_baseline(args.cpu_sample_L)
+        log(f"[bench] CPU baseline {cpu}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; distributions of the pages' workloads)",
+        "config": {"workload": "samu_mixer_fwd_bwd_b1_l32768_d2048", "B": B, "L": L, "D": D,
+                   "M": M, "K": K, "G": G, "io": "bf16", "state": "f32",
+                   "initial_state": "N(0, 0.1^2) with gradient"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "ms_per_step_without_kernel_events": round(ms_plain, 4),
+        "launches_per_step": launches_per_step,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
+                     "us_per_launch": round(dom_ms * 1e3, 2)},
+        "copy_probe_gbs": round(copy_gbs, 1),
+        "kernels": kernels,
+        "rglru": rg,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
