@@ -12,7 +12,9 @@ value = algorithmic floor bytes of the mixer F+B (16 B per token x real
 channel: x_sel, b, y forward; dy, b, x_sel, dx_sel, db backward) / F+B time,
 in GB/s.  The roofline object reports the dominant kernel's algorithmic bytes
 per launch over its average launch time, timed with HIP events recorded by the
-library around every launch on the bench stream during the timed steps.
+library around every launch on the bench stream, over a second run of the
+same timed steps (the event records themselves cost a few microseconds per
+launch, so ms_per_step comes from the first run, without them).
 """
 import argparse
 import hashlib
@@ -28,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-WORKLOAD = dict(B=1, L=32768, D=2048, K=32, G=64)
+WORKLOAD = dict(B=1, L=32768, D=2048, K=32, G=0)   # G=0: library default grouping
 METRIC = "mixer F+B ms and achieved HBM GB/s (% of peak) at B=1,L=32768,D=2048"
 
 
@@ -36,26 +38,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def effective_groups(L, K, G):
+    """Chunks per group the library uses (G=0 asks for at most 128 groups)."""
+    C = -(-L // K)
+    return min(G if G > 0 else -(-C // 128), C)
+
+
 def kernel_bytes(name, B, L, D, K, G):
     """Algorithmic bytes one launch of `name` must move at this shape: the
     streams its job reads and writes, each counted once."""
     M = D // 2
     C = -(-L // K)
-    NG = -(-C // min(G, C))
+    NG = -(-C // effective_groups(L, K, G))
     BL, BLD, BCM = B * L, B * L * D, B * C * M
     n_tiles = -(-M // 64)
     table = {
-        "samu_controller": 2 * BLD + 4 * (D + 1) * 2 + 24 * BL,
-        "samu_chunk_summary": 2 * BLD + 16 * BL + 16 * BCM,
+        # x_sel, both direction vectors -> p, r, (u_phi, u_r), (E, C, S), mode table
+        "samu_controller": 2 * BLD + 8 * (D + 1) + 32 * BL + 32 * M,
+        # b, (E, C, S), mode table -> one affine summary per (chunk, mode)
+        "samu_chunk_summary": 2 * BLD + 16 * BL + 32 * M + 16 * BCM,
+        "samu_reverse_summary": 2 * BLD + 16 * BL + 32 * M + 16 * BCM,
+        # chunk summaries -> group summaries
         "prefix_group_compose": 16 * BCM + 16 * B * NG * M,
-        "prefix_group_outer": 24 * B * NG * M,
-        "prefix_chunk_entries": 16 * BCM + 8 * BCM + 8 * B * NG * M,
-        "samu_replay": 2 * BLD + 16 * BL + 8 * BCM + 2 * BLD,
-        "samu_reverse_summary": 2 * BLD + 16 * BL + 16 * BCM,
-        "samu_bwd_replay": 2 * BLD + 2 * BLD + 16 * BL + 8 * BCM + 8 * BCM + 2 * BLD
+        # group summaries, chunk summaries, initial state -> state entering every chunk
+        "prefix_chunk_entries": 16 * B * NG * M + 16 * BCM + 8 * B * M + 8 * BCM,
+        # b, (E, C, S), entry states -> y, final state
+        "samu_replay": 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 2 * BLD + 8 * B * M,
+        # dy, b, (E, C, S), entry states, adjoint carries -> db, per-tile controller
+        # partials, per-(chunk, mode) spectrum partials
+        "samu_bwd_replay": 2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BCM + 2 * BLD
         + 8 * B * n_tiles * L + 8 * BCM,
-        "samu_controller_bwd": 2 * BLD + 8 * BL + 8 * B * n_tiles * L + 2 * BLD
-        + 8 * (-(-BL // 64)) * (D + 2),
+        # x_sel, p, r, u, per-tile partials -> dx_sel, per-block direction partials
+        "samu_controller_bwd": 2 * BLD + 16 * BL + 8 * B * n_tiles * L + 2 * BLD
+        + 8 * (-(-BL // 64)) * (D + 4),
     }
     return table.get(name)
 
@@ -143,6 +158,7 @@ def main():
 
     B, L, D, K, G = (WORKLOAD[k] for k in ("B", "L", "D", "K", "G"))
     M = D // 2
+    G_eff = effective_groups(L, K, G)
     log(f"[bench] generating inputs B={B} L={L} D={D}")
     inp = inputs.samu_inputs(B, L, D, seed=3002, z0_std=0.1)
 
@@ -191,10 +207,11 @@ def main():
         return e0.elapsed_time(e1) / steps, prof
 
     log(f"[bench] SAMU F+B: warmup {args.warmup}, timing {args.steps} steps")
-    ms, prof = timed(samu_step, args.steps, args.warmup, True)
-    log(f"[bench] SAMU F+B {ms:.4f} ms/step (with per-kernel events)")
-    ms_plain, _ = timed(samu_step, args.steps, 1, False)
-    log(f"[bench] SAMU F+B {ms_plain:.4f} ms/step (no per-kernel events)")
+    ms, _ = timed(samu_step, args.steps, args.warmup, False)
+    log(f"[bench] SAMU F+B {ms:.4f} ms/step")
+    # the same steps again with an event pair around every kernel launch
+    ms_ev, prof = timed(samu_step, args.steps, 1, True)
+    log(f"[bench] SAMU F+B {ms_ev:.4f} ms/step with per-kernel events")
     launches_per_step = sum(c for _, c in prof.values()) / args.steps
     for name, (tot, cnt) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
         log(f"    {name:24s} {tot / cnt * 1e3:9.2f} us/launch  x{cnt // args.steps}/step")
@@ -222,7 +239,7 @@ def main():
         log("[bench] RG-LRU F+B at the same shape (comparison variant)")
         ri = inputs.rglru_inputs(B, L, D, seed=3003, h0_std=0.1)
         rd = {k: dev(v) for k, v in ri.items()}
-        RK, RG = 16, 32
+        RK, RG = 16, 0
         ry = torch.empty((B, L, D), dtype=torch.bfloat16, device=dev_)
         rhf = torch.empty((B, D), **f32)
         rsv = torch.empty(scan.rglru_scan_saved_bytes(B, L, D, RK), dtype=torch.uint8, device=dev_)
@@ -240,7 +257,7 @@ def main():
                                 K=RK, G=RG, out=rout, workspace=rwb)
 
         rg_ms, rg_prof = timed(rg_step, args.steps, args.warmup, False)
-        rg = {"ms_per_step": round(rg_ms, 4), "K": RK, "G": RG,
+        rg = {"ms_per_step": round(rg_ms, 4), "K": RK, "G": effective_groups(L, RK, RG),
               "gbs_floor": round(22.0 * B * L * D / (rg_ms * 1e-3) / 1e9, 1),
               "samu_fb_time_reduction": round((rg_ms - ms) / rg_ms, 4)}
         log(f"[bench] RG-LRU F+B {rg_ms:.4f} ms/step; SAMU reduction {(rg_ms - ms) / rg_ms:.1%}")
@@ -265,10 +282,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; distributions of the pages' workloads)",
         "config": {"workload": "samu_mixer_fwd_bwd_b1_l32768_d2048", "B": B, "L": L, "D": D,
-                   "M": M, "K": K, "G": G, "io": "bf16", "state": "f32",
+                   "M": M, "K": K, "G": G_eff, "io": "bf16", "state": "f32",
                    "initial_state": "N(0, 0.1^2) with gradient"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "ms_per_step_without_kernel_events": round(ms_plain, 4),
+        "ms_per_step_with_kernel_events": round(ms_ev, 4),
         "launches_per_step": launches_per_step,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -28,8 +28,9 @@
  *   - Results are bitwise deterministic for the same inputs, (K, G), device
  *     and library build: every reduction has a fixed order; no atomics.
  *   - K (chunk length) is 16 or 32.  G (chunks per group of the two-level
- *     prefix) is >= 1, or 0 for the library default (SAMU 64, RG-LRU 32);
- *     G >= ceil(L/K) gives the serial chunk-to-chunk prefix.
+ *     prefix) is >= 1, or 0 for the library default ceil(ceil(L/K) / 128),
+ *     i.e. at most 128 groups per sequence; G >= ceil(L/K) gives the serial
+ *     chunk-to-chunk prefix.
  *   - B >= 1, L >= 1 with any remainder (the last chunk has L - (C-1) K
  *     tokens), ceil(L/K) <= 65535, B <= 65535, B*L < 2^31.
  */

@@ -91,11 +91,21 @@ struct Carver {
     }
 };
 
+// default_G <= 0: about kTargetGroups groups per batch row, so the group scan
+// is one short in-workgroup pass and each group walk stays short.
+static constexpr int kTargetGroups = 128;
 static bool chunking(int B, int L, int K, int G, int default_G, Chunking* ch) {
     if (B < 1 || L < 1 || B > 65535 || (K != 16 && K != 32) || G < 0) return false;
     const int64_t C = ceil_div(L, K);
     if (C > 65535 || (int64_t)B * L > 0x7fffffff) return false;
-    const int g = G == 0 ? default_G : G;
+    int g = G;
+    if (g == 0) {
+        if (default_G > 0) {
+            g = default_G;
+        } else {
+            g = (int)ceil_div(C, kTargetGroups);
+        }
+    }
     ch->B = B;
     ch->L = L;
     ch->K = K;
@@ -105,13 +115,12 @@ static bool chunking(int B, int L, int K, int G, int default_G, Chunking* ch) {
     return true;
 }
 
-static constexpr int kSamuDefaultG = 64;
-static constexpr int kRglruDefaultG = 32;
-static constexpr int kParamSegments = 16;
-int samu_ctl_tok_per_blk();
+static constexpr int kSamuDefaultG = 0;      // adaptive, see chunking()
+static constexpr int kRglruDefaultG = 0;
+static constexpr int kParamSegments = 32;
 
 struct SamuSaved {
-    float *p, *r, *ctl, *entries;
+    float *p, *r, *u, *ctl, *mtab, *entries;
 };
 static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t* bytes) {
     Carver cv(base);
@@ -119,27 +128,28 @@ static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t
     const size_t BL = (size_t)ch.B * ch.L;
     s.p = cv.take<float>(BL);
     s.r = cv.take<float>(BL);
+    s.u = cv.take<float>(BL * 2);
     s.ctl = cv.take<float>(BL * 4);
+    s.mtab = cv.take<float>((size_t)M * 8);
     s.entries = cv.take<float>((size_t)ch.B * ch.C * M * 2);
     if (bytes) *bytes = cv.off;
     return s;
 }
 
 struct SamuFwdWs {
-    float *summ, *grp, *grp_in;
+    float *summ, *gsum;
 };
 static SamuFwdWs samu_fwd_ws_layout(void* base, const Chunking& ch, int M, size_t* bytes) {
     Carver cv(base);
     SamuFwdWs w;
     w.summ = cv.take<float>((size_t)ch.B * ch.C * M * 4);
-    w.grp = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * M * 4) : nullptr;
-    w.grp_in = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * M * 2) : nullptr;
+    w.gsum = cv.take<float>((size_t)ch.B * ch.NG * M * 4);
     if (bytes) *bytes = cv.off;
     return w;
 }
 
 struct SamuBwdWs {
-    float *rsumm, *rgrp, *rgrp_in, *carry, *tok_part, *mode_part, *g_part;
+    float *rsumm, *rgsum, *carry, *tok_part, *mode_part, *g_part;
     double *g_seg, *mode_seg;
     int n_tiles, n_blk, n_seg;
 };
@@ -151,13 +161,12 @@ static SamuBwdWs samu_bwd_ws_layout(void* base, const Chunking& ch, int D, int M
     w.n_blk = (int)ceil_div((int64_t)ch.B * ch.L, samu_ctl_tok_per_blk());
     w.n_seg = std::min(kParamSegments, std::max(1, std::min(w.n_blk, ch.B * ch.C)));
     w.rsumm = cv.take<float>(BCM * 4);
-    w.rgrp = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * M * 4) : nullptr;
-    w.rgrp_in = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * M * 2) : nullptr;
+    w.rgsum = cv.take<float>((size_t)ch.B * ch.NG * M * 4);
     w.carry = cv.take<float>(BCM * 2);
     w.tok_part = cv.take<float>((size_t)ch.B * w.n_tiles * ch.L * 2);
     w.mode_part = cv.take<float>(BCM * 2);
-    w.g_part = cv.take<float>((size_t)w.n_blk * (D + 2) * 2);
-    w.g_seg = cv.take<double>((size_t)w.n_seg * (D + 2) * 2);
+    w.g_part = cv.take<float>((size_t)w.n_blk * samu_param_columns(D) * 2);
+    w.g_seg = cv.take<double>((size_t)w.n_seg * samu_param_columns(D) * 2);
     w.mode_seg = cv.take<double>((size_t)w.n_seg * M * 2);
     if (bytes) *bytes = cv.off;
     return w;
@@ -175,15 +184,14 @@ static RgSaved rg_saved_layout(void* base, const Chunking& ch, int D, size_t* by
 }
 
 struct RgWs {
-    float *summ, *grp, *grp_in, *carry, *alpha_part;
+    float *summ, *gsum, *carry, *alpha_part;
 };
 static RgWs rg_ws_layout(void* base, const Chunking& ch, int D, bool backward, size_t* bytes) {
     Carver cv(base);
     RgWs w{};
     const size_t BCD = (size_t)ch.B * ch.C * D;
     w.summ = cv.take<float>(BCD * 2);
-    w.grp = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * D * 2) : nullptr;
-    w.grp_in = ch.NG > 1 ? cv.take<float>((size_t)ch.B * ch.NG * D) : nullptr;
+    w.gsum = cv.take<float>((size_t)ch.B * ch.NG * D * 2);
     if (backward) {
         w.carry = cv.take<float>(BCD);
         w.alpha_part = cv.take<float>(BCD);
@@ -328,10 +336,11 @@ scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
     SamuSaved sv = samu_saved_layout(saved, ch, M, nullptr);
     SamuFwdWs ws = samu_fwd_ws_layout(workspace, ch, M, nullptr);
-    LRS_TRY(launch_samu_controller(p, sv.p, sv.r, sv.ctl, s), "samu controller");
-    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, b, false, ws.summ, s), "samu chunk summary");
-    LRS_TRY(launch_prefix(2, false, ch, M, ws.summ, ws.grp, ws.grp_in, z0, sv.entries, s), "samu prefix");
-    LRS_TRY(launch_samu_replay(p, ch, sv.ctl, sv.entries, y, y_dtype == SCAN_F32, z_final, s), "samu replay");
+    LRS_TRY(launch_samu_controller(p, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, s), "samu controller");
+    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, s), "samu chunk summary");
+    LRS_TRY(launch_prefix(2, false, ch, M, ws.summ, ws.gsum, z0, sv.entries, s), "samu prefix");
+    LRS_TRY(launch_samu_replay(p, ch, sv.ctl, sv.mtab, sv.entries, y, y_dtype == SCAN_F32, z_final, s),
+            "samu replay");
     return SCAN_OK;
 }
 
@@ -379,20 +388,18 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuSaved sv = samu_saved_layout(const_cast<void*>(saved), ch, M, nullptr);
     SamuBwdWs ws = samu_bwd_ws_layout(workspace, ch, D, M, nullptr);
     const int f32 = grad_dtype == SCAN_F32;
-    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, dy, true, ws.rsumm, s), "samu reverse summary");
-    LRS_TRY(launch_prefix(2, true, ch, M, ws.rsumm, ws.rgrp, ws.rgrp_in, dz_final, ws.carry, s),
-            "samu reverse prefix");
-    LRS_TRY(launch_samu_bwd_replay(p, ch, sv.ctl, sv.entries, ws.carry, dy, db, f32, dz0, ws.tok_part,
-                                   ws.n_tiles, ws.mode_part, s),
+    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, s), "samu reverse summary");
+    LRS_TRY(launch_prefix(2, true, ch, M, ws.rsumm, ws.rgsum, dz_final, ws.carry, s), "samu reverse prefix");
+    LRS_TRY(launch_samu_bwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, ws.carry, dy, db, f32, dz0,
+                                   ws.tok_part, ws.n_tiles, ws.mode_part, s),
             "samu backward replay");
-    LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part,
-                                samu_ctl_tok_per_blk(), s),
+    LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, sv.u, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part, s),
             "samu controller backward");
     LRS_TRY(launch_samu_param_reduce(p, ch, ws.g_part, ws.n_blk, ws.mode_part, ws.g_seg, ws.n_seg,
                                      ws.mode_seg, s),
             "samu parameter reduction");
-    LRS_TRY(launch_samu_param_final(p, ch, ws.g_seg, ws.n_seg, ws.mode_seg, ws.n_seg, dw_phi, dw_r, da_phi,
-                                    da_r, dnu, dtheta, s),
+    LRS_TRY(launch_samu_param_final(p, ws.g_seg, ws.mode_seg, ws.n_seg, dw_phi, dw_r, da_phi, da_r, dnu,
+                                    dtheta, s),
             "samu parameter final");
     return SCAN_OK;
 }
@@ -446,7 +453,7 @@ scan_status rglru_scan_fwd(int B, int L, int D, int K, int G, const void* x, con
     RgSaved sv = rg_saved_layout(saved, ch, D, nullptr);
     RgWs ws = rg_ws_layout(workspace, ch, D, false, nullptr);
     LRS_TRY(launch_rglru_summary(p, ch, ws.summ, s), "rglru chunk summary");
-    LRS_TRY(launch_prefix(1, false, ch, D, ws.summ, ws.grp, ws.grp_in, h0, sv.entries, s), "rglru prefix");
+    LRS_TRY(launch_prefix(1, false, ch, D, ws.summ, ws.gsum, h0, sv.entries, s), "rglru prefix");
     LRS_TRY(launch_rglru_replay(p, ch, sv.entries, y, y_dtype == SCAN_F32, h_final, s), "rglru replay");
     return SCAN_OK;
 }
@@ -487,8 +494,7 @@ scan_status rglru_scan_bwd(int B, int L, int D, int K, int G, const void* x, con
     RgWs ws = rg_ws_layout(workspace, ch, D, true, nullptr);
     const int f32 = grad_dtype == SCAN_F32;
     LRS_TRY(launch_rglru_rev_summary(p, ch, dy, ws.summ, s), "rglru reverse summary");
-    LRS_TRY(launch_prefix(1, true, ch, D, ws.summ, ws.grp, ws.grp_in, dh_final, ws.carry, s),
-            "rglru reverse prefix");
+    LRS_TRY(launch_prefix(1, true, ch, D, ws.summ, ws.gsum, dh_final, ws.carry, s), "rglru reverse prefix");
     LRS_TRY(launch_rglru_bwd_replay(p, ch, sv.entries, ws.carry, dy, dx, dlx, dla, f32, dh0, ws.alpha_part, s),
             "rglru backward replay");
     LRS_TRY(launch_rglru_alpha_reduce(p, ch, ws.alpha_part, dalpha, s), "rglru alpha reduction");

@@ -49,13 +49,15 @@ __device__ __forceinline__ cf cfmac(cf a, cf b, cf c) {
 }
 
 // ------------------------------------------------------- mode constants ---
-// Per-mode static spectrum, prepared once per thread.  The unit phasor
-// e^{i theta} is kept as an unevaluated sum hi + lo of two FP32 pairs
-// (evaluated in FP64, split once) so that its rounding does not act as a
-// fixed per-mode bias repeated at every step of a long recurrence.
+// Per-mode static spectrum.  The unit phasor e^{i theta} is kept as an
+// unevaluated sum hi + lo of two FP32 pairs (evaluated in FP64, split once)
+// so that its rounding does not act as a fixed per-mode bias repeated at
+// every step of a long recurrence.  The controller kernel writes one record
+// per mode into the saved forward state; every other kernel reads it.
 struct ModeConst {
     float kappa;           // -nu * log2(e): rho_t = 2^(kappa * E_t)
     float ch, sh, cl, sl;  // cos(theta) = ch + cl, sin(theta) = sh + sl
+    float nu;
 };
 
 __device__ __forceinline__ ModeConst mode_const(float nu, float theta) {
@@ -67,6 +69,21 @@ __device__ __forceinline__ ModeConst mode_const(float nu, float theta) {
     k.sh = (float)s;
     k.sl = (float)(s - (double)k.sh);
     k.kappa = (float)(-(double)nu * 1.4426950408889634074);
+    k.nu = nu;
+    return k;
+}
+
+// Two float4 per mode: (kappa, ch, sh, cl), (sl, nu, 0, 0).
+__device__ __forceinline__ void store_mode(float4* tab, int m, const ModeConst& k) {
+    tab[2 * m] = make_float4(k.kappa, k.ch, k.sh, k.cl);
+    tab[2 * m + 1] = make_float4(k.sl, k.nu, 0.f, 0.f);
+}
+
+__device__ __forceinline__ ModeConst load_mode(const float4* __restrict__ tab, int m) {
+    const float4 a = tab[2 * m], b = tab[2 * m + 1];
+    ModeConst k;
+    k.kappa = a.x; k.ch = a.y; k.sh = a.z; k.cl = a.w;
+    k.sl = b.x; k.nu = b.y;
     return k;
 }
 
@@ -80,8 +97,20 @@ __device__ __forceinline__ cf mode_lambda(const ModeConst& k, float E, float C, 
     return {rho * rr, rho * ri};
 }
 
+// A wave-uniform value the optimizer cannot see through.  Guarding each token
+// step of a serial recurrence with `i < opaque(n)` costs one scalar compare and
+// branch, and puts every step in its own basic block, so instruction
+// selection cannot hoist all of a chunk's transitions (and their LDS control
+// reads) ahead of the chain -- which would cost far more registers than the
+// latency it hides.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // Per-token control record written by the controller kernel.
 struct TokenCtl { float E, C, S, pad; };
+
 
 // ------------------------------------------------------ wave reductions ---
 __device__ __forceinline__ float wave_sum(float v) {

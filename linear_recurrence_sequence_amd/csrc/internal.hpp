@@ -56,15 +56,13 @@ struct Chunking {
 
 // --------------------------------------------------- prefix (all scans) ---
 // Element type of a scan: 1 = real (RG-LRU channels), 2 = complex (SAMU modes).
-// summ:    [B, C, W] affine maps (A, B) in chunk order (2*ELEM floats each)
-// grp:     [B, NG, W] group compositions U_g            (workspace, NG > 1)
-// grp_in:  [B, NG, W] group entry states O_g(init)      (workspace, NG > 1)
+// summ:    [B, C, W] chunk summaries (A, B) in chunk order (2*ELEM floats each)
+// gsum:    [B, NG, W] group summaries U_g in processing order (workspace)
 // init:    [B, W] initial state (NULL = 0)
-// entries: [B, C, W] state entering each chunk (ELEM floats each)
-// reverse: chunks are visited from the last to the first (adjoint scans).
-hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W,
-                         const float* summ, float* grp, float* grp_in, const float* init,
-                         float* entries, hipStream_t s);
+// entries: [B, C, W] state entering each chunk (ELEM floats each); for an
+//          adjoint scan (reverse) the cotangent arriving after its last token
+hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const float* summ,
+                         float* gsum, const float* init, float* entries, hipStream_t s);
 
 // ---------------------------------------------------------------- SAMU ---
 struct SamuParams {
@@ -80,31 +78,36 @@ struct SamuParams {
     const float* z0;         // [B, M, 2] or NULL
 };
 
-hipError_t launch_samu_controller(const SamuParams& p, float* p_out, float* r_out,
-                                  float* ctl, hipStream_t s);
+// saved forward record (per token): p, r, u = (x~ . w^_phi, x~ . w^_r),
+// ctl = (E, C, S, 0); per mode: the two-float4 constant table mtab.
+hipError_t launch_samu_controller(const SamuParams& p, float* p_out, float* r_out, float* u_out,
+                                  float* ctl, float* mtab, hipStream_t s);
+// chunk summaries [B, C, M] (forward, or the conjugate reverse summary of dy)
 hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const float* ctl,
-                               const void* drive, bool reverse, float* summ, hipStream_t s);
+                               const float* mtab, const void* drive, bool reverse, float* summ,
+                               hipStream_t s);
+// replay from the chunk entry states; writes y and z_final
 hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
-                              const float* entries, void* y, int y_f32, float* z_final,
-                              hipStream_t s);
+                              const float* mtab, const float* entries, void* y, int y_f32,
+                              float* z_final, hipStream_t s);
+// carry_in: [B, C, M] cotangent arriving after each chunk's last token;
+// mode_part: [B, C, M] per-chunk (d nu, d theta) partials
 hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
-                                  const float* entries, const float* carry_in,
+                                  const float* mtab, const float* entries, const float* carry_in,
                                   const void* dy, void* db, int db_f32, float* dz0,
-                                  float* tok_part, int n_tiles, float* mode_part,
-                                  hipStream_t s);
+                                  float* tok_part, int n_tiles, float* mode_part, hipStream_t s);
 int samu_bwd_tiles(int M);
 int samu_ctl_tok_per_blk();
+int samu_param_columns(int D);
 hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const float* r_sv,
-                               const float* tok_part, int n_tiles, void* dx_sel, int dx_f32,
-                               float* g_part, int tok_per_blk, hipStream_t s);
+                               const float* u_sv, const float* tok_part, int n_tiles, void* dx_sel,
+                               int dx_f32, float* g_part, hipStream_t s);
 hipError_t launch_samu_param_reduce(const SamuParams& p, const Chunking& ch,
                                     const float* g_part, int n_blk, const float* mode_part,
-                                    double* g_seg, int n_seg, double* mode_seg,
-                                    hipStream_t s);
-hipError_t launch_samu_param_final(const SamuParams& p, const Chunking& ch, const double* g_seg,
-                                   int n_seg, const double* mode_seg, int mode_nseg,
-                                   float* dw_phi, float* dw_r, float* da_phi, float* da_r,
-                                   float* dnu, float* dtheta, hipStream_t s);
+                                    double* g_seg, int n_seg, double* mode_seg, hipStream_t s);
+hipError_t launch_samu_param_final(const SamuParams& p, const double* g_seg, const double* mode_seg,
+                                   int n_seg, float* dw_phi, float* dw_r, float* da_phi,
+                                   float* da_r, float* dnu, float* dtheta, hipStream_t s);
 
 // -------------------------------------------------------------- RG-LRU ---
 struct RglruParams {

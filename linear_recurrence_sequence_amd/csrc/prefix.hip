@@ -1,20 +1,23 @@
-// prefix.hip -- the grouped linear-work prefix over chunk summaries.
+// prefix.hip -- the grouped linear-work prefix over chunk summaries, shared by
+// both scans (real and complex) and both directions (forward states, adjoint
+// carries).
 //
 // Page 'SAMU 与 RG-LRU 的 H800 训练性能对比', sections 04 and 05 (the S_c, L_c,
 // U_g, O_g, Q_c displays): with S_c the affine summary of chunk c and group g
 // covering chunks g0..g1,
 //     U_g = S_{g1} o ... o S_{g0},   O_g = U_{g-1} o ... o U_0,
 //     Q_c = L_c o O_g with L_c = S_{c-1} o ... o S_{g0},
-// and (A2, B2) o (A1, B1) = (A2 A1, A2 B1 + B2) -- the right operand runs
-// first.  The state entering chunk c is Q_c(init): three kernels compute
-// U_g (one thread per group and mode), O_g(init) (one thread per mode, serial
-// over groups) and then walk each group applying S_c to produce every entry
-// state.  With a single group the first two steps vanish and the walk is the
-// serial chunk-to-chunk propagation.  Adjoint scans visit the chunks in
-// reverse order with the same operator.
-//
-// Threads map to modes/channels, so every load and store is coalesced across
-// the wave and no cross-lane traffic is needed.
+// where (A2, B2) o (A1, B1) = (A2 A1, A2 B1 + B2) and the right operand runs
+// first.  The state entering chunk c is Q_c(init).  Two kernels:
+//   * compose: one thread per (group, mode) forms U_g from its chunks;
+//   * scan + expand: a workgroup owns a few modes and a run of groups; an LDS
+//     Hillis-Steele scan (later o earlier at every step, so the order is kept)
+//     gives O_g, applied to the carried state, and each thread then walks its
+//     group's chunks applying S_c, writing the state entering every chunk --
+//     that walk is L_c applied to O_g(init).
+// Adjoint scans visit chunks and groups in reverse order with the same
+// operator.  Threads map to modes/channels (fastest), so loads and stores are
+// contiguous across lanes.
 #include "common.hpp"
 
 namespace lrs {
@@ -23,26 +26,32 @@ namespace {
 template <int E> struct Aff;
 template <> struct Aff<1> {
     float a, b;
+    static constexpr int F = 2;
     __device__ static Aff ident() { return {1.f, 0.f}; }
     __device__ static Aff load(const float* p, size_t i) {
-        float2 v = reinterpret_cast<const float2*>(p)[i];
+        const float2 v = reinterpret_cast<const float2*>(p)[i];
         return {v.x, v.y};
     }
     __device__ void store(float* p, size_t i) const { reinterpret_cast<float2*>(p)[i] = make_float2(a, b); }
     // this o first
     __device__ Aff after(const Aff& f) const { return {a * f.a, fmaf(a, f.b, b)}; }
+    __device__ void to_lds(float* s) const { s[0] = a; s[1] = b; }
+    __device__ static Aff from_lds(const float* s) { return {s[0], s[1]}; }
 };
 template <> struct Aff<2> {
     cf a, b;
+    static constexpr int F = 4;
     __device__ static Aff ident() { return {{1.f, 0.f}, {0.f, 0.f}}; }
     __device__ static Aff load(const float* p, size_t i) {
-        float4 v = reinterpret_cast<const float4*>(p)[i];
+        const float4 v = reinterpret_cast<const float4*>(p)[i];
         return {{v.x, v.y}, {v.z, v.w}};
     }
     __device__ void store(float* p, size_t i) const {
         reinterpret_cast<float4*>(p)[i] = make_float4(a.re, a.im, b.re, b.im);
     }
     __device__ Aff after(const Aff& f) const { return {cmul(a, f.a), cfma(a, f.b, b)}; }
+    __device__ void to_lds(float* s) const { s[0] = a.re; s[1] = a.im; s[2] = b.re; s[3] = b.im; }
+    __device__ static Aff from_lds(const float* s) { return {{s[0], s[1]}, {s[2], s[3]}}; }
 };
 
 template <int E> struct St;
@@ -57,7 +66,7 @@ template <> struct St<2> {
     cf v;
     __device__ static St zero() { return {{0.f, 0.f}}; }
     __device__ static St load(const float* p, size_t i) {
-        float2 x = reinterpret_cast<const float2*>(p)[i];
+        const float2 x = reinterpret_cast<const float2*>(p)[i];
         return {{x.x, x.y}};
     }
     __device__ void store(float* p, size_t i) const {
@@ -66,94 +75,102 @@ template <> struct St<2> {
     __device__ St apply(const Aff<2>& f) const { return {cfma(f.a, v, f.b)}; }
 };
 
-constexpr int PFX_THREADS = 256;
-
 __device__ __forceinline__ int chunk_of(int cc, int C, bool reverse) { return reverse ? C - 1 - cc : cc; }
 
-// U_g for every (batch, group, mode).
+constexpr int CMP_THREADS = 256;
+
+// U_g for every (batch, group, mode), groups numbered in processing order.
 template <int E, bool REV>
-__global__ __launch_bounds__(PFX_THREADS) void prefix_groups_kernel(
-    int C, int G, int NG, int W, const float* __restrict__ summ, float* __restrict__ grp) {
-    const int w = blockIdx.x * PFX_THREADS + threadIdx.x;
-    const int g = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(CMP_THREADS) void prefix_compose_kernel(
+    int C, int G, int NG, int W, const float* __restrict__ summ, float* __restrict__ gsum) {
+    const int w = blockIdx.x * CMP_THREADS + threadIdx.x;
+    const int q = blockIdx.y, b = blockIdx.z;
     if (w >= W) return;
-    const int c0 = g * G;
+    const int c0 = q * G;
     const int n = min(G, C - c0);
     Aff<E> acc = Aff<E>::ident();
 #pragma unroll 8
-    for (int i = 0; i < n; ++i) {
-        const int c = chunk_of(c0 + i, C, REV);
-        acc = Aff<E>::load(summ, ((size_t)b * C + c) * W + w).after(acc);
-    }
-    acc.store(grp, ((size_t)b * NG + g) * W + w);
+    for (int i = 0; i < n; ++i)
+        acc = Aff<E>::load(summ, ((size_t)b * C + chunk_of(c0 + i, C, REV)) * W + w).after(acc);
+    acc.store(gsum, ((size_t)b * NG + q) * W + w);
 }
 
-// O_g(init) for every group, serial over the groups of one (batch, mode).
-template <int E>
-__global__ __launch_bounds__(PFX_THREADS) void prefix_outer_kernel(
-    int NG, int W, const float* __restrict__ grp, const float* __restrict__ init,
-    float* __restrict__ grp_in) {
-    const int w = blockIdx.x * PFX_THREADS + threadIdx.x;
+constexpr int SCAN_THREADS = 1024;
+
+// Scan over groups (processing order) then expansion to chunk entries.
+// MT modes per workgroup, NGB = SCAN_THREADS / MT group slots per segment.
+template <int E, bool REV>
+__global__ __launch_bounds__(SCAN_THREADS) void prefix_scan_expand_kernel(
+    int C, int G, int NG, int W, int MT, const float* __restrict__ summ,
+    const float* __restrict__ gsum, const float* __restrict__ init, float* __restrict__ entries) {
+    constexpr int F = Aff<E>::F;
+    __shared__ float sh[2][SCAN_THREADS * F];
+    const int NGB = SCAN_THREADS / MT;
+    const int tid = threadIdx.x;
+    const int gl = tid / MT, mt = tid - gl * MT;
+    const int w = blockIdx.x * MT + mt;
     const int b = blockIdx.y;
-    if (w >= W) return;
-    St<E> h = init ? St<E>::load(init, (size_t)b * W + w) : St<E>::zero();
-#pragma unroll 4
-    for (int g = 0; g < NG; ++g) {
-        const size_t i = ((size_t)b * NG + g) * W + w;
-        h.store(grp_in, i);
-        h = h.apply(Aff<E>::load(grp, i));
-    }
-}
+    const bool wok = w < W;
+    const int wc = wok ? w : W - 1;
 
-// Entry state of every chunk: start from O_g(init) and apply S_c in order.
-template <int E, bool REV>
-__global__ __launch_bounds__(PFX_THREADS) void prefix_entries_kernel(
-    int C, int G, int NG, int W, const float* __restrict__ summ,
-    const float* __restrict__ grp_in, const float* __restrict__ init,
-    float* __restrict__ entries) {
-    const int w = blockIdx.x * PFX_THREADS + threadIdx.x;
-    const int g = blockIdx.y, b = blockIdx.z;
-    if (w >= W) return;
-    St<E> h;
-    if (NG > 1) h = St<E>::load(grp_in, ((size_t)b * NG + g) * W + w);
-    else h = init ? St<E>::load(init, (size_t)b * W + w) : St<E>::zero();
-    const int c0 = g * G;
-    const int n = min(G, C - c0);
+    St<E> carry = init ? St<E>::load(init, (size_t)b * W + wc) : St<E>::zero();
+    for (int base = 0; base < NG; base += NGB) {
+        const int q = base + gl;
+        Aff<E> x = (q < NG) ? Aff<E>::load(gsum, ((size_t)b * NG + q) * W + wc) : Aff<E>::ident();
+        int buf = 0;
+        x.to_lds(&sh[buf][tid * F]);
+        __syncthreads();
+        for (int d = 1; d < NGB; d <<= 1) {
+            if (gl >= d) x = x.after(Aff<E>::from_lds(&sh[buf][(tid - d * MT) * F]));
+            buf ^= 1;
+            x.to_lds(&sh[buf][tid * F]);
+            __syncthreads();
+        }
+        // O_g applied to the carried state, then the walk over the group's chunks
+        const Aff<E> ex = gl > 0 ? Aff<E>::from_lds(&sh[buf][(tid - MT) * F]) : Aff<E>::ident();
+        const Aff<E> last = Aff<E>::from_lds(&sh[buf][((NGB - 1) * MT + mt) * F]);
+        if (q < NG && wok) {
+            St<E> h = carry.apply(ex);
+            const int c0 = q * G;
+            const int n = min(G, C - c0);
 #pragma unroll 8
-    for (int i = 0; i < n; ++i) {
-        const int c = chunk_of(c0 + i, C, REV);
-        const size_t idx = ((size_t)b * C + c) * W + w;
-        h.store(entries, idx);
-        h = h.apply(Aff<E>::load(summ, idx));
+            for (int i = 0; i < n; ++i) {
+                const size_t idx = ((size_t)b * C + chunk_of(c0 + i, C, REV)) * W + w;
+                const Aff<E> sc = Aff<E>::load(summ, idx);
+                h.store(entries, idx);
+                h = h.apply(sc);
+            }
+        }
+        carry = carry.apply(last);
+        __syncthreads();
     }
-}
-
-template <int E, bool REV>
-hipError_t prefix_impl(const Chunking& ch, int W, const float* summ, float* grp, float* grp_in,
-                       const float* init, float* entries, hipStream_t s) {
-    const dim3 blk(PFX_THREADS);
-    const int wx = (int)ceil_div(W, PFX_THREADS);
-    if (ch.NG > 1) {
-        LRS_LAUNCH(K_PREFIX_GROUPS, (prefix_groups_kernel<E, REV>), dim3(wx, ch.NG, ch.B), blk, 0, s,
-                   ch.C, ch.G, ch.NG, W, summ, grp);
-        LRS_LAUNCH(K_PREFIX_OUTER, (prefix_outer_kernel<E>), dim3(wx, ch.B), blk, 0, s,
-                   ch.NG, W, (const float*)grp, init, grp_in);
-    }
-    LRS_LAUNCH(K_PREFIX_ENTRIES, (prefix_entries_kernel<E, REV>), dim3(wx, ch.NG, ch.B), blk, 0, s,
-               ch.C, ch.G, ch.NG, W, summ, (const float*)grp_in, init, entries);
-    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const float* summ,
-                         float* grp, float* grp_in, const float* init, float* entries,
-                         hipStream_t s) {
-    if (elem == 2)
-        return reverse ? prefix_impl<2, true>(ch, W, summ, grp, grp_in, init, entries, s)
-                       : prefix_impl<2, false>(ch, W, summ, grp, grp_in, init, entries, s);
-    return reverse ? prefix_impl<1, true>(ch, W, summ, grp, grp_in, init, entries, s)
-                   : prefix_impl<1, false>(ch, W, summ, grp, grp_in, init, entries, s);
+                         float* gsum, const float* init, float* entries, hipStream_t s) {
+    const dim3 cgrid((unsigned)ceil_div(W, CMP_THREADS), ch.NG, ch.B);
+    // group slots per segment: all groups when they fit, with >= 8 modes per
+    // workgroup so every group row is read as >= 8 contiguous modes
+    int slots = 1;
+    while (slots < ch.NG && slots < SCAN_THREADS / 8) slots <<= 1;
+    const int MT = SCAN_THREADS / slots;
+    const dim3 sgrid((unsigned)ceil_div(W, MT), ch.B);
+#define PFX(EE, RR)                                                                                          \
+    do {                                                                                                     \
+        LRS_LAUNCH(K_PREFIX_GROUPS, (prefix_compose_kernel<EE, RR>), cgrid, dim3(CMP_THREADS), 0, s, ch.C,   \
+                   ch.G, ch.NG, W, summ, gsum);                                                               \
+        LRS_LAUNCH(K_PREFIX_ENTRIES, (prefix_scan_expand_kernel<EE, RR>), sgrid, dim3(SCAN_THREADS), 0, s,  \
+                   ch.C, ch.G, ch.NG, W, MT, summ, (const float*)gsum, init, entries);                       \
+    } while (0)
+    if (elem == 2) {
+        if (reverse) PFX(2, true); else PFX(2, false);
+    } else {
+        if (reverse) PFX(1, true); else PFX(1, false);
+    }
+#undef PFX
+    return hipGetLastError();
 }
 
 }  // namespace lrs

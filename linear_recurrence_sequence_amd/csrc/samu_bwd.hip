@@ -24,108 +24,174 @@ namespace lrs {
 namespace {
 
 // ------------------------------------------------------------------ K7 ---
-// One lane per mode, one workgroup per (chunk, 128 modes).  The forward
-// recompute keeps lambda_t and w_t = lambda_t z_{t-1} of the chunk in
-// registers; the reverse pass consumes them.  The per-token partial sums of a
-// wave are reduced through a padded LDS transpose (conflict-free both ways).
-constexpr int BWD_THREADS = 128;
-constexpr int BWD_PAD = 65;
+// One lane per mode, one workgroup per (chunk, 256 modes).  The chunk is
+// handled as K/H sub-chunks of H tokens, last one first: a forward pass from
+// the chunk's saved entry state leaves the state entering every sub-chunk in
+// registers; then each sub-chunk recomputes lambda_t and w_t = lambda_t z_{t-1}
+// for its H tokens and runs the adjoint over them in reverse, starting from the
+// cotangent carried in from the following chunk.  All drive and cotangent
+// words of the chunk are requested before any math.  The per-token partial
+// sums of a wave are reduced through a padded LDS transpose (conflict-free
+// both ways), one sub-chunk at a time.
+constexpr int BWD_THREADS = 256;
+#ifndef LRS_BWD_SUB
+#define LRS_BWD_SUB 8
+#endif
 
-template <int K, bool F32>
-__global__ __launch_bounds__(BWD_THREADS) void samu_bwd_replay_kernel(
+// One chunk of the backward replay; FULL = the chunk has all K tokens (only
+// the last chunk of a sequence may not), which keeps the common path free of
+// per-token branches so its loads are issued as one batch.
+template <int K, int H, bool F32, bool FULL>
+__device__ __forceinline__ void bwd_chunk(
+    float (*lds)[64 * (2 * H + 1)], TokenCtl* sctl, const ModeConst& k, bool active, int lane, int wave,
+    int tile, int n_tiles, int L, int M, int C, int b, int c, int mm, const TokenCtl* __restrict__ ctl,
+    const uint32_t* __restrict__ drive, const float2* __restrict__ entries,
+    const uint32_t* __restrict__ dy, void* __restrict__ db, float* __restrict__ tok_part, cf& carry,
+    float& acc_nu, float& acc_th) {
+    constexpr int NH = K / H;
+    constexpr int NV = 2 * H;
+    constexpr int PAD = NV + 1;
+    const int s = c * K;
+    const int kc = FULL ? K : min(K, L - s);
+    const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform; the lane adds mm
+    float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
+    if ((int)threadIdx.x < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + threadIdx.x];
+    uint32_t bw[K], gw[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        if (FULL || i < kc) {
+            bw[i] = (drive + row0 + (size_t)i * M)[mm];
+            gw[i] = (dy + row0 + (size_t)i * M)[mm];
+        } else {
+            bw[i] = 0u;
+            gw[i] = 0u;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const float2 e0 = entries[((size_t)b * C + c) * M + mm];
+    if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
+    __syncthreads();
+    const int kq = opaque(kc);
+
+    // states entering each sub-chunk
+    cf ck[NH];
+    {
+        cf z = {e0.x, e0.y};
+        ck[0] = z;
+#pragma unroll
+        for (int i = 0; i < K - H; ++i) {
+            if (i < kq) {
+                const TokenCtl t = sctl[i];
+                z = cfma(mode_lambda(k, t.E, t.C, t.S), z, {bf16_lo(bw[i]), bf16_hi(bw[i])});
+            }
+            if ((i + 1) % H == 0) ck[(i + 1) / H] = z;
+        }
+    }
+    float* row = &lds[wave][lane * PAD];
+#pragma unroll
+    for (int h = NH - 1; h >= 0; --h) {
+        const int i0 = h * H;
+        if (!FULL && i0 >= kc) continue;  // uniform over the workgroup
+        cf lam[H], wz[H];
+        {
+            cf z = ck[h];
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                if (i0 + j < kq) {
+                    const TokenCtl t = sctl[i0 + j];
+                    lam[j] = mode_lambda(k, t.E, t.C, t.S);
+                    wz[j] = cmul(lam[j], z);
+                    z = {wz[j].re + bf16_lo(bw[i0 + j]), wz[j].im + bf16_hi(bw[i0 + j])};
+                }
+            }
+        }
+#pragma unroll
+        for (int j = H - 1; j >= 0; --j) {
+            float pr = 0.f, pi = 0.f;
+            if (i0 + j < kq) {
+                const size_t rowj = row0 + (size_t)(i0 + j) * M;
+                const float E = sctl[i0 + j].E;
+                const cf gg = {bf16_lo(gw[i0 + j]) + carry.re, bf16_hi(gw[i0 + j]) + carry.im};
+                if (active) {
+                    if (F32) (reinterpret_cast<float2*>(db) + rowj)[mm] = make_float2(gg.re, gg.im);
+                    else (reinterpret_cast<uint32_t*>(db) + rowj)[mm] = pack_bf16x2(gg.re, gg.im);
+                }
+                // gamma = g conj(w)
+                const float gre = fmaf(gg.re, wz[j].re, gg.im * wz[j].im);
+                const float gim = fmaf(gg.im, wz[j].re, -gg.re * wz[j].im);
+                acc_nu = fmaf(E, gre, acc_nu);
+                acc_th += gim;
+                pr = k.nu * gre;
+                pi = gim;
+                carry = cmulc(lam[j], gg);
+            }
+            if (!active) { pr = 0.f; pi = 0.f; }
+            row[2 * j] = pr;
+            row[2 * j + 1] = pi;
+        }
+        __syncthreads();
+        // column col (token col/2, component col%2) summed over the wave's
+        // 64 modes: 64/NV lanes per column, NV rows each, then a butterfly
+        {
+            const int col = lane % NV, grp = lane / NV;
+            const float* src = &lds[wave][grp * NV * PAD + col];
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < NV; ++r) acc += src[r * PAD];
+#pragma unroll
+            for (int o = NV; o < 64; o <<= 1) acc += __shfl_xor(acc, o);
+            const int t = i0 + (col >> 1);
+            if (grp == 0 && t < kc && tile < n_tiles) {
+                if ((col & 1) == 0) acc *= -sctl[t].E;
+                tok_part[(((size_t)b * n_tiles + tile) * L + s + i0) * 2 + col] = acc;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int K, int H, bool F32>
+__global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(3, 8))) void samu_bwd_replay_kernel(
     int L, int M, int C, int n_tiles, const TokenCtl* __restrict__ ctl,
-    const uint32_t* __restrict__ drive, const float* __restrict__ nu,
-    const float* __restrict__ theta, const float2* __restrict__ entries,
-    const float2* __restrict__ carry_in, const uint32_t* __restrict__ dy, void* __restrict__ db,
-    float2* __restrict__ dz0, float* __restrict__ tok_part, float2* __restrict__ mode_part) {
-    static_assert(2 * K <= 64, "one transposed row per lane");
-    __shared__ float lds[BWD_THREADS / 64][64 * BWD_PAD];
+    const uint32_t* __restrict__ drive, const float4* __restrict__ mtab,
+    const float2* __restrict__ entries, const float2* __restrict__ carry_in,
+    const uint32_t* __restrict__ dy, void* __restrict__ db, float2* __restrict__ dz0,
+    float* __restrict__ tok_part, float2* __restrict__ mode_part) {
+    static_assert(K % H == 0 && 64 % (2 * H) == 0, "sub-chunk shape");
+    __shared__ float lds[BWD_THREADS / 64][64 * (2 * H + 1)];
+    __shared__ TokenCtl sctl[K];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = blockIdx.x * BWD_THREADS + threadIdx.x;
     const int c = blockIdx.y, b = blockIdx.z;
     const bool active = m < M;
     const int mm = active ? m : M - 1;
-    const ModeConst k = mode_const(nu[mm], theta[mm]);
-    const float num = nu[mm];
-
-    const int s = c * K;
-    const int kc = min(K, L - s);
-    const TokenCtl* tc = ctl + (size_t)b * L + s;
-    const size_t row0 = ((size_t)b * L + s) * M + mm;
+    const ModeConst k = load_mode(mtab, mm);
+    const int tile = blockIdx.x * (BWD_THREADS / 64) + wave;
     const size_t cidx = ((size_t)b * C + c) * M + mm;
-
-    // forward recompute of the chunk from its saved entry state
-    cf lam[K], wz[K];
-    {
-        const float2 e = entries[cidx];
-        cf z = {e.x, e.y};
-#pragma unroll
-        for (int i = 0; i < K; ++i) {
-            if (i < kc) {
-                const TokenCtl t = tc[i];
-                const uint32_t bw = drive[row0 + (size_t)i * M];
-                lam[i] = mode_lambda(k, t.E, t.C, t.S);
-                wz[i] = cmul(lam[i], z);
-                z = {wz[i].re + bf16_lo(bw), wz[i].im + bf16_hi(bw)};
-            }
-        }
-    }
-
-    // reverse adjoint over the chunk
     const float2 ci = carry_in[cidx];
     cf carry = {ci.x, ci.y};
     float acc_nu = 0.f, acc_th = 0.f;
-    float* row = &lds[wave][lane * BWD_PAD];
-#pragma unroll
-    for (int i = K - 1; i >= 0; --i) {
-        float pr = 0.f, pi = 0.f;
-        if (i < kc) {
-            const float E = tc[i].E;
-            const uint32_t gw = dy[row0 + (size_t)i * M];
-            const cf g = {bf16_lo(gw) + carry.re, bf16_hi(gw) + carry.im};
-            if (active) {
-                if (F32) reinterpret_cast<float2*>(db)[row0 + (size_t)i * M] = make_float2(g.re, g.im);
-                else reinterpret_cast<uint32_t*>(db)[row0 + (size_t)i * M] = pack_bf16x2(g.re, g.im);
-            }
-            // gamma = g conj(w)
-            const float gre = fmaf(g.re, wz[i].re, g.im * wz[i].im);
-            const float gim = fmaf(g.im, wz[i].re, -g.re * wz[i].im);
-            acc_nu = fmaf(E, gre, acc_nu);
-            acc_th += gim;
-            pr = num * gre;
-            pi = gim;
-            carry = cmulc(lam[i], g);
-        }
-        if (!active) { pr = 0.f; pi = 0.f; }
-        row[2 * i] = pr;
-        row[2 * i + 1] = pi;
-    }
+    if ((c + 1) * K <= L)
+        bwd_chunk<K, H, F32, true>(lds, sctl, k, active, lane, wave, tile, n_tiles, L, M, C, b, c, mm, ctl,
+                                   drive, entries, dy, db, tok_part, carry, acc_nu, acc_th);
+    else
+        bwd_chunk<K, H, F32, false>(lds, sctl, k, active, lane, wave, tile, n_tiles, L, M, C, b, c, mm, ctl,
+                                    drive, entries, dy, db, tok_part, carry, acc_nu, acc_th);
     if (active) {
         mode_part[cidx] = make_float2(-acc_nu, acc_th);
         if (dz0 && c == 0) dz0[(size_t)b * M + mm] = make_float2(carry.re, carry.im);
     }
-    __syncthreads();
-    // lane j sums column j (token j/2, component j%2) over the 64 modes of the wave
-    if (lane < 2 * kc) {
-        float acc = 0.f;
-        const float* col = &lds[wave][lane];
-#pragma unroll 16
-        for (int r = 0; r < 64; ++r) acc += col[r * BWD_PAD];
-        const int t = lane >> 1;
-        if ((lane & 1) == 0) acc *= -tc[t].E;
-        const int tile = blockIdx.x * (BWD_THREADS / 64) + wave;
-        if (tile < n_tiles)
-            tok_part[(((size_t)b * n_tiles + tile) * L + s) * 2 + lane] = acc;
-    }
 }
 
 // ------------------------------------------------------------------ K9 ---
-// One workgroup per block of CTL_TB tokens; each thread owns 8 selector
-// columns.  The first stage of the shared-control reduction (over mode tiles)
-// happens here in fixed tile order, then p-bar, r-bar and the per-token u-bar
-// follow; dx_sel = u-bar_phi w^_phi + u-bar_r w^_r, and the block's partial
-// sums of u-bar * x~ (direction gradients) plus sum d-bar p, sum c-bar q are
-// written for the final deterministic reduction.
+// One workgroup per block of CTL_TB tokens; threads own 8 selector columns at
+// a time.  The second stage of the shared-control reduction (over the mode
+// tiles, fixed order) happens here, then p-bar, r-bar and the per-token u-bar
+// follow; dx_sel = u-bar_phi w^_phi + u-bar_r w^_r.  The block writes its
+// partial sums of u-bar * x~ for every column of x~ plus three scalar pairs:
+//   column D     sum u-bar            (the constant 1 of x~)
+//   column D+1   sum d-bar p, sum c-bar q       (amplitude gradients)
+//   column D+2   sum u-bar u  with u = x~ . w^  (= w^ . g, for the projection)
 constexpr int CTL_TB = 64;
 
 template <bool F32>
@@ -134,12 +200,14 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
     const float* __restrict__ w_phi, const float* __restrict__ w_r,
     const float* __restrict__ a_phi, const float* __restrict__ a_r,
     const float* __restrict__ p_sv, const float* __restrict__ r_sv,
-    const float* __restrict__ tok_part, void* __restrict__ dx, float* __restrict__ g_part) {
+    const float2* __restrict__ u_sv, const float* __restrict__ tok_part, void* __restrict__ dx,
+    float* __restrict__ g_part) {
     __shared__ float u_sh[2][CTL_TB];
-    __shared__ float red[4][16];
+    __shared__ float red[2][8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int BL = B * L;
     const int blk = blockIdx.x;
+    const int ncol = D + 4;
 
     // direction norms
     float sp = 0.f, sr = 0.f;
@@ -156,12 +224,11 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
     const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
     const float sM = sqrtf((float)M);
     const float th_phi = tanhf(a_phi[0]), th_r = tanhf(a_r[0]);
-    __syncthreads();
 
-    // per-token u-bar (threads 0..CTL_TB-1, i.e. the first wave)
+    // per-token u-bar (the first wave: CTL_TB == 64 tokens)
     if (tid < CTL_TB) {
         const int tok = blk * CTL_TB + tid;
-        float uphi = 0.f, ur = 0.f, sdp = 0.f, scq = 0.f;
+        float uphi = 0.f, ur = 0.f, sdp = 0.f, scq = 0.f, sup = 0.f, sur = 0.f;
         if (tok < BL) {
             const int bb = tok / L, l = tok - bb * L;
             float cb = 0.f, dbr = 0.f;
@@ -171,6 +238,7 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
                 dbr += v.y;
             }
             const float p = p_sv[tok], r = r_sv[tok];
+            const float2 u = u_sv[tok];
             const float r2 = r * r;
             const float q = r / (1.0f + r2);
             const float pbar = dbr * th_phi / sM;
@@ -179,17 +247,17 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
             ur = rbar * (1.0f - r2);
             sdp = dbr * p;
             scq = cb * q;
+            sup = uphi * u.x;
+            sur = ur * u.y;
         }
         u_sh[0][tid] = uphi;
         u_sh[1][tid] = ur;
-        // bias column of x~ is 1: its gradient partial is sum u-bar
         const float s0 = wave_sum(uphi), s1 = wave_sum(ur), s2 = wave_sum(sdp), s3 = wave_sum(scq);
+        const float s4 = wave_sum(sup), s5 = wave_sum(sur);
         if (tid == 0) {
-            float* gp = g_part + (size_t)blk * (D + 2) * 2;
-            gp[2 * D] = s0;
-            gp[2 * D + 1] = s1;
-            gp[2 * (D + 1)] = s2;
-            gp[2 * (D + 1) + 1] = s3;
+            float4* gp = reinterpret_cast<float4*>(g_part + ((size_t)blk * ncol + D) * 2);
+            gp[0] = make_float4(s0, s1, s2, s3);
+            gp[1] = make_float4(s4, s5, 0.f, 0.f);
         }
     }
     __syncthreads();
@@ -212,43 +280,58 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
                 gr[e] = 0.f;
             }
         }
-#pragma unroll 4
-        for (int t = 0; t < ntok; ++t) {
-            const size_t tok = (size_t)blk * CTL_TB + t;
-            const float uphi = u_sh[0][t], ur = u_sh[1][t];
-            const uint4 xv = x_sel[tok * D8 + j8];
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-            float xs[8];
+        constexpr int TB = 16;  // tokens whose selector words are loaded together
+        for (int t0 = 0; t0 < ntok; t0 += TB) {
+            uint4 xv[TB];
+            if (t0 + TB <= ntok) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { xs[2 * e] = bf16_lo(xw[e]); xs[2 * e + 1] = bf16_hi(xw[e]); }
-            float o[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                o[e] = fmaf(uphi, wp[e], ur * wr[e]);
-                gp[e] = fmaf(uphi, xs[e], gp[e]);
-                gr[e] = fmaf(ur, xs[e], gr[e]);
-            }
-            if (F32) {
-                float4* q = reinterpret_cast<float4*>(dx) + (tok * D8 + j8) * 2;
-                q[0] = make_float4(o[0], o[1], o[2], o[3]);
-                q[1] = make_float4(o[4], o[5], o[6], o[7]);
+                for (int t = 0; t < TB; ++t) xv[t] = x_sel[((size_t)blk * CTL_TB + t0 + t) * D8 + j8];
             } else {
-                reinterpret_cast<uint4*>(dx)[tok * D8 + j8] =
-                    make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                               pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+#pragma unroll
+                for (int t = 0; t < TB; ++t)
+                    xv[t] = (t0 + t < ntok) ? x_sel[((size_t)blk * CTL_TB + t0 + t) * D8 + j8]
+                                            : make_uint4(0, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                if (t0 + t >= ntok) break;
+                const size_t tok = (size_t)blk * CTL_TB + t0 + t;
+                const float uphi = u_sh[0][t0 + t], ur = u_sh[1][t0 + t];
+                const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+                float xs[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { xs[2 * e] = bf16_lo(xw[e]); xs[2 * e + 1] = bf16_hi(xw[e]); }
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    o[e] = fmaf(uphi, wp[e], ur * wr[e]);
+                    gp[e] = fmaf(uphi, xs[e], gp[e]);
+                    gr[e] = fmaf(ur, xs[e], gr[e]);
+                }
+                if (F32) {
+                    float4* q = reinterpret_cast<float4*>(dx) + (tok * D8 + j8) * 2;
+                    q[0] = make_float4(o[0], o[1], o[2], o[3]);
+                    q[1] = make_float4(o[4], o[5], o[6], o[7]);
+                } else {
+                    reinterpret_cast<uint4*>(dx)[tok * D8 + j8] =
+                        make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                   pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+                }
             }
         }
-        float4* out = reinterpret_cast<float4*>(g_part + ((size_t)blk * (D + 2) + 8 * j8) * 2);
+        float4* out = reinterpret_cast<float4*>(g_part + ((size_t)blk * ncol + 8 * j8) * 2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = make_float4(gp[2 * e], gr[2 * e], gp[2 * e + 1], gr[2 * e + 1]);
     }
 }
 
 // ----------------------------------------------------------------- K10 ---
-// Level 1 of the parameter reductions, in FP64 and fixed order:
-//   blocks [0, col_tiles): columns of g_part summed over a segment of token blocks
-//   blocks [col_tiles, ...): modes of mode_part summed over a segment of chunks
-constexpr int RED_THREADS = 256;
+// Level 1 of the parameter reductions, FP64 and fixed order, one thread per
+// column (or mode) and segment:
+//   blocks x in [0, col_tiles): columns of g_part over a segment of token blocks
+//   blocks x in [col_tiles, ...): modes of mode_part over a segment of chunks
+constexpr int RED_THREADS = 64;
 
 __global__ __launch_bounds__(RED_THREADS) void samu_param_reduce_kernel(
     int ncol, int n_blk, int seg_blk, int col_tiles, const float2* __restrict__ g_part,
@@ -262,6 +345,7 @@ __global__ __launch_bounds__(RED_THREADS) void samu_param_reduce_kernel(
         const int b0 = min(n_blk, seg * seg_blk);
         const int b1 = min(n_blk, b0 + seg_blk);
         double sx = 0.0, sy = 0.0;
+#pragma unroll 8
         for (int i = b0; i < b1; ++i) {
             const float2 v = g_part[(size_t)i * ncol + col];
             sx += v.x;
@@ -274,6 +358,7 @@ __global__ __launch_bounds__(RED_THREADS) void samu_param_reduce_kernel(
         const int c0 = min(nchunks, seg * seg_chunk);
         const int c1 = min(nchunks, c0 + seg_chunk);
         double sx = 0.0, sy = 0.0;
+#pragma unroll 8
         for (int i = c0; i < c1; ++i) {
             const float2 v = mode_part[(size_t)i * M + m];
             sx += v.x;
@@ -283,23 +368,25 @@ __global__ __launch_bounds__(RED_THREADS) void samu_param_reduce_kernel(
     }
 }
 
-// Level 2: block 0 finishes the direction and amplitude gradients (projection
-// (g^ - w^ (w^ . g^)) / ||w||), the other blocks finish d nu, d theta.
-constexpr int FIN_THREADS = 1024;
+// Level 2: every column and every mode independently, so the whole grid works
+// in parallel.  dw = (g - w^ (w^ . g)) / ||w|| with w^ . g taken from the
+// per-token sums of u-bar * u (column D+2); da from column D+1.
+constexpr int FIN_THREADS = 256;
 
 __global__ __launch_bounds__(FIN_THREADS) void samu_param_final_kernel(
-    int D, int M, const float* __restrict__ w_phi, const float* __restrict__ w_r,
+    int D, int M, int col_blocks, const float* __restrict__ w_phi, const float* __restrict__ w_r,
     const float* __restrict__ a_phi, const float* __restrict__ a_r,
-    const double2* __restrict__ g_seg, int n_seg, const double2* __restrict__ mode_seg,
-    int mode_nseg, float* __restrict__ dw_phi, float* __restrict__ dw_r,
-    float* __restrict__ da_phi, float* __restrict__ da_r, float* __restrict__ dnu,
-    float* __restrict__ dtheta) {
+    const double2* __restrict__ g_seg, const double2* __restrict__ mode_seg, int n_seg,
+    float* __restrict__ dw_phi, float* __restrict__ dw_r, float* __restrict__ da_phi,
+    float* __restrict__ da_r, float* __restrict__ dnu, float* __restrict__ dtheta) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (blockIdx.x > 0) {
-        const int m = (blockIdx.x - 1) * FIN_THREADS + tid;
+    const int ncol = D + 4;
+    if ((int)blockIdx.x >= col_blocks) {
+        const int m = (blockIdx.x - col_blocks) * FIN_THREADS + tid;
         if (m >= M) return;
         double sx = 0.0, sy = 0.0;
-        for (int i = 0; i < mode_nseg; ++i) {
+#pragma unroll 8
+        for (int i = 0; i < n_seg; ++i) {
             const double2 v = mode_seg[(size_t)i * M + m];
             sx += v.x;
             sy += v.y;
@@ -308,100 +395,95 @@ __global__ __launch_bounds__(FIN_THREADS) void samu_param_final_kernel(
         dtheta[m] = (float)sy;
         return;
     }
-    extern __shared__ double gsh[];  // [D+2][2]
-    __shared__ double red[4][FIN_THREADS / 64];
-    const int ncol = D + 2;
-    double nphi = 0.0, nr = 0.0, dphi = 0.0, dr = 0.0;
-    for (int j = tid; j < ncol; j += FIN_THREADS) {
-        double sx = 0.0, sy = 0.0;
-        for (int i = 0; i < n_seg; ++i) {
-            const double2 v = g_seg[(size_t)i * ncol + j];
-            sx += v.x;
-            sy += v.y;
-        }
-        gsh[2 * j] = sx;
-        gsh[2 * j + 1] = sy;
-        if (j <= D) {
-            const double wp = w_phi[j], wr = w_r[j];
-            nphi += wp * wp;
-            nr += wr * wr;
-            dphi += wp * sx;
-            dr += wr * sy;
-        }
+    __shared__ double red[2][FIN_THREADS / 64];
+    double nphi = 0.0, nr = 0.0;
+    for (int j = tid; j <= D; j += FIN_THREADS) {
+        nphi += (double)w_phi[j] * w_phi[j];
+        nr += (double)w_r[j] * w_r[j];
     }
     nphi = wave_sum_d(nphi);
     nr = wave_sum_d(nr);
-    dphi = wave_sum_d(dphi);
-    dr = wave_sum_d(dr);
-    if (lane == 0) { red[0][wave] = nphi; red[1][wave] = nr; red[2][wave] = dphi; red[3][wave] = dr; }
+    if (lane == 0) { red[0][wave] = nphi; red[1][wave] = nr; }
     __syncthreads();
-    double Np = 0.0, Nr = 0.0, Dp = 0.0, Dr = 0.0;
-    for (int i = 0; i < FIN_THREADS / 64; ++i) { Np += red[0][i]; Nr += red[1][i]; Dp += red[2][i]; Dr += red[3][i]; }
+    double Np = 0.0, Nr = 0.0;
+    for (int i = 0; i < FIN_THREADS / 64; ++i) { Np += red[0][i]; Nr += red[1][i]; }
     const double np = sqrt(Np), nrr = sqrt(Nr);
-    // w^ . g^ = (w . g^) / ||w||
-    const double dotp = Dp / np, dotr = Dr / nrr;
-    for (int j = tid; j <= D; j += FIN_THREADS) {
-        const double whp = w_phi[j] / np, whr = w_r[j] / nrr;
-        dw_phi[j] = (float)((gsh[2 * j] - whp * dotp) / np);
-        dw_r[j] = (float)((gsh[2 * j + 1] - whr * dotr) / nrr);
+    const int j = blockIdx.x * FIN_THREADS + tid;
+    if (j > D) return;
+    double gx = 0.0, gy = 0.0, dotp = 0.0, dotr = 0.0;
+#pragma unroll 8
+    for (int i = 0; i < n_seg; ++i) {
+        const double2 v = g_seg[(size_t)i * ncol + j];
+        const double2 q = g_seg[(size_t)i * ncol + D + 2];
+        gx += v.x;
+        gy += v.y;
+        dotp += q.x;
+        dotr += q.y;
     }
-    if (tid == 0) {
+    dw_phi[j] = (float)((gx - ((double)w_phi[j] / np) * dotp) / np);
+    dw_r[j] = (float)((gy - ((double)w_r[j] / nrr) * dotr) / nrr);
+    if (j == 0) {
+        double sdp = 0.0, scq = 0.0;
+        for (int i = 0; i < n_seg; ++i) {
+            const double2 v = g_seg[(size_t)i * ncol + D + 1];
+            sdp += v.x;
+            scq += v.y;
+        }
         const double sM = sqrt((double)M);
         const double tp = tanh((double)a_phi[0]), tr = tanh((double)a_r[0]);
-        da_phi[0] = (float)((1.0 - tp * tp) / sM * gsh[2 * (D + 1)]);
-        da_r[0] = (float)((1.0 - tr * tr) / sM * gsh[2 * (D + 1) + 1]);
+        da_phi[0] = (float)((1.0 - tp * tp) / sM * sdp);
+        da_r[0] = (float)((1.0 - tr * tr) / sM * scq);
     }
 }
 
 }  // namespace
 
 int samu_bwd_tiles(int M) { return (int)ceil_div(M, 64); }
+int samu_ctl_tok_per_blk() { return CTL_TB; }
 
 hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
-                                  const float* entries, const float* carry_in, const void* dy,
-                                  void* db, int db_f32, float* dz0, float* tok_part, int n_tiles,
-                                  float* mode_part, hipStream_t s) {
+                                  const float* mtab, const float* entries, const float* carry_in,
+                                  const void* dy, void* db, int db_f32, float* dz0, float* tok_part,
+                                  int n_tiles, float* mode_part, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(p.M, BWD_THREADS), ch.C, ch.B);
-#define BWD_CASE(KK, FF)                                                                             \
-    LRS_LAUNCH(K_SAMU_BWD_REPLAY, (samu_bwd_replay_kernel<KK, FF>), grid, dim3(BWD_THREADS), 0, s, \
-               p.L, p.M, ch.C, n_tiles, (const TokenCtl*)ctl, (const uint32_t*)p.b, p.nu, p.theta, \
-               (const float2*)entries, (const float2*)carry_in, (const uint32_t*)dy, db,          \
-               (float2*)dz0, tok_part, (float2*)mode_part)
+#define BWD_CASE(KK, HH, FF)                                                                             \
+    LRS_LAUNCH(K_SAMU_BWD_REPLAY, (samu_bwd_replay_kernel<KK, HH, FF>), grid, dim3(BWD_THREADS), 0, s, \
+               p.L, p.M, ch.C, n_tiles, (const TokenCtl*)ctl, (const uint32_t*)p.b,                   \
+               (const float4*)mtab, (const float2*)entries, (const float2*)carry_in,                  \
+               (const uint32_t*)dy, db, (float2*)dz0, tok_part, (float2*)mode_part)
+    constexpr int H32 = LRS_BWD_SUB, H16 = LRS_BWD_SUB < 16 ? LRS_BWD_SUB : 8;
     if (ch.K == 32) {
-        if (db_f32) BWD_CASE(32, true); else BWD_CASE(32, false);
+        if (db_f32) BWD_CASE(32, H32, true); else BWD_CASE(32, H32, false);
     } else {
-        if (db_f32) BWD_CASE(16, true); else BWD_CASE(16, false);
+        if (db_f32) BWD_CASE(16, H16, true); else BWD_CASE(16, H16, false);
     }
 #undef BWD_CASE
     return hipGetLastError();
 }
 
 hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const float* r_sv,
-                               const float* tok_part, int n_tiles, void* dx_sel, int dx_f32,
-                               float* g_part, int tok_per_blk, hipStream_t s) {
-    (void)tok_per_blk;
+                               const float* u_sv, const float* tok_part, int n_tiles, void* dx_sel,
+                               int dx_f32, float* g_part, hipStream_t s) {
     const int BL = p.B * p.L;
     const int grid = (int)ceil_div(BL, CTL_TB);
     const int threads = (int)std::min<int64_t>(512, std::max<int64_t>(64, ceil_div(ceil_div(p.D, 8), 64) * 64));
-    if (dx_f32)
-        LRS_LAUNCH(K_SAMU_CTL_BWD, samu_ctl_bwd_kernel<true>, dim3(grid), dim3(threads), 0, s, p.B, p.L,
-                   p.D, p.M, n_tiles, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p_sv, r_sv,
-                   tok_part, dx_sel, g_part);
-    else
-        LRS_LAUNCH(K_SAMU_CTL_BWD, samu_ctl_bwd_kernel<false>, dim3(grid), dim3(threads), 0, s, p.B, p.L,
-                   p.D, p.M, n_tiles, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p_sv, r_sv,
-                   tok_part, dx_sel, g_part);
+#define CTLB_CASE(FF)                                                                                 \
+    LRS_LAUNCH(K_SAMU_CTL_BWD, samu_ctl_bwd_kernel<FF>, dim3(grid), dim3(threads), 0, s, p.B, p.L, p.D, \
+               p.M, n_tiles, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p_sv, r_sv,         \
+               (const float2*)u_sv, tok_part, dx_sel, g_part)
+    if (dx_f32) CTLB_CASE(true); else CTLB_CASE(false);
+#undef CTLB_CASE
     return hipGetLastError();
 }
 
-int samu_ctl_tok_per_blk() { return CTL_TB; }
+int samu_param_columns(int D) { return D + 4; }
 
 hipError_t launch_samu_param_reduce(const SamuParams& p, const Chunking& ch, const float* g_part,
                                     int n_blk, const float* mode_part, double* g_seg, int n_seg,
                                     double* mode_seg, hipStream_t s) {
-    const int ncol = p.D + 2;
+    const int ncol = samu_param_columns(p.D);
     const int seg_blk = (int)ceil_div(n_blk, n_seg);
-    const int nchunks = ch.B * ch.C;
+    const int nchunks = ch.B * ch.C;  // rows of mode_part: one per (batch row, chunk)
     const int seg_chunk = (int)ceil_div(nchunks, n_seg);
     const int col_tiles = (int)ceil_div(ncol, RED_THREADS);
     const int mode_tiles = (int)ceil_div(p.M, RED_THREADS);
@@ -411,16 +493,14 @@ hipError_t launch_samu_param_reduce(const SamuParams& p, const Chunking& ch, con
     return hipGetLastError();
 }
 
-hipError_t launch_samu_param_final(const SamuParams& p, const Chunking& ch, const double* g_seg,
-                                   int n_seg, const double* mode_seg, int mode_nseg, float* dw_phi,
-                                   float* dw_r, float* da_phi, float* da_r, float* dnu,
-                                   float* dtheta, hipStream_t s) {
-    (void)ch;
-    const size_t shmem = sizeof(double) * 2 * (size_t)(p.D + 2);
-    const int grid = 1 + (int)ceil_div(p.M, FIN_THREADS);
-    LRS_LAUNCH(K_SAMU_PARAM_FINAL, samu_param_final_kernel, dim3(grid), dim3(FIN_THREADS), shmem, s,
-               p.D, p.M, p.w_phi, p.w_r, p.a_phi, p.a_r, (const double2*)g_seg, n_seg,
-               (const double2*)mode_seg, mode_nseg, dw_phi, dw_r, da_phi, da_r, dnu, dtheta);
+hipError_t launch_samu_param_final(const SamuParams& p, const double* g_seg, const double* mode_seg,
+                                   int n_seg, float* dw_phi, float* dw_r, float* da_phi, float* da_r,
+                                   float* dnu, float* dtheta, hipStream_t s) {
+    const int col_blocks = (int)ceil_div(p.D + 1, FIN_THREADS);
+    const int grid = col_blocks + (int)ceil_div(p.M, FIN_THREADS);
+    LRS_LAUNCH(K_SAMU_PARAM_FINAL, samu_param_final_kernel, dim3(grid), dim3(FIN_THREADS), 0, s, p.D,
+               p.M, col_blocks, p.w_phi, p.w_r, p.a_phi, p.a_r, (const double2*)g_seg,
+               (const double2*)mode_seg, n_seg, dw_phi, dw_r, da_phi, da_r, dnu, dtheta);
     return hipGetLastError();
 }
 

@@ -26,18 +26,26 @@ namespace lrs {
 namespace {
 
 // ------------------------------------------------------------------ K1 ---
-constexpr int CTL_THREADS = 256;        // 4 waves
-constexpr int CTL_TOK_PER_PASS = 4;     // tokens reduced together per wave
-constexpr int CTL_PASSES = 4;
-constexpr int CTL_TOK_PER_BLOCK = 4 * CTL_TOK_PER_PASS * CTL_PASSES;
+// One wave per CTL_TOK tokens: every lane loads 16 bytes (8 selector values)
+// of each token row per 512-column slab, the wave reduces the two dot products
+// and lanes 0..CTL_TOK-1 finish one token each.  The grid also writes the
+// per-mode constant table (strided over all blocks).
+constexpr int CTL_WAVES = 8;
+constexpr int CTL_THREADS = 64 * CTL_WAVES;
+constexpr int CTL_TOK = 4;                          // tokens per wave
+constexpr int CTL_TOK_PER_BLOCK = CTL_WAVES * CTL_TOK;
 
 __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     int BL, int D, int M, const uint4* __restrict__ x_sel, const float* __restrict__ w_phi,
     const float* __restrict__ w_r, const float* __restrict__ a_phi,
-    const float* __restrict__ a_r, float* __restrict__ p_out, float* __restrict__ r_out,
-    TokenCtl* __restrict__ ctl) {
-    __shared__ float red[2][CTL_THREADS / 64];
+    const float* __restrict__ a_r, const float* __restrict__ nu, const float* __restrict__ theta,
+    float* __restrict__ p_out, float* __restrict__ r_out, float2* __restrict__ u_out,
+    TokenCtl* __restrict__ ctl, float4* __restrict__ mtab) {
+    __shared__ float red[2][CTL_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int m = blockIdx.x * CTL_THREADS + tid; m < M; m += gridDim.x * CTL_THREADS)
+        store_mode(mtab, m, mode_const(nu[m], theta[m]));
 
     // direction norms over all D+1 entries
     float sp = 0.f, sr = 0.f;
@@ -51,90 +59,119 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     __syncthreads();
     float np = 0.f, nr = 0.f;
 #pragma unroll
-    for (int i = 0; i < CTL_THREADS / 64; ++i) { np += red[0][i]; nr += red[1][i]; }
+    for (int i = 0; i < CTL_WAVES; ++i) { np += red[0][i]; nr += red[1][i]; }
     const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
     const float amp_phi = tanhf(a_phi[0]) / sqrtf((float)M);
     const float amp_r = tanhf(a_r[0]) / sqrtf((float)M);
     const float bias_phi = w_phi[D], bias_r = w_r[D];
 
     const int D8 = D >> 3;  // 16-byte words per row
-    for (int pass = 0; pass < CTL_PASSES; ++pass) {
-        const int tok0 = blockIdx.x * CTL_TOK_PER_BLOCK + (wave * CTL_PASSES + pass) * CTL_TOK_PER_PASS;
-        float ap[CTL_TOK_PER_PASS], ar[CTL_TOK_PER_PASS];
+    const int tok0 = blockIdx.x * CTL_TOK_PER_BLOCK + wave * CTL_TOK;
+    float ap[CTL_TOK], ar[CTL_TOK];
 #pragma unroll
-        for (int q = 0; q < CTL_TOK_PER_PASS; ++q) { ap[q] = 0.f; ar[q] = 0.f; }
-        for (int j = lane; j < D8; j += 64) {
-            const float4 wp0 = reinterpret_cast<const float4*>(w_phi)[2 * j];
-            const float4 wp1 = reinterpret_cast<const float4*>(w_phi)[2 * j + 1];
-            const float4 wr0 = reinterpret_cast<const float4*>(w_r)[2 * j];
-            const float4 wr1 = reinterpret_cast<const float4*>(w_r)[2 * j + 1];
-            const float wp[8] = {wp0.x, wp0.y, wp0.z, wp0.w, wp1.x, wp1.y, wp1.z, wp1.w};
-            const float wr[8] = {wr0.x, wr0.y, wr0.z, wr0.w, wr1.x, wr1.y, wr1.z, wr1.w};
+    for (int q = 0; q < CTL_TOK; ++q) { ap[q] = 0.f; ar[q] = 0.f; }
+    for (int j = lane; j < D8; j += 64) {
+        uint4 xv[CTL_TOK];
+        if (tok0 + CTL_TOK <= BL) {
 #pragma unroll
-            for (int q = 0; q < CTL_TOK_PER_PASS; ++q) {
-                const int tok = tok0 + q;
-                if (tok < BL) {
-                    const uint4 xv = x_sel[(size_t)tok * D8 + j];
-                    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            for (int q = 0; q < CTL_TOK; ++q) xv[q] = x_sel[(size_t)(tok0 + q) * D8 + j];
+        } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x0 = bf16_lo(xw[e]), x1 = bf16_hi(xw[e]);
-                        ap[q] = fmaf(x0, wp[2 * e], ap[q]);
-                        ap[q] = fmaf(x1, wp[2 * e + 1], ap[q]);
-                        ar[q] = fmaf(x0, wr[2 * e], ar[q]);
-                        ar[q] = fmaf(x1, wr[2 * e + 1], ar[q]);
-                    }
-                }
+            for (int q = 0; q < CTL_TOK; ++q)
+                xv[q] = (tok0 + q < BL) ? x_sel[(size_t)(tok0 + q) * D8 + j] : make_uint4(0, 0, 0, 0);
+        }
+        const float4 wp0 = reinterpret_cast<const float4*>(w_phi)[2 * j];
+        const float4 wp1 = reinterpret_cast<const float4*>(w_phi)[2 * j + 1];
+        const float4 wr0 = reinterpret_cast<const float4*>(w_r)[2 * j];
+        const float4 wr1 = reinterpret_cast<const float4*>(w_r)[2 * j + 1];
+        const float wp[8] = {wp0.x, wp0.y, wp0.z, wp0.w, wp1.x, wp1.y, wp1.z, wp1.w};
+        const float wr[8] = {wr0.x, wr0.y, wr0.z, wr0.w, wr1.x, wr1.y, wr1.z, wr1.w};
+#pragma unroll
+        for (int q = 0; q < CTL_TOK; ++q) {
+            const uint32_t xw[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = bf16_lo(xw[e]), x1 = bf16_hi(xw[e]);
+                ap[q] = fmaf(x0, wp[2 * e], ap[q]);
+                ap[q] = fmaf(x1, wp[2 * e + 1], ap[q]);
+                ar[q] = fmaf(x0, wr[2 * e], ar[q]);
+                ar[q] = fmaf(x1, wr[2 * e + 1], ar[q]);
             }
         }
-        float up = 0.f, ur = 0.f;
+    }
+    float up = 0.f, ur = 0.f;
 #pragma unroll
-        for (int q = 0; q < CTL_TOK_PER_PASS; ++q) {
-            const float sp_q = wave_sum(ap[q]), sr_q = wave_sum(ar[q]);
-            if (lane == q) { up = sp_q; ur = sr_q; }
-        }
-        const int tok = tok0 + lane;
-        if (lane < CTL_TOK_PER_PASS && tok < BL) {
-            const float p = tanhf((up + bias_phi) * inv_phi);
-            const float r = tanhf((ur + bias_r) * inv_r);
-            const float q = r / (1.0f + r * r);
-            const float d = amp_phi * p, c = amp_r * q;
-            p_out[tok] = p;
-            r_out[tok] = r;
-            float sd, cd;
-            sincosf(d, &sd, &cd);
-            TokenCtl t;
-            t.E = expf(c);
-            t.C = cd;
-            t.S = sd;
-            t.pad = 0.f;
-            ctl[tok] = t;
-        }
+    for (int q = 0; q < CTL_TOK; ++q) {
+        const float sp_q = wave_sum(ap[q]), sr_q = wave_sum(ar[q]);
+        if (lane == q) { up = sp_q; ur = sr_q; }
+    }
+    const int tok = tok0 + lane;
+    if (lane < CTL_TOK && tok < BL) {
+        // x~ . w^ = (x_sel . w[0:D] + w[D]) / ||w||
+        const float u_phi = (up + bias_phi) * inv_phi;
+        const float u_r = (ur + bias_r) * inv_r;
+        const float p = tanhf(u_phi);
+        const float r = tanhf(u_r);
+        const float q = r / (1.0f + r * r);
+        const float d = amp_phi * p, c = amp_r * q;
+        p_out[tok] = p;
+        r_out[tok] = r;
+        u_out[tok] = make_float2(u_phi, u_r);
+        float sd, cd;
+        sincosf(d, &sd, &cd);
+        TokenCtl t;
+        t.E = expf(c);
+        t.C = cd;
+        t.S = sd;
+        t.pad = 0.f;
+        ctl[tok] = t;
     }
 }
 
 // ---------------------------------------------------------- K2 / K5 ---
 template <int VM> struct Words;
+// VM packed BF16 complex words of one lane; `row` is wave-uniform and `off`
+// the lane's 32-bit word offset, so the load takes the scalar-base form.
 template <> struct Words<1> {
     uint32_t w[1];
-    __device__ void load(const uint32_t* p) { w[0] = *p; }
+    __device__ void load(const uint32_t* row, int off) { w[0] = row[off]; }
 };
 template <> struct Words<2> {
     uint32_t w[2];
-    __device__ void load(const uint32_t* p) {
-        uint2 v = *reinterpret_cast<const uint2*>(p);
+    __device__ void load(const uint32_t* row, int off) {
+        uint2 v = *reinterpret_cast<const uint2*>(row + off);
         w[0] = v.x; w[1] = v.y;
     }
 };
 template <> struct Words<4> {
     uint32_t w[4];
-    __device__ void load(const uint32_t* p) {
-        uint4 v = *reinterpret_cast<const uint4*>(p);
+    __device__ void load(const uint32_t* row, int off) {
+        uint4 v = *reinterpret_cast<const uint4*>(row + off);
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     }
 };
 
-constexpr int SUM_VM = 4;
+#ifndef LRS_SUM_VM
+#define LRS_SUM_VM 2
+#endif
+#ifndef LRS_REP_VM
+#define LRS_REP_VM 2
+#endif
+constexpr int SUM_VM = LRS_SUM_VM;
+constexpr int REP_VM = LRS_REP_VM;
+
+// All drive words of one chunk for this lane, issued before anything else is
+// scheduled: the recurrence is serial within a lane, so memory-level
+// parallelism comes from requesting the whole chunk at once.  Only the last
+// chunk of a sequence can be partial; full chunks take the branch-free path.
+template <int VM, int K, bool FULL>
+__device__ __forceinline__ void load_chunk(Words<VM> (&w)[K], const uint32_t* __restrict__ rows, int M,
+                                           int off, int kc) {
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        if (FULL || i < kc) w[i].load(rows + (size_t)i * M, off);
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // One step of the forward summary (REV = false) or of the reverse conjugate
 // summary (REV = true) for the VM modes of this lane.
@@ -157,64 +194,83 @@ __device__ __forceinline__ void summary_step(const ModeConst (&k)[VM], cf (&A)[V
     }
 }
 
-template <int VM, int K, bool REV>
-__global__ __launch_bounds__(256) void samu_summary_kernel(
-    int L, int M, int C, const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
-    const float* __restrict__ nu, const float* __restrict__ theta, float* __restrict__ summ) {
-    const int m0 = (blockIdx.x * blockDim.x + threadIdx.x) * VM;
-    const int c = blockIdx.y, b = blockIdx.z;
-    if (m0 >= M) return;
+// Chunk summary S_c (or, REV, the conjugate reverse summary of the chunk),
+// one workgroup per (chunk, slice of modes).  The token controls of the chunk
+// are requested first and staged in LDS; the drive loads follow as one batch.
+template <int VM, int K, bool REV, bool FULL>
+__device__ __forceinline__ void summary_chunk(TokenCtl (&sctl)[K], int L, int M, int C, int b, int c,
+                                              int m0, bool active, const TokenCtl* __restrict__ ctl,
+                                              const uint32_t* __restrict__ drive,
+                                              const float4* __restrict__ mtab, float* __restrict__ summ) {
+    const int s = c * K;
+    const int kc = FULL ? K : L - s;
+    const int mc = active ? m0 : M - VM;
+    float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
+    if ((int)threadIdx.x < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + threadIdx.x];
+    Words<VM> w[K];
+    load_chunk<VM, K, FULL>(w, drive + ((size_t)b * L + s) * M, M, mc, kc);
     ModeConst k[VM];
-#pragma unroll
-    for (int v = 0; v < VM; ++v) k[v] = mode_const(nu[m0 + v], theta[m0 + v]);
     cf A[VM], Bv[VM];
 #pragma unroll
-    for (int v = 0; v < VM; ++v) { A[v] = {1.f, 0.f}; Bv[v] = {0.f, 0.f}; }
-
-    const int s = c * K;
-    const int kc = min(K, L - s);
-    const TokenCtl* tc = ctl + (size_t)b * L + s;
-    const uint32_t* dp = drive + ((size_t)b * L + s) * M + m0;
-    if (kc == K) {
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-            const int i = REV ? K - 1 - j : j;
-            Words<VM> w;
-            w.load(dp + (size_t)i * M);
-            summary_step<VM, REV>(k, A, Bv, tc[i], w);
-        }
-    } else {
-        for (int j = 0; j < kc; ++j) {
-            const int i = REV ? kc - 1 - j : j;
-            Words<VM> w;
-            w.load(dp + (size_t)i * M);
-            summary_step<VM, REV>(k, A, Bv, tc[i], w);
-        }
+    for (int v = 0; v < VM; ++v) {
+        k[v] = load_mode(mtab, mc + v);
+        A[v] = {1.f, 0.f};
+        Bv[v] = {0.f, 0.f};
     }
-    float4* out = reinterpret_cast<float4*>(summ) + ((size_t)b * C + c) * M + m0;
+    if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
+    __syncthreads();
+    const int kq = opaque(kc);
 #pragma unroll
-    for (int v = 0; v < VM; ++v) out[v] = make_float4(A[v].re, A[v].im, Bv[v].re, Bv[v].im);
+    for (int j = 0; j < K; ++j) {
+        const int i = REV ? K - 1 - j : j;
+        if (i < kq) summary_step<VM, REV>(k, A, Bv, sctl[i], w[i]);
+    }
+    if (active) {
+        float4* out = reinterpret_cast<float4*>(summ) + ((size_t)b * C + c) * M + m0;
+#pragma unroll
+        for (int v = 0; v < VM; ++v) out[v] = make_float4(A[v].re, A[v].im, Bv[v].re, Bv[v].im);
+    }
+}
+
+// At least 4 waves per SIMD: otherwise the scheduler hoists every token's
+// transition ahead of the serial chain and occupancy collapses.
+template <int VM, int K, bool REV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void samu_summary_kernel(
+    int L, int M, int C, const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
+    const float4* __restrict__ mtab, float* __restrict__ summ) {
+    __shared__ TokenCtl sctl[K];
+    const int m0 = (blockIdx.x * blockDim.x + threadIdx.x) * VM;
+    const int c = blockIdx.y, b = blockIdx.z;
+    const bool active = m0 < M;
+    if ((c + 1) * K <= L)
+        summary_chunk<VM, K, REV, true>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, summ);
+    else
+        summary_chunk<VM, K, REV, false>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, summ);
 }
 
 // ------------------------------------------------------------------ K4 ---
-constexpr int REP_VM = 4;
-
+// y row `row` (wave-uniform element index of the row start) at the lane's
+// offset `off`, as VM complex values.
 template <int VM, bool F32>
-__device__ __forceinline__ void store_states(void* y, size_t idx, const cf (&z)[VM]) {
+__device__ __forceinline__ void store_states(void* y, size_t row, int off, const cf (&z)[VM]) {
     if (F32) {
-        float2* o = reinterpret_cast<float2*>(y) + idx;
+        float2* o = reinterpret_cast<float2*>(y) + row + off;
         if (VM == 4) {
             reinterpret_cast<float4*>(o)[0] = make_float4(z[0].re, z[0].im, z[1].re, z[1].im);
             reinterpret_cast<float4*>(o)[1] = make_float4(z[2].re, z[2].im, z[3].re, z[3].im);
+        } else if (VM == 2) {
+            reinterpret_cast<float4*>(o)[0] = make_float4(z[0].re, z[0].im, z[1].re, z[1].im);
         } else {
 #pragma unroll
             for (int v = 0; v < VM; ++v) o[v] = make_float2(z[v].re, z[v].im);
         }
     } else {
-        uint32_t* o = reinterpret_cast<uint32_t*>(y) + idx;
+        uint32_t* o = reinterpret_cast<uint32_t*>(y) + row + off;
         if (VM == 4) {
             *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf16x2(z[0].re, z[0].im), pack_bf16x2(z[1].re, z[1].im),
                                                       pack_bf16x2(z[2].re, z[2].im), pack_bf16x2(z[3].re, z[3].im));
+        } else if (VM == 2) {
+            *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(z[0].re, z[0].im), pack_bf16x2(z[1].re, z[1].im));
         } else {
 #pragma unroll
             for (int v = 0; v < VM; ++v) o[v] = pack_bf16x2(z[v].re, z[v].im);
@@ -222,49 +278,65 @@ __device__ __forceinline__ void store_states(void* y, size_t idx, const cf (&z)[
     }
 }
 
-template <int VM, int K, bool F32>
-__global__ __launch_bounds__(256) void samu_replay_kernel(
-    int L, int M, int C, const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
-    const float* __restrict__ nu, const float* __restrict__ theta,
-    const float* __restrict__ entries, void* __restrict__ y, float* __restrict__ z_final) {
-    const int m0 = (blockIdx.x * blockDim.x + threadIdx.x) * VM;
-    const int c = blockIdx.y, b = blockIdx.z;
-    if (m0 >= M) return;
+// Replay of one chunk from its entry state Q_c(init) = L_c(O_g(init)):
+// y_t = z_t for every token; the last chunk also writes z_final.
+template <int VM, int K, bool F32, bool FULL>
+__device__ __forceinline__ void replay_chunk(TokenCtl (&sctl)[K], int L, int M, int C, int b, int c,
+                                             int m0, bool active, const TokenCtl* __restrict__ ctl,
+                                             const uint32_t* __restrict__ drive,
+                                             const float4* __restrict__ mtab,
+                                             const float* __restrict__ entries, void* __restrict__ y,
+                                             float* __restrict__ z_final) {
+    const int s = c * K;
+    const int kc = FULL ? K : L - s;
+    const int mc = active ? m0 : M - VM;
+    const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform
+    float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
+    if ((int)threadIdx.x < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + threadIdx.x];
+    Words<VM> w[K];
+    load_chunk<VM, K, FULL>(w, drive + row0, M, mc, kc);
     ModeConst k[VM];
     cf z[VM];
-    const float2* ent = reinterpret_cast<const float2*>(entries) + ((size_t)b * C + c) * M + m0;
+    const float2* ent = reinterpret_cast<const float2*>(entries) + ((size_t)b * C + c) * M + mc;
 #pragma unroll
     for (int v = 0; v < VM; ++v) {
-        k[v] = mode_const(nu[m0 + v], theta[m0 + v]);
+        k[v] = load_mode(mtab, mc + v);
         const float2 e = ent[v];
         z[v] = {e.x, e.y};
     }
-    const int s = c * K;
-    const int kc = min(K, L - s);
-    const TokenCtl* tc = ctl + (size_t)b * L + s;
-    const size_t row0 = ((size_t)b * L + s) * M + m0;
-    auto step = [&](int i) {
-        Words<VM> w;
-        w.load(drive + row0 + (size_t)i * M);
-        const TokenCtl t = tc[i];
+    if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
+    __syncthreads();
+    const int kq = opaque(kc);
 #pragma unroll
-        for (int v = 0; v < VM; ++v) {
-            const cf lam = mode_lambda(k[v], t.E, t.C, t.S);
-            z[v] = cfma(lam, z[v], {bf16_lo(w.w[v]), bf16_hi(w.w[v])});
+    for (int i = 0; i < K; ++i) {
+        if (i < kq) {
+            const TokenCtl t = sctl[i];
+#pragma unroll
+            for (int v = 0; v < VM; ++v)
+                z[v] = cfma(mode_lambda(k[v], t.E, t.C, t.S), z[v], {bf16_lo(w[i].w[v]), bf16_hi(w[i].w[v])});
+            if (active) store_states<VM, F32>(y, row0 + (size_t)i * M, mc, z);
         }
-        store_states<VM, F32>(y, row0 + (size_t)i * M, z);
-    };
-    if (kc == K) {
-#pragma unroll
-        for (int i = 0; i < K; ++i) step(i);
-    } else {
-        for (int i = 0; i < kc; ++i) step(i);
     }
-    if (z_final && c == C - 1) {
+    if (active && z_final && c == C - 1) {
         float2* zf = reinterpret_cast<float2*>(z_final) + (size_t)b * M + m0;
 #pragma unroll
         for (int v = 0; v < VM; ++v) zf[v] = make_float2(z[v].re, z[v].im);
     }
+}
+
+template <int VM, int K, bool F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void samu_replay_kernel(
+    int L, int M, int C, const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
+    const float4* __restrict__ mtab, const float* __restrict__ entries, void* __restrict__ y,
+    float* __restrict__ z_final) {
+    __shared__ TokenCtl sctl[K];
+    const int m0 = (blockIdx.x * blockDim.x + threadIdx.x) * VM;
+    const int c = blockIdx.y, b = blockIdx.z;
+    const bool active = m0 < M;
+    if ((c + 1) * K <= L)
+        replay_chunk<VM, K, F32, true>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, entries, y, z_final);
+    else
+        replay_chunk<VM, K, F32, false>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, entries, y, z_final);
 }
 
 inline int mode_block(int M, int VM) {
@@ -274,24 +346,25 @@ inline int mode_block(int M, int VM) {
 
 }  // namespace
 
-hipError_t launch_samu_controller(const SamuParams& p, float* p_out, float* r_out, float* ctl,
-                                  hipStream_t s) {
+hipError_t launch_samu_controller(const SamuParams& p, float* p_out, float* r_out, float* u_out,
+                                  float* ctl, float* mtab, hipStream_t s) {
     const int BL = p.B * p.L;
     const int grid = (int)ceil_div(BL, CTL_TOK_PER_BLOCK);
     LRS_LAUNCH(K_SAMU_CONTROLLER, samu_controller_kernel, dim3(grid), dim3(CTL_THREADS), 0, s,
-               BL, p.D, p.M, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p_out, r_out,
-               (TokenCtl*)ctl);
+               BL, p.D, p.M, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p.nu, p.theta,
+               p_out, r_out, (float2*)u_out, (TokenCtl*)ctl, (float4*)mtab);
     return hipGetLastError();
 }
 
 hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const float* ctl,
-                               const void* drive, bool reverse, float* summ, hipStream_t s) {
+                               const float* mtab, const void* drive, bool reverse, float* summ,
+                               hipStream_t s) {
     const int blk = mode_block(p.M, SUM_VM);
     const dim3 grid((unsigned)ceil_div(ceil_div(p.M, SUM_VM), blk), ch.C, ch.B);
     const int id = reverse ? K_SAMU_REV_SUMMARY : K_SAMU_SUMMARY;
 #define SUMMARY_CASE(KK, RR)                                                                        \
     LRS_LAUNCH(id, (samu_summary_kernel<SUM_VM, KK, RR>), grid, dim3(blk), 0, s, p.L, p.M, ch.C, \
-               (const TokenCtl*)ctl, (const uint32_t*)drive, p.nu, p.theta, summ)
+               (const TokenCtl*)ctl, (const uint32_t*)drive, (const float4*)mtab, summ)
     if (ch.K == 32) {
         if (reverse) SUMMARY_CASE(32, true); else SUMMARY_CASE(32, false);
     } else {
@@ -302,14 +375,14 @@ hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const fl
 }
 
 hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
-                              const float* entries, void* y, int y_f32, float* z_final,
-                              hipStream_t s) {
+                              const float* mtab, const float* entries, void* y, int y_f32,
+                              float* z_final, hipStream_t s) {
     const int blk = mode_block(p.M, REP_VM);
     const dim3 grid((unsigned)ceil_div(ceil_div(p.M, REP_VM), blk), ch.C, ch.B);
 #define REPLAY_CASE(KK, FF)                                                                       \
     LRS_LAUNCH(K_SAMU_REPLAY, (samu_replay_kernel<REP_VM, KK, FF>), grid, dim3(blk), 0, s, p.L, \
-               p.M, ch.C, (const TokenCtl*)ctl, (const uint32_t*)p.b, p.nu, p.theta, entries, y, \
-               z_final)
+               p.M, ch.C, (const TokenCtl*)ctl, (const uint32_t*)p.b, (const float4*)mtab,       \
+               entries, y, z_final)
     if (ch.K == 32) {
         if (y_f32) REPLAY_CASE(32, true); else REPLAY_CASE(32, false);
     } else {

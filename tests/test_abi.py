@@ -49,11 +49,17 @@ def test_saved_and_workspace_sizes():
     B, L, D, K = 1, 32768, 2048, 32
     M, C = D // 2, L // K
     sv = scan.samu_scan_saved_bytes(B, L, D, K)
-    # p, r, per-token (E, C, S) record, chunk entry states
-    assert sv >= B * L * (4 + 4 + 16) + B * C * M * 8
-    assert sv < B * L * (4 + 4 + 16) + B * C * M * 8 + 4096
-    assert scan.samu_scan_workspace_bytes(B, L, D, K, 0, False) >= B * C * M * 16
-    assert scan.samu_scan_workspace_bytes(B, L, D, K, 0, True) > B * C * M * 16
+    # p, r, (u_phi, u_r), per-token (E, C, S) record, mode table, chunk entry states
+    need = B * L * (4 + 4 + 8 + 16) + M * 32 + B * C * M * 8
+    assert need <= sv < need + 8 * 256
+    # forward workspace: chunk summaries and group summaries (16 B per mode each)
+    G = 4
+    NG = C // G
+    need = B * C * M * 16 + B * NG * M * 16
+    assert need <= scan.samu_scan_workspace_bytes(B, L, D, K, G, False) < need + 4 * 256
+    # backward adds the per-tile controller partials [B, M/64 tiles, L, 2]
+    assert scan.samu_scan_workspace_bytes(B, L, D, K, G, True) > B * (M // 64) * L * 8
+    assert scan.samu_scan_workspace_bytes(B, L, D, K, 0, False) > 0
     assert scan.samu_scan_workspace_bytes(B, L, 1001, K, 0, False) == 0      # D % 8
     assert scan.samu_scan_workspace_bytes(B, L, D, 24, 0, False) == 0        # K
     assert scan.rglru_scan_saved_bytes(4, 8192, 2560, 16) >= 4 * 512 * 2560 * 4
