@@ -60,8 +60,10 @@ def kernel_bytes(name, B, L, D, K, G):
         "samu_reverse_summary": 2 * BLD + 16 * BL + 32 * M + 16 * BCM,
         # chunk summaries -> group summaries
         "prefix_group_compose": 16 * BCM + 16 * B * NG * M,
-        # group summaries, chunk summaries, initial state -> state entering every chunk
-        "prefix_chunk_entries": 16 * B * NG * M + 16 * BCM + 8 * B * M + 8 * BCM,
+        # group summaries, initial state -> state entering every group
+        "prefix_group_scan": 16 * B * NG * M + 8 * B * M + 8 * B * NG * M,
+        # group entry states, chunk summaries -> state entering every chunk
+        "prefix_chunk_entries": 8 * B * NG * M + 16 * BCM + 8 * BCM,
         # b, (E, C, S), entry states -> y, final state
         "samu_replay": 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 2 * BLD + 8 * B * M,
         # dy, b, (E, C, S), entry states, adjoint carries -> db, per-tile controller

@@ -47,10 +47,11 @@ hipEvent_t pool_get() {
 }  // namespace
 
 static const char* const kKernelNames[K_NUM_KERNELS] = {
-    "samu_controller", "samu_chunk_summary", "prefix_group_compose", "prefix_group_outer",
+    "samu_controller", "samu_chunk_summary", "prefix_group_compose", "prefix_group_scan",
     "prefix_chunk_entries", "samu_replay", "samu_reverse_summary", "samu_bwd_replay",
     "samu_controller_bwd", "samu_param_reduce", "samu_param_final", "rglru_chunk_summary",
-    "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha_reduce"};
+    "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha_reduce",
+    "rglru_alpha_final"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 
@@ -143,7 +144,7 @@ static SamuFwdWs samu_fwd_ws_layout(void* base, const Chunking& ch, int M, size_
     Carver cv(base);
     SamuFwdWs w;
     w.summ = cv.take<float>((size_t)ch.B * ch.C * M * 4);
-    w.gsum = cv.take<float>((size_t)ch.B * ch.NG * M * 4);
+    w.gsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
     if (bytes) *bytes = cv.off;
     return w;
 }
@@ -161,7 +162,7 @@ static SamuBwdWs samu_bwd_ws_layout(void* base, const Chunking& ch, int D, int M
     w.n_blk = (int)ceil_div((int64_t)ch.B * ch.L, samu_ctl_tok_per_blk());
     w.n_seg = std::min(kParamSegments, std::max(1, std::min(w.n_blk, ch.B * ch.C)));
     w.rsumm = cv.take<float>(BCM * 4);
-    w.rgsum = cv.take<float>((size_t)ch.B * ch.NG * M * 4);
+    w.rgsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
     w.carry = cv.take<float>(BCM * 2);
     w.tok_part = cv.take<float>((size_t)ch.B * w.n_tiles * ch.L * 2);
     w.mode_part = cv.take<float>(BCM * 2);
@@ -185,16 +186,20 @@ static RgSaved rg_saved_layout(void* base, const Chunking& ch, int D, size_t* by
 
 struct RgWs {
     float *summ, *gsum, *carry, *alpha_part;
+    double* alpha_seg;
+    int n_seg;
 };
 static RgWs rg_ws_layout(void* base, const Chunking& ch, int D, bool backward, size_t* bytes) {
     Carver cv(base);
     RgWs w{};
     const size_t BCD = (size_t)ch.B * ch.C * D;
     w.summ = cv.take<float>(BCD * 2);
-    w.gsum = cv.take<float>((size_t)ch.B * ch.NG * D * 2);
+    w.gsum = cv.take<float>((size_t)ch.B * ch.NG * D * 3);
     if (backward) {
         w.carry = cv.take<float>(BCD);
         w.alpha_part = cv.take<float>(BCD);
+        w.n_seg = rglru_alpha_segments(ch.B, ch.C);
+        w.alpha_seg = cv.take<double>((size_t)w.n_seg * D);
     }
     if (bytes) *bytes = cv.off;
     return w;
@@ -497,7 +502,7 @@ scan_status rglru_scan_bwd(int B, int L, int D, int K, int G, const void* x, con
     LRS_TRY(launch_prefix(1, true, ch, D, ws.summ, ws.gsum, dh_final, ws.carry, s), "rglru reverse prefix");
     LRS_TRY(launch_rglru_bwd_replay(p, ch, sv.entries, ws.carry, dy, dx, dlx, dla, f32, dh0, ws.alpha_part, s),
             "rglru backward replay");
-    LRS_TRY(launch_rglru_alpha_reduce(p, ch, ws.alpha_part, dalpha, s), "rglru alpha reduction");
+    LRS_TRY(launch_rglru_alpha_reduce(p, ch, ws.alpha_part, ws.alpha_seg, ws.n_seg, dalpha, s), "rglru alpha reduction");
     return SCAN_OK;
 }
 

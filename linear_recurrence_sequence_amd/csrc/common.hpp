@@ -108,6 +108,13 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
+// A per-lane value the optimizer cannot see through: functions of it are
+// computed again instead of being kept live from an earlier evaluation.
+__device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Per-token control record written by the controller kernel.
 struct TokenCtl { float E, C, S, pad; };
 

@@ -31,6 +31,7 @@ enum KernelId {
     K_RGLRU_REV_SUMMARY,
     K_RGLRU_BWD_REPLAY,
     K_RGLRU_ALPHA_REDUCE,
+    K_RGLRU_ALPHA_FINAL,
     K_NUM_KERNELS
 };
 
@@ -57,7 +58,9 @@ struct Chunking {
 // --------------------------------------------------- prefix (all scans) ---
 // Element type of a scan: 1 = real (RG-LRU channels), 2 = complex (SAMU modes).
 // summ:    [B, C, W] chunk summaries (A, B) in chunk order (2*ELEM floats each)
-// gsum:    [B, NG, W] group summaries U_g in processing order (workspace)
+// gsum:    workspace of 3*ELEM floats per (batch, group, element): [B, NG, W]
+//          group summaries U_g in processing order, then [B, NG, W] states
+//          entering each group
 // init:    [B, W] initial state (NULL = 0)
 // entries: [B, C, W] state entering each chunk (ELEM floats each); for an
 //          adjoint scan (reverse) the cotangent arriving after its last token
@@ -130,7 +133,10 @@ hipError_t launch_rglru_bwd_replay(const RglruParams& p, const Chunking& ch,
                                    const float* entries, const float* carry_in, const void* dy,
                                    void* dx, void* dlx, void* dla, int g_f32, float* dh0,
                                    float* alpha_part, hipStream_t s);
+// alpha_part: [B*C, D] per-chunk partials; seg: [n_seg, D] FP64 workspace
+int rglru_alpha_segments(int B, int C);
 hipError_t launch_rglru_alpha_reduce(const RglruParams& p, const Chunking& ch,
-                                     const float* alpha_part, float* dalpha, hipStream_t s);
+                                     const float* alpha_part, double* seg, int n_seg,
+                                     float* dalpha, hipStream_t s);
 
 }  // namespace lrs

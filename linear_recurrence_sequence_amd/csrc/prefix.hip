@@ -8,16 +8,17 @@
 //     U_g = S_{g1} o ... o S_{g0},   O_g = U_{g-1} o ... o U_0,
 //     Q_c = L_c o O_g with L_c = S_{c-1} o ... o S_{g0},
 // where (A2, B2) o (A1, B1) = (A2 A1, A2 B1 + B2) and the right operand runs
-// first.  The state entering chunk c is Q_c(init).  Two kernels:
-//   * compose: one thread per (group, mode) forms U_g from its chunks;
-//   * scan + expand: a workgroup owns a few modes and a run of groups; an LDS
-//     Hillis-Steele scan (later o earlier at every step, so the order is kept)
-//     gives O_g, applied to the carried state, and each thread then walks its
-//     group's chunks applying S_c, writing the state entering every chunk --
+// first.  The state entering chunk c is Q_c(init).  Three kernels:
+//   * compose: one thread per (group, element) forms U_g from its chunks;
+//   * group scan: a workgroup owns a few elements and all groups; an LDS
+//     Hillis-Steele scan (later o earlier at every step, so the order is
+//     kept) gives O_g, and O_g(init), the state entering group g, is stored;
+//   * expand: one thread per (group, element) walks the group's chunks from
+//     that state, applying S_c and storing the state entering every chunk --
 //     that walk is L_c applied to O_g(init).
 // Adjoint scans visit chunks and groups in reverse order with the same
-// operator.  Threads map to modes/channels (fastest), so loads and stores are
-// contiguous across lanes.
+// operator.  In compose and expand, lanes map to consecutive elements, so
+// every row access is contiguous across the wave.
 #include "common.hpp"
 
 namespace lrs {
@@ -97,12 +98,12 @@ __global__ __launch_bounds__(CMP_THREADS) void prefix_compose_kernel(
 
 constexpr int SCAN_THREADS = 1024;
 
-// Scan over groups (processing order) then expansion to chunk entries.
-// MT modes per workgroup, NGB = SCAN_THREADS / MT group slots per segment.
-template <int E, bool REV>
-__global__ __launch_bounds__(SCAN_THREADS) void prefix_scan_expand_kernel(
-    int C, int G, int NG, int W, int MT, const float* __restrict__ summ,
-    const float* __restrict__ gsum, const float* __restrict__ init, float* __restrict__ entries) {
+// Scan over groups (processing order): MT elements per workgroup, NGB = SCAN_THREADS / MT
+// group slots per segment, segments chained through a carried state.
+template <int E>
+__global__ __launch_bounds__(SCAN_THREADS) void prefix_group_scan_kernel(
+    int NG, int W, int MT, const float* __restrict__ gsum, const float* __restrict__ init,
+    float* __restrict__ gentry) {
     constexpr int F = Aff<E>::F;
     __shared__ float sh[2][SCAN_THREADS * F];
     const int NGB = SCAN_THREADS / MT;
@@ -126,23 +127,32 @@ __global__ __launch_bounds__(SCAN_THREADS) void prefix_scan_expand_kernel(
             x.to_lds(&sh[buf][tid * F]);
             __syncthreads();
         }
-        // O_g applied to the carried state, then the walk over the group's chunks
+        // exclusive prefix O_g applied to the carried state
         const Aff<E> ex = gl > 0 ? Aff<E>::from_lds(&sh[buf][(tid - MT) * F]) : Aff<E>::ident();
         const Aff<E> last = Aff<E>::from_lds(&sh[buf][((NGB - 1) * MT + mt) * F]);
-        if (q < NG && wok) {
-            St<E> h = carry.apply(ex);
-            const int c0 = q * G;
-            const int n = min(G, C - c0);
-#pragma unroll 8
-            for (int i = 0; i < n; ++i) {
-                const size_t idx = ((size_t)b * C + chunk_of(c0 + i, C, REV)) * W + w;
-                const Aff<E> sc = Aff<E>::load(summ, idx);
-                h.store(entries, idx);
-                h = h.apply(sc);
-            }
-        }
+        if (q < NG && wok) carry.apply(ex).store(gentry, ((size_t)b * NG + q) * W + w);
         carry = carry.apply(last);
         __syncthreads();
+    }
+}
+
+// State entering every chunk of group q from the state entering the group.
+template <int E, bool REV>
+__global__ __launch_bounds__(CMP_THREADS) void prefix_expand_kernel(
+    int C, int G, int NG, int W, const float* __restrict__ summ, const float* __restrict__ gentry,
+    float* __restrict__ entries) {
+    const int w = blockIdx.x * CMP_THREADS + threadIdx.x;
+    const int q = blockIdx.y, b = blockIdx.z;
+    if (w >= W) return;
+    const int c0 = q * G;
+    const int n = min(G, C - c0);
+    St<E> h = St<E>::load(gentry, ((size_t)b * NG + q) * W + w);
+#pragma unroll 8
+    for (int i = 0; i < n; ++i) {
+        const size_t idx = ((size_t)b * C + chunk_of(c0 + i, C, REV)) * W + w;
+        const Aff<E> sc = Aff<E>::load(summ, idx);
+        h.store(entries, idx);
+        h = h.apply(sc);
     }
 }
 
@@ -150,19 +160,22 @@ __global__ __launch_bounds__(SCAN_THREADS) void prefix_scan_expand_kernel(
 
 hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const float* summ,
                          float* gsum, const float* init, float* entries, hipStream_t s) {
-    const dim3 cgrid((unsigned)ceil_div(W, CMP_THREADS), ch.NG, ch.B);
-    // group slots per segment: all groups when they fit, with >= 8 modes per
-    // workgroup so every group row is read as >= 8 contiguous modes
+    float* gentry = gsum + (size_t)ch.B * ch.NG * W * 2 * elem;
+    const dim3 wgrid((unsigned)ceil_div(W, CMP_THREADS), ch.NG, ch.B);
+    // group slots per segment: all groups when they fit, with >= 8 elements
+    // per workgroup so every group row is read as >= 8 contiguous elements
     int slots = 1;
     while (slots < ch.NG && slots < SCAN_THREADS / 8) slots <<= 1;
     const int MT = SCAN_THREADS / slots;
     const dim3 sgrid((unsigned)ceil_div(W, MT), ch.B);
 #define PFX(EE, RR)                                                                                          \
     do {                                                                                                     \
-        LRS_LAUNCH(K_PREFIX_GROUPS, (prefix_compose_kernel<EE, RR>), cgrid, dim3(CMP_THREADS), 0, s, ch.C,   \
+        LRS_LAUNCH(K_PREFIX_GROUPS, (prefix_compose_kernel<EE, RR>), wgrid, dim3(CMP_THREADS), 0, s, ch.C,   \
                    ch.G, ch.NG, W, summ, gsum);                                                               \
-        LRS_LAUNCH(K_PREFIX_ENTRIES, (prefix_scan_expand_kernel<EE, RR>), sgrid, dim3(SCAN_THREADS), 0, s,  \
-                   ch.C, ch.G, ch.NG, W, MT, summ, (const float*)gsum, init, entries);                       \
+        LRS_LAUNCH(K_PREFIX_OUTER, (prefix_group_scan_kernel<EE>), sgrid, dim3(SCAN_THREADS), 0, s, ch.NG,  \
+                   W, MT, (const float*)gsum, init, gentry);                                                  \
+        LRS_LAUNCH(K_PREFIX_ENTRIES, (prefix_expand_kernel<EE, RR>), wgrid, dim3(CMP_THREADS), 0, s, ch.C,   \
+                   ch.G, ch.NG, W, summ, (const float*)gentry, entries);                                      \
     } while (0)
     if (elem == 2) {
         if (reverse) PFX(2, true); else PFX(2, false);

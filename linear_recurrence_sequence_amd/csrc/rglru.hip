@@ -12,334 +12,474 @@
 //   chunk) alpha partials and reduces them over batch and chunks to [D]; the
 //   square-root derivative is truncated (capped at 1000 here).
 //
-// Layout: lanes run over channels, VM = 2 channels per lane, so each token
-// costs one 32-bit load per input tensor per lane; a workgroup owns one chunk
-// of one batch row and 256 * VM channels.
+// Layout: lanes run over channel pairs (one 32-bit word of each BF16 tensor
+// per lane and token, so a wave reads 256 contiguous bytes of a row); a
+// workgroup owns one chunk of one batch row and 512 channels.  Every chunk
+// but a ragged last one is loaded branch-free from a uniform row base plus
+// a 32-bit lane offset; the last one takes a guarded instance of the same
+// code.
+//
+// Special functions per channel and token: both sigmoids share one
+// reciprocal, 1/((1+e^-lx)(1+e^-la)), and one reciprocal square root gives
+// both sqrt(u) = u rsq(u) and the capped derivative rsq(max(u, u_min)) =
+// min(rsq(u), rsq(u_min)).
 #include "common.hpp"
 
 namespace lrs {
 namespace {
 
-constexpr int RG_VM = 2;
 constexpr int RG_THREADS = 256;
-// 1/(2 sqrt(u)) is capped at 1000: u is clamped below at 1/(4 * 1000^2).
-constexpr float RG_SQRT_UMIN = 2.5e-7f;
+constexpr int RG_CH = 2 * RG_THREADS;     // channels per workgroup
+// 1/(2 sqrt(u)) is capped at 1000: the reciprocal square root used for the
+// derivative is capped at 2000 = rsq(2.5e-7).
+constexpr float RG_RSQ_CAP = 2000.0f;
 constexpr float LOG2E = 1.4426950408889634f;
+// e^-v is formed as 2^min(-v log2 e, 57.7) (v >= -40): the product of two
+// such factors stays below FP32 overflow; sigmoid(-40) ~ 4e-18 absorbs it.
+constexpr float RG_EXP_ARG_MAX = 57.7f;
 
 struct ChanConst {
     float k8;     // -8 softplus(alpha) log2(e): a = 2^(k8 g^a)
-    float sp;     // softplus(alpha)
-    float dsp;    // sigmoid(alpha) = d softplus / d alpha
+    float sp8;    // -8 softplus(alpha)
+    float dsp8;   // -8 sigmoid(alpha) = -8 d softplus / d alpha
 };
 
 __device__ __forceinline__ ChanConst chan_const(float alpha) {
     ChanConst k;
     const float sp = alpha > 20.f ? alpha + log1pf(expf(-alpha)) : log1pf(expf(alpha));
-    k.sp = sp;
-    k.k8 = -8.0f * sp * LOG2E;
-    k.dsp = 1.0f / (1.0f + expf(-alpha));
+    k.sp8 = -8.0f * sp;
+    k.k8 = k.sp8 * LOG2E;
+    k.dsp8 = -8.0f / (1.0f + expf(-alpha));
     return k;
 }
 
-__device__ __forceinline__ float sigm(float v) {
-    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * LOG2E));
+__device__ __forceinline__ float neg_exp(float v) {
+    return __builtin_amdgcn_exp2f(fminf(-v * LOG2E, RG_EXP_ARG_MAX));
 }
 
+__device__ __forceinline__ float sigm(float v) { return __builtin_amdgcn_rcpf(1.0f + neg_exp(v)); }
+
 struct Gate {
-    float a, m, gx, ga;
+    float gx, ga;   // sigmoid(l^x), sigmoid(l^a)
+    float a0;       // retention before a reset
+    float a, m;     // retention and normalization after a reset
+    float r;        // rsq(1 - a0^2) (infinite-free)
 };
 
 // Gates of one channel at one token; rs = segment start.
 __device__ __forceinline__ Gate gates(const ChanConst& k, float lx, float la, bool rs) {
     Gate g;
-    g.gx = sigm(lx);
-    g.ga = sigm(la);
-    const float a = __builtin_amdgcn_exp2f(k.k8 * g.ga);
-    const float u = fmaxf(fmaf(-a, a, 1.0f), 0.0f);
-    g.a = rs ? 0.0f : a;
-    g.m = rs ? 1.0f : __builtin_amdgcn_sqrtf(u);
+    const float px = 1.0f + neg_exp(lx), pa = 1.0f + neg_exp(la);
+    const float q = __builtin_amdgcn_rcpf(px * pa);
+    g.gx = q * pa;
+    g.ga = q * px;
+    g.a0 = __builtin_amdgcn_exp2f(k.k8 * g.ga);
+    // 1 - a^2 >= 0 exactly (a <= 1), so the FMA result is >= 0; the floor only
+    // keeps rsq finite at a = 1, where u rsq(u) is then 0 as it must be
+    const float u = fmaxf(fmaf(-g.a0, g.a0, 1.0f), 1e-30f);
+    g.r = __builtin_amdgcn_rsqf(u);
+    g.a = rs ? 0.0f : g.a0;
+    g.m = rs ? 1.0f : u * g.r;
     return g;
 }
 
+// retention with a segment start applied as a multiplier, so that no uniform
+// branch splits the token loop around the special functions
 __device__ __forceinline__ float retention(const ChanConst& k, float la, bool rs) {
-    return rs ? 0.0f : __builtin_amdgcn_exp2f(k.k8 * sigm(la));
+    return __builtin_amdgcn_exp2f(k.k8 * sigm(la)) * (rs ? 0.0f : 1.0f);
 }
 
-__device__ __forceinline__ bool seg_start(const unsigned char* reset, size_t tok) {
-    return reset != nullptr && reset[tok] != 0;
-}
-
-// ---------------------------------------------------------------- K11 ---
+// Segment-start flags of a chunk as a wave-uniform bit mask (bit i = token
+// i): lane i reads flag i and a ballot gathers them, one load for the chunk,
+// so the token loop has no load or branch on the flag array.  Called at
+// kernel entry, before any lane leaves, by all 64 lanes of the wave.
 template <int K>
-__global__ __launch_bounds__(RG_THREADS) void rglru_summary_kernel(
-    int L, int D, int C, const uint32_t* __restrict__ x, const uint32_t* __restrict__ lx,
-    const uint32_t* __restrict__ la, const float* __restrict__ alpha,
-    const unsigned char* __restrict__ reset, float* __restrict__ summ) {
-    const int d0 = (blockIdx.x * RG_THREADS + threadIdx.x) * RG_VM;
-    const int c = blockIdx.y, b = blockIdx.z;
-    if (d0 >= D) return;
-    const int W = D / 2;  // words per row
-    ChanConst k[RG_VM];
-    float A[RG_VM], Bv[RG_VM];
-#pragma unroll
-    for (int v = 0; v < RG_VM; ++v) { k[v] = chan_const(alpha[d0 + v]); A[v] = 1.f; Bv[v] = 0.f; }
-    const int s = c * K;
-    const int kc = min(K, L - s);
-    const size_t tok0 = (size_t)b * L + s;
-    const size_t w0 = tok0 * W + d0 / 2;
-    auto step = [&](int i) {
-        const bool rs = seg_start(reset, tok0 + i);
-        const uint32_t xw = x[w0 + (size_t)i * W], lxw = lx[w0 + (size_t)i * W], law = la[w0 + (size_t)i * W];
-        const float xv[2] = {bf16_lo(xw), bf16_hi(xw)};
-        const float lxv[2] = {bf16_lo(lxw), bf16_hi(lxw)};
-        const float lav[2] = {bf16_lo(law), bf16_hi(law)};
-#pragma unroll
-        for (int v = 0; v < RG_VM; ++v) {
-            const Gate g = gates(k[v], lxv[v], lav[v], rs);
-            A[v] *= g.a;
-            Bv[v] = fmaf(g.a, Bv[v], xv[v] * g.gx * g.m);
-        }
-    };
-    if (kc == K) {
-#pragma unroll
-        for (int i = 0; i < K; ++i) step(i);
-    } else {
-        for (int i = 0; i < kc; ++i) step(i);
-    }
-    float2* out = reinterpret_cast<float2*>(summ) + ((size_t)b * C + c) * D + d0;
-#pragma unroll
-    for (int v = 0; v < RG_VM; ++v) out[v] = make_float2(A[v], Bv[v]);
+__device__ __forceinline__ uint32_t reset_mask(const unsigned char* reset, size_t tok0, int kc) {
+    static_assert(K <= 32, "one mask word per chunk");
+    if (!reset) return 0;
+    const int l = threadIdx.x & 63;
+    const bool f = l < kc && reset[tok0 + l] != 0;
+    return (uint32_t)__ballot(f);
 }
 
-// ---------------------------------------------------------------- K12 ---
-template <int K, bool F32>
-__global__ __launch_bounds__(RG_THREADS) void rglru_replay_kernel(
-    int L, int D, int C, const uint32_t* __restrict__ x, const uint32_t* __restrict__ lx,
-    const uint32_t* __restrict__ la, const float* __restrict__ alpha,
-    const unsigned char* __restrict__ reset, const float* __restrict__ entries,
-    void* __restrict__ y, float* __restrict__ h_final) {
-    const int d0 = (blockIdx.x * RG_THREADS + threadIdx.x) * RG_VM;
-    const int c = blockIdx.y, b = blockIdx.z;
-    if (d0 >= D) return;
-    const int W = D / 2;
-    ChanConst k[RG_VM];
-    float h[RG_VM];
-    const float* ent = entries + ((size_t)b * C + c) * D + d0;
-#pragma unroll
-    for (int v = 0; v < RG_VM; ++v) { k[v] = chan_const(alpha[d0 + v]); h[v] = ent[v]; }
-    const int s = c * K;
-    const int kc = min(K, L - s);
-    const size_t tok0 = (size_t)b * L + s;
-    const size_t w0 = tok0 * W + d0 / 2;
-    auto step = [&](int i) {
-        const bool rs = seg_start(reset, tok0 + i);
-        const size_t wi = w0 + (size_t)i * W;
-        const uint32_t xw = x[wi], lxw = lx[wi], law = la[wi];
-        const float xv[2] = {bf16_lo(xw), bf16_hi(xw)};
-        const float lxv[2] = {bf16_lo(lxw), bf16_hi(lxw)};
-        const float lav[2] = {bf16_lo(law), bf16_hi(law)};
-#pragma unroll
-        for (int v = 0; v < RG_VM; ++v) {
-            const Gate g = gates(k[v], lxv[v], lav[v], rs);
-            h[v] = fmaf(g.a, h[v], xv[v] * g.gx * g.m);
-        }
-        if (F32) reinterpret_cast<float2*>(y)[wi] = make_float2(h[0], h[1]);
-        else reinterpret_cast<uint32_t*>(y)[wi] = pack_bf16x2(h[0], h[1]);
-    };
-    if (kc == K) {
-#pragma unroll
-        for (int i = 0; i < K; ++i) step(i);
-    } else {
-        for (int i = 0; i < kc; ++i) step(i);
-    }
-    if (h_final && c == C - 1) {
-#pragma unroll
-        for (int v = 0; v < RG_VM; ++v) h_final[(size_t)b * D + d0 + v] = h[v];
-    }
+__device__ __forceinline__ bool bit(uint32_t m, int i) { return (m >> i) & 1u; }
+
+struct RgIn {
+    int L, W;     // W = D / 2 words per row
+    const uint32_t* x;
+    const uint32_t* lx;
+    const uint32_t* la;
+    const unsigned char* reset;
+};
+
+// word of token i of the chunk starting at token tok0: uniform row, lane offset
+__device__ __forceinline__ uint32_t word(const uint32_t* t, size_t tok0, int i, int W, int lw) {
+    return (t + (tok0 + i) * (size_t)W)[lw];
 }
 
-// ---------------------------------------------------------------- K13 ---
-// Reverse summary: carry -> a_t (dy_t + carry) composed from the last token of
-// the chunk to the first.
-template <int K>
-__global__ __launch_bounds__(RG_THREADS) void rglru_rev_summary_kernel(
-    int L, int D, int C, const uint32_t* __restrict__ la, const float* __restrict__ alpha,
-    const unsigned char* __restrict__ reset, const uint32_t* __restrict__ dy,
-    float* __restrict__ summ) {
-    const int d0 = (blockIdx.x * RG_THREADS + threadIdx.x) * RG_VM;
-    const int c = blockIdx.y, b = blockIdx.z;
-    if (d0 >= D) return;
-    const int W = D / 2;
-    ChanConst k[RG_VM];
-    float A[RG_VM], Bv[RG_VM];
+// ---------------------------------------------------------------- summary
+template <int K, bool FULL>
+__device__ __forceinline__ void rg_summary_chunk(const RgIn& in, const ChanConst (&k)[2], size_t tok0,
+                                                 int lw, int kc, uint32_t rm, float (&A)[2], float (&Bv)[2]) {
+    const int kq = FULL ? K : opaque(kc);
 #pragma unroll
-    for (int v = 0; v < RG_VM; ++v) { k[v] = chan_const(alpha[d0 + v]); A[v] = 1.f; Bv[v] = 0.f; }
-    const int s = c * K;
-    const int kc = min(K, L - s);
-    const size_t tok0 = (size_t)b * L + s;
-    const size_t w0 = tok0 * W + d0 / 2;
-    auto step = [&](int i) {
-        const bool rs = seg_start(reset, tok0 + i);
-        const size_t wi = w0 + (size_t)i * W;
-        const uint32_t law = la[wi], gw = dy[wi];
-        const float lav[2] = {bf16_lo(law), bf16_hi(law)};
-        const float gv[2] = {bf16_lo(gw), bf16_hi(gw)};
+    for (int i = 0; i < K; ++i) {
+        if (FULL || i < kq) {
+            const bool rs = bit(rm, i);
+            const uint32_t xw = word(in.x, tok0, i, in.W, lw);
+            const uint32_t lxw = word(in.lx, tok0, i, in.W, lw);
+            const uint32_t law = word(in.la, tok0, i, in.W, lw);
+            const float xv[2] = {bf16_lo(xw), bf16_hi(xw)};
+            const float lxv[2] = {bf16_lo(lxw), bf16_hi(lxw)};
+            const float lav[2] = {bf16_lo(law), bf16_hi(law)};
 #pragma unroll
-        for (int v = 0; v < RG_VM; ++v) {
-            const float a = retention(k[v], lav[v], rs);
-            A[v] *= a;
-            Bv[v] = a * (Bv[v] + gv[v]);
-        }
-    };
-    if (kc == K) {
-#pragma unroll
-        for (int i = K - 1; i >= 0; --i) step(i);
-    } else {
-        for (int i = kc - 1; i >= 0; --i) step(i);
-    }
-    float2* out = reinterpret_cast<float2*>(summ) + ((size_t)b * C + c) * D + d0;
-#pragma unroll
-    for (int v = 0; v < RG_VM; ++v) out[v] = make_float2(A[v], Bv[v]);
-}
-
-// ---------------------------------------------------------------- K14 ---
-// Backward replay: recompute h over the chunk from its entry state (keeping
-// h_{t-1} and the raw input words in registers), then run the adjoint in
-// reverse from the chunk's carry-in, regenerating the gates.
-template <int K, bool F32>
-__global__ __launch_bounds__(RG_THREADS) void rglru_bwd_replay_kernel(
-    int L, int D, int C, const uint32_t* __restrict__ x, const uint32_t* __restrict__ lx,
-    const uint32_t* __restrict__ la, const float* __restrict__ alpha,
-    const unsigned char* __restrict__ reset, const float* __restrict__ entries,
-    const float* __restrict__ carry_in, const uint32_t* __restrict__ dy, void* __restrict__ dx,
-    void* __restrict__ dlx, void* __restrict__ dla, float* __restrict__ dh0,
-    float* __restrict__ alpha_part) {
-    const int d0 = (blockIdx.x * RG_THREADS + threadIdx.x) * RG_VM;
-    const int c = blockIdx.y, b = blockIdx.z;
-    if (d0 >= D) return;
-    const int W = D / 2;
-    ChanConst k[RG_VM];
-#pragma unroll
-    for (int v = 0; v < RG_VM; ++v) k[v] = chan_const(alpha[d0 + v]);
-    const int s = c * K;
-    const int kc = min(K, L - s);
-    const size_t tok0 = (size_t)b * L + s;
-    const size_t w0 = tok0 * W + d0 / 2;
-    const size_t cidx = ((size_t)b * C + c) * D + d0;
-
-    uint32_t xs[K], lxs[K], las[K];
-    float hp[K][RG_VM];
-    {
-        float h[RG_VM];
-#pragma unroll
-        for (int v = 0; v < RG_VM; ++v) h[v] = entries[cidx + v];
-#pragma unroll
-        for (int i = 0; i < K; ++i) {
-            if (i < kc) {
-                const bool rs = seg_start(reset, tok0 + i);
-                const size_t wi = w0 + (size_t)i * W;
-                xs[i] = x[wi];
-                lxs[i] = lx[wi];
-                las[i] = la[wi];
-                const float xv[2] = {bf16_lo(xs[i]), bf16_hi(xs[i])};
-                const float lxv[2] = {bf16_lo(lxs[i]), bf16_hi(lxs[i])};
-                const float lav[2] = {bf16_lo(las[i]), bf16_hi(las[i])};
-#pragma unroll
-                for (int v = 0; v < RG_VM; ++v) {
-                    hp[i][v] = h[v];
-                    const Gate g = gates(k[v], lxv[v], lav[v], rs);
-                    h[v] = fmaf(g.a, h[v], xv[v] * g.gx * g.m);
-                }
+            for (int v = 0; v < 2; ++v) {
+                const Gate g = gates(k[v], lxv[v], lav[v], rs);
+                A[v] *= g.a;
+                Bv[v] = fmaf(g.a, Bv[v], xv[v] * g.gx * g.m);
             }
         }
     }
-    float carry[RG_VM], acc_al[RG_VM];
+}
+
+template <int K>
+__global__ __launch_bounds__(RG_THREADS) void rglru_summary_kernel(RgIn in, int C,
+                                                                   const float* __restrict__ alpha,
+                                                                   float* __restrict__ summ) {
+    const int lw = blockIdx.x * RG_THREADS + threadIdx.x;
+    const int c = blockIdx.y, b = blockIdx.z;
+    const size_t tok0 = (size_t)b * in.L + (size_t)c * K;
+    const int kc = min(K, in.L - c * K);
+    const uint32_t rm = reset_mask<K>(in.reset, tok0, kc);
+    if (lw >= in.W) return;
+    const ChanConst k[2] = {chan_const(alpha[2 * lw]), chan_const(alpha[2 * lw + 1])};
+    float A[2] = {1.f, 1.f}, Bv[2] = {0.f, 0.f};
+    if (kc == K) rg_summary_chunk<K, true>(in, k, tok0, lw, K, rm, A, Bv);
+    else rg_summary_chunk<K, false>(in, k, tok0, lw, kc, rm, A, Bv);
+    float4* out = reinterpret_cast<float4*>(summ + (((size_t)b * C + c) * in.W + lw) * 4);
+    *out = make_float4(A[0], Bv[0], A[1], Bv[1]);
+}
+
+// ----------------------------------------------------------------- replay
+template <int K, bool F32, bool FULL>
+__device__ __forceinline__ void rg_replay_chunk(const RgIn& in, const ChanConst (&k)[2], size_t tok0,
+                                                int lw, int kc, uint32_t rm, float (&h)[2], void* __restrict__ y) {
+    const int kq = FULL ? K : opaque(kc);
+    // all loads of the chunk ahead of its stores (y may not be assumed
+    // disjoint from the inputs held in the struct)
+    uint32_t xs[K], lxs[K], las[K];
 #pragma unroll
-    for (int v = 0; v < RG_VM; ++v) { carry[v] = carry_in[cidx + v]; acc_al[v] = 0.f; }
+    for (int i = 0; i < K; ++i) {
+        if (FULL || i < kq) {
+            xs[i] = word(in.x, tok0, i, in.W, lw);
+            lxs[i] = word(in.lx, tok0, i, in.W, lw);
+            las[i] = word(in.la, tok0, i, in.W, lw);
+        }
+    }
 #pragma unroll
-    for (int i = K - 1; i >= 0; --i) {
-        if (i < kc) {
-            const bool rs = seg_start(reset, tok0 + i);
-            const size_t wi = w0 + (size_t)i * W;
-            const uint32_t gw = dy[wi];
-            const float gv[2] = {bf16_lo(gw), bf16_hi(gw)};
+    for (int i = 0; i < K; ++i) {
+        if (FULL || i < kq) {
+            const bool rs = bit(rm, i);
             const float xv[2] = {bf16_lo(xs[i]), bf16_hi(xs[i])};
             const float lxv[2] = {bf16_lo(lxs[i]), bf16_hi(lxs[i])};
             const float lav[2] = {bf16_lo(las[i]), bf16_hi(las[i])};
-            float ox[RG_VM], olx[RG_VM], ola[RG_VM];
 #pragma unroll
-            for (int v = 0; v < RG_VM; ++v) {
-                const Gate gt = gates(k[v], lxv[v], lav[v], rs);
-                const float g = gv[v] + carry[v];
-                ox[v] = g * gt.gx * gt.m;
-                olx[v] = ox[v] * xv[v] * (1.0f - gt.gx);
-                float abar = 0.f;
-                if (!rs) {
-                    const float u = fmaxf(fmaf(-gt.a, gt.a, 1.0f), RG_SQRT_UMIN);
-                    const float dm_da = -gt.a * __builtin_amdgcn_rsqf(u);
-                    abar = g * fmaf(xv[v] * gt.gx, dm_da, hp[i][v]);
-                }
-                // d a / d l^a = a (-8 sp) g^a (1 - g^a); d a / d alpha = a (-8 g^a) sigmoid(alpha)
-                const float ag = abar * gt.a * gt.ga;
-                ola[v] = ag * (-8.0f * k[v].sp) * (1.0f - gt.ga);
-                acc_al[v] += ag;
-                carry[v] = gt.a * g;
+            for (int v = 0; v < 2; ++v) {
+                const Gate g = gates(k[v], lxv[v], lav[v], rs);
+                h[v] = fmaf(g.a, h[v], xv[v] * g.gx * g.m);
             }
-            if (F32) {
-                reinterpret_cast<float2*>(dx)[wi] = make_float2(ox[0], ox[1]);
-                reinterpret_cast<float2*>(dlx)[wi] = make_float2(olx[0], olx[1]);
-                reinterpret_cast<float2*>(dla)[wi] = make_float2(ola[0], ola[1]);
-            } else {
-                reinterpret_cast<uint32_t*>(dx)[wi] = pack_bf16x2(ox[0], ox[1]);
-                reinterpret_cast<uint32_t*>(dlx)[wi] = pack_bf16x2(olx[0], olx[1]);
-                reinterpret_cast<uint32_t*>(dla)[wi] = pack_bf16x2(ola[0], ola[1]);
+            const size_t row = (tok0 + i) * (size_t)in.W;
+            if (F32) (reinterpret_cast<float2*>(y) + row)[lw] = make_float2(h[0], h[1]);
+            else (reinterpret_cast<uint32_t*>(y) + row)[lw] = pack_bf16x2(h[0], h[1]);
+        }
+    }
+}
+
+template <int K, bool F32>
+__global__ __launch_bounds__(RG_THREADS) void rglru_replay_kernel(RgIn in, int C,
+                                                                  const float* __restrict__ alpha,
+                                                                  const float* __restrict__ entries,
+                                                                  void* __restrict__ y,
+                                                                  float* __restrict__ h_final) {
+    const int lw = blockIdx.x * RG_THREADS + threadIdx.x;
+    const int c = blockIdx.y, b = blockIdx.z;
+    const size_t tok0 = (size_t)b * in.L + (size_t)c * K;
+    const int kc = min(K, in.L - c * K);
+    const uint32_t rm = reset_mask<K>(in.reset, tok0, kc);
+    if (lw >= in.W) return;
+    const ChanConst k[2] = {chan_const(alpha[2 * lw]), chan_const(alpha[2 * lw + 1])};
+    const float2 e = reinterpret_cast<const float2*>(entries)[((size_t)b * C + c) * in.W + lw];
+    float h[2] = {e.x, e.y};
+    if (kc == K) rg_replay_chunk<K, F32, true>(in, k, tok0, lw, K, rm, h, y);
+    else rg_replay_chunk<K, F32, false>(in, k, tok0, lw, kc, rm, h, y);
+    if (h_final && c == C - 1)
+        reinterpret_cast<float2*>(h_final)[(size_t)b * in.W + lw] = make_float2(h[0], h[1]);
+}
+
+// -------------------------------------------------------- reverse summary
+// carry -> a_t (dy_t + carry), composed from the last token of the chunk to
+// the first: (A, B) with carry_before = A carry_after + B.
+template <int K, bool FULL>
+__device__ __forceinline__ void rg_rev_summary_chunk(const RgIn& in, const ChanConst (&k)[2],
+                                                     const uint32_t* __restrict__ dy, size_t tok0,
+                                                     int lw, int kc, uint32_t rm, float (&A)[2],
+                                                     float (&Bv)[2]) {
+    const int kq = FULL ? K : opaque(kc);
+#pragma unroll
+    for (int i = K - 1; i >= 0; --i) {
+        if (FULL || i < kq) {
+            const bool rs = bit(rm, i);
+            const uint32_t law = word(in.la, tok0, i, in.W, lw);
+            const uint32_t gw = word(dy, tok0, i, in.W, lw);
+            const float lav[2] = {bf16_lo(law), bf16_hi(law)};
+            const float gv[2] = {bf16_lo(gw), bf16_hi(gw)};
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const float a = retention(k[v], lav[v], rs);
+                A[v] *= a;
+                Bv[v] = a * (Bv[v] + gv[v]);
+            }
+        }
+    }
+}
+
+template <int K>
+__global__ __launch_bounds__(RG_THREADS) void rglru_rev_summary_kernel(RgIn in, int C,
+                                                                       const float* __restrict__ alpha,
+                                                                       const uint32_t* __restrict__ dy,
+                                                                       float* __restrict__ summ) {
+    const int lw = blockIdx.x * RG_THREADS + threadIdx.x;
+    const int c = blockIdx.y, b = blockIdx.z;
+    const size_t tok0 = (size_t)b * in.L + (size_t)c * K;
+    const int kc = min(K, in.L - c * K);
+    const uint32_t rm = reset_mask<K>(in.reset, tok0, kc);
+    if (lw >= in.W) return;
+    const ChanConst k[2] = {chan_const(alpha[2 * lw]), chan_const(alpha[2 * lw + 1])};
+    float A[2] = {1.f, 1.f}, Bv[2] = {0.f, 0.f};
+    if (kc == K) rg_rev_summary_chunk<K, true>(in, k, dy, tok0, lw, K, rm, A, Bv);
+    else rg_rev_summary_chunk<K, false>(in, k, dy, tok0, lw, kc, rm, A, Bv);
+    float4* out = reinterpret_cast<float4*>(summ + (((size_t)b * C + c) * in.W + lw) * 4);
+    *out = make_float4(A[0], Bv[0], A[1], Bv[1]);
+}
+
+// -------------------------------------------------------- backward replay
+// The chunk is handled H tokens at a time, last sub-chunk first.  For each
+// sub-chunk the forward is recomputed from a checkpoint (the state entering
+// the sub-chunk, found by one forward pass over the earlier sub-chunks),
+// keeping h_{t-1} and the three input words in registers; then the adjoint
+// runs back over it, regenerating the gates, from the cotangent carried in.
+struct RgBwdOut {
+    const uint32_t* dy;
+    void* dx;
+    void* dlx;
+    void* dla;
+};
+
+template <int H, bool F32, bool FULL>
+__device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
+                                           size_t tok0, int lw, int kq, uint32_t rm,
+                                           const float (&h_in)[2], float (&carry)[2], float (&acc)[2]) {
+    uint32_t xs[H], lxs[H], las[H], gws[H];
+    float hp[H][2];
+    float h[2] = {h_in[0], h_in[1]};
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        if (FULL || i < kq) {
+            xs[i] = word(in.x, tok0, i, in.W, lw);
+            lxs[i] = word(in.lx, tok0, i, in.W, lw);
+            las[i] = word(in.la, tok0, i, in.W, lw);
+            gws[i] = word(o.dy, tok0, i, in.W, lw);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        if (FULL || i < kq) {
+            const bool rs = bit(rm, i);
+            const float xv[2] = {bf16_lo(xs[i]), bf16_hi(xs[i])};
+            const float lxv[2] = {bf16_lo(lxs[i]), bf16_hi(lxs[i])};
+            const float lav[2] = {bf16_lo(las[i]), bf16_hi(las[i])};
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                hp[i][v] = h[v];
+                const Gate g = gates(k[v], lxv[v], lav[v], rs);
+                h[v] = fmaf(g.a, h[v], xv[v] * g.gx * g.m);
             }
         }
     }
 #pragma unroll
-    for (int v = 0; v < RG_VM; ++v) alpha_part[cidx + v] = acc_al[v] * (-8.0f * k[v].dsp);
-    if (dh0 && c == 0) {
+    for (int i = H - 1; i >= 0; --i) {
+        if (FULL || i < kq) {
+            const bool rs = bit(rm, i);
+            const float gv[2] = {bf16_lo(gws[i]), bf16_hi(gws[i])};
+            const float xv[2] = {bf16_lo(xs[i]), bf16_hi(xs[i])};
+            // the gates are evaluated again rather than kept from the forward
+            // pass: six live values per token and channel would not fit
+            const uint32_t lxw = opaque_v(lxs[i]), law = opaque_v(las[i]);
+            const float lxv[2] = {bf16_lo(lxw), bf16_hi(lxw)};
+            const float lav[2] = {bf16_lo(law), bf16_hi(law)};
+            float ox[2], olx[2], ola[2];
 #pragma unroll
-        for (int v = 0; v < RG_VM; ++v) dh0[(size_t)b * D + d0 + v] = carry[v];
+            for (int v = 0; v < 2; ++v) {
+                const Gate gt = gates(k[v], lxv[v], lav[v], rs);
+                const float g = gv[v] + carry[v];
+                const float xg = xv[v] * gt.gx;
+                ox[v] = g * gt.gx * gt.m;
+                olx[v] = g * xg * gt.m * (1.0f - gt.gx);
+                // d h / d a = h_{t-1} + x g^x dm/da, dm/da = -a / sqrt(u) (capped);
+                // zero at a segment start, where a and m are constants
+                const float dm_da = -gt.a0 * fminf(gt.r, RG_RSQ_CAP);
+                const float abar = rs ? 0.0f : g * fmaf(xg, dm_da, hp[i][v]);
+                // d a / d l^a = a (-8 sp) g^a (1 - g^a); d a / d alpha = a g^a (-8 sigmoid(alpha))
+                const float ag = abar * gt.a0 * gt.ga;
+                ola[v] = ag * k[v].sp8 * (1.0f - gt.ga);
+                acc[v] += ag;
+                carry[v] = gt.a * g;
+            }
+            const size_t row = (tok0 + i) * (size_t)in.W;
+            if (F32) {
+                (reinterpret_cast<float2*>(o.dx) + row)[lw] = make_float2(ox[0], ox[1]);
+                (reinterpret_cast<float2*>(o.dlx) + row)[lw] = make_float2(olx[0], olx[1]);
+                (reinterpret_cast<float2*>(o.dla) + row)[lw] = make_float2(ola[0], ola[1]);
+            } else {
+                (reinterpret_cast<uint32_t*>(o.dx) + row)[lw] = pack_bf16x2(ox[0], ox[1]);
+                (reinterpret_cast<uint32_t*>(o.dlx) + row)[lw] = pack_bf16x2(olx[0], olx[1]);
+                (reinterpret_cast<uint32_t*>(o.dla) + row)[lw] = pack_bf16x2(ola[0], ola[1]);
+            }
+        }
     }
 }
 
-// ---------------------------------------------------------------- K15 ---
-// d alpha = sum over batch rows and chunks of the per-chunk partials, FP64,
-// fixed order.
-__global__ __launch_bounds__(256) void rglru_alpha_reduce_kernel(
-    int D, int nchunks, const float* __restrict__ part, float* __restrict__ dalpha) {
-    const int d = blockIdx.x * 256 + threadIdx.x;
+// state after `n` tokens (n <= H, guarded when not FULL) from h
+template <int H, bool FULL>
+__device__ __forceinline__ void rg_advance(const RgIn& in, const ChanConst (&k)[2], size_t tok0, int lw,
+                                           int kq, uint32_t rm, float (&h)[2]) {
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        if (FULL || i < kq) {
+            const bool rs = bit(rm, i);
+            const uint32_t xw = word(in.x, tok0, i, in.W, lw);
+            const uint32_t lxw = word(in.lx, tok0, i, in.W, lw);
+            const uint32_t law = word(in.la, tok0, i, in.W, lw);
+            const float xv[2] = {bf16_lo(xw), bf16_hi(xw)};
+            const float lxv[2] = {bf16_lo(lxw), bf16_hi(lxw)};
+            const float lav[2] = {bf16_lo(law), bf16_hi(law)};
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const Gate g = gates(k[v], lxv[v], lav[v], rs);
+                h[v] = fmaf(g.a, h[v], xv[v] * g.gx * g.m);
+            }
+        }
+    }
+}
+
+template <int K, int H, bool F32, bool FULL>
+__device__ __forceinline__ void rg_bwd_chunk(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
+                                             size_t tok0, int lw, int kc, uint32_t rm,
+                                             const float (&h0)[2], float (&carry)[2], float (&acc)[2]) {
+    constexpr int NS = K / H;
+    const int kq = FULL ? K : opaque(kc);
+    float ck[NS][2];
+    float h[2] = {h0[0], h0[1]};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        ck[s][0] = h[0];
+        ck[s][1] = h[1];
+        if (s + 1 < NS) rg_advance<H, FULL>(in, k, tok0 + s * H, lw, kq - s * H, rm >> (s * H), h);
+    }
+#pragma unroll
+    for (int s = NS - 1; s >= 0; --s)
+        rg_bwd_sub<H, F32, FULL>(in, k, o, tok0 + s * H, lw, kq - s * H, rm >> (s * H), ck[s], carry, acc);
+}
+
+template <int K, int H, bool F32>
+__global__ __launch_bounds__(RG_THREADS) void rglru_bwd_replay_kernel(
+    RgIn in, int C, const float* __restrict__ alpha, const float* __restrict__ entries,
+    const float* __restrict__ carry_in, RgBwdOut o, float* __restrict__ dh0,
+    float* __restrict__ alpha_part) {
+    const int lw = blockIdx.x * RG_THREADS + threadIdx.x;
+    const int c = blockIdx.y, b = blockIdx.z;
+    const size_t tok0 = (size_t)b * in.L + (size_t)c * K;
+    const int kc = min(K, in.L - c * K);
+    const uint32_t rm = reset_mask<K>(in.reset, tok0, kc);
+    if (lw >= in.W) return;
+    const ChanConst k[2] = {chan_const(alpha[2 * lw]), chan_const(alpha[2 * lw + 1])};
+    const size_t cw = ((size_t)b * C + c) * in.W + lw;
+    const float2 e = reinterpret_cast<const float2*>(entries)[cw];
+    const float2 ci = reinterpret_cast<const float2*>(carry_in)[cw];
+    const float h0[2] = {e.x, e.y};
+    float carry[2] = {ci.x, ci.y}, acc[2] = {0.f, 0.f};
+    if (kc == K) rg_bwd_chunk<K, H, F32, true>(in, k, o, tok0, lw, K, rm, h0, carry, acc);
+    else rg_bwd_chunk<K, H, F32, false>(in, k, o, tok0, lw, kc, rm, h0, carry, acc);
+    reinterpret_cast<float2*>(alpha_part)[cw] = make_float2(acc[0] * k[0].dsp8, acc[1] * k[1].dsp8);
+    if (dh0 && c == 0) reinterpret_cast<float2*>(dh0)[(size_t)b * in.W + lw] = make_float2(carry[0], carry[1]);
+}
+
+// ------------------------------------------------------ alpha reduction
+// d alpha = sum over the B*C per-chunk partial rows: rows are split into
+// n_seg contiguous segments, each summed in FP64 in a fixed order (4 row
+// lanes, then lane 0 + 1 + 2 + 3), and the segments are summed in order.
+constexpr int AR_COLS = 64;
+constexpr int AR_LANES = 4;
+
+__global__ __launch_bounds__(AR_COLS * AR_LANES) void rglru_alpha_seg_kernel(
+    int R, int D, int n_seg, const float* __restrict__ part, double* __restrict__ seg) {
+    __shared__ double sh[AR_LANES][AR_COLS];
+    const int cl = threadIdx.x % AR_COLS, rl = threadIdx.x / AR_COLS;
+    const int col = blockIdx.x * AR_COLS + cl;
+    const int s = blockIdx.y;
+    const int r0 = (int)((int64_t)R * s / n_seg), r1 = (int)((int64_t)R * (s + 1) / n_seg);
+    double acc = 0.0;
+    if (col < D) {
+#pragma unroll 4
+        for (int r = r0 + rl; r < r1; r += AR_LANES) acc += (double)part[(size_t)r * D + col];
+    }
+    sh[rl][cl] = acc;
+    __syncthreads();
+    if (rl == 0 && col < D) seg[(size_t)s * D + col] = ((sh[0][cl] + sh[1][cl]) + sh[2][cl]) + sh[3][cl];
+}
+
+constexpr int AF_THREADS = 64;
+
+__global__ __launch_bounds__(AF_THREADS) void rglru_alpha_final_kernel(int D, int n_seg,
+                                                                       const double* __restrict__ seg,
+                                                                       float* __restrict__ dalpha) {
+    const int d = blockIdx.x * AF_THREADS + threadIdx.x;
     if (d >= D) return;
     double s = 0.0;
-    for (int i = 0; i < nchunks; ++i) s += part[(size_t)i * D + d];
+#pragma unroll 16
+    for (int i = 0; i < n_seg; ++i) s += seg[(size_t)i * D + d];
     dalpha[d] = (float)s;
 }
 
 inline dim3 rg_grid(int D, const Chunking& ch) {
-    return dim3((unsigned)ceil_div(ceil_div(D, RG_VM), RG_THREADS), ch.C, ch.B);
+    return dim3((unsigned)ceil_div(D, RG_CH), ch.C, ch.B);
+}
+
+inline RgIn rg_in(const RglruParams& p) {
+    return RgIn{p.L, p.D / 2, (const uint32_t*)p.x, (const uint32_t*)p.lx, (const uint32_t*)p.la, p.reset};
 }
 
 }  // namespace
 
+int rglru_alpha_segments(int B, int C) { return (int)std::min<int64_t>(64, (int64_t)B * C); }
+
 hipError_t launch_rglru_summary(const RglruParams& p, const Chunking& ch, float* summ, hipStream_t s) {
     const dim3 grid = rg_grid(p.D, ch);
-#define RG_SUM(KK)                                                                                  \
-    LRS_LAUNCH(K_RGLRU_SUMMARY, rglru_summary_kernel<KK>, grid, dim3(RG_THREADS), 0, s, p.L, p.D, \
-               ch.C, (const uint32_t*)p.x, (const uint32_t*)p.lx, (const uint32_t*)p.la, p.alpha,  \
-               p.reset, summ)
-    if (ch.K == 32) RG_SUM(32); else RG_SUM(16);
-#undef RG_SUM
+    const RgIn in = rg_in(p);
+    if (ch.K == 32)
+        LRS_LAUNCH(K_RGLRU_SUMMARY, rglru_summary_kernel<32>, grid, dim3(RG_THREADS), 0, s, in, ch.C, p.alpha, summ);
+    else
+        LRS_LAUNCH(K_RGLRU_SUMMARY, rglru_summary_kernel<16>, grid, dim3(RG_THREADS), 0, s, in, ch.C, p.alpha, summ);
     return hipGetLastError();
 }
 
 hipError_t launch_rglru_replay(const RglruParams& p, const Chunking& ch, const float* entries, void* y,
                                int y_f32, float* h_final, hipStream_t s) {
     const dim3 grid = rg_grid(p.D, ch);
-#define RG_REP(KK, FF)                                                                                 \
-    LRS_LAUNCH(K_RGLRU_REPLAY, (rglru_replay_kernel<KK, FF>), grid, dim3(RG_THREADS), 0, s, p.L, p.D, \
-               ch.C, (const uint32_t*)p.x, (const uint32_t*)p.lx, (const uint32_t*)p.la, p.alpha,     \
-               p.reset, entries, y, h_final)
+    const RgIn in = rg_in(p);
+#define RG_REP(KK, FF)                                                                                  \
+    LRS_LAUNCH(K_RGLRU_REPLAY, (rglru_replay_kernel<KK, FF>), grid, dim3(RG_THREADS), 0, s, in, ch.C, \
+               p.alpha, entries, y, h_final)
     if (ch.K == 32) { if (y_f32) RG_REP(32, true); else RG_REP(32, false); }
     else { if (y_f32) RG_REP(16, true); else RG_REP(16, false); }
 #undef RG_REP
@@ -349,11 +489,13 @@ hipError_t launch_rglru_replay(const RglruParams& p, const Chunking& ch, const f
 hipError_t launch_rglru_rev_summary(const RglruParams& p, const Chunking& ch, const void* dy,
                                     float* summ, hipStream_t s) {
     const dim3 grid = rg_grid(p.D, ch);
-#define RG_RSUM(KK)                                                                                   \
-    LRS_LAUNCH(K_RGLRU_REV_SUMMARY, rglru_rev_summary_kernel<KK>, grid, dim3(RG_THREADS), 0, s, p.L, \
-               p.D, ch.C, (const uint32_t*)p.la, p.alpha, p.reset, (const uint32_t*)dy, summ)
-    if (ch.K == 32) RG_RSUM(32); else RG_RSUM(16);
-#undef RG_RSUM
+    const RgIn in = rg_in(p);
+    if (ch.K == 32)
+        LRS_LAUNCH(K_RGLRU_REV_SUMMARY, rglru_rev_summary_kernel<32>, grid, dim3(RG_THREADS), 0, s, in, ch.C,
+                   p.alpha, (const uint32_t*)dy, summ);
+    else
+        LRS_LAUNCH(K_RGLRU_REV_SUMMARY, rglru_rev_summary_kernel<16>, grid, dim3(RG_THREADS), 0, s, in, ch.C,
+                   p.alpha, (const uint32_t*)dy, summ);
     return hipGetLastError();
 }
 
@@ -361,11 +503,11 @@ hipError_t launch_rglru_bwd_replay(const RglruParams& p, const Chunking& ch, con
                                    const float* carry_in, const void* dy, void* dx, void* dlx, void* dla,
                                    int g_f32, float* dh0, float* alpha_part, hipStream_t s) {
     const dim3 grid = rg_grid(p.D, ch);
-#define RG_BWD(KK, FF)                                                                                \
-    LRS_LAUNCH(K_RGLRU_BWD_REPLAY, (rglru_bwd_replay_kernel<KK, FF>), grid, dim3(RG_THREADS), 0, s,  \
-               p.L, p.D, ch.C, (const uint32_t*)p.x, (const uint32_t*)p.lx, (const uint32_t*)p.la,   \
-               p.alpha, p.reset, entries, carry_in, (const uint32_t*)dy, dx, dlx, dla, dh0,          \
-               alpha_part)
+    const RgIn in = rg_in(p);
+    const RgBwdOut o{(const uint32_t*)dy, dx, dlx, dla};
+#define RG_BWD(KK, FF)                                                                                  \
+    LRS_LAUNCH(K_RGLRU_BWD_REPLAY, (rglru_bwd_replay_kernel<KK, 16, FF>), grid, dim3(RG_THREADS), 0, s, \
+               in, ch.C, p.alpha, entries, carry_in, o, dh0, alpha_part)
     if (ch.K == 32) { if (g_f32) RG_BWD(32, true); else RG_BWD(32, false); }
     else { if (g_f32) RG_BWD(16, true); else RG_BWD(16, false); }
 #undef RG_BWD
@@ -373,9 +515,13 @@ hipError_t launch_rglru_bwd_replay(const RglruParams& p, const Chunking& ch, con
 }
 
 hipError_t launch_rglru_alpha_reduce(const RglruParams& p, const Chunking& ch, const float* alpha_part,
-                                     float* dalpha, hipStream_t s) {
-    LRS_LAUNCH(K_RGLRU_ALPHA_REDUCE, rglru_alpha_reduce_kernel, dim3((unsigned)ceil_div(p.D, 256)),
-               dim3(256), 0, s, p.D, ch.B * ch.C, alpha_part, dalpha);
+                                     double* seg, int n_seg, float* dalpha, hipStream_t s) {
+    LRS_LAUNCH(K_RGLRU_ALPHA_REDUCE, rglru_alpha_seg_kernel,
+               dim3((unsigned)ceil_div(p.D, AR_COLS), (unsigned)n_seg), dim3(AR_COLS * AR_LANES), 0, s,
+               ch.B * ch.C, p.D, n_seg, alpha_part, seg);
+    LRS_LAUNCH(K_RGLRU_ALPHA_FINAL, rglru_alpha_final_kernel, dim3((unsigned)ceil_div(p.D, AF_THREADS)),
+               dim3(AF_THREADS), 0,
+               s, p.D, n_seg, (const double*)seg, dalpha);
     return hipGetLastError();
 }
 

@@ -52,10 +52,11 @@ def test_saved_and_workspace_sizes():
     # p, r, (u_phi, u_r), per-token (E, C, S) record, mode table, chunk entry states
     need = B * L * (4 + 4 + 8 + 16) + M * 32 + B * C * M * 8
     assert need <= sv < need + 8 * 256
-    # forward workspace: chunk summaries and group summaries (16 B per mode each)
+    # forward workspace: chunk summaries and group summaries (16 B per mode
+    # each), group entry states (8 B per mode)
     G = 4
     NG = C // G
-    need = B * C * M * 16 + B * NG * M * 16
+    need = B * C * M * 16 + B * NG * M * 24
     assert need <= scan.samu_scan_workspace_bytes(B, L, D, K, G, False) < need + 4 * 256
     # backward adds the per-tile controller partials [B, M/64 tiles, L, 2]
     assert scan.samu_scan_workspace_bytes(B, L, D, K, G, True) > B * (M // 64) * L * 8
