@@ -29,6 +29,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// ------------------------------------------------------- output streams ---
+// Stores of the large [B, L, *] outputs (y, db, dx, ...), which no later
+// kernel of the same pass reads.  With LRS_STREAM_NT they carry the
+// non-temporal hint, so they do not settle in the memory-side cache as dirty
+// lines that a later kernel's reads must first write back.
+#ifndef LRS_STREAM_NT
+#define LRS_STREAM_NT 1
+#endif
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <class T, bool NT = (LRS_STREAM_NT != 0)>
+__device__ __forceinline__ void out_store(void* p, T v) {
+    if (NT) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+    else *reinterpret_cast<T*>(p) = v;
+}
+__device__ __forceinline__ void out_u32(void* p, uint32_t a) { out_store<uint32_t>(p, a); }
+__device__ __forceinline__ void out_u32x2(void* p, uint32_t a, uint32_t b) { out_store<u32x2_t>(p, u32x2_t{a, b}); }
+__device__ __forceinline__ void out_u32x4(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    out_store<u32x4_t>(p, u32x4_t{a, b, c, d});
+}
+__device__ __forceinline__ void out_f32x2(void* p, float a, float b) { out_store<f32x2_t>(p, f32x2_t{a, b}); }
+__device__ __forceinline__ void out_f32x4(void* p, float a, float b, float c, float d) {
+    out_store<f32x4_t>(p, f32x4_t{a, b, c, d});
+}
+
 // -------------------------------------------------------------- complex ---
 struct cf { float re, im; };
 

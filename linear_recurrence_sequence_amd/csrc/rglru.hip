@@ -189,8 +189,8 @@ __device__ __forceinline__ void rg_replay_chunk(const RgIn& in, const ChanConst 
                 h[v] = fmaf(g.a, h[v], xv[v] * g.gx * g.m);
             }
             const size_t row = (tok0 + i) * (size_t)in.W;
-            if (F32) (reinterpret_cast<float2*>(y) + row)[lw] = make_float2(h[0], h[1]);
-            else (reinterpret_cast<uint32_t*>(y) + row)[lw] = pack_bf16x2(h[0], h[1]);
+            if (F32) out_f32x2(reinterpret_cast<float2*>(y) + row + lw, h[0], h[1]);
+            else out_u32(reinterpret_cast<uint32_t*>(y) + row + lw, pack_bf16x2(h[0], h[1]));
         }
     }
 }
@@ -337,13 +337,13 @@ __device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[
             }
             const size_t row = (tok0 + i) * (size_t)in.W;
             if (F32) {
-                (reinterpret_cast<float2*>(o.dx) + row)[lw] = make_float2(ox[0], ox[1]);
-                (reinterpret_cast<float2*>(o.dlx) + row)[lw] = make_float2(olx[0], olx[1]);
-                (reinterpret_cast<float2*>(o.dla) + row)[lw] = make_float2(ola[0], ola[1]);
+                out_f32x2(reinterpret_cast<float2*>(o.dx) + row + lw, ox[0], ox[1]);
+                out_f32x2(reinterpret_cast<float2*>(o.dlx) + row + lw, olx[0], olx[1]);
+                out_f32x2(reinterpret_cast<float2*>(o.dla) + row + lw, ola[0], ola[1]);
             } else {
-                (reinterpret_cast<uint32_t*>(o.dx) + row)[lw] = pack_bf16x2(ox[0], ox[1]);
-                (reinterpret_cast<uint32_t*>(o.dlx) + row)[lw] = pack_bf16x2(olx[0], olx[1]);
-                (reinterpret_cast<uint32_t*>(o.dla) + row)[lw] = pack_bf16x2(ola[0], ola[1]);
+                out_u32(reinterpret_cast<uint32_t*>(o.dx) + row + lw, pack_bf16x2(ox[0], ox[1]));
+                out_u32(reinterpret_cast<uint32_t*>(o.dlx) + row + lw, pack_bf16x2(olx[0], olx[1]));
+                out_u32(reinterpret_cast<uint32_t*>(o.dla) + row + lw, pack_bf16x2(ola[0], ola[1]));
             }
         }
     }

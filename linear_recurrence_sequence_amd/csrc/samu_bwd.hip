@@ -35,7 +35,7 @@ namespace {
 // both ways), one sub-chunk at a time.
 constexpr int BWD_THREADS = 256;
 #ifndef LRS_BWD_SUB
-#define LRS_BWD_SUB 8
+#define LRS_BWD_SUB 16
 #endif
 
 // One chunk of the backward replay; FULL = the chunk has all K tokens (only
@@ -113,8 +113,8 @@ __device__ __forceinline__ void bwd_chunk(
                 const float E = sctl[i0 + j].E;
                 const cf gg = {bf16_lo(gw[i0 + j]) + carry.re, bf16_hi(gw[i0 + j]) + carry.im};
                 if (active) {
-                    if (F32) (reinterpret_cast<float2*>(db) + rowj)[mm] = make_float2(gg.re, gg.im);
-                    else (reinterpret_cast<uint32_t*>(db) + rowj)[mm] = pack_bf16x2(gg.re, gg.im);
+                    if (F32) out_f32x2(reinterpret_cast<float2*>(db) + rowj + mm, gg.re, gg.im);
+                    else out_u32(reinterpret_cast<uint32_t*>(db) + rowj + mm, pack_bf16x2(gg.re, gg.im));
                 }
                 // gamma = g conj(w)
                 const float gre = fmaf(gg.re, wz[j].re, gg.im * wz[j].im);
@@ -193,6 +193,13 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(3, 
 //   column D+1   sum d-bar p, sum c-bar q       (amplitude gradients)
 //   column D+2   sum u-bar u  with u = x~ . w^  (= w^ . g, for the projection)
 constexpr int CTL_TB = 64;
+// dx_sel stores carry the non-temporal hint like the other output streams
+// (measured: a plain store makes this kernel faster but the pass slower, as
+// the next kernel then writes the dirty lines back)
+#ifndef LRS_DX_NT
+#define LRS_DX_NT 1
+#endif
+constexpr bool DX_NT = LRS_DX_NT != 0;
 
 template <bool F32>
 __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
@@ -311,12 +318,12 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
                 }
                 if (F32) {
                     float4* q = reinterpret_cast<float4*>(dx) + (tok * D8 + j8) * 2;
-                    q[0] = make_float4(o[0], o[1], o[2], o[3]);
-                    q[1] = make_float4(o[4], o[5], o[6], o[7]);
+                    out_store<f32x4_t, DX_NT>(q, f32x4_t{o[0], o[1], o[2], o[3]});
+                    out_store<f32x4_t, DX_NT>(q + 1, f32x4_t{o[4], o[5], o[6], o[7]});
                 } else {
-                    reinterpret_cast<uint4*>(dx)[tok * D8 + j8] =
-                        make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                   pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+                    out_store<u32x4_t, DX_NT>(reinterpret_cast<uint4*>(dx) + tok * D8 + j8,
+                                              u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                      pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])});
                 }
             }
         }
@@ -451,7 +458,7 @@ hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const
                p.L, p.M, ch.C, n_tiles, (const TokenCtl*)ctl, (const uint32_t*)p.b,                   \
                (const float4*)mtab, (const float2*)entries, (const float2*)carry_in,                  \
                (const uint32_t*)dy, db, (float2*)dz0, tok_part, (float2*)mode_part)
-    constexpr int H32 = LRS_BWD_SUB, H16 = LRS_BWD_SUB < 16 ? LRS_BWD_SUB : 8;
+    constexpr int H32 = LRS_BWD_SUB, H16 = LRS_BWD_SUB < 16 ? LRS_BWD_SUB : 16;
     if (ch.K == 32) {
         if (db_f32) BWD_CASE(32, H32, true); else BWD_CASE(32, H32, false);
     } else {

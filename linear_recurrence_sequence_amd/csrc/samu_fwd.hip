@@ -152,10 +152,10 @@ template <> struct Words<4> {
 };
 
 #ifndef LRS_SUM_VM
-#define LRS_SUM_VM 2
+#define LRS_SUM_VM 1
 #endif
 #ifndef LRS_REP_VM
-#define LRS_REP_VM 2
+#define LRS_REP_VM 1
 #endif
 constexpr int SUM_VM = LRS_SUM_VM;
 constexpr int REP_VM = LRS_REP_VM;
@@ -256,24 +256,24 @@ __device__ __forceinline__ void store_states(void* y, size_t row, int off, const
     if (F32) {
         float2* o = reinterpret_cast<float2*>(y) + row + off;
         if (VM == 4) {
-            reinterpret_cast<float4*>(o)[0] = make_float4(z[0].re, z[0].im, z[1].re, z[1].im);
-            reinterpret_cast<float4*>(o)[1] = make_float4(z[2].re, z[2].im, z[3].re, z[3].im);
+            out_f32x4(o, z[0].re, z[0].im, z[1].re, z[1].im);
+            out_f32x4(o + 2, z[2].re, z[2].im, z[3].re, z[3].im);
         } else if (VM == 2) {
-            reinterpret_cast<float4*>(o)[0] = make_float4(z[0].re, z[0].im, z[1].re, z[1].im);
+            out_f32x4(o, z[0].re, z[0].im, z[1].re, z[1].im);
         } else {
 #pragma unroll
-            for (int v = 0; v < VM; ++v) o[v] = make_float2(z[v].re, z[v].im);
+            for (int v = 0; v < VM; ++v) out_f32x2(o + v, z[v].re, z[v].im);
         }
     } else {
         uint32_t* o = reinterpret_cast<uint32_t*>(y) + row + off;
         if (VM == 4) {
-            *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf16x2(z[0].re, z[0].im), pack_bf16x2(z[1].re, z[1].im),
-                                                      pack_bf16x2(z[2].re, z[2].im), pack_bf16x2(z[3].re, z[3].im));
+            out_u32x4(o, pack_bf16x2(z[0].re, z[0].im), pack_bf16x2(z[1].re, z[1].im),
+                      pack_bf16x2(z[2].re, z[2].im), pack_bf16x2(z[3].re, z[3].im));
         } else if (VM == 2) {
-            *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(z[0].re, z[0].im), pack_bf16x2(z[1].re, z[1].im));
+            out_u32x2(o, pack_bf16x2(z[0].re, z[0].im), pack_bf16x2(z[1].re, z[1].im));
         } else {
 #pragma unroll
-            for (int v = 0; v < VM; ++v) o[v] = pack_bf16x2(z[v].re, z[v].im);
+            for (int v = 0; v < VM; ++v) out_u32(o + v, pack_bf16x2(z[v].re, z[v].im));
         }
     }
 }

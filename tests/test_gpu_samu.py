@@ -140,7 +140,7 @@ def test_samu_bitwise_deterministic():
 
 def test_samu_metric_shape_full_parity():
     """The configuration the benchmark times (B=1, L=32768, D=2048, K=32, the
-    default 64-chunk groups, nonzero initial state), checked element by
+    library's default grouping, nonzero initial state), checked element by
     element against the oracle."""
     name, B, L, D, K, G = "metric_b1_l32768_d2048", 1, 32768, 2048, 32, 0
     inp = _inputs(B, L, D, 3002, 0.1)
