@@ -77,9 +77,19 @@ def kernel_bytes(name, B, L, D, K, G):
     return table.get(name)
 
 
+def sources_digest(paths):
+    """First 16 hex digits of the SHA-256 of the given repository files, in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def traffic_record(kernel):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source (else None)."""
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, scaled by a 512 MiB device
+    copy), if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_counters.md")
     if not os.path.exists(path):
         return None
@@ -90,10 +100,10 @@ def traffic_record(kernel):
     rec = json.loads(m.group(1)).get(kernel)
     if not rec:
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src):
-        return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec["source_sha256_16"]:
+    try:
+        if sources_digest(rec["sources"]) != rec["sources_sha256_16"]:
+            return None
+    except OSError:
         return None
     return rec["bytes_per_launch"]
 
@@ -117,24 +127,31 @@ def copy_probe(torch, nbytes=512 << 20, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(sample_L):
-    """The FP64 oracle, as it stands, on the host cores: one forward+backward
-    over the first `sample_L` tokens of the same workload."""
+def cpu_baseline(sample_L, reps=3):
+    """The FP64 oracle, as it stands, on the host cores: forward+backward over
+    the first `sample_L` tokens of the same workload (all of it by default),
+    median wall time of `reps` runs."""
     import oracle
     from linear_recurrence_sequence_amd import inputs
     B, D = WORKLOAD["B"], WORKLOAD["D"]
     inp = inputs.samu_inputs(B, sample_L, D, seed=3002, z0_std=0.1)
-    t0 = time.perf_counter()
-    oracle.samu_fwd(inp["x_sel"], inp["b"], inp["w_phi"], inp["w_r"], inp["a_phi"], inp["a_r"],
-                    inp["nu"], inp["theta"], inp["z0"])
-    oracle.samu_bwd(inp["x_sel"], inp["b"], inp["w_phi"], inp["w_r"], inp["a_phi"], inp["a_r"],
-                    inp["nu"], inp["theta"], inp["z0"], inp["dy"], None)
-    dt = time.perf_counter() - t0
+    z0 = inp["z0"]
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.samu_fwd(inp["x_sel"], inp["b"], inp["w_phi"], inp["w_r"], inp["a_phi"], inp["a_r"],
+                        inp["nu"], inp["theta"], z0)
+        oracle.samu_bwd(inp["x_sel"], inp["b"], inp["w_phi"], inp["w_r"], inp["a_phi"], inp["a_r"],
+                        inp["nu"], inp["theta"], z0, inp["dy"], None)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     floor = 16.0 * B * sample_L * D
+    whole = sample_L == WORKLOAD["L"]
     return {"value": round(floor / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
             "kind": "oracle", "ms_per_step": round(dt * 1e3, 1),
-            "sample": f"one forward+backward of B={B}, L={sample_L} (of {WORKLOAD['L']}), D={D}; "
-                      f"same seed and distributions; floor bytes / wall time"}
+            "sample": (f"{'the whole workload' if whole else 'a prefix of the workload'}: one "
+                       f"forward+backward of B={B}, L={sample_L} (of {WORKLOAD['L']}), D={D}, same "
+                       f"seed and distributions; floor bytes / median wall time of {reps} runs")}
 
 
 def main():
@@ -142,13 +159,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-L", type=int, default=4096)
+    ap.add_argument("--cpu-sample-L", type=int, default=WORKLOAD["L"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rglru", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the scan library has no multi-GPU path "
+              "(no collectives, no sequence or mode sharding); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

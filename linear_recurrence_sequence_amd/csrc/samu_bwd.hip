@@ -23,7 +23,7 @@
 namespace lrs {
 namespace {
 
-// ------------------------------------------------------------------ K7 ---
+// ------------------------------------------------------ backward replay ---
 // One lane per mode, one workgroup per (chunk, 256 modes).  The chunk is
 // handled as K/H sub-chunks of H tokens, last one first: a forward pass from
 // the chunk's saved entry state leaves the state entering every sub-chunk in
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(3, 
     }
 }
 
-// ------------------------------------------------------------------ K9 ---
+// -------------------------------------------------- controller backward ---
 // One workgroup per block of CTL_TB tokens; threads own 8 selector columns at
 // a time.  The second stage of the shared-control reduction (over the mode
 // tiles, fixed order) happens here, then p-bar, r-bar and the per-token u-bar
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
     }
 }
 
-// ----------------------------------------------------------------- K10 ---
+// ------------------------------------------------ parameter reductions ---
 // Level 1 of the parameter reductions, FP64 and fixed order, one thread per
 // column (or mode) and segment:
 //   blocks x in [0, col_tiles): columns of g_part over a segment of token blocks

@@ -18,14 +18,15 @@
 // Layout: lanes run over modes (VM consecutive modes per lane, so one BF16
 // complex drive word per mode and one 4*VM-byte load per token); a workgroup
 // owns one chunk of one batch row and a slice of the modes, so every wave
-// streams contiguous rows of the [B, L, M, 2] tensors.  Token controls are
-// wave-uniform and arrive through the scalar cache.
+// streams contiguous rows of the [B, L, M, 2] tensors.  The chunk's token
+// controls (one 16-byte (E, C, S) record per token) are staged in LDS and
+// read back as wave-uniform broadcasts.
 #include "common.hpp"
 
 namespace lrs {
 namespace {
 
-// ------------------------------------------------------------------ K1 ---
+// ----------------------------------------------------------- controller ---
 // One wave per CTL_TOK tokens: every lane loads 16 bytes (8 selector values)
 // of each token row per 512-column slab, the wave reduces the two dot products
 // and lanes 0..CTL_TOK-1 finish one token each.  The grid also writes the
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     }
 }
 
-// ---------------------------------------------------------- K2 / K5 ---
+// ----------------------------------------- chunk and reverse summaries ---
 template <int VM> struct Words;
 // VM packed BF16 complex words of one lane; `row` is wave-uniform and `off`
 // the lane's 32-bit word offset, so the load takes the scalar-base form.
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         summary_chunk<VM, K, REV, false>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, summ);
 }
 
-// ------------------------------------------------------------------ K4 ---
+// --------------------------------------------------------------- replay ---
 // y row `row` (wave-uniform element index of the row start) at the lane's
 // offset `off`, as VM complex values.
 template <int VM, bool F32>
