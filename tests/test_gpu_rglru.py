@@ -102,3 +102,37 @@ def test_rglru_packed_full_size_parity():
     name = "packed_b4_l8192_d2560"
     inp = inputs.rglru_inputs(4, 8192, 2560, 4000, reset_p=1.0 / 512, h0_std=0.1)
     _check(name, inp, 16, 0, bf16=False)
+
+
+# The pages' other full-size RG-LRU workloads (no segment starts): the long
+# sequence at D=1024 and the widest state at L=32768 with an initial state.
+FULL_CASES = [
+    ("long_b1_l131072_d1024", 1, 131072, 1024, None, 2102),
+    ("wide_b1_l32768_d2560", 1, 32768, 2560, 0.1, 3103),
+]
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=[c[0] for c in FULL_CASES])
+def test_rglru_full_size_parity(case):
+    name, B, L, D, std, seed = case
+    inp = inputs.rglru_inputs(B, L, D, seed, h0_std=std)
+    _check(name, inp, 16, 0, bf16=False)
+
+
+@pytest.mark.parametrize("L", [2048, 16384])
+def test_rglru_forward_sweep_parity(L):
+    """Forward-only latency sweep workload: B=8, D=1024, no resets, zero
+    initial state."""
+    B, D, K = 8, 1024, 16
+    inp = inputs.rglru_inputs(B, L, D, 1100 + L // 2048, with_dy=False)
+    say(f"[rglru parity] sweep_b8_l{L}_d1024: oracle forward")
+    rf = oracle.rglru_fwd(inp["x"], inp["lx"], inp["la"], inp["alpha"], None, None)
+    d = {k: dev_tensor(v) for k, v in inp.items()}
+    from linear_recurrence_sequence_amd import scan
+    say(f"[rglru parity] sweep_b8_l{L}_d1024: rglru_scan_fwd f32")
+    y, hf, _ = scan.rglru_scan_fwd(d["x"], d["lx"], d["la"], d["alpha"], None, None, K=K, G=0,
+                                   y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ey, eh = rel_l2(to_f64(y), rf["y"]), rel_l2(to_f64(hf), rf["h_final"])
+    say(f"   errors: y {ey:.2e} h_final {eh:.2e}")
+    assert ey <= TOL_OUT and eh <= TOL_OUT

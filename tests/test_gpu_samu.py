@@ -138,21 +138,64 @@ def test_samu_bitwise_deterministic():
             assert torch.equal(a[2][k], b[2][k]), k
 
 
-def test_samu_metric_shape_full_parity():
-    """The configuration the benchmark times (B=1, L=32768, D=2048, K=32, the
-    library's default grouping, nonzero initial state), checked element by
-    element against the oracle."""
-    name, B, L, D, K, G = "metric_b1_l32768_d2048", 1, 32768, 2048, 32, 0
-    inp = _inputs(B, L, D, 3002, 0.1)
-    say(f"[samu parity] {name}: oracle forward+backward (tens of seconds)")
+def _check_full(name, B, L, D, K, G, state_std, seed):
+    inp = _inputs(B, L, D, seed, state_std)
+    say(f"[samu parity] {name}: B={B} L={L} D={D} K={K} G={G} seed={seed} -> oracle forward+backward")
     rf, rg = _oracle(inp)
     say(f"[samu parity] {name}: samu_scan_fwd/bwd f32")
     y, zf, g = _gpu(inp, K, G, torch.float32)
     errs = {"y": rel_l2(to_f64(y), rf["y"]), "z_final": rel_l2(to_f64(zf), rf["z_final"])}
-    for k in ("dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta", "dz0"):
+    keys = ["dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta"] + (["dz0"] if state_std else [])
+    for k in keys:
         errs[k] = rel_l2(to_f64(g[k]), rg[k])
+    for k in ("da_phi", "da_r"):
+        errs[k] = abs(float(g[k].item()) - rg[k]) / max(abs(rg[k]), 1e-30)
     say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
     for k in ("y", "z_final"):
         assert errs[k] <= TOL_OUT, (k, errs[k])
-    for k in ("dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta", "dz0"):
+    for k in keys + ["da_phi", "da_r"]:
         assert errs[k] <= TOL_GRAD, (k, errs[k])
+
+
+def test_samu_metric_shape_full_parity():
+    """The configuration the benchmark times (B=1, L=32768, D=2048, K=32, the
+    library's default grouping, nonzero initial state), checked element by
+    element against the oracle."""
+    _check_full("metric_b1_l32768_d2048", 1, 32768, 2048, 32, 0, 0.1, 3002)
+
+
+# The pages' other full-size F+B workloads: long sequences at D=1024 with
+# 64-chunk groups and a zero initial state; wide states at L=32768 with a
+# nonzero initial state and its gradient.
+FULL_CASES = [
+    ("long_b1_l65536_d1024", 1, 65536, 1024, 32, 64, None, 2001),
+    ("long_b1_l131072_d1024", 1, 131072, 1024, 32, 64, None, 2002),
+    ("wide_b1_l32768_d1024", 1, 32768, 1024, 32, 0, 0.1, 3000),
+    ("wide_b1_l32768_d1536", 1, 32768, 1536, 32, 0, 0.1, 3001),
+    ("wide_b1_l32768_d2560", 1, 32768, 2560, 32, 0, 0.1, 3003),
+]
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=[c[0] for c in FULL_CASES])
+def test_samu_full_size_parity(case):
+    _check_full(*case)
+
+
+@pytest.mark.parametrize("L", [2048, 16384])
+def test_samu_forward_sweep_parity(L):
+    """Forward-only latency sweep workload: B=8, D=1024 (shortest and longest
+    lengths of the sweep), zero initial state."""
+    B, D, K = 8, 1024, 32
+    inp = inputs.samu_inputs(B, L, D, 1000 + L // 2048, with_dy=False)
+    say(f"[samu parity] sweep_b8_l{L}_d1024: oracle forward")
+    rf = oracle.samu_fwd(inp["x_sel"], inp["b"], inp["w_phi"], inp["w_r"], inp["a_phi"],
+                         inp["a_r"], inp["nu"], inp["theta"], None)
+    d = {k: dev_tensor(v) for k, v in inp.items()}
+    from linear_recurrence_sequence_amd import scan
+    say(f"[samu parity] sweep_b8_l{L}_d1024: samu_scan_fwd f32")
+    y, zf, _ = scan.samu_scan_fwd(d["x_sel"], d["b"], d["w_phi"], d["w_r"], d["a_phi"], d["a_r"],
+                                  d["nu"], d["theta"], None, K=K, G=0, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ey, ez = rel_l2(to_f64(y), rf["y"]), rel_l2(to_f64(zf), rf["z_final"])
+    say(f"   errors: y {ey:.2e} z_final {ez:.2e}")
+    assert ey <= TOL_OUT and ez <= TOL_OUT
