@@ -201,20 +201,50 @@ constexpr int CTL_TB = 64;
 #endif
 constexpr bool DX_NT = LRS_DX_NT != 0;
 
+// Threads: CT column threads (16-byte column groups) x TS token splits of the
+// block's CTL_TB tokens; the TS partial sums of u-bar * x~ of a column group
+// are added in split order through LDS, so the result is fixed for a given D.
+constexpr int CTL_TOKB = 16;  // tokens whose selector words are loaded together
+
 template <bool F32>
-__global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
-    int B, int L, int D, int M, int n_tiles, const uint4* __restrict__ x_sel,
+__device__ __forceinline__ void ctl_load_batch(uint4 (&xv)[CTL_TOKB], const uint4* __restrict__ x_sel,
+                                               size_t tok0, int D8, int j8, bool act, int nt) {
+    if (act && nt == CTL_TOKB) {
+#pragma unroll
+        for (int t = 0; t < CTL_TOKB; ++t) xv[t] = x_sel[(tok0 + t) * D8 + j8];
+    } else {
+#pragma unroll
+        for (int t = 0; t < CTL_TOKB; ++t)
+            xv[t] = (act && t < nt) ? x_sel[(tok0 + t) * D8 + j8] : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <bool F32>
+__global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
+    int B, int L, int D, int M, int n_tiles, int TS, const uint4* __restrict__ x_sel,
     const float* __restrict__ w_phi, const float* __restrict__ w_r,
     const float* __restrict__ a_phi, const float* __restrict__ a_r,
     const float* __restrict__ p_sv, const float* __restrict__ r_sv,
     const float2* __restrict__ u_sv, const float* __restrict__ tok_part, void* __restrict__ dx,
     float* __restrict__ g_part) {
+    extern __shared__ float4 comb[];  // [(TS - 1) * CT][4]
     __shared__ float u_sh[2][CTL_TB];
-    __shared__ float red[2][8];
+    __shared__ float red[2][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int BL = B * L;
     const int blk = blockIdx.x;
     const int ncol = D + 4;
+    const int D8 = D >> 3;
+    const int CT = blockDim.x / TS;
+    const int ts = tid / CT, cj = tid - ts * CT;
+    const int ntok = min(CTL_TB, BL - blk * CTL_TB);
+    const int tper = CTL_TB / TS;
+    const int tlo = ts * tper, thi = min(tlo + tper, ntok);
+    const size_t tokb = (size_t)blk * CTL_TB;
+
+    // the first selector batch does not depend on u-bar: request it now
+    uint4 xv[CTL_TOKB];
+    ctl_load_batch<F32>(xv, x_sel, tokb + tlo, D8, cj, cj < D8, max(0, min(CTL_TOKB, thi - tlo)));
 
     // direction norms
     float sp = 0.f, sr = 0.f;
@@ -225,12 +255,6 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
     sp = wave_sum(sp);
     sr = wave_sum(sr);
     if (lane == 0) { red[0][wave] = sp; red[1][wave] = sr; }
-    __syncthreads();
-    float np = 0.f, nr = 0.f;
-    for (int i = 0; i < nw; ++i) { np += red[0][i]; nr += red[1][i]; }
-    const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
-    const float sM = sqrtf((float)M);
-    const float th_phi = tanhf(a_phi[0]), th_r = tanhf(a_r[0]);
 
     // per-token u-bar (the first wave: CTL_TB == 64 tokens)
     if (tid < CTL_TB) {
@@ -238,9 +262,23 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
         float uphi = 0.f, ur = 0.f, sdp = 0.f, scq = 0.f, sup = 0.f, sur = 0.f;
         if (tok < BL) {
             const int bb = tok / L, l = tok - bb * L;
+            // second stage of the shared-control reduction: tiles in order,
+            // their partials requested 8 at a time
+            const float2* tp = reinterpret_cast<const float2*>(tok_part) + (size_t)bb * n_tiles * L + l;
             float cb = 0.f, dbr = 0.f;
-            for (int t = 0; t < n_tiles; ++t) {
-                const float2 v = reinterpret_cast<const float2*>(tok_part)[((size_t)bb * n_tiles + t) * L + l];
+            int t = 0;
+            for (; t + 8 <= n_tiles; t += 8) {
+                float2 v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = tp[(size_t)(t + i) * L];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    cb += v[i].x;
+                    dbr += v[i].y;
+                }
+            }
+            for (; t < n_tiles; ++t) {
+                const float2 v = tp[(size_t)t * L];
                 cb += v.x;
                 dbr += v.y;
             }
@@ -248,8 +286,9 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
             const float2 u = u_sv[tok];
             const float r2 = r * r;
             const float q = r / (1.0f + r2);
-            const float pbar = dbr * th_phi / sM;
-            const float rbar = cb * th_r / sM * (1.0f - r2) / ((1.0f + r2) * (1.0f + r2));
+            const float sM = sqrtf((float)M);
+            const float pbar = dbr * tanhf(a_phi[0]) / sM;
+            const float rbar = cb * tanhf(a_r[0]) / sM * (1.0f - r2) / ((1.0f + r2) * (1.0f + r2));
             uphi = pbar * (1.0f - p * p);
             ur = rbar * (1.0f - r2);
             sdp = dbr * p;
@@ -268,12 +307,17 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
         }
     }
     __syncthreads();
+    float np = 0.f, nr = 0.f;
+    for (int i = 0; i < nw; ++i) { np += red[0][i]; nr += red[1][i]; }
+    const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
 
-    const int D8 = D >> 3;
-    const int ntok = min(CTL_TB, BL - blk * CTL_TB);
-    for (int j8 = tid; j8 < D8; j8 += blockDim.x) {  // 16-byte column group
+    for (int jb = 0; jb < D8; jb += CT) {  // uniform trip count: barriers below
+        const int j8 = jb + cj;
+        const bool act = j8 < D8;
         float wp[8], wr[8], gp[8], gr[8];
-        {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { wp[e] = 0.f; wr[e] = 0.f; gp[e] = 0.f; gr[e] = 0.f; }
+        if (act) {
             const float4* a = reinterpret_cast<const float4*>(w_phi) + 2 * j8;
             const float4* c = reinterpret_cast<const float4*>(w_r) + 2 * j8;
             const float4 a0 = a[0], a1 = a[1], c0 = c[0], c1 = c[1];
@@ -283,27 +327,16 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
             for (int e = 0; e < 8; ++e) {
                 wp[e] = av[e] * inv_phi;
                 wr[e] = cv[e] * inv_r;
-                gp[e] = 0.f;
-                gr[e] = 0.f;
             }
         }
-        constexpr int TB = 16;  // tokens whose selector words are loaded together
-        for (int t0 = 0; t0 < ntok; t0 += TB) {
-            uint4 xv[TB];
-            if (t0 + TB <= ntok) {
-#pragma unroll
-                for (int t = 0; t < TB; ++t) xv[t] = x_sel[((size_t)blk * CTL_TB + t0 + t) * D8 + j8];
-            } else {
-#pragma unroll
-                for (int t = 0; t < TB; ++t)
-                    xv[t] = (t0 + t < ntok) ? x_sel[((size_t)blk * CTL_TB + t0 + t) * D8 + j8]
-                                            : make_uint4(0, 0, 0, 0);
-            }
+        for (int t0 = tlo; t0 < thi; t0 += CTL_TOKB) {
+            const int nt = min(CTL_TOKB, thi - t0);
+            if (jb > 0 || t0 > tlo) ctl_load_batch<F32>(xv, x_sel, tokb + t0, D8, j8, act, nt);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < TB; ++t) {
-                if (t0 + t >= ntok) break;
-                const size_t tok = (size_t)blk * CTL_TB + t0 + t;
+            for (int t = 0; t < CTL_TOKB; ++t) {
+                if (t >= nt) continue;  // no early exit: the loop must unroll
+                const size_t tok = tokb + t0 + t;
                 const float uphi = u_sh[0][t0 + t], ur = u_sh[1][t0 + t];
                 const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
                 float xs[8];
@@ -316,20 +349,46 @@ __global__ __launch_bounds__(512) void samu_ctl_bwd_kernel(
                     gp[e] = fmaf(uphi, xs[e], gp[e]);
                     gr[e] = fmaf(ur, xs[e], gr[e]);
                 }
-                if (F32) {
-                    float4* q = reinterpret_cast<float4*>(dx) + (tok * D8 + j8) * 2;
-                    out_store<f32x4_t, DX_NT>(q, f32x4_t{o[0], o[1], o[2], o[3]});
-                    out_store<f32x4_t, DX_NT>(q + 1, f32x4_t{o[4], o[5], o[6], o[7]});
-                } else {
-                    out_store<u32x4_t, DX_NT>(reinterpret_cast<uint4*>(dx) + tok * D8 + j8,
-                                              u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                                      pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])});
+                if (act) {
+                    if (F32) {
+                        float4* q = reinterpret_cast<float4*>(dx) + (tok * D8 + j8) * 2;
+                        out_store<f32x4_t, DX_NT>(q, f32x4_t{o[0], o[1], o[2], o[3]});
+                        out_store<f32x4_t, DX_NT>(q + 1, f32x4_t{o[4], o[5], o[6], o[7]});
+                    } else {
+                        out_store<u32x4_t, DX_NT>(reinterpret_cast<uint4*>(dx) + tok * D8 + j8,
+                                                  u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                          pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])});
+                    }
                 }
             }
         }
-        float4* out = reinterpret_cast<float4*>(g_part + ((size_t)blk * ncol + 8 * j8) * 2);
+        // partial sums of the token splits, added in split order
+        if (TS > 1) {
+            if (act && ts > 0) {
+                float4* c = comb + ((size_t)(ts - 1) * CT + cj) * 4;
+                c[0] = make_float4(gp[0], gp[1], gp[2], gp[3]);
+                c[1] = make_float4(gp[4], gp[5], gp[6], gp[7]);
+                c[2] = make_float4(gr[0], gr[1], gr[2], gr[3]);
+                c[3] = make_float4(gr[4], gr[5], gr[6], gr[7]);
+            }
+            __syncthreads();
+            if (act && ts == 0) {
+                for (int k = 1; k < TS; ++k) {
+                    const float4* c = comb + ((size_t)(k - 1) * CT + cj) * 4;
+                    const float4 c0 = c[0], c1 = c[1], c2 = c[2], c3 = c[3];
+                    gp[0] += c0.x; gp[1] += c0.y; gp[2] += c0.z; gp[3] += c0.w;
+                    gp[4] += c1.x; gp[5] += c1.y; gp[6] += c1.z; gp[7] += c1.w;
+                    gr[0] += c2.x; gr[1] += c2.y; gr[2] += c2.z; gr[3] += c2.w;
+                    gr[4] += c3.x; gr[5] += c3.y; gr[6] += c3.z; gr[7] += c3.w;
+                }
+            }
+            __syncthreads();
+        }
+        if (act && ts == 0) {
+            float4* out = reinterpret_cast<float4*>(g_part + ((size_t)blk * ncol + 8 * j8) * 2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = make_float4(gp[2 * e], gr[2 * e], gp[2 * e + 1], gr[2 * e + 1]);
+            for (int e = 0; e < 4; ++e) out[e] = make_float4(gp[2 * e], gr[2 * e], gp[2 * e + 1], gr[2 * e + 1]);
+        }
     }
 }
 
@@ -431,6 +490,7 @@ __global__ __launch_bounds__(FIN_THREADS) void samu_param_final_kernel(
     dw_r[j] = (float)((gy - ((double)w_r[j] / nrr) * dotr) / nrr);
     if (j == 0) {
         double sdp = 0.0, scq = 0.0;
+#pragma unroll 8
         for (int i = 0; i < n_seg; ++i) {
             const double2 v = g_seg[(size_t)i * ncol + D + 1];
             sdp += v.x;
@@ -473,10 +533,14 @@ hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const flo
                                int dx_f32, float* g_part, hipStream_t s) {
     const int BL = p.B * p.L;
     const int grid = (int)ceil_div(BL, CTL_TB);
-    const int threads = (int)std::min<int64_t>(512, std::max<int64_t>(64, ceil_div(ceil_div(p.D, 8), 64) * 64));
-#define CTLB_CASE(FF)                                                                                 \
-    LRS_LAUNCH(K_SAMU_CTL_BWD, samu_ctl_bwd_kernel<FF>, dim3(grid), dim3(threads), 0, s, p.B, p.L, p.D, \
-               p.M, n_tiles, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p_sv, r_sv,         \
+    // column threads (a multiple of 64, at most 1024) and token splits (1, 2 or 4)
+    const int CT = (int)std::min<int64_t>(1024, ceil_div(p.D / 8, 64) * 64);
+    int TS = 1;
+    while (TS < 4 && CT * TS * 2 <= 1024) TS *= 2;
+    const size_t shmem = (size_t)(TS - 1) * CT * 4 * sizeof(float4);
+#define CTLB_CASE(FF)                                                                                    \
+    LRS_LAUNCH(K_SAMU_CTL_BWD, samu_ctl_bwd_kernel<FF>, dim3(grid), dim3(CT * TS), shmem, s, p.B, p.L, p.D, \
+               p.M, n_tiles, TS, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p_sv, r_sv,        \
                (const float2*)u_sv, tok_part, dx_sel, g_part)
     if (dx_f32) CTLB_CASE(true); else CTLB_CASE(false);
 #undef CTLB_CASE

@@ -35,6 +35,10 @@ constexpr int CTL_WAVES = 8;
 constexpr int CTL_THREADS = 64 * CTL_WAVES;
 constexpr int CTL_TOK = 4;                          // tokens per wave
 constexpr int CTL_TOK_PER_BLOCK = CTL_WAVES * CTL_TOK;
+#ifndef LRS_CTL_SLAB
+#define LRS_CTL_SLAB 1
+#endif
+constexpr int CTL_SLAB = LRS_CTL_SLAB;  // 512-column slabs loaded together
 
 __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     int BL, int D, int M, const uint4* __restrict__ x_sel, const float* __restrict__ w_phi,
@@ -71,32 +75,39 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     float ap[CTL_TOK], ar[CTL_TOK];
 #pragma unroll
     for (int q = 0; q < CTL_TOK; ++q) { ap[q] = 0.f; ar[q] = 0.f; }
-    for (int j = lane; j < D8; j += 64) {
-        uint4 xv[CTL_TOK];
-        if (tok0 + CTL_TOK <= BL) {
+    // CTL_SLAB column slabs of 512 selector columns per iteration, all their
+    // loads issued before the arithmetic
+    for (int j0 = lane; j0 < D8; j0 += 64 * CTL_SLAB) {
+        uint4 xv[CTL_SLAB][CTL_TOK];
 #pragma unroll
-            for (int q = 0; q < CTL_TOK; ++q) xv[q] = x_sel[(size_t)(tok0 + q) * D8 + j];
-        } else {
+        for (int sl = 0; sl < CTL_SLAB; ++sl) {
+            const int j = j0 + 64 * sl;
 #pragma unroll
             for (int q = 0; q < CTL_TOK; ++q)
-                xv[q] = (tok0 + q < BL) ? x_sel[(size_t)(tok0 + q) * D8 + j] : make_uint4(0, 0, 0, 0);
+                xv[sl][q] = (j < D8 && tok0 + q < BL) ? x_sel[(size_t)(tok0 + q) * D8 + j]
+                                                      : make_uint4(0, 0, 0, 0);
         }
-        const float4 wp0 = reinterpret_cast<const float4*>(w_phi)[2 * j];
-        const float4 wp1 = reinterpret_cast<const float4*>(w_phi)[2 * j + 1];
-        const float4 wr0 = reinterpret_cast<const float4*>(w_r)[2 * j];
-        const float4 wr1 = reinterpret_cast<const float4*>(w_r)[2 * j + 1];
-        const float wp[8] = {wp0.x, wp0.y, wp0.z, wp0.w, wp1.x, wp1.y, wp1.z, wp1.w};
-        const float wr[8] = {wr0.x, wr0.y, wr0.z, wr0.w, wr1.x, wr1.y, wr1.z, wr1.w};
 #pragma unroll
-        for (int q = 0; q < CTL_TOK; ++q) {
-            const uint32_t xw[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+        for (int sl = 0; sl < CTL_SLAB; ++sl) {
+            const int j = j0 + 64 * sl;
+            if (j >= D8) break;
+            const float4 wp0 = reinterpret_cast<const float4*>(w_phi)[2 * j];
+            const float4 wp1 = reinterpret_cast<const float4*>(w_phi)[2 * j + 1];
+            const float4 wr0 = reinterpret_cast<const float4*>(w_r)[2 * j];
+            const float4 wr1 = reinterpret_cast<const float4*>(w_r)[2 * j + 1];
+            const float wp[8] = {wp0.x, wp0.y, wp0.z, wp0.w, wp1.x, wp1.y, wp1.z, wp1.w};
+            const float wr[8] = {wr0.x, wr0.y, wr0.z, wr0.w, wr1.x, wr1.y, wr1.z, wr1.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x0 = bf16_lo(xw[e]), x1 = bf16_hi(xw[e]);
-                ap[q] = fmaf(x0, wp[2 * e], ap[q]);
-                ap[q] = fmaf(x1, wp[2 * e + 1], ap[q]);
-                ar[q] = fmaf(x0, wr[2 * e], ar[q]);
-                ar[q] = fmaf(x1, wr[2 * e + 1], ar[q]);
+            for (int q = 0; q < CTL_TOK; ++q) {
+                const uint32_t xw[4] = {xv[sl][q].x, xv[sl][q].y, xv[sl][q].z, xv[sl][q].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = bf16_lo(xw[e]), x1 = bf16_hi(xw[e]);
+                    ap[q] = fmaf(x0, wp[2 * e], ap[q]);
+                    ap[q] = fmaf(x1, wp[2 * e + 1], ap[q]);
+                    ar[q] = fmaf(x0, wr[2 * e], ar[q]);
+                    ar[q] = fmaf(x1, wr[2 * e + 1], ar[q]);
+                }
             }
         }
     }
