@@ -162,6 +162,7 @@ def main():
     ap.add_argument("--cpu-sample-L", type=int, default=WORKLOAD["L"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rglru", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the scan library has no multi-GPU path "
@@ -281,6 +282,31 @@ def main():
               "samu_fb_time_reduction": round((rg_ms - ms) / rg_ms, 4)}
         log(f"[bench] RG-LRU F+B {rg_ms:.4f} ms/step; SAMU reduction {(rg_ms - ms) / rg_ms:.1%}")
 
+    dec = None
+    if not args.no_decode:
+        log("[bench] SAMU decode step (one token, state in place) at D=%d" % D)
+        dec = {}
+        for Bd in (1, 16, 256):
+            di = inputs.samu_inputs(Bd, 1, D, seed=3004, z0_std=0.1, with_dy=False)
+            dd = {k: dev(v) for k, v in di.items()}
+            xs, bs, z = dd["x_sel"][:, 0].contiguous(), dd["b"][:, 0].contiguous(), dd["z0"]
+            yd = torch.empty((Bd, M, 2), dtype=torch.bfloat16, device=dev_)
+
+            def dec_step():
+                scan.samu_scan_decode(xs, bs, d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"],
+                                      d["theta"], z, y=yd, z_out=z)
+
+            n = 200
+            dms, _ = timed(dec_step, n, 10, False)
+            _, dprof = timed(dec_step, n, 1, True)
+            kus = dprof["samu_decode"][0] / dprof["samu_decode"][1] * 1e3
+            # x_sel, b, state in and out, y, both directions, nu and theta
+            nbytes = Bd * (2 * D + 4 * M + 16 * M + 4 * M) + 8 * (D + 1) + 8 * M
+            dec[f"B{Bd}"] = {"us_per_step": round(dms * 1e3, 2), "kernel_us": round(kus, 2),
+                             "bytes_per_step": nbytes,
+                             "kernel_gbs": round(nbytes / (kus * 1e-6) / 1e9, 1)}
+            log(f"    B={Bd}: {dms * 1e3:.2f} us/step ({kus:.2f} us kernel, {nbytes} B)")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle F+B over L={args.cpu_sample_L}")
@@ -313,6 +339,7 @@ def main():
         "copy_probe_gbs": round(copy_gbs, 1),
         "kernels": kernels,
         "rglru": rg,
+        "decode": dec,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -144,6 +144,27 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G,
                           float* dnu, float* dtheta,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* One generation step for B sequences in a single launch (page "Griffin 第
+ * 4、5 节 H800 对照协议", "SAMU 的固定方程": control projection, transition
+ * rebuild, FP32 state update and BF16 output in one kernel; equations of
+ * page "SAMU 与 RG-LRU 的 H800 训练性能对比", section 05, at one token):
+ *   z_out = lambda(x_sel) z_in + b,  y = z_out.
+ *   x_sel   bf16 [B, D]            selector of the new token
+ *   b       bf16 [B, M, 2]         complex drive of the new token
+ *   w_phi, w_r, a_phi, a_r, nu, theta  as for samu_scan_fwd
+ *   z_in    f32 [B, M, 2] or NULL  state before the token (NULL = 0)
+ *   z_out   f32 [B, M, 2]          state after the token; may equal z_in
+ *                                  (updated in place), must not overlap it
+ *                                  otherwise
+ *   y       [B, M, 2] of y_dtype   output of the token
+ * Needs 1 <= B <= 65535 and D as for samu_scan_fwd; allocates nothing. */
+scan_status samu_scan_decode(int B, int D, const void* x_sel, const void* b,
+                             const float* w_phi, const float* w_r,
+                             const float* a_phi, const float* a_r,
+                             const float* nu, const float* theta,
+                             const float* z_in, float* z_out, void* y, int y_dtype,
+                             void* stream);
+
 /* ======================================================================
  * RG-LRU scan (page "SAMU 与 RG-LRU 的 H800 训练性能对比", section 04; reset
  * semantics also page "Griffin 第 4、5 节 H800 对照协议", "RG-LRU 的固定方程").

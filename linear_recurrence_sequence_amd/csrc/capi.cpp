@@ -51,7 +51,7 @@ static const char* const kKernelNames[K_NUM_KERNELS] = {
     "prefix_chunk_entries", "samu_replay", "samu_reverse_summary", "samu_bwd_replay",
     "samu_controller_bwd", "samu_param_reduce", "samu_param_final", "rglru_chunk_summary",
     "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha_reduce",
-    "rglru_alpha_final"};
+    "rglru_alpha_final", "samu_decode"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 
@@ -406,6 +406,38 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     LRS_TRY(launch_samu_param_final(p, ws.g_seg, ws.mode_seg, ws.n_seg, dw_phi, dw_r, da_phi, da_r, dnu,
                                     dtheta, s),
             "samu parameter final");
+    return SCAN_OK;
+}
+
+// ------------------------------------------------------- SAMU decode ---
+scan_status samu_scan_decode(int B, int D, const void* x_sel, const void* b, const float* w_phi,
+                             const float* w_r, const float* a_phi, const float* a_r, const float* nu,
+                             const float* theta, const float* z_in, float* z_out, void* y, int y_dtype,
+                             void* stream) {
+    if (B < 1 || B > 65535 || D < 8 || D % 8 != 0)
+        return fail(SCAN_ERR_SHAPE, "samu_scan_decode: unsupported shape B=" + std::to_string(B) +
+                                        " D=" + std::to_string(D) +
+                                        " (need 1 <= B <= 65535, D >= 8 a multiple of 8)");
+    if (y_dtype != SCAN_BF16 && y_dtype != SCAN_F32)
+        return fail(SCAN_ERR_SHAPE, "samu_scan_decode: y_dtype must be SCAN_BF16 or SCAN_F32");
+    scan_status st = check_ptrs({{x_sel, 0, "x_sel"}, {b, 0, "b"}, {w_phi, 0, "w_phi"}, {w_r, 0, "w_r"},
+                                 {a_phi, 0, "a_phi"}, {a_r, 0, "a_r"}, {nu, 0, "nu"}, {theta, 0, "theta"},
+                                 {z_out, 0, "z_out"}, {y, 0, "y"}},
+                                {{z_in, 0, "z_in"}});
+    if (st != SCAN_OK) return st;
+    const int M = D / 2;
+    const size_t BM = (size_t)B * M;
+    std::vector<Span> ins = {{x_sel, (size_t)B * D * 2, "x_sel"}, {b, BM * 4, "b"},
+                             {w_phi, (size_t)(D + 1) * 4, "w_phi"}, {w_r, (size_t)(D + 1) * 4, "w_r"},
+                             {a_phi, 4, "a_phi"}, {a_r, 4, "a_r"}, {nu, (size_t)M * 4, "nu"},
+                             {theta, (size_t)M * 4, "theta"}};
+    // the state may be updated in place (z_out == z_in), never partly overlapped
+    if (z_in != z_out) ins.push_back({z_in, BM * 8, "z_in"});
+    st = check_alias(ins, {{z_out, BM * 8, "z_out"}, {y, BM * 2 * (y_dtype == SCAN_F32 ? 4 : 2), "y"}});
+    if (st != SCAN_OK) return st;
+    LRS_TRY(launch_samu_decode(B, D, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z_in, z_out, y,
+                               y_dtype == SCAN_F32, (hipStream_t)stream),
+            "samu decode");
     return SCAN_OK;
 }
 

@@ -32,6 +32,7 @@ enum KernelId {
     K_RGLRU_BWD_REPLAY,
     K_RGLRU_ALPHA_REDUCE,
     K_RGLRU_ALPHA_FINAL,
+    K_SAMU_DECODE,
     K_NUM_KERNELS
 };
 
@@ -111,6 +112,13 @@ hipError_t launch_samu_param_reduce(const SamuParams& p, const Chunking& ch,
 hipError_t launch_samu_param_final(const SamuParams& p, const double* g_seg, const double* mode_seg,
                                    int n_seg, float* dw_phi, float* dw_r, float* da_phi,
                                    float* da_r, float* dnu, float* dtheta, hipStream_t s);
+
+// one generation step: z_out = lambda(x_sel) z_in + b, y = z_out (z_in NULL = 0;
+// z_out may be z_in)
+hipError_t launch_samu_decode(int B, int D, const void* x_sel, const void* b, const float* w_phi,
+                              const float* w_r, const float* a_phi, const float* a_r, const float* nu,
+                              const float* theta, const float* z_in, float* z_out, void* y, int y_f32,
+                              hipStream_t s);
 
 // -------------------------------------------------------------- RG-LRU ---
 struct RglruParams {

@@ -1,0 +1,123 @@
+// samu_decode.hip -- one SAMU generation step for a batch of sequences, in a
+// single launch.
+//
+// Page 'Griffin 第 4、5 节 H800 对照协议', 'SAMU 的固定方程': the decode kernel
+// performs the control projection, the transition rebuild, the FP32 state
+// update and the BF16 output in one launch.  The equations are those of page
+// 'SAMU 与 RG-LRU 的 H800 训练性能对比', section 05, for one token:
+//   u = x~ . w^ (x~ = [x_sel; 1], w^ = w/||w|| over all D+1 entries),
+//   p = tanh(u_phi), r = tanh(u_r), q = r/(1+r^2),
+//   d = tanh(a_phi)/sqrt(M) p, c = tanh(a_r)/sqrt(M) q,
+//   lambda_m = exp(-nu_m e^c) [(cos th_m cos d - sin th_m sin d) + i (...)],
+//   z' = lambda z + b,  y = z'.
+//
+// Grid (ceil(M / 256), B): each workgroup forms the two dot products and the
+// two direction norms of its batch row (every mode block repeats this; it is
+// D+1 values against the M/256-fold larger mode work), then 256 lanes advance
+// one mode each.  Sums run in a fixed order, so a step is bitwise
+// reproducible.
+#include "common.hpp"
+
+namespace lrs {
+namespace {
+
+constexpr int DEC_THREADS = 256;
+constexpr int DEC_WAVES = DEC_THREADS / 64;
+
+template <bool F32>
+__global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
+    int D, int M, const uint32_t* __restrict__ x_sel, const uint32_t* __restrict__ drive,
+    const float* __restrict__ w_phi, const float* __restrict__ w_r, const float* __restrict__ a_phi,
+    const float* __restrict__ a_r, const float* __restrict__ nu, const float* __restrict__ theta,
+    const float2* z_in, float2* z_out, void* __restrict__ y) {
+    __shared__ float red[4][DEC_WAVES];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.y;
+    const int W = D / 2;  // selector words per row
+    const uint32_t* xr = x_sel + (size_t)b * W;
+
+    // this lane's mode: its inputs are requested first and its constant
+    // phasor is formed while the selector reduction is in flight
+    const int m = blockIdx.x * DEC_THREADS + tid;
+    const bool act = m < M;
+    const int mc = act ? m : M - 1;
+    const size_t i = (size_t)b * M + mc;
+    const float2 z0 = z_in ? z_in[i] : make_float2(0.f, 0.f);
+    const uint32_t bw = drive[i];
+    const float nu_m = nu[mc], th_m = theta[mc];
+
+    float sp = 0.f, sr = 0.f, np = 0.f, nr = 0.f;
+#pragma unroll 4
+    for (int j = tid; j < W; j += DEC_THREADS) {
+        const uint32_t xw = xr[j];
+        const float2 wp = reinterpret_cast<const float2*>(w_phi)[j];
+        const float2 wr = reinterpret_cast<const float2*>(w_r)[j];
+        const float x0 = bf16_lo(xw), x1 = bf16_hi(xw);
+        sp = fmaf(x1, wp.y, fmaf(x0, wp.x, sp));
+        sr = fmaf(x1, wr.y, fmaf(x0, wr.x, sr));
+        np = fmaf(wp.y, wp.y, fmaf(wp.x, wp.x, np));
+        nr = fmaf(wr.y, wr.y, fmaf(wr.x, wr.x, nr));
+    }
+    if (tid == 0) {  // the constant 1 of x~ and the bias slot of each direction
+        const float bp = w_phi[D], br = w_r[D];
+        sp += bp;
+        sr += br;
+        np = fmaf(bp, bp, np);
+        nr = fmaf(br, br, nr);
+    }
+    const ModeConst k = mode_const(nu_m, th_m);
+    sp = wave_sum(sp);
+    sr = wave_sum(sr);
+    np = wave_sum(np);
+    nr = wave_sum(nr);
+    if (lane == 0) {
+        red[0][wave] = sp;
+        red[1][wave] = sr;
+        red[2][wave] = np;
+        red[3][wave] = nr;
+    }
+    __syncthreads();
+    float Sp = 0.f, Sr = 0.f, Np = 0.f, Nr = 0.f;
+#pragma unroll
+    for (int w = 0; w < DEC_WAVES; ++w) {
+        Sp += red[0][w];
+        Sr += red[1][w];
+        Np += red[2][w];
+        Nr += red[3][w];
+    }
+    const float p = tanhf(Sp / sqrtf(Np));
+    const float r = tanhf(Sr / sqrtf(Nr));
+    const float q = r / (1.0f + r * r);
+    const float sM = sqrtf((float)M);
+    const float d = tanhf(a_phi[0]) / sM * p;
+    const float c = tanhf(a_r[0]) / sM * q;
+    const float E = expf(c);
+    float S, Cd;
+    sincosf(d, &S, &Cd);
+
+    if (!act) return;
+    const cf lam = mode_lambda(k, E, Cd, S);
+    const cf z = cfma(lam, {z0.x, z0.y}, {bf16_lo(bw), bf16_hi(bw)});
+    z_out[i] = make_float2(z.re, z.im);
+    if (F32) reinterpret_cast<float2*>(y)[i] = make_float2(z.re, z.im);
+    else reinterpret_cast<uint32_t*>(y)[i] = pack_bf16x2(z.re, z.im);
+}
+
+}  // namespace
+
+hipError_t launch_samu_decode(int B, int D, const void* x_sel, const void* b, const float* w_phi,
+                              const float* w_r, const float* a_phi, const float* a_r, const float* nu,
+                              const float* theta, const float* z_in, float* z_out, void* y, int y_f32,
+                              hipStream_t s) {
+    const int M = D / 2;
+    const dim3 grid((unsigned)ceil_div(M, DEC_THREADS), (unsigned)B);
+#define DEC_CASE(FF)                                                                                        \
+    LRS_LAUNCH(K_SAMU_DECODE, samu_decode_kernel<FF>, grid, dim3(DEC_THREADS), 0, s, D, M,                \
+               (const uint32_t*)x_sel, (const uint32_t*)b, w_phi, w_r, a_phi, a_r, nu, theta,              \
+               (const float2*)z_in, (float2*)z_out, y)
+    if (y_f32) DEC_CASE(true); else DEC_CASE(false);
+#undef DEC_CASE
+    return hipGetLastError();
+}
+
+}  // namespace lrs

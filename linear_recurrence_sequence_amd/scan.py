@@ -51,6 +51,8 @@ def lib():
     L.samu_scan_fwd.restype = i
     L.samu_scan_bwd.argtypes = [i] * 5 + [vp] * 8 + [vp, vp, vp, vp, vp, i, vp] + [vp] * 6 + [vp, sz, vp]
     L.samu_scan_bwd.restype = i
+    L.samu_scan_decode.argtypes = [i, i] + [vp] * 10 + [vp, i, vp]
+    L.samu_scan_decode.restype = i
     L.rglru_scan_fwd.argtypes = [i] * 5 + [vp] * 6 + [vp, i, vp, vp, vp, sz, vp]
     L.rglru_scan_fwd.restype = i
     L.rglru_scan_bwd.argtypes = [i] * 5 + [vp] * 5 + [vp, vp, vp, vp, vp, vp, i, vp, vp, vp, sz, vp]
@@ -173,6 +175,25 @@ def samu_scan_bwd(x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, saved, dy, dz_fin
 
 
 # ----------------------------------------------------------------- RG-LRU ---
+def samu_scan_decode(x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z=None, *,
+                     y_dtype=torch.bfloat16, y=None, z_out=None, stream=None):
+    """One generation step.  x_sel [B, D] bf16, b [B, M, 2] bf16, z [B, M, 2]
+    f32 or None (= 0).  Returns (y [B, M, 2], z_out [B, M, 2] f32); pass
+    z_out=z to update the state in place."""
+    B, D = x_sel.shape
+    M = D // 2
+    dev = x_sel.device
+    if y is None:
+        y = torch.empty((B, M, 2), dtype=y_dtype, device=dev)
+    if z_out is None:
+        z_out = torch.empty((B, M, 2), dtype=torch.float32, device=dev)
+    st = lib().samu_scan_decode(B, D, _p(x_sel), _p(b), _p(w_phi), _p(w_r), _p(a_phi), _p(a_r),
+                                _p(nu), _p(theta), _p(z), _p(z_out), _p(y), _code(y.dtype),
+                                _stream(stream))
+    _check(st, "samu_scan_decode")
+    return y, z_out
+
+
 def rglru_scan_fwd(x, lx, la, alpha, reset=None, h0=None, *, K=16, G=0, y_dtype=torch.bfloat16,
                    y=None, h_final=None, saved=None, workspace=None, stream=None):
     """Returns (y [B,L,D], h_final [B,D] f32, saved uint8)."""

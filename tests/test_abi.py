@@ -121,3 +121,30 @@ def test_rglru_fwd_rejects_before_enqueue():
     # workspace too small
     assert L.rglru_scan_fwd(1, 8, 4, 16, 0, ok["x"], ok["lx"], ok["la"], ok["al"], None, None,
                             f(0x500000), 0, None, f(0x600000), f(0x700000), 8, None) == -4
+
+
+def _call_decode(**over):
+    from linear_recurrence_sequence_amd import scan
+    a = dict(B=2, D=16, x_sel=0x100000, b=0x200000, w_phi=0x300000, w_r=0x300100, a_phi=0x300200,
+             a_r=0x300210, nu=0x300300, theta=0x300400, z_in=0x500000, z_out=0x600000,
+             y=0x700000, y_dtype=0)
+    a.update(over)
+    v = lambda x: None if x is None else _fake(x)
+    return scan.lib().samu_scan_decode(a["B"], a["D"], v(a["x_sel"]), v(a["b"]), v(a["w_phi"]),
+                                       v(a["w_r"]), v(a["a_phi"]), v(a["a_r"]), v(a["nu"]),
+                                       v(a["theta"]), v(a["z_in"]), v(a["z_out"]), v(a["y"]),
+                                       a["y_dtype"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(D=12), -2), (dict(B=0), -2), (dict(B=70000), -2), (dict(y_dtype=2), -2),
+    (dict(z_out=None), -1), (dict(y=None), -1), (dict(theta=None), -1),
+    (dict(b=0x200008), -3),
+    (dict(y=0x100000), -6),                 # y overlaps x_sel
+    (dict(z_out=0x500020), -6),             # z_out partly overlaps z_in
+    (dict(z_out=0x700000), -6),             # z_out overlaps y
+])
+def test_samu_decode_rejects_before_enqueue(over, status):
+    from linear_recurrence_sequence_amd import scan
+    assert _call_decode(**over) == status
+    assert scan.lib().scan_last_error().decode()
