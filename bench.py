@@ -38,10 +38,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def effective_groups(L, K, G):
-    """Chunks per group the library uses (G=0 asks for at most 128 groups)."""
+def effective_groups(L, K, G, min_group=8):
+    """Chunks per group the library uses for G (0 = its choice by shape:
+    serial up to 128 chunks, else about 128 groups of >= min_group chunks)."""
     C = -(-L // K)
-    return min(G if G > 0 else -(-C // 128), C)
+    if G == 0:
+        G = C if C <= 128 else max(min_group, -(-C // 128))
+    return min(G, C)
 
 
 def kernel_bytes(name, B, L, D, K, G):
@@ -277,7 +280,7 @@ def main():
                                 K=RK, G=RG, out=rout, workspace=rwb)
 
         rg_ms, rg_prof = timed(rg_step, args.steps, args.warmup, False)
-        rg = {"ms_per_step": round(rg_ms, 4), "K": RK, "G": effective_groups(L, RK, RG),
+        rg = {"ms_per_step": round(rg_ms, 4), "K": RK, "G": effective_groups(L, RK, RG, 16),
               "gbs_floor": round(22.0 * B * L * D / (rg_ms * 1e-3) / 1e9, 1),
               "samu_fb_time_reduction": round((rg_ms - ms) / rg_ms, 4)}
         log(f"[bench] RG-LRU F+B {rg_ms:.4f} ms/step; SAMU reduction {(rg_ms - ms) / rg_ms:.1%}")

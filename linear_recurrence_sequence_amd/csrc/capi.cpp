@@ -92,21 +92,20 @@ struct Carver {
     }
 };
 
-// default_G <= 0: about kTargetGroups groups per batch row, so the group scan
-// is one short in-workgroup pass and each group walk stays short.
-static constexpr int kTargetGroups = 128;
-static bool chunking(int B, int L, int K, int G, int default_G, Chunking* ch) {
+// G == 0 picks the grouping from the shape (measured on MI355X at the
+// pages' workloads, F+B at B = 1 and 8, D = 1024..2560, L = 2K..131K):
+//   * at most kSerialMaxChunks chunks per row: the serial prefix (one group;
+//     one launch per direction instead of three, and the walk is short);
+//   * otherwise about kTargetGroups groups per row, each at least
+//     min_group chunks long (8 for the complex scan, 16 for the real one).
+static constexpr int64_t kSerialMaxChunks = 128;
+static constexpr int64_t kTargetGroups = 128;
+static bool chunking(int B, int L, int K, int G, int min_group, Chunking* ch) {
     if (B < 1 || L < 1 || B > 65535 || (K != 16 && K != 32) || G < 0) return false;
     const int64_t C = ceil_div(L, K);
     if (C > 65535 || (int64_t)B * L > 0x7fffffff) return false;
-    int g = G;
-    if (g == 0) {
-        if (default_G > 0) {
-            g = default_G;
-        } else {
-            g = (int)ceil_div(C, kTargetGroups);
-        }
-    }
+    int64_t g = G;
+    if (g == 0) g = C <= kSerialMaxChunks ? C : std::max<int64_t>(min_group, ceil_div(C, kTargetGroups));
     ch->B = B;
     ch->L = L;
     ch->K = K;
@@ -116,8 +115,8 @@ static bool chunking(int B, int L, int K, int G, int default_G, Chunking* ch) {
     return true;
 }
 
-static constexpr int kSamuDefaultG = 0;      // adaptive, see chunking()
-static constexpr int kRglruDefaultG = 0;
+static constexpr int kSamuMinGroup = 8;      // see chunking()
+static constexpr int kRglruMinGroup = 16;
 static constexpr int kParamSegments = 32;
 
 struct SamuSaved {
@@ -256,12 +255,12 @@ static scan_status device_status(hipError_t e, const char* where) {
 
 static bool samu_shape(int B, int L, int D, int K, int G, Chunking* ch) {
     if (D < 8 || D % 8 != 0) return false;
-    return chunking(B, L, K, G, kSamuDefaultG, ch);
+    return chunking(B, L, K, G, kSamuMinGroup, ch);
 }
 
 static bool rglru_shape(int B, int L, int D, int K, int G, Chunking* ch) {
     if (D < 2 || D % 2 != 0) return false;
-    return chunking(B, L, K, G, kRglruDefaultG, ch);
+    return chunking(B, L, K, G, kRglruMinGroup, ch);
 }
 
 static std::string shape_text(int B, int L, int D, int K, int G) {

@@ -16,6 +16,8 @@
 //   * expand: one thread per (group, element) walks the group's chunks from
 //     that state, applying S_c and storing the state entering every chunk --
 //     that walk is L_c applied to O_g(init).
+// With a single group (the serial prefix, G >= C) only the walk runs, from
+// init itself.
 // Adjoint scans visit chunks and groups in reverse order with the same
 // operator.  In compose and expand, lanes map to consecutive elements, so
 // every row access is contiguous across the wave.
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(CMP_THREADS) void prefix_expand_kernel(
     if (w >= W) return;
     const int c0 = q * G;
     const int n = min(G, C - c0);
-    St<E> h = St<E>::load(gentry, ((size_t)b * NG + q) * W + w);
+    St<E> h = gentry ? St<E>::load(gentry, ((size_t)b * NG + q) * W + w) : St<E>::zero();
 #pragma unroll 8
     for (int i = 0; i < n; ++i) {
         const size_t idx = ((size_t)b * C + chunk_of(c0 + i, C, REV)) * W + w;
@@ -168,8 +170,16 @@ hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, cons
     while (slots < ch.NG && slots < SCAN_THREADS / 8) slots <<= 1;
     const int MT = SCAN_THREADS / slots;
     const dim3 sgrid((unsigned)ceil_div(W, MT), ch.B);
+    // a single group (the serial prefix) needs no group summaries: the walk
+    // starts from the initial state itself
+    const bool serial = ch.NG == 1;
 #define PFX(EE, RR)                                                                                          \
     do {                                                                                                     \
+        if (serial) {                                                                                        \
+            LRS_LAUNCH(K_PREFIX_ENTRIES, (prefix_expand_kernel<EE, RR>), wgrid, dim3(CMP_THREADS), 0, s,     \
+                       ch.C, ch.G, ch.NG, W, summ, init, entries);                                            \
+            break;                                                                                           \
+        }                                                                                                    \
         LRS_LAUNCH(K_PREFIX_GROUPS, (prefix_compose_kernel<EE, RR>), wgrid, dim3(CMP_THREADS), 0, s, ch.C,   \
                    ch.G, ch.NG, W, summ, gsum);                                                               \
         LRS_LAUNCH(K_PREFIX_OUTER, (prefix_group_scan_kernel<EE>), sgrid, dim3(SCAN_THREADS), 0, s, ch.NG,  \

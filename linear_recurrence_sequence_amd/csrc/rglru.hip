@@ -29,6 +29,14 @@ namespace lrs {
 namespace {
 
 constexpr int RG_THREADS = 256;
+#ifndef LRS_RG_BWD_H
+#define LRS_RG_BWD_H 16
+#endif
+#ifndef LRS_RG_BWD_KEEP
+#define LRS_RG_BWD_KEEP 0
+#endif
+constexpr int RG_BWD_H = LRS_RG_BWD_H;       // backward sub-chunk length
+constexpr bool RG_BWD_KEEP = LRS_RG_BWD_KEEP; // keep forward gates live (vs recompute)
 constexpr int RG_CH = 2 * RG_THREADS;     // channels per workgroup
 // 1/(2 sqrt(u)) is capped at 1000: the reciprocal square root used for the
 // derivative is capped at 2000 = rsq(2.5e-7).
@@ -314,7 +322,8 @@ __device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[
             const float xv[2] = {bf16_lo(xs[i]), bf16_hi(xs[i])};
             // the gates are evaluated again rather than kept from the forward
             // pass: six live values per token and channel would not fit
-            const uint32_t lxw = opaque_v(lxs[i]), law = opaque_v(las[i]);
+            const uint32_t lxw = RG_BWD_KEEP ? lxs[i] : opaque_v(lxs[i]);
+            const uint32_t law = RG_BWD_KEEP ? las[i] : opaque_v(las[i]);
             const float lxv[2] = {bf16_lo(lxw), bf16_hi(lxw)};
             const float lav[2] = {bf16_lo(law), bf16_hi(law)};
             float ox[2], olx[2], ola[2];
@@ -391,8 +400,11 @@ __device__ __forceinline__ void rg_bwd_chunk(const RgIn& in, const ChanConst (&k
         rg_bwd_sub<H, F32, FULL>(in, k, o, tok0 + s * H, lw, kq - s * H, rm >> (s * H), ck[s], carry, acc);
 }
 
+#ifndef LRS_RG_BWD_WPE
+#define LRS_RG_BWD_WPE 1
+#endif
 template <int K, int H, bool F32>
-__global__ __launch_bounds__(RG_THREADS) void rglru_bwd_replay_kernel(
+__global__ __launch_bounds__(RG_THREADS) __attribute__((amdgpu_waves_per_eu(LRS_RG_BWD_WPE, 8))) void rglru_bwd_replay_kernel(
     RgIn in, int C, const float* __restrict__ alpha, const float* __restrict__ entries,
     const float* __restrict__ carry_in, RgBwdOut o, float* __restrict__ dh0,
     float* __restrict__ alpha_part) {
@@ -506,7 +518,7 @@ hipError_t launch_rglru_bwd_replay(const RglruParams& p, const Chunking& ch, con
     const RgIn in = rg_in(p);
     const RgBwdOut o{(const uint32_t*)dy, dx, dlx, dla};
 #define RG_BWD(KK, FF)                                                                                  \
-    LRS_LAUNCH(K_RGLRU_BWD_REPLAY, (rglru_bwd_replay_kernel<KK, 16, FF>), grid, dim3(RG_THREADS), 0, s, \
+    LRS_LAUNCH(K_RGLRU_BWD_REPLAY, (rglru_bwd_replay_kernel<KK, RG_BWD_H, FF>), grid, dim3(RG_THREADS), 0, s, \
                in, ch.C, p.alpha, entries, carry_in, o, dh0, alpha_part)
     if (ch.K == 32) { if (g_f32) RG_BWD(32, true); else RG_BWD(32, false); }
     else { if (g_f32) RG_BWD(16, true); else RG_BWD(16, false); }

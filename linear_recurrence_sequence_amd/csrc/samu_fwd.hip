@@ -31,9 +31,15 @@ namespace {
 // of each token row per 512-column slab, the wave reduces the two dot products
 // and lanes 0..CTL_TOK-1 finish one token each.  The grid also writes the
 // per-mode constant table (strided over all blocks).
-constexpr int CTL_WAVES = 8;
+#ifndef LRS_CTL_WAVES
+#define LRS_CTL_WAVES 8
+#endif
+#ifndef LRS_CTL_TOK
+#define LRS_CTL_TOK 8
+#endif
+constexpr int CTL_WAVES = LRS_CTL_WAVES;
 constexpr int CTL_THREADS = 64 * CTL_WAVES;
-constexpr int CTL_TOK = 4;                          // tokens per wave
+constexpr int CTL_TOK = LRS_CTL_TOK;                // tokens per wave
 constexpr int CTL_TOK_PER_BLOCK = CTL_WAVES * CTL_TOK;
 #ifndef LRS_CTL_SLAB
 #define LRS_CTL_SLAB 1

@@ -199,3 +199,25 @@ def test_samu_forward_sweep_parity(L):
     ey, ez = rel_l2(to_f64(y), rf["y"]), rel_l2(to_f64(zf), rf["z_final"])
     say(f"   errors: y {ey:.2e} z_final {ez:.2e}")
     assert ey <= TOL_OUT and ez <= TOL_OUT
+
+
+def test_samu_hybrid_prefix_parity():
+    """Serial forward prefix with a grouped reverse prefix (the parenthesization
+    the pages select for very long sequences): the grouping only re-associates
+    an exact composition, so both directions still match the oracle."""
+    from linear_recurrence_sequence_amd import scan
+    B, L, D, K = 1, 9000, 256, 32
+    inp = _inputs(B, L, D, 4242, 0.1)
+    say(f"[samu parity] hybrid B={B} L={L} D={D}: oracle")
+    rf, rg = _oracle(inp)
+    d = {k: dev_tensor(v) for k, v in inp.items()}
+    say("[samu parity] hybrid: samu_scan_fwd serial, samu_scan_bwd G=4")
+    y, zf, saved = scan.samu_scan_fwd(d["x_sel"], d["b"], d["w_phi"], d["w_r"], d["a_phi"], d["a_r"],
+                                      d["nu"], d["theta"], d["z0"], K=K, G=10**6, y_dtype=torch.float32)
+    g = scan.samu_scan_bwd(d["x_sel"], d["b"], d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"],
+                           d["theta"], saved, d["dy"], d["dz_final"], K=K, G=4, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_l2(to_f64(y), rf["y"]) <= TOL_OUT
+    assert rel_l2(to_f64(zf), rf["z_final"]) <= TOL_OUT
+    for k in ("dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta", "dz0"):
+        assert rel_l2(to_f64(g[k]), rg[k]) <= TOL_GRAD, k
