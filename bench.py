@@ -303,12 +303,27 @@ def main():
             dms, _ = timed(dec_step, n, 10, False)
             _, dprof = timed(dec_step, n, 1, True)
             kus = dprof["samu_decode"][0] / dprof["samu_decode"][1] * 1e3
+            # the same steps replayed from a captured HIP graph (32 steps per graph)
+            gs = torch.cuda.Stream()
+            gs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(gs):
+                for _ in range(3):
+                    dec_step()
+            torch.cuda.current_stream().wait_stream(gs)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(32):
+                    dec_step()
+            gms, _ = timed(graph.replay, 20, 3, False)
             # x_sel, b, state in and out, y, both directions, nu and theta
             nbytes = Bd * (2 * D + 4 * M + 16 * M + 4 * M) + 8 * (D + 1) + 8 * M
-            dec[f"B{Bd}"] = {"us_per_step": round(dms * 1e3, 2), "kernel_us": round(kus, 2),
+            dec[f"B{Bd}"] = {"us_per_step": round(dms * 1e3, 2),
+                             "us_per_step_graph": round(gms * 1e3 / 32, 2), "kernel_us": round(kus, 2),
                              "bytes_per_step": nbytes,
                              "kernel_gbs": round(nbytes / (kus * 1e-6) / 1e9, 1)}
-            log(f"    B={Bd}: {dms * 1e3:.2f} us/step ({kus:.2f} us kernel, {nbytes} B)")
+            log(f"    B={Bd}: {dms * 1e3:.2f} us/step eager, {gms * 1e3 / 32:.2f} us/step from a graph "
+                f"({kus:.2f} us kernel with events, {nbytes} B)")
 
     cpu = None
     if not args.no_cpu_baseline:

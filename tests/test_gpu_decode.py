@@ -80,3 +80,45 @@ def test_decode_bitwise_deterministic():
                               d["z0"], y_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_graph_replays_match_eager():
+    """32 in-place steps captured in a HIP graph: every replay, started from
+    the same state (restored eagerly between replays), equals the eager run."""
+    from linear_recurrence_sequence_amd import scan
+    B, D, T = 4, 512, 32
+    inp = inputs.samu_inputs(B, T, D, 123, z0_std=0.1, with_dy=False)
+    d = _dev(inp)
+    xs = [d["x_sel"][:, t].contiguous() for t in range(T)]
+    bs = [d["b"][:, t].contiguous() for t in range(T)]
+    z = d["z0"].clone()
+    y = torch.empty((B, D // 2, 2), dtype=torch.float32, device="cuda")
+
+    def steps():
+        for t in range(T):
+            scan.samu_scan_decode(xs[t], bs[t], *_params(d), z, y=y, z_out=z)
+
+    say("[samu decode] graph: eager reference")
+    steps()
+    torch.cuda.synchronize()
+    z_ref, y_ref = z.clone(), y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        z.copy_(d["z0"])
+        steps()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("[samu decode] graph: capture")
+    g = torch.cuda.CUDAGraph()
+    z.copy_(d["z0"])
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        steps()
+    for r in range(4):
+        say(f"[samu decode] graph: replay {r}")
+        z.copy_(d["z0"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(z, z_ref) and torch.equal(y, y_ref), r
