@@ -130,26 +130,27 @@ static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t
     s.r = cv.take<float>(BL);
     s.u = cv.take<float>(BL * 2);
     s.ctl = cv.take<float>(BL * 4);
-    s.mtab = cv.take<float>((size_t)M * 8);
+    s.mtab = cv.take<float>((size_t)M * 16);
     s.entries = cv.take<float>((size_t)ch.B * ch.C * M * 2);
     if (bytes) *bytes = cv.off;
     return s;
 }
 
 struct SamuFwdWs {
-    float *summ, *gsum;
+    float *summ, *chunk, *gsum;
 };
 static SamuFwdWs samu_fwd_ws_layout(void* base, const Chunking& ch, int M, size_t* bytes) {
     Carver cv(base);
     SamuFwdWs w;
-    w.summ = cv.take<float>((size_t)ch.B * ch.C * M * 4);
+    w.summ = cv.take<float>((size_t)ch.B * ch.C * M * 2);
+    w.chunk = cv.take<float>((size_t)ch.B * ch.C * 4);
     w.gsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
     if (bytes) *bytes = cv.off;
     return w;
 }
 
 struct SamuBwdWs {
-    float *rsumm, *rgsum, *carry, *tok_part, *mode_part, *g_part;
+    float *rsumm, *rchunk, *rgsum, *carry, *tok_part, *mode_part, *g_part;
     double *g_seg, *mode_seg;
     int n_tiles, n_blk, n_seg;
 };
@@ -160,7 +161,8 @@ static SamuBwdWs samu_bwd_ws_layout(void* base, const Chunking& ch, int D, int M
     w.n_tiles = samu_bwd_tiles(M);
     w.n_blk = (int)ceil_div((int64_t)ch.B * ch.L, samu_ctl_tok_per_blk());
     w.n_seg = std::min(kParamSegments, std::max(1, std::min(w.n_blk, ch.B * ch.C)));
-    w.rsumm = cv.take<float>(BCM * 4);
+    w.rsumm = cv.take<float>(BCM * 2);
+    w.rchunk = cv.take<float>((size_t)ch.B * ch.C * 4);
     w.rgsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
     w.carry = cv.take<float>(BCM * 2);
     w.tok_part = cv.take<float>((size_t)ch.B * w.n_tiles * ch.L * 2);
@@ -340,9 +342,11 @@ scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
     SamuSaved sv = samu_saved_layout(saved, ch, M, nullptr);
     SamuFwdWs ws = samu_fwd_ws_layout(workspace, ch, M, nullptr);
-    LRS_TRY(launch_samu_controller(p, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, s), "samu controller");
-    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, s), "samu chunk summary");
-    LRS_TRY(launch_prefix(2, false, ch, M, ws.summ, ws.gsum, z0, sv.entries, s), "samu prefix");
+    LRS_TRY(launch_samu_controller(p, ch, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, s), "samu controller");
+    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, ws.chunk, s), "samu chunk summary");
+    LRS_TRY(launch_prefix(2, false, ch, M, PrefixSummaries{nullptr, ws.summ, ws.chunk, sv.mtab}, ws.gsum, z0,
+                          sv.entries, s),
+            "samu prefix");
     LRS_TRY(launch_samu_replay(p, ch, sv.ctl, sv.mtab, sv.entries, y, y_dtype == SCAN_F32, z_final, s),
             "samu replay");
     return SCAN_OK;
@@ -392,8 +396,11 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuSaved sv = samu_saved_layout(const_cast<void*>(saved), ch, M, nullptr);
     SamuBwdWs ws = samu_bwd_ws_layout(workspace, ch, D, M, nullptr);
     const int f32 = grad_dtype == SCAN_F32;
-    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, s), "samu reverse summary");
-    LRS_TRY(launch_prefix(2, true, ch, M, ws.rsumm, ws.rgsum, dz_final, ws.carry, s), "samu reverse prefix");
+    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, ws.rchunk, s),
+            "samu reverse summary");
+    LRS_TRY(launch_prefix(2, true, ch, M, PrefixSummaries{nullptr, ws.rsumm, ws.rchunk, sv.mtab}, ws.rgsum,
+                          dz_final, ws.carry, s),
+            "samu reverse prefix");
     LRS_TRY(launch_samu_bwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, ws.carry, dy, db, f32, dz0,
                                    ws.tok_part, ws.n_tiles, ws.mode_part, s),
             "samu backward replay");
@@ -489,7 +496,9 @@ scan_status rglru_scan_fwd(int B, int L, int D, int K, int G, const void* x, con
     RgSaved sv = rg_saved_layout(saved, ch, D, nullptr);
     RgWs ws = rg_ws_layout(workspace, ch, D, false, nullptr);
     LRS_TRY(launch_rglru_summary(p, ch, ws.summ, s), "rglru chunk summary");
-    LRS_TRY(launch_prefix(1, false, ch, D, ws.summ, ws.gsum, h0, sv.entries, s), "rglru prefix");
+    LRS_TRY(launch_prefix(1, false, ch, D, PrefixSummaries{ws.summ, nullptr, nullptr, nullptr}, ws.gsum, h0,
+                          sv.entries, s),
+            "rglru prefix");
     LRS_TRY(launch_rglru_replay(p, ch, sv.entries, y, y_dtype == SCAN_F32, h_final, s), "rglru replay");
     return SCAN_OK;
 }
@@ -530,7 +539,9 @@ scan_status rglru_scan_bwd(int B, int L, int D, int K, int G, const void* x, con
     RgWs ws = rg_ws_layout(workspace, ch, D, true, nullptr);
     const int f32 = grad_dtype == SCAN_F32;
     LRS_TRY(launch_rglru_rev_summary(p, ch, dy, ws.summ, s), "rglru reverse summary");
-    LRS_TRY(launch_prefix(1, true, ch, D, ws.summ, ws.gsum, dh_final, ws.carry, s), "rglru reverse prefix");
+    LRS_TRY(launch_prefix(1, true, ch, D, PrefixSummaries{ws.summ, nullptr, nullptr, nullptr}, ws.gsum,
+                          dh_final, ws.carry, s),
+            "rglru reverse prefix");
     LRS_TRY(launch_rglru_bwd_replay(p, ch, sv.entries, ws.carry, dy, dx, dlx, dla, f32, dh0, ws.alpha_part, s),
             "rglru backward replay");
     LRS_TRY(launch_rglru_alpha_reduce(p, ch, ws.alpha_part, ws.alpha_seg, ws.n_seg, dalpha, s), "rglru alpha reduction");

@@ -101,14 +101,39 @@ __device__ __forceinline__ ModeConst mode_const(float nu, float theta) {
     return k;
 }
 
-// Two float4 per mode: (kappa, ch, sh, cl), (sl, nu, 0, 0).
-__device__ __forceinline__ void store_mode(float4* tab, int m, const ModeConst& k) {
-    tab[2 * m] = make_float4(k.kappa, k.ch, k.sh, k.cl);
-    tab[2 * m + 1] = make_float4(k.sl, k.nu, 0.f, 0.f);
+// e^{i n theta} for a whole chunk of n tokens, split like the unit phasor
+// (hi + lo pairs from an FP64 evaluation).  With it, the product of a chunk's
+// transitions has the closed form (page 'SAMU strengthened-baseline H800
+// report', 'Candidates that remain disabled', the compressed G/D closure)
+//   prod_t lambda_{t,m} = exp(-nu_m G_c) e^{i n theta_m} e^{i D_c},
+//   G_c = sum_t E_t, D_c = sum_t d_t.
+struct ChunkPhase { float ch, sh, cl, sl; };
+
+__device__ __forceinline__ ChunkPhase chunk_phase(float theta, int n) {
+    ChunkPhase p;
+    double s, c;
+    sincos((double)n * (double)theta, &s, &c);
+    p.ch = (float)c;
+    p.cl = (float)(c - (double)p.ch);
+    p.sh = (float)s;
+    p.sl = (float)(s - (double)p.sh);
+    return p;
+}
+
+// Four float4 per mode: (kappa, ch, sh, cl), (sl, nu, 0, 0), then the chunk
+// phasors e^{i K theta} and e^{i K_last theta} as (ch, sh, cl, sl).
+constexpr int MODE_REC = 4;
+
+__device__ __forceinline__ void store_mode(float4* tab, int m, const ModeConst& k, const ChunkPhase& full,
+                                           const ChunkPhase& last) {
+    tab[MODE_REC * m] = make_float4(k.kappa, k.ch, k.sh, k.cl);
+    tab[MODE_REC * m + 1] = make_float4(k.sl, k.nu, 0.f, 0.f);
+    tab[MODE_REC * m + 2] = make_float4(full.ch, full.sh, full.cl, full.sl);
+    tab[MODE_REC * m + 3] = make_float4(last.ch, last.sh, last.cl, last.sl);
 }
 
 __device__ __forceinline__ ModeConst load_mode(const float4* __restrict__ tab, int m) {
-    const float4 a = tab[2 * m], b = tab[2 * m + 1];
+    const float4 a = tab[MODE_REC * m], b = tab[MODE_REC * m + 1];
     ModeConst k;
     k.kappa = a.x; k.ch = a.y; k.sh = a.z; k.cl = a.w;
     k.sl = b.x; k.nu = b.y;
@@ -143,8 +168,12 @@ __device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
     return x;
 }
 
-// Per-token control record written by the controller kernel.
-struct TokenCtl { float E, C, S, pad; };
+// Per-token control record written by the controller kernel: E = e^c,
+// (C, S) = (cos d, sin d) and d itself.
+struct TokenCtl { float E, C, S, d; };
+
+// Per-chunk record of the compressed summaries: (G_c, cos D_c, sin D_c, 0).
+struct ChunkCtl { float G, cD, sD, pad; };
 
 
 // ------------------------------------------------------ wave reductions ---

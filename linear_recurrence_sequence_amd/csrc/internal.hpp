@@ -58,14 +58,24 @@ struct Chunking {
 
 // --------------------------------------------------- prefix (all scans) ---
 // Element type of a scan: 1 = real (RG-LRU channels), 2 = complex (SAMU modes).
-// summ:    [B, C, W] chunk summaries (A, B) in chunk order (2*ELEM floats each)
+// Chunk summaries in chunk order:
+//   real:    full = [B, C, W] (A, B) pairs;
+//   complex: bpart = [B, C, W] complex B parts, chunk = [B, C] float4
+//            (G_c, cos D_c, sin D_c, 0), mtab = the mode table (the chunk
+//            phasors e^{i K theta}, e^{i K_last theta} and kappa per mode).
+struct PrefixSummaries {
+    const float* full;
+    const float* bpart;
+    const float* chunk;
+    const float* mtab;
+};
 // gsum:    workspace of 3*ELEM floats per (batch, group, element): [B, NG, W]
 //          group summaries U_g in processing order, then [B, NG, W] states
-//          entering each group
+//          entering each group (unused with a single group)
 // init:    [B, W] initial state (NULL = 0)
 // entries: [B, C, W] state entering each chunk (ELEM floats each); for an
 //          adjoint scan (reverse) the cotangent arriving after its last token
-hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const float* summ,
+hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const PrefixSummaries& sm,
                          float* gsum, const float* init, float* entries, hipStream_t s);
 
 // ---------------------------------------------------------------- SAMU ---
@@ -83,13 +93,14 @@ struct SamuParams {
 };
 
 // saved forward record (per token): p, r, u = (x~ . w^_phi, x~ . w^_r),
-// ctl = (E, C, S, 0); per mode: the two-float4 constant table mtab.
-hipError_t launch_samu_controller(const SamuParams& p, float* p_out, float* r_out, float* u_out,
-                                  float* ctl, float* mtab, hipStream_t s);
-// chunk summaries [B, C, M] (forward, or the conjugate reverse summary of dy)
+// ctl = (E, C, S, d); per mode: the four-float4 constant table mtab.
+hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
+                                  float* u_out, float* ctl, float* mtab, hipStream_t s);
+// compressed chunk summaries (forward, or the conjugate reverse summary of
+// dy): B parts [B, C, M] complex and per-chunk records [B, C] float4
 hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const float* ctl,
                                const float* mtab, const void* drive, bool reverse, float* summ,
-                               hipStream_t s);
+                               float* chunk_rec, hipStream_t s);
 // replay from the chunk entry states; writes y and z_final
 hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
                               const float* mtab, const float* entries, void* y, int y_f32,

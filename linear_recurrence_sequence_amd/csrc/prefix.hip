@@ -9,7 +9,9 @@
 //     Q_c = L_c o O_g with L_c = S_{c-1} o ... o S_{g0},
 // where (A2, B2) o (A1, B1) = (A2 A1, A2 B1 + B2) and the right operand runs
 // first.  The state entering chunk c is Q_c(init).  Three kernels:
-//   * compose: one thread per (group, element) forms U_g from its chunks;
+//   * compose: one thread per (group, element) forms U_g from its chunks
+//     (complex summaries arrive compressed: the transition product of each
+//     chunk is rebuilt from two per-chunk scalars, see CompressedSummaries);
 //   * group scan: a workgroup owns a few elements and all groups; an LDS
 //     Hillis-Steele scan (later o earlier at every step, so the order is
 //     kept) gives O_g, and O_g(init), the state entering group g, is stored;
@@ -80,21 +82,64 @@ template <> struct St<2> {
 
 __device__ __forceinline__ int chunk_of(int cc, int C, bool reverse) { return reverse ? C - 1 - cc : cc; }
 
+// Chunk summaries stored whole: (A, B) per (batch, chunk, element).
+template <int E>
+struct FullSummaries {
+    const float* summ;
+    int C, W;
+    __device__ void bind(int) {}
+    __device__ Aff<E> operator()(int b, int c, int w) const {
+        return Aff<E>::load(summ, ((size_t)b * C + c) * W + w);
+    }
+};
+
+// Complex chunk summaries stored compressed: B per (batch, chunk, mode) and
+// (G_c, cos D_c, sin D_c) per (batch, chunk); the transition product is
+//   A_{c,m} = 2^(kappa_m G_c) e^{i n_c theta_m} e^{i D_c}
+// with e^{i n theta} from the mode table (n = K, or K_last for the last
+// chunk), and its conjugate for the adjoint (REV) scan.
+template <bool REV>
+struct CompressedSummaries {
+    const float* bpart;
+    const float4* chunk;
+    const float4* mtab;
+    int C, W;
+    float kappa;
+    float4 ph_full, ph_last;
+    __device__ void bind(int w) {
+        kappa = mtab[MODE_REC * w].x;
+        ph_full = mtab[MODE_REC * w + 2];
+        ph_last = mtab[MODE_REC * w + 3];
+    }
+    __device__ Aff<2> operator()(int b, int c, int w) const {
+        const float2 bb = reinterpret_cast<const float2*>(bpart)[((size_t)b * C + c) * W + w];
+        const float4 g = chunk[(size_t)b * C + c];
+        const float4 ph = c == C - 1 ? ph_last : ph_full;  // (ch, sh, cl, sl)
+        const float re = fmaf(ph.x, g.y, -ph.y * g.z) + fmaf(ph.z, g.y, -ph.w * g.z);
+        const float im = fmaf(ph.x, g.z, ph.y * g.y) + fmaf(ph.z, g.z, ph.w * g.y);
+        const float rho = __builtin_amdgcn_exp2f(kappa * g.x);
+        Aff<2> f;
+        f.a = {rho * re, REV ? -rho * im : rho * im};
+        f.b = {bb.x, bb.y};
+        return f;
+    }
+};
+
 constexpr int CMP_THREADS = 256;
 
-// U_g for every (batch, group, mode), groups numbered in processing order.
-template <int E, bool REV>
-__global__ __launch_bounds__(CMP_THREADS) void prefix_compose_kernel(
-    int C, int G, int NG, int W, const float* __restrict__ summ, float* __restrict__ gsum) {
+// U_g for every (batch, group, element), groups numbered in processing order.
+template <int E, bool REV, class Sum>
+__global__ __launch_bounds__(CMP_THREADS) void prefix_compose_kernel(int C, int G, int NG, int W, Sum sm,
+                                                                     float* __restrict__ gsum) {
     const int w = blockIdx.x * CMP_THREADS + threadIdx.x;
     const int q = blockIdx.y, b = blockIdx.z;
     if (w >= W) return;
+    sm.bind(w);
     const int c0 = q * G;
     const int n = min(G, C - c0);
     Aff<E> acc = Aff<E>::ident();
 #pragma unroll 8
-    for (int i = 0; i < n; ++i)
-        acc = Aff<E>::load(summ, ((size_t)b * C + chunk_of(c0 + i, C, REV)) * W + w).after(acc);
+    for (int i = 0; i < n; ++i) acc = sm(b, chunk_of(c0 + i, C, REV), w).after(acc);
     acc.store(gsum, ((size_t)b * NG + q) * W + w);
 }
 
@@ -138,61 +183,70 @@ __global__ __launch_bounds__(SCAN_THREADS) void prefix_group_scan_kernel(
     }
 }
 
-// State entering every chunk of group q from the state entering the group.
-template <int E, bool REV>
-__global__ __launch_bounds__(CMP_THREADS) void prefix_expand_kernel(
-    int C, int G, int NG, int W, const float* __restrict__ summ, const float* __restrict__ gentry,
-    float* __restrict__ entries) {
+// State entering every chunk of group q from the state entering the group
+// (gentry NULL: the initial state is zero).
+template <int E, bool REV, class Sum>
+__global__ __launch_bounds__(CMP_THREADS) void prefix_expand_kernel(int C, int G, int NG, int W, Sum sm,
+                                                                    const float* __restrict__ gentry,
+                                                                    float* __restrict__ entries) {
     const int w = blockIdx.x * CMP_THREADS + threadIdx.x;
     const int q = blockIdx.y, b = blockIdx.z;
     if (w >= W) return;
+    sm.bind(w);
     const int c0 = q * G;
     const int n = min(G, C - c0);
     St<E> h = gentry ? St<E>::load(gentry, ((size_t)b * NG + q) * W + w) : St<E>::zero();
 #pragma unroll 8
     for (int i = 0; i < n; ++i) {
-        const size_t idx = ((size_t)b * C + chunk_of(c0 + i, C, REV)) * W + w;
-        const Aff<E> sc = Aff<E>::load(summ, idx);
-        h.store(entries, idx);
+        const int c = chunk_of(c0 + i, C, REV);
+        const Aff<E> sc = sm(b, c, w);
+        h.store(entries, ((size_t)b * C + c) * W + w);
         h = h.apply(sc);
     }
 }
 
-}  // namespace
-
-hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const float* summ,
-                         float* gsum, const float* init, float* entries, hipStream_t s) {
-    float* gentry = gsum + (size_t)ch.B * ch.NG * W * 2 * elem;
+template <int E, bool REV, class Sum>
+void run_prefix(const Chunking& ch, int W, Sum sm, float* gsum, const float* init, float* entries,
+                hipStream_t s) {
     const dim3 wgrid((unsigned)ceil_div(W, CMP_THREADS), ch.NG, ch.B);
+    if (ch.NG == 1) {
+        // a single group (the serial prefix): the walk starts from init itself
+        LRS_LAUNCH(K_PREFIX_ENTRIES, (prefix_expand_kernel<E, REV, Sum>), wgrid, dim3(CMP_THREADS), 0, s,
+                   ch.C, ch.G, ch.NG, W, sm, init, entries);
+        return;
+    }
+    float* gentry = gsum + (size_t)ch.B * ch.NG * W * 2 * E;
     // group slots per segment: all groups when they fit, with >= 8 elements
     // per workgroup so every group row is read as >= 8 contiguous elements
     int slots = 1;
     while (slots < ch.NG && slots < SCAN_THREADS / 8) slots <<= 1;
     const int MT = SCAN_THREADS / slots;
     const dim3 sgrid((unsigned)ceil_div(W, MT), ch.B);
-    // a single group (the serial prefix) needs no group summaries: the walk
-    // starts from the initial state itself
-    const bool serial = ch.NG == 1;
-#define PFX(EE, RR)                                                                                          \
-    do {                                                                                                     \
-        if (serial) {                                                                                        \
-            LRS_LAUNCH(K_PREFIX_ENTRIES, (prefix_expand_kernel<EE, RR>), wgrid, dim3(CMP_THREADS), 0, s,     \
-                       ch.C, ch.G, ch.NG, W, summ, init, entries);                                            \
-            break;                                                                                           \
-        }                                                                                                    \
-        LRS_LAUNCH(K_PREFIX_GROUPS, (prefix_compose_kernel<EE, RR>), wgrid, dim3(CMP_THREADS), 0, s, ch.C,   \
-                   ch.G, ch.NG, W, summ, gsum);                                                               \
-        LRS_LAUNCH(K_PREFIX_OUTER, (prefix_group_scan_kernel<EE>), sgrid, dim3(SCAN_THREADS), 0, s, ch.NG,  \
-                   W, MT, (const float*)gsum, init, gentry);                                                  \
-        LRS_LAUNCH(K_PREFIX_ENTRIES, (prefix_expand_kernel<EE, RR>), wgrid, dim3(CMP_THREADS), 0, s, ch.C,   \
-                   ch.G, ch.NG, W, summ, (const float*)gentry, entries);                                      \
-    } while (0)
+    LRS_LAUNCH(K_PREFIX_GROUPS, (prefix_compose_kernel<E, REV, Sum>), wgrid, dim3(CMP_THREADS), 0, s, ch.C,
+               ch.G, ch.NG, W, sm, gsum);
+    LRS_LAUNCH(K_PREFIX_OUTER, (prefix_group_scan_kernel<E>), sgrid, dim3(SCAN_THREADS), 0, s, ch.NG, W, MT,
+               (const float*)gsum, init, gentry);
+    LRS_LAUNCH(K_PREFIX_ENTRIES, (prefix_expand_kernel<E, REV, Sum>), wgrid, dim3(CMP_THREADS), 0, s, ch.C,
+               ch.G, ch.NG, W, sm, (const float*)gentry, entries);
+}
+
+}  // namespace
+
+hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const PrefixSummaries& sm,
+                         float* gsum, const float* init, float* entries, hipStream_t s) {
     if (elem == 2) {
-        if (reverse) PFX(2, true); else PFX(2, false);
+        if (reverse)
+            run_prefix<2, true>(ch, W, CompressedSummaries<true>{sm.bpart, (const float4*)sm.chunk,
+                                                                 (const float4*)sm.mtab, ch.C, W},
+                                gsum, init, entries, s);
+        else
+            run_prefix<2, false>(ch, W, CompressedSummaries<false>{sm.bpart, (const float4*)sm.chunk,
+                                                                   (const float4*)sm.mtab, ch.C, W},
+                                 gsum, init, entries, s);
     } else {
-        if (reverse) PFX(1, true); else PFX(1, false);
+        if (reverse) run_prefix<1, true>(ch, W, FullSummaries<1>{sm.full, ch.C, W}, gsum, init, entries, s);
+        else run_prefix<1, false>(ch, W, FullSummaries<1>{sm.full, ch.C, W}, gsum, init, entries, s);
     }
-#undef PFX
     return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@ constexpr int CTL_TOK_PER_BLOCK = CTL_WAVES * CTL_TOK;
 constexpr int CTL_SLAB = LRS_CTL_SLAB;  // 512-column slabs loaded together
 
 __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
-    int BL, int D, int M, const uint4* __restrict__ x_sel, const float* __restrict__ w_phi,
+    int BL, int D, int M, int K, int K_last, const uint4* __restrict__ x_sel, const float* __restrict__ w_phi,
     const float* __restrict__ w_r, const float* __restrict__ a_phi,
     const float* __restrict__ a_r, const float* __restrict__ nu, const float* __restrict__ theta,
     float* __restrict__ p_out, float* __restrict__ r_out, float2* __restrict__ u_out,
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     for (int m = blockIdx.x * CTL_THREADS + tid; m < M; m += gridDim.x * CTL_THREADS)
-        store_mode(mtab, m, mode_const(nu[m], theta[m]));
+        store_mode(mtab, m, mode_const(nu[m], theta[m]), chunk_phase(theta[m], K), chunk_phase(theta[m], K_last));
 
     // direction norms over all D+1 entries
     float sp = 0.f, sr = 0.f;
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
         t.E = expf(c);
         t.C = cd;
         t.S = sd;
-        t.pad = 0.f;
+        t.d = d;
         ctl[tok] = t;
     }
 }
@@ -192,34 +192,33 @@ __device__ __forceinline__ void load_chunk(Words<VM> (&w)[K], const uint32_t* __
 }
 
 // One step of the forward summary (REV = false) or of the reverse conjugate
-// summary (REV = true) for the VM modes of this lane.
+// summary (REV = true) for the VM modes of this lane: only the affine part B
+// is carried; the chunk's transition product follows from (G_c, D_c).
 template <int VM, bool REV>
-__device__ __forceinline__ void summary_step(const ModeConst (&k)[VM], cf (&A)[VM], cf (&Bv)[VM],
-                                             const TokenCtl& tc, const Words<VM>& dw) {
+__device__ __forceinline__ void summary_step(const ModeConst (&k)[VM], cf (&Bv)[VM], const TokenCtl& tc,
+                                             const Words<VM>& dw) {
 #pragma unroll
     for (int v = 0; v < VM; ++v) {
         const cf lam = mode_lambda(k[v], tc.E, tc.C, tc.S);
         const cf x = {bf16_lo(dw.w[v]), bf16_hi(dw.w[v])};
-        if (!REV) {
-            // (lam, x) o (A, B) = (lam A, lam B + x)
-            A[v] = cmul(lam, A[v]);
-            Bv[v] = cfma(lam, Bv[v], x);
-        } else {
-            // carry -> conj(lam) (x + carry)
-            A[v] = cmulc(lam, A[v]);
-            Bv[v] = cmulc(lam, {Bv[v].re + x.re, Bv[v].im + x.im});
-        }
+        if (!REV) Bv[v] = cfma(lam, Bv[v], x);                            // B -> lam B + x
+        else Bv[v] = cmulc(lam, {Bv[v].re + x.re, Bv[v].im + x.im});     // B -> conj(lam) (x + B)
     }
 }
 
 // Chunk summary S_c (or, REV, the conjugate reverse summary of the chunk),
-// one workgroup per (chunk, slice of modes).  The token controls of the chunk
-// are requested first and staged in LDS; the drive loads follow as one batch.
+// one workgroup per (chunk, slice of modes), stored compressed: the affine
+// part B per mode, and once per chunk (G_c, cos D_c, sin D_c) from which the
+// prefix rebuilds the transition product of every mode (the closed form in
+// common.hpp; the reverse product is its conjugate, so both directions write
+// the same record).  The token controls of the chunk are requested first and
+// staged in LDS; the drive loads follow as one batch.
 template <int VM, int K, bool REV, bool FULL>
 __device__ __forceinline__ void summary_chunk(TokenCtl (&sctl)[K], int L, int M, int C, int b, int c,
                                               int m0, bool active, const TokenCtl* __restrict__ ctl,
                                               const uint32_t* __restrict__ drive,
-                                              const float4* __restrict__ mtab, float* __restrict__ summ) {
+                                              const float4* __restrict__ mtab, float* __restrict__ summ,
+                                              float4* __restrict__ chunk_rec) {
     const int s = c * K;
     const int kc = FULL ? K : L - s;
     const int mc = active ? m0 : M - VM;
@@ -228,11 +227,10 @@ __device__ __forceinline__ void summary_chunk(TokenCtl (&sctl)[K], int L, int M,
     Words<VM> w[K];
     load_chunk<VM, K, FULL>(w, drive + ((size_t)b * L + s) * M, M, mc, kc);
     ModeConst k[VM];
-    cf A[VM], Bv[VM];
+    cf Bv[VM];
 #pragma unroll
     for (int v = 0; v < VM; ++v) {
         k[v] = load_mode(mtab, mc + v);
-        A[v] = {1.f, 0.f};
         Bv[v] = {0.f, 0.f};
     }
     if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
@@ -241,12 +239,23 @@ __device__ __forceinline__ void summary_chunk(TokenCtl (&sctl)[K], int L, int M,
 #pragma unroll
     for (int j = 0; j < K; ++j) {
         const int i = REV ? K - 1 - j : j;
-        if (i < kq) summary_step<VM, REV>(k, A, Bv, sctl[i], w[i]);
+        if (i < kq) summary_step<VM, REV>(k, Bv, sctl[i], w[i]);
     }
     if (active) {
-        float4* out = reinterpret_cast<float4*>(summ) + ((size_t)b * C + c) * M + m0;
+        float2* out = reinterpret_cast<float2*>(summ) + ((size_t)b * C + c) * M + m0;
 #pragma unroll
-        for (int v = 0; v < VM; ++v) out[v] = make_float4(A[v].re, A[v].im, Bv[v].re, Bv[v].im);
+        for (int v = 0; v < VM; ++v) out[v] = make_float2(Bv[v].re, Bv[v].im);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        // G_c and D_c in token order, the same in both directions
+        float G = 0.f, Dd = 0.f;
+        for (int i = 0; i < kc; ++i) {
+            G += sctl[i].E;
+            Dd += sctl[i].d;
+        }
+        float sD, cD;
+        sincosf(Dd, &sD, &cD);
+        chunk_rec[(size_t)b * C + c] = make_float4(G, cD, sD, 0.f);
     }
 }
 
@@ -255,15 +264,15 @@ __device__ __forceinline__ void summary_chunk(TokenCtl (&sctl)[K], int L, int M,
 template <int VM, int K, bool REV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void samu_summary_kernel(
     int L, int M, int C, const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
-    const float4* __restrict__ mtab, float* __restrict__ summ) {
+    const float4* __restrict__ mtab, float* __restrict__ summ, float4* __restrict__ chunk_rec) {
     __shared__ TokenCtl sctl[K];
     const int m0 = (blockIdx.x * blockDim.x + threadIdx.x) * VM;
     const int c = blockIdx.y, b = blockIdx.z;
     const bool active = m0 < M;
     if ((c + 1) * K <= L)
-        summary_chunk<VM, K, REV, true>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, summ);
+        summary_chunk<VM, K, REV, true>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, summ, chunk_rec);
     else
-        summary_chunk<VM, K, REV, false>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, summ);
+        summary_chunk<VM, K, REV, false>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, summ, chunk_rec);
 }
 
 // --------------------------------------------------------------- replay ---
@@ -364,25 +373,27 @@ inline int mode_block(int M, int VM) {
 
 }  // namespace
 
-hipError_t launch_samu_controller(const SamuParams& p, float* p_out, float* r_out, float* u_out,
-                                  float* ctl, float* mtab, hipStream_t s) {
+hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
+                                  float* u_out, float* ctl, float* mtab, hipStream_t s) {
     const int BL = p.B * p.L;
     const int grid = (int)ceil_div(BL, CTL_TOK_PER_BLOCK);
+    const int K_last = p.L - (ch.C - 1) * ch.K;
     LRS_LAUNCH(K_SAMU_CONTROLLER, samu_controller_kernel, dim3(grid), dim3(CTL_THREADS), 0, s,
-               BL, p.D, p.M, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p.nu, p.theta,
-               p_out, r_out, (float2*)u_out, (TokenCtl*)ctl, (float4*)mtab);
+               BL, p.D, p.M, ch.K, K_last, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p.nu,
+               p.theta, p_out, r_out, (float2*)u_out, (TokenCtl*)ctl, (float4*)mtab);
     return hipGetLastError();
 }
 
 hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const float* ctl,
                                const float* mtab, const void* drive, bool reverse, float* summ,
-                               hipStream_t s) {
+                               float* chunk_rec, hipStream_t s) {
     const int blk = mode_block(p.M, SUM_VM);
     const dim3 grid((unsigned)ceil_div(ceil_div(p.M, SUM_VM), blk), ch.C, ch.B);
     const int id = reverse ? K_SAMU_REV_SUMMARY : K_SAMU_SUMMARY;
 #define SUMMARY_CASE(KK, RR)                                                                        \
     LRS_LAUNCH(id, (samu_summary_kernel<SUM_VM, KK, RR>), grid, dim3(blk), 0, s, p.L, p.M, ch.C, \
-               (const TokenCtl*)ctl, (const uint32_t*)drive, (const float4*)mtab, summ)
+               (const TokenCtl*)ctl, (const uint32_t*)drive, (const float4*)mtab, summ,           \
+               (float4*)chunk_rec)
     if (ch.K == 32) {
         if (reverse) SUMMARY_CASE(32, true); else SUMMARY_CASE(32, false);
     } else {

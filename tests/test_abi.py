@@ -49,14 +49,16 @@ def test_saved_and_workspace_sizes():
     B, L, D, K = 1, 32768, 2048, 32
     M, C = D // 2, L // K
     sv = scan.samu_scan_saved_bytes(B, L, D, K)
-    # p, r, (u_phi, u_r), per-token (E, C, S) record, mode table, chunk entry states
-    need = B * L * (4 + 4 + 8 + 16) + M * 32 + B * C * M * 8
+    # p, r, (u_phi, u_r), per-token (E, C, S, d) record, mode table (four
+    # float4 per mode), chunk entry states
+    need = B * L * (4 + 4 + 8 + 16) + M * 64 + B * C * M * 8
     assert need <= sv < need + 8 * 256
-    # forward workspace: chunk summaries and group summaries (16 B per mode
-    # each), group entry states (8 B per mode)
+    # forward workspace: compressed chunk summaries (8 B per mode plus a 16 B
+    # record per chunk), group summaries (16 B per mode) and group entry
+    # states (8 B per mode)
     G = 4
     NG = C // G
-    need = B * C * M * 16 + B * NG * M * 24
+    need = B * C * M * 8 + B * C * 16 + B * NG * M * 24
     assert need <= scan.samu_scan_workspace_bytes(B, L, D, K, G, False) < need + 4 * 256
     # backward adds the per-tile controller partials [B, M/64 tiles, L, 2]
     assert scan.samu_scan_workspace_bytes(B, L, D, K, G, True) > B * (M // 64) * L * 8
