@@ -55,21 +55,22 @@ def kernel_bytes(name, B, L, D, K, G):
     NG = -(-C // effective_groups(L, K, G))
     BL, BLD, BCM = B * L, B * L * D, B * C * M
     n_tiles = -(-M // 64)
+    BC = B * C
     table = {
-        # x_sel, both direction vectors -> p, r, (u_phi, u_r), (E, C, S), mode table
-        "samu_controller": 2 * BLD + 8 * (D + 1) + 32 * BL + 32 * M,
-        # b, (E, C, S), mode table -> one affine summary per (chunk, mode)
-        "samu_chunk_summary": 2 * BLD + 16 * BL + 32 * M + 16 * BCM,
-        "samu_reverse_summary": 2 * BLD + 16 * BL + 32 * M + 16 * BCM,
-        # chunk summaries -> group summaries
-        "prefix_group_compose": 16 * BCM + 16 * B * NG * M,
+        # x_sel, both direction vectors -> p, r, (u_phi, u_r), (E, C, S, d), mode table
+        "samu_controller": 2 * BLD + 8 * (D + 1) + 32 * BL + 64 * M,
+        # b, (E, C, S, d), mode table -> B part per (chunk, mode), (G_c, e^{i D_c}) per chunk
+        "samu_chunk_summary": 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 16 * BC,
+        "samu_reverse_summary": 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 16 * BC,
+        # compressed chunk summaries, mode constants -> group summaries
+        "prefix_group_compose": 8 * BCM + 16 * BC + 48 * M + 16 * B * NG * M,
         # group summaries, initial state -> state entering every group
         "prefix_group_scan": 16 * B * NG * M + 8 * B * M + 8 * B * NG * M,
-        # group entry states, chunk summaries -> state entering every chunk
-        "prefix_chunk_entries": 8 * B * NG * M + 16 * BCM + 8 * BCM,
-        # b, (E, C, S), entry states -> y, final state
+        # group entry states, compressed chunk summaries -> state entering every chunk
+        "prefix_chunk_entries": 8 * B * NG * M + 8 * BCM + 16 * BC + 48 * M + 8 * BCM,
+        # b, (E, C, S, d), entry states -> y, final state
         "samu_replay": 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 2 * BLD + 8 * B * M,
-        # dy, b, (E, C, S), entry states, adjoint carries -> db, per-tile controller
+        # dy, b, (E, C, S, d), entry states, adjoint carries -> db, per-tile controller
         # partials, per-(chunk, mode) spectrum partials
         "samu_bwd_replay": 2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BCM + 2 * BLD
         + 8 * B * n_tiles * L + 8 * BCM,
