@@ -210,6 +210,43 @@ scan_status rglru_scan_bwd(int B, int L, int D, int K, int G,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
+ * Comparison scans of the scan-latency experiment (page "Griffin 第 4、5 节
+ * H800 对照协议", experiment-coverage matrix, the Fig. 8(a) row: the exact
+ * chunked scan against a per-channel on-chip sequential scan and
+ * associative scans, for SAMU and RG-LRU).  Forward only; same equations,
+ * arguments and output conventions as samu_scan_fwd / rglru_scan_fwd.
+ *   SCAN_BASELINE_SEQUENTIAL   one lane per (batch row, mode or channel)
+ *                              walks all L tokens in order;
+ *   SCAN_BASELINE_ASSOCIATIVE  the recursive pairwise (log-depth) scan:
+ *                              log2(L) reduce and log2(L) expand passes over
+ *                              HBM level arrays held in the workspace.
+ * These are baselines for measurement, not the fast path.
+ * ====================================================================== */
+typedef enum {
+    SCAN_BASELINE_SEQUENTIAL = 0,
+    SCAN_BASELINE_ASSOCIATIVE = 1
+} scan_baseline;
+
+/* Workspace bytes (0 = unsupported variant or shape; the RG-LRU sequential
+ * scan needs none).  The SAMU workspace holds the controller's per-token
+ * record and the mode table as well. */
+size_t samu_scan_baseline_workspace_bytes(int variant, int B, int L, int D);
+size_t rglru_scan_baseline_workspace_bytes(int variant, int B, int L, int D);
+
+scan_status samu_scan_baseline_fwd(int variant, int B, int L, int D,
+                                   const void* x_sel, const void* b,
+                                   const float* w_phi, const float* w_r,
+                                   const float* a_phi, const float* a_r,
+                                   const float* nu, const float* theta, const float* z0,
+                                   void* y, int y_dtype, float* z_final,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+scan_status rglru_scan_baseline_fwd(int variant, int B, int L, int D,
+                                    const void* x, const void* lx, const void* la,
+                                    const float* alpha, const unsigned char* reset,
+                                    const float* h0, void* y, int y_dtype, float* h_final,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
  * Per-kernel timing (page "SAMU 与 RG-LRU 的 H800 训练性能对比", section 05,
  * the backward component times; section 06 and page "SAMU
  * strengthened-baseline H800 report" count kernel launches per F+B).

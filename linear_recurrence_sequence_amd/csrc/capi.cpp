@@ -51,7 +51,7 @@ static const char* const kKernelNames[K_NUM_KERNELS] = {
     "prefix_chunk_entries", "samu_replay", "samu_reverse_summary", "samu_bwd_replay",
     "samu_controller_bwd", "samu_param_reduce", "samu_param_final", "rglru_chunk_summary",
     "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha_reduce",
-    "rglru_alpha_final", "samu_decode"};
+    "rglru_alpha_final", "samu_decode", "baseline_sequential", "baseline_associative"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 
@@ -412,6 +412,110 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     LRS_TRY(launch_samu_param_final(p, ws.g_seg, ws.mode_seg, ws.n_seg, dw_phi, dw_r, da_phi, da_r, dnu,
                                     dtheta, s),
             "samu parameter final");
+    return SCAN_OK;
+}
+
+// ---------------------------------------------------- comparison scans ---
+struct SamuBaseWs {
+    float *p, *r, *u, *ctl, *mtab, *levels;
+};
+static SamuBaseWs samu_base_layout(void* base, int B, int L, int M, int variant, size_t* bytes) {
+    Carver cv(base);
+    SamuBaseWs w{};
+    const size_t BL = (size_t)B * L;
+    w.p = cv.take<float>(BL);
+    w.r = cv.take<float>(BL);
+    w.u = cv.take<float>(BL * 2);
+    w.ctl = cv.take<float>(BL * 4);
+    w.mtab = cv.take<float>((size_t)M * 16);
+    if (variant == SCAN_BASELINE_ASSOCIATIVE) w.levels = cv.take<float>(assoc_level_maps(L) * B * M * 4);
+    if (bytes) *bytes = cv.off;
+    return w;
+}
+
+static bool base_shape(int variant, int B, int L, int D, bool samu) {
+    if (variant != SCAN_BASELINE_SEQUENTIAL && variant != SCAN_BASELINE_ASSOCIATIVE) return false;
+    if (B < 1 || B > 65535 || L < 1 || (int64_t)B * L > 0x7fffffff) return false;
+    return samu ? (D >= 8 && D % 8 == 0) : (D >= 2 && D % 2 == 0);
+}
+
+size_t samu_scan_baseline_workspace_bytes(int variant, int B, int L, int D) {
+    if (!base_shape(variant, B, L, D, true)) return 0;
+    size_t n = 0;
+    samu_base_layout(nullptr, B, L, D / 2, variant, &n);
+    return n;
+}
+
+size_t rglru_scan_baseline_workspace_bytes(int variant, int B, int L, int D) {
+    if (!base_shape(variant, B, L, D, false)) return 0;
+    return variant == SCAN_BASELINE_ASSOCIATIVE ? assoc_level_maps(L) * B * D * 2 * sizeof(float) : 0;
+}
+
+scan_status samu_scan_baseline_fwd(int variant, int B, int L, int D, const void* x_sel, const void* b,
+                                   const float* w_phi, const float* w_r, const float* a_phi,
+                                   const float* a_r, const float* nu, const float* theta, const float* z0,
+                                   void* y, int y_dtype, float* z_final, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!base_shape(variant, B, L, D, true))
+        return fail(SCAN_ERR_SHAPE, "samu_scan_baseline_fwd: unsupported variant or shape B=" +
+                                        std::to_string(B) + " L=" + std::to_string(L) + " D=" + std::to_string(D));
+    if (y_dtype != SCAN_BF16 && y_dtype != SCAN_F32)
+        return fail(SCAN_ERR_SHAPE, "samu_scan_baseline_fwd: y_dtype must be SCAN_BF16 or SCAN_F32");
+    scan_status st = check_ptrs({{x_sel, 0, "x_sel"}, {b, 0, "b"}, {w_phi, 0, "w_phi"}, {w_r, 0, "w_r"},
+                                 {a_phi, 0, "a_phi"}, {a_r, 0, "a_r"}, {nu, 0, "nu"}, {theta, 0, "theta"},
+                                 {y, 0, "y"}, {workspace, 0, "workspace"}},
+                                {{z0, 0, "z0"}, {z_final, 0, "z_final"}});
+    if (st != SCAN_OK) return st;
+    const int M = D / 2;
+    size_t need = 0;
+    samu_base_layout(nullptr, B, L, M, variant, &need);
+    if (workspace_bytes < need)
+        return fail(SCAN_ERR_WORKSPACE, "samu_scan_baseline_fwd: workspace_bytes " +
+                                            std::to_string(workspace_bytes) + " < " + std::to_string(need));
+    const size_t BL = (size_t)B * L, BLM = BL * M;
+    st = check_alias({{x_sel, BL * D * 2, "x_sel"}, {b, BLM * 4, "b"}, {w_phi, (size_t)(D + 1) * 4, "w_phi"},
+                      {w_r, (size_t)(D + 1) * 4, "w_r"}, {a_phi, 4, "a_phi"}, {a_r, 4, "a_r"},
+                      {nu, (size_t)M * 4, "nu"}, {theta, (size_t)M * 4, "theta"}, {z0, (size_t)B * M * 8, "z0"}},
+                     {{y, BLM * 2 * (y_dtype == SCAN_F32 ? 4 : 2), "y"}, {z_final, (size_t)B * M * 8, "z_final"},
+                      {workspace, need, "workspace"}});
+    if (st != SCAN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    Chunking ch;
+    chunking(B, L, 32, 0, kSamuMinGroup, &ch);  // the controller's chunk phasors are not used here
+    SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
+    SamuBaseWs ws = samu_base_layout(workspace, B, L, M, variant, nullptr);
+    LRS_TRY(launch_samu_controller(p, ch, ws.p, ws.r, ws.u, ws.ctl, ws.mtab, s), "samu controller");
+    LRS_TRY(launch_samu_baseline(variant, p, ws.ctl, ws.mtab, ws.levels, y, y_dtype == SCAN_F32, z_final, s),
+            "samu comparison scan");
+    return SCAN_OK;
+}
+
+scan_status rglru_scan_baseline_fwd(int variant, int B, int L, int D, const void* x, const void* lx,
+                                    const void* la, const float* alpha, const unsigned char* reset,
+                                    const float* h0, void* y, int y_dtype, float* h_final, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (!base_shape(variant, B, L, D, false))
+        return fail(SCAN_ERR_SHAPE, "rglru_scan_baseline_fwd: unsupported variant or shape B=" +
+                                        std::to_string(B) + " L=" + std::to_string(L) + " D=" + std::to_string(D));
+    if (y_dtype != SCAN_BF16 && y_dtype != SCAN_F32)
+        return fail(SCAN_ERR_SHAPE, "rglru_scan_baseline_fwd: y_dtype must be SCAN_BF16 or SCAN_F32");
+    const size_t need = rglru_scan_baseline_workspace_bytes(variant, B, L, D);
+    scan_status st = check_ptrs({{x, 0, "x"}, {lx, 0, "lx"}, {la, 0, "la"}, {alpha, 0, "alpha"}, {y, 0, "y"}},
+                                {{h0, 0, "h0"}, {h_final, 0, "h_final"}, {workspace, 0, "workspace"}});
+    if (st != SCAN_OK) return st;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SCAN_ERR_WORKSPACE, "rglru_scan_baseline_fwd: workspace_bytes " +
+                                            std::to_string(workspace_bytes) + " < " + std::to_string(need));
+    const size_t BL = (size_t)B * L, BLD = BL * D;
+    st = check_alias({{x, BLD * 2, "x"}, {lx, BLD * 2, "lx"}, {la, BLD * 2, "la"}, {alpha, (size_t)D * 4, "alpha"},
+                      {reset, BL, "reset"}, {h0, (size_t)B * D * 4, "h0"}},
+                     {{y, BLD * (y_dtype == SCAN_F32 ? 4 : 2), "y"}, {h_final, (size_t)B * D * 4, "h_final"},
+                      {need ? workspace : nullptr, need, "workspace"}});
+    if (st != SCAN_OK) return st;
+    RglruParams p{B, L, D, x, lx, la, alpha, reset, h0};
+    LRS_TRY(launch_rglru_baseline(variant, p, (float*)workspace, y, y_dtype == SCAN_F32, h_final,
+                                  (hipStream_t)stream),
+            "rglru comparison scan");
     return SCAN_OK;
 }
 

@@ -33,6 +33,8 @@ enum KernelId {
     K_RGLRU_ALPHA_REDUCE,
     K_RGLRU_ALPHA_FINAL,
     K_SAMU_DECODE,
+    K_BASE_SEQ,
+    K_BASE_ASSOC,
     K_NUM_KERNELS
 };
 
@@ -157,5 +159,14 @@ int rglru_alpha_segments(int B, int C);
 hipError_t launch_rglru_alpha_reduce(const RglruParams& p, const Chunking& ch,
                                      const float* alpha_part, double* seg, int n_seg,
                                      float* dalpha, hipStream_t s);
+
+// ------------------------------------------------------ comparison scans ---
+// variant 0: per-channel sequential scan; 1: associative (recursive pairwise)
+// scan over `levels` (assoc_level_maps(L) maps per batch row and element).
+size_t assoc_level_maps(int L);
+hipError_t launch_samu_baseline(int variant, const SamuParams& p, const float* ctl, const float* mtab,
+                                float* levels, void* y, int y_f32, float* z_final, hipStream_t s);
+hipError_t launch_rglru_baseline(int variant, const RglruParams& p, float* levels, void* y, int y_f32,
+                                 float* h_final, hipStream_t s);
 
 }  // namespace lrs

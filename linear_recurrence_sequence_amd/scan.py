@@ -51,6 +51,13 @@ def lib():
     L.samu_scan_fwd.restype = i
     L.samu_scan_bwd.argtypes = [i] * 5 + [vp] * 8 + [vp, vp, vp, vp, vp, i, vp] + [vp] * 6 + [vp, sz, vp]
     L.samu_scan_bwd.restype = i
+    for n in ("samu_scan_baseline_workspace_bytes", "rglru_scan_baseline_workspace_bytes"):
+        getattr(L, n).argtypes = [i, i, i, i]
+        getattr(L, n).restype = sz
+    L.samu_scan_baseline_fwd.argtypes = [i] * 4 + [vp] * 9 + [vp, i, vp, vp, sz, vp]
+    L.samu_scan_baseline_fwd.restype = i
+    L.rglru_scan_baseline_fwd.argtypes = [i] * 4 + [vp] * 6 + [vp, i, vp, vp, sz, vp]
+    L.rglru_scan_baseline_fwd.restype = i
     L.samu_scan_decode.argtypes = [i, i] + [vp] * 10 + [vp, i, vp]
     L.samu_scan_decode.restype = i
     L.rglru_scan_fwd.argtypes = [i] * 5 + [vp] * 6 + [vp, i, vp, vp, vp, sz, vp]
@@ -192,6 +199,52 @@ def samu_scan_decode(x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z=None, *,
                                 _stream(stream))
     _check(st, "samu_scan_decode")
     return y, z_out
+
+
+BASELINES = {"sequential": 0, "associative": 1}
+
+
+def samu_scan_baseline_fwd(variant, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0=None, *,
+                           y_dtype=torch.bfloat16, y=None, z_final=None, workspace=None, stream=None):
+    """Comparison scan (variant "sequential" or "associative"), forward only.
+    Returns (y [B,L,M,2], z_final [B,M,2] f32)."""
+    v = BASELINES[variant]
+    B, L, D = x_sel.shape
+    M = D // 2
+    dev = x_sel.device
+    if y is None:
+        y = torch.empty((B, L, M, 2), dtype=y_dtype, device=dev)
+    if z_final is None:
+        z_final = torch.empty((B, M, 2), dtype=torch.float32, device=dev)
+    n = lib().samu_scan_baseline_workspace_bytes(v, B, L, D)
+    if workspace is None:
+        workspace = _bytes(n, dev)
+    st = lib().samu_scan_baseline_fwd(v, B, L, D, _p(x_sel), _p(b), _p(w_phi), _p(w_r), _p(a_phi),
+                                      _p(a_r), _p(nu), _p(theta), _p(z0), _p(y), _code(y.dtype),
+                                      _p(z_final), _p(workspace), workspace.numel(), _stream(stream))
+    _check(st, "samu_scan_baseline_fwd")
+    return y, z_final
+
+
+def rglru_scan_baseline_fwd(variant, x, lx, la, alpha, reset=None, h0=None, *, y_dtype=torch.bfloat16,
+                            y=None, h_final=None, workspace=None, stream=None):
+    """Comparison scan (variant "sequential" or "associative"), forward only.
+    Returns (y [B,L,D], h_final [B,D] f32)."""
+    v = BASELINES[variant]
+    B, L, D = x.shape
+    dev = x.device
+    if y is None:
+        y = torch.empty((B, L, D), dtype=y_dtype, device=dev)
+    if h_final is None:
+        h_final = torch.empty((B, D), dtype=torch.float32, device=dev)
+    n = lib().rglru_scan_baseline_workspace_bytes(v, B, L, D)
+    if workspace is None and n > 0:
+        workspace = _bytes(n, dev)
+    st = lib().rglru_scan_baseline_fwd(v, B, L, D, _p(x), _p(lx), _p(la), _p(alpha), _p(reset), _p(h0),
+                                       _p(y), _code(y.dtype), _p(h_final), _p(workspace),
+                                       0 if workspace is None else workspace.numel(), _stream(stream))
+    _check(st, "rglru_scan_baseline_fwd")
+    return y, h_final
 
 
 def rglru_scan_fwd(x, lx, la, alpha, reset=None, h0=None, *, K=16, G=0, y_dtype=torch.bfloat16,

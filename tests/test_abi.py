@@ -150,3 +150,25 @@ def test_samu_decode_rejects_before_enqueue(over, status):
     from linear_recurrence_sequence_amd import scan
     assert _call_decode(**over) == status
     assert scan.lib().scan_last_error().decode()
+
+
+def test_baseline_scans_reject_before_enqueue():
+    from linear_recurrence_sequence_amd import scan
+    L = scan.lib()
+    f = _fake
+    # sizes: the associative scan keeps its level arrays; the sequential RG-LRU scan needs none
+    assert L.samu_scan_baseline_workspace_bytes(2, 1, 64, 16) == 0               # unknown variant
+    assert L.samu_scan_baseline_workspace_bytes(0, 1, 64, 12) == 0               # D % 8
+    assert L.samu_scan_baseline_workspace_bytes(1, 2, 64, 16) > L.samu_scan_baseline_workspace_bytes(0, 2, 64, 16)
+    assert L.rglru_scan_baseline_workspace_bytes(0, 2, 64, 16) == 0
+    assert L.rglru_scan_baseline_workspace_bytes(1, 2, 64, 16) == (32 + 16 + 8 + 4 + 2 + 1) * 2 * 16 * 8
+    p = [f(0x100000), f(0x200000), f(0x300000), f(0x300100), f(0x300200), f(0x300210), f(0x300300),
+         f(0x300400)]
+    ws = L.samu_scan_baseline_workspace_bytes(1, 1, 64, 16)
+    assert L.samu_scan_baseline_fwd(5, 1, 64, 16, *p, None, f(0x400000), 0, None, f(0x600000), ws, None) == -2
+    assert L.samu_scan_baseline_fwd(1, 1, 64, 16, *p, None, f(0x400000), 0, None, f(0x600000), 8, None) == -4
+    assert L.samu_scan_baseline_fwd(1, 1, 64, 16, *p, None, f(0x100000), 0, None, f(0x600000), ws, None) == -6
+    r = [f(0x100000), f(0x200000), f(0x300000), f(0x400000)]
+    assert L.rglru_scan_baseline_fwd(0, 1, 8, 3, *r, None, None, f(0x500000), 0, None, None, 0, None) == -2
+    assert L.rglru_scan_baseline_fwd(1, 1, 8, 4, *r, None, None, f(0x500000), 0, None, None, 0, None) == -4
+    assert L.rglru_scan_baseline_fwd(0, 1, 8, 4, *r, None, None, f(0x200000), 0, None, None, 0, None) == -6
