@@ -158,6 +158,53 @@ def cpu_baseline(sample_L, reps=3):
                        f"seed and distributions; floor bytes / median wall time of {reps} runs")}
 
 
+def scan_latency_sweep(torch, inputs, scan, dev, timed, B=8, D=1024, Ls=(2048, 4096, 8192, 16384)):
+    """Forward scan latency at B=8, D=1024 over L (the pages' Fig. 8(a)
+    shapes): the chunked scan against the per-channel sequential and the
+    recursive associative comparison scans, for SAMU and RG-LRU, in ms."""
+    log("[bench] scan-latency sweep (forward, B=8, D=1024)")
+    Lmax = max(Ls)
+    si = inputs.samu_inputs(B, Lmax, D, seed=1004, with_dy=False)
+    ri = inputs.rglru_inputs(B, Lmax, D, seed=1104, with_dy=False)
+    sd = {k: dev(v) for k, v in si.items()}
+    rd = {k: dev(v) for k, v in ri.items()}
+    M = D // 2
+    out = {}
+    for L in Ls:
+        xs, bs = sd["x_sel"][:, :L].contiguous(), sd["b"][:, :L].contiguous()
+        pr = (sd["w_phi"], sd["w_r"], sd["a_phi"], sd["a_r"], sd["nu"], sd["theta"])
+        x, lx, la = (rd[k][:, :L].contiguous() for k in ("x", "lx", "la"))
+        y = torch.empty((B, L, M, 2), dtype=torch.bfloat16, device="cuda")
+        ry = torch.empty((B, L, D), dtype=torch.bfloat16, device="cuda")
+        zf = torch.empty((B, M, 2), dtype=torch.float32, device="cuda")
+        hf = torch.empty((B, D), dtype=torch.float32, device="cuda")
+        saved = torch.empty(scan.samu_scan_saved_bytes(B, L, D, 32), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(scan.samu_scan_workspace_bytes(B, L, D, 32, 0, False), dtype=torch.uint8, device="cuda")
+        rsaved = torch.empty(scan.rglru_scan_saved_bytes(B, L, D, 16), dtype=torch.uint8, device="cuda")
+        rws = torch.empty(scan.rglru_scan_workspace_bytes(B, L, D, 16, 0, False), dtype=torch.uint8, device="cuda")
+        row = {}
+        row["samu_chunked"] = timed(lambda: scan.samu_scan_fwd(xs, bs, *pr, None, K=32, G=0, y=y, z_final=zf,
+                                                                saved=saved, workspace=ws), 10, 2, False)[0]
+        row["rglru_chunked"] = timed(lambda: scan.rglru_scan_fwd(x, lx, la, rd["alpha"], None, None, K=16, G=0,
+                                                                 y=ry, h_final=hf, saved=rsaved, workspace=rws),
+                                     10, 2, False)[0]
+        for v in ("sequential", "associative"):
+            sw = torch.empty(max(1, scan.lib().samu_scan_baseline_workspace_bytes(scan.BASELINES[v], B, L, D)),
+                             dtype=torch.uint8, device="cuda")
+            n = scan.lib().rglru_scan_baseline_workspace_bytes(scan.BASELINES[v], B, L, D)
+            rw = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+            row[f"samu_{v}"] = timed(lambda: scan.samu_scan_baseline_fwd(v, xs, bs, *pr, None, y=y, z_final=zf,
+                                                                          workspace=sw), 5, 1, False)[0]
+            row[f"rglru_{v}"] = timed(lambda: scan.rglru_scan_baseline_fwd(v, x, lx, la, rd["alpha"], None, None,
+                                                                           y=ry, h_final=hf, workspace=rw),
+                                      5, 1, False)[0]
+            del sw, rw
+        out[f"L{L}"] = {k: round(v, 4) for k, v in row.items()}
+        log(f"    L={L}: " + " ".join(f"{k}={v:.3f}" for k, v in row.items()) + " ms")
+        del y, ry, saved, ws, rsaved, rws
+    return {"B": B, "D": D, "unit": "ms", "direction": "forward", "by_L": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +214,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rglru", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the scan library has no multi-GPU path "
@@ -326,6 +374,10 @@ def main():
             log(f"    B={Bd}: {dms * 1e3:.2f} us/step eager, {gms * 1e3 / 32:.2f} us/step from a graph "
                 f"({kus:.2f} us kernel with events, {nbytes} B)")
 
+    sweep = None
+    if not args.no_sweep:
+        sweep = scan_latency_sweep(torch, inputs, scan, dev, timed)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle F+B over L={args.cpu_sample_L}")
@@ -359,6 +411,7 @@ def main():
         "kernels": kernels,
         "rglru": rg,
         "decode": dec,
+        "scan_latency_sweep": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
