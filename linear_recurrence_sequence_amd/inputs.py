@@ -96,6 +96,22 @@ def rglru_inputs(B, L, D, seed, *, reset_p=0.0, h0_std=None, dh_final_std=None,
     return out
 
 
+def rglru_proj_inputs(D, seed):
+    """Weights of the two 16-block block-diagonal gate projections: w_x, w_a
+    bf16 [16, D/16, D/16] (block, output, input) ~ N(0, 1/(D/16)) so the
+    logits keep unit scale for unit inputs; b_x, b_a f32 [D] ~ N(0, 0.1^2)."""
+    if D % 16:
+        raise ValueError("D must be a multiple of 16")
+    Db = D // 16
+    rng = _rng(seed)
+    out = {}
+    for g in ("x", "a"):
+        w = rng.standard_normal((16, Db, Db), dtype=np.float32) / np.float32(math.sqrt(Db))
+        out["w_" + g] = bf16_bits(w)
+        out["b_" + g] = (0.1 * rng.standard_normal(D)).astype(np.float32)
+    return out
+
+
 # Workloads the pages measure (seed = 1000 * workload index + row index).
 WORKLOADS = {
     "samu_b1_l2048_d1024": dict(kind="samu", B=1, L=2048, D=1024, seed=0),

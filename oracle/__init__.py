@@ -52,6 +52,8 @@ def _load():
     i, d = ctypes.c_int, ctypes.c_double
     n64, n8 = _Nullable(np.float64), _Nullable(np.uint8)
     P = _f64p
+    lib.oracle_rglru_gate_proj.argtypes = [i, i, i, P, P, P, P]
+    lib.oracle_rglru_gate_proj_bwd.argtypes = [i, i, i, P, P, P, P, P, P]
     lib.oracle_max_threads.restype = i
     lib.oracle_set_threads.argtypes = [i]
     lib.oracle_samu_controller.argtypes = [i, i, i, P, P, P, d, d] + [P] * 7
@@ -169,3 +171,28 @@ def rglru_bwd(x, lx, la, alpha, reset, h0, dy, dh_final=None):
     lib.oracle_rglru_bwd(B, L, D, xx, widen(lx), widen(la), widen(alpha), _reset_u8(reset),
                          widen(h0), widen(dy), widen(dh_final), dx, dlx, dla, dal, dh0)
     return dict(dx=dx, dlx=dlx, dla=dla, dalpha=dal, dh0=dh0)
+
+
+def rglru_gate_proj(x, w, bias):
+    """Block-diagonal gate projection (16 blocks): x [B, L, D], w [16, D/16,
+    D/16] as (block, output, input), bias [D] -> FP64 logits [B, L, D]."""
+    x, w, bias = widen(x), widen(w), widen(bias)
+    B, L, D = x.shape
+    if D % 16 or w.shape != (16, D // 16, D // 16) or bias.shape != (D,):
+        raise ValueError("expected D % 16 == 0, w [16, D/16, D/16] and bias [D]")
+    out = np.empty((B, L, D), np.float64)
+    _load().oracle_rglru_gate_proj(B, L, D, x, w, bias, out)
+    return out
+
+
+def rglru_gate_proj_bwd(x, w, dl, dx=None):
+    """Adjoint of rglru_gate_proj for the logit cotangent dl [B, L, D]:
+    returns (dx + W^T dl per block, dW [16, D/16, D/16], dbias [D]); dx
+    (FP64, optional) is the gradient already collected for x."""
+    x, w, dl = widen(x), widen(w), widen(dl)
+    B, L, D = x.shape
+    dxo = np.zeros((B, L, D), np.float64) if dx is None else np.array(widen(dx), np.float64, copy=True)
+    dw = np.empty((16, D // 16, D // 16), np.float64)
+    db = np.empty((D,), np.float64)
+    _load().oracle_rglru_gate_proj_bwd(B, L, D, x, w, dl, dxo, dw, db)
+    return dxo, dw, db

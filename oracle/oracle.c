@@ -417,3 +417,62 @@ void oracle_rglru_bwd(int B, int L, int D, const double *x, const double *lx,
         free(hh);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* RG-LRU gate projections ([PROTOCOL] "RG-LRU 的固定方程": both gates come   */
+/* from 16-block block-diagonal linear layers).  Reading: block i covers     */
+/* channels [i Db, (i+1) Db) with Db = D/16, the weight is stored [16, Db,   */
+/* Db] as (block, output, input), and each channel has a bias:               */
+/*   l[t, i Db + o] = bias[i Db + o] + sum_k W[i][o][k] x[t, i Db + k].      */
+/* ------------------------------------------------------------------------ */
+void oracle_rglru_gate_proj(int B, int L, int D, const double *x, const double *w,
+                            const double *bias, double *out)
+{
+    const int Db = D / 16;
+    const long BL = (long)B * L;
+#pragma omp parallel for schedule(static)
+    for (long bt = 0; bt < BL; ++bt) {
+        for (int i = 0; i < 16; ++i) {
+            const double *xb = x + bt * D + (long)i * Db;
+            for (int o = 0; o < Db; ++o) {
+                const double *wr = w + ((long)i * Db + o) * Db;
+                double s = bias[i * Db + o];
+                for (int k = 0; k < Db; ++k) s += wr[k] * xb[k];
+                out[bt * D + (long)i * Db + o] = s;
+            }
+        }
+    }
+}
+
+/* Adjoint of the projection for a cotangent dl of l:                        */
+/*   dx[t, i Db + k] += sum_o W[i][o][k] dl[t, i Db + o]    (accumulated),   */
+/*   dW[i][o][k] = sum_t dl[t, i Db + o] x[t, i Db + k],  dbias = sum_t dl.  */
+void oracle_rglru_gate_proj_bwd(int B, int L, int D, const double *x, const double *w,
+                                const double *dl, double *dx, double *dw, double *dbias)
+{
+    const int Db = D / 16;
+    const long BL = (long)B * L;
+#pragma omp parallel for schedule(static)
+    for (long bt = 0; bt < BL; ++bt) {
+        for (int i = 0; i < 16; ++i) {
+            for (int k = 0; k < Db; ++k) {
+                double s = 0.0;
+                for (int o = 0; o < Db; ++o)
+                    s += w[((long)i * Db + o) * Db + k] * dl[bt * D + (long)i * Db + o];
+                dx[bt * D + (long)i * Db + k] += s;
+            }
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < D; ++c) {
+        const int i = c / Db, o = c - i * Db;
+        double sb = 0.0;
+        for (long bt = 0; bt < BL; ++bt) sb += dl[bt * D + c];
+        dbias[c] = sb;
+        for (int k = 0; k < Db; ++k) {
+            double s = 0.0;
+            for (long bt = 0; bt < BL; ++bt) s += dl[bt * D + c] * x[bt * D + (long)i * Db + k];
+            dw[((long)i * Db + o) * Db + k] = s;
+        }
+    }
+}

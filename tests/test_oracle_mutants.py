@@ -41,6 +41,14 @@ MUTANTS = {
     "dalpha_chain": ("galpha += abar * k.a * (-8.0 * k.ga) * dsp;", "galpha += abar * k.a * (-8.0 * k.ga) * sp;"),
     "sqrt_cap_constant": ("#define RGLRU_SQRT_GRAD_UMIN 2.5e-7", "#define RGLRU_SQRT_GRAD_UMIN 1e-6"),
     "dx_without_multiplier": ("dx[o] = g * k.gx * k.m;", "dx[o] = g * k.gx;"),
+    "proj_weight_transposed": ("const double *wr = w + ((long)i * Db + o) * Db;\n                double s = bias[i * Db + o];\n                for (int k = 0; k < Db; ++k) s += wr[k] * xb[k];",
+                               "const double *wr = w + (long)i * Db * Db + o;\n                double s = bias[i * Db + o];\n                for (int k = 0; k < Db; ++k) s += wr[(long)k * Db] * xb[k];"),
+    "proj_bias_dropped": ("double s = bias[i * Db + o];\n                for (int k = 0; k < Db; ++k) s += wr[k] * xb[k];",
+                          "double s = 0.0;\n                for (int k = 0; k < Db; ++k) s += wr[k] * xb[k];"),
+    "proj_block_offset": ("const double *xb = x + bt * D + (long)i * Db;", "const double *xb = x + bt * D;"),
+    "proj_adjoint_not_transposed": ("s += w[((long)i * Db + o) * Db + k] * dl[bt * D + (long)i * Db + o];",
+                                    "s += w[((long)i * Db + k) * Db + o] * dl[bt * D + (long)i * Db + o];"),
+    "proj_dw_wrong_input": ("s += dl[bt * D + c] * x[bt * D + (long)i * Db + k];", "s += dl[bt * D + c] * x[bt * D + c];"),
 }
 
 
@@ -56,6 +64,7 @@ def test_mutant_is_caught(name, tmp_path):
                     str(c), "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_samu.py", "tests/test_oracle_rglru.py"],
+                        "tests/test_oracle_samu.py", "tests/test_oracle_rglru.py",
+                        "tests/test_oracle_rglru_proj.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived the oracle pins"
