@@ -210,6 +210,38 @@ scan_status rglru_scan_bwd(int B, int L, int D, int K, int G,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
+ * RG-LRU gate projections (page "Griffin 第 4、5 节 H800 对照协议",
+ * "RG-LRU 的固定方程": both gates come from 16-block block-diagonal linear
+ * layers).  With Db = D/16 and block i covering channels [i Db, (i+1) Db):
+ *   l[t, i Db + o] = b[i Db + o] + sum_k W[i][o][k] x[t, i Db + k],
+ * for (l^x; W_x, b_x) and (l^a; W_a, b_a).  BF16 matrix-core products with
+ * FP32 accumulation; the logits are rounded to BF16 (nearest even), the
+ * input format of rglru_scan_fwd.  Needs D a multiple of 256, D <= 2560.
+ *   x         bf16 [B, L, D]
+ *   w_x, w_a  bf16 [16, D/16, D/16]  (block, output, input)
+ *   b_x, b_a  f32 [D]
+ *   lx, la    bf16 [B, L, D]        (written) */
+scan_status rglru_gate_proj_fwd(int B, int L, int D, const void* x,
+                                const void* w_x, const float* b_x,
+                                const void* w_a, const float* b_a,
+                                void* lx, void* la, void* stream);
+
+/* Adjoint of the projections for the logit cotangents dlx, dla (as written
+ * by rglru_scan_bwd, of grad_dtype):
+ *   dx_out = dx_in + per block W_x^T dlx + W_a^T dla   ([B, L, D], grad_dtype;
+ *            dx_out may equal dx_in, must not overlap it otherwise),
+ *   dw = sum_t dl x^T per block (f32 [16, D/16, D/16]), db = sum_t dl (f32 [D]).
+ * SCAN_F32 cotangents use FP32 matrix-core products; the token sums are
+ * split over fixed ranges and added in range order (deterministic). */
+size_t rglru_gate_proj_bwd_workspace_bytes(int B, int L, int D);
+scan_status rglru_gate_proj_bwd(int B, int L, int D, const void* x,
+                                const void* w_x, const void* w_a,
+                                const void* dlx, const void* dla, int grad_dtype,
+                                const void* dx_in, void* dx_out,
+                                float* dw_x, float* db_x, float* dw_a, float* db_a,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
  * Comparison scans of the scan-latency experiment (page "Griffin 第 4、5 节
  * H800 对照协议", experiment-coverage matrix, the Fig. 8(a) row: the exact
  * chunked scan against a per-channel on-chip sequential scan and

@@ -51,7 +51,8 @@ static const char* const kKernelNames[K_NUM_KERNELS] = {
     "prefix_chunk_entries", "samu_replay", "samu_reverse_summary", "samu_bwd_replay",
     "samu_controller_bwd", "samu_param_reduce", "samu_param_final", "rglru_chunk_summary",
     "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha_reduce",
-    "rglru_alpha_final", "samu_decode", "baseline_sequential", "baseline_associative"};
+    "rglru_alpha_final", "samu_decode", "baseline_sequential", "baseline_associative",
+    "gate_projection", "gate_projection_bwd"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 
@@ -516,6 +517,83 @@ scan_status rglru_scan_baseline_fwd(int variant, int B, int L, int D, const void
     LRS_TRY(launch_rglru_baseline(variant, p, (float*)workspace, y, y_dtype == SCAN_F32, h_final,
                                   (hipStream_t)stream),
             "rglru comparison scan");
+    return SCAN_OK;
+}
+
+// --------------------------------------------- RG-LRU gate projections ---
+static bool proj_shape(int B, int L, int D) {
+    return B >= 1 && L >= 1 && (int64_t)B * L <= 0x7fffffff && D >= 256 && D <= 2560 && D % 256 == 0;
+}
+
+static void proj_bwd_layout(int BL, int D, float** dw_part, float** db_part, void* base, size_t* bytes) {
+    Carver cv(base);
+    const int nr = gate_proj_ranges(BL), Db = D / 16;
+    float* a = cv.take<float>((size_t)nr * 2 * 16 * Db * Db);
+    float* b = cv.take<float>((size_t)nr * 2 * D);
+    if (dw_part) *dw_part = a;
+    if (db_part) *db_part = b;
+    if (bytes) *bytes = cv.off;
+}
+
+size_t rglru_gate_proj_bwd_workspace_bytes(int B, int L, int D) {
+    if (!proj_shape(B, L, D)) return 0;
+    size_t n = 0;
+    proj_bwd_layout(B * L, D, nullptr, nullptr, nullptr, &n);
+    return n;
+}
+
+scan_status rglru_gate_proj_fwd(int B, int L, int D, const void* x, const void* w_x, const float* b_x,
+                                const void* w_a, const float* b_a, void* lx, void* la, void* stream) {
+    if (!proj_shape(B, L, D))
+        return fail(SCAN_ERR_SHAPE, "rglru_gate_proj_fwd: unsupported shape B=" + std::to_string(B) + " L=" +
+                                        std::to_string(L) + " D=" + std::to_string(D) +
+                                        " (need D a multiple of 256, 256 <= D <= 2560)");
+    scan_status st = check_ptrs({{x, 0, "x"}, {w_x, 0, "w_x"}, {b_x, 0, "b_x"}, {w_a, 0, "w_a"}, {b_a, 0, "b_a"},
+                                 {lx, 0, "lx"}, {la, 0, "la"}},
+                                {});
+    if (st != SCAN_OK) return st;
+    const size_t BLD = (size_t)B * L * D, W = (size_t)D * (D / 16) * 2;
+    st = check_alias({{x, BLD * 2, "x"}, {w_x, W, "w_x"}, {b_x, (size_t)D * 4, "b_x"}, {w_a, W, "w_a"},
+                      {b_a, (size_t)D * 4, "b_a"}},
+                     {{lx, BLD * 2, "lx"}, {la, BLD * 2, "la"}});
+    if (st != SCAN_OK) return st;
+    LRS_TRY(launch_gate_proj_fwd(B * L, D, x, w_x, b_x, w_a, b_a, lx, la, (hipStream_t)stream),
+            "rglru gate projection");
+    return SCAN_OK;
+}
+
+scan_status rglru_gate_proj_bwd(int B, int L, int D, const void* x, const void* w_x, const void* w_a,
+                                const void* dlx, const void* dla, int grad_dtype, const void* dx_in, void* dx_out,
+                                float* dw_x, float* db_x, float* dw_a, float* db_a, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (!proj_shape(B, L, D))
+        return fail(SCAN_ERR_SHAPE, "rglru_gate_proj_bwd: unsupported shape B=" + std::to_string(B) + " L=" +
+                                        std::to_string(L) + " D=" + std::to_string(D));
+    if (grad_dtype != SCAN_BF16 && grad_dtype != SCAN_F32)
+        return fail(SCAN_ERR_SHAPE, "rglru_gate_proj_bwd: grad_dtype must be SCAN_BF16 or SCAN_F32");
+    scan_status st = check_ptrs({{x, 0, "x"}, {w_x, 0, "w_x"}, {w_a, 0, "w_a"}, {dlx, 0, "dlx"}, {dla, 0, "dla"},
+                                 {dx_in, 0, "dx_in"}, {dx_out, 0, "dx_out"}, {dw_x, 0, "dw_x"}, {db_x, 0, "db_x"},
+                                 {dw_a, 0, "dw_a"}, {db_a, 0, "db_a"}, {workspace, 0, "workspace"}},
+                                {});
+    if (st != SCAN_OK) return st;
+    size_t need = 0;
+    proj_bwd_layout(B * L, D, nullptr, nullptr, nullptr, &need);
+    if (workspace_bytes < need)
+        return fail(SCAN_ERR_WORKSPACE, "rglru_gate_proj_bwd: workspace_bytes " + std::to_string(workspace_bytes) +
+                                            " < " + std::to_string(need));
+    const size_t BLD = (size_t)B * L * D, W = (size_t)D * (D / 16) * 2, g = grad_dtype == SCAN_F32 ? 4 : 2;
+    std::vector<Span> ins = {{x, BLD * 2, "x"}, {w_x, W, "w_x"}, {w_a, W, "w_a"}, {dlx, BLD * g, "dlx"},
+                             {dla, BLD * g, "dla"}};
+    // dx may be accumulated in place (dx_out == dx_in), never partly overlapped
+    if (dx_in != dx_out) ins.push_back({dx_in, BLD * g, "dx_in"});
+    st = check_alias(ins, {{dx_out, BLD * g, "dx_out"}, {dw_x, W * 2, "dw_x"}, {db_x, (size_t)D * 4, "db_x"},
+                           {dw_a, W * 2, "dw_a"}, {db_a, (size_t)D * 4, "db_a"}, {workspace, need, "workspace"}});
+    if (st != SCAN_OK) return st;
+    float *dw_part, *db_part;
+    proj_bwd_layout(B * L, D, &dw_part, &db_part, workspace, nullptr);
+    LRS_TRY(launch_gate_proj_bwd(B * L, D, x, w_x, w_a, dlx, dla, grad_dtype == SCAN_F32, dx_in, dx_out, dw_x, db_x,
+                                 dw_a, db_a, dw_part, db_part, (hipStream_t)stream),
+            "rglru gate projection backward");
     return SCAN_OK;
 }
 

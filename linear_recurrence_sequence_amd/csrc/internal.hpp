@@ -35,6 +35,8 @@ enum KernelId {
     K_SAMU_DECODE,
     K_BASE_SEQ,
     K_BASE_ASSOC,
+    K_GATE_PROJ,
+    K_GATE_PROJ_BWD,
     K_NUM_KERNELS
 };
 
@@ -168,5 +170,16 @@ hipError_t launch_samu_baseline(int variant, const SamuParams& p, const float* c
                                 float* levels, void* y, int y_f32, float* z_final, hipStream_t s);
 hipError_t launch_rglru_baseline(int variant, const RglruParams& p, float* levels, void* y, int y_f32,
                                  float* h_final, hipStream_t s);
+
+// ------------------------------------------------ RG-LRU gate projections ---
+// 16-block block-diagonal projections x -> l^x, l^a (BF16) and their adjoint;
+// dw_part / db_part: gate_proj_ranges(BL) x [2][16][Db][Db] / [2][D] floats.
+int gate_proj_ranges(int BL);
+hipError_t launch_gate_proj_fwd(int BL, int D, const void* x, const void* w_x, const float* b_x,
+                                const void* w_a, const float* b_a, void* lx, void* la, hipStream_t s);
+hipError_t launch_gate_proj_bwd(int BL, int D, const void* x, const void* w_x, const void* w_a, const void* dlx,
+                                const void* dla, int f32, const void* dx_in, void* dx_out, float* dw_x,
+                                float* db_x, float* dw_a, float* db_a, float* dw_part, float* db_part,
+                                hipStream_t s);
 
 }  // namespace lrs

@@ -58,6 +58,12 @@ def lib():
     L.samu_scan_baseline_fwd.restype = i
     L.rglru_scan_baseline_fwd.argtypes = [i] * 4 + [vp] * 6 + [vp, i, vp, vp, sz, vp]
     L.rglru_scan_baseline_fwd.restype = i
+    L.rglru_gate_proj_fwd.argtypes = [i, i, i] + [vp] * 8
+    L.rglru_gate_proj_fwd.restype = i
+    L.rglru_gate_proj_bwd_workspace_bytes.argtypes = [i, i, i]
+    L.rglru_gate_proj_bwd_workspace_bytes.restype = sz
+    L.rglru_gate_proj_bwd.argtypes = [i, i, i] + [vp] * 5 + [i] + [vp] * 7 + [sz, vp]
+    L.rglru_gate_proj_bwd.restype = i
     L.samu_scan_decode.argtypes = [i, i] + [vp] * 10 + [vp, i, vp]
     L.samu_scan_decode.restype = i
     L.rglru_scan_fwd.argtypes = [i] * 5 + [vp] * 6 + [vp, i, vp, vp, vp, sz, vp]
@@ -199,6 +205,39 @@ def samu_scan_decode(x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z=None, *,
                                 _stream(stream))
     _check(st, "samu_scan_decode")
     return y, z_out
+
+
+def rglru_gate_proj_fwd(x, w_x, b_x, w_a, b_a, *, lx=None, la=None, stream=None):
+    """Gate logits of the two 16-block block-diagonal projections (BF16).
+    Returns (lx, la) [B, L, D]."""
+    B, L, D = x.shape
+    if lx is None:
+        lx = torch.empty_like(x)
+    if la is None:
+        la = torch.empty_like(x)
+    st = lib().rglru_gate_proj_fwd(B, L, D, _p(x), _p(w_x), _p(b_x), _p(w_a), _p(b_a), _p(lx), _p(la),
+                                   _stream(stream))
+    _check(st, "rglru_gate_proj_fwd")
+    return lx, la
+
+
+def rglru_gate_proj_bwd(x, w_x, w_a, dlx, dla, dx, *, dx_out=None, workspace=None, stream=None):
+    """Adjoint of the projections: returns dict(dx = dx + W^T dl, dw_x, db_x,
+    dw_a, db_a); pass dx_out=dx to accumulate in place."""
+    B, L, D = x.shape
+    dev = x.device
+    if dx_out is None:
+        dx_out = torch.empty_like(dx)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=dx_out, dw_x=torch.empty((16, D // 16, D // 16), **f32), db_x=torch.empty(D, **f32),
+               dw_a=torch.empty((16, D // 16, D // 16), **f32), db_a=torch.empty(D, **f32))
+    if workspace is None:
+        workspace = _bytes(lib().rglru_gate_proj_bwd_workspace_bytes(B, L, D), dev)
+    st = lib().rglru_gate_proj_bwd(B, L, D, _p(x), _p(w_x), _p(w_a), _p(dlx), _p(dla), _code(dlx.dtype), _p(dx),
+                                   _p(dx_out), _p(out["dw_x"]), _p(out["db_x"]), _p(out["dw_a"]),
+                                   _p(out["db_a"]), _p(workspace), workspace.numel(), _stream(stream))
+    _check(st, "rglru_gate_proj_bwd")
+    return out
 
 
 BASELINES = {"sequential": 0, "associative": 1}

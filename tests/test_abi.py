@@ -172,3 +172,25 @@ def test_baseline_scans_reject_before_enqueue():
     assert L.rglru_scan_baseline_fwd(0, 1, 8, 3, *r, None, None, f(0x500000), 0, None, None, 0, None) == -2
     assert L.rglru_scan_baseline_fwd(1, 1, 8, 4, *r, None, None, f(0x500000), 0, None, None, 0, None) == -4
     assert L.rglru_scan_baseline_fwd(0, 1, 8, 4, *r, None, None, f(0x200000), 0, None, None, 0, None) == -6
+
+
+def test_gate_projection_rejects_before_enqueue():
+    from linear_recurrence_sequence_amd import scan
+    L = scan.lib()
+    f = _fake
+    assert L.rglru_gate_proj_bwd_workspace_bytes(1, 64, 384) == 0           # D % 256
+    assert L.rglru_gate_proj_bwd_workspace_bytes(1, 64, 2816) == 0          # D > 2560
+    n = L.rglru_gate_proj_bwd_workspace_bytes(1, 4096, 512)
+    # two range partials of [2][16][32][32] plus [2][512] floats, 256-byte aligned
+    assert 2 * (2 * 16 * 32 * 32 + 2 * 512) * 4 <= n < 2 * (2 * 16 * 32 * 32 + 2 * 512) * 4 + 512
+    args = [f(0x100000), f(0x300000), f(0x310000), f(0x320000), f(0x330000)]
+    assert L.rglru_gate_proj_fwd(1, 8, 384, *args, f(0x500000), f(0x600000), None) == -2
+    assert L.rglru_gate_proj_fwd(1, 8, 256, *args, None, f(0x600000), None) == -1
+    assert L.rglru_gate_proj_fwd(1, 8, 256, *args, f(0x100000), f(0x600000), None) == -6     # lx over x
+    bw = [f(0x100000), f(0x300000), f(0x320000), f(0x400000), f(0x500000)]
+    outs = [f(0x700000), f(0x710000), f(0x720000), f(0x730000)]
+    ws = L.rglru_gate_proj_bwd_workspace_bytes(1, 8, 256)
+    assert L.rglru_gate_proj_bwd(1, 8, 256, *bw, 0, f(0x600000), f(0x600000), *outs, f(0x800000), 8, None) == -4
+    assert L.rglru_gate_proj_bwd(1, 8, 256, *bw, 3, f(0x600000), f(0x600000), *outs, f(0x800000), ws, None) == -2
+    assert L.rglru_gate_proj_bwd(1, 8, 256, *bw, 0, f(0x600000), f(0x600010), *outs, f(0x800000), ws, None) == -6
+    assert L.rglru_gate_proj_bwd(1, 8, 256, *bw, 0, f(0x600000), f(0x400000), *outs, f(0x800000), ws, None) == -6

@@ -1,0 +1,118 @@
+"""GPU parity of the RG-LRU gate projections (16-block block-diagonal,
+matrix cores) and of the whole input-to-output RG-LRU layer against the FP64
+oracle.
+
+The logits are rounded to BF16, a rounding decision: the GPU (FP32
+accumulation) must return the BF16 rounding of the exact FP64 logit except
+within FP32 accumulation error of a rounding tie.  The scan and the
+projection adjoint are then compared against the oracle fed the GPU's own
+BF16 logits, so both sides share that decision."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrence_sequence_amd import inputs
+from tests.helpers import dev_tensor, rel_l2, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL_OUT, TOL_GRAD = 1e-5, 1e-4
+
+
+def _check_logits(name, gpu_bf16, x, w, b):
+    exact = oracle.rglru_gate_proj(x, w, b)
+    mag = oracle.rglru_gate_proj(np.abs(oracle.widen(x)), np.abs(oracle.widen(w)), np.zeros(exact.shape[-1]))
+    g = to_f64(gpu_bf16)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 7)
+    err = np.abs(g - exact)
+    slack = 1e-6 * mag + 1e-30
+    assert np.all(err <= 0.5 * ulp + slack), (name, float(np.max(err / (0.5 * ulp + slack))))
+    rne = torch.from_numpy(exact).to(torch.bfloat16).double().numpy()
+    frac = np.mean(g != rne)
+    say(f"   {name}: logits differing from the FP64 rounding (near ties): {frac:.2e}")
+    assert frac < 1e-3
+
+
+def _layer(B, L, D, seed, reset_p, std):
+    inp = inputs.rglru_inputs(B, L, D, seed, reset_p=reset_p, h0_std=std, dh_final_std=std)
+    prm = inputs.rglru_proj_inputs(D, seed + 1)
+    return inp, prm
+
+
+def _run(B, L, D, seed, reset_p=0.0, std=0.1, dtype=torch.float32):
+    from linear_recurrence_sequence_amd import scan
+    inp, prm = _layer(B, L, D, seed, reset_p, std)
+    d = {k: dev_tensor(v) for k, v in {**inp, **prm}.items()}
+    lx, la = scan.rglru_gate_proj_fwd(d["x"], d["w_x"], d["b_x"], d["w_a"], d["b_a"])
+    y, hf, saved = scan.rglru_scan_fwd(d["x"], lx, la, d["alpha"], d["reset"], d["h0"], y_dtype=dtype)
+    g = scan.rglru_scan_bwd(d["x"], lx, la, d["alpha"], d["reset"], saved, d["dy"], d["dh_final"],
+                            grad_dtype=dtype)
+    p = scan.rglru_gate_proj_bwd(d["x"], d["w_x"], d["w_a"], g["dlx"], g["dla"], g["dx"])
+    torch.cuda.synchronize()
+    return inp, prm, lx, la, y, hf, g, p
+
+
+@pytest.mark.parametrize("B,L,D,reset_p", [(2, 300, 256, 1 / 64), (1, 1000, 2560, 0.0), (3, 77, 512, 0.1)])
+def test_layer_parity(B, L, D, reset_p):
+    say(f"[gate proj] B={B} L={L} D={D}: projections, scan F+B, projection adjoint (f32)")
+    inp, prm, lx, la, y, hf, g, p = _run(B, L, D, 700 + L, reset_p)
+    _check_logits("l^x", lx, inp["x"], prm["w_x"], prm["b_x"])
+    _check_logits("l^a", la, inp["x"], prm["w_a"], prm["b_a"])
+    lxg = lx.view(torch.int16).cpu().numpy().view(np.uint16)
+    lag = la.view(torch.int16).cpu().numpy().view(np.uint16)
+    say(f"[gate proj] B={B} L={L} D={D}: oracle on the GPU's logits")
+    rf = oracle.rglru_fwd(inp["x"], lxg, lag, inp["alpha"], inp["reset"], inp["h0"])
+    rg = oracle.rglru_bwd(inp["x"], lxg, lag, inp["alpha"], inp["reset"], inp["h0"], inp["dy"], inp["dh_final"])
+    dx, dw_x, db_x = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_x"], rg["dlx"], rg["dx"])
+    dx, dw_a, db_a = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_a"], rg["dla"], dx)
+    errs = {"y": rel_l2(to_f64(y), rf["y"]), "h_final": rel_l2(to_f64(hf), rf["h_final"]),
+            "dx": rel_l2(to_f64(p["dx"]), dx), "dw_x": rel_l2(to_f64(p["dw_x"]), dw_x),
+            "db_x": rel_l2(to_f64(p["db_x"]), db_x), "dw_a": rel_l2(to_f64(p["dw_a"]), dw_a),
+            "db_a": rel_l2(to_f64(p["db_a"]), db_a), "dalpha": rel_l2(to_f64(g["dalpha"]), rg["dalpha"])}
+    say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["y"] <= TOL_OUT and errs["h_final"] <= TOL_OUT
+    for k in ("dx", "dw_x", "db_x", "dw_a", "db_a", "dalpha"):
+        assert errs[k] <= TOL_GRAD, (k, errs[k])
+
+
+def test_layer_full_size_and_bf16_mode():
+    """B=1, L=32768, D=2048 (the metric shape): FP32-mode parity, then the
+    BF16 mode (BF16 cotangents into BF16 matrix-core products) against it."""
+    B, L, D = 1, 32768, 2048
+    say(f"[gate proj] full size B={B} L={L} D={D}")
+    inp, prm, lx, la, y, hf, g, p = _run(B, L, D, 3103, 0.0)
+    lxg = lx.view(torch.int16).cpu().numpy().view(np.uint16)
+    lag = la.view(torch.int16).cpu().numpy().view(np.uint16)
+    say("[gate proj] full size: oracle on the GPU's logits")
+    rg = oracle.rglru_bwd(inp["x"], lxg, lag, inp["alpha"], inp["reset"], inp["h0"], inp["dy"], inp["dh_final"])
+    dx, dw_x, db_x = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_x"], rg["dlx"], rg["dx"])
+    dx, dw_a, db_a = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_a"], rg["dla"], dx)
+    errs = {"dx": rel_l2(to_f64(p["dx"]), dx), "dw_x": rel_l2(to_f64(p["dw_x"]), dw_x),
+            "dw_a": rel_l2(to_f64(p["dw_a"]), dw_a), "db_x": rel_l2(to_f64(p["db_x"]), db_x)}
+    say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL_GRAD, (k, v)
+    say("[gate proj] full size: BF16 mode")
+    _, _, _, _, _, _, gb, pb = _run(B, L, D, 3103, 0.0, dtype=torch.bfloat16)
+    for k in ("dw_x", "dw_a", "db_x", "db_a"):
+        e = rel_l2(to_f64(pb[k]), to_f64(p[k]))
+        say(f"   bf16 vs f32 mode {k}: {e:.2e}")
+        assert e <= 2e-2, (k, e)
+
+
+def test_projection_in_place_and_deterministic():
+    from linear_recurrence_sequence_amd import scan
+    inp, prm = _layer(2, 500, 512, 41, 0.0, 0.1)
+    d = {k: dev_tensor(v) for k, v in {**inp, **prm}.items()}
+    say("[gate proj] in-place accumulation and determinism B=2 L=500 D=512")
+    dl1 = torch.randn(2, 500, 512, device="cuda")
+    dl2 = torch.randn(2, 500, 512, device="cuda")
+    dx = torch.randn(2, 500, 512, device="cuda")
+    a = scan.rglru_gate_proj_bwd(d["x"], d["w_x"], d["w_a"], dl1, dl2, dx)
+    b = scan.rglru_gate_proj_bwd(d["x"], d["w_x"], d["w_a"], dl1, dl2, dx)
+    dx2 = dx.clone()
+    c = scan.rglru_gate_proj_bwd(d["x"], d["w_x"], d["w_a"], dl1, dl2, dx2, dx_out=dx2)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]) and torch.equal(a[k], c[k]), k
