@@ -329,10 +329,28 @@ def main():
                                 K=RK, G=RG, out=rout, workspace=rwb)
 
         rg_ms, rg_prof = timed(rg_step, args.steps, args.warmup, False)
+
+        # the same F+B from the input: the two block-diagonal gate projections
+        # (matrix cores) in front, their adjoint behind
+        prm = {k: dev(v) for k, v in inputs.rglru_proj_inputs(D, 3005).items()}
+        pws = torch.empty(scan.lib().rglru_gate_proj_bwd_workspace_bytes(B, L, D), dtype=torch.uint8, device=dev_)
+
+        def layer_step():
+            scan.rglru_gate_proj_fwd(rd["x"], prm["w_x"], prm["b_x"], prm["w_a"], prm["b_a"], lx=rd["lx"],
+                                     la=rd["la"])
+            rg_step()
+            scan.rglru_gate_proj_bwd(rd["x"], prm["w_x"], prm["w_a"], rout["dlx"], rout["dla"], rout["dx"],
+                                     dx_out=rout["dx"], workspace=pws)
+
+        layer_ms, _ = timed(layer_step, args.steps, args.warmup, False)
+        _, lprof = timed(layer_step, args.steps, 1, True)
+        proj = {n: round(t / c * 1e3, 2) for n, (t, c) in lprof.items() if n.startswith("gate_projection")}
         rg = {"ms_per_step": round(rg_ms, 4), "K": RK, "G": effective_groups(L, RK, RG, 16),
+              "layer_ms_per_step": round(layer_ms, 4), "gate_projection_us": proj,
               "gbs_floor": round(22.0 * B * L * D / (rg_ms * 1e-3) / 1e9, 1),
               "samu_fb_time_reduction": round((rg_ms - ms) / rg_ms, 4)}
-        log(f"[bench] RG-LRU F+B {rg_ms:.4f} ms/step; SAMU reduction {(rg_ms - ms) / rg_ms:.1%}")
+        log(f"[bench] RG-LRU F+B {rg_ms:.4f} ms/step; SAMU reduction {(rg_ms - ms) / rg_ms:.1%}; "
+            f"with gate projections {layer_ms:.4f} ms/step {proj}")
 
     dec = None
     if not args.no_decode:

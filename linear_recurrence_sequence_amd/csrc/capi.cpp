@@ -52,7 +52,8 @@ static const char* const kKernelNames[K_NUM_KERNELS] = {
     "samu_controller_bwd", "samu_param_reduce", "samu_param_final", "rglru_chunk_summary",
     "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha_reduce",
     "rglru_alpha_final", "samu_decode", "baseline_sequential", "baseline_associative",
-    "gate_projection", "gate_projection_bwd"};
+    "gate_projection", "gate_projection_dx", "gate_projection_dw",
+    "gate_projection_reduce"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 

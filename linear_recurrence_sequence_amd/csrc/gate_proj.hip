@@ -11,277 +11,643 @@
 //   dx[t, i Db + k] += sum_o (W_x[i][o][k] dl^x + W_a[i][o][k] dl^a)[t, i Db + o]
 //   dW[i][o][k] = sum_t dl[t, i Db + o] x[t, i Db + k],  db = sum_t dl.
 //
-// Matrix-core layout (v_mfma_f32_16x16x16_bf16; 16x16x4_f32 for FP32
-// cotangents): lane l holds A[l%16][4(l/16)+j] and B[4(l/16)+j][l%16],
-// j = 0..3, and receives D[4(l/16)+r][l%16], r = 0..3.  Every product is
-// arranged so that D's rows run over channels and its columns over tokens:
-// each lane then owns four consecutive channels of one token, one 8- or
-// 16-byte store.  Tiles are staged in LDS with rows padded by 4 elements so
-// the 16 rows a fragment read touches fall on different banks.
+// All products run on v_mfma_f32_16x16x32_bf16: lane l supplies eight
+// consecutive reduction elements of row l%16 of A and of column l%16 of B
+// (group l/16 of the 32) and receives D[4(l/16)+r][l%16], r = 0..3.  A and
+// B use the same assignment of reduction indices to (lane group, slot), so
+// the sum is the full 32-term dot product whatever order the unit takes.
+// FP32 cotangents are split exactly into three BF16 terms (hi + mid + lo =
+// the FP32 value: each step keeps the next 8 significand bits), and each
+// product with a BF16 operand is then three BF16 products with FP32
+// accumulation -- the same exact products as an FP32 multiply, at the BF16
+// matrix-core rate.
+//
+// The work is HBM-bound (a few dozen flops per byte moved), so the kernels
+// are shaped for bytes in flight: the forward and dx hold their weights in
+// registers as matrix fragments for the life of a workgroup, token tiles are
+// requested up to two tiles ahead into registers with branch-free loads
+// (so the wait for one tile never covers the tiles behind it), and the grid
+// runs the 16 blocks fastest, so that neighbouring workgroups read whole
+// token rows.  Output rows of the forward and of dx are permuted inside each
+// pair of 16-channel tiles (row i of half h is channel 8 (i/4) + 4 h + i%4
+// of the pair) so that every lane ends with eight consecutive channels of
+// one token and writes them as one 16-byte store.  dW reduces over tokens:
+// its tiles stay in their natural layout in LDS and its fragments come from
+// the gfx950 transposing LDS read.
 #include "common.hpp"
 
 namespace lrs {
 namespace {
 
-typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int GP_THREADS = 256;   // 4 waves
-constexpr int GP_TT = 64;         // tokens per workgroup in the forward and dx kernels
-constexpr int GP_PAD = 4;         // elements of padding per LDS row
-constexpr int GP_RANGE = 2048;    // tokens per dW partial
+constexpr int TT = 64;    // tokens per tile
+constexpr int XPAD = 8;   // BF16 elements of LDS row padding (rows of 16-byte fragment reads)
+constexpr int FPAD = 4;   // FP32 elements of LDS row padding
 
-__device__ __forceinline__ v4s lds4(const uint16_t* p) { return *reinterpret_cast<const v4s*>(p); }
+#ifndef LRS_GP_TARGET_WG
+#define LRS_GP_TARGET_WG 1024   // forward / dx workgroups aimed for
+#endif
+#ifndef LRS_GP_DW_RANGE
+#define LRS_GP_DW_RANGE 2048    // tokens per dW partial sum
+#endif
 
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) { return pack_bf16x2(lo, hi); }
+template <int MT>
+struct Geo {
+    static constexpr int Db = 16 * MT;
+    static constexpr int P = (MT + 1) / 2;   // pairs of 16-channel tiles
+    static constexpr int KS = (MT + 1) / 2;  // 32-wide reduction steps over Db
+    static constexpr bool ODD = (MT & 1) != 0;  // last pair / step half used
+};
 
-// Copy a [rows, Db] BF16 tile (row stride `gstride` elements) into LDS rows of
-// Db + GP_PAD elements, 16 bytes per thread step; rows past `valid` are zero.
-__device__ __forceinline__ void stage_rows(uint16_t* lds, const uint16_t* g, size_t gstride, int rows, int valid,
-                                           int Db) {
-    const int per_row = Db / 8;
-    for (int c = threadIdx.x; c < rows * per_row; c += GP_THREADS) {
-        const int r = c / per_row, k8 = (c - r * per_row) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < valid) v = *reinterpret_cast<const uint4*>(g + (size_t)r * gstride + k8);
-        uint16_t* d = lds + r * (Db + GP_PAD) + k8;
-        reinterpret_cast<uint2*>(d)[0] = make_uint2(v.x, v.y);
-        reinterpret_cast<uint2*>(d)[1] = make_uint2(v.z, v.w);
+__device__ __forceinline__ v4f mfma(v4u a, v4u b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
+                                                   0, 0);
+}
+__device__ __forceinline__ v4u ld16(const void* p) { return *reinterpret_cast<const v4u*>(p); }
+__device__ __forceinline__ void st16(void* p, v4u v) { *reinterpret_cast<v4u*>(p) = v; }
+__device__ __forceinline__ v4u zero4() { return v4u{0u, 0u, 0u, 0u}; }
+
+// channel (within the block) of fragment row i, half h, of pair p
+__device__ __forceinline__ int pair_chan(int p, int i, int h) { return 32 * p + 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// Exact split of eight FP32 values into BF16 hi + mid + lo (truncations: the
+// residual after each step is exact in FP32 and holds at most 16, then 8,
+// significant bits).
+__device__ __forceinline__ void split3(v4u a, v4u b, v4u& hi, v4u& mid, v4u& lo) {
+    const uint32_t f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        h[j] = f[j] & 0xffff0000u;
+        const float r1 = __uint_as_float(f[j]) - __uint_as_float(h[j]);
+        m[j] = __float_as_uint(r1) & 0xffff0000u;
+        const float r2 = r1 - __uint_as_float(m[j]);
+        l[j] = __float_as_uint(r2) & 0xffff0000u;
+    }
+#define GP_PK(v, j) (((v)[2 * (j)] >> 16) | (v)[2 * (j) + 1])
+    hi = v4u{GP_PK(h, 0), GP_PK(h, 1), GP_PK(h, 2), GP_PK(h, 3)};
+    mid = v4u{GP_PK(m, 0), GP_PK(m, 1), GP_PK(m, 2), GP_PK(m, 3)};
+    lo = v4u{GP_PK(l, 0), GP_PK(l, 1), GP_PK(l, 2), GP_PK(l, 3)};
+#undef GP_PK
+}
+
+// Scheduling fence: nothing moves across it.  The loads of successive
+// prefetch stages stay in stage order (so the wait for one stage never
+// covers the stages behind it) and work on a prefetched tile stays after the
+// barrier that precedes its use.
+#ifndef LRS_GP_FENCE
+#define LRS_GP_FENCE 1
+#endif
+#ifndef LRS_GP_FWD_NT
+#define LRS_GP_FWD_NT 1
+#endif
+__device__ __forceinline__ void sched_fence() {
+    if (LRS_GP_FENCE) __builtin_amdgcn_sched_barrier(0);
+}
+
+// element j (0..3) of four consecutive BF16 values held as (lo word, hi word)
+__device__ __forceinline__ uint32_t bf16_at(uint2 v, int j) {
+    return ((j < 2 ? v.x : v.y) >> ((j & 1) ? 16 : 0)) & 0xffffu;
+}
+
+// dst[c][t] = src[t][c] for a [T, C] BF16 block (row stride gs), dst rows of
+// TS elements; each thread moves 4x4 blocks.
+__device__ __forceinline__ void stage_transposed_bf16(uint16_t* dst, int TS, const uint16_t* src, size_t gs, int T,
+                                                      int C, int nthreads) {
+    const int qc = C / 4;
+    for (int q = threadIdx.x; q < (T / 4) * qc; q += nthreads) {
+        const int a = q / qc, bq = q - a * qc;
+        uint2 v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const uint2*>(src + (size_t)(4 * a + r) * gs + 4 * bq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<uint2*>(dst + (size_t)(4 * bq + j) * TS + 4 * a) =
+                make_uint2(bf16_at(v[0], j) | (bf16_at(v[1], j) << 16), bf16_at(v[2], j) | (bf16_at(v[3], j) << 16));
     }
 }
 
+// workgroup token ranges of the forward and dx kernels: whole tiles, about
+// LRS_GP_TARGET_WG workgroups over the 16 blocks
+int stream_range(int BL) {
+    const int64_t tiles = ceil_div(BL, TT);
+    const int64_t per = std::max<int64_t>(1, ceil_div(tiles * 16, LRS_GP_TARGET_WG));
+    return (int)(per * TT);
+}
+
 // ------------------------------------------------------------- forward ---
-// grid (ceil(BL / GP_TT), 16 blocks); wave w owns tokens [16 w, 16 w + 16).
-__global__ __launch_bounds__(GP_THREADS) void gate_proj_fwd_kernel(
-    int BL, int D, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_x,
+// grid (16 blocks, ranges).  l^T[o][t] = W[o][k] x^T[k][t]: A = W rows
+// (registers), B = x rows (LDS).  Wave w owns unit (gate w / P, pair w % P)
+// and all tokens; waves past 2 P only help stage tiles.
+template <int MT>
+constexpr int fwd_waves() {
+    return 2 * Geo<MT>::P > 4 ? 2 * Geo<MT>::P : 4;
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * fwd_waves<MT>()) void gate_proj_fwd_kernel(
+    int BL, int D, int range, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_x,
     const float* __restrict__ b_x, const uint16_t* __restrict__ w_a, const float* __restrict__ b_a,
     uint16_t* __restrict__ lx, uint16_t* __restrict__ la) {
+    using G = Geo<MT>;
+    constexpr int Db = G::Db, NW = fwd_waves<MT>(), NT = 64 * NW, RS = Db + XPAD;
+    constexpr int CPR = Db / 8, NCH = TT * CPR, S = (NCH + NT - 1) / NT;  // 16-byte chunks
     extern __shared__ uint16_t gp_lds[];
-    const int Db = D / 16, RS = Db + GP_PAD;
-    uint16_t* sWx = gp_lds;
-    uint16_t* sWa = sWx + Db * RS;
-    uint16_t* sX = sWa + Db * RS;
-    const int blk = blockIdx.y;
-    const size_t t0 = (size_t)blockIdx.x * GP_TT;
-    const int valid = (int)min((size_t)GP_TT, (size_t)BL - t0);
-    stage_rows(sWx, w_x + (size_t)blk * Db * Db, Db, Db, Db, Db);
-    stage_rows(sWa, w_a + (size_t)blk * Db * Db, Db, Db, Db, Db);
-    stage_rows(sX, x + t0 * D + (size_t)blk * Db, D, GP_TT, valid, Db);
-    __syncthreads();
+    uint16_t* const buf0 = gp_lds;
+    uint16_t* const buf1 = gp_lds + TT * RS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
+    const int blk = blockIdx.x;
+    const size_t tr0 = (size_t)blockIdx.y * range, tr1 = min((size_t)BL, tr0 + range);
+    const int ntile = (int)((tr1 - tr0 + TT - 1) / TT);
+    const bool has_unit = wave < 2 * G::P;
+    const int g = has_unit ? wave / G::P : 0, p = has_unit ? wave % G::P : 0;
+    const uint16_t* W = (g ? w_a : w_x) + (size_t)blk * Db * Db;
+    const int c0 = 32 * p + 8 * grp;            // first of this lane's eight output channels
+    const bool cv = has_unit && c0 + 8 <= Db;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 15, grp = lane >> 4;
-    const int MT = Db / 16;
-    const uint16_t* xrow = sX + (wave * 16 + col) * RS + 4 * grp;  // B = x^T, token column `col`
-    for (int mt = 0; mt < MT; ++mt) {
-        v4f ax = {0.f, 0.f, 0.f, 0.f}, aa = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* wxr = sWx + (mt * 16 + col) * RS + 4 * grp;  // A = W rows (outputs)
-        const uint16_t* war = sWa + (mt * 16 + col) * RS + 4 * grp;
-        for (int kb = 0; kb < Db; kb += 16) {
-            const v4s bx = lds4(xrow + kb);
-            ax = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds4(wxr + kb), bx, ax, 0, 0, 0);
-            aa = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds4(war + kb), bx, aa, 0, 0, 0);
+    v4u wf[2][G::KS];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int o = pair_chan(p, col, h);
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+            const int k0 = 32 * ks + 8 * grp;
+            wf[h][ks] = (has_unit && o < Db && k0 < Db) ? ld16(W + (size_t)o * Db + k0) : zero4();
         }
-        const int tok = wave * 16 + col;
-        if (tok < valid) {
-            const int o = blk * Db + mt * 16 + 4 * grp;  // four consecutive channels
-            const float4 bxv = *reinterpret_cast<const float4*>(b_x + o);
-            const float4 bav = *reinterpret_cast<const float4*>(b_a + o);
-            const size_t dst = (t0 + tok) * D + o;
-            *reinterpret_cast<uint2*>(lx + dst) =
-                make_uint2(bf16_pair(ax[0] + bxv.x, ax[1] + bxv.y), bf16_pair(ax[2] + bxv.z, ax[3] + bxv.w));
-            *reinterpret_cast<uint2*>(la + dst) =
-                make_uint2(bf16_pair(aa[0] + bav.x, aa[1] + bav.y), bf16_pair(aa[2] + bav.z, aa[3] + bav.w));
+    }
+    float4 bz0 = make_float4(0.f, 0.f, 0.f, 0.f), bz1 = bz0;
+    if (cv) {
+        const float* bias = (g ? b_a : b_x) + (size_t)blk * Db + c0;
+        bz0 = *reinterpret_cast<const float4*>(bias);
+        bz1 = *reinterpret_cast<const float4*>(bias + 4);
+    }
+    uint16_t* const out = (g ? la : lx) + (size_t)blk * Db + c0;
+
+    // Loads are unconditional (no branches, so the wait for a tile does not
+    // also wait for the tiles behind it): rows past the range re-read its
+    // last row and tiles past the range its last tile.  Such rows only feed
+    // tokens whose outputs are not stored.
+    struct Regs { v4u v[S]; };
+    auto load = [&](Regs& r, int i) {
+        const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * TT;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int c = NCH % NT == 0 ? threadIdx.x + s * NT : min((int)threadIdx.x + s * NT, NCH - 1);
+            const int row = c / CPR, k8 = (c - row * CPR) * 8;
+            r.v[s] = ld16(x + min(t0 + row, tr1 - 1) * D + (size_t)blk * Db + k8);
         }
+    };
+    auto store = [&](const Regs& r, uint16_t* dst) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int c = threadIdx.x + s * NT;
+            const int row = c / CPR, k8 = (c - row * CPR) * 8;
+            if (NCH % NT == 0 || c < NCH) st16(dst + row * RS + k8, r.v[s]);
+        }
+    };
+    auto compute = [&](int i, const uint16_t* bufp) {
+        if (2 * G::P < NW && !has_unit) return;
+        const size_t t0 = tr0 + (size_t)i * TT;
+#pragma unroll
+        for (int tg = 0; tg < TT / 16; ++tg) {
+            const int tok = tg * 16 + col;
+            v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) {
+                const bool half = G::ODD && ks == G::KS - 1;  // lanes grp >= 2 lie past Db
+                const int k0 = 32 * ks + 8 * grp - ((half && grp >= 2) ? 16 : 0);
+                v4u xf = ld16(bufp + tok * RS + k0);
+                if (half && grp >= 2) xf = zero4();
+                a0 = mfma(wf[0][ks], xf, a0);
+                a1 = mfma(wf[1][ks], xf, a1);
+            }
+            if (cv && t0 + tok < tr1)  // streamed past the caches by default (measured the better choice for the layer)
+                out_store<u32x4_t, LRS_GP_FWD_NT != 0>(
+                    out + (t0 + tok) * D,
+                    u32x4_t{pack_bf16x2(a0[0] + bz0.x, a0[1] + bz0.y), pack_bf16x2(a0[2] + bz0.z, a0[3] + bz0.w),
+                            pack_bf16x2(a1[0] + bz1.x, a1[1] + bz1.y), pack_bf16x2(a1[2] + bz1.z, a1[3] + bz1.w)});
+        }
+    };
+
+    // LDS double buffer; tiles i + 1 and i + 2 are in registers or in flight
+    // while tile i is multiplied.  The body always runs both halves (a tile
+    // past the range stores nothing), so every load is issued on every path
+    // and the wait for one tile never covers the tile behind it.
+    Regs ra, rb;
+    load(ra, 0);
+    sched_fence();
+    load(rb, 1);
+    sched_fence();
+    store(ra, buf0);
+    load(ra, 2);
+    sched_fence();
+    __syncthreads();
+    for (int i = 0; i < ntile; i += 2) {
+        compute(i, buf0);
+        sched_fence();
+        store(rb, buf1);
+        load(rb, i + 3);
+        sched_fence();
+        __syncthreads();
+        compute(i + 1, buf1);
+        sched_fence();
+        store(ra, buf0);
+        load(ra, i + 4);
+        sched_fence();
+        __syncthreads();
     }
 }
 
 // ------------------------------------------------------------ dx (adjoint)
-// dx^T[k][t] = sum_o W^T[k][o] dl^T[o][t] summed over both gates (one gate
-// at a time through LDS: W^T rows are inputs k, dl rows are tokens), then
-// added to dx_in.  Each wave owns 16 tokens and every input tile.
-constexpr int GP_MT_MAX = 10;  // Db <= 160
+// grid (16 blocks, ranges).  dx^T[k][t] = sum_g W_g^T[k][o] dl_g^T[o][t]:
+// A = W^T rows (staged transposed through LDS once, then registers), B = dl
+// rows (LDS).  Waves per pair: 4 for P = 1, 2 for P = 2..4, 1 for P = 5
+// (a workgroup of more than eight waves would cap each at 168 registers);
+// the waves of a pair split the four token groups of a tile.
+template <int MT>
+constexpr int dx_waves() {
+    return Geo<MT>::P == 1 ? 4 : (2 * Geo<MT>::P <= 8 ? 2 * Geo<MT>::P : Geo<MT>::P);
+}
 
-template <bool F32>
-__global__ __launch_bounds__(GP_THREADS) void gate_proj_dx_kernel(
-    int BL, int D, const uint16_t* __restrict__ w_x, const uint16_t* __restrict__ w_a,
+// tiles requested ahead: two where the registers allow it
+template <int MT, bool F32>
+constexpr int prefetch_depth() {
+    return (F32 || MT >= 9) ? 1 : 2;
+}
+
+template <int MT, bool F32>
+constexpr size_t dx_lds_bytes() {
+    constexpr int Db = 16 * MT;
+    constexpr size_t tile = (size_t)2 * TT * (Db + (F32 ? FPAD : XPAD)) * (F32 ? 4 : 2);
+    constexpr size_t wt = (size_t)Db * (Db + XPAD) * 2;
+    return tile > wt ? tile : wt;
+}
+
+template <int MT, bool F32>
+__global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
+    int BL, int D, int range, const uint16_t* __restrict__ w_x, const uint16_t* __restrict__ w_a,
     const void* __restrict__ dlx, const void* __restrict__ dla, const void* dx_in, void* dx_out) {
+    using G = Geo<MT>;
+    constexpr int Db = G::Db, NW = dx_waves<MT>(), NT = 64 * NW, ES = F32 ? 4 : 2;
+    constexpr int RS = Db + (F32 ? FPAD : XPAD), RW = Db + XPAD;
+    constexpr int WPP = NW / G::P, TGW = 4 / WPP;  // waves per pair, token groups per wave and tile
+    constexpr int CPR = Db * ES / 16, NCH = 2 * TT * CPR, S = (NCH + NT - 1) / NT;
+    constexpr int PF = prefetch_depth<MT, F32>();
     extern __shared__ uint16_t gp_lds[];
-    const int Db = D / 16, RS = Db + GP_PAD;
-    uint16_t* sW = gp_lds;                                   // W_g^T [k][o] bf16
-    float* sDf = reinterpret_cast<float*>(sW + Db * RS);     // F32: dl_g [t][o]
-    uint16_t* sDb = sW + Db * RS;                            // BF16: dl_g [t][o]
-    const int blk = blockIdx.y;
-    const size_t t0 = (size_t)blockIdx.x * GP_TT;
-    const int valid = (int)min((size_t)GP_TT, (size_t)BL - t0);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 15, grp = lane >> 4;
-    const int MT = Db / 16;
-    const int tok = wave * 16 + col;
-    v4f acc[GP_MT_MAX];
+    unsigned char* const tile = reinterpret_cast<unsigned char*>(gp_lds);  // [2 gates][TT][RS] x ES bytes
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
+    const int blk = blockIdx.x;
+    const size_t tr0 = (size_t)blockIdx.y * range, tr1 = min((size_t)BL, tr0 + range);
+    const int ntile = (int)((tr1 - tr0 + TT - 1) / TT);
+    const int p = wave / WPP;
+    const int tgb = (wave - p * WPP) * TGW;
+    const int c0 = 32 * p + 8 * grp;
+    const bool cv = c0 + 8 <= Db;
+
+    // A fragments of both gates: W_g^T row k = pair_chan(p, col, h), columns o
+    v4u wf[2][2][G::KS];
 #pragma unroll
-    for (int m = 0; m < GP_MT_MAX; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < 2; ++g) {
-        const uint16_t* w = (g ? w_a : w_x) + (size_t)blk * Db * Db;
-        const void* dl = g ? dla : dlx;
-        if (g) __syncthreads();  // the first gate's tiles are no longer read
-        for (int c = threadIdx.x; c < Db * Db; c += GP_THREADS) {
-            const int o = c / Db, k = c - o * Db;
-            sW[k * RS + o] = w[c];
-        }
-        if (F32) {
-            const int per_row = Db / 4;
-            for (int c = threadIdx.x; c < GP_TT * per_row; c += GP_THREADS) {
-                const int r = c / per_row, k4 = (c - r * per_row) * 4;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (r < valid)
-                    v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(dl) + (t0 + r) * D +
-                                                         (size_t)blk * Db + k4);
-                *reinterpret_cast<float4*>(sDf + (size_t)r * RS + k4) = v;
-            }
-        } else {
-            stage_rows(sDb, reinterpret_cast<const uint16_t*>(dl) + t0 * D + (size_t)blk * Db, D, GP_TT, valid, Db);
-        }
+    for (int gg = 0; gg < 2; ++gg) {
+        if (gg) __syncthreads();
+        stage_transposed_bf16(gp_lds, RW, (gg ? w_a : w_x) + (size_t)blk * Db * Db, Db, Db, Db, NT);
         __syncthreads();
 #pragma unroll
-        for (int mt = 0; mt < GP_MT_MAX; ++mt) {
-            if (mt >= MT) continue;
-            v4f a = acc[mt];
-            if (F32) {
-                // 16x16x4: lane l holds A[l%16][l/16], B[l/16][l%16]
-                for (int kb = 0; kb < Db; kb += 4) {
-                    const int o = kb + grp;
-                    const float av = __uint_as_float((uint32_t)sW[(mt * 16 + col) * RS + o] << 16);
-                    a = __builtin_amdgcn_mfma_f32_16x16x4f32(av, sDf[(size_t)tok * RS + o], a, 0, 0, 0);
-                }
-            } else {
-                const uint16_t* wr = sW + (mt * 16 + col) * RS + 4 * grp;
-                const uint16_t* dr = sDb + (size_t)tok * RS + 4 * grp;
-                for (int kb = 0; kb < Db; kb += 16)
-                    a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds4(wr + kb), lds4(dr + kb), a, 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+            const int k = pair_chan(p, col, h);
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) {
+                const int o0 = 32 * ks + 8 * grp;
+                wf[gg][h][ks] = (k < Db && o0 < Db) ? ld16(gp_lds + k * RW + o0) : zero4();
             }
-            acc[mt] = a;
         }
     }
-    if (tok >= valid) return;
+
+    struct Regs { v4u v[S]; };
+    // unconditional loads, as in the forward: rows past the range re-read
+    // its last row and only feed tokens whose dx is not stored
+    auto load = [&](Regs& r, int i) {
+        const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * TT;
 #pragma unroll
-    for (int mt = 0; mt < GP_MT_MAX; ++mt) {
-        if (mt >= MT) continue;
-        const size_t dst = (t0 + tok) * D + (size_t)blk * Db + mt * 16 + 4 * grp;
-        if (F32) {
-            const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(dx_in) + dst);
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(dx_out) + dst) =
-                make_float4(a.x + acc[mt][0], a.y + acc[mt][1], a.z + acc[mt][2], a.w + acc[mt][3]);
-        } else {
-            const uint2 a = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(dx_in) + dst);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dx_out) + dst) =
-                make_uint2(bf16_pair(bf16_lo(a.x) + acc[mt][0], bf16_hi(a.x) + acc[mt][1]),
-                           bf16_pair(bf16_lo(a.y) + acc[mt][2], bf16_hi(a.y) + acc[mt][3]));
+        for (int s = 0; s < S; ++s) {
+            const int c = NCH % NT == 0 ? threadIdx.x + s * NT : min((int)threadIdx.x + s * NT, NCH - 1);
+            const int gg = c / (TT * CPR), rem = c - gg * TT * CPR, row = rem / CPR, ch = rem - row * CPR;
+            r.v[s] = ld16(reinterpret_cast<const unsigned char*>(gg ? dla : dlx) +
+                          (min(t0 + row, tr1 - 1) * D + (size_t)blk * Db) * ES + ch * 16);
+        }
+    };
+    auto store = [&](const Regs& r) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int c = threadIdx.x + s * NT;
+            const int gg = c / (TT * CPR), rem = c - gg * TT * CPR, row = rem / CPR, ch = rem - row * CPR;
+            if (NCH % NT == 0 || c < NCH) st16(tile + ((size_t)(gg * TT + row) * RS) * ES + ch * 16, r.v[s]);
+        }
+    };
+    // dx_in of the tile, requested before the prefetch of later tiles so
+    // that waiting for it does not wait for them; a lane that stores nothing
+    // reads inside the range and the block
+    struct In { v4u v[TGW][F32 ? 2 : 1]; };
+    auto load_in = [&](In& d, int i) {
+        const size_t t0 = tr0 + (size_t)i * TT;
+#pragma unroll
+        for (int q = 0; q < TGW; ++q) {
+            const int tok = (tgb + q) * 16 + col;
+            const size_t src = (min(t0 + tok, tr1 - 1) * D + (size_t)blk * Db + min(c0, Db - 8)) * ES;
+#pragma unroll
+            for (int u = 0; u < (F32 ? 2 : 1); ++u)
+                d.v[q][u] = ld16(reinterpret_cast<const unsigned char*>(dx_in) + src + 16 * u);
+        }
+    };
+    auto compute = [&](int i, const In& d) {
+        const size_t t0 = tr0 + (size_t)i * TT;
+#pragma unroll
+        for (int q = 0; q < TGW; ++q) {
+            const int tok = (tgb + q) * 16 + col;
+            const bool tv = cv && t0 + tok < tr1;
+            const size_t dst = ((t0 + tok) * D + (size_t)blk * Db + c0) * ES;
+            const v4u in0 = d.v[q][0];
+            const v4u in1 = d.v[q][F32 ? 1 : 0];
+            v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+            for (int gg = 0; gg < 2; ++gg) {
+#pragma unroll
+                for (int ks = 0; ks < G::KS; ++ks) {
+                    const bool half = G::ODD && ks == G::KS - 1;
+                    const int o0 = 32 * ks + 8 * grp - ((half && grp >= 2) ? 16 : 0);
+                    const unsigned char* src = tile + ((size_t)(gg * TT + tok) * RS + o0) * ES;
+                    if (F32) {
+                        v4u hi, mid, lo;
+                        split3(ld16(src), ld16(src + 16), hi, mid, lo);
+                        if (half && grp >= 2) hi = mid = lo = zero4();
+                        a0 = mfma(wf[gg][0][ks], hi, a0);
+                        a1 = mfma(wf[gg][1][ks], hi, a1);
+                        a0 = mfma(wf[gg][0][ks], mid, a0);
+                        a1 = mfma(wf[gg][1][ks], mid, a1);
+                        a0 = mfma(wf[gg][0][ks], lo, a0);
+                        a1 = mfma(wf[gg][1][ks], lo, a1);
+                    } else {
+                        v4u bf = ld16(src);
+                        if (half && grp >= 2) bf = zero4();
+                        a0 = mfma(wf[gg][0][ks], bf, a0);
+                        a1 = mfma(wf[gg][1][ks], bf, a1);
+                    }
+                }
+            }
+            if (tv) {
+                unsigned char* o = reinterpret_cast<unsigned char*>(dx_out) + dst;
+                if (F32) {
+                    out_f32x4(o, __uint_as_float(in0.x) + a0[0], __uint_as_float(in0.y) + a0[1],
+                              __uint_as_float(in0.z) + a0[2], __uint_as_float(in0.w) + a0[3]);
+                    out_f32x4(o + 16, __uint_as_float(in1.x) + a1[0], __uint_as_float(in1.y) + a1[1],
+                              __uint_as_float(in1.z) + a1[2], __uint_as_float(in1.w) + a1[3]);
+                } else {
+                    out_u32x4(o, pack_bf16x2(bf16_lo(in0.x) + a0[0], bf16_hi(in0.x) + a0[1]),
+                              pack_bf16x2(bf16_lo(in0.y) + a0[2], bf16_hi(in0.y) + a0[3]),
+                              pack_bf16x2(bf16_lo(in0.z) + a1[0], bf16_hi(in0.z) + a1[1]),
+                              pack_bf16x2(bf16_lo(in0.w) + a1[2], bf16_hi(in0.w) + a1[3]));
+                }
+            }
+        }
+    };
+
+    // one LDS tile; the next PF tiles in registers or in flight.  Every
+    // iteration runs all PF stages (a tile past the range stores nothing),
+    // so each load is issued on every path.
+    Regs rr[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        load(rr[j], j);
+        sched_fence();
+    }
+    for (int i = 0; i < ntile; i += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            In d;
+            load_in(d, i + j);
+            sched_fence();
+            __syncthreads();  // the previous tile (or the weight staging) is no longer read
+            sched_fence();
+            store(rr[j]);
+            load(rr[j], i + j + PF);
+            sched_fence();
+            __syncthreads();
+            compute(i + j, d);
         }
     }
 }
 
 // ------------------------------------------------------- dW, db (adjoint)
-// Partial sums over one token range r: dW^(r)[o][k] = sum_t dl[t][o] x[t][k].
-// grid (n_ranges, 16 blocks, ceil(MT / 4) output-tile groups): wave w owns
-// output tile ot = 4 * group + w (16 outputs) against every input tile, for
-// both gates.  A = dl^T (rows o), B = x (columns k), both staged transposed
-// (rows = channels, columns = tokens) so fragment reads are contiguous.
-template <bool F32>
-__global__ __launch_bounds__(GP_THREADS) void gate_proj_dw_kernel(
+// grid (16 blocks, ranges of LRS_GP_DW_RANGE tokens).  Partial sums over the
+// range: dW[o][k] = sum_t dl^T[o][t] x[t][k] with the tokens as the
+// reduction index.  Tiles sit in LDS in their natural layout (rows = tokens)
+// and fragments come from transposing LDS reads (ds_read_b64_tr_b16: within
+// each 16-lane group, lane i receives element i%4 of the 8 bytes read by
+// lanes 4j + i/4, j = 0..3; a lane that reads row t0 + s/4 at channel
+// c0 + 4 (s%4) thus hands lane i channel c0 + i at tokens t0..t0+3).  Wave w
+// owns R rows (gate, 16-row tile mo) with all MT column tiles plus one bias
+// tile whose B operand is the constant column (1, 0, ..., 0): its first
+// column is db = sum_t dl, summed by the matrix cores alongside dW.  FP32
+// cotangents are split into three BF16 planes when they are staged.
+template <int MT>
+constexpr int dw_waves() {
+    return MT >= 4 ? MT : 4;
+}
+template <int MT>
+constexpr int dw_rows() {
+    return (2 * MT + dw_waves<MT>() - 1) / dw_waves<MT>();
+}
+// LDS row stride (BF16 elements): an odd multiple of 16, so the four rows
+// one 16-lane group reads fall on disjoint banks
+template <int MT>
+constexpr int dw_row() {
+    return 16 * (MT | 1);
+}
+template <int MT, bool F32>
+constexpr size_t dw_lds_bytes() {
+    return (size_t)TT * dw_row<MT>() * 2 * (1 + 2 * (F32 ? 3 : 1));
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+// eight consecutive tokens (rows p and p + 4 RS.. as two transposing reads) of one channel per lane
+__device__ __forceinline__ v4u tr_frag(const uint16_t* p, int rs) {
+    typedef __attribute__((address_space(3))) v4s* lp;
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p + 4 * rs));
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return v4u{ua.x, ua.y, ub.x, ub.y};
+}
+
+// four FP32 values -> BF16 hi, mid, lo (exact split, as split3)
+__device__ __forceinline__ void split3x4(v4u f, uint2& hi, uint2& mid, uint2& lo) {
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = f[j] & 0xffff0000u;
+        const float r1 = __uint_as_float(f[j]) - __uint_as_float(h[j]);
+        m[j] = __float_as_uint(r1) & 0xffff0000u;
+        const float r2 = r1 - __uint_as_float(m[j]);
+        l[j] = __float_as_uint(r2) & 0xffff0000u;
+    }
+    hi = make_uint2((h[0] >> 16) | h[1], (h[2] >> 16) | h[3]);
+    mid = make_uint2((m[0] >> 16) | m[1], (m[2] >> 16) | m[3]);
+    lo = make_uint2((l[0] >> 16) | l[1], (l[2] >> 16) | l[3]);
+}
+
+template <int MT, bool F32>
+__global__ __launch_bounds__(64 * dw_waves<MT>()) void gate_proj_dw_kernel(
     int BL, int D, int range, const uint16_t* __restrict__ x, const void* __restrict__ dlx,
     const void* __restrict__ dla, float* __restrict__ dw_part, float* __restrict__ db_part) {
-    extern __shared__ uint16_t gp_lds[];
-    const int Db = D / 16;
-    const int TS = GP_TT + GP_PAD;
-    uint16_t* sX = gp_lds;                                  // x^T [k][t] bf16, all Db inputs
-    float* sLf = reinterpret_cast<float*>(sX + Db * TS);    // F32: dl^T [2][64 outputs][t]
-    uint16_t* sLb = sX + Db * TS;                           // BF16: same
-    const int r = blockIdx.x, blk = blockIdx.y, og = blockIdx.z;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 15, grp = lane >> 4;
-    const int MT = Db / 16;
-    const int o0 = og * 64;                                 // first output of the group
-    const int ot = 4 * og + wave;                           // this wave's output tile
-    const size_t tr0 = (size_t)r * range;
-    const size_t tr1 = min((size_t)BL, tr0 + range);
-    v4f acc[2][GP_MT_MAX];
+    constexpr int Db = 16 * MT, NW = dw_waves<MT>(), NT = 64 * NW, R = dw_rows<MT>();
+    constexpr int RS = dw_row<MT>(), ES = F32 ? 4 : 2, NPL = F32 ? 3 : 1;
+    constexpr int PF = prefetch_depth<MT, F32>();
+    constexpr int XCR = Db / 8, XC = TT * XCR;             // 16-byte chunks of x: per row, per tile
+    constexpr int LCR = Db * ES / 16, LC = TT * LCR;       // of one cotangent tile
+    constexpr int SX = (XC + NT - 1) / NT, SL = (LC + NT - 1) / NT;
+    extern __shared__ uint16_t gp_lds[];  // x [TT][RS], dl [2 gates][NPL planes][TT][RS]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
+    const int blk = blockIdx.x, r = blockIdx.y;
+    const size_t tr0 = (size_t)r * range, tr1 = min((size_t)BL, tr0 + range);
+    const int ntile = (int)((tr1 - tr0 + TT - 1) / TT);
+
+    v4f acc[R][MT + 1];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int j = 0; j < R; ++j)
 #pragma unroll
-        for (int n = 0; n < GP_MT_MAX; ++n) acc[g][n] = v4f{0.f, 0.f, 0.f, 0.f};
-    float dbs[2] = {0.f, 0.f};  // thread j < 64: column sums of output o0 + j
-    for (size_t t0 = tr0; t0 < tr1; t0 += GP_TT) {
-        const int valid = (int)min((size_t)GP_TT, tr1 - t0);
-        __syncthreads();
-        for (int c = threadIdx.x; c < GP_TT * Db; c += GP_THREADS) {
-            const int t = c / Db, k = c - t * Db;
-            sX[k * TS + t] = t < valid ? x[(t0 + t) * D + (size_t)blk * Db + k] : (uint16_t)0;
+        for (int n = 0; n <= MT; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Loads are unconditional (rows past the range re-read its last row,
+    // tiles past it its last tile); a row mask, applied when the chunk is
+    // written to LDS, zeroes the rows that do not belong to this tile.
+    struct Regs {
+        v4u x[SX];
+        v4u l[2][SL];
+        uint32_t okx, okl;  // bit s (+ SL for gate 1): the chunk's token row is in the range
+    };
+    auto chunk = [&](int s, int nchunks) {
+        const int c = threadIdx.x + s * NT;
+        return nchunks % NT == 0 ? c : min(c, nchunks - 1);
+    };
+    auto load = [&](Regs& b, int i) {
+        const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * TT;
+        b.okx = b.okl = 0;
+#pragma unroll
+        for (int s = 0; s < SX; ++s) {
+            const int c = chunk(s, XC), row = c / XCR, c8 = c - row * XCR;
+            const size_t t = t0 + row;
+            b.okx |= (i < ntile && t < tr1) ? 1u << s : 0u;
+            b.x[s] = ld16(x + min(t, tr1 - 1) * D + (size_t)blk * Db + 8 * c8);
         }
-        for (int c = threadIdx.x; c < 2 * GP_TT * 64; c += GP_THREADS) {
-            const int g = c / (GP_TT * 64), rem = c - g * GP_TT * 64;
-            const int t = rem / 64, j = rem - t * 64;
-            const bool ok = t < valid && o0 + j < Db;
-            const size_t src = (t0 + t) * D + (size_t)blk * Db + o0 + j;
-            const void* dl = g ? dla : dlx;
-            if (F32) sLf[((size_t)g * 64 + j) * TS + t] = ok ? reinterpret_cast<const float*>(dl)[src] : 0.f;
-            else sLb[(g * 64 + j) * TS + t] = ok ? reinterpret_cast<const uint16_t*>(dl)[src] : (uint16_t)0;
-        }
-        __syncthreads();
-        if (threadIdx.x < 64) {
-            const int j = threadIdx.x;
-            for (int t = 0; t < valid; ++t) {
 #pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    dbs[g] += F32 ? sLf[((size_t)g * 64 + j) * TS + t]
-                                  : __uint_as_float((uint32_t)sLb[(g * 64 + j) * TS + t] << 16);
+        for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+            for (int s = 0; s < SL; ++s) {
+                const int c = chunk(s, LC), row = c / LCR, ch = c - row * LCR;
+                const size_t t = t0 + row;
+                b.okl |= (i < ntile && t < tr1) ? 1u << (gg * SL + s) : 0u;
+                b.l[gg][s] = ld16(reinterpret_cast<const unsigned char*>(gg ? dla : dlx) +
+                                  (min(t, tr1 - 1) * D + (size_t)blk * Db) * ES + 16 * ch);
             }
+    };
+    auto store = [&](const Regs& b, uint16_t* sx) {
+        uint16_t* const sl = sx + TT * RS;
+#pragma unroll
+        for (int s = 0; s < SX; ++s) {
+            const int c = threadIdx.x + s * NT;
+            if (XC % NT != 0 && c >= XC) continue;
+            const int row = c / XCR, c8 = c - row * XCR;
+            st16(sx + row * RS + 8 * c8, (b.okx >> s & 1u) ? b.x[s] : zero4());
         }
-        if (ot < MT) {
 #pragma unroll
-            for (int g = 0; g < 2; ++g)
+        for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
-                for (int n = 0; n < GP_MT_MAX; ++n) {
-                    if (n >= MT) continue;
-                    v4f a = acc[g][n];
-                    if (F32) {
-                        for (int kt = 0; kt < GP_TT; kt += 4) {
-                            const float av = sLf[((size_t)g * 64 + wave * 16 + col) * TS + kt + grp];
-                            const float bv = __uint_as_float((uint32_t)sX[(n * 16 + col) * TS + kt + grp] << 16);
-                            a = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, a, 0, 0, 0);
-                        }
-                    } else {
-                        const uint16_t* ar = sLb + (g * 64 + wave * 16 + col) * TS + 4 * grp;
-                        const uint16_t* br = sX + (n * 16 + col) * TS + 4 * grp;
-                        for (int kt = 0; kt < GP_TT; kt += 16)
-                            a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds4(ar + kt), lds4(br + kt), a, 0, 0, 0);
-                    }
-                    acc[g][n] = a;
-                }
-        }
-    }
-    // D[o][k]: lane holds o = 16 ot + 4 grp + i, k = 16 n + col
-    if (ot < MT) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int n = 0; n < GP_MT_MAX; ++n) {
-                if (n >= MT) continue;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const size_t o = (size_t)ot * 16 + 4 * grp + i;
-                    dw_part[((((size_t)r * 2 + g) * 16 + blk) * Db + o) * Db + n * 16 + col] = acc[g][n][i];
+            for (int s = 0; s < SL; ++s) {
+                const int c = threadIdx.x + s * NT;
+                if (LC % NT != 0 && c >= LC) continue;
+                const int row = c / LCR, ch = c - row * LCR;
+                const v4u v = (b.okl >> (gg * SL + s) & 1u) ? b.l[gg][s] : zero4();
+                if (F32) {
+                    uint2 hi, mid, lo;
+                    split3x4(v, hi, mid, lo);
+                    uint16_t* d = sl + ((gg * 3) * TT + row) * RS + 4 * ch;
+                    *reinterpret_cast<uint2*>(d) = hi;
+                    *reinterpret_cast<uint2*>(d + TT * RS) = mid;
+                    *reinterpret_cast<uint2*>(d + 2 * TT * RS) = lo;
+                } else {
+                    st16(sl + (gg * TT + row) * RS + 8 * ch, v);
                 }
             }
-    }
-    if (threadIdx.x < 64 && o0 + (int)threadIdx.x < Db) {
+    };
+    const v4u ones = col == 0 ? v4u{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u} : zero4();
+    auto compute = [&](const uint16_t* sx) {
+        const uint16_t* const sl = sx + TT * RS;
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
-            db_part[((size_t)r * 2 + g) * D + (size_t)blk * Db + o0 + threadIdx.x] = dbs[g];
+        for (int kt = 0; kt < TT; kt += 32) {
+            const int toff = (kt + 8 * grp + (col >> 2)) * RS + 4 * (col & 3);  // this lane's read address
+            v4u af[R][NPL];
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const int row = wave * R + j;  // gate row / MT, tile row % MT
+                const int rc = row < 2 * MT ? row : 0;
+                const int gg = rc / MT, mo = rc - gg * MT;
+#pragma unroll
+                for (int p = 0; p < NPL; ++p) af[j][p] = tr_frag(sl + (gg * NPL + p) * TT * RS + toff + mo * 16, RS);
+            }
+#pragma unroll
+            for (int n = 0; n <= MT; ++n) {
+                const v4u bf = n < MT ? tr_frag(sx + toff + n * 16, RS) : ones;
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    if (2 * MT % NW != 0 && wave * R + j >= 2 * MT) continue;
+#pragma unroll
+                    for (int p = 0; p < NPL; ++p) acc[j][n] = mfma(af[j][p], bf, acc[j][n]);
+                }
+            }
+        }
+    };
+
+    // all PF stages every iteration: a tile past the range is masked to zero
+    Regs rr[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        load(rr[j], j);
+        sched_fence();
+    }
+    for (int i = 0; i < ntile; i += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            __syncthreads();
+            sched_fence();
+            store(rr[j], gp_lds);
+            load(rr[j], i + j + PF);
+            sched_fence();
+            __syncthreads();
+            compute(gp_lds);
+        }
+    }
+
+    // D[o][k]: lane holds o = mo 16 + 4 grp + e, k = n 16 + col
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int row = wave * R + j;
+        if (row >= 2 * MT) continue;
+        const int gg = row / MT, mo = row - gg * MT;
+        float* dst = dw_part + ((((size_t)r * 2 + gg) * 16 + blk) * Db + mo * 16 + 4 * grp) * Db + col;
+#pragma unroll
+        for (int n = 0; n < MT; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(size_t)e * Db + n * 16] = acc[j][n][e];
+        if (col == 0) {
+            float* db = db_part + ((size_t)r * 2 + gg) * D + (size_t)blk * Db + mo * 16 + 4 * grp;
+            *reinterpret_cast<float4*>(db) = make_float4(acc[j][MT][0], acc[j][MT][1], acc[j][MT][2], acc[j][MT][3]);
+        }
     }
 }
 
 // Sum of the range partials in range order (FP64): dw [2][16][Db][Db], db [2][D].
+// The loads of eight ranges are issued ahead of their additions.
 __global__ __launch_bounds__(256) void gate_proj_reduce_kernel(int n_ranges, int nw, int D,
                                                                const float* __restrict__ dw_part,
                                                                const float* __restrict__ db_part,
@@ -291,82 +657,98 @@ __global__ __launch_bounds__(256) void gate_proj_reduce_kernel(int n_ranges, int
     const int half = nw / 2;
     if (e < nw) {
         double s = 0.0;
+#pragma unroll 8
         for (int r = 0; r < n_ranges; ++r) s += dw_part[(size_t)r * nw + e];
         if (e < half) dw_x[e] = (float)s;
         else dw_a[e - half] = (float)s;
     } else if (e < nw + 2 * D) {
         const int f = e - nw;
         double s = 0.0;
+#pragma unroll 8
         for (int r = 0; r < n_ranges; ++r) s += db_part[(size_t)r * 2 * D + f];
         if (f < D) db_x[f] = (float)s;
         else db_a[f - D] = (float)s;
     }
 }
 
-}  // namespace
-
-int gate_proj_ranges(int BL) { return (int)std::max<int64_t>(1, ceil_div(BL, GP_RANGE)); }
-
-size_t gate_proj_fwd_lds(int D) {
-    const int Db = D / 16;
-    return (size_t)(2 * Db + GP_TT) * (Db + GP_PAD) * 2;
+template <class F>
+hipError_t allow_lds(F* kernel, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
 }
 
-hipError_t launch_gate_proj_fwd(int BL, int D, const void* x, const void* w_x, const float* b_x,
-                                const void* w_a, const float* b_a, void* lx, void* la, hipStream_t s) {
-    const dim3 grid((unsigned)ceil_div(BL, GP_TT), 16);
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gate_proj_fwd_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)gate_proj_fwd_lds(D));
+}  // namespace
+
+int gate_proj_ranges(int BL) { return (int)std::max<int64_t>(1, ceil_div(BL, LRS_GP_DW_RANGE)); }
+
+namespace {
+
+template <int MT>
+hipError_t fwd_mt(int BL, int D, const void* x, const void* w_x, const float* b_x, const void* w_a,
+                  const float* b_a, void* lx, void* la, hipStream_t s) {
+    constexpr int Db = 16 * MT;
+    const size_t lds = (size_t)2 * TT * (Db + XPAD) * 2;
+    const hipError_t e = allow_lds(gate_proj_fwd_kernel<MT>, lds);
     if (e != hipSuccess) return e;
-    LRS_LAUNCH(K_GATE_PROJ, gate_proj_fwd_kernel, grid, dim3(GP_THREADS), gate_proj_fwd_lds(D), s, BL, D,
-               (const uint16_t*)x, (const uint16_t*)w_x, b_x, (const uint16_t*)w_a, b_a, (uint16_t*)lx,
-               (uint16_t*)la);
+    const int range = stream_range(BL);
+    LRS_LAUNCH(K_GATE_PROJ, gate_proj_fwd_kernel<MT>, dim3(16, (unsigned)ceil_div(BL, range)),
+               dim3(64 * fwd_waves<MT>()), lds, s, BL, D, range, (const uint16_t*)x, (const uint16_t*)w_x, b_x,
+               (const uint16_t*)w_a, b_a, (uint16_t*)lx, (uint16_t*)la);
     return hipGetLastError();
 }
 
-size_t gate_proj_dx_lds(int D, int f32) {
-    const int Db = D / 16;
-    return (size_t)Db * (Db + GP_PAD) * 2 + (size_t)GP_TT * (Db + GP_PAD) * (f32 ? 4 : 2);
+template <int MT, bool F32>
+hipError_t bwd_mt(int BL, int D, const void* x, const void* w_x, const void* w_a, const void* dlx, const void* dla,
+                  const void* dx_in, void* dx_out, float* dw_part, float* db_part, hipStream_t s) {
+    constexpr size_t lds_dx = dx_lds_bytes<MT, F32>(), lds_dw = dw_lds_bytes<MT, F32>();
+    hipError_t e;
+    if ((e = allow_lds(gate_proj_dx_kernel<MT, F32>, lds_dx)) != hipSuccess) return e;
+    if ((e = allow_lds(gate_proj_dw_kernel<MT, F32>, lds_dw)) != hipSuccess) return e;
+    const int range = stream_range(BL);
+    LRS_LAUNCH(K_GATE_PROJ_DX, (gate_proj_dx_kernel<MT, F32>), dim3(16, (unsigned)ceil_div(BL, range)),
+               dim3(64 * dx_waves<MT>()), lds_dx, s, BL, D, range, (const uint16_t*)w_x, (const uint16_t*)w_a, dlx,
+               dla, dx_in, dx_out);
+    LRS_LAUNCH(K_GATE_PROJ_DW, (gate_proj_dw_kernel<MT, F32>), dim3(16, (unsigned)gate_proj_ranges(BL)),
+               dim3(64 * dw_waves<MT>()), lds_dw, s, BL, D, LRS_GP_DW_RANGE, (const uint16_t*)x, dlx, dla, dw_part,
+               db_part);
+    return hipGetLastError();
 }
 
-size_t gate_proj_dw_lds(int D, int f32) {
-    const int Db = D / 16;
-    return (size_t)Db * (GP_TT + GP_PAD) * 2 + (size_t)2 * 64 * (GP_TT + GP_PAD) * (f32 ? 4 : 2);
-}
+}  // namespace
 
-template <class F>
-static hipError_t allow_lds(F* kernel, size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)bytes);
+#define GP_MT_CASES(F) F(1) F(2) F(3) F(4) F(5) F(6) F(7) F(8) F(9) F(10)
+
+hipError_t launch_gate_proj_fwd(int BL, int D, const void* x, const void* w_x, const float* b_x,
+                                const void* w_a, const float* b_a, void* lx, void* la, hipStream_t s) {
+    switch (D / 256) {
+#define GP_FWD_CASE(M) \
+    case M: return fwd_mt<M>(BL, D, x, w_x, b_x, w_a, b_a, lx, la, s);
+        GP_MT_CASES(GP_FWD_CASE)
+#undef GP_FWD_CASE
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gate_proj_bwd(int BL, int D, const void* x, const void* w_x, const void* w_a, const void* dlx,
                                 const void* dla, int f32, const void* dx_in, void* dx_out, float* dw_x,
                                 float* db_x, float* dw_a, float* db_a, float* dw_part, float* db_part,
                                 hipStream_t s) {
-    const int Db = D / 16;
-    const size_t lds_dx = gate_proj_dx_lds(D, f32), lds_dw = gate_proj_dw_lds(D, f32);
-    const int nr = gate_proj_ranges(BL);
-    const dim3 gdx((unsigned)ceil_div(BL, GP_TT), 16), gdw((unsigned)nr, 16, (unsigned)ceil_div(Db / 16, 4));
-    hipError_t e;
-    if (f32) {
-        if ((e = allow_lds(gate_proj_dx_kernel<true>, lds_dx)) != hipSuccess) return e;
-        if ((e = allow_lds(gate_proj_dw_kernel<true>, lds_dw)) != hipSuccess) return e;
-        LRS_LAUNCH(K_GATE_PROJ_BWD, gate_proj_dx_kernel<true>, gdx, dim3(GP_THREADS), lds_dx, s, BL, D,
-                   (const uint16_t*)w_x, (const uint16_t*)w_a, dlx, dla, dx_in, dx_out);
-        LRS_LAUNCH(K_GATE_PROJ_BWD, gate_proj_dw_kernel<true>, gdw, dim3(GP_THREADS), lds_dw, s, BL, D, GP_RANGE,
-                   (const uint16_t*)x, dlx, dla, dw_part, db_part);
-    } else {
-        if ((e = allow_lds(gate_proj_dx_kernel<false>, lds_dx)) != hipSuccess) return e;
-        if ((e = allow_lds(gate_proj_dw_kernel<false>, lds_dw)) != hipSuccess) return e;
-        LRS_LAUNCH(K_GATE_PROJ_BWD, gate_proj_dx_kernel<false>, gdx, dim3(GP_THREADS), lds_dx, s, BL, D,
-                   (const uint16_t*)w_x, (const uint16_t*)w_a, dlx, dla, dx_in, dx_out);
-        LRS_LAUNCH(K_GATE_PROJ_BWD, gate_proj_dw_kernel<false>, gdw, dim3(GP_THREADS), lds_dw, s, BL, D,
-                   GP_RANGE, (const uint16_t*)x, dlx, dla, dw_part, db_part);
+    hipError_t e = hipErrorInvalidValue;
+    switch (D / 256) {
+#define GP_BWD_CASE(M)                                                                                       \
+    case M:                                                                                                  \
+        e = f32 ? bwd_mt<M, true>(BL, D, x, w_x, w_a, dlx, dla, dx_in, dx_out, dw_part, db_part, s)          \
+                : bwd_mt<M, false>(BL, D, x, w_x, w_a, dlx, dla, dx_in, dx_out, dw_part, db_part, s);        \
+        break;
+        GP_MT_CASES(GP_BWD_CASE)
+#undef GP_BWD_CASE
+        default: break;
     }
+    if (e != hipSuccess) return e;
+    const int Db = D / 16;
     const int nw = 2 * 16 * Db * Db;
-    LRS_LAUNCH(K_GATE_PROJ_BWD, gate_proj_reduce_kernel, dim3((unsigned)ceil_div(nw + 2 * D, 256)), dim3(256), 0,
-               s, nr, nw, D, dw_part, db_part, dw_x, dw_a, db_x, db_a);
+    LRS_LAUNCH(K_GATE_PROJ_REDUCE, gate_proj_reduce_kernel, dim3((unsigned)ceil_div(nw + 2 * D, 256)), dim3(256), 0,
+               s, gate_proj_ranges(BL), nw, D, dw_part, db_part, dw_x, dw_a, db_x, db_a);
     return hipGetLastError();
 }
 

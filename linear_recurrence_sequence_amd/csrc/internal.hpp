@@ -36,7 +36,9 @@ enum KernelId {
     K_BASE_SEQ,
     K_BASE_ASSOC,
     K_GATE_PROJ,
-    K_GATE_PROJ_BWD,
+    K_GATE_PROJ_DX,
+    K_GATE_PROJ_DW,
+    K_GATE_PROJ_REDUCE,
     K_NUM_KERNELS
 };
 

@@ -112,6 +112,17 @@ def rglru_proj_inputs(D, seed):
     return out
 
 
+def proj_cotangents(B, L, D, seed, *, bf16=False, std=0.01):
+    """Logit cotangents dlx, dla and an incoming input gradient dx, all
+    [B, L, D] ~ N(0, std^2): FP32, or BF16 bits when bf16 is set."""
+    rng = _rng(seed)
+    out = {}
+    for k in ("dlx", "dla", "dx"):
+        a = (std * rng.standard_normal((B, L, D), dtype=np.float32)).astype(np.float32)
+        out[k] = bf16_bits(a) if bf16 else a
+    return out
+
+
 # Workloads the pages measure (seed = 1000 * workload index + row index).
 WORKLOADS = {
     "samu_b1_l2048_d1024": dict(kind="samu", B=1, L=2048, D=1024, seed=0),

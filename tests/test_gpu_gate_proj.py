@@ -116,3 +116,53 @@ def test_projection_in_place_and_deterministic():
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k], b[k]) and torch.equal(a[k], c[k]), k
+
+
+def _check_bf16_output(name, gpu_bf16, exact, mag):
+    """A BF16 result rounded from an FP32 sum: within half a BF16 ulp of the
+    exact value plus FP32 accumulation slack, and RNE of it off ties."""
+    g = to_f64(gpu_bf16)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact), 1e-30))) - 7)
+    slack = 1e-6 * mag + 1e-30
+    err = np.abs(g - exact)
+    assert np.all(err <= 0.5 * ulp + slack), (name, float(np.max(err / (0.5 * ulp + slack))))
+    rne = torch.from_numpy(exact).to(torch.bfloat16).double().numpy()
+    frac = np.mean(g != rne)
+    say(f"   {name}: values differing from the FP64 rounding (near ties): {frac:.2e}")
+    assert frac < 1e-3
+
+
+@pytest.mark.parametrize("D", [768, 1280, 2304])
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_projection_odd_tiles_and_modes(D, mode):
+    """Block widths of an odd number of 16-channel tiles (half-used last
+    pair), a ragged token count, both cotangent precisions: logits, dx, dW
+    and db against the FP64 oracle."""
+    from linear_recurrence_sequence_amd import scan
+    B, L = 2, 333
+    say(f"[gate proj] B={B} L={L} D={D} cotangents {mode}")
+    x = inputs.rglru_inputs(B, L, D, 900 + D)["x"]
+    prm = inputs.rglru_proj_inputs(D, 901 + D)
+    ct = inputs.proj_cotangents(B, L, D, 902 + D, bf16=(mode == "bf16"))
+    d = {k: dev_tensor(v) for k, v in {"x": x, **prm, **ct}.items()}
+    lx, la = scan.rglru_gate_proj_fwd(d["x"], d["w_x"], d["b_x"], d["w_a"], d["b_a"])
+    p = scan.rglru_gate_proj_bwd(d["x"], d["w_x"], d["w_a"], d["dlx"], d["dla"], d["dx"])
+    torch.cuda.synchronize()
+    _check_logits("l^x", lx, x, prm["w_x"], prm["b_x"])
+    _check_logits("l^a", la, x, prm["w_a"], prm["b_a"])
+    dx, dw_x, db_x = oracle.rglru_gate_proj_bwd(x, prm["w_x"], ct["dlx"], ct["dx"])
+    dx, dw_a, db_a = oracle.rglru_gate_proj_bwd(x, prm["w_a"], ct["dla"], dx)
+    errs = {"dw_x": rel_l2(to_f64(p["dw_x"]), dw_x), "db_x": rel_l2(to_f64(p["db_x"]), db_x),
+            "dw_a": rel_l2(to_f64(p["dw_a"]), dw_a), "db_a": rel_l2(to_f64(p["db_a"]), db_a)}
+    if mode == "f32":
+        errs["dx"] = rel_l2(to_f64(p["dx"]), dx)
+    else:
+        # |dx_in| + sum |W| |dl| bounds the FP32 accumulation error
+        mx, _, _ = oracle.rglru_gate_proj_bwd(np.abs(oracle.widen(x)), np.abs(oracle.widen(prm["w_x"])),
+                                              np.abs(oracle.widen(ct["dlx"])), np.abs(oracle.widen(ct["dx"])))
+        mag, _, _ = oracle.rglru_gate_proj_bwd(np.abs(oracle.widen(x)), np.abs(oracle.widen(prm["w_a"])),
+                                               np.abs(oracle.widen(ct["dla"])), mx)
+        _check_bf16_output("dx", p["dx"], dx, mag)
+    say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL_OUT, (k, v)
