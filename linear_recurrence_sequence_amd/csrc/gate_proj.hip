@@ -277,11 +277,17 @@ template <int MT, bool F32>
 constexpr int prefetch_depth() {
     return (F32 || MT >= 9) ? 1 : 2;
 }
+// tokens per tile of the adjoint kernels: halved for FP32 cotangents of the
+// widest blocks, whose staging registers would otherwise spill
+template <int MT, bool F32>
+constexpr int adj_tile() {
+    return (F32 && MT >= 9) ? 32 : TT;
+}
 
 template <int MT, bool F32>
 constexpr size_t dx_lds_bytes() {
     constexpr int Db = 16 * MT;
-    constexpr size_t tile = (size_t)2 * TT * (Db + (F32 ? FPAD : XPAD)) * (F32 ? 4 : 2);
+    constexpr size_t tile = (size_t)2 * adj_tile<MT, F32>() * (Db + (F32 ? FPAD : XPAD)) * (F32 ? 4 : 2);
     constexpr size_t wt = (size_t)Db * (Db + XPAD) * 2;
     return tile > wt ? tile : wt;
 }
@@ -293,15 +299,17 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
     using G = Geo<MT>;
     constexpr int Db = G::Db, NW = dx_waves<MT>(), NT = 64 * NW, ES = F32 ? 4 : 2;
     constexpr int RS = Db + (F32 ? FPAD : XPAD), RW = Db + XPAD;
-    constexpr int WPP = NW / G::P, TGW = 4 / WPP;  // waves per pair, token groups per wave and tile
-    constexpr int CPR = Db * ES / 16, NCH = 2 * TT * CPR, S = (NCH + NT - 1) / NT;
+    constexpr int T = adj_tile<MT, F32>();         // tokens per tile
+    constexpr int WPP = NW / G::P, TGW = (T / 16) / WPP;  // waves per pair, token groups per wave and tile
+    static_assert(TGW >= 1, "every wave owns a token group");
+    constexpr int CPR = Db * ES / 16, NCH = 2 * T * CPR, S = (NCH + NT - 1) / NT;
     constexpr int PF = prefetch_depth<MT, F32>();
     extern __shared__ uint16_t gp_lds[];
-    unsigned char* const tile = reinterpret_cast<unsigned char*>(gp_lds);  // [2 gates][TT][RS] x ES bytes
+    unsigned char* const tile = reinterpret_cast<unsigned char*>(gp_lds);  // [2 gates][T][RS] x ES bytes
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
     const int blk = blockIdx.x;
     const size_t tr0 = (size_t)blockIdx.y * range, tr1 = min((size_t)BL, tr0 + range);
-    const int ntile = (int)((tr1 - tr0 + TT - 1) / TT);
+    const int ntile = (int)((tr1 - tr0 + T - 1) / T);
     const int p = wave / WPP;
     const int tgb = (wave - p * WPP) * TGW;
     const int c0 = 32 * p + 8 * grp;
@@ -329,11 +337,11 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
     // unconditional loads, as in the forward: rows past the range re-read
     // its last row and only feed tokens whose dx is not stored
     auto load = [&](Regs& r, int i) {
-        const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * TT;
+        const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * T;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int c = NCH % NT == 0 ? threadIdx.x + s * NT : min((int)threadIdx.x + s * NT, NCH - 1);
-            const int gg = c / (TT * CPR), rem = c - gg * TT * CPR, row = rem / CPR, ch = rem - row * CPR;
+            const int gg = c / (T * CPR), rem = c - gg * T * CPR, row = rem / CPR, ch = rem - row * CPR;
             r.v[s] = ld16(reinterpret_cast<const unsigned char*>(gg ? dla : dlx) +
                           (min(t0 + row, tr1 - 1) * D + (size_t)blk * Db) * ES + ch * 16);
         }
@@ -342,8 +350,8 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int c = threadIdx.x + s * NT;
-            const int gg = c / (TT * CPR), rem = c - gg * TT * CPR, row = rem / CPR, ch = rem - row * CPR;
-            if (NCH % NT == 0 || c < NCH) st16(tile + ((size_t)(gg * TT + row) * RS) * ES + ch * 16, r.v[s]);
+            const int gg = c / (T * CPR), rem = c - gg * T * CPR, row = rem / CPR, ch = rem - row * CPR;
+            if (NCH % NT == 0 || c < NCH) st16(tile + ((size_t)(gg * T + row) * RS) * ES + ch * 16, r.v[s]);
         }
     };
     // dx_in of the tile, requested before the prefetch of later tiles so
@@ -351,7 +359,7 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
     // reads inside the range and the block
     struct In { v4u v[TGW][F32 ? 2 : 1]; };
     auto load_in = [&](In& d, int i) {
-        const size_t t0 = tr0 + (size_t)i * TT;
+        const size_t t0 = tr0 + (size_t)i * T;
 #pragma unroll
         for (int q = 0; q < TGW; ++q) {
             const int tok = (tgb + q) * 16 + col;
@@ -362,7 +370,7 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
         }
     };
     auto compute = [&](int i, const In& d) {
-        const size_t t0 = tr0 + (size_t)i * TT;
+        const size_t t0 = tr0 + (size_t)i * T;
 #pragma unroll
         for (int q = 0; q < TGW; ++q) {
             const int tok = (tgb + q) * 16 + col;
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
                 for (int ks = 0; ks < G::KS; ++ks) {
                     const bool half = G::ODD && ks == G::KS - 1;
                     const int o0 = 32 * ks + 8 * grp - ((half && grp >= 2) ? 16 : 0);
-                    const unsigned char* src = tile + ((size_t)(gg * TT + tok) * RS + o0) * ES;
+                    const unsigned char* src = tile + ((size_t)(gg * T + tok) * RS + o0) * ES;
                     if (F32) {
                         v4u hi, mid, lo;
                         split3(ld16(src), ld16(src + 16), hi, mid, lo);
@@ -467,7 +475,7 @@ constexpr int dw_row() {
 }
 template <int MT, bool F32>
 constexpr size_t dw_lds_bytes() {
-    return (size_t)TT * dw_row<MT>() * 2 * (1 + 2 * (F32 ? 3 : 1));
+    return (size_t)adj_tile<MT, F32>() * dw_row<MT>() * 2 * (1 + 2 * (F32 ? 3 : 1));
 }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -503,14 +511,15 @@ __global__ __launch_bounds__(64 * dw_waves<MT>()) void gate_proj_dw_kernel(
     constexpr int Db = 16 * MT, NW = dw_waves<MT>(), NT = 64 * NW, R = dw_rows<MT>();
     constexpr int RS = dw_row<MT>(), ES = F32 ? 4 : 2, NPL = F32 ? 3 : 1;
     constexpr int PF = prefetch_depth<MT, F32>();
-    constexpr int XCR = Db / 8, XC = TT * XCR;             // 16-byte chunks of x: per row, per tile
-    constexpr int LCR = Db * ES / 16, LC = TT * LCR;       // of one cotangent tile
+    constexpr int T = adj_tile<MT, F32>();  // tokens per tile
+    constexpr int XCR = Db / 8, XC = T * XCR;             // 16-byte chunks of x: per row, per tile
+    constexpr int LCR = Db * ES / 16, LC = T * LCR;       // of one cotangent tile
     constexpr int SX = (XC + NT - 1) / NT, SL = (LC + NT - 1) / NT;
-    extern __shared__ uint16_t gp_lds[];  // x [TT][RS], dl [2 gates][NPL planes][TT][RS]
+    extern __shared__ uint16_t gp_lds[];  // x [T][RS], dl [2 gates][NPL planes][T][RS]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
     const int blk = blockIdx.x, r = blockIdx.y;
     const size_t tr0 = (size_t)r * range, tr1 = min((size_t)BL, tr0 + range);
-    const int ntile = (int)((tr1 - tr0 + TT - 1) / TT);
+    const int ntile = (int)((tr1 - tr0 + T - 1) / T);
 
     v4f acc[R][MT + 1];
 #pragma unroll
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(64 * dw_waves<MT>()) void gate_proj_dw_kernel(
         return nchunks % NT == 0 ? c : min(c, nchunks - 1);
     };
     auto load = [&](Regs& b, int i) {
-        const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * TT;
+        const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * T;
         b.okx = b.okl = 0;
 #pragma unroll
         for (int s = 0; s < SX; ++s) {
@@ -552,7 +561,7 @@ __global__ __launch_bounds__(64 * dw_waves<MT>()) void gate_proj_dw_kernel(
             }
     };
     auto store = [&](const Regs& b, uint16_t* sx) {
-        uint16_t* const sl = sx + TT * RS;
+        uint16_t* const sl = sx + T * RS;
 #pragma unroll
         for (int s = 0; s < SX; ++s) {
             const int c = threadIdx.x + s * NT;
@@ -571,20 +580,20 @@ __global__ __launch_bounds__(64 * dw_waves<MT>()) void gate_proj_dw_kernel(
                 if (F32) {
                     uint2 hi, mid, lo;
                     split3x4(v, hi, mid, lo);
-                    uint16_t* d = sl + ((gg * 3) * TT + row) * RS + 4 * ch;
+                    uint16_t* d = sl + ((gg * 3) * T + row) * RS + 4 * ch;
                     *reinterpret_cast<uint2*>(d) = hi;
-                    *reinterpret_cast<uint2*>(d + TT * RS) = mid;
-                    *reinterpret_cast<uint2*>(d + 2 * TT * RS) = lo;
+                    *reinterpret_cast<uint2*>(d + T * RS) = mid;
+                    *reinterpret_cast<uint2*>(d + 2 * T * RS) = lo;
                 } else {
-                    st16(sl + (gg * TT + row) * RS + 8 * ch, v);
+                    st16(sl + (gg * T + row) * RS + 8 * ch, v);
                 }
             }
     };
     const v4u ones = col == 0 ? v4u{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u} : zero4();
     auto compute = [&](const uint16_t* sx) {
-        const uint16_t* const sl = sx + TT * RS;
+        const uint16_t* const sl = sx + T * RS;
 #pragma unroll
-        for (int kt = 0; kt < TT; kt += 32) {
+        for (int kt = 0; kt < T; kt += 32) {
             const int toff = (kt + 8 * grp + (col >> 2)) * RS + 4 * (col & 3);  // this lane's read address
             v4u af[R][NPL];
 #pragma unroll
@@ -593,7 +602,7 @@ __global__ __launch_bounds__(64 * dw_waves<MT>()) void gate_proj_dw_kernel(
                 const int rc = row < 2 * MT ? row : 0;
                 const int gg = rc / MT, mo = rc - gg * MT;
 #pragma unroll
-                for (int p = 0; p < NPL; ++p) af[j][p] = tr_frag(sl + (gg * NPL + p) * TT * RS + toff + mo * 16, RS);
+                for (int p = 0; p < NPL; ++p) af[j][p] = tr_frag(sl + (gg * NPL + p) * T * RS + toff + mo * 16, RS);
             }
 #pragma unroll
             for (int n = 0; n <= MT; ++n) {
