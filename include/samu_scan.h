@@ -231,8 +231,14 @@ scan_status rglru_gate_proj_fwd(int B, int L, int D, const void* x,
  *   dx_out = dx_in + per block W_x^T dlx + W_a^T dla   ([B, L, D], grad_dtype;
  *            dx_out may equal dx_in, must not overlap it otherwise),
  *   dw = sum_t dl x^T per block (f32 [16, D/16, D/16]), db = sum_t dl (f32 [D]).
- * SCAN_F32 cotangents use FP32 matrix-core products; the token sums are
- * split over fixed ranges and added in range order (deterministic). */
+ * SCAN_F32 cotangents are split exactly into three BF16 terms (hi + mid +
+ * lo), each multiplied on the BF16 matrix cores with FP32 accumulation --
+ * the same exact products as FP32 multiplies.  The token sums for dw and db
+ * are split over fixed ranges of 2048 tokens, whose FP32 partials (in the
+ * caller's workspace, rglru_gate_proj_bwd_workspace_bytes bytes) are added
+ * in range order in FP64: results are bitwise reproducible.  Errors as for
+ * the scans: shape, dtype code, NULL, alignment, aliasing and workspace size
+ * are checked before anything is queued. */
 size_t rglru_gate_proj_bwd_workspace_bytes(int B, int L, int D);
 scan_status rglru_gate_proj_bwd(int B, int L, int D, const void* x,
                                 const void* w_x, const void* w_a,
