@@ -104,6 +104,12 @@ __device__ __forceinline__ void split3(v4u a, v4u b, v4u& hi, v4u& mid, v4u& lo)
 #ifndef LRS_GP_FWD_NT
 #define LRS_GP_FWD_NT 1
 #endif
+// forward logits staged through LDS and written as whole token rows (each
+// 128-byte line by one store instruction) instead of by the four lanes that
+// hold a token's channels of one pair
+#ifndef LRS_GP_FWD_STAGE
+#define LRS_GP_FWD_STAGE 1
+#endif
 __device__ __forceinline__ void sched_fence() {
     if (LRS_GP_FENCE) __builtin_amdgcn_sched_barrier(0);
 }
@@ -155,9 +161,11 @@ __global__ __launch_bounds__(64 * fwd_waves<MT>()) void gate_proj_fwd_kernel(
     using G = Geo<MT>;
     constexpr int Db = G::Db, NW = fwd_waves<MT>(), NT = 64 * NW, RS = Db + XPAD;
     constexpr int CPR = Db / 8, NCH = TT * CPR, S = (NCH + NT - 1) / NT;  // 16-byte chunks
+    constexpr bool STAGE = LRS_GP_FWD_STAGE != 0;
     extern __shared__ uint16_t gp_lds[];
     uint16_t* const buf0 = gp_lds;
     uint16_t* const buf1 = gp_lds + TT * RS;
+    uint16_t* const sout = gp_lds + 2 * TT * RS;  // STAGE: logits [2 gates][TT][RS]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
     const int blk = blockIdx.x;
     const size_t tr0 = (size_t)blockIdx.y * range, tr1 = min((size_t)BL, tr0 + range);
@@ -224,11 +232,27 @@ __global__ __launch_bounds__(64 * fwd_waves<MT>()) void gate_proj_fwd_kernel(
                 a0 = mfma(wf[0][ks], xf, a0);
                 a1 = mfma(wf[1][ks], xf, a1);
             }
-            if (cv && t0 + tok < tr1)  // streamed past the caches by default (measured the better choice for the layer)
-                out_store<u32x4_t, LRS_GP_FWD_NT != 0>(
-                    out + (t0 + tok) * D,
-                    u32x4_t{pack_bf16x2(a0[0] + bz0.x, a0[1] + bz0.y), pack_bf16x2(a0[2] + bz0.z, a0[3] + bz0.w),
-                            pack_bf16x2(a1[0] + bz1.x, a1[1] + bz1.y), pack_bf16x2(a1[2] + bz1.z, a1[3] + bz1.w)});
+            const u32x4_t v{pack_bf16x2(a0[0] + bz0.x, a0[1] + bz0.y), pack_bf16x2(a0[2] + bz0.z, a0[3] + bz0.w),
+                            pack_bf16x2(a1[0] + bz1.x, a1[1] + bz1.y), pack_bf16x2(a1[2] + bz1.z, a1[3] + bz1.w)};
+            if (STAGE) {
+                if (cv) *reinterpret_cast<u32x4_t*>(sout + (g * TT + tok) * RS + c0) = v;
+            } else if (cv && t0 + tok < tr1) {  // streamed past the caches by default (the better choice for the layer)
+                out_store<u32x4_t, LRS_GP_FWD_NT != 0>(out + (t0 + tok) * D, v);
+            }
+        }
+    };
+    // the staged logits of tile i, whole rows of Db channels per gate
+    constexpr int OCH = 2 * TT * CPR, SO = (OCH + NT - 1) / NT;
+    auto flush = [&](int i) {
+        const size_t t0 = tr0 + (size_t)i * TT;
+#pragma unroll
+        for (int s = 0; s < SO; ++s) {
+            const int c = threadIdx.x + s * NT;
+            if (OCH % NT != 0 && c >= OCH) continue;
+            const int gg = c / (TT * CPR), rem = c - gg * TT * CPR, row = rem / CPR, k8 = (rem - row * CPR) * 8;
+            if (t0 + row < tr1)
+                out_store<u32x4_t, LRS_GP_FWD_NT != 0>((gg ? la : lx) + (t0 + row) * D + (size_t)blk * Db + k8,
+                                                       *reinterpret_cast<const u32x4_t*>(sout + (gg * TT + row) * RS + k8));
         }
     };
 
@@ -252,12 +276,20 @@ __global__ __launch_bounds__(64 * fwd_waves<MT>()) void gate_proj_fwd_kernel(
         load(rb, i + 3);
         sched_fence();
         __syncthreads();
+        if (STAGE) {
+            flush(i);
+            __syncthreads();  // the staged logits are read before the next tile overwrites them
+        }
         compute(i + 1, buf1);
         sched_fence();
         store(ra, buf0);
         load(ra, i + 4);
         sched_fence();
         __syncthreads();
+        if (STAGE) {
+            flush(i + 1);
+            __syncthreads();
+        }
     }
 }
 
@@ -696,7 +728,7 @@ template <int MT>
 hipError_t fwd_mt(int BL, int D, const void* x, const void* w_x, const float* b_x, const void* w_a,
                   const float* b_a, void* lx, void* la, hipStream_t s) {
     constexpr int Db = 16 * MT;
-    const size_t lds = (size_t)2 * TT * (Db + XPAD) * 2;
+    const size_t lds = (size_t)(LRS_GP_FWD_STAGE ? 4 : 2) * TT * (Db + XPAD) * 2;
     const hipError_t e = allow_lds(gate_proj_fwd_kernel<MT>, lds);
     if (e != hipSuccess) return e;
     const int range = stream_range(BL);
