@@ -316,10 +316,23 @@ constexpr int adj_tile() {
     return (F32 && MT >= 9) ? 32 : TT;
 }
 
+// dx_in rows staged through LDS with the cotangent tiles and dx_out written
+// back from there as whole token rows (rather than 64-byte pieces per lane
+// group); measured faster up to 8 tiles per block, slower for the five-wave
+// workgroups of the widest blocks
+#ifndef LRS_GP_DX_STAGE
+#define LRS_GP_DX_STAGE 1
+#endif
+template <int MT>
+constexpr bool dx_stage() {
+    return LRS_GP_DX_STAGE != 0 && MT <= 8;
+}
+
 template <int MT, bool F32>
 constexpr size_t dx_lds_bytes() {
     constexpr int Db = 16 * MT;
-    constexpr size_t tile = (size_t)2 * adj_tile<MT, F32>() * (Db + (F32 ? FPAD : XPAD)) * (F32 ? 4 : 2);
+    constexpr size_t tile =
+        (size_t)(dx_stage<MT>() ? 3 : 2) * adj_tile<MT, F32>() * (Db + (F32 ? FPAD : XPAD)) * (F32 ? 4 : 2);
     constexpr size_t wt = (size_t)Db * (Db + XPAD) * 2;
     return tile > wt ? tile : wt;
 }
@@ -334,10 +347,14 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
     constexpr int T = adj_tile<MT, F32>();         // tokens per tile
     constexpr int WPP = NW / G::P, TGW = (T / 16) / WPP;  // waves per pair, token groups per wave and tile
     static_assert(TGW >= 1, "every wave owns a token group");
-    constexpr int CPR = Db * ES / 16, NCH = 2 * T * CPR, S = (NCH + NT - 1) / NT;
+    constexpr bool STAGE = dx_stage<MT>();
+    constexpr int DX_PLANES = STAGE ? 3 : 2;
+    constexpr int CPR = Db * ES / 16, NCH = T * CPR, S = (NCH + NT - 1) / NT;  // 16-byte chunks per plane
     constexpr int PF = prefetch_depth<MT, F32>();
     extern __shared__ uint16_t gp_lds[];
-    unsigned char* const tile = reinterpret_cast<unsigned char*>(gp_lds);  // [2 gates][T][RS] x ES bytes
+    // [2 gates (+ dx rows when STAGE)][T][RS] x ES bytes
+    unsigned char* const tile = reinterpret_cast<unsigned char*>(gp_lds);
+    unsigned char* const sio = tile + (size_t)2 * T * RS * ES;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
     const int blk = blockIdx.x;
     const size_t tr0 = (size_t)blockIdx.y * range, tr1 = min((size_t)BL, tr0 + range);
@@ -365,26 +382,32 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
         }
     }
 
-    struct Regs { v4u v[S]; };
+    // planes: dl^x, dl^a and (STAGE) the dx_in rows
+    struct Regs { v4u v[DX_PLANES][S]; };
     // unconditional loads, as in the forward: rows past the range re-read
     // its last row and only feed tokens whose dx is not stored
     auto load = [&](Regs& r, int i) {
         const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * T;
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const int c = NCH % NT == 0 ? threadIdx.x + s * NT : min((int)threadIdx.x + s * NT, NCH - 1);
-            const int gg = c / (T * CPR), rem = c - gg * T * CPR, row = rem / CPR, ch = rem - row * CPR;
-            r.v[s] = ld16(reinterpret_cast<const unsigned char*>(gg ? dla : dlx) +
-                          (min(t0 + row, tr1 - 1) * D + (size_t)blk * Db) * ES + ch * 16);
+        for (int pl = 0; pl < DX_PLANES; ++pl) {
+            const unsigned char* src = reinterpret_cast<const unsigned char*>(pl == 0 ? dlx : (pl == 1 ? dla : dx_in));
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int c = NCH % NT == 0 ? threadIdx.x + s * NT : min((int)threadIdx.x + s * NT, NCH - 1);
+                const int row = c / CPR, ch = c - row * CPR;
+                r.v[pl][s] = ld16(src + (min(t0 + row, tr1 - 1) * D + (size_t)blk * Db) * ES + ch * 16);
+            }
         }
     };
     auto store = [&](const Regs& r) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const int c = threadIdx.x + s * NT;
-            const int gg = c / (T * CPR), rem = c - gg * T * CPR, row = rem / CPR, ch = rem - row * CPR;
-            if (NCH % NT == 0 || c < NCH) st16(tile + ((size_t)(gg * T + row) * RS) * ES + ch * 16, r.v[s]);
-        }
+        for (int pl = 0; pl < DX_PLANES; ++pl)
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int c = threadIdx.x + s * NT;
+                const int row = c / CPR, ch = c - row * CPR;
+                if (NCH % NT == 0 || c < NCH) st16(tile + ((size_t)(pl * T + row) * RS) * ES + ch * 16, r.v[pl][s]);
+            }
     };
     // dx_in of the tile, requested before the prefetch of later tiles so
     // that waiting for it does not wait for them; a lane that stores nothing
@@ -408,8 +431,15 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
             const int tok = (tgb + q) * 16 + col;
             const bool tv = cv && t0 + tok < tr1;
             const size_t dst = ((t0 + tok) * D + (size_t)blk * Db + c0) * ES;
-            const v4u in0 = d.v[q][0];
-            const v4u in1 = d.v[q][F32 ? 1 : 0];
+            unsigned char* const sdx = sio + ((size_t)tok * RS + min(c0, Db - 8)) * ES;
+            v4u in0, in1 = zero4();
+            if constexpr (STAGE) {
+                in0 = ld16(sdx);
+                if (F32) in1 = ld16(sdx + 16);
+            } else {
+                in0 = d.v[q][0];
+                in1 = d.v[q][F32 ? 1 : 0];
+            }
             v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
             for (int gg = 0; gg < 2; ++gg) {
@@ -436,19 +466,44 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
                     }
                 }
             }
-            if (tv) {
-                unsigned char* o = reinterpret_cast<unsigned char*>(dx_out) + dst;
-                if (F32) {
-                    out_f32x4(o, __uint_as_float(in0.x) + a0[0], __uint_as_float(in0.y) + a0[1],
-                              __uint_as_float(in0.z) + a0[2], __uint_as_float(in0.w) + a0[3]);
-                    out_f32x4(o + 16, __uint_as_float(in1.x) + a1[0], __uint_as_float(in1.y) + a1[1],
-                              __uint_as_float(in1.z) + a1[2], __uint_as_float(in1.w) + a1[3]);
-                } else {
-                    out_u32x4(o, pack_bf16x2(bf16_lo(in0.x) + a0[0], bf16_hi(in0.x) + a0[1]),
-                              pack_bf16x2(bf16_lo(in0.y) + a0[2], bf16_hi(in0.y) + a0[3]),
-                              pack_bf16x2(bf16_lo(in0.z) + a1[0], bf16_hi(in0.z) + a1[1]),
-                              pack_bf16x2(bf16_lo(in0.w) + a1[2], bf16_hi(in0.w) + a1[3]));
+            v4u r0, r1 = zero4();
+            if (F32) {
+                r0 = v4u{__float_as_uint(__uint_as_float(in0.x) + a0[0]), __float_as_uint(__uint_as_float(in0.y) + a0[1]),
+                         __float_as_uint(__uint_as_float(in0.z) + a0[2]), __float_as_uint(__uint_as_float(in0.w) + a0[3])};
+                r1 = v4u{__float_as_uint(__uint_as_float(in1.x) + a1[0]), __float_as_uint(__uint_as_float(in1.y) + a1[1]),
+                         __float_as_uint(__uint_as_float(in1.z) + a1[2]), __float_as_uint(__uint_as_float(in1.w) + a1[3])};
+            } else {
+                r0 = v4u{pack_bf16x2(bf16_lo(in0.x) + a0[0], bf16_hi(in0.x) + a0[1]),
+                         pack_bf16x2(bf16_lo(in0.y) + a0[2], bf16_hi(in0.y) + a0[3]),
+                         pack_bf16x2(bf16_lo(in0.z) + a1[0], bf16_hi(in0.z) + a1[1]),
+                         pack_bf16x2(bf16_lo(in0.w) + a1[2], bf16_hi(in0.w) + a1[3])};
+            }
+            if (STAGE) {  // back into the staged row, written out whole by flush()
+                if (cv) {
+                    st16(sdx, r0);
+                    if (F32) st16(sdx + 16, r1);
                 }
+            } else if (tv) {
+                unsigned char* o = reinterpret_cast<unsigned char*>(dx_out) + dst;
+                out_store<u32x4_t>(o, u32x4_t{r0.x, r0.y, r0.z, r0.w});
+                if (F32) out_store<u32x4_t>(o + 16, u32x4_t{r1.x, r1.y, r1.z, r1.w});
+            }
+        }
+    };
+    // the staged dx rows of tile i
+    constexpr int OCH = NCH, SO = S;
+    auto flush = [&](int i) {
+        const size_t t0 = tr0 + (size_t)i * T;
+#pragma unroll
+        for (int s = 0; s < SO; ++s) {
+            const int c = threadIdx.x + s * NT;
+            if (OCH % NT != 0 && c >= OCH) continue;
+            const int row = c / CPR, ch = c - row * CPR;
+            if (t0 + row < tr1) {
+                const v4u v = ld16(sio + (size_t)row * RS * ES + ch * 16);
+                out_store<u32x4_t>(reinterpret_cast<unsigned char*>(dx_out) + ((t0 + row) * D + (size_t)blk * Db) * ES +
+                                       ch * 16,
+                                   u32x4_t{v.x, v.y, v.z, v.w});
             }
         }
     };
@@ -466,7 +521,7 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             In d;
-            load_in(d, i + j);
+            if constexpr (!STAGE) load_in(d, i + j);
             sched_fence();
             __syncthreads();  // the previous tile (or the weight staging) is no longer read
             sched_fence();
@@ -475,6 +530,10 @@ __global__ __launch_bounds__(64 * dx_waves<MT>()) void gate_proj_dx_kernel(
             sched_fence();
             __syncthreads();
             compute(i + j, d);
+            if (STAGE) {
+                __syncthreads();  // the tile's dx rows are complete
+                flush(i + j);
+            }
         }
     }
 }
