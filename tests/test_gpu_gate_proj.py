@@ -132,12 +132,13 @@ def _check_bf16_output(name, gpu_bf16, exact, mag):
     assert frac < 1e-3
 
 
-@pytest.mark.parametrize("D", [768, 1280, 2304])
+@pytest.mark.parametrize("D", [768, 1024, 1280, 1536, 1792, 2304])
 @pytest.mark.parametrize("mode", ["f32", "bf16"])
 def test_projection_odd_tiles_and_modes(D, mode):
-    """Block widths of an odd number of 16-channel tiles (half-used last
-    pair), a ragged token count, both cotangent precisions: logits, dx, dW
-    and db against the FP64 oracle."""
+    """Every block width the other tests do not reach (3 to 9 tiles of 16
+    channels, the odd ones with a half-used last pair), a ragged token count,
+    both cotangent precisions: logits, dx, dW and db against the FP64
+    oracle."""
     from linear_recurrence_sequence_amd import scan
     B, L = 2, 333
     say(f"[gate proj] B={B} L={L} D={D} cotangents {mode}")
