@@ -288,6 +288,30 @@ def main():
     for name, (tot, cnt) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
         log(f"    {name:24s} {tot / cnt * 1e3:9.2f} us/launch  x{cnt // args.steps}/step")
 
+    # the same step replayed from a captured HIP graph (8 steps per graph; no
+    # library call allocates or clears memory, so the whole pass captures);
+    # the replayed gradients must equal an eager step's bit for bit
+    log("[bench] SAMU F+B replayed from a HIP graph")
+    samu_step()
+    torch.cuda.synchronize()
+    db_ref = out["db"].clone()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gs):
+        for _ in range(2):
+            samu_step()
+    torch.cuda.current_stream().wait_stream(gs)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(8):
+            samu_step()
+    gms, _ = timed(graph.replay, max(2, args.steps // 8), 1, False)
+    ms_graph = gms / 8
+    graph_equal = bool(torch.equal(out["db"], db_ref))
+    del graph
+    log(f"[bench] SAMU F+B {ms_graph:.4f} ms/step from a graph (replayed db equal to eager: {graph_equal})")
+
     floor_bytes = 16.0 * B * L * D
     value = floor_bytes / (ms * 1e-3) / 1e9
 
@@ -421,6 +445,7 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "ms_per_step_with_kernel_events": round(ms_ev, 4),
         "launches_per_step": launches_per_step,
+        "ms_per_step_graph": round(ms_graph, 4), "graph_replay_equal": graph_equal,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
