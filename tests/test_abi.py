@@ -184,7 +184,12 @@ def test_gate_projection_rejects_before_enqueue():
     # two range partials of [2][16][32][32] plus [2][512] floats, 256-byte aligned
     assert 2 * (2 * 16 * 32 * 32 + 2 * 512) * 4 <= n < 2 * (2 * 16 * 32 * 32 + 2 * 512) * 4 + 512
     args = [f(0x100000), f(0x300000), f(0x310000), f(0x320000), f(0x330000)]
+    assert L.rglru_gate_proj_bwd_workspace_bytes(0, 64, 512) == 0            # empty batch
+    assert L.rglru_gate_proj_bwd_workspace_bytes(1, 0, 512) == 0             # empty sequence
     assert L.rglru_gate_proj_fwd(1, 8, 384, *args, f(0x500000), f(0x600000), None) == -2
+    assert L.rglru_gate_proj_fwd(0, 8, 256, *args, f(0x500000), f(0x600000), None) == -2
+    assert L.rglru_gate_proj_fwd(1, 0, 256, *args, f(0x500000), f(0x600000), None) == -2
+    assert L.rglru_gate_proj_fwd(1, 8, 256, *args, f(0x500008), f(0x600000), None) == -3   # misaligned
     assert L.rglru_gate_proj_fwd(1, 8, 256, *args, None, f(0x600000), None) == -1
     assert L.rglru_gate_proj_fwd(1, 8, 256, *args, f(0x100000), f(0x600000), None) == -6     # lx over x
     bw = [f(0x100000), f(0x300000), f(0x320000), f(0x400000), f(0x500000)]
