@@ -19,6 +19,7 @@ launch, so ms_per_step comes from the first run, without them).
 import argparse
 import hashlib
 import json
+import statistics
 import os
 import re
 import sys
@@ -376,6 +377,35 @@ def main():
         log(f"[bench] RG-LRU F+B {rg_ms:.4f} ms/step; SAMU reduction {(rg_ms - ms) / rg_ms:.1%}; "
             f"with gate projections {layer_ms:.4f} ms/step {proj}")
 
+        # the pages' sampling protocol: after warmups, two rounds of five
+        # individually timed F+B samples per variant, the order of the
+        # variants swapped between rounds; median, [min, max] and every sample
+        log("[bench] paired protocol: 2 rounds x 5 samples, order swapped between rounds")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def one(step):
+            torch.cuda.synchronize()
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
+        samples = {"samu": [], "rglru": []}
+        steps_by = {"samu": samu_step, "rglru": rg_step}
+        for _ in range(3):
+            samu_step()
+            rg_step()
+        for rnd in range(2):
+            for name in (("samu", "rglru") if rnd == 0 else ("rglru", "samu")):
+                samples[name] += [round(one(steps_by[name]), 4) for _ in range(5)]
+        paired = {n: {"median_ms": round(statistics.median(v), 4), "min_ms": min(v), "max_ms": max(v),
+                      "samples_ms": v} for n, v in samples.items()}
+        paired["samu_time_reduction_median"] = round(
+            (paired["rglru"]["median_ms"] - paired["samu"]["median_ms"]) / paired["rglru"]["median_ms"], 4)
+        rg["paired_protocol"] = paired
+        log(f"[bench] paired medians: SAMU {paired['samu']['median_ms']} ms, RG-LRU {paired['rglru']['median_ms']} ms")
+
     dec = None
     if not args.no_decode:
         log("[bench] SAMU decode step (one token, state in place) at D=%d" % D)
@@ -445,6 +475,11 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "ms_per_step_with_kernel_events": round(ms_ev, 4),
         "launches_per_step": launches_per_step,
+        "token_channels_per_s": round(B * L * D / (ms * 1e-3), 1),
+        "workspace_bytes": {"saved": scan.samu_scan_saved_bytes(B, L, D, K),
+                            "forward": scan.samu_scan_workspace_bytes(B, L, D, K, G, False),
+                            "backward": scan.samu_scan_workspace_bytes(B, L, D, K, G, True),
+                            "pages_prefix_scratch_formula": scan.scan_prefix_scratch_bytes(B, L, D, K, G)},
         "ms_per_step_graph": round(ms_graph, 4), "graph_replay_equal": graph_equal,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
