@@ -55,27 +55,6 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     __shared__ float red[2][CTL_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    for (int m = blockIdx.x * CTL_THREADS + tid; m < M; m += gridDim.x * CTL_THREADS)
-        store_mode(mtab, m, mode_const(nu[m], theta[m]), chunk_phase(theta[m], K), chunk_phase(theta[m], K_last));
-
-    // direction norms over all D+1 entries
-    float sp = 0.f, sr = 0.f;
-    for (int j = tid; j <= D; j += CTL_THREADS) {
-        sp = fmaf(w_phi[j], w_phi[j], sp);
-        sr = fmaf(w_r[j], w_r[j], sr);
-    }
-    sp = wave_sum(sp);
-    sr = wave_sum(sr);
-    if (lane == 0) { red[0][wave] = sp; red[1][wave] = sr; }
-    __syncthreads();
-    float np = 0.f, nr = 0.f;
-#pragma unroll
-    for (int i = 0; i < CTL_WAVES; ++i) { np += red[0][i]; nr += red[1][i]; }
-    const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
-    const float amp_phi = tanhf(a_phi[0]) / sqrtf((float)M);
-    const float amp_r = tanhf(a_r[0]) / sqrtf((float)M);
-    const float bias_phi = w_phi[D], bias_r = w_r[D];
-
     const int D8 = D >> 3;  // 16-byte words per row
     const int tok0 = blockIdx.x * CTL_TOK_PER_BLOCK + wave * CTL_TOK;
     float ap[CTL_TOK], ar[CTL_TOK];
@@ -123,6 +102,30 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
         const float sp_q = wave_sum(ap[q]), sr_q = wave_sum(ar[q]);
         if (lane == q) { up = sp_q; ur = sr_q; }
     }
+
+    // The dot products above use the raw directions, so the norms (small,
+    // cache-resident reads) come after the selector stream has been consumed
+    // rather than delaying its first request.
+    for (int m = blockIdx.x * CTL_THREADS + tid; m < M; m += gridDim.x * CTL_THREADS)
+        store_mode(mtab, m, mode_const(nu[m], theta[m]), chunk_phase(theta[m], K), chunk_phase(theta[m], K_last));
+    // direction norms over all D+1 entries
+    float sp = 0.f, sr = 0.f;
+    for (int j = tid; j <= D; j += CTL_THREADS) {
+        sp = fmaf(w_phi[j], w_phi[j], sp);
+        sr = fmaf(w_r[j], w_r[j], sr);
+    }
+    sp = wave_sum(sp);
+    sr = wave_sum(sr);
+    if (lane == 0) { red[0][wave] = sp; red[1][wave] = sr; }
+    __syncthreads();
+    float np = 0.f, nr = 0.f;
+#pragma unroll
+    for (int i = 0; i < CTL_WAVES; ++i) { np += red[0][i]; nr += red[1][i]; }
+    const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
+    const float amp_phi = tanhf(a_phi[0]) / sqrtf((float)M);
+    const float amp_r = tanhf(a_r[0]) / sqrtf((float)M);
+    const float bias_phi = w_phi[D], bias_r = w_r[D];
+
     const int tok = tok0 + lane;
     if (lane < CTL_TOK && tok < BL) {
         // x~ . w^ = (x_sel . w[0:D] + w[D]) / ||w||
