@@ -57,6 +57,8 @@ def kernel_bytes(name, B, L, D, K, G):
     BL, BLD, BCM = B * L, B * L * D, B * C * M
     n_tiles = -(-M // 64)
     BC = B * C
+    NMID = K // 16 - 1 if K > 16 else 0  # states entering the later 16-token halves of a chunk
+    BMID = B * C * NMID * M
     table = {
         # x_sel, both direction vectors -> p, r, (u_phi, u_r), (E, C, S, d), mode table
         "samu_controller": 2 * BLD + 8 * (D + 1) + 32 * BL + 64 * M,
@@ -69,11 +71,11 @@ def kernel_bytes(name, B, L, D, K, G):
         "prefix_group_scan": 16 * B * NG * M + 8 * B * M + 8 * B * NG * M,
         # group entry states, compressed chunk summaries -> state entering every chunk
         "prefix_chunk_entries": 8 * B * NG * M + 8 * BCM + 16 * BC + 48 * M + 8 * BCM,
-        # b, (E, C, S, d), entry states -> y, final state
-        "samu_replay": 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 2 * BLD + 8 * B * M,
-        # dy, b, (E, C, S, d), entry states, adjoint carries -> db, per-tile controller
-        # partials, per-(chunk, mode) spectrum partials
-        "samu_bwd_replay": 2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BCM + 2 * BLD
+        # b, (E, C, S, d), entry states -> y, final state, mid-chunk states
+        "samu_replay": 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 2 * BLD + 8 * B * M + 8 * BMID,
+        # dy, b, (E, C, S, d), entry and mid-chunk states, adjoint carries -> db,
+        # per-tile controller partials, per-(chunk, mode) spectrum partials
+        "samu_bwd_replay": 2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BMID + 8 * BCM + 2 * BLD
         + 8 * B * n_tiles * L + 8 * BCM,
         # x_sel, p, r, u, per-tile partials -> dx_sel, per-block direction partials
         "samu_controller_bwd": 2 * BLD + 16 * BL + 8 * B * n_tiles * L + 2 * BLD

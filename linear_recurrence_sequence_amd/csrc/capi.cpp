@@ -122,7 +122,7 @@ static constexpr int kRglruMinGroup = 16;
 static constexpr int kParamSegments = 32;
 
 struct SamuSaved {
-    float *p, *r, *u, *ctl, *mtab, *entries;
+    float *p, *r, *u, *ctl, *mtab, *entries, *mid;
 };
 static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t* bytes) {
     Carver cv(base);
@@ -134,6 +134,7 @@ static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t
     s.ctl = cv.take<float>(BL * 4);
     s.mtab = cv.take<float>((size_t)M * 16);
     s.entries = cv.take<float>((size_t)ch.B * ch.C * M * 2);
+    s.mid = cv.take<float>((size_t)ch.B * ch.C * samu_mid_states(ch.K) * M * 2);
     if (bytes) *bytes = cv.off;
     return s;
 }
@@ -349,7 +350,7 @@ scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, 
     LRS_TRY(launch_prefix(2, false, ch, M, PrefixSummaries{nullptr, ws.summ, ws.chunk, sv.mtab}, ws.gsum, z0,
                           sv.entries, s),
             "samu prefix");
-    LRS_TRY(launch_samu_replay(p, ch, sv.ctl, sv.mtab, sv.entries, y, y_dtype == SCAN_F32, z_final, s),
+    LRS_TRY(launch_samu_replay(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, y, y_dtype == SCAN_F32, z_final, s),
             "samu replay");
     return SCAN_OK;
 }
@@ -403,7 +404,7 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     LRS_TRY(launch_prefix(2, true, ch, M, PrefixSummaries{nullptr, ws.rsumm, ws.rchunk, sv.mtab}, ws.rgsum,
                           dz_final, ws.carry, s),
             "samu reverse prefix");
-    LRS_TRY(launch_samu_bwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, ws.carry, dy, db, f32, dz0,
+    LRS_TRY(launch_samu_bwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, ws.carry, dy, db, f32, dz0,
                                    ws.tok_part, ws.n_tiles, ws.mode_part, s),
             "samu backward replay");
     LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, sv.u, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part, s),

@@ -102,20 +102,27 @@ struct SamuParams {
 // ctl = (E, C, S, d); per mode: the four-float4 constant table mtab.
 hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
                                   float* u_out, float* ctl, float* mtab, hipStream_t s);
+// The backward replay handles a chunk as K / SAMU_BWD_SUB sub-chunks; the
+// forward replay keeps the state entering each sub-chunk after the first
+// (mid [B, C, samu_mid_states(K), M] complex), so the backward need not run
+// the forward recurrence to reach them.
+constexpr int SAMU_BWD_SUB = 16;
+__host__ __device__ constexpr inline int samu_mid_states(int K) { return K > SAMU_BWD_SUB ? K / SAMU_BWD_SUB - 1 : 0; }
+
 // compressed chunk summaries (forward, or the conjugate reverse summary of
 // dy): B parts [B, C, M] complex and per-chunk records [B, C] float4
 hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const float* ctl,
                                const float* mtab, const void* drive, bool reverse, float* summ,
                                float* chunk_rec, hipStream_t s);
-// replay from the chunk entry states; writes y and z_final
+// replay from the chunk entry states; writes y, z_final and the mid states
 hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
-                              const float* mtab, const float* entries, void* y, int y_f32,
+                              const float* mtab, const float* entries, float* mid, void* y, int y_f32,
                               float* z_final, hipStream_t s);
 // carry_in: [B, C, M] cotangent arriving after each chunk's last token;
 // mode_part: [B, C, M] per-chunk (d nu, d theta) partials
 hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
-                                  const float* mtab, const float* entries, const float* carry_in,
-                                  const void* dy, void* db, int db_f32, float* dz0,
+                                  const float* mtab, const float* entries, const float* mid,
+                                  const float* carry_in, const void* dy, void* db, int db_f32, float* dz0,
                                   float* tok_part, int n_tiles, float* mode_part, hipStream_t s);
 int samu_bwd_tiles(int M);
 int samu_ctl_tok_per_blk();

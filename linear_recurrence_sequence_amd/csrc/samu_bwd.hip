@@ -25,17 +25,18 @@ namespace {
 
 // ------------------------------------------------------ backward replay ---
 // One lane per mode, one workgroup per (chunk, 256 modes).  The chunk is
-// handled as K/H sub-chunks of H tokens, last one first: a forward pass from
-// the chunk's saved entry state leaves the state entering every sub-chunk in
-// registers; then each sub-chunk recomputes lambda_t and w_t = lambda_t z_{t-1}
-// for its H tokens and runs the adjoint over them in reverse, starting from the
-// cotangent carried in from the following chunk.  All drive and cotangent
-// words of the chunk are requested before any math.  The per-token partial
-// sums of a wave are reduced through a padded LDS transpose (conflict-free
-// both ways), one sub-chunk at a time.
+// handled as K/H sub-chunks of H tokens, last one first, each from the state
+// entering it (the chunk's saved entry state, or the saved mid state the
+// forward replay kept): a sub-chunk recomputes lambda_t and
+// w_t = lambda_t z_{t-1} for its H tokens and runs the adjoint over them in
+// reverse, starting from the cotangent carried in from the following chunk.
+// All drive and cotangent words of the chunk are requested before any math,
+// right after the saved states.  The per-token partial sums of a wave are
+// reduced through a padded LDS transpose (conflict-free both ways), one
+// sub-chunk at a time.
 constexpr int BWD_THREADS = 256;
-#ifndef LRS_BWD_SUB
-#define LRS_BWD_SUB 16
+#ifndef LRS_BWD_WAVES
+#define LRS_BWD_WAVES 3  // waves per SIMD the register budget is sized for
 #endif
 
 // One chunk of the backward replay; FULL = the chunk has all K tokens (only
@@ -45,10 +46,12 @@ template <int K, int H, bool F32, bool FULL>
 __device__ __forceinline__ void bwd_chunk(
     float (*lds)[64 * (2 * H + 1)], TokenCtl* sctl, const ModeConst& k, bool active, int lane, int wave,
     int tile, int n_tiles, int L, int M, int C, int b, int c, int mm, const TokenCtl* __restrict__ ctl,
-    const uint32_t* __restrict__ drive, const float2* __restrict__ entries,
+    const uint32_t* __restrict__ drive, const float2* __restrict__ entries, const float2* __restrict__ mid,
     const uint32_t* __restrict__ dy, void* __restrict__ db, float* __restrict__ tok_part, cf& carry,
     float& acc_nu, float& acc_th) {
     constexpr int NH = K / H;
+    static_assert(NH == 1 || (H == SAMU_BWD_SUB && NH - 1 == samu_mid_states(K)),
+                  "sub-chunks must match the forward's mid states");
     constexpr int NV = 2 * H;
     constexpr int PAD = NV + 1;
     const int s = c * K;
@@ -56,6 +59,19 @@ __device__ __forceinline__ void bwd_chunk(
     const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform; the lane adds mm
     float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
     if ((int)threadIdx.x < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + threadIdx.x];
+    // states entering each sub-chunk: the chunk's entry state and the mid
+    // states the forward replay kept (those of sub-chunks past a partial
+    // chunk's end are never used)
+    cf ck[NH];
+    {
+        const float2 e0 = entries[((size_t)b * C + c) * M + mm];
+        ck[0] = {e0.x, e0.y};
+#pragma unroll
+        for (int h = 1; h < NH; ++h) {
+            const float2 v = mid[(((size_t)b * C + c) * (NH - 1) + h - 1) * M + mm];
+            ck[h] = {v.x, v.y};
+        }
+    }
     uint32_t bw[K], gw[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
@@ -68,25 +84,9 @@ __device__ __forceinline__ void bwd_chunk(
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    const float2 e0 = entries[((size_t)b * C + c) * M + mm];
     if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
     __syncthreads();
     const int kq = opaque(kc);
-
-    // states entering each sub-chunk
-    cf ck[NH];
-    {
-        cf z = {e0.x, e0.y};
-        ck[0] = z;
-#pragma unroll
-        for (int i = 0; i < K - H; ++i) {
-            if (i < kq) {
-                const TokenCtl t = sctl[i];
-                z = cfma(mode_lambda(k, t.E, t.C, t.S), z, {bf16_lo(bw[i]), bf16_hi(bw[i])});
-            }
-            if ((i + 1) % H == 0) ck[(i + 1) / H] = z;
-        }
-    }
     float* row = &lds[wave][lane * PAD];
 #pragma unroll
     for (int h = NH - 1; h >= 0; --h) {
@@ -151,10 +151,10 @@ __device__ __forceinline__ void bwd_chunk(
 }
 
 template <int K, int H, bool F32>
-__global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(3, 8))) void samu_bwd_replay_kernel(
+__global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(LRS_BWD_WAVES, 8))) void samu_bwd_replay_kernel(
     int L, int M, int C, int n_tiles, const TokenCtl* __restrict__ ctl,
     const uint32_t* __restrict__ drive, const float4* __restrict__ mtab,
-    const float2* __restrict__ entries, const float2* __restrict__ carry_in,
+    const float2* __restrict__ entries, const float2* __restrict__ mid, const float2* __restrict__ carry_in,
     const uint32_t* __restrict__ dy, void* __restrict__ db, float2* __restrict__ dz0,
     float* __restrict__ tok_part, float2* __restrict__ mode_part) {
     static_assert(K % H == 0 && 64 % (2 * H) == 0, "sub-chunk shape");
@@ -173,10 +173,10 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(3, 
     float acc_nu = 0.f, acc_th = 0.f;
     if ((c + 1) * K <= L)
         bwd_chunk<K, H, F32, true>(lds, sctl, k, active, lane, wave, tile, n_tiles, L, M, C, b, c, mm, ctl,
-                                   drive, entries, dy, db, tok_part, carry, acc_nu, acc_th);
+                                   drive, entries, mid, dy, db, tok_part, carry, acc_nu, acc_th);
     else
         bwd_chunk<K, H, F32, false>(lds, sctl, k, active, lane, wave, tile, n_tiles, L, M, C, b, c, mm, ctl,
-                                    drive, entries, dy, db, tok_part, carry, acc_nu, acc_th);
+                                    drive, entries, mid, dy, db, tok_part, carry, acc_nu, acc_th);
     if (active) {
         mode_part[cidx] = make_float2(-acc_nu, acc_th);
         if (dz0 && c == 0) dz0[(size_t)b * M + mm] = make_float2(carry.re, carry.im);
@@ -509,16 +509,16 @@ int samu_bwd_tiles(int M) { return (int)ceil_div(M, 64); }
 int samu_ctl_tok_per_blk() { return CTL_TB; }
 
 hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
-                                  const float* mtab, const float* entries, const float* carry_in,
-                                  const void* dy, void* db, int db_f32, float* dz0, float* tok_part,
-                                  int n_tiles, float* mode_part, hipStream_t s) {
+                                  const float* mtab, const float* entries, const float* mid,
+                                  const float* carry_in, const void* dy, void* db, int db_f32, float* dz0,
+                                  float* tok_part, int n_tiles, float* mode_part, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(p.M, BWD_THREADS), ch.C, ch.B);
 #define BWD_CASE(KK, HH, FF)                                                                             \
     LRS_LAUNCH(K_SAMU_BWD_REPLAY, (samu_bwd_replay_kernel<KK, HH, FF>), grid, dim3(BWD_THREADS), 0, s, \
                p.L, p.M, ch.C, n_tiles, (const TokenCtl*)ctl, (const uint32_t*)p.b,                   \
-               (const float4*)mtab, (const float2*)entries, (const float2*)carry_in,                  \
-               (const uint32_t*)dy, db, (float2*)dz0, tok_part, (float2*)mode_part)
-    constexpr int H32 = LRS_BWD_SUB, H16 = LRS_BWD_SUB < 16 ? LRS_BWD_SUB : 16;
+               (const float4*)mtab, (const float2*)entries, (const float2*)mid,                       \
+               (const float2*)carry_in, (const uint32_t*)dy, db, (float2*)dz0, tok_part, (float2*)mode_part)
+    constexpr int H32 = SAMU_BWD_SUB, H16 = SAMU_BWD_SUB < 16 ? SAMU_BWD_SUB : 16;
     if (ch.K == 32) {
         if (db_f32) BWD_CASE(32, H32, true); else BWD_CASE(32, H32, false);
     } else {

@@ -309,14 +309,16 @@ __device__ __forceinline__ void store_states(void* y, size_t row, int off, const
 }
 
 // Replay of one chunk from its entry state Q_c(init) = L_c(O_g(init)):
-// y_t = z_t for every token; the last chunk also writes z_final.
+// y_t = z_t for every token; the last chunk also writes z_final.  The state
+// entering each backward sub-chunk after the first goes to `mid`.
 template <int VM, int K, bool F32, bool FULL>
 __device__ __forceinline__ void replay_chunk(TokenCtl (&sctl)[K], int L, int M, int C, int b, int c,
                                              int m0, bool active, const TokenCtl* __restrict__ ctl,
                                              const uint32_t* __restrict__ drive,
                                              const float4* __restrict__ mtab,
-                                             const float* __restrict__ entries, void* __restrict__ y,
-                                             float* __restrict__ z_final) {
+                                             const float* __restrict__ entries, float* __restrict__ mid,
+                                             void* __restrict__ y, float* __restrict__ z_final) {
+    constexpr int NMID = samu_mid_states(K);
     const int s = c * K;
     const int kc = FULL ? K : L - s;
     const int mc = active ? m0 : M - VM;
@@ -345,6 +347,12 @@ __device__ __forceinline__ void replay_chunk(TokenCtl (&sctl)[K], int L, int M, 
             for (int v = 0; v < VM; ++v)
                 z[v] = cfma(mode_lambda(k[v], t.E, t.C, t.S), z[v], {bf16_lo(w[i].w[v]), bf16_hi(w[i].w[v])});
             if (active) store_states<VM, F32>(y, row0 + (size_t)i * M, mc, z);
+            if (NMID > 0 && (i + 1) % SAMU_BWD_SUB == 0 && i + 1 < K && active) {
+                float2* md = reinterpret_cast<float2*>(mid) +
+                             (((size_t)b * C + c) * NMID + (i + 1) / SAMU_BWD_SUB - 1) * M + mc;
+#pragma unroll
+                for (int v = 0; v < VM; ++v) md[v] = make_float2(z[v].re, z[v].im);
+            }
         }
     }
     if (active && z_final && c == C - 1) {
@@ -357,16 +365,18 @@ __device__ __forceinline__ void replay_chunk(TokenCtl (&sctl)[K], int L, int M, 
 template <int VM, int K, bool F32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void samu_replay_kernel(
     int L, int M, int C, const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
-    const float4* __restrict__ mtab, const float* __restrict__ entries, void* __restrict__ y,
-    float* __restrict__ z_final) {
+    const float4* __restrict__ mtab, const float* __restrict__ entries, float* __restrict__ mid,
+    void* __restrict__ y, float* __restrict__ z_final) {
     __shared__ TokenCtl sctl[K];
     const int m0 = (blockIdx.x * blockDim.x + threadIdx.x) * VM;
     const int c = blockIdx.y, b = blockIdx.z;
     const bool active = m0 < M;
     if ((c + 1) * K <= L)
-        replay_chunk<VM, K, F32, true>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, entries, y, z_final);
+        replay_chunk<VM, K, F32, true>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, entries, mid, y,
+                                       z_final);
     else
-        replay_chunk<VM, K, F32, false>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, entries, y, z_final);
+        replay_chunk<VM, K, F32, false>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, entries, mid, y,
+                                        z_final);
 }
 
 inline int mode_block(int M, int VM) {
@@ -407,14 +417,14 @@ hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const fl
 }
 
 hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
-                              const float* mtab, const float* entries, void* y, int y_f32,
+                              const float* mtab, const float* entries, float* mid, void* y, int y_f32,
                               float* z_final, hipStream_t s) {
     const int blk = mode_block(p.M, REP_VM);
     const dim3 grid((unsigned)ceil_div(ceil_div(p.M, REP_VM), blk), ch.C, ch.B);
 #define REPLAY_CASE(KK, FF)                                                                       \
     LRS_LAUNCH(K_SAMU_REPLAY, (samu_replay_kernel<REP_VM, KK, FF>), grid, dim3(blk), 0, s, p.L, \
                p.M, ch.C, (const TokenCtl*)ctl, (const uint32_t*)p.b, (const float4*)mtab,       \
-               entries, y, z_final)
+               entries, mid, y, z_final)
     if (ch.K == 32) {
         if (y_f32) REPLAY_CASE(32, true); else REPLAY_CASE(32, false);
     } else {
