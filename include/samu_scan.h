@@ -81,7 +81,10 @@ const char* scan_last_error(void);
  * ====================================================================== */
 
 /* Bytes of the forward-to-backward record: p, r, the per-token special
- * functions and the entry state of every chunk. */
+ * functions, the mode table, the entry state of every chunk and, for K = 32,
+ * the state entering the second 16-token half of every chunk (the backward
+ * replay starts its sub-chunks from these instead of recomputing them).
+ * Independent of G, so a backward may use another grouping than its forward. */
 size_t samu_scan_saved_bytes(int B, int L, int D, int K);
 
 /* Workspace bytes of samu_scan_fwd (backward = 0) or samu_scan_bwd
