@@ -434,10 +434,47 @@ __global__ __launch_bounds__(RED_THREADS) void samu_param_reduce_kernel(
     }
 }
 
-// Level 2: every column and every mode independently, so the whole grid works
-// in parallel.  dw = (g - w^ (w^ . g)) / ||w|| with w^ . g taken from the
-// per-token sums of u-bar * u (column D+2); da from column D+1.
-constexpr int FIN_THREADS = 256;
+// Level 2: the segment sums of every column and every mode.  A workgroup
+// owns FIN_ITEMS columns (or modes) and splits the segments over FIN_SG
+// groups of threads: each thread adds up to FIN_SEG_PER segments in order,
+// all requested at once, and the group sums are added in group order through
+// LDS, so the result is fixed for a given shape.  Column workgroups also form
+// the FP64 direction norms and the sums of the scalar columns, then
+// dw = (g - w^ (w^ . g)) / ||w|| with w^ . g from the per-token sums of
+// u-bar * u (column D+2); the first one also writes da from column D+1.
+// This kernel is latency alone (a few MB), so it is laid out for few
+// dependent rounds of loads.
+constexpr int FIN_SG = 8;
+constexpr int FIN_ITEMS = 32;
+constexpr int FIN_THREADS = FIN_SG * FIN_ITEMS;
+constexpr int FIN_SEG_PER = 4;  // FIN_SG * FIN_SEG_PER >= the segment count
+constexpr int FIN_NORM_BATCH = 8;
+
+// Sum over the segments of one item: this thread's share, then the groups.
+__device__ __forceinline__ double2 fin_segment_sum(const double2* __restrict__ seg, size_t stride, int item,
+                                                   int n_seg, int sg, int ii, double2 (*sh)[FIN_ITEMS]) {
+    double2 v[FIN_SEG_PER];
+#pragma unroll
+    for (int k = 0; k < FIN_SEG_PER; ++k) v[k] = seg[(size_t)min(sg * FIN_SEG_PER + k, n_seg - 1) * stride + item];
+    double sx = 0.0, sy = 0.0;
+#pragma unroll
+    for (int k = 0; k < FIN_SEG_PER; ++k) {
+        const bool ok = sg * FIN_SEG_PER + k < n_seg;
+        sx += ok ? v[k].x : 0.0;
+        sy += ok ? v[k].y : 0.0;
+    }
+    sh[sg][ii] = make_double2(sx, sy);
+    __syncthreads();
+    double tx = 0.0, ty = 0.0;
+    if (sg == 0) {
+#pragma unroll
+        for (int g = 0; g < FIN_SG; ++g) {
+            tx += sh[g][ii].x;
+            ty += sh[g][ii].y;
+        }
+    }
+    return make_double2(tx, ty);
+}
 
 __global__ __launch_bounds__(FIN_THREADS) void samu_param_final_kernel(
     int D, int M, int col_blocks, const float* __restrict__ w_phi, const float* __restrict__ w_r,
@@ -445,61 +482,70 @@ __global__ __launch_bounds__(FIN_THREADS) void samu_param_final_kernel(
     const double2* __restrict__ g_seg, const double2* __restrict__ mode_seg, int n_seg,
     float* __restrict__ dw_phi, float* __restrict__ dw_r, float* __restrict__ da_phi,
     float* __restrict__ da_r, float* __restrict__ dnu, float* __restrict__ dtheta) {
+    __shared__ double2 sh[FIN_SG][FIN_ITEMS];
+    __shared__ double red[2][FIN_THREADS / 64];
+    __shared__ double2 scal[2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sg = tid / FIN_ITEMS, ii = tid - sg * FIN_ITEMS;
     const int ncol = D + 4;
     if ((int)blockIdx.x >= col_blocks) {
-        const int m = (blockIdx.x - col_blocks) * FIN_THREADS + tid;
-        if (m >= M) return;
-        double sx = 0.0, sy = 0.0;
-#pragma unroll 8
-        for (int i = 0; i < n_seg; ++i) {
-            const double2 v = mode_seg[(size_t)i * M + m];
-            sx += v.x;
-            sy += v.y;
+        const int m0 = (blockIdx.x - col_blocks) * FIN_ITEMS;
+        const int m = min(m0 + ii, M - 1);
+        const double2 t = fin_segment_sum(mode_seg, M, m, n_seg, sg, ii, sh);
+        if (sg == 0 && m0 + ii < M) {
+            dnu[m] = (float)t.x;
+            dtheta[m] = (float)t.y;
         }
-        dnu[m] = (float)sx;
-        dtheta[m] = (float)sy;
         return;
     }
-    __shared__ double red[2][FIN_THREADS / 64];
+    // direction norms, FIN_NORM_BATCH loads in flight per thread
     double nphi = 0.0, nr = 0.0;
-    for (int j = tid; j <= D; j += FIN_THREADS) {
-        nphi += (double)w_phi[j] * w_phi[j];
-        nr += (double)w_r[j] * w_r[j];
+    for (int j0 = tid; j0 <= D; j0 += FIN_NORM_BATCH * FIN_THREADS) {
+        float a[FIN_NORM_BATCH], c[FIN_NORM_BATCH];
+#pragma unroll
+        for (int k = 0; k < FIN_NORM_BATCH; ++k) {
+            const int j = min(j0 + k * FIN_THREADS, D);
+            a[k] = w_phi[j];
+            c[k] = w_r[j];
+        }
+#pragma unroll
+        for (int k = 0; k < FIN_NORM_BATCH; ++k) {
+            const bool ok = j0 + k * FIN_THREADS <= D;
+            nphi += ok ? (double)a[k] * a[k] : 0.0;
+            nr += ok ? (double)c[k] * c[k] : 0.0;
+        }
     }
     nphi = wave_sum_d(nphi);
     nr = wave_sum_d(nr);
     if (lane == 0) { red[0][wave] = nphi; red[1][wave] = nr; }
-    __syncthreads();
-    double Np = 0.0, Nr = 0.0;
-    for (int i = 0; i < FIN_THREADS / 64; ++i) { Np += red[0][i]; Nr += red[1][i]; }
-    const double np = sqrt(Np), nrr = sqrt(Nr);
-    const int j = blockIdx.x * FIN_THREADS + tid;
-    if (j > D) return;
-    double gx = 0.0, gy = 0.0, dotp = 0.0, dotr = 0.0;
-#pragma unroll 8
-    for (int i = 0; i < n_seg; ++i) {
-        const double2 v = g_seg[(size_t)i * ncol + j];
-        const double2 q = g_seg[(size_t)i * ncol + D + 2];
-        gx += v.x;
-        gy += v.y;
-        dotp += q.x;
-        dotr += q.y;
-    }
-    dw_phi[j] = (float)((gx - ((double)w_phi[j] / np) * dotp) / np);
-    dw_r[j] = (float)((gy - ((double)w_r[j] / nrr) * dotr) / nrr);
-    if (j == 0) {
-        double sdp = 0.0, scq = 0.0;
-#pragma unroll 8
-        for (int i = 0; i < n_seg; ++i) {
-            const double2 v = g_seg[(size_t)i * ncol + D + 1];
-            sdp += v.x;
-            scq += v.y;
+    // the scalar columns D+1 and D+2 over the segments: one segment per lane
+    // of the first wave (n_seg <= 64), then a fixed butterfly
+    if (wave == 0) {
+        const int i = min(lane, n_seg - 1);
+        const double2 v1 = g_seg[(size_t)i * ncol + D + 1], v2 = g_seg[(size_t)i * ncol + D + 2];
+        const bool ok = lane < n_seg;
+        const double s1x = wave_sum_d(ok ? v1.x : 0.0), s1y = wave_sum_d(ok ? v1.y : 0.0);
+        const double s2x = wave_sum_d(ok ? v2.x : 0.0), s2y = wave_sum_d(ok ? v2.y : 0.0);
+        if (lane == 0) {
+            scal[0] = make_double2(s1x, s1y);  // sum d-bar p, sum c-bar q
+            scal[1] = make_double2(s2x, s2y);  // w^ . g for phi and r
         }
+    }
+    const int j = min((int)blockIdx.x * FIN_ITEMS + ii, D);
+    const double2 g = fin_segment_sum(g_seg, ncol, j, n_seg, sg, ii, sh);  // its barrier also covers red, scal
+    if (sg != 0 || (int)blockIdx.x * FIN_ITEMS + ii > D) return;
+    double Np = 0.0, Nr = 0.0;
+    for (int k = 0; k < FIN_THREADS / 64; ++k) { Np += red[0][k]; Nr += red[1][k]; }
+    const double np = sqrt(Np), nrr = sqrt(Nr);
+    const double2 dot = scal[1];
+    dw_phi[j] = (float)((g.x - ((double)w_phi[j] / np) * dot.x) / np);
+    dw_r[j] = (float)((g.y - ((double)w_r[j] / nrr) * dot.y) / nrr);
+    if (j == 0) {
+        const double2 sa = scal[0];
         const double sM = sqrt((double)M);
         const double tp = tanh((double)a_phi[0]), tr = tanh((double)a_r[0]);
-        da_phi[0] = (float)((1.0 - tp * tp) / sM * sdp);
-        da_r[0] = (float)((1.0 - tr * tr) / sM * scq);
+        da_phi[0] = (float)((1.0 - tp * tp) / sM * sa.x);
+        da_r[0] = (float)((1.0 - tr * tr) / sM * sa.y);
     }
 }
 
@@ -567,8 +613,9 @@ hipError_t launch_samu_param_reduce(const SamuParams& p, const Chunking& ch, con
 hipError_t launch_samu_param_final(const SamuParams& p, const double* g_seg, const double* mode_seg,
                                    int n_seg, float* dw_phi, float* dw_r, float* da_phi, float* da_r,
                                    float* dnu, float* dtheta, hipStream_t s) {
-    const int col_blocks = (int)ceil_div(p.D + 1, FIN_THREADS);
-    const int grid = col_blocks + (int)ceil_div(p.M, FIN_THREADS);
+    if (n_seg > FIN_SG * FIN_SEG_PER) return hipErrorInvalidValue;
+    const int col_blocks = (int)ceil_div(p.D + 1, FIN_ITEMS);
+    const int grid = col_blocks + (int)ceil_div(p.M, FIN_ITEMS);
     LRS_LAUNCH(K_SAMU_PARAM_FINAL, samu_param_final_kernel, dim3(grid), dim3(FIN_THREADS), 0, s, p.D,
                p.M, col_blocks, p.w_phi, p.w_r, p.a_phi, p.a_r, (const double2*)g_seg,
                (const double2*)mode_seg, n_seg, dw_phi, dw_r, da_phi, da_r, dnu, dtheta);

@@ -31,6 +31,9 @@ CASES = [
     ("groups_of_one_chunk", 1, 300, 40, 32, 1, 0.1),
     ("modes_not_tile_multiple", 1, 129, 1032, 32, 3, 0.1),
     ("serial_prefix", 2, 700, 256, 32, 1000, 0.1),
+    # last chunk of 20 tokens: the backward starts its second half from the
+    # mid-chunk state the forward stored
+    ("ragged_second_half", 2, 660, 128, 32, 4, 0.1),
 ]
 
 
