@@ -122,7 +122,7 @@ static constexpr int kRglruMinGroup = 16;
 static constexpr int kParamSegments = 32;
 
 struct SamuSaved {
-    float *p, *r, *u, *ctl, *mtab, *entries, *mid;
+    float *p, *r, *u, *ctl, *mtab, *inv_norm, *entries, *mid;
 };
 static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t* bytes) {
     Carver cv(base);
@@ -133,6 +133,7 @@ static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t
     s.u = cv.take<float>(BL * 2);
     s.ctl = cv.take<float>(BL * 4);
     s.mtab = cv.take<float>((size_t)M * 16);
+    s.inv_norm = cv.take<float>(4);
     s.entries = cv.take<float>((size_t)ch.B * ch.C * M * 2);
     s.mid = cv.take<float>((size_t)ch.B * ch.C * samu_mid_states(ch.K) * M * 2);
     if (bytes) *bytes = cv.off;
@@ -345,7 +346,7 @@ scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
     SamuSaved sv = samu_saved_layout(saved, ch, M, nullptr);
     SamuFwdWs ws = samu_fwd_ws_layout(workspace, ch, M, nullptr);
-    LRS_TRY(launch_samu_controller(p, ch, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, s), "samu controller");
+    LRS_TRY(launch_samu_controller(p, ch, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, sv.inv_norm, s), "samu controller");
     LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, ws.chunk, s), "samu chunk summary");
     LRS_TRY(launch_prefix(2, false, ch, M, PrefixSummaries{nullptr, ws.summ, ws.chunk, sv.mtab}, ws.gsum, z0,
                           sv.entries, s),
@@ -407,7 +408,7 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     LRS_TRY(launch_samu_bwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, ws.carry, dy, db, f32, dz0,
                                    ws.tok_part, ws.n_tiles, ws.mode_part, s),
             "samu backward replay");
-    LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, sv.u, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part, s),
+    LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, sv.u, sv.inv_norm, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part, s),
             "samu controller backward");
     LRS_TRY(launch_samu_param_reduce(p, ch, ws.g_part, ws.n_blk, ws.mode_part, ws.g_seg, ws.n_seg,
                                      ws.mode_seg, s),
@@ -487,7 +488,7 @@ scan_status samu_scan_baseline_fwd(int variant, int B, int L, int D, const void*
     chunking(B, L, 32, 0, kSamuMinGroup, &ch);  // the controller's chunk phasors are not used here
     SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
     SamuBaseWs ws = samu_base_layout(workspace, B, L, M, variant, nullptr);
-    LRS_TRY(launch_samu_controller(p, ch, ws.p, ws.r, ws.u, ws.ctl, ws.mtab, s), "samu controller");
+    LRS_TRY(launch_samu_controller(p, ch, ws.p, ws.r, ws.u, ws.ctl, ws.mtab, nullptr, s), "samu controller");
     LRS_TRY(launch_samu_baseline(variant, p, ws.ctl, ws.mtab, ws.levels, y, y_dtype == SCAN_F32, z_final, s),
             "samu comparison scan");
     return SCAN_OK;

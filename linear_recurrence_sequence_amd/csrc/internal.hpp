@@ -99,9 +99,10 @@ struct SamuParams {
 };
 
 // saved forward record (per token): p, r, u = (x~ . w^_phi, x~ . w^_r),
-// ctl = (E, C, S, d); per mode: the four-float4 constant table mtab.
+// ctl = (E, C, S, d); per mode: the four-float4 constant table mtab;
+// inv_norm (NULL: not written) = (1/||w_phi||, 1/||w_r||).
 hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
-                                  float* u_out, float* ctl, float* mtab, hipStream_t s);
+                                  float* u_out, float* ctl, float* mtab, float* inv_norm, hipStream_t s);
 // The backward replay handles a chunk as K / SAMU_BWD_SUB sub-chunks; the
 // forward replay keeps the state entering each sub-chunk after the first
 // (mid [B, C, samu_mid_states(K), M] complex), so the backward need not run
@@ -128,8 +129,8 @@ int samu_bwd_tiles(int M);
 int samu_ctl_tok_per_blk();
 int samu_param_columns(int D);
 hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const float* r_sv,
-                               const float* u_sv, const float* tok_part, int n_tiles, void* dx_sel,
-                               int dx_f32, float* g_part, hipStream_t s);
+                               const float* u_sv, const float* inv_norm, const float* tok_part, int n_tiles,
+                               void* dx_sel, int dx_f32, float* g_part, hipStream_t s);
 hipError_t launch_samu_param_reduce(const SamuParams& p, const Chunking& ch,
                                     const float* g_part, int n_blk, const float* mode_part,
                                     double* g_seg, int n_seg, double* mode_seg, hipStream_t s);

@@ -206,18 +206,28 @@ constexpr bool DX_NT = LRS_DX_NT != 0;
 // are added in split order through LDS, so the result is fixed for a given D.
 constexpr int CTL_TOKB = 16;  // tokens whose selector words are loaded together
 
-template <bool F32>
-__device__ __forceinline__ void ctl_load_batch(uint4 (&xv)[CTL_TOKB], const uint4* __restrict__ x_sel,
-                                               size_t tok0, int D8, int j8, bool act, int nt) {
-    if (act && nt == CTL_TOKB) {
+// Token tok0 + i clamped to the last token (unsigned: tok0 + i may pass 2^31 - 1).
+__device__ __forceinline__ int clamp_tok(int tok0, int i, int BL) {
+    return (int)min((unsigned)tok0 + (unsigned)i, (unsigned)(BL - 1));
+}
+
+// Selector words of tokens tok0 .. tok0 + CTL_TOKB - 1 in column group j8.
+// Tokens are clamped into the tensor, so every load is issued unconditionally
+// (a guarded load becomes a branch, after which waiting for any earlier
+// request turns into waiting for all of them); the consumer skips the rest.
+__device__ __forceinline__ void ctl_load_batch(uint4 (&xv)[CTL_TOKB], const uint4* __restrict__ x_sel, int tok0,
+                                               int BL, int D8, int j8) {
 #pragma unroll
-        for (int t = 0; t < CTL_TOKB; ++t) xv[t] = x_sel[(tok0 + t) * D8 + j8];
-    } else {
-#pragma unroll
-        for (int t = 0; t < CTL_TOKB; ++t)
-            xv[t] = (act && t < nt) ? x_sel[(tok0 + t) * D8 + j8] : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < CTL_TOKB; ++t) {
+        const uint4* row = x_sel + (size_t)clamp_tok(tok0, t, BL) * D8;  // wave-uniform
+        xv[t] = row[j8];
     }
 }
+
+// Tile partials of a block staged through LDS (the first wave reads any
+// further ones directly), and how many each thread requests up front.
+constexpr int CTL_LDS_TILES = 64;
+constexpr int CTL_TPL = 2;
 
 template <bool F32>
 __global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
@@ -225,91 +235,101 @@ __global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
     const float* __restrict__ w_phi, const float* __restrict__ w_r,
     const float* __restrict__ a_phi, const float* __restrict__ a_r,
     const float* __restrict__ p_sv, const float* __restrict__ r_sv,
-    const float2* __restrict__ u_sv, const float* __restrict__ tok_part, void* __restrict__ dx,
-    float* __restrict__ g_part) {
-    extern __shared__ float4 comb[];  // [(TS - 1) * CT][4]
+    const float2* __restrict__ u_sv, const float* __restrict__ inv_norm, const float* __restrict__ tok_part,
+    void* __restrict__ dx, float* __restrict__ g_part) {
+    // the block's tile partials [tiles][CTL_TB] float2, later the split sums [(TS - 1) * CT][4]
+    extern __shared__ float4 dyn[];
+    float4* comb = dyn;
     __shared__ float u_sh[2][CTL_TB];
-    __shared__ float red[2][16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nthr = blockDim.x;
     const int BL = B * L;
     const int blk = blockIdx.x;
     const int ncol = D + 4;
     const int D8 = D >> 3;
     const int CT = blockDim.x / TS;
-    const int ts = tid / CT, cj = tid - ts * CT;
+    // CT is a multiple of 64, so a wave lies in one split: make that visible
+    // to the compiler, and every token row offset becomes a scalar
+    const int ts = __builtin_amdgcn_readfirstlane(tid / CT), cj = tid - ts * CT;
     const int ntok = min(CTL_TB, BL - blk * CTL_TB);
     const int tper = CTL_TB / TS;
     const int tlo = ts * tper, thi = min(tlo + tper, ntok);
     const size_t tokb = (size_t)blk * CTL_TB;
+    const int tokb32 = blk * CTL_TB;
 
-    // the first selector batch does not depend on u-bar: request it now
-    uint4 xv[CTL_TOKB];
-    ctl_load_batch<F32>(xv, x_sel, tokb + tlo, D8, cj, cj < D8, max(0, min(CTL_TOKB, thi - tlo)));
-
-    // direction norms
-    float sp = 0.f, sr = 0.f;
-    for (int j = tid; j <= D; j += blockDim.x) {
-        sp = fmaf(w_phi[j], w_phi[j], sp);
-        sr = fmaf(w_r[j], w_r[j], sr);
+    // Requests that do not wait on the selector stream go first, so the
+    // first wave forms u-bar while the selector words are in flight: the
+    // block's tile partials (coalesced over tokens) and the per-token saved
+    // values of the first wave's tokens.
+    const int ltiles = min(n_tiles, CTL_LDS_TILES);
+    const int npairs = ltiles * CTL_TB;
+    const float2* tp2 = reinterpret_cast<const float2*>(tok_part);
+    float2 tv[CTL_TPL];
+#pragma unroll
+    for (int k = 0; k < CTL_TPL; ++k) {
+        const int idx = min(tid + k * nthr, npairs - 1);
+        const int tok = clamp_tok(tokb32, idx % CTL_TB, BL);
+        const int bb = tok / L;
+        tv[k] = tp2[((size_t)bb * n_tiles + idx / CTL_TB) * L + (tok - bb * L)];
     }
-    sp = wave_sum(sp);
-    sr = wave_sum(sr);
-    if (lane == 0) { red[0][wave] = sp; red[1][wave] = sr; }
+    const int mytok = clamp_tok(tokb32, lane, BL);
+    const float pv = p_sv[mytok], rv = r_sv[mytok];
+    const float2 uv = u_sv[mytok];
 
-    // per-token u-bar (the first wave: CTL_TB == 64 tokens)
-    if (tid < CTL_TB) {
-        const int tok = blk * CTL_TB + tid;
-        float uphi = 0.f, ur = 0.f, sdp = 0.f, scq = 0.f, sup = 0.f, sur = 0.f;
-        if (tok < BL) {
-            const int bb = tok / L, l = tok - bb * L;
-            // second stage of the shared-control reduction: tiles in order,
-            // their partials requested 8 at a time
-            const float2* tp = reinterpret_cast<const float2*>(tok_part) + (size_t)bb * n_tiles * L + l;
-            float cb = 0.f, dbr = 0.f;
-            int t = 0;
-            for (; t + 8 <= n_tiles; t += 8) {
-                float2 v[8];
+    // the first selector batch
+    uint4 xv[CTL_TOKB];
+    ctl_load_batch(xv, x_sel, tokb32 + tlo, BL, D8, min(cj, D8 - 1));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // per-token u-bar: the tiles summed in order by the first wave (CTL_TB == 64)
+    float2* tps = reinterpret_cast<float2*>(dyn);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = tp[(size_t)(t + i) * L];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    cb += v[i].x;
-                    dbr += v[i].y;
-                }
-            }
-            for (; t < n_tiles; ++t) {
-                const float2 v = tp[(size_t)t * L];
+    for (int k = 0; k < CTL_TPL; ++k) tps[min(tid + k * nthr, npairs - 1)] = tv[k];  // repeats store equal values
+    for (int idx = CTL_TPL * nthr + tid; idx < npairs; idx += nthr) {
+        const int tok = clamp_tok(tokb32, idx % CTL_TB, BL);
+        const int bb = tok / L;
+        tps[idx] = tp2[((size_t)bb * n_tiles + idx / CTL_TB) * L + (tok - bb * L)];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const bool valid = lane < ntok;
+        float cb = 0.f, dbr = 0.f;
+        for (int t = 0; t < ltiles; ++t) {
+            const float2 v = tps[t * CTL_TB + lane];
+            cb += v.x;
+            dbr += v.y;
+        }
+        if (n_tiles > ltiles) {  // tiles beyond the staged ones, in order
+            const int bb = mytok / L;
+            const float2* tq = tp2 + (size_t)bb * n_tiles * L + (mytok - bb * L);
+            for (int t = ltiles; t < n_tiles; ++t) {
+                const float2 v = tq[(size_t)t * L];
                 cb += v.x;
                 dbr += v.y;
             }
-            const float p = p_sv[tok], r = r_sv[tok];
-            const float2 u = u_sv[tok];
-            const float r2 = r * r;
-            const float q = r / (1.0f + r2);
-            const float sM = sqrtf((float)M);
-            const float pbar = dbr * tanhf(a_phi[0]) / sM;
-            const float rbar = cb * tanhf(a_r[0]) / sM * (1.0f - r2) / ((1.0f + r2) * (1.0f + r2));
-            uphi = pbar * (1.0f - p * p);
-            ur = rbar * (1.0f - r2);
-            sdp = dbr * p;
-            scq = cb * q;
-            sup = uphi * u.x;
-            sur = ur * u.y;
         }
-        u_sh[0][tid] = uphi;
-        u_sh[1][tid] = ur;
+        const float r2 = rv * rv;
+        const float q = rv / (1.0f + r2);
+        const float sM = sqrtf((float)M);
+        const float pbar = dbr * tanhf(a_phi[0]) / sM;
+        const float rbar = cb * tanhf(a_r[0]) / sM * (1.0f - r2) / ((1.0f + r2) * (1.0f + r2));
+        const float uphi = valid ? pbar * (1.0f - pv * pv) : 0.f;
+        const float ur = valid ? rbar * (1.0f - r2) : 0.f;
+        const float sdp = valid ? dbr * pv : 0.f;
+        const float scq = valid ? cb * q : 0.f;
+        u_sh[0][lane] = uphi;
+        u_sh[1][lane] = ur;
         const float s0 = wave_sum(uphi), s1 = wave_sum(ur), s2 = wave_sum(sdp), s3 = wave_sum(scq);
-        const float s4 = wave_sum(sup), s5 = wave_sum(sur);
-        if (tid == 0) {
-            float4* gp = reinterpret_cast<float4*>(g_part + ((size_t)blk * ncol + D) * 2);
-            gp[0] = make_float4(s0, s1, s2, s3);
-            gp[1] = make_float4(s4, s5, 0.f, 0.f);
+        const float s4 = wave_sum(uphi * uv.x), s5 = wave_sum(ur * uv.y);
+        if (lane == 0) {
+            float4* gq = reinterpret_cast<float4*>(g_part + ((size_t)blk * ncol + D) * 2);
+            gq[0] = make_float4(s0, s1, s2, s3);
+            gq[1] = make_float4(s4, s5, 0.f, 0.f);
         }
     }
     __syncthreads();
-    float np = 0.f, nr = 0.f;
-    for (int i = 0; i < nw; ++i) { np += red[0][i]; nr += red[1][i]; }
-    const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
+    // 1/||w||, kept by the forward controller
+    const float inv_phi = inv_norm[0], inv_r = inv_norm[1];
 
     for (int jb = 0; jb < D8; jb += CT) {  // uniform trip count: barriers below
         const int j8 = jb + cj;
@@ -331,7 +351,7 @@ __global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
         }
         for (int t0 = tlo; t0 < thi; t0 += CTL_TOKB) {
             const int nt = min(CTL_TOKB, thi - t0);
-            if (jb > 0 || t0 > tlo) ctl_load_batch<F32>(xv, x_sel, tokb + t0, D8, j8, act, nt);
+            if (jb > 0 || t0 > tlo) ctl_load_batch(xv, x_sel, tokb32 + t0, BL, D8, min(j8, D8 - 1));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < CTL_TOKB; ++t) {
@@ -351,13 +371,13 @@ __global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
                 }
                 if (act) {
                     if (F32) {
-                        float4* q = reinterpret_cast<float4*>(dx) + (tok * D8 + j8) * 2;
-                        out_store<f32x4_t, DX_NT>(q, f32x4_t{o[0], o[1], o[2], o[3]});
-                        out_store<f32x4_t, DX_NT>(q + 1, f32x4_t{o[4], o[5], o[6], o[7]});
+                        float4* row = reinterpret_cast<float4*>(dx) + tok * D8 * 2;  // wave-uniform
+                        out_store<f32x4_t, DX_NT>(row + 2 * j8, f32x4_t{o[0], o[1], o[2], o[3]});
+                        out_store<f32x4_t, DX_NT>(row + 2 * j8 + 1, f32x4_t{o[4], o[5], o[6], o[7]});
                     } else {
-                        out_store<u32x4_t, DX_NT>(reinterpret_cast<uint4*>(dx) + tok * D8 + j8,
-                                                  u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                                          pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])});
+                        uint4* row = reinterpret_cast<uint4*>(dx) + tok * D8;  // wave-uniform
+                        out_store<u32x4_t, DX_NT>(row + j8, u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                                    pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])});
                     }
                 }
             }
@@ -575,19 +595,20 @@ hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const
 }
 
 hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const float* r_sv,
-                               const float* u_sv, const float* tok_part, int n_tiles, void* dx_sel,
-                               int dx_f32, float* g_part, hipStream_t s) {
+                               const float* u_sv, const float* inv_norm, const float* tok_part, int n_tiles,
+                               void* dx_sel, int dx_f32, float* g_part, hipStream_t s) {
     const int BL = p.B * p.L;
     const int grid = (int)ceil_div(BL, CTL_TB);
     // column threads (a multiple of 64, at most 1024) and token splits (1, 2 or 4)
     const int CT = (int)std::min<int64_t>(1024, ceil_div(p.D / 8, 64) * 64);
     int TS = 1;
     while (TS < 4 && CT * TS * 2 <= 1024) TS *= 2;
-    const size_t shmem = (size_t)(TS - 1) * CT * 4 * sizeof(float4);
+    const size_t shmem = std::max((size_t)(TS - 1) * CT * 4 * sizeof(float4),
+                                  (size_t)std::min(n_tiles, CTL_LDS_TILES) * CTL_TB * sizeof(float2));
 #define CTLB_CASE(FF)                                                                                    \
     LRS_LAUNCH(K_SAMU_CTL_BWD, samu_ctl_bwd_kernel<FF>, dim3(grid), dim3(CT * TS), shmem, s, p.B, p.L, p.D, \
                p.M, n_tiles, TS, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p_sv, r_sv,        \
-               (const float2*)u_sv, tok_part, dx_sel, g_part)
+               (const float2*)u_sv, inv_norm, tok_part, dx_sel, g_part)
     if (dx_f32) CTLB_CASE(true); else CTLB_CASE(false);
 #undef CTLB_CASE
     return hipGetLastError();

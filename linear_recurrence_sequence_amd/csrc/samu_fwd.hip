@@ -51,7 +51,7 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     const float* __restrict__ w_r, const float* __restrict__ a_phi,
     const float* __restrict__ a_r, const float* __restrict__ nu, const float* __restrict__ theta,
     float* __restrict__ p_out, float* __restrict__ r_out, float2* __restrict__ u_out,
-    TokenCtl* __restrict__ ctl, float4* __restrict__ mtab) {
+    TokenCtl* __restrict__ ctl, float4* __restrict__ mtab, float* __restrict__ inv_norm) {
     __shared__ float red[2][CTL_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -122,6 +122,10 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
 #pragma unroll
     for (int i = 0; i < CTL_WAVES; ++i) { np += red[0][i]; nr += red[1][i]; }
     const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
+    if (inv_norm && blockIdx.x == 0 && tid == 0) {  // for the controller backward
+        inv_norm[0] = inv_phi;
+        inv_norm[1] = inv_r;
+    }
     const float amp_phi = tanhf(a_phi[0]) / sqrtf((float)M);
     const float amp_r = tanhf(a_r[0]) / sqrtf((float)M);
     const float bias_phi = w_phi[D], bias_r = w_r[D];
@@ -387,13 +391,13 @@ inline int mode_block(int M, int VM) {
 }  // namespace
 
 hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
-                                  float* u_out, float* ctl, float* mtab, hipStream_t s) {
+                                  float* u_out, float* ctl, float* mtab, float* inv_norm, hipStream_t s) {
     const int BL = p.B * p.L;
     const int grid = (int)ceil_div(BL, CTL_TOK_PER_BLOCK);
     const int K_last = p.L - (ch.C - 1) * ch.K;
     LRS_LAUNCH(K_SAMU_CONTROLLER, samu_controller_kernel, dim3(grid), dim3(CTL_THREADS), 0, s,
                BL, p.D, p.M, ch.K, K_last, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p.nu,
-               p.theta, p_out, r_out, (float2*)u_out, (TokenCtl*)ctl, (float4*)mtab);
+               p.theta, p_out, r_out, (float2*)u_out, (TokenCtl*)ctl, (float4*)mtab, inv_norm);
     return hipGetLastError();
 }
 
