@@ -231,8 +231,8 @@ __device__ __forceinline__ void summary_chunk(TokenCtl (&sctl)[K], int L, int M,
     const int mc = active ? m0 : M - VM;
     float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
     if ((int)threadIdx.x < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + threadIdx.x];
-    Words<VM> w[K];
-    load_chunk<VM, K, FULL>(w, drive + ((size_t)b * L + s) * M, M, mc, kc);
+    // the mode constants first: the first step then waits for its own drive
+    // word only, not for the whole chunk's
     ModeConst k[VM];
     cf Bv[VM];
 #pragma unroll
@@ -240,6 +240,8 @@ __device__ __forceinline__ void summary_chunk(TokenCtl (&sctl)[K], int L, int M,
         k[v] = load_mode(mtab, mc + v);
         Bv[v] = {0.f, 0.f};
     }
+    Words<VM> w[K];
+    load_chunk<VM, K, FULL>(w, drive + ((size_t)b * L + s) * M, M, mc, kc);
     if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
     __syncthreads();
     const int kq = opaque(kc);
@@ -329,8 +331,8 @@ __device__ __forceinline__ void replay_chunk(TokenCtl (&sctl)[K], int L, int M, 
     const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform
     float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
     if ((int)threadIdx.x < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + threadIdx.x];
-    Words<VM> w[K];
-    load_chunk<VM, K, FULL>(w, drive + row0, M, mc, kc);
+    // the mode constants and the entry state first: the first token then
+    // waits for its own drive word only, not for the whole chunk's
     ModeConst k[VM];
     cf z[VM];
     const float2* ent = reinterpret_cast<const float2*>(entries) + ((size_t)b * C + c) * M + mc;
@@ -340,6 +342,8 @@ __device__ __forceinline__ void replay_chunk(TokenCtl (&sctl)[K], int L, int M, 
         const float2 e = ent[v];
         z[v] = {e.x, e.y};
     }
+    Words<VM> w[K];
+    load_chunk<VM, K, FULL>(w, drive + row0, M, mc, kc);
     if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
     __syncthreads();
     const int kq = opaque(kc);
