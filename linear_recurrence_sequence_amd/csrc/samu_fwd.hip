@@ -189,12 +189,16 @@ constexpr int REP_VM = LRS_REP_VM;
 // scheduled: the recurrence is serial within a lane, so memory-level
 // parallelism comes from requesting the whole chunk at once.  Only the last
 // chunk of a sequence can be partial; full chunks take the branch-free path.
-template <int VM, int K, bool FULL>
+// REV: requested last token first, the order the reverse summary consumes
+// them in (waits are in issue order).
+template <int VM, int K, bool FULL, bool REV = false>
 __device__ __forceinline__ void load_chunk(Words<VM> (&w)[K], const uint32_t* __restrict__ rows, int M,
                                            int off, int kc) {
 #pragma unroll
-    for (int i = 0; i < K; ++i)
+    for (int j = 0; j < K; ++j) {
+        const int i = REV ? K - 1 - j : j;
         if (FULL || i < kc) w[i].load(rows + (size_t)i * M, off);
+    }
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -241,7 +245,7 @@ __device__ __forceinline__ void summary_chunk(TokenCtl (&sctl)[K], int L, int M,
         Bv[v] = {0.f, 0.f};
     }
     Words<VM> w[K];
-    load_chunk<VM, K, FULL>(w, drive + ((size_t)b * L + s) * M, M, mc, kc);
+    load_chunk<VM, K, FULL, REV>(w, drive + ((size_t)b * L + s) * M, M, mc, kc);
     if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
     __syncthreads();
     const int kq = opaque(kc);
