@@ -49,11 +49,10 @@ hipEvent_t pool_get() {
 static const char* const kKernelNames[K_NUM_KERNELS] = {
     "samu_controller", "samu_chunk_summary", "prefix_group_compose", "prefix_group_scan",
     "prefix_chunk_entries", "samu_replay", "samu_reverse_summary", "samu_bwd_replay",
-    "samu_controller_bwd", "samu_param_reduce", "samu_param_final", "rglru_chunk_summary",
-    "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha_reduce",
-    "rglru_alpha_final", "samu_decode", "baseline_sequential", "baseline_associative",
-    "gate_projection", "gate_projection_dx", "gate_projection_dw",
-    "gate_projection_reduce"};
+    "samu_controller_bwd", "samu_params", "rglru_chunk_summary", "rglru_replay",
+    "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha", "samu_decode",
+    "baseline_sequential", "baseline_associative", "gate_projection", "gate_projection_dx",
+    "gate_projection_dw", "gate_projection_reduce"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 
@@ -119,7 +118,6 @@ static bool chunking(int B, int L, int K, int G, int min_group, Chunking* ch) {
 
 static constexpr int kSamuMinGroup = 8;      // see chunking()
 static constexpr int kRglruMinGroup = 16;
-static constexpr int kParamSegments = 32;
 
 struct SamuSaved {
     float *p, *r, *u, *ctl, *mtab, *inv_norm, *entries, *mid;
@@ -155,8 +153,7 @@ static SamuFwdWs samu_fwd_ws_layout(void* base, const Chunking& ch, int M, size_
 
 struct SamuBwdWs {
     float *rsumm, *rchunk, *rgsum, *carry, *tok_part, *mode_part, *g_part;
-    double *g_seg, *mode_seg;
-    int n_tiles, n_blk, n_seg;
+    int n_tiles, n_blk;
 };
 static SamuBwdWs samu_bwd_ws_layout(void* base, const Chunking& ch, int D, int M, size_t* bytes) {
     Carver cv(base);
@@ -164,7 +161,6 @@ static SamuBwdWs samu_bwd_ws_layout(void* base, const Chunking& ch, int D, int M
     const size_t BCM = (size_t)ch.B * ch.C * M;
     w.n_tiles = samu_bwd_tiles(M);
     w.n_blk = (int)ceil_div((int64_t)ch.B * ch.L, samu_ctl_tok_per_blk());
-    w.n_seg = std::min(kParamSegments, std::max(1, std::min(w.n_blk, ch.B * ch.C)));
     w.rsumm = cv.take<float>(BCM * 2);
     w.rchunk = cv.take<float>((size_t)ch.B * ch.C * 4);
     w.rgsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
@@ -172,8 +168,6 @@ static SamuBwdWs samu_bwd_ws_layout(void* base, const Chunking& ch, int D, int M
     w.tok_part = cv.take<float>((size_t)ch.B * w.n_tiles * ch.L * 2);
     w.mode_part = cv.take<float>(BCM * 2);
     w.g_part = cv.take<float>((size_t)w.n_blk * samu_param_columns(D) * 2);
-    w.g_seg = cv.take<double>((size_t)w.n_seg * samu_param_columns(D) * 2);
-    w.mode_seg = cv.take<double>((size_t)w.n_seg * M * 2);
     if (bytes) *bytes = cv.off;
     return w;
 }
@@ -191,8 +185,6 @@ static RgSaved rg_saved_layout(void* base, const Chunking& ch, int D, size_t* by
 
 struct RgWs {
     float *summ, *gsum, *carry, *alpha_part;
-    double* alpha_seg;
-    int n_seg;
 };
 static RgWs rg_ws_layout(void* base, const Chunking& ch, int D, bool backward, size_t* bytes) {
     Carver cv(base);
@@ -203,8 +195,6 @@ static RgWs rg_ws_layout(void* base, const Chunking& ch, int D, bool backward, s
     if (backward) {
         w.carry = cv.take<float>(BCD);
         w.alpha_part = cv.take<float>(BCD);
-        w.n_seg = rglru_alpha_segments(ch.B, ch.C);
-        w.alpha_seg = cv.take<double>((size_t)w.n_seg * D);
     }
     if (bytes) *bytes = cv.off;
     return w;
@@ -410,12 +400,9 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
             "samu backward replay");
     LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, sv.u, sv.inv_norm, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part, s),
             "samu controller backward");
-    LRS_TRY(launch_samu_param_reduce(p, ch, ws.g_part, ws.n_blk, ws.mode_part, ws.g_seg, ws.n_seg,
-                                     ws.mode_seg, s),
-            "samu parameter reduction");
-    LRS_TRY(launch_samu_param_final(p, ws.g_seg, ws.mode_seg, ws.n_seg, dw_phi, dw_r, da_phi, da_r, dnu,
-                                    dtheta, s),
-            "samu parameter final");
+    LRS_TRY(launch_samu_params(p, ch, ws.g_part, ws.n_blk, ws.mode_part, dw_phi, dw_r, da_phi, da_r, dnu, dtheta,
+                               s),
+            "samu parameter reductions");
     return SCAN_OK;
 }
 
@@ -729,7 +716,7 @@ scan_status rglru_scan_bwd(int B, int L, int D, int K, int G, const void* x, con
             "rglru reverse prefix");
     LRS_TRY(launch_rglru_bwd_replay(p, ch, sv.entries, ws.carry, dy, dx, dlx, dla, f32, dh0, ws.alpha_part, s),
             "rglru backward replay");
-    LRS_TRY(launch_rglru_alpha_reduce(p, ch, ws.alpha_part, ws.alpha_seg, ws.n_seg, dalpha, s), "rglru alpha reduction");
+    LRS_TRY(launch_rglru_alpha_reduce(p, ch, ws.alpha_part, dalpha, s), "rglru alpha reduction");
     return SCAN_OK;
 }
 

@@ -24,14 +24,12 @@ enum KernelId {
     K_SAMU_REV_SUMMARY,
     K_SAMU_BWD_REPLAY,
     K_SAMU_CTL_BWD,
-    K_SAMU_PARAM_REDUCE,
-    K_SAMU_PARAM_FINAL,
+    K_SAMU_PARAMS,
     K_RGLRU_SUMMARY,
     K_RGLRU_REPLAY,
     K_RGLRU_REV_SUMMARY,
     K_RGLRU_BWD_REPLAY,
-    K_RGLRU_ALPHA_REDUCE,
-    K_RGLRU_ALPHA_FINAL,
+    K_RGLRU_ALPHA,
     K_SAMU_DECODE,
     K_BASE_SEQ,
     K_BASE_ASSOC,
@@ -131,12 +129,10 @@ int samu_param_columns(int D);
 hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const float* r_sv,
                                const float* u_sv, const float* inv_norm, const float* tok_part, int n_tiles,
                                void* dx_sel, int dx_f32, float* g_part, hipStream_t s);
-hipError_t launch_samu_param_reduce(const SamuParams& p, const Chunking& ch,
-                                    const float* g_part, int n_blk, const float* mode_part,
-                                    double* g_seg, int n_seg, double* mode_seg, hipStream_t s);
-hipError_t launch_samu_param_final(const SamuParams& p, const double* g_seg, const double* mode_seg,
-                                   int n_seg, float* dw_phi, float* dw_r, float* da_phi,
-                                   float* da_r, float* dnu, float* dtheta, hipStream_t s);
+// g_part: [n_blk, D+4] token-block partials; mode_part: [B*C, M] chunk partials
+hipError_t launch_samu_params(const SamuParams& p, const Chunking& ch, const float* g_part, int n_blk,
+                              const float* mode_part, float* dw_phi, float* dw_r, float* da_phi, float* da_r,
+                              float* dnu, float* dtheta, hipStream_t s);
 
 // one generation step: z_out = lambda(x_sel) z_in + b, y = z_out (z_in NULL = 0;
 // z_out may be z_in)
@@ -166,10 +162,8 @@ hipError_t launch_rglru_bwd_replay(const RglruParams& p, const Chunking& ch,
                                    const float* entries, const float* carry_in, const void* dy,
                                    void* dx, void* dlx, void* dla, int g_f32, float* dh0,
                                    float* alpha_part, hipStream_t s);
-// alpha_part: [B*C, D] per-chunk partials; seg: [n_seg, D] FP64 workspace
-int rglru_alpha_segments(int B, int C);
-hipError_t launch_rglru_alpha_reduce(const RglruParams& p, const Chunking& ch,
-                                     const float* alpha_part, double* seg, int n_seg,
+// alpha_part: [B*C, D] per-chunk partials
+hipError_t launch_rglru_alpha_reduce(const RglruParams& p, const Chunking& ch, const float* alpha_part,
                                      float* dalpha, hipStream_t s);
 
 // ------------------------------------------------------ comparison scans ---

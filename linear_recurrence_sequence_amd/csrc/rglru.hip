@@ -427,40 +427,47 @@ __global__ __launch_bounds__(RG_THREADS) __attribute__((amdgpu_waves_per_eu(LRS_
 }
 
 // ------------------------------------------------------ alpha reduction
-// d alpha = sum over the B*C per-chunk partial rows: rows are split into
-// n_seg contiguous segments, each summed in FP64 in a fixed order (4 row
-// lanes, then lane 0 + 1 + 2 + 3), and the segments are summed in order.
-constexpr int AR_COLS = 64;
-constexpr int AR_LANES = 4;
+// d alpha = the sum of the B*C per-chunk partial rows, in one launch: a
+// workgroup owns AR_COLS columns and splits the rows over AR_SG thread
+// groups; group sg adds rows sg, sg + AR_SG, ... in FP64 and in order,
+// AR_NB of them requested at once, and the group sums are added in group
+// order through LDS, AR_L2 at a time.  The result depends on the shape alone.
+constexpr int AR_COLS = 16;
+constexpr int AR_SG = 64;
+constexpr int AR_THREADS = AR_COLS * AR_SG;
+constexpr int AR_NB = 16;
+constexpr int AR_L2 = 8;
 
-__global__ __launch_bounds__(AR_COLS * AR_LANES) void rglru_alpha_seg_kernel(
-    int R, int D, int n_seg, const float* __restrict__ part, double* __restrict__ seg) {
-    __shared__ double sh[AR_LANES][AR_COLS];
-    const int cl = threadIdx.x % AR_COLS, rl = threadIdx.x / AR_COLS;
-    const int col = blockIdx.x * AR_COLS + cl;
-    const int s = blockIdx.y;
-    const int r0 = (int)((int64_t)R * s / n_seg), r1 = (int)((int64_t)R * (s + 1) / n_seg);
+__global__ __launch_bounds__(AR_THREADS) void rglru_alpha_kernel(int R, int D, const float* __restrict__ part,
+                                                                 float* __restrict__ dalpha) {
+    __shared__ double g1[AR_SG][AR_COLS];
+    __shared__ double g2[AR_SG / AR_L2][AR_COLS];
+    const int sg = threadIdx.x / AR_COLS, cl = threadIdx.x - sg * AR_COLS;
+    const int c0 = blockIdx.x * AR_COLS;
+    const int col = min(c0 + cl, D - 1);
     double acc = 0.0;
-    if (col < D) {
-#pragma unroll 4
-        for (int r = r0 + rl; r < r1; r += AR_LANES) acc += (double)part[(size_t)r * D + col];
+    for (int r0 = sg; r0 < R; r0 += AR_SG * AR_NB) {
+        float v[AR_NB];
+#pragma unroll
+        for (int k = 0; k < AR_NB; ++k) v[k] = part[(size_t)min(r0 + k * AR_SG, R - 1) * D + col];
+#pragma unroll
+        for (int k = 0; k < AR_NB; ++k) acc += r0 + k * AR_SG < R ? (double)v[k] : 0.0;
     }
-    sh[rl][cl] = acc;
+    g1[sg][cl] = acc;
     __syncthreads();
-    if (rl == 0 && col < D) seg[(size_t)s * D + col] = ((sh[0][cl] + sh[1][cl]) + sh[2][cl]) + sh[3][cl];
-}
-
-constexpr int AF_THREADS = 64;
-
-__global__ __launch_bounds__(AF_THREADS) void rglru_alpha_final_kernel(int D, int n_seg,
-                                                                       const double* __restrict__ seg,
-                                                                       float* __restrict__ dalpha) {
-    const int d = blockIdx.x * AF_THREADS + threadIdx.x;
-    if (d >= D) return;
-    double s = 0.0;
-#pragma unroll 16
-    for (int i = 0; i < n_seg; ++i) s += seg[(size_t)i * D + d];
-    dalpha[d] = (float)s;
+    if (sg < AR_SG / AR_L2) {
+        double t = 0.0;
+#pragma unroll
+        for (int g = 0; g < AR_L2; ++g) t += g1[sg * AR_L2 + g][cl];
+        g2[sg][cl] = t;
+    }
+    __syncthreads();
+    if (sg == 0 && c0 + cl < D) {
+        double t = 0.0;
+#pragma unroll
+        for (int g = 0; g < AR_SG / AR_L2; ++g) t += g2[g][cl];
+        dalpha[col] = (float)t;
+    }
 }
 
 inline dim3 rg_grid(int D, const Chunking& ch) {
@@ -472,8 +479,6 @@ inline RgIn rg_in(const RglruParams& p) {
 }
 
 }  // namespace
-
-int rglru_alpha_segments(int B, int C) { return (int)std::min<int64_t>(64, (int64_t)B * C); }
 
 hipError_t launch_rglru_summary(const RglruParams& p, const Chunking& ch, float* summ, hipStream_t s) {
     const dim3 grid = rg_grid(p.D, ch);
@@ -527,13 +532,9 @@ hipError_t launch_rglru_bwd_replay(const RglruParams& p, const Chunking& ch, con
 }
 
 hipError_t launch_rglru_alpha_reduce(const RglruParams& p, const Chunking& ch, const float* alpha_part,
-                                     double* seg, int n_seg, float* dalpha, hipStream_t s) {
-    LRS_LAUNCH(K_RGLRU_ALPHA_REDUCE, rglru_alpha_seg_kernel,
-               dim3((unsigned)ceil_div(p.D, AR_COLS), (unsigned)n_seg), dim3(AR_COLS * AR_LANES), 0, s,
-               ch.B * ch.C, p.D, n_seg, alpha_part, seg);
-    LRS_LAUNCH(K_RGLRU_ALPHA_FINAL, rglru_alpha_final_kernel, dim3((unsigned)ceil_div(p.D, AF_THREADS)),
-               dim3(AF_THREADS), 0,
-               s, p.D, n_seg, (const double*)seg, dalpha);
+                                     float* dalpha, hipStream_t s) {
+    LRS_LAUNCH(K_RGLRU_ALPHA, rglru_alpha_kernel, dim3((unsigned)ceil_div(p.D, AR_COLS)), dim3(AR_THREADS), 0, s,
+               ch.B * ch.C, p.D, alpha_part, dalpha);
     return hipGetLastError();
 }
 

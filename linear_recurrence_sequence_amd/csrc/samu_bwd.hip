@@ -413,155 +413,160 @@ __global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
 }
 
 // ------------------------------------------------ parameter reductions ---
-// Level 1 of the parameter reductions, FP64 and fixed order, one thread per
-// column (or mode) and segment:
-//   blocks x in [0, col_tiles): columns of g_part over a segment of token blocks
-//   blocks x in [col_tiles, ...): modes of mode_part over a segment of chunks
-constexpr int RED_THREADS = 64;
-
-__global__ __launch_bounds__(RED_THREADS) void samu_param_reduce_kernel(
-    int ncol, int n_blk, int seg_blk, int col_tiles, const float2* __restrict__ g_part,
-    double2* __restrict__ g_seg, int M, int nchunks, int seg_chunk,
-    const float2* __restrict__ mode_part, double2* __restrict__ mode_seg) {
-    const int seg = blockIdx.y;
-    // an empty segment (past the end) still writes zeros: level 2 sums all segments
-    if ((int)blockIdx.x < col_tiles) {
-        const int col = blockIdx.x * RED_THREADS + threadIdx.x;
-        if (col >= ncol) return;
-        const int b0 = min(n_blk, seg * seg_blk);
-        const int b1 = min(n_blk, b0 + seg_blk);
-        double sx = 0.0, sy = 0.0;
-#pragma unroll 8
-        for (int i = b0; i < b1; ++i) {
-            const float2 v = g_part[(size_t)i * ncol + col];
-            sx += v.x;
-            sy += v.y;
-        }
-        g_seg[(size_t)seg * ncol + col] = make_double2(sx, sy);
-    } else {
-        const int m = (blockIdx.x - col_tiles) * RED_THREADS + threadIdx.x;
-        if (m >= M) return;
-        const int c0 = min(nchunks, seg * seg_chunk);
-        const int c1 = min(nchunks, c0 + seg_chunk);
-        double sx = 0.0, sy = 0.0;
-#pragma unroll 8
-        for (int i = c0; i < c1; ++i) {
-            const float2 v = mode_part[(size_t)i * M + m];
-            sx += v.x;
-            sy += v.y;
-        }
-        mode_seg[(size_t)seg * M + m] = make_double2(sx, sy);
-    }
-}
-
-// Level 2: the segment sums of every column and every mode.  A workgroup
-// owns FIN_ITEMS columns (or modes) and splits the segments over FIN_SG
-// groups of threads: each thread adds up to FIN_SEG_PER segments in order,
-// all requested at once, and the group sums are added in group order through
-// LDS, so the result is fixed for a given shape.  Column workgroups also form
-// the FP64 direction norms and the sums of the scalar columns, then
+// One launch sums the token-block partials g_part [n_blk, D+4] (a float2 of
+// phi and r terms per column) and the chunk partials mode_part [B*C, M] (a
+// float2 of nu and theta terms per mode) in FP64 and in a fixed order, then
+// forms the parameter gradients.  A workgroup owns PR_ITEMS columns (or
+// modes) and splits the rows over PR_SG thread groups: group sg adds rows
+// sg, sg + PR_SG, ... in order, PR_NB of them requested at once, and the
+// group sums are added in group order through LDS, PR_L2 at a time.  The
+// result depends on the shape alone.  Column workgroups also form the FP64
+// direction norms and the sums of the scalar columns, then
 // dw = (g - w^ (w^ . g)) / ||w|| with w^ . g from the per-token sums of
 // u-bar * u (column D+2); the first one also writes da from column D+1.
-// This kernel is latency alone (a few MB), so it is laid out for few
-// dependent rounds of loads.
-constexpr int FIN_SG = 8;
-constexpr int FIN_ITEMS = 32;
-constexpr int FIN_THREADS = FIN_SG * FIN_ITEMS;
-constexpr int FIN_SEG_PER = 4;  // FIN_SG * FIN_SEG_PER >= the segment count
-constexpr int FIN_NORM_BATCH = 8;
+// A few MB in all, so the layout aims at few dependent rounds of loads with
+// one 1024-thread workgroup per CU.  (Issuing the norm, scalar-column and
+// row loads together measured slower than this order.)
+constexpr int PR_ITEMS = 16;
+constexpr int PR_SG = 64;
+constexpr int PR_THREADS = PR_ITEMS * PR_SG;
+constexpr int PR_NB = 16;
+constexpr int PR_L2 = 8;
+constexpr int PR_NORM = 4;  // direction entries per thread per round of loads
 
-// Sum over the segments of one item: this thread's share, then the groups.
-__device__ __forceinline__ double2 fin_segment_sum(const double2* __restrict__ seg, size_t stride, int item,
-                                                   int n_seg, int sg, int ii, double2 (*sh)[FIN_ITEMS]) {
-    double2 v[FIN_SEG_PER];
-#pragma unroll
-    for (int k = 0; k < FIN_SEG_PER; ++k) v[k] = seg[(size_t)min(sg * FIN_SEG_PER + k, n_seg - 1) * stride + item];
+struct ParamLds {
+    double2 g1[PR_SG][PR_ITEMS];
+    double2 g2[PR_SG / PR_L2][PR_ITEMS];
+    double norm[2][PR_THREADS / 64];
+    double2 scal[2];
+};
+
+// Sum of item `item` over rows [0, n) of part (row stride `stride`); valid in
+// the threads with sg == 0.
+__device__ __forceinline__ double2 pr_rows_sum(const float2* __restrict__ part, size_t stride, int item, int n,
+                                               int sg, int ii, ParamLds& sh) {
     double sx = 0.0, sy = 0.0;
+    for (int r0 = sg; r0 < n; r0 += PR_SG * PR_NB) {
+        float2 v[PR_NB];
 #pragma unroll
-    for (int k = 0; k < FIN_SEG_PER; ++k) {
-        const bool ok = sg * FIN_SEG_PER + k < n_seg;
-        sx += ok ? v[k].x : 0.0;
-        sy += ok ? v[k].y : 0.0;
+        for (int k = 0; k < PR_NB; ++k) v[k] = part[(size_t)min(r0 + k * PR_SG, n - 1) * stride + item];
+#pragma unroll
+        for (int k = 0; k < PR_NB; ++k) {
+            const bool ok = r0 + k * PR_SG < n;
+            sx += ok ? (double)v[k].x : 0.0;
+            sy += ok ? (double)v[k].y : 0.0;
+        }
     }
-    sh[sg][ii] = make_double2(sx, sy);
+    sh.g1[sg][ii] = make_double2(sx, sy);
+    __syncthreads();
+    if (sg < PR_SG / PR_L2) {
+        double tx = 0.0, ty = 0.0;
+#pragma unroll
+        for (int g = 0; g < PR_L2; ++g) {
+            tx += sh.g1[sg * PR_L2 + g][ii].x;
+            ty += sh.g1[sg * PR_L2 + g][ii].y;
+        }
+        sh.g2[sg][ii] = make_double2(tx, ty);
+    }
     __syncthreads();
     double tx = 0.0, ty = 0.0;
     if (sg == 0) {
 #pragma unroll
-        for (int g = 0; g < FIN_SG; ++g) {
-            tx += sh[g][ii].x;
-            ty += sh[g][ii].y;
+        for (int g = 0; g < PR_SG / PR_L2; ++g) {
+            tx += sh.g2[g][ii].x;
+            ty += sh.g2[g][ii].y;
         }
     }
     return make_double2(tx, ty);
 }
 
-__global__ __launch_bounds__(FIN_THREADS) void samu_param_final_kernel(
+__global__ __launch_bounds__(PR_THREADS) void samu_param_kernel(
     int D, int M, int col_blocks, const float* __restrict__ w_phi, const float* __restrict__ w_r,
-    const float* __restrict__ a_phi, const float* __restrict__ a_r,
-    const double2* __restrict__ g_seg, const double2* __restrict__ mode_seg, int n_seg,
-    float* __restrict__ dw_phi, float* __restrict__ dw_r, float* __restrict__ da_phi,
-    float* __restrict__ da_r, float* __restrict__ dnu, float* __restrict__ dtheta) {
-    __shared__ double2 sh[FIN_SG][FIN_ITEMS];
-    __shared__ double red[2][FIN_THREADS / 64];
-    __shared__ double2 scal[2];
+    const float* __restrict__ a_phi, const float* __restrict__ a_r, const float2* __restrict__ g_part, int n_blk,
+    const float2* __restrict__ mode_part, int nchunks, float* __restrict__ dw_phi, float* __restrict__ dw_r,
+    float* __restrict__ da_phi, float* __restrict__ da_r, float* __restrict__ dnu, float* __restrict__ dtheta) {
+    __shared__ ParamLds sh;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sg = tid / FIN_ITEMS, ii = tid - sg * FIN_ITEMS;
-    const int ncol = D + 4;
+    const int sg = tid / PR_ITEMS, ii = tid - sg * PR_ITEMS;
     if ((int)blockIdx.x >= col_blocks) {
-        const int m0 = (blockIdx.x - col_blocks) * FIN_ITEMS;
+        const int m0 = (blockIdx.x - col_blocks) * PR_ITEMS;
         const int m = min(m0 + ii, M - 1);
-        const double2 t = fin_segment_sum(mode_seg, M, m, n_seg, sg, ii, sh);
+        const double2 t = pr_rows_sum(mode_part, M, m, nchunks, sg, ii, sh);
         if (sg == 0 && m0 + ii < M) {
             dnu[m] = (float)t.x;
             dtheta[m] = (float)t.y;
         }
         return;
     }
-    // direction norms, FIN_NORM_BATCH loads in flight per thread
+    const int ncol = D + 4;
+    const int j = min((int)blockIdx.x * PR_ITEMS + ii, D);
+    const float wpj = w_phi[j], wrj = w_r[j];
+    // direction norms
     double nphi = 0.0, nr = 0.0;
-    for (int j0 = tid; j0 <= D; j0 += FIN_NORM_BATCH * FIN_THREADS) {
-        float a[FIN_NORM_BATCH], c[FIN_NORM_BATCH];
+    for (int j0 = tid; j0 <= D; j0 += PR_NORM * PR_THREADS) {
+        float a[PR_NORM], c[PR_NORM];
 #pragma unroll
-        for (int k = 0; k < FIN_NORM_BATCH; ++k) {
-            const int j = min(j0 + k * FIN_THREADS, D);
-            a[k] = w_phi[j];
-            c[k] = w_r[j];
+        for (int k = 0; k < PR_NORM; ++k) {
+            const int jj = min(j0 + k * PR_THREADS, D);
+            a[k] = w_phi[jj];
+            c[k] = w_r[jj];
         }
 #pragma unroll
-        for (int k = 0; k < FIN_NORM_BATCH; ++k) {
-            const bool ok = j0 + k * FIN_THREADS <= D;
+        for (int k = 0; k < PR_NORM; ++k) {
+            const bool ok = j0 + k * PR_THREADS <= D;
             nphi += ok ? (double)a[k] * a[k] : 0.0;
             nr += ok ? (double)c[k] * c[k] : 0.0;
         }
     }
     nphi = wave_sum_d(nphi);
     nr = wave_sum_d(nr);
-    if (lane == 0) { red[0][wave] = nphi; red[1][wave] = nr; }
-    // the scalar columns D+1 and D+2 over the segments: one segment per lane
-    // of the first wave (n_seg <= 64), then a fixed butterfly
+    if (lane == 0) {
+        sh.norm[0][wave] = nphi;
+        sh.norm[1][wave] = nr;
+    }
+    // the scalar columns D+1 and D+2 over all token blocks: rows lane,
+    // lane + 64, ... of the first wave, then a fixed butterfly
     if (wave == 0) {
-        const int i = min(lane, n_seg - 1);
-        const double2 v1 = g_seg[(size_t)i * ncol + D + 1], v2 = g_seg[(size_t)i * ncol + D + 2];
-        const bool ok = lane < n_seg;
-        const double s1x = wave_sum_d(ok ? v1.x : 0.0), s1y = wave_sum_d(ok ? v1.y : 0.0);
-        const double s2x = wave_sum_d(ok ? v2.x : 0.0), s2y = wave_sum_d(ok ? v2.y : 0.0);
+        double s1x = 0.0, s1y = 0.0, s2x = 0.0, s2y = 0.0;
+        for (int r0 = lane; r0 < n_blk; r0 += 64 * PR_NB) {
+            float2 v1[PR_NB], v2[PR_NB];
+#pragma unroll
+            for (int k = 0; k < PR_NB; ++k) {
+                const size_t row = (size_t)min(r0 + k * 64, n_blk - 1) * ncol;
+                v1[k] = g_part[row + D + 1];
+                v2[k] = g_part[row + D + 2];
+            }
+#pragma unroll
+            for (int k = 0; k < PR_NB; ++k) {
+                const bool ok = r0 + k * 64 < n_blk;
+                s1x += ok ? (double)v1[k].x : 0.0;
+                s1y += ok ? (double)v1[k].y : 0.0;
+                s2x += ok ? (double)v2[k].x : 0.0;
+                s2y += ok ? (double)v2[k].y : 0.0;
+            }
+        }
+        s1x = wave_sum_d(s1x);
+        s1y = wave_sum_d(s1y);
+        s2x = wave_sum_d(s2x);
+        s2y = wave_sum_d(s2y);
         if (lane == 0) {
-            scal[0] = make_double2(s1x, s1y);  // sum d-bar p, sum c-bar q
-            scal[1] = make_double2(s2x, s2y);  // w^ . g for phi and r
+            sh.scal[0] = make_double2(s1x, s1y);  // sum d-bar p, sum c-bar q
+            sh.scal[1] = make_double2(s2x, s2y);  // w^ . g for phi and r
         }
     }
-    const int j = min((int)blockIdx.x * FIN_ITEMS + ii, D);
-    const double2 g = fin_segment_sum(g_seg, ncol, j, n_seg, sg, ii, sh);  // its barrier also covers red, scal
-    if (sg != 0 || (int)blockIdx.x * FIN_ITEMS + ii > D) return;
+    const double2 g = pr_rows_sum(g_part, ncol, j, n_blk, sg, ii, sh);  // its barriers cover norm, scal
+    if (sg != 0 || (int)blockIdx.x * PR_ITEMS + ii > D) return;
     double Np = 0.0, Nr = 0.0;
-    for (int k = 0; k < FIN_THREADS / 64; ++k) { Np += red[0][k]; Nr += red[1][k]; }
+    for (int k = 0; k < PR_THREADS / 64; ++k) {
+        Np += sh.norm[0][k];
+        Nr += sh.norm[1][k];
+    }
     const double np = sqrt(Np), nrr = sqrt(Nr);
-    const double2 dot = scal[1];
-    dw_phi[j] = (float)((g.x - ((double)w_phi[j] / np) * dot.x) / np);
-    dw_r[j] = (float)((g.y - ((double)w_r[j] / nrr) * dot.y) / nrr);
+    const double2 dot = sh.scal[1];
+    dw_phi[j] = (float)((g.x - ((double)wpj / np) * dot.x) / np);
+    dw_r[j] = (float)((g.y - ((double)wrj / nrr) * dot.y) / nrr);
     if (j == 0) {
-        const double2 sa = scal[0];
+        const double2 sa = sh.scal[0];
         const double sM = sqrt((double)M);
         const double tp = tanh((double)a_phi[0]), tr = tanh((double)a_r[0]);
         da_phi[0] = (float)((1.0 - tp * tp) / sM * sa.x);
@@ -616,30 +621,14 @@ hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const flo
 
 int samu_param_columns(int D) { return D + 4; }
 
-hipError_t launch_samu_param_reduce(const SamuParams& p, const Chunking& ch, const float* g_part,
-                                    int n_blk, const float* mode_part, double* g_seg, int n_seg,
-                                    double* mode_seg, hipStream_t s) {
-    const int ncol = samu_param_columns(p.D);
-    const int seg_blk = (int)ceil_div(n_blk, n_seg);
-    const int nchunks = ch.B * ch.C;  // rows of mode_part: one per (batch row, chunk)
-    const int seg_chunk = (int)ceil_div(nchunks, n_seg);
-    const int col_tiles = (int)ceil_div(ncol, RED_THREADS);
-    const int mode_tiles = (int)ceil_div(p.M, RED_THREADS);
-    LRS_LAUNCH(K_SAMU_PARAM_REDUCE, samu_param_reduce_kernel, dim3(col_tiles + mode_tiles, n_seg),
-               dim3(RED_THREADS), 0, s, ncol, n_blk, seg_blk, col_tiles, (const float2*)g_part,
-               (double2*)g_seg, p.M, nchunks, seg_chunk, (const float2*)mode_part, (double2*)mode_seg);
-    return hipGetLastError();
-}
-
-hipError_t launch_samu_param_final(const SamuParams& p, const double* g_seg, const double* mode_seg,
-                                   int n_seg, float* dw_phi, float* dw_r, float* da_phi, float* da_r,
-                                   float* dnu, float* dtheta, hipStream_t s) {
-    if (n_seg > FIN_SG * FIN_SEG_PER) return hipErrorInvalidValue;
-    const int col_blocks = (int)ceil_div(p.D + 1, FIN_ITEMS);
-    const int grid = col_blocks + (int)ceil_div(p.M, FIN_ITEMS);
-    LRS_LAUNCH(K_SAMU_PARAM_FINAL, samu_param_final_kernel, dim3(grid), dim3(FIN_THREADS), 0, s, p.D,
-               p.M, col_blocks, p.w_phi, p.w_r, p.a_phi, p.a_r, (const double2*)g_seg,
-               (const double2*)mode_seg, n_seg, dw_phi, dw_r, da_phi, da_r, dnu, dtheta);
+hipError_t launch_samu_params(const SamuParams& p, const Chunking& ch, const float* g_part, int n_blk,
+                              const float* mode_part, float* dw_phi, float* dw_r, float* da_phi, float* da_r,
+                              float* dnu, float* dtheta, hipStream_t s) {
+    const int col_blocks = (int)ceil_div(p.D + 1, PR_ITEMS);
+    const int grid = col_blocks + (int)ceil_div(p.M, PR_ITEMS);
+    LRS_LAUNCH(K_SAMU_PARAMS, samu_param_kernel, dim3(grid), dim3(PR_THREADS), 0, s, p.D, p.M, col_blocks,
+               p.w_phi, p.w_r, p.a_phi, p.a_r, (const float2*)g_part, n_blk, (const float2*)mode_part,
+               ch.B * ch.C, dw_phi, dw_r, da_phi, da_r, dnu, dtheta);
     return hipGetLastError();
 }
 
