@@ -31,7 +31,7 @@ namespace {
 // w_t = lambda_t z_{t-1} for its H tokens and runs the adjoint over them in
 // reverse, starting from the cotangent carried in from the following chunk.
 // All drive and cotangent words of the chunk are requested before any math,
-// right after the saved states.  The per-token partial sums of a wave are
+// right after the saved states, in the order the sub-chunks consume them.  The per-token partial sums of a wave are
 // reduced through a padded LDS transpose (conflict-free both ways), one
 // sub-chunk at a time.
 constexpr int BWD_THREADS = 256;
@@ -73,14 +73,19 @@ __device__ __forceinline__ void bwd_chunk(
         }
     }
     uint32_t bw[K], gw[K];
+    // requested in the order they are consumed: the last sub-chunk first,
+    // its drive words forward in time, then its cotangent words backward
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-        if (FULL || i < kc) {
-            bw[i] = (drive + row0 + (size_t)i * M)[mm];
-            gw[i] = (dy + row0 + (size_t)i * M)[mm];
-        } else {
-            bw[i] = 0u;
-            gw[i] = 0u;
+    for (int h = NH - 1; h >= 0; --h) {
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            const int i = h * H + j;
+            bw[i] = (FULL || i < kc) ? (drive + row0 + (size_t)i * M)[mm] : 0u;
+        }
+#pragma unroll
+        for (int j = H - 1; j >= 0; --j) {
+            const int i = h * H + j;
+            gw[i] = (FULL || i < kc) ? (dy + row0 + (size_t)i * M)[mm] : 0u;
         }
     }
     __builtin_amdgcn_sched_barrier(0);
