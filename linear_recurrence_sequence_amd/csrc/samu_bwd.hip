@@ -242,7 +242,7 @@ __global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
     const float* __restrict__ p_sv, const float* __restrict__ r_sv,
     const float2* __restrict__ u_sv, const float* __restrict__ inv_norm, const float* __restrict__ tok_part,
     void* __restrict__ dx, float* __restrict__ g_part) {
-    // the block's tile partials [tiles][CTL_TB] float2, later the split sums [(TS - 1) * CT][4]
+    // the block's tile partials [tiles][CTL_TB] float2, later the split sums [TS - 1][4][CT]
     extern __shared__ float4 dyn[];
     float4* comb = dyn;
     __shared__ float u_sh[2][CTL_TB];
@@ -390,17 +390,18 @@ __global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
         // partial sums of the token splits, added in split order
         if (TS > 1) {
             if (act && ts > 0) {
-                float4* c = comb + ((size_t)(ts - 1) * CT + cj) * 4;
+                // [split][quarter][column thread]: lanes write adjacent 16-byte words
+                float4* c = comb + (size_t)(ts - 1) * 4 * CT + cj;
                 c[0] = make_float4(gp[0], gp[1], gp[2], gp[3]);
-                c[1] = make_float4(gp[4], gp[5], gp[6], gp[7]);
-                c[2] = make_float4(gr[0], gr[1], gr[2], gr[3]);
-                c[3] = make_float4(gr[4], gr[5], gr[6], gr[7]);
+                c[CT] = make_float4(gp[4], gp[5], gp[6], gp[7]);
+                c[2 * CT] = make_float4(gr[0], gr[1], gr[2], gr[3]);
+                c[3 * CT] = make_float4(gr[4], gr[5], gr[6], gr[7]);
             }
             __syncthreads();
             if (act && ts == 0) {
                 for (int k = 1; k < TS; ++k) {
-                    const float4* c = comb + ((size_t)(k - 1) * CT + cj) * 4;
-                    const float4 c0 = c[0], c1 = c[1], c2 = c[2], c3 = c[3];
+                    const float4* c = comb + (size_t)(k - 1) * 4 * CT + cj;
+                    const float4 c0 = c[0], c1 = c[CT], c2 = c[2 * CT], c3 = c[3 * CT];
                     gp[0] += c0.x; gp[1] += c0.y; gp[2] += c0.z; gp[3] += c0.w;
                     gp[4] += c1.x; gp[5] += c1.y; gp[6] += c1.z; gp[7] += c1.w;
                     gr[0] += c2.x; gr[1] += c2.y; gr[2] += c2.z; gr[3] += c2.w;
