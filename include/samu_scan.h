@@ -81,7 +81,8 @@ const char* scan_last_error(void);
  * ====================================================================== */
 
 /* Bytes of the forward-to-backward record: p, r, the per-token special
- * functions, the mode table, the entry state of every chunk and, for K = 32,
+ * functions, the mode table, the direction norms (1/||w|| and the FP64
+ * squared norms), the entry state of every chunk and, for K = 32,
  * the state entering the second 16-token half of every chunk (the backward
  * replay starts its sub-chunks from these instead of recomputing them).
  * Independent of G, so a backward may use another grouping than its forward. */

@@ -131,7 +131,7 @@ static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t
     s.u = cv.take<float>(BL * 2);
     s.ctl = cv.take<float>(BL * 4);
     s.mtab = cv.take<float>((size_t)M * 16);
-    s.inv_norm = cv.take<float>(4);
+    s.inv_norm = cv.take<float>(8);  // 1/||w_phi||, 1/||w_r||, pad, then the FP64 squared norms
     s.entries = cv.take<float>((size_t)ch.B * ch.C * M * 2);
     s.mid = cv.take<float>((size_t)ch.B * ch.C * samu_mid_states(ch.K) * M * 2);
     if (bytes) *bytes = cv.off;
@@ -400,8 +400,8 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
             "samu backward replay");
     LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, sv.u, sv.inv_norm, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part, s),
             "samu controller backward");
-    LRS_TRY(launch_samu_params(p, ch, ws.g_part, ws.n_blk, ws.mode_part, dw_phi, dw_r, da_phi, da_r, dnu, dtheta,
-                               s),
+    LRS_TRY(launch_samu_params(p, ch, reinterpret_cast<const double*>(sv.inv_norm + 4), ws.g_part, ws.n_blk,
+                               ws.mode_part, dw_phi, dw_r, da_phi, da_r, dnu, dtheta, s),
             "samu parameter reductions");
     return SCAN_OK;
 }

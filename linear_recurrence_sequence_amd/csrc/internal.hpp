@@ -98,7 +98,8 @@ struct SamuParams {
 
 // saved forward record (per token): p, r, u = (x~ . w^_phi, x~ . w^_r),
 // ctl = (E, C, S, d); per mode: the four-float4 constant table mtab;
-// inv_norm (NULL: not written) = (1/||w_phi||, 1/||w_r||).
+// inv_norm (NULL: not written): floats 0-1 = (1/||w_phi||, 1/||w_r||), floats
+// 4-7 = the FP64 squared norms (||w_phi||^2, ||w_r||^2) summed in a fixed order.
 hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
                                   float* u_out, float* ctl, float* mtab, float* inv_norm, hipStream_t s);
 // The backward replay handles a chunk as K / SAMU_BWD_SUB sub-chunks; the
@@ -130,9 +131,10 @@ hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const flo
                                const float* u_sv, const float* inv_norm, const float* tok_part, int n_tiles,
                                void* dx_sel, int dx_f32, float* g_part, hipStream_t s);
 // g_part: [n_blk, D+4] token-block partials; mode_part: [B*C, M] chunk partials
-hipError_t launch_samu_params(const SamuParams& p, const Chunking& ch, const float* g_part, int n_blk,
-                              const float* mode_part, float* dw_phi, float* dw_r, float* da_phi, float* da_r,
-                              float* dnu, float* dtheta, hipStream_t s);
+// wnorm2: the two FP64 squared direction norms the forward controller kept
+hipError_t launch_samu_params(const SamuParams& p, const Chunking& ch, const double* wnorm2, const float* g_part,
+                              int n_blk, const float* mode_part, float* dw_phi, float* dw_r, float* da_phi,
+                              float* da_r, float* dnu, float* dtheta, hipStream_t s);
 
 // one generation step: z_out = lambda(x_sel) z_in + b, y = z_out (z_in NULL = 0;
 // z_out may be z_in)

@@ -426,13 +426,14 @@ __global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
 // modes) and splits the rows over PR_SG thread groups: group sg adds rows
 // sg, sg + PR_SG, ... in order, PR_NB of them requested at once, and the
 // group sums are added in group order through LDS, PR_L2 at a time.  The
-// result depends on the shape alone.  Column workgroups also form the FP64
-// direction norms and the sums of the scalar columns, then
+// result depends on the shape alone.  Column workgroups also form the sums
+// of the scalar columns and, with the FP64 squared direction norms the
+// forward controller kept,
 // dw = (g - w^ (w^ . g)) / ||w|| with w^ . g from the per-token sums of
 // u-bar * u (column D+2); the first one also writes da from column D+1.
 // A few MB in all, so the layout aims at few dependent rounds of loads with
-// one 1024-thread workgroup per CU.  (Issuing the norm, scalar-column and
-// row loads together measured slower than this order.)
+// one 1024-thread workgroup per CU.  (Issuing the scalar-column and row loads
+// of a column workgroup together measured slower than this order.)
 constexpr int PR_ITEMS = 16;
 constexpr int PR_SG = 64;
 constexpr int PR_THREADS = PR_ITEMS * PR_SG;
@@ -443,7 +444,6 @@ constexpr int PR_NORM = 4;  // direction entries per thread per round of loads
 struct ParamLds {
     double2 g1[PR_SG][PR_ITEMS];
     double2 g2[PR_SG / PR_L2][PR_ITEMS];
-    double norm[2][PR_THREADS / 64];
     double2 scal[2];
 };
 
@@ -488,8 +488,9 @@ __device__ __forceinline__ double2 pr_rows_sum(const float2* __restrict__ part, 
 
 __global__ __launch_bounds__(PR_THREADS) void samu_param_kernel(
     int D, int M, int col_blocks, const float* __restrict__ w_phi, const float* __restrict__ w_r,
-    const float* __restrict__ a_phi, const float* __restrict__ a_r, const float2* __restrict__ g_part, int n_blk,
-    const float2* __restrict__ mode_part, int nchunks, float* __restrict__ dw_phi, float* __restrict__ dw_r,
+    const float* __restrict__ a_phi, const float* __restrict__ a_r, const double* __restrict__ wnorm2,
+    const float2* __restrict__ g_part, int n_blk, const float2* __restrict__ mode_part, int nchunks,
+    float* __restrict__ dw_phi, float* __restrict__ dw_r,
     float* __restrict__ da_phi, float* __restrict__ da_r, float* __restrict__ dnu, float* __restrict__ dtheta) {
     __shared__ ParamLds sh;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -507,29 +508,8 @@ __global__ __launch_bounds__(PR_THREADS) void samu_param_kernel(
     const int ncol = D + 4;
     const int j = min((int)blockIdx.x * PR_ITEMS + ii, D);
     const float wpj = w_phi[j], wrj = w_r[j];
-    // direction norms
-    double nphi = 0.0, nr = 0.0;
-    for (int j0 = tid; j0 <= D; j0 += PR_NORM * PR_THREADS) {
-        float a[PR_NORM], c[PR_NORM];
-#pragma unroll
-        for (int k = 0; k < PR_NORM; ++k) {
-            const int jj = min(j0 + k * PR_THREADS, D);
-            a[k] = w_phi[jj];
-            c[k] = w_r[jj];
-        }
-#pragma unroll
-        for (int k = 0; k < PR_NORM; ++k) {
-            const bool ok = j0 + k * PR_THREADS <= D;
-            nphi += ok ? (double)a[k] * a[k] : 0.0;
-            nr += ok ? (double)c[k] * c[k] : 0.0;
-        }
-    }
-    nphi = wave_sum_d(nphi);
-    nr = wave_sum_d(nr);
-    if (lane == 0) {
-        sh.norm[0][wave] = nphi;
-        sh.norm[1][wave] = nr;
-    }
+    // FP64 squared direction norms, formed by the forward controller
+    const double Np = wnorm2[0], Nr = wnorm2[1];
     // the scalar columns D+1 and D+2 over all token blocks: rows lane,
     // lane + 64, ... of the first wave, then a fixed butterfly
     if (wave == 0) {
@@ -560,13 +540,8 @@ __global__ __launch_bounds__(PR_THREADS) void samu_param_kernel(
             sh.scal[1] = make_double2(s2x, s2y);  // w^ . g for phi and r
         }
     }
-    const double2 g = pr_rows_sum(g_part, ncol, j, n_blk, sg, ii, sh);  // its barriers cover norm, scal
+    const double2 g = pr_rows_sum(g_part, ncol, j, n_blk, sg, ii, sh);  // its barriers cover scal
     if (sg != 0 || (int)blockIdx.x * PR_ITEMS + ii > D) return;
-    double Np = 0.0, Nr = 0.0;
-    for (int k = 0; k < PR_THREADS / 64; ++k) {
-        Np += sh.norm[0][k];
-        Nr += sh.norm[1][k];
-    }
     const double np = sqrt(Np), nrr = sqrt(Nr);
     const double2 dot = sh.scal[1];
     dw_phi[j] = (float)((g.x - ((double)wpj / np) * dot.x) / np);
@@ -627,13 +602,13 @@ hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const flo
 
 int samu_param_columns(int D) { return D + 4; }
 
-hipError_t launch_samu_params(const SamuParams& p, const Chunking& ch, const float* g_part, int n_blk,
-                              const float* mode_part, float* dw_phi, float* dw_r, float* da_phi, float* da_r,
-                              float* dnu, float* dtheta, hipStream_t s) {
+hipError_t launch_samu_params(const SamuParams& p, const Chunking& ch, const double* wnorm2, const float* g_part,
+                              int n_blk, const float* mode_part, float* dw_phi, float* dw_r, float* da_phi,
+                              float* da_r, float* dnu, float* dtheta, hipStream_t s) {
     const int col_blocks = (int)ceil_div(p.D + 1, PR_ITEMS);
     const int grid = col_blocks + (int)ceil_div(p.M, PR_ITEMS);
     LRS_LAUNCH(K_SAMU_PARAMS, samu_param_kernel, dim3(grid), dim3(PR_THREADS), 0, s, p.D, p.M, col_blocks,
-               p.w_phi, p.w_r, p.a_phi, p.a_r, (const float2*)g_part, n_blk, (const float2*)mode_part,
+               p.w_phi, p.w_r, p.a_phi, p.a_r, wnorm2, (const float2*)g_part, n_blk, (const float2*)mode_part,
                ch.B * ch.C, dw_phi, dw_r, da_phi, da_r, dnu, dtheta);
     return hipGetLastError();
 }

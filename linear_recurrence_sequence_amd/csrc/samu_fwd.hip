@@ -122,9 +122,34 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
 #pragma unroll
     for (int i = 0; i < CTL_WAVES; ++i) { np += red[0][i]; nr += red[1][i]; }
     const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
-    if (inv_norm && blockIdx.x == 0 && tid == 0) {  // for the controller backward
-        inv_norm[0] = inv_phi;
-        inv_norm[1] = inv_r;
+    if (inv_norm && blockIdx.x == 0) {
+        // for the backward: 1/||w|| as used here (controller backward), and
+        // the FP64 squared norms in a fixed order (parameter gradients)
+        double sp2 = 0.0, sr2 = 0.0;
+        for (int j = tid; j <= D; j += CTL_THREADS) {
+            sp2 += (double)w_phi[j] * w_phi[j];
+            sr2 += (double)w_r[j] * w_r[j];
+        }
+        sp2 = wave_sum_d(sp2);
+        sr2 = wave_sum_d(sr2);
+        __shared__ double dred[2][CTL_WAVES];
+        if (lane == 0) {
+            dred[0][wave] = sp2;
+            dred[1][wave] = sr2;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            double np2 = 0.0, nr2 = 0.0;
+            for (int i = 0; i < CTL_WAVES; ++i) {
+                np2 += dred[0][i];
+                nr2 += dred[1][i];
+            }
+            inv_norm[0] = inv_phi;
+            inv_norm[1] = inv_r;
+            double* n2 = reinterpret_cast<double*>(inv_norm + 4);
+            n2[0] = np2;
+            n2[1] = nr2;
+        }
     }
     const float amp_phi = tanhf(a_phi[0]) / sqrtf((float)M);
     const float amp_r = tanhf(a_r[0]) / sqrtf((float)M);
