@@ -80,6 +80,9 @@ def kernel_bytes(name, B, L, D, K, G):
         # x_sel, p, r, u, per-tile partials -> dx_sel, per-block direction partials
         "samu_controller_bwd": 2 * BLD + 16 * BL + 8 * B * n_tiles * L + 2 * BLD
         + 8 * (-(-BL // 64)) * (D + 4),
+        # per-block direction partials, per-(chunk, mode) spectrum partials, both
+        # directions and their squared norms -> dw_phi, dw_r, da, dnu, dtheta
+        "samu_params": 8 * (-(-BL // 64)) * (D + 4) + 8 * BCM + 8 * (D + 1) + 16 + 8 * (D + 1) + 8 + 8 * M,
     }
     return table.get(name)
 
