@@ -30,8 +30,10 @@ namespace {
 // forward replay kept): a sub-chunk recomputes lambda_t and
 // w_t = lambda_t z_{t-1} for its H tokens and runs the adjoint over them in
 // reverse, starting from the cotangent carried in from the following chunk.
-// All drive and cotangent words of the chunk are requested before any math,
-// right after the saved states, in the order the sub-chunks consume them.  The per-token partial sums of a wave are
+// All drive words and the last sub-chunk's cotangent words are requested
+// before any math, right after the saved states, in the order the sub-chunks
+// consume them; each earlier sub-chunk requests its cotangent words as it
+// starts.  The per-token partial sums of a wave are
 // reduced through a padded LDS transpose (conflict-free both ways), one
 // sub-chunk at a time.
 constexpr int BWD_THREADS = 256;
@@ -74,7 +76,11 @@ __device__ __forceinline__ void bwd_chunk(
     }
     uint32_t bw[K], gw[K];
     // requested in the order they are consumed: the last sub-chunk first,
-    // its drive words forward in time, then its cotangent words backward
+    // its drive words forward in time, then its cotangent words backward.
+    // The cotangent words of the earlier sub-chunks are requested when their
+    // sub-chunk starts: holding them through the last sub-chunk would take
+    // the kernel past 128 VGPRs, i.e. from 4 to 3 waves per SIMD, which
+    // costs more than the latency the early request hides.
 #pragma unroll
     for (int h = NH - 1; h >= 0; --h) {
 #pragma unroll
@@ -82,6 +88,7 @@ __device__ __forceinline__ void bwd_chunk(
             const int i = h * H + j;
             bw[i] = (FULL || i < kc) ? (drive + row0 + (size_t)i * M)[mm] : 0u;
         }
+        if (h != NH - 1) continue;  // earlier sub-chunks: requested when they start
 #pragma unroll
         for (int j = H - 1; j >= 0; --j) {
             const int i = h * H + j;
@@ -97,6 +104,13 @@ __device__ __forceinline__ void bwd_chunk(
     for (int h = NH - 1; h >= 0; --h) {
         const int i0 = h * H;
         if (!FULL && i0 >= kc) continue;  // uniform over the workgroup
+        if (h != NH - 1) {
+#pragma unroll
+            for (int j = H - 1; j >= 0; --j) {
+                const int i = i0 + j;
+                gw[i] = (FULL || i < kc) ? (dy + row0 + (size_t)i * M)[mm] : 0u;
+            }
+        }
         cf lam[H], wz[H];
         {
             cf z = ck[h];
