@@ -274,8 +274,10 @@ __global__ __launch_bounds__(RG_THREADS) void rglru_rev_summary_kernel(RgIn in, 
 // The chunk is handled H tokens at a time, last sub-chunk first.  For each
 // sub-chunk the forward is recomputed from a checkpoint (the state entering
 // the sub-chunk, found by one forward pass over the earlier sub-chunks),
-// keeping h_{t-1} and the three input words in registers; then the adjoint
-// runs back over it, regenerating the gates, from the cotangent carried in.
+// keeping the three input words in registers and h_{t-1} in the lane's own
+// LDS slots; then the adjoint runs back over it, regenerating the gates,
+// from the cotangent carried in.  The history in LDS keeps the kernel at
+// 4 waves per SIMD (123 VGPRs; in registers it took 139, 3 waves).
 struct RgBwdOut {
     const uint32_t* dy;
     void* dx;
@@ -286,9 +288,9 @@ struct RgBwdOut {
 template <int H, bool F32, bool FULL>
 __device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
                                            size_t tok0, int lw, int kq, uint32_t rm,
-                                           const float (&h_in)[2], float (&carry)[2], float (&acc)[2]) {
+                                           const float (&h_in)[2], float (&carry)[2], float (&acc)[2],
+                                           float2* hist) {
     uint32_t xs[H], lxs[H], las[H], gws[H];
-    float hp[H][2];
     float h[2] = {h_in[0], h_in[1]};
 #pragma unroll
     for (int i = 0; i < H; ++i) {
@@ -306,14 +308,15 @@ __device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[
             const float xv[2] = {bf16_lo(xs[i]), bf16_hi(xs[i])};
             const float lxv[2] = {bf16_lo(lxs[i]), bf16_hi(lxs[i])};
             const float lav[2] = {bf16_lo(las[i]), bf16_hi(las[i])};
+            hist[i * 64] = make_float2(h[0], h[1]);
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
-                hp[i][v] = h[v];
                 const Gate g = gates(k[v], lxv[v], lav[v], rs);
                 h[v] = fmaf(g.a, h[v], xv[v] * g.gx * g.m);
             }
         }
     }
+    asm volatile("" ::: "memory");  // read the history back from LDS, not from registers
 #pragma unroll
     for (int i = H - 1; i >= 0; --i) {
         if (FULL || i < kq) {
@@ -326,6 +329,8 @@ __device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[
             const uint32_t law = RG_BWD_KEEP ? las[i] : opaque_v(las[i]);
             const float lxv[2] = {bf16_lo(lxw), bf16_hi(lxw)};
             const float lav[2] = {bf16_lo(law), bf16_hi(law)};
+            const float2 hv = hist[i * 64];
+            const float hpv[2] = {hv.x, hv.y};
             float ox[2], olx[2], ola[2];
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
@@ -337,7 +342,7 @@ __device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[
                 // d h / d a = h_{t-1} + x g^x dm/da, dm/da = -a / sqrt(u) (capped);
                 // zero at a segment start, where a and m are constants
                 const float dm_da = -gt.a0 * fminf(gt.r, RG_RSQ_CAP);
-                const float abar = rs ? 0.0f : g * fmaf(xg, dm_da, hp[i][v]);
+                const float abar = rs ? 0.0f : g * fmaf(xg, dm_da, hpv[v]);
                 // d a / d l^a = a (-8 sp) g^a (1 - g^a); d a / d alpha = a g^a (-8 sigmoid(alpha))
                 const float ag = abar * gt.a0 * gt.ga;
                 ola[v] = ag * k[v].sp8 * (1.0f - gt.ga);
@@ -384,7 +389,8 @@ __device__ __forceinline__ void rg_advance(const RgIn& in, const ChanConst (&k)[
 template <int K, int H, bool F32, bool FULL>
 __device__ __forceinline__ void rg_bwd_chunk(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
                                              size_t tok0, int lw, int kc, uint32_t rm,
-                                             const float (&h0)[2], float (&carry)[2], float (&acc)[2]) {
+                                             const float (&h0)[2], float (&carry)[2], float (&acc)[2],
+                                             float2* hist) {
     constexpr int NS = K / H;
     const int kq = FULL ? K : opaque(kc);
     float ck[NS][2];
@@ -397,7 +403,8 @@ __device__ __forceinline__ void rg_bwd_chunk(const RgIn& in, const ChanConst (&k
     }
 #pragma unroll
     for (int s = NS - 1; s >= 0; --s)
-        rg_bwd_sub<H, F32, FULL>(in, k, o, tok0 + s * H, lw, kq - s * H, rm >> (s * H), ck[s], carry, acc);
+        rg_bwd_sub<H, F32, FULL>(in, k, o, tok0 + s * H, lw, kq - s * H, rm >> (s * H), ck[s], carry, acc,
+                                 hist);
 }
 
 #ifndef LRS_RG_BWD_WPE
@@ -420,8 +427,11 @@ __global__ __launch_bounds__(RG_THREADS) __attribute__((amdgpu_waves_per_eu(LRS_
     const float2 ci = reinterpret_cast<const float2*>(carry_in)[cw];
     const float h0[2] = {e.x, e.y};
     float carry[2] = {ci.x, ci.y}, acc[2] = {0.f, 0.f};
-    if (kc == K) rg_bwd_chunk<K, H, F32, true>(in, k, o, tok0, lw, K, rm, h0, carry, acc);
-    else rg_bwd_chunk<K, H, F32, false>(in, k, o, tok0, lw, kc, rm, h0, carry, acc);
+    // each lane's h_{t-1} history of a sub-chunk, [wave][token][lane]
+    __shared__ float2 hist_all[RG_THREADS / 64][H][64];
+    float2* hist = &hist_all[threadIdx.x >> 6][0][threadIdx.x & 63];
+    if (kc == K) rg_bwd_chunk<K, H, F32, true>(in, k, o, tok0, lw, K, rm, h0, carry, acc, hist);
+    else rg_bwd_chunk<K, H, F32, false>(in, k, o, tok0, lw, kc, rm, h0, carry, acc, hist);
     reinterpret_cast<float2*>(alpha_part)[cw] = make_float2(acc[0] * k[0].dsp8, acc[1] * k[1].dsp8);
     if (dh0 && c == 0) reinterpret_cast<float2*>(dh0)[(size_t)b * in.W + lw] = make_float2(carry[0], carry[1]);
 }
