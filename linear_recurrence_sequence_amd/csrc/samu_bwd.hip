@@ -190,7 +190,12 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(LRS
     const float2 ci = carry_in[cidx];
     cf carry = {ci.x, ci.y};
     float acc_nu = 0.f, acc_th = 0.f;
-    if ((c + 1) * K <= L)
+    // full chunks of workgroups whose lanes all hold a mode take a copy with
+    // the per-token lane masks folded away
+    if ((c + 1) * K <= L && (int)(blockIdx.x + 1) * BWD_THREADS <= M)
+        bwd_chunk<K, H, F32, true>(lds, sctl, k, true, lane, wave, tile, n_tiles, L, M, C, b, c, mm, ctl,
+                                   drive, entries, mid, dy, db, tok_part, carry, acc_nu, acc_th);
+    else if ((c + 1) * K <= L)
         bwd_chunk<K, H, F32, true>(lds, sctl, k, active, lane, wave, tile, n_tiles, L, M, C, b, c, mm, ctl,
                                    drive, entries, mid, dy, db, tok_part, carry, acc_nu, acc_th);
     else
