@@ -408,7 +408,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const int m0 = (blockIdx.x * blockDim.x + threadIdx.x) * VM;
     const int c = blockIdx.y, b = blockIdx.z;
     const bool active = m0 < M;
-    if ((c + 1) * K <= L)
+    // full chunks of workgroups whose lanes all hold modes take a copy with
+    // the per-token lane masks folded away
+    if ((c + 1) * K <= L && (int)((blockIdx.x + 1) * blockDim.x) * VM <= M)
+        replay_chunk<VM, K, F32, true>(sctl, L, M, C, b, c, m0, true, ctl, drive, mtab, entries, mid, y,
+                                       z_final);
+    else if ((c + 1) * K <= L)
         replay_chunk<VM, K, F32, true>(sctl, L, M, C, b, c, m0, active, ctl, drive, mtab, entries, mid, y,
                                        z_final);
     else
