@@ -1,11 +1,18 @@
 """The C ABI: every function include/samu_scan.h declares is exported by the
 built library, size queries follow the documented layouts, and invalid
-arguments return their status before anything is enqueued (these calls never
-reach the GPU, so they run on the CPU)."""
+arguments return their status before anything is enqueued.
+
+The rejection tests pass made-up device addresses.  They only ever run in a
+process that sees no GPU: if a validation check regressed and let a call
+through, its launch would then fail for want of a device instead of touching
+those addresses.  Where a GPU is visible, the module re-runs itself in a child
+process with HIP_VISIBLE_DEVICES and ROCR_VISIBLE_DEVICES empty."""
 import ctypes
 import json
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -14,6 +21,23 @@ HEADER = os.path.join(ROOT, "include", "samu_scan.h")
 LIB = os.path.join(ROOT, "linear_recurrence_sequence_amd", "libsamu_scan.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libsamu_scan.so not built")
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0    # counts devices without initializing them
+
+
+fake_pointers = pytest.mark.skipif(_gpu_visible(), reason="made-up device addresses run only where no GPU "
+                                                          "is visible (see test_rejections_in_a_gpu_free_child)")
+
+
+@pytest.mark.skipif(not _gpu_visible(), reason="the rejection tests run in this process")
+def test_rejections_in_a_gpu_free_child():
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", __file__],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
 
 
 def declared_functions():
@@ -101,12 +125,14 @@ def _call_samu_fwd(a):
     (dict(ws=16), -4),
     (dict(y=0x100000), -6), (dict(z_final=0x300300), -6), (dict(workspace=0x400000), -6),
 ])
+@fake_pointers
 def test_samu_fwd_rejects_before_enqueue(over, status):
     from linear_recurrence_sequence_amd import scan
     assert _call_samu_fwd(_samu_fwd_args(**over)) == status
     assert scan.lib().scan_last_error().decode()
 
 
+@fake_pointers
 def test_rglru_fwd_rejects_before_enqueue():
     from linear_recurrence_sequence_amd import scan
     L = scan.lib()
@@ -147,12 +173,14 @@ def _call_decode(**over):
     (dict(z_out=0x500020), -6),             # z_out partly overlaps z_in
     (dict(z_out=0x700000), -6),             # z_out overlaps y
 ])
+@fake_pointers
 def test_samu_decode_rejects_before_enqueue(over, status):
     from linear_recurrence_sequence_amd import scan
     assert _call_decode(**over) == status
     assert scan.lib().scan_last_error().decode()
 
 
+@fake_pointers
 def test_baseline_scans_reject_before_enqueue():
     from linear_recurrence_sequence_amd import scan
     L = scan.lib()
@@ -175,6 +203,7 @@ def test_baseline_scans_reject_before_enqueue():
     assert L.rglru_scan_baseline_fwd(0, 1, 8, 4, *r, None, None, f(0x200000), 0, None, None, 0, None) == -6
 
 
+@fake_pointers
 def test_gate_projection_rejects_before_enqueue():
     from linear_recurrence_sequence_amd import scan
     L = scan.lib()
@@ -200,3 +229,4 @@ def test_gate_projection_rejects_before_enqueue():
     assert L.rglru_gate_proj_bwd(1, 8, 256, *bw, 3, f(0x600000), f(0x600000), *outs, f(0x800000), ws, None) == -2
     assert L.rglru_gate_proj_bwd(1, 8, 256, *bw, 0, f(0x600000), f(0x600010), *outs, f(0x800000), ws, None) == -6
     assert L.rglru_gate_proj_bwd(1, 8, 256, *bw, 0, f(0x600000), f(0x400000), *outs, f(0x800000), ws, None) == -6
+

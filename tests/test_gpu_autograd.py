@@ -33,7 +33,16 @@ def test_samu_scan_autograd_matches_direct_adjoint():
         assert torch.equal(leaves[leaf].grad, g[name]), leaf
 
 
-def test_rglru_layer_autograd_matches_composition():
+def test_rglru_layer_autograd_matches_composition_and_oracle():
+    """The layer's gradients through autograd: equal bit for bit to the
+    entry-point composition (scan adjoint in FP32, projection adjoint
+    accumulated into that dx, one rounding to BF16), and within the BF16
+    floor + 1e-4 (1e-5 for y) of the FP64 oracle fed the GPU's logits."""
+    import numpy as np
+
+    import oracle
+    from tests.helpers import bf16_floor
+
     B, L, D = 2, 200, 512
     say(f"[autograd] RG-LRU layer B={B} L={L} D={D}")
     inp = inputs.rglru_inputs(B, L, D, 52, reset_p=0.05, h0_std=0.1, dh_final_std=0.1)
@@ -46,14 +55,42 @@ def test_rglru_layer_autograd_matches_composition():
     # the same layer from the entry points
     lx, la = scan.rglru_gate_proj_fwd(d["x"], d["w_x"], d["b_x"], d["w_a"], d["b_a"])
     y2, hf2, saved = scan.rglru_scan_fwd(d["x"], lx, la, d["alpha"], d["reset"], d["h0"])
-    g = scan.rglru_scan_bwd(d["x"], lx, la, d["alpha"], d["reset"], saved, d["dy"], d["dh_final"])
+    g = scan.rglru_scan_bwd(d["x"], lx, la, d["alpha"], d["reset"], saved, d["dy"], d["dh_final"],
+                            grad_dtype=torch.float32)
     p = scan.rglru_gate_proj_bwd(d["x"], d["w_x"], d["w_a"], g["dlx"], g["dla"], g["dx"])
     torch.cuda.synchronize()
     assert torch.equal(y, y2) and torch.equal(hf, hf2)
     assert torch.equal(leaves["alpha"].grad, g["dalpha"]) and torch.equal(leaves["h0"].grad, g["dh0"])
     assert torch.equal(leaves["b_x"].grad, p["db_x"]) and torch.equal(leaves["b_a"].grad, p["db_a"])
-    # weight gradients come back in the weights' BF16; dx is summed by autograd in BF16 from its two paths
-    for k, ref in (("w_x", p["dw_x"]), ("w_a", p["dw_a"]), ("x", p["dx"])):
-        e = rel_l2(to_f64(leaves[k].grad), to_f64(ref))
-        say(f"   {k}: rel-L2 {e:.2e} against the composition")
-        assert e <= 1e-2, (k, e)
+    assert torch.equal(leaves["x"].grad, p["dx"].to(torch.bfloat16))
+    assert torch.equal(leaves["w_x"].grad, p["dw_x"].to(torch.bfloat16))
+    assert torch.equal(leaves["w_a"].grad, p["dw_a"].to(torch.bfloat16))
+    # against the oracle, on the GPU's own BF16 logits (a rounding decision both sides share)
+    lxg = lx.view(torch.int16).cpu().numpy().view(np.uint16)
+    lag = la.view(torch.int16).cpu().numpy().view(np.uint16)
+    rf = oracle.rglru_fwd(inp["x"], lxg, lag, inp["alpha"], inp["reset"], inp["h0"])
+    rg = oracle.rglru_bwd(inp["x"], lxg, lag, inp["alpha"], inp["reset"], inp["h0"], inp["dy"], inp["dh_final"])
+    dx, dw_x, db_x = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_x"], rg["dlx"], rg["dx"])
+    dx, dw_a, db_a = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_a"], rg["dla"], dx)
+    e = {"y": rel_l2(to_f64(y), rf["y"]), "h_final": rel_l2(to_f64(hf), rf["h_final"]),
+         "x": rel_l2(to_f64(leaves["x"].grad), dx), "w_x": rel_l2(to_f64(leaves["w_x"].grad), dw_x),
+         "w_a": rel_l2(to_f64(leaves["w_a"].grad), dw_a), "b_x": rel_l2(to_f64(leaves["b_x"].grad), db_x),
+         "b_a": rel_l2(to_f64(leaves["b_a"].grad), db_a), "alpha": rel_l2(to_f64(leaves["alpha"].grad), rg["dalpha"]),
+         "h0": rel_l2(to_f64(leaves["h0"].grad), rg["dh0"])}
+    say("   errors:", {k: f"{v:.2e}" for k, v in e.items()})
+    assert e["y"] <= bf16_floor(rf["y"]) + 1e-5 and e["h_final"] <= 1e-5
+    for k, ref in (("x", dx), ("w_x", dw_x), ("w_a", dw_a)):
+        assert e[k] <= bf16_floor(ref) + 1e-4, (k, e[k])
+    for k in ("b_x", "b_a", "alpha", "h0"):
+        assert e[k] <= 1e-4, (k, e[k])
+
+
+def test_autograd_refuses_non_bf16_streams():
+    inp = inputs.samu_inputs(1, 40, 16, 54)
+    d = {k: dev_tensor(v) for k, v in inp.items()}
+    with pytest.raises(ValueError, match="bfloat16"):
+        ag.samu_scan(d["x_sel"].float(), d["b"], d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"],
+                     d["theta"])
+    with pytest.raises(ValueError, match="bfloat16"):
+        ag.samu_scan(d["x_sel"], d["b"].float(), d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"],
+                     d["theta"])

@@ -76,29 +76,61 @@ def test_layer_parity(B, L, D, reset_p):
         assert errs[k] <= TOL_GRAD, (k, errs[k])
 
 
+def _u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
 def test_layer_full_size_and_bf16_mode():
-    """B=1, L=32768, D=2048 (the metric shape): FP32-mode parity, then the
-    BF16 mode (BF16 cotangents into BF16 matrix-core products) against it."""
+    """B=1, L=32768, D=2048 (the metric shape): every output of the layer
+    against the oracle fed the GPU's BF16 logits (a rounding decision both
+    sides then share).
+      * FP32 mode: y, h_final at 1e-5; dx (scan and projection adjoints
+        summed), dW, db, d alpha, dh0 at 1e-4.
+      * BF16 mode: y within the BF16 floor + 1e-5, h_final, d alpha, dh0 at
+        1e-5 / 1e-4; the projection adjoint against the oracle fed the same
+        BF16 cotangents the GPU multiplied: dx_out within half a BF16 ulp of
+        the exact sum plus FP32 accumulation slack, dW and db at 1e-5."""
+    from tests.helpers import bf16_floor
     B, L, D = 1, 32768, 2048
-    say(f"[gate proj] full size B={B} L={L} D={D}")
-    inp, prm, lx, la, y, hf, g, p = _run(B, L, D, 3103, 0.0)
-    lxg = lx.view(torch.int16).cpu().numpy().view(np.uint16)
-    lag = la.view(torch.int16).cpu().numpy().view(np.uint16)
-    say("[gate proj] full size: oracle on the GPU's logits")
-    rg = oracle.rglru_bwd(inp["x"], lxg, lag, inp["alpha"], inp["reset"], inp["h0"], inp["dy"], inp["dh_final"])
-    dx, dw_x, db_x = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_x"], rg["dlx"], rg["dx"])
-    dx, dw_a, db_a = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_a"], rg["dla"], dx)
-    errs = {"dx": rel_l2(to_f64(p["dx"]), dx), "dw_x": rel_l2(to_f64(p["dw_x"]), dw_x),
-            "dw_a": rel_l2(to_f64(p["dw_a"]), dw_a), "db_x": rel_l2(to_f64(p["db_x"]), db_x)}
-    say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
-    for k, v in errs.items():
-        assert v <= TOL_GRAD, (k, v)
-    say("[gate proj] full size: BF16 mode")
-    _, _, _, _, _, _, gb, pb = _run(B, L, D, 3103, 0.0, dtype=torch.bfloat16)
-    for k in ("dw_x", "dw_a", "db_x", "db_a"):
-        e = rel_l2(to_f64(pb[k]), to_f64(p[k]))
-        say(f"   bf16 vs f32 mode {k}: {e:.2e}")
-        assert e <= 2e-2, (k, e)
+    for mode, dt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        say(f"[gate proj] full size B={B} L={L} D={D}, {mode} mode")
+        inp, prm, lx, la, y, hf, g, p = _run(B, L, D, 3103, 0.0, dtype=dt)
+        _check_logits("l^x", lx, inp["x"], prm["w_x"], prm["b_x"])
+        _check_logits("l^a", la, inp["x"], prm["w_a"], prm["b_a"])
+        say(f"[gate proj] full size {mode}: oracle on the GPU's logits")
+        lxg, lag = _u16(lx), _u16(la)
+        rf = oracle.rglru_fwd(inp["x"], lxg, lag, inp["alpha"], inp["reset"], inp["h0"])
+        rg = oracle.rglru_bwd(inp["x"], lxg, lag, inp["alpha"], inp["reset"], inp["h0"], inp["dy"],
+                              inp["dh_final"])
+        e = {"y": rel_l2(to_f64(y), rf["y"]), "h_final": rel_l2(to_f64(hf), rf["h_final"]),
+             "dalpha": rel_l2(to_f64(g["dalpha"]), rg["dalpha"]), "dh0": rel_l2(to_f64(g["dh0"]), rg["dh0"])}
+        if mode == "f32":
+            dl_x, dl_a, dx_in = rg["dlx"], rg["dla"], rg["dx"]
+        else:
+            dl_x, dl_a, dx_in = _u16(g["dlx"]), _u16(g["dla"]), _u16(g["dx"])
+        dx, dw_x, db_x = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_x"], dl_x, dx_in)
+        dx, dw_a, db_a = oracle.rglru_gate_proj_bwd(inp["x"], prm["w_a"], dl_a, dx)
+        for k, ref in (("dw_x", dw_x), ("db_x", db_x), ("dw_a", dw_a), ("db_a", db_a)):
+            e[k] = rel_l2(to_f64(p[k]), ref)
+        if mode == "f32":
+            e["dx"] = rel_l2(to_f64(p["dx"]), dx)
+        say("   errors:", {k: f"{v:.2e}" for k, v in e.items()})
+        assert e["y"] <= (bf16_floor(rf["y"]) if mode == "bf16" else 0.0) + TOL_OUT
+        assert e["h_final"] <= TOL_OUT
+        for k in ("dalpha", "dh0") + (("dx",) if mode == "f32" else ()):
+            assert e[k] <= TOL_GRAD, (k, e[k])
+        for k in ("dw_x", "db_x", "dw_a", "db_a"):
+            assert e[k] <= (TOL_GRAD if mode == "f32" else TOL_OUT), (k, e[k])
+        if mode == "bf16":
+            # |dx_in| + sum |W| |dl| bounds the FP32 accumulation error
+            ax = np.abs(oracle.widen(inp["x"]))
+            mx, _, _ = oracle.rglru_gate_proj_bwd(ax, np.abs(oracle.widen(prm["w_x"])),
+                                                  np.abs(oracle.widen(dl_x)), np.abs(oracle.widen(dx_in)))
+            mag, _, _ = oracle.rglru_gate_proj_bwd(ax, np.abs(oracle.widen(prm["w_a"])),
+                                                   np.abs(oracle.widen(dl_a)), mx)
+            _check_bf16_output("dx", p["dx"], dx, mag)
+            del ax, mx, mag
+        del inp, prm, lx, la, y, hf, g, p, rf, rg, dx
 
 
 def test_projection_in_place_and_deterministic():

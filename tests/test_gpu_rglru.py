@@ -98,16 +98,22 @@ def test_rglru_bitwise_deterministic():
 
 def test_rglru_packed_full_size_parity():
     """The packed-sequence workload at full size: B=4, L=8192, D=2560,
-    segment starts with p = 1/512, nonzero initial state."""
+    segment starts with p = 1/512, nonzero initial state; both output modes."""
     name = "packed_b4_l8192_d2560"
     inp = inputs.rglru_inputs(4, 8192, 2560, 4000, reset_p=1.0 / 512, h0_std=0.1)
-    _check(name, inp, 16, 0, bf16=False)
+    _check(name, inp, 16, 0)
 
 
-# The pages' other full-size RG-LRU workloads (no segment starts): the long
-# sequence at D=1024 and the widest state at L=32768 with an initial state.
+# The pages' other full-size RG-LRU workloads (no segment starts): long
+# sequences at D=1024 with a zero initial state, and every width at L=32768
+# with an initial state and its gradient; both output modes.
 FULL_CASES = [
+    ("long_b1_l32768_d1024", 1, 32768, 1024, None, 2100),
+    ("long_b1_l65536_d1024", 1, 65536, 1024, None, 2101),
     ("long_b1_l131072_d1024", 1, 131072, 1024, None, 2102),
+    ("wide_b1_l32768_d1024", 1, 32768, 1024, 0.1, 3100),
+    ("wide_b1_l32768_d1536", 1, 32768, 1536, 0.1, 3101),
+    ("wide_b1_l32768_d2048", 1, 32768, 2048, 0.1, 3102),
     ("wide_b1_l32768_d2560", 1, 32768, 2560, 0.1, 3103),
 ]
 
@@ -116,7 +122,50 @@ FULL_CASES = [
 def test_rglru_full_size_parity(case):
     name, B, L, D, std, seed = case
     inp = inputs.rglru_inputs(B, L, D, seed, h0_std=std)
-    _check(name, inp, 16, 0, bf16=False)
+    _check(name, inp, 16, 0)
+
+
+def test_rglru_k32_metric_shape_parity():
+    """K=32 chunks (the other chunk length the library offers) at the
+    metric shape B=1, L=32768, D=2048, with the grouping the library picks."""
+    inp = inputs.rglru_inputs(1, 32768, 2048, 3202, h0_std=0.1)
+    _check("k32_b1_l32768_d2048", inp, 32, 0)
+
+
+def test_rglru_sqrt_derivative_cap():
+    """Channels whose softplus(alpha) is ~1e-9 keep 1 - a_t^2 below 2.5e-7 at
+    every token, so the backward takes the capped square-root derivative
+    (-a / sqrt(max(1 - a^2, 2.5e-7))) everywhere in them; there it dominates
+    d alpha by three orders of magnitude.  Compared with the oracle:
+      * d alpha of the capped channels at rel 1e-4 each, and every gradient
+        of the other channels at the usual tolerances;
+      * y and h_final of the capped channels to an absolute bound: there
+        sqrt(1 - a^2) ~ 1e-4 is set by a_t's FP32 rounding (a_t sits within
+        a few FP32 ulps of 1), so those channels carry about 1e-4 x |x| per
+        token of rounding, not a 1e-5 relative error."""
+    B, L, D = 2, 700, 64
+    inp = inputs.rglru_inputs(B, L, D, 9312, reset_p=1.0 / 64, h0_std=0.1, dh_final_std=0.1)
+    capped = np.arange(D) % 16 == 5
+    inp["alpha"][capped] = np.float32(-20.0)       # softplus = 2.1e-9
+    say(f"[rglru parity] sqrt cap: B={B} L={L} D={D}, {int(capped.sum())} capped channels")
+    rf, rg = _oracle(inp)
+    y, hf, g = _gpu(inp, 16, 4, torch.float32)
+    free = ~capped
+    e = {"y": rel_l2(to_f64(y)[..., free], rf["y"][..., free]),
+         "h_final": rel_l2(to_f64(hf)[..., free], rf["h_final"][..., free])}
+    for k in ("dx", "dlx", "dla", "dh0"):
+        e[k] = rel_l2(to_f64(g[k])[..., free], rg[k][..., free])
+    e["dalpha_free"] = rel_l2(to_f64(g["dalpha"])[free], rg["dalpha"][free])
+    da_g, da_o = to_f64(g["dalpha"])[capped], rg["dalpha"][capped]
+    e["dalpha_capped"] = float(np.max(np.abs(da_g - da_o) / np.abs(da_o)))
+    e["y_capped_abs"] = float(np.max(np.abs(to_f64(y)[..., capped] - rf["y"][..., capped])))
+    say("   errors:", {k: f"{v:.2e}" for k, v in e.items()})
+    assert e["y"] <= TOL_OUT and e["h_final"] <= TOL_OUT
+    for k in ("dx", "dlx", "dla", "dh0", "dalpha_free", "dalpha_capped"):
+        assert e[k] <= TOL_GRAD, (k, e[k])
+    # a cap constant off by 2x would move d alpha of the capped channels by ~2x
+    assert np.all(np.abs(da_o) > 0)
+    assert e["y_capped_abs"] <= 1e-4 * np.sqrt(L) * 4
 
 
 @pytest.mark.parametrize("L", [2048, 16384])

@@ -142,6 +142,9 @@ def test_samu_bitwise_deterministic():
 
 
 def _check_full(name, B, L, D, K, G, state_std, seed):
+    """Full-size F+B in both output modes: FP32 mode against the oracle at
+    1e-5 / 1e-4; BF16 mode (the one the benchmark times) bitwise the RNE of
+    the FP32-mode values and within the BF16 floor + tolerance."""
     inp = _inputs(B, L, D, seed, state_std)
     say(f"[samu parity] {name}: B={B} L={L} D={D} K={K} G={G} seed={seed} -> oracle forward+backward")
     rf, rg = _oracle(inp)
@@ -158,6 +161,20 @@ def _check_full(name, B, L, D, K, G, state_std, seed):
         assert errs[k] <= TOL_OUT, (k, errs[k])
     for k in keys + ["da_phi", "da_r"]:
         assert errs[k] <= TOL_GRAD, (k, errs[k])
+    say(f"[samu parity] {name}: samu_scan_fwd/bwd bf16")
+    yb, zfb, gb = _gpu(inp, K, G, torch.bfloat16)
+    assert torch.equal(yb, y.to(torch.bfloat16))
+    assert torch.equal(gb["dx_sel"], g["dx_sel"].to(torch.bfloat16))
+    assert torch.equal(gb["db"], g["db"].to(torch.bfloat16))
+    assert torch.equal(zfb, zf)
+    for k in keys[2:] + ["da_phi", "da_r"]:
+        assert torch.equal(gb[k], g[k]), k
+    eb = {"y": (rel_l2(to_f64(yb), rf["y"]), bf16_floor(rf["y"]) + TOL_OUT),
+          "dx_sel": (rel_l2(to_f64(gb["dx_sel"]), rg["dx_sel"]), bf16_floor(rg["dx_sel"]) + TOL_GRAD),
+          "db": (rel_l2(to_f64(gb["db"]), rg["db"]), bf16_floor(rg["db"]) + TOL_GRAD)}
+    say("   bf16 errors (bound):", {k: f"{v:.3e} ({b:.3e})" for k, (v, b) in eb.items()})
+    for k, (v, b) in eb.items():
+        assert v <= b, (k, v, b)
 
 
 def test_samu_metric_shape_full_parity():
@@ -224,3 +241,25 @@ def test_samu_hybrid_prefix_parity():
     assert rel_l2(to_f64(zf), rf["z_final"]) <= TOL_OUT
     for k in ("dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta", "dz0"):
         assert rel_l2(to_f64(g[k]), rg[k]) <= TOL_GRAD, k
+
+
+@pytest.mark.parametrize("amp,D", [(-1.5, 256), (4.0, 16), (-4.0, 8)])
+def test_samu_signed_and_large_amplitudes(amp, D):
+    """Negative and large controller amplitudes: with few modes (1/sqrt(M)
+    large) the per-token rotation d_t reaches about 0.5 rad and the decay
+    factor e^{c_t} moves by up to 30%, far from the near-identity controls of
+    the unit-amplitude workloads."""
+    B, L, K = 2, 1100, 32
+    inp = inputs.samu_inputs(B, L, D, 8800 + D, z0_std=0.1, dz_final_std=0.1, amp=amp)
+    say(f"[samu parity] amplitude a_phi=a_r={amp}: B={B} L={L} D={D}")
+    rf, rg = _oracle(inp)
+    y, zf, g = _gpu(inp, K, 4, torch.float32)
+    errs = {"y": rel_l2(to_f64(y), rf["y"]), "z_final": rel_l2(to_f64(zf), rf["z_final"])}
+    for k in ("dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta", "dz0"):
+        errs[k] = rel_l2(to_f64(g[k]), rg[k])
+    for k in ("da_phi", "da_r"):
+        errs[k] = abs(float(g[k].item()) - rg[k]) / max(abs(rg[k]), 1e-30)
+    say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["y"] <= TOL_OUT and errs["z_final"] <= TOL_OUT
+    for k in ("dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta", "dz0", "da_phi", "da_r"):
+        assert errs[k] <= TOL_GRAD, (k, errs[k])
