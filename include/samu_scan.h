@@ -152,6 +152,26 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G,
                           float* dnu, float* dtheta,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as samu_scan_fwd, with the same arguments except the workspace,
+ * which this call takes from a static device array of
+ * SAMU_SCAN_NOALLOC_SCRATCH_BYTES bytes that each device holds until the
+ * process ends.  The call allocates nothing.  A shape whose forward workspace
+ * (samu_scan_workspace_bytes(..., 0)) exceeds that size returns
+ * SCAN_ERR_WORKSPACE before anything is enqueued.  All calls on one device
+ * share its array: calls that overlap in time on one device (on two streams
+ * or from two threads) race on it and must be serialized by the caller.
+ * The caller still provides y, z_final and the saved record. */
+#define SAMU_SCAN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+scan_status samu_scan_fwd_noalloc(int B, int L, int D, int K, int G,
+                                  const void* x_sel, const void* b,
+                                  const float* w_phi, const float* w_r,
+                                  const float* a_phi, const float* a_r,
+                                  const float* nu, const float* theta, const float* z0,
+                                  void* y, int y_dtype, float* z_final, void* saved,
+                                  void* stream);
+
 /* One generation step for B sequences in a single launch (page "Griffin 第
  * 4、5 节 H800 对照协议", "SAMU 的固定方程": control projection, transition
  * rebuild, FP32 state update and BF16 output in one kernel; equations of

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsamu_scan.so")
 ARCH = "gfx950"
 
-SOURCES = ["capi.cpp", "prefix.hip", "samu_fwd.hip", "samu_bwd.hip", "samu_decode.hip", "rglru.hip", "baseline.hip", "gate_proj.hip"]
+SOURCES = ["capi.cpp", "prefix.hip", "samu_fwd.hip", "samu_bwd.hip", "samu_decode.hip", "rglru.hip", "baseline.hip", "gate_proj.hip", "noalloc.hip"]
 
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -21,6 +21,8 @@ static scan_status fail(scan_status st, const std::string& msg) {
     return st;
 }
 
+scan_status set_last_error(scan_status st, const char* msg) { return fail(st, msg); }
+
 // ----------------------------------------------------------- profiler ---
 namespace {
 struct ProfRecord {

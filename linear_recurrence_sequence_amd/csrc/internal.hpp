@@ -41,6 +41,8 @@ enum KernelId {
 };
 
 const char* kernel_name(int id);
+// sets the thread-local text scan_last_error() returns; returns st
+int set_last_error(int st, const char* msg);
 bool profiler_enabled();
 void profiler_before(int id, hipStream_t s);
 void profiler_after(int id, hipStream_t s);

@@ -51,6 +51,8 @@ def lib():
     L.samu_scan_fwd.restype = i
     L.samu_scan_bwd.argtypes = [i] * 5 + [vp] * 8 + [vp, vp, vp, vp, vp, i, vp] + [vp] * 6 + [vp, sz, vp]
     L.samu_scan_bwd.restype = i
+    L.samu_scan_fwd_noalloc.argtypes = [i] * 5 + [vp] * 9 + [vp, i, vp, vp, vp]
+    L.samu_scan_fwd_noalloc.restype = i
     for n in ("samu_scan_baseline_workspace_bytes", "rglru_scan_baseline_workspace_bytes"):
         getattr(L, n).argtypes = [i, i, i, i]
         getattr(L, n).restype = sz

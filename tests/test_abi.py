@@ -230,3 +230,17 @@ def test_gate_projection_rejects_before_enqueue():
     assert L.rglru_gate_proj_bwd(1, 8, 256, *bw, 0, f(0x600000), f(0x600010), *outs, f(0x800000), ws, None) == -6
     assert L.rglru_gate_proj_bwd(1, 8, 256, *bw, 0, f(0x600000), f(0x400000), *outs, f(0x800000), ws, None) == -6
 
+
+@fake_pointers
+def test_noalloc_forward_rejects_before_enqueue():
+    from linear_recurrence_sequence_amd import scan
+    L = scan.lib()
+    f = _fake
+    p = [f(0x100000), f(0x200000), f(0x300000), f(0x300100), f(0x300200), f(0x300210), f(0x300300),
+         f(0x300400)]
+    # a forward workspace above the 32 MiB static scratch
+    assert L.samu_scan_fwd_noalloc(4, 131072, 2048, 32, 0, *p, None, f(0x400000), 0, None, f(0x500000),
+                                   None) == -4
+    assert b"static scratch" in L.scan_last_error()
+    # an unsupported shape is named by the forward's own check
+    assert L.samu_scan_fwd_noalloc(1, 64, 12, 32, 0, *p, None, f(0x400000), 0, None, f(0x500000), None) == -2
