@@ -49,12 +49,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def effective_groups(L, K, G, min_group=8):
-    """Chunks per group the library uses for G (0 = its choice by shape:
-    serial up to 128 chunks, else about 128 groups of >= min_group chunks)."""
+def effective_groups(L, K, G, min_group=8, samu=None):
+    """Chunks per group the library uses for G (0 = its choice: SAMU groups
+    of 8 chunks, one workgroup each; RG-LRU serial up to 128 chunks, else
+    about 128 groups of >= min_group chunks)."""
     C = -(-L // K)
+    if samu is None:
+        samu = min_group == 8
     if G == 0:
-        G = C if C <= 128 else max(min_group, -(-C // 128))
+        if samu:
+            G = 8
+        else:
+            G = C if C <= 128 else max(min_group, -(-C // 128))
     return min(G, C)
 
 
@@ -102,13 +108,33 @@ def samu_kernel_bytes(B, L, D, K, G):
         "samu_bwd_replay": (8 * BCM + 8 * BCM + 2 * BLD + 2 * BLD + 2 * BLD + 8 * B * n_tiles * L + 8 * BCM,
                             2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BMID + 8 * BCM + 2 * BLD
                             + 8 * B * n_tiles * L + 8 * BCM),
+    }
+    if effective_groups(L, K, G) <= 16:
+        # the grouped path: the summary kernels also write U_g per group and
+        # mode, the replays read the group's summaries and the state entering
+        # the group instead of per-chunk entry states or carries, and the
+        # forward replay writes the entry states the backward reads
+        NGM = B * NG * M
+        tab.update({
+            "samu_chunk_summary": (tab["samu_chunk_summary"][0],
+                                   2 * BLD + 16 * BL + 32 * M + 8 * BCM + 16 * BC + 16 * NGM),
+            "samu_reverse_summary": (tab["samu_reverse_summary"][0],
+                                     2 * BLD + 16 * BL + 32 * M + 8 * BCM + 16 * BC + 16 * NGM),
+            "samu_replay": (tab["samu_replay"][0],
+                            2 * BLD + 16 * BL + 32 * M + 8 * BCM + 16 * BC + 8 * NGM + 2 * BLD + 8 * B * M
+                            + 8 * BMID + 8 * BCM),
+            "samu_bwd_replay": (tab["samu_bwd_replay"][0],
+                                2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BMID + 8 * BCM + 16 * BC
+                                + 8 * NGM + 2 * BLD + 8 * B * n_tiles * L + 8 * BCM),
+        })
+    tab.update({
         # x_sel, p, r, per-tile partials -> dx_sel, per-block direction partials
         "samu_controller_bwd": (2 * BLD + 8 * BL + 8 * B * n_tiles * L + 2 * BLD + 8 * n_blk * (D + 1),
                                 2 * BLD + 16 * BL + 8 * B * n_tiles * L + 2 * BLD + 8 * n_blk * (D + 4)),
         # block and chunk partials -> dw_phi, dw_r, da, dnu, dtheta
         "samu_params": (8 * n_blk * (D + 1) + 8 * BCM + 8 * (D + 1) + 8 * (D + 1) + 8 * M,
                         8 * n_blk * (D + 4) + 8 * BCM + 8 * (D + 1) + 16 + 8 * (D + 1) + 8 + 8 * M),
-    }
+    })
     return tab
 
 

@@ -103,11 +103,12 @@ struct Carver {
 //     min_group chunks long (8 for the complex scan, 16 for the real one).
 static constexpr int64_t kSerialMaxChunks = 128;
 static constexpr int64_t kTargetGroups = 128;
-static bool chunking(int B, int L, int K, int G, int min_group, Chunking* ch) {
+static bool chunking(int B, int L, int K, int G, int min_group, Chunking* ch, int default_group = 0) {
     if (B < 1 || L < 1 || B > 65535 || (K != 16 && K != 32) || G < 0) return false;
     const int64_t C = ceil_div(L, K);
     if (C > 65535 || (int64_t)B * L > 0x7fffffff) return false;
     int64_t g = G;
+    if (g == 0 && default_group > 0) g = default_group;
     if (g == 0) g = C <= kSerialMaxChunks ? C : std::max<int64_t>(min_group, ceil_div(C, kTargetGroups));
     ch->B = B;
     ch->L = L;
@@ -120,6 +121,11 @@ static bool chunking(int B, int L, int K, int G, int min_group, Chunking* ch) {
 
 static constexpr int kSamuMinGroup = 8;      // see chunking()
 static constexpr int kRglruMinGroup = 16;
+// SAMU with G == 0: groups of kSamuGroup chunks on the grouped path (one
+// workgroup per group; see launch_samu_gsummary), which any G up to
+// SAMU_GROUP_MAX takes; longer groups take the three-kernel prefix.
+static constexpr int kSamuGroup = 8;
+static bool samu_fused(const Chunking& ch) { return ch.G <= SAMU_GROUP_MAX; }
 
 struct SamuSaved {
     float *p, *r, *u, *ctl, *mtab, *inv_norm, *entries, *mid;
@@ -166,7 +172,7 @@ static SamuBwdWs samu_bwd_ws_layout(void* base, const Chunking& ch, int D, int M
     w.rsumm = cv.take<float>(BCM * 2);
     w.rchunk = cv.take<float>((size_t)ch.B * ch.C * 4);
     w.rgsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
-    w.carry = cv.take<float>(BCM * 2);
+    w.carry = samu_fused(ch) ? nullptr : cv.take<float>(BCM * 2);  // the grouped path forms carries in LDS
     w.tok_part = cv.take<float>((size_t)ch.B * w.n_tiles * ch.L * 2);
     w.mode_part = cv.take<float>(BCM * 2);
     w.g_part = cv.take<float>((size_t)w.n_blk * samu_param_columns(D) * 2);
@@ -253,7 +259,7 @@ static scan_status device_status(hipError_t e, const char* where) {
 
 static bool samu_shape(int B, int L, int D, int K, int G, Chunking* ch) {
     if (D < 8 || D % 8 != 0) return false;
-    return chunking(B, L, K, G, kSamuMinGroup, ch);
+    return chunking(B, L, K, G, kSamuMinGroup, ch, kSamuGroup);
 }
 
 static bool rglru_shape(int B, int L, int D, int K, int G, Chunking* ch) {
@@ -339,6 +345,22 @@ scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuSaved sv = samu_saved_layout(saved, ch, M, nullptr);
     SamuFwdWs ws = samu_fwd_ws_layout(workspace, ch, M, nullptr);
     LRS_TRY(launch_samu_controller(p, ch, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, sv.inv_norm, s), "samu controller");
+    if (samu_fused(ch)) {
+        // summaries with U_g composed per group, the scan over groups (when
+        // there is more than one), and the replay forming its chunk entries
+        LRS_TRY(launch_samu_gsummary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, ws.chunk, ws.gsum, s),
+                "samu chunk summary");
+        const float* gstate = z0;
+        if (ch.NG > 1) {
+            float* gentry = ws.gsum + (size_t)ch.B * ch.NG * M * 4;
+            LRS_TRY(launch_group_scan(2, ch, M, ws.gsum, z0, gentry, s), "samu group scan");
+            gstate = gentry;
+        }
+        LRS_TRY(launch_samu_greplay(p, ch, sv.ctl, sv.mtab, ws.summ, ws.chunk, gstate, sv.entries, sv.mid, y,
+                                    y_dtype == SCAN_F32, z_final, s),
+                "samu replay");
+        return SCAN_OK;
+    }
     LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, ws.chunk, s), "samu chunk summary");
     LRS_TRY(launch_prefix(2, false, ch, M, PrefixSummaries{nullptr, ws.summ, ws.chunk, sv.mtab}, ws.gsum, z0,
                           sv.entries, s),
@@ -392,14 +414,28 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuSaved sv = samu_saved_layout(const_cast<void*>(saved), ch, M, nullptr);
     SamuBwdWs ws = samu_bwd_ws_layout(workspace, ch, D, M, nullptr);
     const int f32 = grad_dtype == SCAN_F32;
-    LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, ws.rchunk, s),
-            "samu reverse summary");
-    LRS_TRY(launch_prefix(2, true, ch, M, PrefixSummaries{nullptr, ws.rsumm, ws.rchunk, sv.mtab}, ws.rgsum,
-                          dz_final, ws.carry, s),
-            "samu reverse prefix");
-    LRS_TRY(launch_samu_bwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, ws.carry, dy, db, f32, dz0,
-                                   ws.tok_part, ws.n_tiles, ws.mode_part, s),
-            "samu backward replay");
+    if (samu_fused(ch)) {
+        LRS_TRY(launch_samu_gsummary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, ws.rchunk, ws.rgsum, s),
+                "samu reverse summary");
+        const float* gcarry = dz_final;
+        if (ch.NG > 1) {
+            float* gentry = ws.rgsum + (size_t)ch.B * ch.NG * M * 4;
+            LRS_TRY(launch_group_scan(2, ch, M, ws.rgsum, dz_final, gentry, s), "samu reverse group scan");
+            gcarry = gentry;
+        }
+        LRS_TRY(launch_samu_gbwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, ws.rsumm, ws.rchunk, gcarry, dy,
+                                        db, f32, dz0, ws.tok_part, ws.n_tiles, ws.mode_part, s),
+                "samu backward replay");
+    } else {
+        LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, ws.rchunk, s),
+                "samu reverse summary");
+        LRS_TRY(launch_prefix(2, true, ch, M, PrefixSummaries{nullptr, ws.rsumm, ws.rchunk, sv.mtab}, ws.rgsum,
+                              dz_final, ws.carry, s),
+                "samu reverse prefix");
+        LRS_TRY(launch_samu_bwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, ws.carry, dy, db, f32, dz0,
+                                       ws.tok_part, ws.n_tiles, ws.mode_part, s),
+                "samu backward replay");
+    }
     LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, sv.u, sv.inv_norm, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part, s),
             "samu controller backward");
     LRS_TRY(launch_samu_params(p, ch, reinterpret_cast<const double*>(sv.inv_norm + 4), ws.g_part, ws.n_blk,

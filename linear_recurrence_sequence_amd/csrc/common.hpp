@@ -150,6 +150,28 @@ __device__ __forceinline__ cf mode_lambda(const ModeConst& k, float E, float C, 
     return {rho * rr, rho * ri};
 }
 
+// Transition product of a whole chunk for one mode, from the chunk's record
+// (G_c, cos D_c, sin D_c) and the mode's chunk phasor e^{i n theta} (n = K,
+// or K_last for the last chunk) kept as (ch, sh, cl, sl):
+//   A = 2^(kappa G_c) e^{i n theta} e^{i D_c};
+// the adjoint scan uses its conjugate (REV).
+template <bool REV>
+__device__ __forceinline__ cf chunk_transition(float kappa, float4 ph, float4 rec) {
+    const float re = fmaf(ph.x, rec.y, -ph.y * rec.z) + fmaf(ph.z, rec.y, -ph.w * rec.z);
+    const float im = fmaf(ph.x, rec.z, ph.y * rec.y) + fmaf(ph.z, rec.z, ph.w * rec.y);
+    const float rho = __builtin_amdgcn_exp2f(kappa * rec.x);
+    return {rho * re, REV ? -rho * im : rho * im};
+}
+
+// Orders LDS traffic among the lanes of one wave (a region no other wave
+// touches): the wave's LDS instructions execute in program order, so only
+// the compiler has to be kept from moving accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // A wave-uniform value the optimizer cannot see through.  Guarding each token
 // step of a serial recurrence with `i < opaque(n)` costs one scalar compare and
 // branch, and puts every step in its own basic block, so instruction

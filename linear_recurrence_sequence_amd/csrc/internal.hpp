@@ -84,6 +84,12 @@ struct PrefixSummaries {
 hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const PrefixSummaries& sm,
                          float* gsum, const float* init, float* entries, hipStream_t s);
 
+// The scan over group summaries alone (the middle launch of launch_prefix):
+// gsum [B, NG, W] U_g (ELEM-complex affine maps) -> gentry [B, NG, W], the
+// state entering each group (processing order).
+hipError_t launch_group_scan(int elem, const Chunking& ch, int W, const float* gsum, const float* init,
+                             float* gentry, hipStream_t s);
+
 // ---------------------------------------------------------------- SAMU ---
 struct SamuParams {
     int B, L, D, M;
@@ -120,6 +126,30 @@ hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const fl
 hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
                               const float* mtab, const float* entries, float* mid, void* y, int y_f32,
                               float* z_final, hipStream_t s);
+// Grouped path without the compose and expand launches: a workgroup owns one
+// group of ch.G <= SAMU_GROUP_MAX consecutive chunks (processing order) and
+// 64 modes, one wave per chunk.
+//   gsummary: compressed summaries as launch_samu_summary, plus U_g of every
+//             group composed in LDS -> gsum [B, NG, M] (A, B) complex pairs;
+//   greplay:  entry state of every chunk from the state entering its group
+//             (gstate [B, NG, M] complex, or with one group the initial
+//             state [B, M] / NULL) and the group's earlier summaries, in
+//             LDS; then the replay, which also writes the entry states
+//             [B, C, M] the backward reads;
+//   gbwd_replay: the same for the adjoint (groups aligned from the last
+//             chunk), carries formed in LDS, then the backward replay.
+constexpr int SAMU_GROUP_MAX = 16;
+hipError_t launch_samu_gsummary(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                                const void* drive, bool reverse, float* summ, float* chunk_rec, float* gsum,
+                                hipStream_t s);
+hipError_t launch_samu_greplay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                               const float* summ, const float* chunk_rec, const float* gstate, float* entries,
+                               float* mid, void* y, int y_f32, float* z_final, hipStream_t s);
+hipError_t launch_samu_gbwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                                   const float* entries, const float* mid, const float* rsumm,
+                                   const float* rchunk, const float* gcarry, const void* dy, void* db,
+                                   int db_f32, float* dz0, float* tok_part, int n_tiles, float* mode_part,
+                                   hipStream_t s);
 // carry_in: [B, C, M] cotangent arriving after each chunk's last token;
 // mode_part: [B, C, M] per-chunk (d nu, d theta) partials
 hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl,

@@ -113,13 +113,8 @@ struct CompressedSummaries {
     }
     __device__ Aff<2> operator()(int b, int c, int w) const {
         const float2 bb = reinterpret_cast<const float2*>(bpart)[((size_t)b * C + c) * W + w];
-        const float4 g = chunk[(size_t)b * C + c];
-        const float4 ph = c == C - 1 ? ph_last : ph_full;  // (ch, sh, cl, sl)
-        const float re = fmaf(ph.x, g.y, -ph.y * g.z) + fmaf(ph.z, g.y, -ph.w * g.z);
-        const float im = fmaf(ph.x, g.z, ph.y * g.y) + fmaf(ph.z, g.z, ph.w * g.y);
-        const float rho = __builtin_amdgcn_exp2f(kappa * g.x);
         Aff<2> f;
-        f.a = {rho * re, REV ? -rho * im : rho * im};
+        f.a = chunk_transition<REV>(kappa, c == C - 1 ? ph_last : ph_full, chunk[(size_t)b * C + c]);
         f.b = {bb.x, bb.y};
         return f;
     }
@@ -231,6 +226,21 @@ void run_prefix(const Chunking& ch, int W, Sum sm, float* gsum, const float* ini
 }
 
 }  // namespace
+
+hipError_t launch_group_scan(int elem, const Chunking& ch, int W, const float* gsum, const float* init,
+                             float* gentry, hipStream_t s) {
+    int slots = 1;
+    while (slots < ch.NG && slots < SCAN_THREADS / 8) slots <<= 1;
+    const int MT = SCAN_THREADS / slots;
+    const dim3 sgrid((unsigned)ceil_div(W, MT), ch.B);
+    if (elem == 2)
+        LRS_LAUNCH(K_PREFIX_OUTER, (prefix_group_scan_kernel<2>), sgrid, dim3(SCAN_THREADS), 0, s, ch.NG, W, MT,
+                   gsum, init, gentry);
+    else
+        LRS_LAUNCH(K_PREFIX_OUTER, (prefix_group_scan_kernel<1>), sgrid, dim3(SCAN_THREADS), 0, s, ch.NG, W, MT,
+                   gsum, init, gentry);
+    return hipGetLastError();
+}
 
 hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const PrefixSummaries& sm,
                          float* gsum, const float* init, float* entries, hipStream_t s) {

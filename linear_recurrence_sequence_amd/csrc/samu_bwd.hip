@@ -41,79 +41,96 @@ constexpr int BWD_THREADS = 256;
 #define LRS_BWD_WAVES 3  // waves per SIMD the register budget is sized for
 #endif
 
-// One chunk of the backward replay; FULL = the chunk has all K tokens (only
-// the last chunk of a sequence may not), which keeps the common path free of
-// per-token branches so its loads are issued as one batch.
-template <int K, int H, bool F32, bool FULL>
-__device__ __forceinline__ void bwd_chunk(
-    float (*lds)[64 * (2 * H + 1)], TokenCtl* sctl, const ModeConst& k, bool active, int lane, int wave,
-    int tile, int n_tiles, int L, int M, int C, int b, int c, int mm, const TokenCtl* __restrict__ ctl,
-    const uint32_t* __restrict__ drive, const float2* __restrict__ entries, const float2* __restrict__ mid,
-    const uint32_t* __restrict__ dy, void* __restrict__ db, float* __restrict__ tok_part, cf& carry,
-    float& acc_nu, float& acc_th) {
+// Requests of one chunk of the backward replay, in the order it consumes
+// them: the states entering each sub-chunk (the chunk's saved entry state and
+// the mid states the forward replay kept; those of sub-chunks past a partial
+// chunk's end are never used), the last sub-chunk's drive words forward in
+// time, then its cotangent words backward.  The cotangent words of the earlier
+// sub-chunks are requested when their sub-chunk starts: holding them through
+// the last sub-chunk would take the kernel past 128 VGPRs, i.e. from 4 to 3
+// waves per SIMD, which costs more than the latency the early request hides.
+// Past a partial chunk's end (token i >= kc) a load is skipped (CLAMP false:
+// the word reads as zero) or re-reads token kc - 1 (CLAMP true: no branch;
+// the word is never used).
+template <int K, int H, bool FULL, bool CLAMP>
+__device__ __forceinline__ void bwd_issue(cf (&ck)[K / H], uint32_t (&bw)[K], uint32_t (&gw)[K], int kc,
+                                          size_t row0, int M, int mm, size_t bc,
+                                          const float2* __restrict__ entries, const float2* __restrict__ mid,
+                                          const uint32_t* __restrict__ drive, const uint32_t* __restrict__ dy) {
     constexpr int NH = K / H;
-    static_assert(NH == 1 || (H == SAMU_BWD_SUB && NH - 1 == samu_mid_states(K)),
-                  "sub-chunks must match the forward's mid states");
-    constexpr int NV = 2 * H;
-    constexpr int PAD = NV + 1;
-    const int s = c * K;
-    const int kc = FULL ? K : min(K, L - s);
-    const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform; the lane adds mm
-    float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
-    if ((int)threadIdx.x < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + threadIdx.x];
-    // states entering each sub-chunk: the chunk's entry state and the mid
-    // states the forward replay kept (those of sub-chunks past a partial
-    // chunk's end are never used)
-    cf ck[NH];
     {
-        const float2 e0 = entries[((size_t)b * C + c) * M + mm];
+        const float2 e0 = entries[bc * M + mm];
         ck[0] = {e0.x, e0.y};
 #pragma unroll
         for (int h = 1; h < NH; ++h) {
-            const float2 v = mid[(((size_t)b * C + c) * (NH - 1) + h - 1) * M + mm];
+            const float2 v = mid[(bc * (NH - 1) + h - 1) * M + mm];
             ck[h] = {v.x, v.y};
         }
     }
-    uint32_t bw[K], gw[K];
-    // requested in the order they are consumed: the last sub-chunk first,
-    // its drive words forward in time, then its cotangent words backward.
-    // The cotangent words of the earlier sub-chunks are requested when their
-    // sub-chunk starts: holding them through the last sub-chunk would take
-    // the kernel past 128 VGPRs, i.e. from 4 to 3 waves per SIMD, which
-    // costs more than the latency the early request hides.
 #pragma unroll
     for (int h = NH - 1; h >= 0; --h) {
 #pragma unroll
         for (int j = 0; j < H; ++j) {
             const int i = h * H + j;
-            bw[i] = (FULL || i < kc) ? (drive + row0 + (size_t)i * M)[mm] : 0u;
+            if (FULL || CLAMP) bw[i] = (drive + row0 + (size_t)(FULL ? i : min(i, kc - 1)) * M)[mm];
+            else bw[i] = i < kc ? (drive + row0 + (size_t)i * M)[mm] : 0u;
         }
         if (h != NH - 1) continue;  // earlier sub-chunks: requested when they start
 #pragma unroll
         for (int j = H - 1; j >= 0; --j) {
             const int i = h * H + j;
-            gw[i] = (FULL || i < kc) ? (dy + row0 + (size_t)i * M)[mm] : 0u;
+            if (FULL || CLAMP) gw[i] = (dy + row0 + (size_t)(FULL ? i : min(i, kc - 1)) * M)[mm];
+            else gw[i] = i < kc ? (dy + row0 + (size_t)i * M)[mm] : 0u;
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
-    __syncthreads();
+}
+
+// The adjoint over one chunk, sub-chunk by sub-chunk, last one first, from
+// the cotangent `carry` arriving after the chunk's last token; `sctl` holds
+// the chunk's token controls.  FULL = the chunk has all K tokens (only the
+// last chunk of a sequence may not), which keeps the common path free of
+// per-token branches.  The per-token partial sums of a wave are reduced
+// through its own padded LDS rows `lds_w` (conflict-free both ways); WSYNC
+// orders that traffic with wave-local fences (every wave of the workgroup
+// on its own chunk) instead of workgroup barriers.  CLAMP: one copy of the
+// code for full and partial chunks alike -- loads past a partial chunk's end
+// re-read its last token and every use is guarded by the token count.
+// STASH: the first sub-chunk's state is read from ck0_lds, so ck[0] need not
+// stay in a register through the later sub-chunks.
+template <int K, int H, bool F32, bool FULL, bool WSYNC, bool CLAMP = false, bool STASH = false>
+__device__ __forceinline__ void bwd_body(float* lds_w, const TokenCtl* sctl, const ModeConst& k, bool active,
+                                         int lane, int tile, int n_tiles, int L, int M, int b, int s, int kc,
+                                         size_t row0, int mm, const uint32_t* __restrict__ dy, void* __restrict__ db,
+                                         float* __restrict__ tok_part, const cf (&ck)[K / H], const uint32_t (&bw)[K],
+                                         uint32_t (&gw)[K], cf& carry, float& acc_nu, float& acc_th,
+                                         const float2* ck0_lds = nullptr) {
+    constexpr int NH = K / H;
+    static_assert(NH == 1 || (H == SAMU_BWD_SUB && NH - 1 == samu_mid_states(K)),
+                  "sub-chunks must match the forward's mid states");
+    constexpr int NV = 2 * H;
+    constexpr int PAD = NV + 1;
     const int kq = opaque(kc);
-    float* row = &lds[wave][lane * PAD];
+    float* row = &lds_w[lane * PAD];
 #pragma unroll
     for (int h = NH - 1; h >= 0; --h) {
         const int i0 = h * H;
-        if (!FULL && i0 >= kc) continue;  // uniform over the workgroup
+        if (!FULL && i0 >= kc) continue;  // uniform over the wave (and, unless WSYNC, the workgroup)
         if (h != NH - 1) {
 #pragma unroll
             for (int j = H - 1; j >= 0; --j) {
                 const int i = i0 + j;
-                gw[i] = (FULL || i < kc) ? (dy + row0 + (size_t)i * M)[mm] : 0u;
+                if (CLAMP) gw[i] = (dy + row0 + (size_t)min(i, kc - 1) * M)[mm];
+                else gw[i] = (FULL || i < kc) ? (dy + row0 + (size_t)i * M)[mm] : 0u;
             }
         }
         cf lam[H], wz[H];
         {
             cf z = ck[h];
+            if (STASH && h == 0) {  // the entry state, kept in LDS meanwhile
+                const float2 e0 = *ck0_lds;
+                z = {e0.x, e0.y};
+            }
 #pragma unroll
             for (int j = 0; j < H; ++j) {
                 if (i0 + j < kq) {
@@ -148,12 +165,12 @@ __device__ __forceinline__ void bwd_chunk(
             row[2 * j] = pr;
             row[2 * j + 1] = pi;
         }
-        __syncthreads();
+        if (WSYNC) wave_lds_sync(); else __syncthreads();
         // column col (token col/2, component col%2) summed over the wave's
         // 64 modes: 64/NV lanes per column, NV rows each, then a butterfly
         {
             const int col = lane % NV, grp = lane / NV;
-            const float* src = &lds[wave][grp * NV * PAD + col];
+            const float* src = &lds_w[grp * NV * PAD + col];
             float acc = 0.f;
 #pragma unroll
             for (int r = 0; r < NV; ++r) acc += src[r * PAD];
@@ -165,8 +182,31 @@ __device__ __forceinline__ void bwd_chunk(
                 tok_part[(((size_t)b * n_tiles + tile) * L + s + i0) * 2 + col] = acc;
             }
         }
-        __syncthreads();
+        if (WSYNC) wave_lds_sync(); else __syncthreads();
     }
+}
+
+// One chunk of the backward replay, one workgroup per (chunk, 256 modes).
+template <int K, int H, bool F32, bool FULL>
+__device__ __forceinline__ void bwd_chunk(
+    float (*lds)[64 * (2 * H + 1)], TokenCtl* sctl, const ModeConst& k, bool active, int lane, int wave,
+    int tile, int n_tiles, int L, int M, int C, int b, int c, int mm, const TokenCtl* __restrict__ ctl,
+    const uint32_t* __restrict__ drive, const float2* __restrict__ entries, const float2* __restrict__ mid,
+    const uint32_t* __restrict__ dy, void* __restrict__ db, float* __restrict__ tok_part, cf& carry,
+    float& acc_nu, float& acc_th) {
+    constexpr int NH = K / H;
+    const int s = c * K;
+    const int kc = FULL ? K : min(K, L - s);
+    const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform; the lane adds mm
+    float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
+    if ((int)threadIdx.x < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + threadIdx.x];
+    cf ck[NH];
+    uint32_t bw[K], gw[K];
+    bwd_issue<K, H, FULL, false>(ck, bw, gw, kc, row0, M, mm, (size_t)b * C + c, entries, mid, drive, dy);
+    if ((int)threadIdx.x < kc) reinterpret_cast<float4*>(sctl)[threadIdx.x] = tn;
+    __syncthreads();
+    bwd_body<K, H, F32, FULL, false>(lds[wave], sctl, k, active, lane, tile, n_tiles, L, M, b, s, kc, row0, mm, dy,
+                                     db, tok_part, ck, bw, gw, carry, acc_nu, acc_th);
 }
 
 template <int K, int H, bool F32>
@@ -205,6 +245,109 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(LRS
         mode_part[cidx] = make_float2(-acc_nu, acc_th);
         if (dz0 && c == 0) dz0[(size_t)b * M + mm] = make_float2(carry.re, carry.im);
     }
+}
+
+// Grouped backward replay: a workgroup owns one group of G chunks in the
+// adjoint's processing order (chunk C - 1 - (q G + w) for wave w) and 64
+// modes.  Each wave rebuilds its chunk's conjugate reverse summary (the
+// compressed B part and the chunk record the reverse summary kernel wrote)
+// into the group's LDS table; after the workgroup's one barrier, wave w forms
+// the cotangent arriving after its chunk by applying the group's earlier
+// summaries (processing order) to the cotangent entering the group, then runs
+// the adjoint of its chunk with wave-local LDS traffic only.
+constexpr int GB_LANES = 64;
+
+template <int K, int H, bool F32, bool ALLACT>
+__device__ __forceinline__ void gbwd_body(float4* gdyn, int G, int L, int M, int C, int n_tiles, int per_group,
+                                          const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
+                                          const float4* __restrict__ mtab, const float2* __restrict__ entries,
+                                          const float2* __restrict__ mid, const float2* __restrict__ rsumm,
+                                          const float4* __restrict__ rchunk, const float2* __restrict__ gcarry,
+                                          const uint32_t* __restrict__ dy, void* __restrict__ db,
+                                          float2* __restrict__ dz0, float* __restrict__ tok_part,
+                                          float2* __restrict__ mode_part) {
+    constexpr int NH = K / H;
+    constexpr int ROW = 64 * (2 * H + 1);  // floats of one wave's transpose rows
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    // LDS: [G][64] entry states, [G][K] token controls, [G][ROW] transpose
+    // rows; the group's summary table [G][64] float4 overlays the rows (it is
+    // read only before the second barrier, the rows only after it)
+    float2* stash = reinterpret_cast<float2*>(gdyn) + w * GB_LANES + lane;
+    TokenCtl* sctl = reinterpret_cast<TokenCtl*>(reinterpret_cast<float2*>(gdyn) + G * GB_LANES) + w * K;
+    float* rows = reinterpret_cast<float*>(reinterpret_cast<TokenCtl*>(reinterpret_cast<float2*>(gdyn) + G * GB_LANES) +
+                                           G * K);
+    float* lds_w = rows + w * ROW;
+    float4* comp = reinterpret_cast<float4*>(rows);
+    const int q = blockIdx.y, b = blockIdx.z, NG = gridDim.y;
+    const int pc = q * G + w;
+    const bool valid = pc < C;  // wave-uniform
+    const int c = C - 1 - min(pc, C - 1);
+    const int m = blockIdx.x * GB_LANES + lane;
+    const bool active = ALLACT || m < M;
+    const int mm = active ? m : M - 1;
+    const int tile = blockIdx.x;
+    const int s = c * K;
+    const int kc = min(K, L - s);
+    const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform
+    const size_t bc = (size_t)b * C + c;
+
+    // requests: token controls, mode constants, this chunk's reverse summary,
+    // the cotangent entering the group, then the replay's own words
+    float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + lane];
+    const ModeConst k = load_mode(mtab, mm);
+    const float4 ph = mtab[MODE_REC * mm + (c == C - 1 ? 3 : 2)];
+    const float4 rec = rchunk[bc];
+    const float2 bp = rsumm[bc * M + mm];
+    float2 g0 = make_float2(0.f, 0.f);
+    if (gcarry) g0 = per_group ? gcarry[((size_t)b * NG + q) * M + mm] : gcarry[(size_t)b * M + mm];
+    cf ck[NH];
+    uint32_t bw[K], gw[K];
+    bwd_issue<K, H, false, true>(ck, bw, gw, kc, row0, M, mm, bc, entries, mid, drive, dy);
+    if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
+    {
+        const cf a = chunk_transition<true>(k.kappa, ph, rec);
+        comp[w * GB_LANES + lane] = make_float4(a.re, a.im, bp.x, bp.y);
+    }
+    if (NH > 1) *stash = make_float2(ck[0].re, ck[0].im);
+    __syncthreads();
+    // the cotangent arriving after this chunk: the group's earlier summaries
+    // (processing order) applied to the cotangent entering the group
+    cf carry = {g0.x, g0.y};
+    if (valid) {
+        for (int j = 0; j < w; ++j) {
+            const float4 f = comp[j * GB_LANES + lane];
+            carry = cfma({f.x, f.y}, carry, {f.z, f.w});
+        }
+    }
+    __syncthreads();  // the summary table's LDS becomes the transpose rows
+    if (!valid) return;
+    float acc_nu = 0.f, acc_th = 0.f;
+    bwd_body<K, H, F32, false, true, true, (NH > 1)>(lds_w, sctl, k, active, lane, tile, n_tiles, L, M, b, s, kc,
+                                                     row0, mm, dy, db, tok_part, ck, bw, gw, carry, acc_nu, acc_th,
+                                                     stash);
+    if (active) {
+        mode_part[bc * M + m] = make_float2(-acc_nu, acc_th);
+        if (dz0 && c == 0) dz0[(size_t)b * M + m] = make_float2(carry.re, carry.im);
+    }
+}
+
+template <int K, int H, bool F32>
+__global__ __launch_bounds__(GB_LANES * SAMU_GROUP_MAX) __attribute__((amdgpu_waves_per_eu(4, 8))) void
+samu_gbwd_replay_kernel(int L, int M, int C, int G, int n_tiles, int per_group, const TokenCtl* __restrict__ ctl,
+                        const uint32_t* __restrict__ drive, const float4* __restrict__ mtab,
+                        const float2* __restrict__ entries, const float2* __restrict__ mid,
+                        const float2* __restrict__ rsumm, const float4* __restrict__ rchunk,
+                        const float2* __restrict__ gcarry, const uint32_t* __restrict__ dy, void* __restrict__ db,
+                        float2* __restrict__ dz0, float* __restrict__ tok_part, float2* __restrict__ mode_part) {
+    static_assert(K % H == 0 && 64 % (2 * H) == 0, "sub-chunk shape");
+    extern __shared__ float4 gdyn[];
+    if ((int)(blockIdx.x + 1) * GB_LANES <= M)  // uniform over the workgroup
+        gbwd_body<K, H, F32, true>(gdyn, G, L, M, C, n_tiles, per_group, ctl, drive, mtab, entries, mid, rsumm,
+                                   rchunk, gcarry, dy, db, dz0, tok_part, mode_part);
+    else
+        gbwd_body<K, H, F32, false>(gdyn, G, L, M, C, n_tiles, per_group, ctl, drive, mtab, entries, mid, rsumm,
+                                    rchunk, gcarry, dy, db, dz0, tok_part, mode_part);
 }
 
 // -------------------------------------------------- controller backward ---
@@ -596,6 +739,35 @@ hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const
         if (db_f32) BWD_CASE(16, H16, true); else BWD_CASE(16, H16, false);
     }
 #undef BWD_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_samu_gbwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                                   const float* entries, const float* mid, const float* rsumm,
+                                   const float* rchunk, const float* gcarry, const void* dy, void* db,
+                                   int db_f32, float* dz0, float* tok_part, int n_tiles, float* mode_part,
+                                   hipStream_t s) {
+    const dim3 grid((unsigned)ceil_div(p.M, GB_LANES), ch.NG, ch.B);
+    const dim3 block(GB_LANES * ch.G);
+    const int H = ch.K == 32 ? SAMU_BWD_SUB : 16;
+    // entry-state stash, token controls, transpose rows (the summary table
+    // overlays the rows, which are larger)
+    const size_t lds = (size_t)ch.G * GB_LANES * sizeof(float2) + (size_t)ch.G * ch.K * sizeof(TokenCtl) +
+                       (size_t)ch.G * 64 * (2 * H + 1) * sizeof(float);
+    const int per_group = ch.NG > 1;
+#define GBWD_CASE(KK, HH, FF)                                                                               \
+    LRS_LAUNCH(K_SAMU_BWD_REPLAY, (samu_gbwd_replay_kernel<KK, HH, FF>), grid, block, lds, s, p.L, p.M,   \
+               ch.C, ch.G, n_tiles, per_group, (const TokenCtl*)ctl, (const uint32_t*)p.b,               \
+               (const float4*)mtab, (const float2*)entries, (const float2*)mid, (const float2*)rsumm,     \
+               (const float4*)rchunk, (const float2*)gcarry, (const uint32_t*)dy, db, (float2*)dz0,      \
+               tok_part, (float2*)mode_part)
+    constexpr int H32 = SAMU_BWD_SUB, H16 = SAMU_BWD_SUB < 16 ? SAMU_BWD_SUB : 16;
+    if (ch.K == 32) {
+        if (db_f32) GBWD_CASE(32, H32, true); else GBWD_CASE(32, H32, false);
+    } else {
+        if (db_f32) GBWD_CASE(16, H16, true); else GBWD_CASE(16, H16, false);
+    }
+#undef GBWD_CASE
     return hipGetLastError();
 }
 

@@ -421,6 +421,194 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
                                         z_final);
 }
 
+// ------------------------------------------------ grouped (fused) path ---
+// A workgroup owns one group of G consecutive chunks in processing order
+// (forward: chunk q G + w; adjoint: chunk C - 1 - (q G + w)) and 64 modes:
+// wave w handles chunk w of the group, lane l mode 64 blockIdx.x + l.  The
+// group's chunk summaries meet in LDS, so the summary kernel composes U_g
+// there, and the replays form L_c applied to the state entering the group
+// there: neither the compose nor the expand pass of the three-kernel prefix
+// runs, and the per-chunk entry states are never read back from memory.
+// Every wave reaches the workgroup's single barrier, including those past
+// the last chunk; all loads are issued unconditionally before it (a partial
+// last chunk re-reads its last token row instead of branching).
+constexpr int GRP_LANES = 64;
+
+// (A, B) of this wave's chunk for this lane's mode, into the group's LDS
+// table; A from the chunk record and the mode's chunk phasor.
+__device__ __forceinline__ void group_put(float4* comp, int w, int lane, cf A, cf B) {
+    comp[w * GRP_LANES + lane] = make_float4(A.re, A.im, B.re, B.im);
+}
+
+// The drive words of one chunk, clamped into the chunk: token i >= kc
+// re-reads token kc - 1 (its value is never used), so no load is guarded.
+template <int K, bool REV>
+__device__ __forceinline__ void load_chunk_clamped(Words<1> (&w)[K], const uint32_t* __restrict__ rows, int M,
+                                                   int off, int kc) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int i = REV ? K - 1 - j : j;
+        w[i].load(rows + (size_t)min(i, kc - 1) * M, off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int K, bool REV, bool ALLACT>
+__device__ __forceinline__ void gsummary_body(float4* gdyn, int G, int L, int M, int C,
+                                              const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
+                                              const float4* __restrict__ mtab, float* __restrict__ summ,
+                                              float4* __restrict__ chunk_rec, float4* __restrict__ gsum) {
+    float4* comp = gdyn;
+    TokenCtl* sctl = reinterpret_cast<TokenCtl*>(gdyn + G * GRP_LANES);
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int q = blockIdx.y, b = blockIdx.z, NG = gridDim.y;
+    const int pc = q * G + w;
+    const bool valid = pc < C;  // wave-uniform
+    const int pcc = min(pc, C - 1);
+    const int c = REV ? C - 1 - pcc : pcc;
+    const int m = blockIdx.x * GRP_LANES + lane;
+    const bool active = ALLACT || m < M;
+    const int mc = active ? m : M - 1;
+    const int s = c * K;
+    const int kc = min(K, L - s);
+    sctl += w * K;
+
+    float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + lane];
+    ModeConst k[1];
+    k[0] = load_mode(mtab, mc);
+    const float4 ph = mtab[MODE_REC * mc + (c == C - 1 ? 3 : 2)];
+    Words<1> wd[K];
+    load_chunk_clamped<K, REV>(wd, drive + ((size_t)b * L + s) * M, M, mc, kc);
+    if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
+    wave_lds_sync();
+    cf A = {1.f, 0.f}, Bv[1] = {{0.f, 0.f}};
+    if (valid) {
+        // the chunk record: G_c = sum E_t and D_c = sum d_t (the same value
+        // in every lane), once per chunk
+        const float Gc = wave_sum(lane < kc ? tn.x : 0.f);
+        const float Dc = wave_sum(lane < kc ? tn.w : 0.f);
+        float sD, cD;
+        sincosf(Dc, &sD, &cD);
+        const int kq = opaque(kc);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int i = REV ? K - 1 - j : j;
+            if (i < kq) summary_step<1, REV>(k, Bv, sctl[i], wd[i]);
+        }
+        const float4 rec = make_float4(Gc, cD, sD, 0.f);
+        if (active) reinterpret_cast<float2*>(summ)[((size_t)b * C + c) * M + m] = make_float2(Bv[0].re, Bv[0].im);
+        if (blockIdx.x == 0 && lane == 0) chunk_rec[(size_t)b * C + c] = rec;
+        A = chunk_transition<REV>(k[0].kappa, ph, rec);
+    }
+    group_put(comp, w, lane, A, Bv[0]);
+    __syncthreads();
+    if (w == 0 && active) {
+        // U_g = S_{n-1} o ... o S_0 in processing order (the right operand first)
+        const int n = min(G, C - q * G);
+        cf ua = {1.f, 0.f}, ub = {0.f, 0.f};
+        for (int j = 0; j < n; ++j) {
+            const float4 f = comp[j * GRP_LANES + lane];
+            const cf fa = {f.x, f.y}, fb = {f.z, f.w};
+            ub = cfma(fa, ub, fb);
+            ua = cmul(fa, ua);
+        }
+        gsum[((size_t)b * NG + q) * M + m] = make_float4(ua.re, ua.im, ub.re, ub.im);
+    }
+}
+
+template <int K, bool REV>
+__global__ __launch_bounds__(GRP_LANES * SAMU_GROUP_MAX) __attribute__((amdgpu_waves_per_eu(4, 8))) void
+samu_gsummary_kernel(int L, int M, int C, int G, const TokenCtl* __restrict__ ctl,
+                     const uint32_t* __restrict__ drive, const float4* __restrict__ mtab, float* __restrict__ summ,
+                     float4* __restrict__ chunk_rec, float4* __restrict__ gsum) {
+    extern __shared__ float4 gdyn[];
+    if ((int)(blockIdx.x + 1) * GRP_LANES <= M)  // uniform over the workgroup
+        gsummary_body<K, REV, true>(gdyn, G, L, M, C, ctl, drive, mtab, summ, chunk_rec, gsum);
+    else
+        gsummary_body<K, REV, false>(gdyn, G, L, M, C, ctl, drive, mtab, summ, chunk_rec, gsum);
+}
+
+template <int K, bool F32, bool ALLACT>
+__device__ __forceinline__ void greplay_body(float4* gdyn, int G, int L, int M, int C, int per_group,
+                                             const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
+                                             const float4* __restrict__ mtab, const float2* __restrict__ summ,
+                                             const float4* __restrict__ chunk_rec, const float2* __restrict__ gstate,
+                                             float2* __restrict__ entries, float* __restrict__ mid,
+                                             void* __restrict__ y, float* __restrict__ z_final) {
+    constexpr int NMID = samu_mid_states(K);
+    float4* comp = gdyn;
+    TokenCtl* sctl = reinterpret_cast<TokenCtl*>(gdyn + G * GRP_LANES);
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int q = blockIdx.y, b = blockIdx.z, NG = gridDim.y;
+    const int pc = q * G + w;
+    const bool valid = pc < C;  // wave-uniform
+    const int c = min(pc, C - 1);
+    const int m = blockIdx.x * GRP_LANES + lane;
+    const bool active = ALLACT || m < M;
+    const int mc = active ? m : M - 1;
+    const int s = c * K;
+    const int kc = min(K, L - s);
+    const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform
+    sctl += w * K;
+
+    // requests: the token controls, the mode constants, this chunk's
+    // summary, the state entering the group, then the chunk's drive words
+    float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + lane];
+    const ModeConst k = load_mode(mtab, mc);
+    const float4 ph = mtab[MODE_REC * mc + (c == C - 1 ? 3 : 2)];
+    const float4 rec = chunk_rec[(size_t)b * C + c];
+    const float2 bp = summ[((size_t)b * C + c) * M + mc];
+    float2 g0 = make_float2(0.f, 0.f);
+    if (gstate) g0 = per_group ? gstate[((size_t)b * NG + q) * M + mc] : gstate[(size_t)b * M + mc];
+    Words<1> wd[K];
+    load_chunk_clamped<K, false>(wd, drive + row0, M, mc, kc);
+    if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
+    group_put(comp, w, lane, chunk_transition<false>(k.kappa, ph, rec), {bp.x, bp.y});
+    __syncthreads();
+    if (!valid) return;
+    // the state entering this chunk: L_c applied to the state entering the group
+    cf z = {g0.x, g0.y};
+    for (int j = 0; j < w; ++j) {
+        const float4 f = comp[j * GRP_LANES + lane];
+        z = cfma({f.x, f.y}, z, {f.z, f.w});
+    }
+    if (active) entries[((size_t)b * C + c) * M + m] = make_float2(z.re, z.im);
+    const int kq = opaque(kc);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        if (i < kq) {
+            const TokenCtl t = sctl[i];
+            z = cfma(mode_lambda(k, t.E, t.C, t.S), z, {bf16_lo(wd[i].w[0]), bf16_hi(wd[i].w[0])});
+            const cf zz[1] = {z};
+            if (active) store_states<1, F32>(y, row0 + (size_t)i * M, mc, zz);
+            if (NMID > 0 && (i + 1) % SAMU_BWD_SUB == 0 && i + 1 < K && active)
+                reinterpret_cast<float2*>(mid)[(((size_t)b * C + c) * NMID + (i + 1) / SAMU_BWD_SUB - 1) * M + mc] =
+                    make_float2(z.re, z.im);
+        }
+    }
+    if (active && z_final && c == C - 1)
+        reinterpret_cast<float2*>(z_final)[(size_t)b * M + m] = make_float2(z.re, z.im);
+}
+
+// 8 waves per SIMD: fits 64 VGPRs without spilling
+template <int K, bool F32>
+__global__ __launch_bounds__(GRP_LANES * SAMU_GROUP_MAX) __attribute__((amdgpu_waves_per_eu(8, 8))) void
+samu_greplay_kernel(int L, int M, int C, int G, int per_group, const TokenCtl* __restrict__ ctl,
+                    const uint32_t* __restrict__ drive, const float4* __restrict__ mtab,
+                    const float2* __restrict__ summ, const float4* __restrict__ chunk_rec,
+                    const float2* __restrict__ gstate, float2* __restrict__ entries, float* __restrict__ mid,
+                    void* __restrict__ y, float* __restrict__ z_final) {
+    extern __shared__ float4 gdyn[];
+    if ((int)(blockIdx.x + 1) * GRP_LANES <= M)  // uniform over the workgroup
+        greplay_body<K, F32, true>(gdyn, G, L, M, C, per_group, ctl, drive, mtab, summ, chunk_rec, gstate, entries,
+                                   mid, y, z_final);
+    else
+        greplay_body<K, F32, false>(gdyn, G, L, M, C, per_group, ctl, drive, mtab, summ, chunk_rec, gstate,
+                                    entries, mid, y, z_final);
+}
+
 inline int mode_block(int M, int VM) {
     const int lanes = (int)ceil_div(M, VM);
     return lanes >= 256 ? 256 : (int)ceil_div(lanes, 64) * 64;
@@ -473,6 +661,49 @@ hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const flo
         if (y_f32) REPLAY_CASE(16, true); else REPLAY_CASE(16, false);
     }
 #undef REPLAY_CASE
+    return hipGetLastError();
+}
+
+static size_t samu_group_lds_bytes(int G, int K) { return (size_t)G * GRP_LANES * sizeof(float4) + (size_t)G * K * sizeof(TokenCtl); }
+
+hipError_t launch_samu_gsummary(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                                const void* drive, bool reverse, float* summ, float* chunk_rec, float* gsum,
+                                hipStream_t s) {
+    const dim3 grid((unsigned)ceil_div(p.M, GRP_LANES), ch.NG, ch.B);
+    const dim3 block(GRP_LANES * ch.G);
+    const size_t lds = samu_group_lds_bytes(ch.G, ch.K);
+    const int id = reverse ? K_SAMU_REV_SUMMARY : K_SAMU_SUMMARY;
+#define GSUM_CASE(KK, RR)                                                                                  \
+    LRS_LAUNCH(id, (samu_gsummary_kernel<KK, RR>), grid, block, lds, s, p.L, p.M, ch.C, ch.G,            \
+               (const TokenCtl*)ctl, (const uint32_t*)drive, (const float4*)mtab, summ, (float4*)chunk_rec, \
+               (float4*)gsum)
+    if (ch.K == 32) {
+        if (reverse) GSUM_CASE(32, true); else GSUM_CASE(32, false);
+    } else {
+        if (reverse) GSUM_CASE(16, true); else GSUM_CASE(16, false);
+    }
+#undef GSUM_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_samu_greplay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                               const float* summ, const float* chunk_rec, const float* gstate, float* entries,
+                               float* mid, void* y, int y_f32, float* z_final, hipStream_t s) {
+    const dim3 grid((unsigned)ceil_div(p.M, GRP_LANES), ch.NG, ch.B);
+    const dim3 block(GRP_LANES * ch.G);
+    const size_t lds = samu_group_lds_bytes(ch.G, ch.K);
+    const int per_group = ch.NG > 1;
+#define GREP_CASE(KK, FF)                                                                                   \
+    LRS_LAUNCH(K_SAMU_REPLAY, (samu_greplay_kernel<KK, FF>), grid, block, lds, s, p.L, p.M, ch.C, ch.G,   \
+               per_group, (const TokenCtl*)ctl, (const uint32_t*)p.b, (const float4*)mtab,               \
+               (const float2*)summ, (const float4*)chunk_rec, (const float2*)gstate, (float2*)entries, mid, \
+               y, z_final)
+    if (ch.K == 32) {
+        if (y_f32) GREP_CASE(32, true); else GREP_CASE(32, false);
+    } else {
+        if (y_f32) GREP_CASE(16, true); else GREP_CASE(16, false);
+    }
+#undef GREP_CASE
     return hipGetLastError();
 }
 

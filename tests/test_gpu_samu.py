@@ -34,6 +34,12 @@ CASES = [
     # last chunk of 20 tokens: the backward starts its second half from the
     # mid-chunk state the forward stored
     ("ragged_second_half", 2, 660, 128, 32, 4, 0.1),
+    # the largest group one workgroup holds (16 chunks, a partial last group,
+    # a partial last 64-mode block), and the next size, which takes the
+    # three-kernel prefix
+    ("group_of_16", 2, 2000, 136, 32, 16, 0.1),
+    ("three_kernel_prefix_g17", 1, 1500, 72, 32, 17, 0.1),
+    ("k16_group_of_16", 1, 1000, 200, 16, 16, 0.1),
 ]
 
 
