@@ -28,13 +28,19 @@
  *   - Results are bitwise deterministic for the same inputs, (K, G), device
  *     and library build: every reduction has a fixed order; no atomics.
  *   - K (chunk length) is 16 or 32.  G (chunks per group of the two-level
- *     prefix) is >= 1, or 0 for the library's choice by shape: the serial
- *     prefix when ceil(L/K) <= 128, else groups of max(g_min, ceil(ceil(L/K)
- *     / 128)) chunks with g_min = 8 (SAMU) or 16 (RG-LRU).  G >= ceil(L/K)
- *     gives the serial chunk-to-chunk prefix.  The forward and backward
- *     calls may use different G (e.g. a serial forward prefix with a
- *     grouped reverse prefix): the grouping changes only the
- *     parenthesization of an exact composition.
+ *     prefix) is >= 1, or 0 for the library's choice.
+ *       SAMU: G = 0 means groups of 8 chunks.  Any G <= 16 runs the grouped
+ *       path (one workgroup per group of chunks: the group's composition U_g
+ *       and the state entering each chunk are formed on chip, with one scan
+ *       over the groups between the summary and replay launches); G > 16
+ *       runs the three-launch prefix (compose U_g, scan over groups, chunk
+ *       entries).
+ *       RG-LRU: G = 0 means the serial prefix when ceil(L/K) <= 128, else
+ *       groups of max(16, ceil(ceil(L/K) / 128)) chunks.
+ *     G >= ceil(L/K) gives a single group (the serial chunk-to-chunk
+ *     prefix).  The forward and backward calls may use different G (e.g. a
+ *     serial forward prefix with a grouped reverse prefix): the grouping
+ *     changes only the parenthesization of an exact composition.
  *   - B >= 1, L >= 1 with any remainder (the last chunk has L - (C-1) K
  *     tokens), ceil(L/K) <= 65535, B <= 65535, B*L < 2^31.
  */
