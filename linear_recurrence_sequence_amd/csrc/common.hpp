@@ -163,6 +163,25 @@ __device__ __forceinline__ cf chunk_transition(float kappa, float4 ph, float4 re
     return {rho * re, REV ? -rho * im : rho * im};
 }
 
+// The 32-bit words of one chunk's rows of a [B, L, M] word tensor, read
+// through a raw buffer descriptor whose range ends at the chunk's last token:
+// a row past it (token i >= kc of a partial last chunk) reads as 0, with no
+// branch and no per-load clamp, and no access can leave the chunk.  The
+// token offset goes into the per-lane offset, which the range check covers
+// (the scalar offset it does not).  0x00020000 is the gfx9 descriptor word 3
+// for raw 32-bit loads.
+struct ChunkRows {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int M;
+    __device__ ChunkRows(const uint32_t* chunk_row0, int kc, int M_)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(chunk_row0), (short)0, kc * M_ * 4,
+                                                 0x00020000)),
+          M(M_) {}
+    __device__ uint32_t load(int i, int m) const {
+        return __builtin_amdgcn_raw_buffer_load_b32(rsrc, (i * M + m) * 4, 0, 0);
+    }
+};
+
 // Orders LDS traffic among the lanes of one wave (a region no other wave
 // touches): the wave's LDS instructions execute in program order, so only
 // the compiler has to be kept from moving accesses across this point.

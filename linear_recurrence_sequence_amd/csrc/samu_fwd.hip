@@ -440,15 +440,16 @@ __device__ __forceinline__ void group_put(float4* comp, int w, int lane, cf A, c
     comp[w * GRP_LANES + lane] = make_float4(A.re, A.im, B.re, B.im);
 }
 
-// The drive words of one chunk, clamped into the chunk: token i >= kc
-// re-reads token kc - 1 (its value is never used), so no load is guarded.
+// The drive words of one chunk through its range-checked rows (tokens past a
+// partial chunk's end read as 0 and are never used).
 template <int K, bool REV>
 __device__ __forceinline__ void load_chunk_clamped(Words<1> (&w)[K], const uint32_t* __restrict__ rows, int M,
                                                    int off, int kc) {
+    const ChunkRows cr(rows, kc, M);
 #pragma unroll
     for (int j = 0; j < K; ++j) {
         const int i = REV ? K - 1 - j : j;
-        w[i].load(rows + (size_t)min(i, kc - 1) * M, off);
+        w[i].w[0] = cr.load(i, off);
     }
     __builtin_amdgcn_sched_barrier(0);
 }
