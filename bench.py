@@ -708,15 +708,19 @@ def main():
             dd = {k: dev(v) for k, v in di.items()}
             xs, bs, z = dd["x_sel"][:, 0].contiguous(), dd["b"][:, 0].contiguous(), dd["z0"]
             yd = torch.empty((Bd, M, 2), dtype=torch.bfloat16, device="cuda")
+            tab = scan.samu_scan_decode_prepare(d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"], d["theta"])
 
-            def dec_step():
+            def dec_step(tab=tab):
                 scan.samu_scan_decode(xs, bs, d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"],
-                                      d["theta"], z, y=yd, z_out=z)
+                                      d["theta"], z, y=yd, z_out=z, table=tab)
 
             n = 200
             dms, _ = timed(dec_step, n, 10, False)
             _, dprof = timed(dec_step, n, 1, True)
             kus = dprof["samu_decode"][0] / dprof["samu_decode"][1] * 1e3
+            # the same step forming its constants itself (no prepared table)
+            _, dprof0 = timed(lambda: dec_step(None), n, 10, True)
+            kus0 = dprof0["samu_decode"][0] / dprof0["samu_decode"][1] * 1e3
             # the same steps replayed from a captured HIP graph (32 steps per graph)
             gs = torch.cuda.Stream()
             gs.wait_stream(torch.cuda.current_stream())
@@ -730,12 +734,14 @@ def main():
                 for _ in range(32):
                     dec_step()
             gms, _ = timed(graph.replay, 20, 3, False)
-            # x_sel, b, state in and out, y, both directions, nu and theta
-            nbytes = Bd * (2 * D + 4 * M + 16 * M + 4 * M) + 8 * (D + 1) + 8 * M
+            # x_sel, b, state in and out, y per row; both directions and the
+            # constant table (64 B per mode) once
+            nbytes = Bd * (2 * D + 4 * M + 16 * M + 4 * M) + 8 * (D + 1) + 64 * M + 16
             dec[f"B{Bd}"] = {"us_per_step": round(dms * 1e3, 2),
                              "us_per_step_graph": round(gms * 1e3 / 32, 2), "kernel_us": round(kus, 2),
                              "bytes_per_step": nbytes,
-                             "kernel_gbs": round(nbytes / (kus * 1e-6) / 1e9, 1)}
+                             "kernel_gbs": round(nbytes / (kus * 1e-6) / 1e9, 1),
+                             "kernel_us_without_table": round(kus0, 2)}
             log(f"    B={Bd}: {dms * 1e3:.2f} us/step eager, {gms * 1e3 / 32:.2f} us/step from a graph "
                 f"({kus:.2f} us kernel with events, {nbytes} B)")
             del graph

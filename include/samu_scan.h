@@ -187,6 +187,10 @@ scan_status samu_scan_fwd_noalloc(int B, int L, int D, int K, int G,
  *   b       bf16 [B, M, 2]         complex drive of the new token
  *   w_phi, w_r, a_phi, a_r, nu, theta  as for samu_scan_fwd
  *   z_in    f32 [B, M, 2] or NULL  state before the token (NULL = 0)
+ *   table   samu_scan_decode_table_bytes(D) bytes written by
+ *           samu_scan_decode_prepare for these parameters, or
+ *           NULL: the step then forms the per-mode phasors (in FP64) and the
+ *           direction norms itself, every call
  *   z_out   f32 [B, M, 2]          state after the token; may equal z_in
  *                                  (updated in place), must not overlap it
  *                                  otherwise
@@ -195,9 +199,22 @@ scan_status samu_scan_fwd_noalloc(int B, int L, int D, int K, int G,
 scan_status samu_scan_decode(int B, int D, const void* x_sel, const void* b,
                              const float* w_phi, const float* w_r,
                              const float* a_phi, const float* a_r,
-                             const float* nu, const float* theta,
+                             const float* nu, const float* theta, const void* table,
                              const float* z_in, float* z_out, void* y, int y_dtype,
                              void* stream);
+
+/* The per-parameter constants of the decode step, formed once for a set of
+ * parameters and reused by every step: for each mode the phasor e^{i theta}
+ * (an FP32 hi + lo pair from an FP64 evaluation) and -nu log2(e); 1/||w|| of
+ * both directions (norm over all D+1 entries) and tanh(a)/sqrt(M) of both
+ * amplitudes.  The table is caller-owned, 16-byte aligned,
+ * samu_scan_decode_table_bytes(D) bytes (0 = unsupported D); it must be
+ * prepared again when a parameter changes. */
+size_t samu_scan_decode_table_bytes(int D);
+scan_status samu_scan_decode_prepare(int D, const float* w_phi, const float* w_r,
+                                     const float* a_phi, const float* a_r,
+                                     const float* nu, const float* theta,
+                                     void* table, void* stream);
 
 /* ======================================================================
  * RG-LRU scan (page "SAMU 与 RG-LRU 的 H800 训练性能对比", section 04; reset

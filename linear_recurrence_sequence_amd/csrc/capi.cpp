@@ -626,10 +626,37 @@ scan_status rglru_gate_proj_bwd(int B, int L, int D, const void* x, const void* 
 }
 
 // ------------------------------------------------------- SAMU decode ---
+size_t samu_scan_decode_table_bytes(int D) {
+    if (D < 8 || D % 8 != 0) return 0;
+    return samu_decode_table_floats(D / 2) * sizeof(float);
+}
+
+scan_status samu_scan_decode_prepare(int D, const float* w_phi, const float* w_r, const float* a_phi,
+                                     const float* a_r, const float* nu, const float* theta, void* table,
+                                     void* stream) {
+    if (D < 8 || D % 8 != 0)
+        return fail(SCAN_ERR_SHAPE, "samu_scan_decode_prepare: unsupported D=" + std::to_string(D) +
+                                        " (need D >= 8 a multiple of 8)");
+    scan_status st = check_ptrs({{w_phi, 0, "w_phi"}, {w_r, 0, "w_r"}, {a_phi, 0, "a_phi"}, {a_r, 0, "a_r"},
+                                 {nu, 0, "nu"}, {theta, 0, "theta"}, {table, 0, "table"}},
+                                {});
+    if (st != SCAN_OK) return st;
+    const int M = D / 2;
+    st = check_alias({{w_phi, (size_t)(D + 1) * 4, "w_phi"}, {w_r, (size_t)(D + 1) * 4, "w_r"},
+                      {a_phi, 4, "a_phi"}, {a_r, 4, "a_r"}, {nu, (size_t)M * 4, "nu"},
+                      {theta, (size_t)M * 4, "theta"}},
+                     {{table, samu_scan_decode_table_bytes(D), "table"}});
+    if (st != SCAN_OK) return st;
+    LRS_TRY(launch_samu_decode_prepare(D, w_phi, w_r, a_phi, a_r, nu, theta, (float*)table,
+                                       (hipStream_t)stream),
+            "samu decode table");
+    return SCAN_OK;
+}
+
 scan_status samu_scan_decode(int B, int D, const void* x_sel, const void* b, const float* w_phi,
                              const float* w_r, const float* a_phi, const float* a_r, const float* nu,
-                             const float* theta, const float* z_in, float* z_out, void* y, int y_dtype,
-                             void* stream) {
+                             const float* theta, const void* table, const float* z_in, float* z_out, void* y,
+                             int y_dtype, void* stream) {
     if (B < 1 || B > 65535 || D < 8 || D % 8 != 0)
         return fail(SCAN_ERR_SHAPE, "samu_scan_decode: unsupported shape B=" + std::to_string(B) +
                                         " D=" + std::to_string(D) +
@@ -639,20 +666,21 @@ scan_status samu_scan_decode(int B, int D, const void* x_sel, const void* b, con
     scan_status st = check_ptrs({{x_sel, 0, "x_sel"}, {b, 0, "b"}, {w_phi, 0, "w_phi"}, {w_r, 0, "w_r"},
                                  {a_phi, 0, "a_phi"}, {a_r, 0, "a_r"}, {nu, 0, "nu"}, {theta, 0, "theta"},
                                  {z_out, 0, "z_out"}, {y, 0, "y"}},
-                                {{z_in, 0, "z_in"}});
+                                {{z_in, 0, "z_in"}, {table, 0, "table"}});
     if (st != SCAN_OK) return st;
     const int M = D / 2;
     const size_t BM = (size_t)B * M;
     std::vector<Span> ins = {{x_sel, (size_t)B * D * 2, "x_sel"}, {b, BM * 4, "b"},
                              {w_phi, (size_t)(D + 1) * 4, "w_phi"}, {w_r, (size_t)(D + 1) * 4, "w_r"},
                              {a_phi, 4, "a_phi"}, {a_r, 4, "a_r"}, {nu, (size_t)M * 4, "nu"},
-                             {theta, (size_t)M * 4, "theta"}};
+                             {theta, (size_t)M * 4, "theta"},
+                             {table, samu_scan_decode_table_bytes(D), "table"}};
     // the state may be updated in place (z_out == z_in), never partly overlapped
     if (z_in != z_out) ins.push_back({z_in, BM * 8, "z_in"});
     st = check_alias(ins, {{z_out, BM * 8, "z_out"}, {y, BM * 2 * (y_dtype == SCAN_F32 ? 4 : 2), "y"}});
     if (st != SCAN_OK) return st;
-    LRS_TRY(launch_samu_decode(B, D, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z_in, z_out, y,
-                               y_dtype == SCAN_F32, (hipStream_t)stream),
+    LRS_TRY(launch_samu_decode(B, D, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, (const float*)table, z_in,
+                               z_out, y, y_dtype == SCAN_F32, (hipStream_t)stream),
             "samu decode");
     return SCAN_OK;
 }

@@ -169,11 +169,15 @@ hipError_t launch_samu_params(const SamuParams& p, const Chunking& ch, const dou
                               float* da_r, float* dnu, float* dtheta, hipStream_t s);
 
 // one generation step: z_out = lambda(x_sel) z_in + b, y = z_out (z_in NULL = 0;
-// z_out may be z_in)
+// z_out may be z_in); table (NULL: formed per step) from launch_samu_decode_prepare
+size_t samu_decode_table_floats(int M);
+hipError_t launch_samu_decode_prepare(int D, const float* w_phi, const float* w_r, const float* a_phi,
+                                      const float* a_r, const float* nu, const float* theta, float* table,
+                                      hipStream_t s);
 hipError_t launch_samu_decode(int B, int D, const void* x_sel, const void* b, const float* w_phi,
                               const float* w_r, const float* a_phi, const float* a_r, const float* nu,
-                              const float* theta, const float* z_in, float* z_out, void* y, int y_f32,
-                              hipStream_t s);
+                              const float* theta, const float* table, const float* z_in, float* z_out, void* y,
+                              int y_f32, hipStream_t s);
 
 // -------------------------------------------------------------- RG-LRU ---
 struct RglruParams {

@@ -11,11 +11,11 @@
 //   lambda_m = exp(-nu_m e^c) [(cos th_m cos d - sin th_m sin d) + i (...)],
 //   z' = lambda z + b,  y = z'.
 //
-// Grid (ceil(M / 256), B): each workgroup forms the two dot products and the
-// two direction norms of its batch row (every mode block repeats this; it is
-// D+1 values against the M/256-fold larger mode work), then 256 lanes advance
-// one mode each.  Sums run in a fixed order, so a step is bitwise
-// reproducible.
+// Grid (ceil(M / 256), B): each workgroup forms the two dot products (and,
+// without a prepared table, the two direction norms) of its batch row --
+// every mode block repeats this small reduction, which measured faster than
+// one larger workgroup per row at B = 1..256 -- then 256 lanes advance one
+// mode each.  Sums run in a fixed order, so a step is bitwise reproducible.
 #include "common.hpp"
 
 namespace lrs {
@@ -24,12 +24,15 @@ namespace {
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_WAVES = DEC_THREADS / 64;
 
-template <bool F32>
+// TAB: the mode constants, 1/||w|| and tanh(a)/sqrt(M) come from a table
+// written once by samu_decode_prepare_kernel (no FP64 phasor, no norm
+// reduction and no amplitude tanh per step).
+template <bool F32, bool TAB>
 __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
     int D, int M, const uint32_t* __restrict__ x_sel, const uint32_t* __restrict__ drive,
     const float* __restrict__ w_phi, const float* __restrict__ w_r, const float* __restrict__ a_phi,
     const float* __restrict__ a_r, const float* __restrict__ nu, const float* __restrict__ theta,
-    const float2* z_in, float2* z_out, void* __restrict__ y) {
+    const float4* __restrict__ table, const float2* z_in, float2* z_out, void* __restrict__ y) {
     __shared__ float red[4][DEC_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.y;
@@ -37,14 +40,23 @@ __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
     const uint32_t* xr = x_sel + (size_t)b * W;
 
     // this lane's mode: its inputs are requested first and its constant
-    // phasor is formed while the selector reduction is in flight
+    // phasor is formed (or loaded) while the selector reduction is in flight
     const int m = blockIdx.x * DEC_THREADS + tid;
     const bool act = m < M;
     const int mc = act ? m : M - 1;
     const size_t i = (size_t)b * M + mc;
     const float2 z0 = z_in ? z_in[i] : make_float2(0.f, 0.f);
     const uint32_t bw = drive[i];
-    const float nu_m = nu[mc], th_m = theta[mc];
+    ModeConst k;
+    float4 inv = make_float4(0.f, 0.f, 0.f, 0.f);
+    float nu_m = 0.f, th_m = 0.f;
+    if (TAB) {
+        k = load_mode(table, mc);
+        inv = table[(size_t)M * MODE_REC];
+    } else {
+        nu_m = nu[mc];
+        th_m = theta[mc];
+    }
 
     float sp = 0.f, sr = 0.f, np = 0.f, nr = 0.f;
 #pragma unroll 4
@@ -55,8 +67,10 @@ __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
         const float x0 = bf16_lo(xw), x1 = bf16_hi(xw);
         sp = fmaf(x1, wp.y, fmaf(x0, wp.x, sp));
         sr = fmaf(x1, wr.y, fmaf(x0, wr.x, sr));
-        np = fmaf(wp.y, wp.y, fmaf(wp.x, wp.x, np));
-        nr = fmaf(wr.y, wr.y, fmaf(wr.x, wr.x, nr));
+        if (!TAB) {
+            np = fmaf(wp.y, wp.y, fmaf(wp.x, wp.x, np));
+            nr = fmaf(wr.y, wr.y, fmaf(wr.x, wr.x, nr));
+        }
     }
     if (tid == 0) {  // the constant 1 of x~ and the bias slot of each direction
         const float bp = w_phi[D], br = w_r[D];
@@ -65,11 +79,13 @@ __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
         np = fmaf(bp, bp, np);
         nr = fmaf(br, br, nr);
     }
-    const ModeConst k = mode_const(nu_m, th_m);
+    if (!TAB) k = mode_const(nu_m, th_m);
     sp = wave_sum(sp);
     sr = wave_sum(sr);
-    np = wave_sum(np);
-    nr = wave_sum(nr);
+    if (!TAB) {
+        np = wave_sum(np);
+        nr = wave_sum(nr);
+    }
     if (lane == 0) {
         red[0][wave] = sp;
         red[1][wave] = sr;
@@ -82,15 +98,17 @@ __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
     for (int w = 0; w < DEC_WAVES; ++w) {
         Sp += red[0][w];
         Sr += red[1][w];
-        Np += red[2][w];
-        Nr += red[3][w];
+        if (!TAB) {
+            Np += red[2][w];
+            Nr += red[3][w];
+        }
     }
-    const float p = tanhf(Sp / sqrtf(Np));
-    const float r = tanhf(Sr / sqrtf(Nr));
+    const float p = tanhf(TAB ? Sp * inv.x : Sp / sqrtf(Np));
+    const float r = tanhf(TAB ? Sr * inv.y : Sr / sqrtf(Nr));
     const float q = r / (1.0f + r * r);
     const float sM = sqrtf((float)M);
-    const float d = tanhf(a_phi[0]) / sM * p;
-    const float c = tanhf(a_r[0]) / sM * q;
+    const float d = (TAB ? inv.z : tanhf(a_phi[0]) / sM) * p;
+    const float c = (TAB ? inv.w : tanhf(a_r[0]) / sM) * q;
     const float E = expf(c);
     float S, Cd;
     sincosf(d, &S, &Cd);
@@ -103,19 +121,77 @@ __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
     else reinterpret_cast<uint32_t*>(y)[i] = pack_bf16x2(z.re, z.im);
 }
 
+// The table of samu_decode_kernel<.., true>: the per-mode constant records
+// (the layout of the scan's mode table; its chunk phasors are not used here)
+// and (1/||w_phi||, 1/||w_r||, tanh(a_phi)/sqrt(M), tanh(a_r)/sqrt(M)), the
+// norms over all D+1 entries summed in a fixed order.
+__global__ __launch_bounds__(DEC_THREADS) void samu_decode_prepare_kernel(int D, int M, const float* __restrict__ w_phi,
+                                                                          const float* __restrict__ w_r,
+                                                                          const float* __restrict__ a_phi,
+                                                                          const float* __restrict__ a_r,
+                                                                          const float* __restrict__ nu,
+                                                                          const float* __restrict__ theta,
+                                                                          float4* __restrict__ table) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = blockIdx.x * DEC_THREADS + tid;
+    if (m < M) {
+        const ChunkPhase one = chunk_phase(theta[m], 1);
+        store_mode(table, m, mode_const(nu[m], theta[m]), one, one);
+    }
+    if (blockIdx.x != 0) return;
+    __shared__ float red[2][DEC_WAVES];
+    float np = 0.f, nr = 0.f;
+    for (int j = tid; j <= D; j += DEC_THREADS) {
+        np = fmaf(w_phi[j], w_phi[j], np);
+        nr = fmaf(w_r[j], w_r[j], nr);
+    }
+    np = wave_sum(np);
+    nr = wave_sum(nr);
+    if (lane == 0) {
+        red[0][wave] = np;
+        red[1][wave] = nr;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float Np = 0.f, Nr = 0.f;
+        for (int w = 0; w < DEC_WAVES; ++w) {
+            Np += red[0][w];
+            Nr += red[1][w];
+        }
+        const float sM = sqrtf((float)M);
+        table[(size_t)M * MODE_REC] =
+            make_float4(1.0f / sqrtf(Np), 1.0f / sqrtf(Nr), tanhf(a_phi[0]) / sM, tanhf(a_r[0]) / sM);
+    }
+}
+
 }  // namespace
+
+size_t samu_decode_table_floats(int M) { return ((size_t)M * MODE_REC + 1) * 4; }
+
+hipError_t launch_samu_decode_prepare(int D, const float* w_phi, const float* w_r, const float* a_phi,
+                                      const float* a_r, const float* nu, const float* theta, float* table,
+                                      hipStream_t s) {
+    const int M = D / 2;
+    LRS_LAUNCH(K_SAMU_DECODE, samu_decode_prepare_kernel, dim3((unsigned)ceil_div(M, DEC_THREADS)),
+               dim3(DEC_THREADS), 0, s, D, M, w_phi, w_r, a_phi, a_r, nu, theta, (float4*)table);
+    return hipGetLastError();
+}
 
 hipError_t launch_samu_decode(int B, int D, const void* x_sel, const void* b, const float* w_phi,
                               const float* w_r, const float* a_phi, const float* a_r, const float* nu,
-                              const float* theta, const float* z_in, float* z_out, void* y, int y_f32,
-                              hipStream_t s) {
+                              const float* theta, const float* table, const float* z_in, float* z_out, void* y,
+                              int y_f32, hipStream_t s) {
     const int M = D / 2;
     const dim3 grid((unsigned)ceil_div(M, DEC_THREADS), (unsigned)B);
-#define DEC_CASE(FF)                                                                                        \
-    LRS_LAUNCH(K_SAMU_DECODE, samu_decode_kernel<FF>, grid, dim3(DEC_THREADS), 0, s, D, M,                \
+#define DEC_CASE(FF, TT)                                                                                    \
+    LRS_LAUNCH(K_SAMU_DECODE, (samu_decode_kernel<FF, TT>), grid, dim3(DEC_THREADS), 0, s, D, M,          \
                (const uint32_t*)x_sel, (const uint32_t*)b, w_phi, w_r, a_phi, a_r, nu, theta,              \
-               (const float2*)z_in, (float2*)z_out, y)
-    if (y_f32) DEC_CASE(true); else DEC_CASE(false);
+               (const float4*)table, (const float2*)z_in, (float2*)z_out, y)
+    if (table) {
+        if (y_f32) DEC_CASE(true, true); else DEC_CASE(false, true);
+    } else {
+        if (y_f32) DEC_CASE(true, false); else DEC_CASE(false, false);
+    }
 #undef DEC_CASE
     return hipGetLastError();
 }

@@ -66,8 +66,12 @@ def lib():
     L.rglru_gate_proj_bwd_workspace_bytes.restype = sz
     L.rglru_gate_proj_bwd.argtypes = [i, i, i] + [vp] * 5 + [i] + [vp] * 7 + [sz, vp]
     L.rglru_gate_proj_bwd.restype = i
-    L.samu_scan_decode.argtypes = [i, i] + [vp] * 10 + [vp, i, vp]
+    L.samu_scan_decode.argtypes = [i, i] + [vp] * 11 + [vp, i, vp]
     L.samu_scan_decode.restype = i
+    L.samu_scan_decode_table_bytes.argtypes = [i]
+    L.samu_scan_decode_table_bytes.restype = sz
+    L.samu_scan_decode_prepare.argtypes = [i] + [vp] * 7 + [vp]
+    L.samu_scan_decode_prepare.restype = i
     L.rglru_scan_fwd.argtypes = [i] * 5 + [vp] * 6 + [vp, i, vp, vp, vp, sz, vp]
     L.rglru_scan_fwd.restype = i
     L.rglru_scan_bwd.argtypes = [i] * 5 + [vp] * 5 + [vp, vp, vp, vp, vp, vp, i, vp, vp, vp, sz, vp]
@@ -277,11 +281,32 @@ def samu_scan_bwd(x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, saved, dy, dz_fin
 
 
 # ---------------------------------------------------------- SAMU decode ---
+def samu_scan_decode_prepare(w_phi, w_r, a_phi, a_r, nu, theta, *, table=None, stream=None):
+    """The decode step's constant table for these parameters (uint8 tensor)."""
+    D = w_phi.shape[0] - 1
+    M = D // 2
+    _want(w_phi, "w_phi", _F32, (D + 1,))
+    _want(w_r, "w_r", _F32, (D + 1,))
+    _want(a_phi, "a_phi", _F32, (1,))
+    _want(a_r, "a_r", _F32, (1,))
+    _want(nu, "nu", _F32, (M,))
+    _want(theta, "theta", _F32, (M,))
+    n = lib().samu_scan_decode_table_bytes(D)
+    if table is None:
+        table = _bytes(n, w_phi.device)
+    _want_bytes(table, "table", n)
+    st = lib().samu_scan_decode_prepare(D, _p(w_phi), _p(w_r), _p(a_phi), _p(a_r), _p(nu), _p(theta), _p(table),
+                                        _stream(stream))
+    _check(st, "samu_scan_decode_prepare")
+    return table
+
+
 def samu_scan_decode(x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z=None, *,
-                     y_dtype=torch.bfloat16, y=None, z_out=None, stream=None):
+                     y_dtype=torch.bfloat16, y=None, z_out=None, table=None, stream=None):
     """One generation step.  x_sel [B, D] bf16, b [B, M, 2] bf16, z [B, M, 2]
-    f32 or None (= 0).  Returns (y [B, M, 2], z_out [B, M, 2] f32); pass
-    z_out=z to update the state in place."""
+    f32 or None (= 0); table from samu_scan_decode_prepare (or None: the
+    step forms its constants itself).  Returns (y [B, M, 2], z_out [B, M, 2]
+    f32); pass z_out=z to update the state in place."""
     if x_sel.dim() != 2:
         raise ValueError(f"x_sel must be [B, D], got shape {tuple(x_sel.shape)}")
     B, L, D, M = _samu_params(x_sel.unsqueeze(1), w_phi, w_r, a_phi, a_r, nu, theta)
@@ -294,8 +319,10 @@ def samu_scan_decode(x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z=None, *,
     if z_out is None:
         z_out = torch.empty((B, M, 2), dtype=torch.float32, device=dev)
     _want(z_out, "z_out", _F32, (B, M, 2))
+    if table is not None:
+        _want_bytes(table, "table", lib().samu_scan_decode_table_bytes(D))
     st = lib().samu_scan_decode(B, D, _p(x_sel), _p(b), _p(w_phi), _p(w_r), _p(a_phi), _p(a_r),
-                                _p(nu), _p(theta), _p(z), _p(z_out), _p(y), _code(y.dtype),
+                                _p(nu), _p(theta), _p(table), _p(z), _p(z_out), _p(y), _code(y.dtype),
                                 _stream(stream))
     _check(st, "samu_scan_decode")
     return y, z_out

@@ -155,13 +155,13 @@ def test_rglru_fwd_rejects_before_enqueue():
 def _call_decode(**over):
     from linear_recurrence_sequence_amd import scan
     a = dict(B=2, D=16, x_sel=0x100000, b=0x200000, w_phi=0x300000, w_r=0x300100, a_phi=0x300200,
-             a_r=0x300210, nu=0x300300, theta=0x300400, z_in=0x500000, z_out=0x600000,
+             a_r=0x300210, nu=0x300300, theta=0x300400, table=None, z_in=0x500000, z_out=0x600000,
              y=0x700000, y_dtype=0)
     a.update(over)
     v = lambda x: None if x is None else _fake(x)
     return scan.lib().samu_scan_decode(a["B"], a["D"], v(a["x_sel"]), v(a["b"]), v(a["w_phi"]),
                                        v(a["w_r"]), v(a["a_phi"]), v(a["a_r"]), v(a["nu"]),
-                                       v(a["theta"]), v(a["z_in"]), v(a["z_out"]), v(a["y"]),
+                                       v(a["theta"]), v(a["table"]), v(a["z_in"]), v(a["z_out"]), v(a["y"]),
                                        a["y_dtype"], None)
 
 
@@ -172,6 +172,8 @@ def _call_decode(**over):
     (dict(y=0x100000), -6),                 # y overlaps x_sel
     (dict(z_out=0x500020), -6),             # z_out partly overlaps z_in
     (dict(z_out=0x700000), -6),             # z_out overlaps y
+    (dict(table=0x800008), -3),             # misaligned table
+    (dict(y=0x800000, table=0x800000), -6),  # y overlaps the table
 ])
 @fake_pointers
 def test_samu_decode_rejects_before_enqueue(over, status):
@@ -244,3 +246,17 @@ def test_noalloc_forward_rejects_before_enqueue():
     assert b"static scratch" in L.scan_last_error()
     # an unsupported shape is named by the forward's own check
     assert L.samu_scan_fwd_noalloc(1, 64, 12, 32, 0, *p, None, f(0x400000), 0, None, f(0x500000), None) == -2
+
+
+@fake_pointers
+def test_decode_prepare_rejects_before_enqueue():
+    from linear_recurrence_sequence_amd import scan
+    L = scan.lib()
+    f = _fake
+    assert L.samu_scan_decode_table_bytes(12) == 0
+    assert L.samu_scan_decode_table_bytes(16) == (8 * 4 + 1) * 16     # 4 float4 per mode + the norms
+    p = [f(0x300000), f(0x300100), f(0x300200), f(0x300210), f(0x300300), f(0x300400)]
+    assert L.samu_scan_decode_prepare(12, *p, f(0x800000), None) == -2
+    assert L.samu_scan_decode_prepare(16, *p, None, None) == -1
+    assert L.samu_scan_decode_prepare(16, *p, f(0x800004), None) == -3
+    assert L.samu_scan_decode_prepare(16, *p, f(0x300300), None) == -6      # table over nu
