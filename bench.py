@@ -116,16 +116,20 @@ def samu_kernel_bytes(B, L, D, K, G):
         # forward replay writes the entry states the backward reads
         NGM = B * NG * M
         tab.update({
+            # the controller also writes one (G_c, e^{i D_c}) record per chunk
+            "samu_controller": (tab["samu_controller"][0], tab["samu_controller"][1] + 16 * BC),
             "samu_chunk_summary": (tab["samu_chunk_summary"][0],
-                                   2 * BLD + 16 * BL + 32 * M + 8 * BCM + 16 * BC + 16 * NGM),
+                                   2 * BLD + 16 * BL + 32 * M + 16 * BC + 8 * BCM + 16 * NGM),
             "samu_reverse_summary": (tab["samu_reverse_summary"][0],
-                                     2 * BLD + 16 * BL + 32 * M + 8 * BCM + 16 * BC + 16 * NGM),
+                                     2 * BLD + 16 * BL + 32 * M + 16 * BC + 8 * BCM + 16 * NGM),
             "samu_replay": (tab["samu_replay"][0],
                             2 * BLD + 16 * BL + 32 * M + 8 * BCM + 16 * BC + 8 * NGM + 2 * BLD + 8 * B * M
                             + 8 * BMID + 8 * BCM),
+            # (d nu, d theta) summed over each group's chunks: one row per group
             "samu_bwd_replay": (tab["samu_bwd_replay"][0],
                                 2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BMID + 8 * BCM + 16 * BC
-                                + 8 * NGM + 2 * BLD + 8 * B * n_tiles * L + 8 * BCM),
+                                + 8 * NGM + 2 * BLD + 8 * B * n_tiles * L + 8 * NGM),
+            "samu_params": (tab["samu_params"][0] - 8 * BCM + 8 * NGM, tab["samu_params"][1] - 8 * BCM + 8 * NGM),
         })
     tab.update({
         # x_sel, p, r, per-tile partials -> dx_sel, per-block direction partials

@@ -128,7 +128,7 @@ static constexpr int kSamuGroup = 8;
 static bool samu_fused(const Chunking& ch) { return ch.G <= SAMU_GROUP_MAX; }
 
 struct SamuSaved {
-    float *p, *r, *u, *ctl, *mtab, *inv_norm, *entries, *mid;
+    float *p, *r, *u, *ctl, *mtab, *inv_norm, *entries, *mid, *crec;
 };
 static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t* bytes) {
     Carver cv(base);
@@ -142,6 +142,7 @@ static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t
     s.inv_norm = cv.take<float>(8);  // 1/||w_phi||, 1/||w_r||, pad, then the FP64 squared norms
     s.entries = cv.take<float>((size_t)ch.B * ch.C * M * 2);
     s.mid = cv.take<float>((size_t)ch.B * ch.C * samu_mid_states(ch.K) * M * 2);
+    s.crec = cv.take<float>((size_t)ch.B * ch.C * 4);  // (G_c, cos D_c, sin D_c, 0) per chunk
     if (bytes) *bytes = cv.off;
     return s;
 }
@@ -344,11 +345,12 @@ scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
     SamuSaved sv = samu_saved_layout(saved, ch, M, nullptr);
     SamuFwdWs ws = samu_fwd_ws_layout(workspace, ch, M, nullptr);
-    LRS_TRY(launch_samu_controller(p, ch, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, sv.inv_norm, s), "samu controller");
+    LRS_TRY(launch_samu_controller(p, ch, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, sv.inv_norm, sv.crec, s),
+            "samu controller");
     if (samu_fused(ch)) {
         // summaries with U_g composed per group, the scan over groups (when
         // there is more than one), and the replay forming its chunk entries
-        LRS_TRY(launch_samu_gsummary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, ws.chunk, ws.gsum, s),
+        LRS_TRY(launch_samu_gsummary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, sv.crec, ws.gsum, s),
                 "samu chunk summary");
         const float* gstate = z0;
         if (ch.NG > 1) {
@@ -356,7 +358,7 @@ scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, 
             LRS_TRY(launch_group_scan(2, ch, M, ws.gsum, z0, gentry, s), "samu group scan");
             gstate = gentry;
         }
-        LRS_TRY(launch_samu_greplay(p, ch, sv.ctl, sv.mtab, ws.summ, ws.chunk, gstate, sv.entries, sv.mid, y,
+        LRS_TRY(launch_samu_greplay(p, ch, sv.ctl, sv.mtab, ws.summ, sv.crec, gstate, sv.entries, sv.mid, y,
                                     y_dtype == SCAN_F32, z_final, s),
                 "samu replay");
         return SCAN_OK;
@@ -415,7 +417,7 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuBwdWs ws = samu_bwd_ws_layout(workspace, ch, D, M, nullptr);
     const int f32 = grad_dtype == SCAN_F32;
     if (samu_fused(ch)) {
-        LRS_TRY(launch_samu_gsummary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, ws.rchunk, ws.rgsum, s),
+        LRS_TRY(launch_samu_gsummary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, sv.crec, ws.rgsum, s),
                 "samu reverse summary");
         const float* gcarry = dz_final;
         if (ch.NG > 1) {
@@ -423,7 +425,7 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
             LRS_TRY(launch_group_scan(2, ch, M, ws.rgsum, dz_final, gentry, s), "samu reverse group scan");
             gcarry = gentry;
         }
-        LRS_TRY(launch_samu_gbwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, ws.rsumm, ws.rchunk, gcarry, dy,
+        LRS_TRY(launch_samu_gbwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, ws.rsumm, sv.crec, gcarry, dy,
                                         db, f32, dz0, ws.tok_part, ws.n_tiles, ws.mode_part, s),
                 "samu backward replay");
     } else {
@@ -439,7 +441,8 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     LRS_TRY(launch_samu_ctl_bwd(p, sv.p, sv.r, sv.u, sv.inv_norm, ws.tok_part, ws.n_tiles, dx_sel, f32, ws.g_part, s),
             "samu controller backward");
     LRS_TRY(launch_samu_params(p, ch, reinterpret_cast<const double*>(sv.inv_norm + 4), ws.g_part, ws.n_blk,
-                               ws.mode_part, dw_phi, dw_r, da_phi, da_r, dnu, dtheta, s),
+                               ws.mode_part, samu_fused(ch) ? ch.B * ch.NG : ch.B * ch.C, dw_phi, dw_r, da_phi,
+                               da_r, dnu, dtheta, s),
             "samu parameter reductions");
     return SCAN_OK;
 }
@@ -513,7 +516,8 @@ scan_status samu_scan_baseline_fwd(int variant, int B, int L, int D, const void*
     chunking(B, L, 32, 0, kSamuMinGroup, &ch);  // the controller's chunk phasors are not used here
     SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
     SamuBaseWs ws = samu_base_layout(workspace, B, L, M, variant, nullptr);
-    LRS_TRY(launch_samu_controller(p, ch, ws.p, ws.r, ws.u, ws.ctl, ws.mtab, nullptr, s), "samu controller");
+    LRS_TRY(launch_samu_controller(p, ch, ws.p, ws.r, ws.u, ws.ctl, ws.mtab, nullptr, nullptr, s),
+            "samu controller");
     LRS_TRY(launch_samu_baseline(variant, p, ws.ctl, ws.mtab, ws.levels, y, y_dtype == SCAN_F32, z_final, s),
             "samu comparison scan");
     return SCAN_OK;

@@ -108,8 +108,11 @@ struct SamuParams {
 // ctl = (E, C, S, d); per mode: the four-float4 constant table mtab;
 // inv_norm (NULL: not written): floats 0-1 = (1/||w_phi||, 1/||w_r||), floats
 // 4-7 = the FP64 squared norms (||w_phi||^2, ||w_r||^2) summed in a fixed order.
+// crec (NULL: not written): [B, C] float4 record of every chunk, (G_c, cos D_c,
+// sin D_c, 0) with G_c = sum E_t and D_c = sum d_t in token order
 hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
-                                  float* u_out, float* ctl, float* mtab, float* inv_norm, hipStream_t s);
+                                  float* u_out, float* ctl, float* mtab, float* inv_norm, float* crec,
+                                  hipStream_t s);
 // The backward replay handles a chunk as K / SAMU_BWD_SUB sub-chunks; the
 // forward replay keeps the state entering each sub-chunk after the first
 // (mid [B, C, samu_mid_states(K), M] complex), so the backward need not run
@@ -129,8 +132,9 @@ hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const flo
 // Grouped path without the compose and expand launches: a workgroup owns one
 // group of ch.G <= SAMU_GROUP_MAX consecutive chunks (processing order) and
 // 64 modes, one wave per chunk.
-//   gsummary: compressed summaries as launch_samu_summary, plus U_g of every
-//             group composed in LDS -> gsum [B, NG, M] (A, B) complex pairs;
+//   gsummary: the B parts of the compressed summaries, with the chunk
+//             records the controller wrote (chunk_rec, read only), plus U_g
+//             of every group composed in LDS -> gsum [B, NG, M] (A, B) pairs;
 //   greplay:  entry state of every chunk from the state entering its group
 //             (gstate [B, NG, M] complex, or with one group the initial
 //             state [B, M] / NULL) and the group's earlier summaries, in
@@ -140,7 +144,7 @@ hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const flo
 //             chunk), carries formed in LDS, then the backward replay.
 constexpr int SAMU_GROUP_MAX = 16;
 hipError_t launch_samu_gsummary(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
-                                const void* drive, bool reverse, float* summ, float* chunk_rec, float* gsum,
+                                const void* drive, bool reverse, float* summ, const float* chunk_rec, float* gsum,
                                 hipStream_t s);
 hipError_t launch_samu_greplay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
                                const float* summ, const float* chunk_rec, const float* gstate, float* entries,
@@ -151,7 +155,8 @@ hipError_t launch_samu_gbwd_replay(const SamuParams& p, const Chunking& ch, cons
                                    int db_f32, float* dz0, float* tok_part, int n_tiles, float* mode_part,
                                    hipStream_t s);
 // carry_in: [B, C, M] cotangent arriving after each chunk's last token;
-// mode_part: [B, C, M] per-chunk (d nu, d theta) partials
+// mode_part: [B, C, M] per-chunk (d nu, d theta) partials (gbwd_replay:
+// [B, NG, M] per-group sums)
 hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
                                   const float* mtab, const float* entries, const float* mid,
                                   const float* carry_in, const void* dy, void* db, int db_f32, float* dz0,
@@ -162,11 +167,12 @@ int samu_param_columns(int D);
 hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const float* r_sv,
                                const float* u_sv, const float* inv_norm, const float* tok_part, int n_tiles,
                                void* dx_sel, int dx_f32, float* g_part, hipStream_t s);
-// g_part: [n_blk, D+4] token-block partials; mode_part: [B*C, M] chunk partials
+// g_part: [n_blk, D+4] token-block partials; mode_part: [mode_rows, M] partials
+// per chunk (B*C rows) or per group of chunks (B*NG rows, the grouped path)
 // wnorm2: the two FP64 squared direction norms the forward controller kept
 hipError_t launch_samu_params(const SamuParams& p, const Chunking& ch, const double* wnorm2, const float* g_part,
-                              int n_blk, const float* mode_part, float* dw_phi, float* dw_r, float* da_phi,
-                              float* da_r, float* dnu, float* dtheta, hipStream_t s);
+                              int n_blk, const float* mode_part, int mode_rows, float* dw_phi, float* dw_r,
+                              float* da_phi, float* da_r, float* dnu, float* dtheta, hipStream_t s);
 
 // one generation step: z_out = lambda(x_sel) z_in + b, y = z_out (z_in NULL = 0;
 // z_out may be z_in); table (NULL: formed per step) from launch_samu_decode_prepare

@@ -321,14 +321,27 @@ __device__ __forceinline__ void gbwd_body(float4* gdyn, int G, int L, int M, int
         }
     }
     __syncthreads();  // the summary table's LDS becomes the transpose rows
-    if (!valid) return;
     float acc_nu = 0.f, acc_th = 0.f;
-    bwd_body<K, H, F32, false, true, true, (NH > 1)>(lds_w, sctl, k, active, lane, tile, n_tiles, L, M, b, s, kc,
-                                                     row0, mm, dy, db, tok_part, ck, bw, gw, carry, acc_nu, acc_th,
-                                                     stash);
-    if (active) {
-        mode_part[bc * M + m] = make_float2(-acc_nu, acc_th);
-        if (dz0 && c == 0) dz0[(size_t)b * M + m] = make_float2(carry.re, carry.im);
+    if (valid) {
+        bwd_body<K, H, F32, false, true, true, (NH > 1)>(lds_w, sctl, k, active, lane, tile, n_tiles, L, M, b, s,
+                                                         kc, row0, mm, dy, db, tok_part, ck, bw, gw, carry, acc_nu,
+                                                         acc_th, stash);
+        if (active && dz0 && c == 0) dz0[(size_t)b * M + m] = make_float2(carry.re, carry.im);
+    }
+    // the (d nu, d theta) partials of the group's chunks, added in processing
+    // order through the waves' stash slots (free again): one row per group
+    *stash = make_float2(-acc_nu, acc_th);
+    __syncthreads();
+    if (w == 0 && active) {
+        const float2* part = reinterpret_cast<const float2*>(gdyn) + lane;
+        const int n = min(G, C - q * G);
+        float sx = 0.f, sy = 0.f;
+        for (int j = 0; j < n; ++j) {
+            const float2 v = part[j * GB_LANES];
+            sx += v.x;
+            sy += v.y;
+        }
+        mode_part[((size_t)b * NG + q) * M + m] = make_float2(sx, sy);
     }
 }
 
@@ -582,7 +595,8 @@ __global__ __launch_bounds__(1024) void samu_ctl_bwd_kernel(
 
 // ------------------------------------------------ parameter reductions ---
 // One launch sums the token-block partials g_part [n_blk, D+4] (a float2 of
-// phi and r terms per column) and the chunk partials mode_part [B*C, M] (a
+// phi and r terms per column) and the chunk (or group) partials mode_part
+// [mode_rows, M] (a
 // float2 of nu and theta terms per mode) in FP64 and in a fixed order, then
 // forms the parameter gradients.  A workgroup owns PR_ITEMS columns (or
 // modes) and splits the rows over PR_SG thread groups: group sg adds rows
@@ -794,13 +808,13 @@ hipError_t launch_samu_ctl_bwd(const SamuParams& p, const float* p_sv, const flo
 int samu_param_columns(int D) { return D + 4; }
 
 hipError_t launch_samu_params(const SamuParams& p, const Chunking& ch, const double* wnorm2, const float* g_part,
-                              int n_blk, const float* mode_part, float* dw_phi, float* dw_r, float* da_phi,
-                              float* da_r, float* dnu, float* dtheta, hipStream_t s) {
+                              int n_blk, const float* mode_part, int mode_rows, float* dw_phi, float* dw_r,
+                              float* da_phi, float* da_r, float* dnu, float* dtheta, hipStream_t s) {
     const int col_blocks = (int)ceil_div(p.D + 1, PR_ITEMS);
     const int grid = col_blocks + (int)ceil_div(p.M, PR_ITEMS);
     LRS_LAUNCH(K_SAMU_PARAMS, samu_param_kernel, dim3(grid), dim3(PR_THREADS), 0, s, p.D, p.M, col_blocks,
                p.w_phi, p.w_r, p.a_phi, p.a_r, wnorm2, (const float2*)g_part, n_blk, (const float2*)mode_part,
-               ch.B * ch.C, dw_phi, dw_r, da_phi, da_r, dnu, dtheta);
+               mode_rows, dw_phi, dw_r, da_phi, da_r, dnu, dtheta);
     return hipGetLastError();
 }
 

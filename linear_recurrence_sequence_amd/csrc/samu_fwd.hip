@@ -47,16 +47,22 @@ constexpr int CTL_TOK_PER_BLOCK = CTL_WAVES * CTL_TOK;
 constexpr int CTL_SLAB = LRS_CTL_SLAB;  // 512-column slabs loaded together
 
 __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
-    int BL, int D, int M, int K, int K_last, const uint4* __restrict__ x_sel, const float* __restrict__ w_phi,
+    int L, int D, int M, int K, int K_last, int C, const uint4* __restrict__ x_sel, const float* __restrict__ w_phi,
     const float* __restrict__ w_r, const float* __restrict__ a_phi,
     const float* __restrict__ a_r, const float* __restrict__ nu, const float* __restrict__ theta,
     float* __restrict__ p_out, float* __restrict__ r_out, float2* __restrict__ u_out,
-    TokenCtl* __restrict__ ctl, float4* __restrict__ mtab, float* __restrict__ inv_norm) {
+    TokenCtl* __restrict__ ctl, float4* __restrict__ mtab, float* __restrict__ inv_norm,
+    float4* __restrict__ crec) {
     __shared__ float red[2][CTL_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     const int D8 = D >> 3;  // 16-byte words per row
-    const int tok0 = blockIdx.x * CTL_TOK_PER_BLOCK + wave * CTL_TOK;
+    // blocks are aligned to batch rows: block (b, jb) owns tokens
+    // jb * CTL_TOK_PER_BLOCK ... of row b, so each chunk lies in one block
+    const int nbr = (int)ceil_div(L, CTL_TOK_PER_BLOCK);
+    const int b = blockIdx.x / nbr, jb = blockIdx.x - b * nbr;
+    const int t0 = jb * CTL_TOK_PER_BLOCK + wave * CTL_TOK;  // token within the row
+    const int tok0 = b * L + t0;                              // flat token
     float ap[CTL_TOK], ar[CTL_TOK];
 #pragma unroll
     for (int q = 0; q < CTL_TOK; ++q) { ap[q] = 0.f; ar[q] = 0.f; }
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
             const int j = j0 + 64 * sl;
 #pragma unroll
             for (int q = 0; q < CTL_TOK; ++q)
-                xv[sl][q] = (j < D8 && tok0 + q < BL) ? x_sel[(size_t)(tok0 + q) * D8 + j]
+                xv[sl][q] = (j < D8 && t0 + q < L) ? x_sel[(size_t)(tok0 + q) * D8 + j]
                                                       : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
@@ -156,7 +162,8 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     const float bias_phi = w_phi[D], bias_r = w_r[D];
 
     const int tok = tok0 + lane;
-    if (lane < CTL_TOK && tok < BL) {
+    __shared__ float2 sed[CTL_TOK_PER_BLOCK];  // (E, d) of the block's tokens, for the chunk records
+    if (lane < CTL_TOK && t0 + lane < L) {
         // x~ . w^ = (x_sel . w[0:D] + w[D]) / ||w||
         const float u_phi = (up + bias_phi) * inv_phi;
         const float u_r = (ur + bias_r) * inv_r;
@@ -175,6 +182,26 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
         t.S = sd;
         t.d = d;
         ctl[tok] = t;
+        sed[wave * CTL_TOK + lane] = make_float2(t.E, d);
+    }
+    if (crec) {  // uniform over the grid
+        // the record of every chunk in this block: G_c = sum E_t and
+        // D_c = sum d_t in token order, and (cos D_c, sin D_c)
+        __syncthreads();
+        const int nck = CTL_TOK_PER_BLOCK / K;
+        const int tb = jb * CTL_TOK_PER_BLOCK + tid * K;  // the chunk's first token in the row
+        if (tid < nck && tb < L) {
+            const int kc = min(K, L - tb);
+            float G = 0.f, Dd = 0.f;
+            for (int i = 0; i < kc; ++i) {
+                const float2 v = sed[tid * K + i];
+                G += v.x;
+                Dd += v.y;
+            }
+            float sD, cD;
+            sincosf(Dd, &sD, &cD);
+            crec[(size_t)b * C + tb / K] = make_float4(G, cD, sD, 0.f);
+        }
     }
 }
 
@@ -458,7 +485,7 @@ template <int K, bool REV, bool ALLACT>
 __device__ __forceinline__ void gsummary_body(float4* gdyn, int G, int L, int M, int C,
                                               const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
                                               const float4* __restrict__ mtab, float* __restrict__ summ,
-                                              float4* __restrict__ chunk_rec, float4* __restrict__ gsum) {
+                                              const float4* __restrict__ chunk_rec, float4* __restrict__ gsum) {
     float4* comp = gdyn;
     TokenCtl* sctl = reinterpret_cast<TokenCtl*>(gdyn + G * GRP_LANES);
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -479,27 +506,20 @@ __device__ __forceinline__ void gsummary_body(float4* gdyn, int G, int L, int M,
     ModeConst k[1];
     k[0] = load_mode(mtab, mc);
     const float4 ph = mtab[MODE_REC * mc + (c == C - 1 ? 3 : 2)];
+    const float4 rec = chunk_rec[(size_t)b * C + c];  // (G_c, cos D_c, sin D_c), from the controller
     Words<1> wd[K];
     load_chunk_clamped<K, REV>(wd, drive + ((size_t)b * L + s) * M, M, mc, kc);
     if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
     wave_lds_sync();
     cf A = {1.f, 0.f}, Bv[1] = {{0.f, 0.f}};
     if (valid) {
-        // the chunk record: G_c = sum E_t and D_c = sum d_t (the same value
-        // in every lane), once per chunk
-        const float Gc = wave_sum(lane < kc ? tn.x : 0.f);
-        const float Dc = wave_sum(lane < kc ? tn.w : 0.f);
-        float sD, cD;
-        sincosf(Dc, &sD, &cD);
         const int kq = opaque(kc);
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const int i = REV ? K - 1 - j : j;
             if (i < kq) summary_step<1, REV>(k, Bv, sctl[i], wd[i]);
         }
-        const float4 rec = make_float4(Gc, cD, sD, 0.f);
         if (active) reinterpret_cast<float2*>(summ)[((size_t)b * C + c) * M + m] = make_float2(Bv[0].re, Bv[0].im);
-        if (blockIdx.x == 0 && lane == 0) chunk_rec[(size_t)b * C + c] = rec;
         A = chunk_transition<REV>(k[0].kappa, ph, rec);
     }
     group_put(comp, w, lane, A, Bv[0]);
@@ -522,7 +542,7 @@ template <int K, bool REV>
 __global__ __launch_bounds__(GRP_LANES * SAMU_GROUP_MAX) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 samu_gsummary_kernel(int L, int M, int C, int G, const TokenCtl* __restrict__ ctl,
                      const uint32_t* __restrict__ drive, const float4* __restrict__ mtab, float* __restrict__ summ,
-                     float4* __restrict__ chunk_rec, float4* __restrict__ gsum) {
+                     const float4* __restrict__ chunk_rec, float4* __restrict__ gsum) {
     extern __shared__ float4 gdyn[];
     if ((int)(blockIdx.x + 1) * GRP_LANES <= M)  // uniform over the workgroup
         gsummary_body<K, REV, true>(gdyn, G, L, M, C, ctl, drive, mtab, summ, chunk_rec, gsum);
@@ -618,13 +638,14 @@ inline int mode_block(int M, int VM) {
 }  // namespace
 
 hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
-                                  float* u_out, float* ctl, float* mtab, float* inv_norm, hipStream_t s) {
-    const int BL = p.B * p.L;
-    const int grid = (int)ceil_div(BL, CTL_TOK_PER_BLOCK);
+                                  float* u_out, float* ctl, float* mtab, float* inv_norm, float* crec,
+                                  hipStream_t s) {
+    static_assert(CTL_TOK_PER_BLOCK % 32 == 0, "chunks of 16 and 32 tokens must lie in one block");
+    const int grid = p.B * (int)ceil_div(p.L, CTL_TOK_PER_BLOCK);
     const int K_last = p.L - (ch.C - 1) * ch.K;
     LRS_LAUNCH(K_SAMU_CONTROLLER, samu_controller_kernel, dim3(grid), dim3(CTL_THREADS), 0, s,
-               BL, p.D, p.M, ch.K, K_last, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p.nu,
-               p.theta, p_out, r_out, (float2*)u_out, (TokenCtl*)ctl, (float4*)mtab, inv_norm);
+               p.L, p.D, p.M, ch.K, K_last, ch.C, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p.nu,
+               p.theta, p_out, r_out, (float2*)u_out, (TokenCtl*)ctl, (float4*)mtab, inv_norm, (float4*)crec);
     return hipGetLastError();
 }
 
@@ -668,7 +689,7 @@ hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const flo
 static size_t samu_group_lds_bytes(int G, int K) { return (size_t)G * GRP_LANES * sizeof(float4) + (size_t)G * K * sizeof(TokenCtl); }
 
 hipError_t launch_samu_gsummary(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
-                                const void* drive, bool reverse, float* summ, float* chunk_rec, float* gsum,
+                                const void* drive, bool reverse, float* summ, const float* chunk_rec, float* gsum,
                                 hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(p.M, GRP_LANES), ch.NG, ch.B);
     const dim3 block(GRP_LANES * ch.G);
@@ -676,8 +697,8 @@ hipError_t launch_samu_gsummary(const SamuParams& p, const Chunking& ch, const f
     const int id = reverse ? K_SAMU_REV_SUMMARY : K_SAMU_SUMMARY;
 #define GSUM_CASE(KK, RR)                                                                                  \
     LRS_LAUNCH(id, (samu_gsummary_kernel<KK, RR>), grid, block, lds, s, p.L, p.M, ch.C, ch.G,            \
-               (const TokenCtl*)ctl, (const uint32_t*)drive, (const float4*)mtab, summ, (float4*)chunk_rec, \
-               (float4*)gsum)
+               (const TokenCtl*)ctl, (const uint32_t*)drive, (const float4*)mtab, summ,                    \
+               (const float4*)chunk_rec, (float4*)gsum)
     if (ch.K == 32) {
         if (reverse) GSUM_CASE(32, true); else GSUM_CASE(32, false);
     } else {

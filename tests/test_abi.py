@@ -75,9 +75,10 @@ def test_saved_and_workspace_sizes():
     sv = scan.samu_scan_saved_bytes(B, L, D, K)
     # p, r, (u_phi, u_r), per-token (E, C, S, d) record, mode table (four
     # float4 per mode), chunk entry states, and the state entering the second
-    # 16-token half of every 32-token chunk
-    need = B * L * (4 + 4 + 8 + 16) + M * 64 + B * C * M * 8 + B * C * M * 8
-    assert need <= sv < need + 8 * 256
+    # 16-token half of every 32-token chunk, and one (G_c, cos D_c, sin D_c)
+    # record per chunk
+    need = B * L * (4 + 4 + 8 + 16) + M * 64 + B * C * M * 8 + B * C * M * 8 + B * C * 16
+    assert need <= sv < need + 9 * 256
     # forward workspace: compressed chunk summaries (8 B per mode plus a 16 B
     # record per chunk), group summaries (16 B per mode) and group entry
     # states (8 B per mode)
