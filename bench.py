@@ -129,7 +129,6 @@ def samu_kernel_bytes(B, L, D, K, G):
             "samu_bwd_replay": (tab["samu_bwd_replay"][0],
                                 2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BMID + 8 * BCM + 16 * BC
                                 + 8 * NGM + 2 * BLD + 8 * B * n_tiles * L + 8 * NGM),
-            "samu_params": (tab["samu_params"][0] - 8 * BCM + 8 * NGM, tab["samu_params"][1] - 8 * BCM + 8 * NGM),
         })
     tab.update({
         # x_sel, p, r, per-tile partials -> dx_sel, per-block direction partials
@@ -139,6 +138,10 @@ def samu_kernel_bytes(B, L, D, K, G):
         "samu_params": (8 * n_blk * (D + 1) + 8 * BCM + 8 * (D + 1) + 8 * (D + 1) + 8 * M,
                         8 * n_blk * (D + 4) + 8 * BCM + 8 * (D + 1) + 16 + 8 * (D + 1) + 8 + 8 * M),
     })
+    if effective_groups(L, K, G) <= 16:
+        # the grouped backward writes one (d nu, d theta) row per group
+        dif = 8 * BCM - 8 * B * NG * M
+        tab["samu_params"] = (tab["samu_params"][0] - dif, tab["samu_params"][1] - dif)
     return tab
 
 
