@@ -10,11 +10,15 @@ stdout; progress goes to stderr.
 
 value = algorithmic floor bytes of the mixer F+B (16 B per token x real
 channel: x_sel, b, y forward; dy, b, x_sel, dx_sel, db backward) / F+B time,
-in GB/s.  The roofline object reports the dominant kernel's algorithmic bytes
+in GB/s.  The timed steps are the K steps captured once into a HIP graph and
+replayed (median of three replays, each exactly K steps between device
+synchronizations; the replayed gradients are checked bit for bit against an
+eager step's); ms_per_step_eager is the same K steps launched one call at a
+time.  The roofline object reports the dominant kernel's algorithmic bytes
 per launch over its average launch time, timed with HIP events recorded by the
-library around every launch on the bench stream, over a second run of the
-same timed steps (the event records themselves cost a few microseconds per
-launch, so ms_per_step comes from the first run, without them).
+library around every launch on the bench stream, over a separate eager run of
+the same steps (the event records themselves cost a few microseconds per
+launch, so no step time comes from that run).
 
 Besides the headline, the line carries every other workload of the pages'
 measurement plan, each F+B timed the same way with per-kernel rates:
@@ -325,6 +329,38 @@ class Timer:
         prof = scan.scan_profile_collect()
         return e0.elapsed_time(e1) / steps, prof
 
+    def graph(self, step, steps, warmup, repeats=3):
+        """The same `steps` steps captured once into a HIP graph, then
+        replayed `repeats` times; each replay (exactly `steps` steps) is
+        timed between device synchronizations.  Returns the median ms per
+        step and every replay's.  No library call allocates or clears device
+        memory, so the whole step captures."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(max(1, warmup)):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                step()
+        g.replay()  # untimed
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        runs = []
+        for _ in range(repeats):
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1) / steps)
+        del g
+        return statistics.median(runs), runs
+
 
 def _dev(torch):
     def dev(a):
@@ -421,20 +457,24 @@ STREAM_KERNELS = ("samu_controller", "samu_chunk_summary", "samu_replay", "samu_
 
 
 def run_case(timer, kind, step, B, L, D, K, G, steps, warmup, resets=False, repeats=3):
-    """F+B of one workload: the median of `repeats` timed runs of `steps`
-    steps (after `warmup` steps), then one run with per-launch events."""
+    """F+B of one workload: the median of `repeats` replays of a HIP graph
+    holding `steps` steps (ms_per_step), the median of `repeats` eager runs
+    of `steps` steps (ms_per_step_eager), then one eager run with per-launch
+    events for the kernel rates."""
     runs = []
     for r in range(repeats):
         t, _ = timer(step, steps, warmup if r == 0 else 1, False)
         runs.append(t)
-    ms = statistics.median(runs)
+    ms_eager = statistics.median(runs)
+    ms, gruns = timer.graph(step, steps, 1, repeats)
     _, prof = timer(step, steps, 1, True)
     floor = (FLOOR_SAMU if kind == "samu" else FLOOR_RGLRU) * B * L * D
     table = samu_kernel_bytes(B, L, D, K, G) if kind == "samu" else rglru_kernel_bytes(B, L, D, K, G, resets)
     ks = kernel_rates(prof, steps, table)
     row = {"B": B, "L": L, "D": D, "K": K,
            "G": effective_groups(L, K, G, 8 if kind == "samu" else 16),
-           "ms_per_step": round(ms, 4), "ms_runs": [round(t, 4) for t in runs],
+           "ms_per_step": round(ms, 4), "ms_runs": [round(t, 4) for t in gruns],
+           "ms_per_step_eager": round(ms_eager, 4), "ms_runs_eager": [round(t, 4) for t in runs],
            "token_channels_per_s": round(B * L * D / (ms * 1e-3), 1),
            "floor_gbs": round(floor / (ms * 1e-3) / 1e9, 1),
            "floor_pct_of_peak": round(100 * floor / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -563,8 +603,8 @@ def main():
     d, out = sb["d"], sb["out"]
 
     log(f"[bench] SAMU F+B: warmup {args.warmup}, timing {args.steps} steps")
-    ms, _ = timed(samu_step, args.steps, args.warmup, False)
-    log(f"[bench] SAMU F+B {ms:.4f} ms/step")
+    ms_eager, _ = timed(samu_step, args.steps, args.warmup, False)
+    log(f"[bench] SAMU F+B {ms_eager:.4f} ms/step, eager launches")
     # the same steps again with an event pair around every kernel launch
     ms_ev, prof = timed(samu_step, args.steps, 1, True)
     log(f"[bench] SAMU F+B {ms_ev:.4f} ms/step with per-kernel events")
@@ -572,31 +612,19 @@ def main():
     for name, (tot, cnt) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
         log(f"    {name:24s} {tot / cnt * 1e3:9.2f} us/launch  x{cnt // args.steps}/step")
 
-    ms_graph, graph_equal = None, None
+    ms, graph_runs, graph_equal = ms_eager, None, None
     if not args.no_graph:
-        # the same step replayed from a captured HIP graph (8 steps per graph; no
-        # library call allocates or clears memory, so the whole pass captures);
-        # the replayed gradients must equal an eager step's bit for bit
-        log("[bench] SAMU F+B replayed from a HIP graph")
+        # the timed steps: the same K steps captured into one HIP graph and
+        # replayed (three replays, median); the gradients left by the replays
+        # must equal an eager step's bit for bit
         samu_step()
         torch.cuda.synchronize()
         db_ref = out["db"].clone()
-        gs = torch.cuda.Stream()
-        gs.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(gs):
-            for _ in range(2):
-                samu_step()
-        torch.cuda.current_stream().wait_stream(gs)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(8):
-                samu_step()
-        gms, _ = timed(graph.replay, max(2, args.steps // 8), 1, False)
-        ms_graph = round(gms / 8, 4)
+        ms, graph_runs = timed.graph(samu_step, args.steps, args.warmup)
         graph_equal = bool(torch.equal(out["db"], db_ref))
-        del graph
-        log(f"[bench] SAMU F+B {ms_graph:.4f} ms/step from a graph (replayed db equal to eager: {graph_equal})")
+        del db_ref
+        log(f"[bench] SAMU F+B {ms:.4f} ms/step replayed from a graph of {args.steps} steps "
+            f"(runs {[round(t, 4) for t in graph_runs]}; db equal to eager: {graph_equal})")
 
     floor_bytes = FLOOR_SAMU * B * L * D
     value = floor_bytes / (ms * 1e-3) / 1e9
@@ -624,8 +652,7 @@ def main():
             for RG in (0, 8, 16, 32, 64):
                 step, rb = rglru_case(torch, scan, inputs, B, L, D, RK, RG, 3003, 0.1, d=rd)
                 rd = rb["d"]
-                t = statistics.median([timed(step, args.steps, args.warmup if r == 0 else 1, False)[0]
-                                       for r in range(3)])
+                t = timed.graph(step, args.steps, args.warmup)[0]
                 geff = effective_groups(L, RK, RG, 16)
                 key = f"K{RK}_G{geff}"
                 if key in variants:
@@ -655,7 +682,8 @@ def main():
             scan.rglru_gate_proj_bwd(rd["x"], prm["w_x"], prm["w_a"], rout["dlx"], rout["dla"], rout["dx"],
                                      dx_out=rout["dx"], workspace=pws)
 
-        layer_ms, _ = timed(layer_step, args.steps, args.warmup, False)
+        layer_ms_eager, _ = timed(layer_step, args.steps, args.warmup, False)
+        layer_ms, _ = timed.graph(layer_step, args.steps, 1)
         _, lprof = timed(layer_step, args.steps, 1, True)
         BLD = B * L * D
         pbytes = {"gate_projection": 6 * BLD, "gate_projection_dx": 8 * BLD, "gate_projection_dw": 6 * BLD}
@@ -670,9 +698,12 @@ def main():
         rg = {"ms_per_step": rg_ms, "K": RK, "G": effective_groups(L, RK, RG, 16),
               "chosen_as": "fastest of the K x G sweep below",
               "k_g_sweep_ms": variants, "kernels": rg_row["kernels"],
-              "layer_ms_per_step": round(layer_ms, 4), "gate_projection": proj,
+              "ms_per_step_eager": rg_row["ms_per_step_eager"],
+              "layer_ms_per_step": round(layer_ms, 4), "layer_ms_per_step_eager": round(layer_ms_eager, 4),
+              "gate_projection": proj,
               "gbs_floor": round(FLOOR_RGLRU * B * L * D / (rg_ms * 1e-3) / 1e9, 1),
-              "samu_fb_time_reduction": round((rg_ms - ms) / rg_ms, 4)}
+              "samu_fb_time_reduction": round((rg_ms - ms) / rg_ms, 4),
+              "samu_fb_time_reduction_eager": round(1 - ms_eager / rg_row["ms_per_step_eager"], 4)}
         log(f"[bench] RG-LRU F+B {rg_ms:.4f} ms/step (K={RK}, G={rg['G']}); SAMU reduction "
             f"{(rg_ms - ms) / rg_ms:.1%}; with gate projections {layer_ms:.4f} ms/step {proj}")
 
@@ -794,7 +825,9 @@ def main():
                             "forward": scan.samu_scan_workspace_bytes(B, L, D, K, G, False),
                             "backward": scan.samu_scan_workspace_bytes(B, L, D, K, G, True),
                             "pages_prefix_scratch_formula": scan.scan_prefix_scratch_bytes(B, L, D, K, G)},
-        "ms_per_step_graph": ms_graph, "graph_replay_equal": graph_equal,
+        "timing": "HIP graph replay of the K steps" if graph_runs else "eager launches",
+        "ms_per_step_runs": [round(t, 4) for t in graph_runs] if graph_runs else None,
+        "ms_per_step_eager": round(ms_eager, 4), "graph_replay_equal": graph_equal,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": meth_bytes,
