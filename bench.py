@@ -114,21 +114,30 @@ def samu_kernel_bytes(B, L, D, K, G):
                             + 8 * B * n_tiles * L + 8 * BCM),
     }
     if effective_groups(L, K, G) <= 16:
-        # the grouped path: the summary kernels also write U_g per group and
-        # mode, the replays read the group's summaries and the state entering
-        # the group instead of per-chunk entry states or carries, and the
-        # forward replay writes the entry states the backward reads
+        # the grouped path: the forward is one single-pass kernel; the reverse
+        # summary also writes U_g per group and mode, and the backward replay
+        # reads the group's summaries and the carry entering the group
+        # instead of per-chunk carries
         NGM = B * NG * M
+        G_ = effective_groups(L, K, G)
+        for k in ("samu_chunk_summary", "samu_replay", "prefix_group_compose", "prefix_chunk_entries"):
+            tab.pop(k, None)
         tab.update({
             # the controller also writes one (G_c, e^{i D_c}) record per chunk
-            "samu_controller": (tab["samu_controller"][0], tab["samu_controller"][1] + 16 * BC),
-            "samu_chunk_summary": (tab["samu_chunk_summary"][0],
-                                   2 * BLD + 16 * BL + 32 * M + 16 * BC + 8 * BCM + 16 * NGM),
+            # and clears the single-pass forward's hand-off words (48 B per
+            # group and mode)
+            "samu_controller": (tab["samu_controller"][0], tab["samu_controller"][1] + 16 * BC + 48 * NGM),
             "samu_reverse_summary": (tab["samu_reverse_summary"][0],
                                      2 * BLD + 16 * BL + 32 * M + 16 * BC + 8 * BCM + 16 * NGM),
-            "samu_replay": (tab["samu_replay"][0],
-                            2 * BLD + 16 * BL + 32 * M + 8 * BCM + 16 * BC + 8 * NGM + 2 * BLD + 8 * B * M
-                            + 8 * BMID + 8 * BCM),
+            # the single-pass forward: b read once, y and the entry states
+            # written; the design adds the token and chunk records, the mode
+            # table, the mid-chunk states, and the hand-off words (U_g or the
+            # leaving state published per group and mode, and what each
+            # group reads of its segment's earlier groups: on average
+            # (G - 1) / 2 maps of 32 B and one 16 B state)
+            "samu_forward_scan": (2 * BLD + 12 * BL + 8 * M + 2 * BLD + 8 * B * M + 8 * BCM,
+                                  2 * BLD + 16 * BL + 64 * M + 16 * BC + 2 * BLD + 8 * B * M + 8 * BMID
+                                  + 8 * BCM + 32 * NGM + (16 * (G_ - 1) + 16) * NGM),
             # (d nu, d theta) summed over each group's chunks: one row per group
             "samu_bwd_replay": (tab["samu_bwd_replay"][0],
                                 2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BMID + 8 * BCM + 16 * BC
@@ -451,7 +460,7 @@ def kernel_rates(prof, steps, table):
 
 # prefix launches stream only summaries (a few MB); the bar applies to the
 # kernels that stream the [B, L, D] tensors
-STREAM_KERNELS = ("samu_controller", "samu_chunk_summary", "samu_replay", "samu_reverse_summary",
+STREAM_KERNELS = ("samu_controller", "samu_chunk_summary", "samu_replay", "samu_forward_scan", "samu_reverse_summary",
                   "samu_bwd_replay", "samu_controller_bwd", "rglru_chunk_summary", "rglru_replay",
                   "rglru_reverse_summary", "rglru_bwd_replay")
 

@@ -54,7 +54,7 @@ static const char* const kKernelNames[K_NUM_KERNELS] = {
     "samu_controller_bwd", "samu_params", "rglru_chunk_summary", "rglru_replay",
     "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha", "samu_decode",
     "baseline_sequential", "baseline_associative", "gate_projection", "gate_projection_dx",
-    "gate_projection_dw", "gate_projection_reduce"};
+    "gate_projection_dw", "gate_projection_reduce", "samu_forward_scan"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 
@@ -122,7 +122,7 @@ static bool chunking(int B, int L, int K, int G, int min_group, Chunking* ch, in
 static constexpr int kSamuMinGroup = 8;      // see chunking()
 static constexpr int kRglruMinGroup = 16;
 // SAMU with G == 0: groups of kSamuGroup chunks on the grouped path (one
-// workgroup per group; see launch_samu_gsummary), which any G up to
+// workgroup per group; see launch_samu_gscan), which any G up to
 // SAMU_GROUP_MAX takes; longer groups take the three-kernel prefix.
 static constexpr int kSamuGroup = 8;
 static bool samu_fused(const Chunking& ch) { return ch.G <= SAMU_GROUP_MAX; }
@@ -147,15 +147,24 @@ static SamuSaved samu_saved_layout(void* base, const Chunking& ch, int M, size_t
     return s;
 }
 
+// The grouped path needs only the single-pass forward's hand-off words; the
+// three-kernel prefix keeps chunk summaries, records and group summaries.
 struct SamuFwdWs {
     float *summ, *chunk, *gsum;
+    void* pub;
+    size_t pub_bytes;
 };
 static SamuFwdWs samu_fwd_ws_layout(void* base, const Chunking& ch, int M, size_t* bytes) {
     Carver cv(base);
-    SamuFwdWs w;
-    w.summ = cv.take<float>((size_t)ch.B * ch.C * M * 2);
-    w.chunk = cv.take<float>((size_t)ch.B * ch.C * 4);
-    w.gsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
+    SamuFwdWs w{};
+    if (samu_fused(ch)) {
+        w.pub_bytes = samu_gscan_pub_bytes(ch, M);
+        w.pub = cv.take<uint64_t>(w.pub_bytes / sizeof(uint64_t));
+    } else {
+        w.summ = cv.take<float>((size_t)ch.B * ch.C * M * 2);
+        w.chunk = cv.take<float>((size_t)ch.B * ch.C * 4);
+        w.gsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
+    }
     if (bytes) *bytes = cv.off;
     return w;
 }
@@ -345,22 +354,16 @@ scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
     SamuSaved sv = samu_saved_layout(saved, ch, M, nullptr);
     SamuFwdWs ws = samu_fwd_ws_layout(workspace, ch, M, nullptr);
-    LRS_TRY(launch_samu_controller(p, ch, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, sv.inv_norm, sv.crec, s),
+    // the controller also clears the single-pass forward's hand-off words
+    LRS_TRY(launch_samu_controller(p, ch, sv.p, sv.r, sv.u, sv.ctl, sv.mtab, sv.inv_norm, sv.crec, ws.pub,
+                                   ws.pub_bytes, s),
             "samu controller");
     if (samu_fused(ch)) {
-        // summaries with U_g composed per group, the scan over groups (when
-        // there is more than one), and the replay forming its chunk entries
-        LRS_TRY(launch_samu_gsummary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, sv.crec, ws.gsum, s),
-                "samu chunk summary");
-        const float* gstate = z0;
-        if (ch.NG > 1) {
-            float* gentry = ws.gsum + (size_t)ch.B * ch.NG * M * 4;
-            LRS_TRY(launch_group_scan(2, ch, M, ws.gsum, z0, gentry, s), "samu group scan");
-            gstate = gentry;
-        }
-        LRS_TRY(launch_samu_greplay(p, ch, sv.ctl, sv.mtab, ws.summ, sv.crec, gstate, sv.entries, sv.mid, y,
-                                    y_dtype == SCAN_F32, z_final, s),
-                "samu replay");
+        // summaries, U_g, the look-back over earlier groups and the replay,
+        // in one launch
+        LRS_TRY(launch_samu_gscan(p, ch, sv.ctl, sv.mtab, sv.crec, ws.pub, sv.entries, sv.mid, y,
+                                  y_dtype == SCAN_F32, z_final, s),
+                "samu forward scan");
         return SCAN_OK;
     }
     LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, b, false, ws.summ, ws.chunk, s), "samu chunk summary");
@@ -516,7 +519,7 @@ scan_status samu_scan_baseline_fwd(int variant, int B, int L, int D, const void*
     chunking(B, L, 32, 0, kSamuMinGroup, &ch);  // the controller's chunk phasors are not used here
     SamuParams p{B, L, D, M, x_sel, b, w_phi, w_r, a_phi, a_r, nu, theta, z0};
     SamuBaseWs ws = samu_base_layout(workspace, B, L, M, variant, nullptr);
-    LRS_TRY(launch_samu_controller(p, ch, ws.p, ws.r, ws.u, ws.ctl, ws.mtab, nullptr, nullptr, s),
+    LRS_TRY(launch_samu_controller(p, ch, ws.p, ws.r, ws.u, ws.ctl, ws.mtab, nullptr, nullptr, nullptr, 0, s),
             "samu controller");
     LRS_TRY(launch_samu_baseline(variant, p, ws.ctl, ws.mtab, ws.levels, y, y_dtype == SCAN_F32, z_final, s),
             "samu comparison scan");

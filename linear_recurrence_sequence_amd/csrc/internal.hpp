@@ -37,6 +37,7 @@ enum KernelId {
     K_GATE_PROJ_DX,
     K_GATE_PROJ_DW,
     K_GATE_PROJ_REDUCE,
+    K_SAMU_FWD_SCAN,
     K_NUM_KERNELS
 };
 
@@ -110,9 +111,11 @@ struct SamuParams {
 // 4-7 = the FP64 squared norms (||w_phi||^2, ||w_r||^2) summed in a fixed order.
 // crec (NULL: not written): [B, C] float4 record of every chunk, (G_c, cos D_c,
 // sin D_c, 0) with G_c = sum E_t and D_c = sum d_t in token order
+// crec: per-chunk records (NULL: not written); clear: clear_bytes (a multiple
+// of 16) zeroed after the controller's own work (NULL: none)
 hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
                                   float* u_out, float* ctl, float* mtab, float* inv_norm, float* crec,
-                                  hipStream_t s);
+                                  void* clear, size_t clear_bytes, hipStream_t s);
 // The backward replay handles a chunk as K / SAMU_BWD_SUB sub-chunks; the
 // forward replay keeps the state entering each sub-chunk after the first
 // (mid [B, C, samu_mid_states(K), M] complex), so the backward need not run
@@ -132,23 +135,25 @@ hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const flo
 // Grouped path without the compose and expand launches: a workgroup owns one
 // group of ch.G <= SAMU_GROUP_MAX consecutive chunks (processing order) and
 // 64 modes, one wave per chunk.
-//   gsummary: the B parts of the compressed summaries, with the chunk
-//             records the controller wrote (chunk_rec, read only), plus U_g
-//             of every group composed in LDS -> gsum [B, NG, M] (A, B) pairs;
-//   greplay:  entry state of every chunk from the state entering its group
-//             (gstate [B, NG, M] complex, or with one group the initial
-//             state [B, M] / NULL) and the group's earlier summaries, in
-//             LDS; then the replay, which also writes the entry states
-//             [B, C, M] the backward reads;
-//   gbwd_replay: the same for the adjoint (groups aligned from the last
-//             chunk), carries formed in LDS, then the backward replay.
+//   gscan:    the whole forward after the controller in one launch (chunk
+//             summaries, U_g, the state entering the group from the groups
+//             before it, the replay, which also writes the entry states
+//             [B, C, M] the backward reads); pub: samu_gscan_pub_bytes() of
+//             hand-off words, cleared to zero by the controller launch before
+//             it (its `clear` argument);
+//   gsummary: the reverse summaries of dy (B parts, with the chunk records
+//             the controller wrote, read only) plus the reverse U_g of every
+//             group composed in LDS -> gsum [B, NG, M] (A, B) pairs;
+//   gbwd_replay: carries formed in LDS from the carry entering the group,
+//             then the backward replay (groups aligned from the last chunk).
 constexpr int SAMU_GROUP_MAX = 16;
+size_t samu_gscan_pub_bytes(const Chunking& ch, int M);
+hipError_t launch_samu_gscan(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                             const float* chunk_rec, void* pub, float* entries, float* mid, void* y, int y_f32,
+                             float* z_final, hipStream_t s);
 hipError_t launch_samu_gsummary(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
                                 const void* drive, bool reverse, float* summ, const float* chunk_rec, float* gsum,
                                 hipStream_t s);
-hipError_t launch_samu_greplay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
-                               const float* summ, const float* chunk_rec, const float* gstate, float* entries,
-                               float* mid, void* y, int y_f32, float* z_final, hipStream_t s);
 hipError_t launch_samu_gbwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
                                    const float* entries, const float* mid, const float* rsumm,
                                    const float* rchunk, const float* gcarry, const void* dy, void* db,

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     const float* __restrict__ a_r, const float* __restrict__ nu, const float* __restrict__ theta,
     float* __restrict__ p_out, float* __restrict__ r_out, float2* __restrict__ u_out,
     TokenCtl* __restrict__ ctl, float4* __restrict__ mtab, float* __restrict__ inv_norm,
-    float4* __restrict__ crec) {
+    float4* __restrict__ crec, uint4* __restrict__ clear, size_t n_clear) {
     __shared__ float red[2][CTL_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -203,6 +203,9 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
             crec[(size_t)b * C + tb / K] = make_float4(G, cD, sD, 0.f);
         }
     }
+    // the single-pass forward's hand-off words start invalid (zero)
+    for (size_t i = (size_t)blockIdx.x * CTL_THREADS + tid; i < n_clear; i += (size_t)gridDim.x * CTL_THREADS)
+        clear[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ----------------------------------------- chunk and reverse summaries ---
@@ -550,16 +553,98 @@ samu_gsummary_kernel(int L, int M, int C, int G, const TokenCtl* __restrict__ ct
         gsummary_body<K, REV, false>(gdyn, G, L, M, C, ctl, drive, mtab, summ, chunk_rec, gsum);
 }
 
+// ----------------------------------------- single-pass grouped forward ---
+// The whole scan after the controller in one launch: each workgroup (one
+// group of G chunks x 64 modes, as above) reads its drive words once, forms
+// its chunks' summaries and U_q in LDS, learns the state entering its group
+// from the groups before it, and replays its chunks from the words still in
+// registers.  Chunk summaries, group summaries and group entry states never
+// go to memory as tensors, and b is read once instead of twice.
+//
+// Fixed order of evaluation.  The groups form segments of G consecutive
+// groups.  The last group of a segment publishes the state leaving it (its
+// chunks' maps applied in order to the state entering it); every other group
+// publishes its U_q = (A_q, B_q).  Group q takes the state leaving the
+// previous segment (z0 for the first) and applies the published U of the
+// segment's groups before it, oldest first: at most G - 1 maps and one
+// state, read by G waves at once.  Which words a group reads and the order it
+// applies them in depend only on q and G, never on timing, so the result is
+// bitwise the same on every run.  The only serial dependence across
+// workgroups is the chain of segment states, one link per G groups.
+//
+// Hand-off.  Each published value is its own 64-bit word (1 << 32 | float
+// bits), written and read with relaxed device-scope atomics; the controller
+// clears the area to zero before every forward, so a word is valid exactly
+// when its high half is 1.  A word is never torn, so a reader that sees
+// every word it needs valid holds consistent values, and no fence is needed
+// between words.
+//
+// Progress.  Workgroups are dispatched in grid order (mode tiles fastest,
+// then groups), and a workgroup only waits for words of lower-numbered
+// groups of its own row and mode tile, which were dispatched before it and
+// never wait for it, so every wait ends.  Each wait is nevertheless bounded
+// (SCAN_SPIN_MAX polls).
+constexpr int SCAN_SPIN_MAX = 1 << 14;
+constexpr int SCAN_PUB_WORDS = 6;  // A.re, A.im, B.re, B.im of U_q, then the leaving state
+
+// Word `i` of a group for one lane: `grp` is the group's (wave-uniform) first
+// word, `off` the lane's byte offset (mode * 8) and `Mb` = M * 8, so the
+// address is a uniform base plus a 32-bit lane offset.
+__device__ __forceinline__ uint64_t* pub_word(const uint64_t* grp, int i, uint32_t Mb, uint32_t off) {
+    return reinterpret_cast<uint64_t*>(const_cast<char*>(reinterpret_cast<const char*>(grp)) +
+                                       (size_t)i * Mb + off);
+}
+__device__ __forceinline__ uint64_t pub_load(const uint64_t* grp, int i, uint32_t Mb, uint32_t off) {
+    return __hip_atomic_load(pub_word(grp, i, Mb, off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void pub_store(uint64_t* grp, int i, uint32_t Mb, uint32_t off, float v) {
+    __hip_atomic_store(pub_word(grp, i, Mb, off), (uint64_t(1) << 32) | (uint64_t)__float_as_uint(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool pub_ok(uint64_t w) { return (uint32_t)(w >> 32) == 1u; }
+__device__ __forceinline__ float pub_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// Words [i0, i0 + N) of an earlier group for this lane's mode, once all are
+// published: U as (A.re, A.im, B.re, B.im) for i0 = 0, N = 4, or the leaving
+// state as (z.re, z.im, 0, 0) for i0 = 4, N = 2.
+template <int N>
+__device__ __forceinline__ float4 wait_words(const uint64_t* grp, int i0, uint32_t Mb, uint32_t off) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    bool ok = false;
+    for (int it = 0; it < SCAN_SPIN_MAX; ++it) {
+        if (!ok) {
+            // the lane offset afresh each poll: addresses kept across the
+            // loop would cost two registers each
+            const uint32_t o = opaque_v(off);
+            uint64_t wv[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) wv[i] = pub_load(grp, i0 + i, Mb, o);
+            bool all = true;
+#pragma unroll
+            for (int i = 0; i < N; ++i) all = all && pub_ok(wv[i]);
+            if (all) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) v[i] = pub_val(wv[i]);
+                ok = true;
+            }
+        }
+        if (__all(ok)) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 template <int K, bool F32, bool ALLACT>
-__device__ __forceinline__ void greplay_body(float4* gdyn, int G, int L, int M, int C, int per_group,
-                                             const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
-                                             const float4* __restrict__ mtab, const float2* __restrict__ summ,
-                                             const float4* __restrict__ chunk_rec, const float2* __restrict__ gstate,
-                                             float2* __restrict__ entries, float* __restrict__ mid,
-                                             void* __restrict__ y, float* __restrict__ z_final) {
+__device__ __forceinline__ void gscan_body(float4* gdyn, int G, int L, int M, int C,
+                                           const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
+                                           const float4* __restrict__ mtab, const float4* __restrict__ chunk_rec,
+                                           const float2* __restrict__ z0, uint64_t* __restrict__ pub,
+                                           float2* __restrict__ entries, float* __restrict__ mid,
+                                           void* __restrict__ y, float* __restrict__ z_final) {
     constexpr int NMID = samu_mid_states(K);
-    float4* comp = gdyn;
-    TokenCtl* sctl = reinterpret_cast<TokenCtl*>(gdyn + G * GRP_LANES);
+    float4* comp = gdyn;                   // [G][64] (A_c, B_c) of the group's chunks
+    float4* look = gdyn + G * GRP_LANES;   // [G][64] what each wave read of the earlier groups
+    TokenCtl* sctl = reinterpret_cast<TokenCtl*>(gdyn + 2 * G * GRP_LANES);
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int q = blockIdx.y, b = blockIdx.z, NG = gridDim.y;
     const int pc = q * G + w;
@@ -573,35 +658,100 @@ __device__ __forceinline__ void greplay_body(float4* gdyn, int G, int L, int M, 
     const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform
     sctl += w * K;
 
-    // requests: the token controls, the mode constants, this chunk's
-    // summary, the state entering the group, then the chunk's drive words
+    // requests: the token controls, the mode constants, the chunk record,
+    // then the chunk's drive words, held until the replay
     float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lane < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + lane];
-    const ModeConst k = load_mode(mtab, mc);
+    ModeConst k[1];
+    k[0] = load_mode(mtab, mc);
     const float4 ph = mtab[MODE_REC * mc + (c == C - 1 ? 3 : 2)];
     const float4 rec = chunk_rec[(size_t)b * C + c];
-    const float2 bp = summ[((size_t)b * C + c) * M + mc];
-    float2 g0 = make_float2(0.f, 0.f);
-    if (gstate) g0 = per_group ? gstate[((size_t)b * NG + q) * M + mc] : gstate[(size_t)b * M + mc];
     Words<1> wd[K];
     load_chunk_clamped<K, false>(wd, drive + row0, M, mc, kc);
     if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
-    group_put(comp, w, lane, chunk_transition<false>(k.kappa, ph, rec), {bp.x, bp.y});
+    wave_lds_sync();
+    const int kq = opaque(kc);
+    cf A = {1.f, 0.f}, Bv[1] = {{0.f, 0.f}};
+    if (valid) {
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+            if (i < kq) summary_step<1, false>(k, Bv, sctl[i], wd[i]);
+        A = chunk_transition<false>(k[0].kappa, ph, rec);
+    }
+    group_put(comp, w, lane, A, Bv[0]);
     __syncthreads();
+
+    const uint32_t Mb = (uint32_t)M * 8u, moff = (uint32_t)mc * 8u;
+    uint64_t* mine = pub + ((size_t)b * NG + q) * SCAN_PUB_WORDS * M;  // wave-uniform
+    const int nprev = q % G;                          // earlier groups of this segment
+    const bool seg_last = nprev == G - 1 || q == NG - 1;
+    if (w == 0 && active && q + 1 < NG && !seg_last) {
+        // U_q = S_{n-1} o ... o S_0 (the right operand first), published at once
+        cf ua = {1.f, 0.f}, ub = {0.f, 0.f};
+        for (int j = 0; j < G; ++j) {  // all G chunks: a group short of G chunks is the last one
+            const float4 f = comp[j * GRP_LANES + lane];
+            ub = cfma({f.x, f.y}, ub, {f.z, f.w});
+            ua = cmul({f.x, f.y}, ua);
+        }
+        pub_store(mine, 0, Mb, moff, ua.re);
+        pub_store(mine, 1, Mb, moff, ua.im);
+        pub_store(mine, 2, Mb, moff, ub.re);
+        pub_store(mine, 3, Mb, moff, ub.im);
+    }
+    // wave w < nprev reads U of group q-1-w, wave nprev the state entering
+    // the segment
+    if (w < nprev) {
+        look[w * GRP_LANES + lane] =
+            wait_words<4>(pub + ((size_t)b * NG + q - 1 - w) * SCAN_PUB_WORDS * M, 0, Mb, moff);
+    } else if (w == nprev) {
+        float4 zs = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q - nprev > 0)
+            zs = wait_words<2>(pub + ((size_t)b * NG + q - nprev - 1) * SCAN_PUB_WORDS * M, 4, Mb, moff);
+        else if (z0)
+            zs = make_float4(z0[(size_t)b * M + mc].x, z0[(size_t)b * M + mc].y, 0.f, 0.f);
+        look[w * GRP_LANES + lane] = zs;
+    }
+    __syncthreads();
+    if (w == 0) {
+        const float4 zs = look[nprev * GRP_LANES + lane];
+        cf z = {zs.x, zs.y};
+        for (int v = nprev - 1; v >= 0; --v) {  // oldest first
+            const float4 f = look[v * GRP_LANES + lane];
+            z = cfma({f.x, f.y}, z, {f.z, f.w});
+        }
+        if (active && q + 1 < NG && seg_last) {
+            // the state leaving the group, for the next segment: this
+            // group's chunks applied in order, as in the chain
+            cf zo = z;
+            for (int j = 0; j < G; ++j) {
+                const float4 f = comp[j * GRP_LANES + lane];
+                zo = cfma({f.x, f.y}, zo, {f.z, f.w});
+            }
+            pub_store(mine, 4, Mb, moff, zo.re);
+            pub_store(mine, 5, Mb, moff, zo.im);
+        }
+        look[lane] = make_float4(z.re, z.im, 0.f, 0.f);
+    }
+    __syncthreads();
+    const float4 gin = look[lane];
     if (!valid) return;
+    // the mode constants again (a fresh load, not registers held across the
+    // hand-off)
+    const ModeConst k2 = load_mode(mtab, (int)opaque_v((uint32_t)mc));
     // the state entering this chunk: L_c applied to the state entering the group
-    cf z = {g0.x, g0.y};
+    cf z = {gin.x, gin.y};
     for (int j = 0; j < w; ++j) {
         const float4 f = comp[j * GRP_LANES + lane];
         z = cfma({f.x, f.y}, z, {f.z, f.w});
     }
     if (active) entries[((size_t)b * C + c) * M + m] = make_float2(z.re, z.im);
-    const int kq = opaque(kc);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         if (i < kq) {
             const TokenCtl t = sctl[i];
-            z = cfma(mode_lambda(k, t.E, t.C, t.S), z, {bf16_lo(wd[i].w[0]), bf16_hi(wd[i].w[0])});
+            // the word again, not the summary's unpacked pair kept live since
+            const uint32_t xw = opaque_v(wd[i].w[0]);
+            z = cfma(mode_lambda(k2, t.E, t.C, t.S), z, {bf16_lo(xw), bf16_hi(xw)});
             const cf zz[1] = {z};
             if (active) store_states<1, F32>(y, row0 + (size_t)i * M, mc, zz);
             if (NMID > 0 && (i + 1) % SAMU_BWD_SUB == 0 && i + 1 < K && active)
@@ -613,21 +763,17 @@ __device__ __forceinline__ void greplay_body(float4* gdyn, int G, int L, int M, 
         reinterpret_cast<float2*>(z_final)[(size_t)b * M + m] = make_float2(z.re, z.im);
 }
 
-// 8 waves per SIMD: fits 64 VGPRs without spilling
 template <int K, bool F32>
-__global__ __launch_bounds__(GRP_LANES * SAMU_GROUP_MAX) __attribute__((amdgpu_waves_per_eu(8, 8))) void
-samu_greplay_kernel(int L, int M, int C, int G, int per_group, const TokenCtl* __restrict__ ctl,
-                    const uint32_t* __restrict__ drive, const float4* __restrict__ mtab,
-                    const float2* __restrict__ summ, const float4* __restrict__ chunk_rec,
-                    const float2* __restrict__ gstate, float2* __restrict__ entries, float* __restrict__ mid,
-                    void* __restrict__ y, float* __restrict__ z_final) {
+__global__ __launch_bounds__(GRP_LANES * SAMU_GROUP_MAX) __attribute__((amdgpu_waves_per_eu(4, 8))) void
+samu_gscan_kernel(int L, int M, int C, int G, const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
+                  const float4* __restrict__ mtab, const float4* __restrict__ chunk_rec,
+                  const float2* __restrict__ z0, uint64_t* __restrict__ pub, float2* __restrict__ entries,
+                  float* __restrict__ mid, void* __restrict__ y, float* __restrict__ z_final) {
     extern __shared__ float4 gdyn[];
     if ((int)(blockIdx.x + 1) * GRP_LANES <= M)  // uniform over the workgroup
-        greplay_body<K, F32, true>(gdyn, G, L, M, C, per_group, ctl, drive, mtab, summ, chunk_rec, gstate, entries,
-                                   mid, y, z_final);
+        gscan_body<K, F32, true>(gdyn, G, L, M, C, ctl, drive, mtab, chunk_rec, z0, pub, entries, mid, y, z_final);
     else
-        greplay_body<K, F32, false>(gdyn, G, L, M, C, per_group, ctl, drive, mtab, summ, chunk_rec, gstate,
-                                    entries, mid, y, z_final);
+        gscan_body<K, F32, false>(gdyn, G, L, M, C, ctl, drive, mtab, chunk_rec, z0, pub, entries, mid, y, z_final);
 }
 
 inline int mode_block(int M, int VM) {
@@ -639,13 +785,14 @@ inline int mode_block(int M, int VM) {
 
 hipError_t launch_samu_controller(const SamuParams& p, const Chunking& ch, float* p_out, float* r_out,
                                   float* u_out, float* ctl, float* mtab, float* inv_norm, float* crec,
-                                  hipStream_t s) {
+                                  void* clear, size_t clear_bytes, hipStream_t s) {
     static_assert(CTL_TOK_PER_BLOCK % 32 == 0, "chunks of 16 and 32 tokens must lie in one block");
     const int grid = p.B * (int)ceil_div(p.L, CTL_TOK_PER_BLOCK);
     const int K_last = p.L - (ch.C - 1) * ch.K;
     LRS_LAUNCH(K_SAMU_CONTROLLER, samu_controller_kernel, dim3(grid), dim3(CTL_THREADS), 0, s,
                p.L, p.D, p.M, ch.K, K_last, ch.C, (const uint4*)p.x_sel, p.w_phi, p.w_r, p.a_phi, p.a_r, p.nu,
-               p.theta, p_out, r_out, (float2*)u_out, (TokenCtl*)ctl, (float4*)mtab, inv_norm, (float4*)crec);
+               p.theta, p_out, r_out, (float2*)u_out, (TokenCtl*)ctl, (float4*)mtab, inv_norm, (float4*)crec,
+               (uint4*)clear, clear ? clear_bytes / 16 : (size_t)0);
     return hipGetLastError();
 }
 
@@ -708,25 +855,30 @@ hipError_t launch_samu_gsummary(const SamuParams& p, const Chunking& ch, const f
     return hipGetLastError();
 }
 
-hipError_t launch_samu_greplay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
-                               const float* summ, const float* chunk_rec, const float* gstate, float* entries,
-                               float* mid, void* y, int y_f32, float* z_final, hipStream_t s) {
-    const dim3 grid((unsigned)ceil_div(p.M, GRP_LANES), ch.NG, ch.B);
-    const dim3 block(GRP_LANES * ch.G);
-    const size_t lds = samu_group_lds_bytes(ch.G, ch.K);
-    const int per_group = ch.NG > 1;
-#define GREP_CASE(KK, FF)                                                                                   \
-    LRS_LAUNCH(K_SAMU_REPLAY, (samu_greplay_kernel<KK, FF>), grid, block, lds, s, p.L, p.M, ch.C, ch.G,   \
-               per_group, (const TokenCtl*)ctl, (const uint32_t*)p.b, (const float4*)mtab,               \
-               (const float2*)summ, (const float4*)chunk_rec, (const float2*)gstate, (float2*)entries, mid, \
-               y, z_final)
-    if (ch.K == 32) {
-        if (y_f32) GREP_CASE(32, true); else GREP_CASE(32, false);
-    } else {
-        if (y_f32) GREP_CASE(16, true); else GREP_CASE(16, false);
-    }
-#undef GREP_CASE
-    return hipGetLastError();
+
+}  // namespace lrs
+
+namespace lrs {
+size_t samu_gscan_pub_bytes(const Chunking& ch, int M) {
+    return (size_t)ch.B * ch.NG * SCAN_PUB_WORDS * M * sizeof(uint64_t);
 }
 
+hipError_t launch_samu_gscan(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                             const float* chunk_rec, void* pub, float* entries, float* mid, void* y, int y_f32,
+                             float* z_final, hipStream_t s) {
+    const dim3 grid((unsigned)ceil_div(p.M, GRP_LANES), ch.NG, ch.B);
+    const dim3 block(GRP_LANES * ch.G);
+    const size_t lds = (size_t)2 * ch.G * GRP_LANES * sizeof(float4) + (size_t)ch.G * ch.K * sizeof(TokenCtl);
+#define GSCAN_CASE(KK, FF)                                                                                     \
+    LRS_LAUNCH(K_SAMU_FWD_SCAN, (samu_gscan_kernel<KK, FF>), grid, block, lds, s, p.L, p.M, ch.C, ch.G,       \
+               (const TokenCtl*)ctl, (const uint32_t*)p.b, (const float4*)mtab, (const float4*)chunk_rec,      \
+               (const float2*)p.z0, (uint64_t*)pub, (float2*)entries, mid, y, z_final)
+    if (ch.K == 32) {
+        if (y_f32) GSCAN_CASE(32, true); else GSCAN_CASE(32, false);
+    } else {
+        if (y_f32) GSCAN_CASE(16, true); else GSCAN_CASE(16, false);
+    }
+#undef GSCAN_CASE
+    return hipGetLastError();
+}
 }  // namespace lrs

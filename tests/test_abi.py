@@ -79,10 +79,16 @@ def test_saved_and_workspace_sizes():
     # record per chunk
     need = B * L * (4 + 4 + 8 + 16) + M * 64 + B * C * M * 8 + B * C * M * 8 + B * C * 16
     assert need <= sv < need + 9 * 256
-    # forward workspace: compressed chunk summaries (8 B per mode plus a 16 B
-    # record per chunk), group summaries (16 B per mode) and group entry
-    # states (8 B per mode)
+    # forward workspace, grouped path (G <= 16): the single-pass forward's
+    # hand-off words, six 8-byte words per (group, mode)
     G = 4
+    NG = C // G
+    need = B * NG * M * 48
+    assert need <= scan.samu_scan_workspace_bytes(B, L, D, K, G, False) < need + 256
+    # three-kernel prefix (G > 16): compressed chunk summaries (8 B per mode
+    # plus a 16 B record per chunk), group summaries (16 B per mode) and group
+    # entry states (8 B per mode)
+    G = 32
     NG = C // G
     need = B * C * M * 8 + B * C * 16 + B * NG * M * 24
     assert need <= scan.samu_scan_workspace_bytes(B, L, D, K, G, False) < need + 4 * 256
