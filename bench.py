@@ -68,7 +68,12 @@ def effective_groups(L, K, G, min_group=8, samu=None):
     return min(G, C)
 
 
-def samu_kernel_bytes(B, L, D, K, G):
+def samu_kernel_bytes_unfused(B, L, D, K, G):
+    """samu_kernel_bytes with the separate summary, prefix and replay passes."""
+    return samu_kernel_bytes(B, L, D, K, G, unfused=True)
+
+
+def samu_kernel_bytes(B, L, D, K, G, unfused=False):
     """Bytes one launch of each SAMU kernel moves at this shape, as
     (method, design):
       method  the streams the method's step itself reads and writes (the
@@ -113,35 +118,40 @@ def samu_kernel_bytes(B, L, D, K, G):
                             2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BMID + 8 * BCM + 2 * BLD
                             + 8 * B * n_tiles * L + 8 * BCM),
     }
-    if effective_groups(L, K, G) <= 16:
-        # the grouped path: the forward is one single-pass kernel; the reverse
-        # summary also writes U_g per group and mode, and the backward replay
-        # reads the group's summaries and the carry entering the group
-        # instead of per-chunk carries
+    if effective_groups(L, K, G) <= 16 and not unfused:
+        # the grouped path: one single-pass kernel per direction (chunk
+        # summaries, the state or carry entering each group, replay), the
+        # groups handing states on through 16 B per (group, mode)
         NGM = B * NG * M
         G_ = effective_groups(L, K, G)
-        for k in ("samu_chunk_summary", "samu_replay", "prefix_group_compose", "prefix_chunk_entries"):
+        for k in ("samu_chunk_summary", "samu_replay", "samu_reverse_summary", "samu_bwd_replay",
+                  "prefix_group_compose", "prefix_group_scan", "prefix_chunk_entries"):
             tab.pop(k, None)
+        # what one group reads of its segment's earlier groups, on average:
+        # (G - 1) / 2 published words of 16 B and one 16 B state
+        handoff = 16 * NGM + (8 * (G_ - 1) + 16) * NGM
         tab.update({
             # the controller also writes one (G_c, e^{i D_c}) record per chunk
-            # and clears the single-pass forward's hand-off words (48 B per
-            # group and mode)
-            "samu_controller": (tab["samu_controller"][0], tab["samu_controller"][1] + 16 * BC + 48 * NGM),
-            "samu_reverse_summary": (tab["samu_reverse_summary"][0],
-                                     2 * BLD + 16 * BL + 32 * M + 16 * BC + 8 * BCM + 16 * NGM),
-            # the single-pass forward: b read once, y and the entry states
-            # written; the design adds the token and chunk records, the mode
-            # table, the mid-chunk states, and the hand-off words (U_g or the
-            # leaving state published per group and mode, and what each
-            # group reads of its segment's earlier groups: on average
-            # (G - 1) / 2 maps of 32 B and one 16 B state)
+            # and clears the forward's hand-off words
+            "samu_controller": (tab["samu_controller"][0], tab["samu_controller"][1] + 16 * BC + 16 * NGM),
+            # b read once, y and the entry states written; the design adds the
+            # token and chunk records, the mode table, the mid-chunk states
+            # and the hand-off
             "samu_forward_scan": (2 * BLD + 12 * BL + 8 * M + 2 * BLD + 8 * B * M + 8 * BCM,
                                   2 * BLD + 16 * BL + 64 * M + 16 * BC + 2 * BLD + 8 * B * M + 8 * BMID
-                                  + 8 * BCM + 32 * NGM + (16 * (G_ - 1) + 16) * NGM),
-            # (d nu, d theta) summed over each group's chunks: one row per group
-            "samu_bwd_replay": (tab["samu_bwd_replay"][0],
-                                2 * BLD + 2 * BLD + 16 * BL + 32 * M + 8 * BCM + 8 * BMID + 8 * BCM + 16 * BC
-                                + 8 * NGM + 2 * BLD + 8 * B * n_tiles * L + 8 * NGM),
+                                  + 8 * BCM + handoff),
+            # dy read once (the reverse summary and the replay), b, the entry
+            # states, db, the per-tile controller partials and the (d nu,
+            # d theta) partials; the design re-reads the first half of every
+            # chunk's dy (held neither in registers nor in LDS across the
+            # hand-off), reads the mid-chunk states, the records and the
+            # mode table, writes one (d nu, d theta) row per group, and the
+            # hand-off
+            "samu_backward_scan": (2 * BLD + 2 * BLD + 2 * BLD + 12 * BL + 8 * M + 8 * BCM
+                                   + 8 * B * n_tiles * L + 8 * BCM,
+                                   2 * BLD + BLD + 2 * BLD + 2 * BLD + 16 * BL + 64 * M + 16 * BC + 8 * BCM
+                                   + 8 * BMID + 8 * B * n_tiles * L + 8 * NGM + handoff),
+            "clear": (0, 16 * NGM),
         })
     tab.update({
         # x_sel, p, r, per-tile partials -> dx_sel, per-block direction partials
@@ -151,7 +161,7 @@ def samu_kernel_bytes(B, L, D, K, G):
         "samu_params": (8 * n_blk * (D + 1) + 8 * BCM + 8 * (D + 1) + 8 * (D + 1) + 8 * M,
                         8 * n_blk * (D + 4) + 8 * BCM + 8 * (D + 1) + 16 + 8 * (D + 1) + 8 + 8 * M),
     })
-    if effective_groups(L, K, G) <= 16:
+    if effective_groups(L, K, G) <= 16 and not unfused:
         # the grouped backward writes one (d nu, d theta) row per group
         dif = 8 * BCM - 8 * B * NG * M
         tab["samu_params"] = (tab["samu_params"][0] - dif, tab["samu_params"][1] - dif)
@@ -439,12 +449,26 @@ def rglru_case(torch, scan, inputs, B, L, D, K, G, seed, h0_std, reset_p=0.0, d=
     return step, dict(d=d, y=y, hf=hf, saved=saved, wf=wf, wb=wb, out=out)
 
 
-def kernel_rates(prof, steps, table):
+# A single-pass kernel does the work of several of the method's steps; the
+# bytes those steps move as separate passes (summary, prefix, replay) are
+# reported beside its own, as what the same work costs without the fusion.
+def fused_step_bytes(B, L, D, K, G):
+    full = samu_kernel_bytes_unfused(B, L, D, K, G)
+    return {"samu_forward_scan": full["samu_chunk_summary"][0] + full["prefix_group_scan"][0]
+            + full["samu_replay"][0],
+            "samu_backward_scan": full["samu_reverse_summary"][0] + full["prefix_group_scan"][0]
+            + full["samu_bwd_replay"][0]}
+
+
+def kernel_rates(prof, steps, table, fused=None):
     """Per-kernel us/launch and GB/s from a profiled run (prefix kernels of
     both directions share one name): gbs_design and gbs_method from the two
     byte counts, and frac, the fraction of peak on the smaller of the two
     (the conservative rate: the compressed summaries move fewer bytes than
-    the method's FP32 (A, B) pairs, the replays more than its streams)."""
+    the method's FP32 (A, B) pairs, the replays more than its streams).  A
+    single-pass kernel also gets frac_method_steps: the bytes of the
+    method's separate steps it does the work of, over its time."""
+    fused = fused or {}
     ks = {}
     for n, (t, c) in prof.items():
         us = t / c * 1e3
@@ -454,6 +478,9 @@ def kernel_rates(prof, steps, table):
             row["gbs_design"] = round(des / (us * 1e-6) / 1e9, 1)
             row["gbs_method"] = round(meth / (us * 1e-6) / 1e9, 1)
             row["frac"] = round(min(meth, des) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        if n in fused:
+            row["method_steps_bytes"] = fused[n]
+            row["frac_method_steps"] = round(fused[n] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         ks[n] = row
     return ks
 
@@ -461,7 +488,7 @@ def kernel_rates(prof, steps, table):
 # prefix launches stream only summaries (a few MB); the bar applies to the
 # kernels that stream the [B, L, D] tensors
 STREAM_KERNELS = ("samu_controller", "samu_chunk_summary", "samu_replay", "samu_forward_scan", "samu_reverse_summary",
-                  "samu_bwd_replay", "samu_controller_bwd", "rglru_chunk_summary", "rglru_replay",
+                  "samu_bwd_replay", "samu_backward_scan", "samu_controller_bwd", "rglru_chunk_summary", "rglru_replay",
                   "rglru_reverse_summary", "rglru_bwd_replay")
 
 
@@ -479,7 +506,7 @@ def run_case(timer, kind, step, B, L, D, K, G, steps, warmup, resets=False, repe
     _, prof = timer(step, steps, 1, True)
     floor = (FLOOR_SAMU if kind == "samu" else FLOOR_RGLRU) * B * L * D
     table = samu_kernel_bytes(B, L, D, K, G) if kind == "samu" else rglru_kernel_bytes(B, L, D, K, G, resets)
-    ks = kernel_rates(prof, steps, table)
+    ks = kernel_rates(prof, steps, table, fused_step_bytes(B, L, D, K, G) if kind == "samu" else None)
     row = {"B": B, "L": L, "D": D, "K": K,
            "G": effective_groups(L, K, G, 8 if kind == "samu" else 16),
            "ms_per_step": round(ms, 4), "ms_runs": [round(t, 4) for t in gruns],
@@ -646,7 +673,8 @@ def main():
     meth_bytes, des_bytes = table[dom]
     achieved = meth_bytes / (dom_ms * 1e-3) / 1e9
     traffic = traffic_record(dom)
-    kernels = kernel_rates(prof, args.steps, table)
+    fused = fused_step_bytes(B, L, D, K, G)
+    kernels = kernel_rates(prof, args.steps, table, fused)
 
     log("[bench] copy probe (512 MiB)")
     copy_gbs = copy_probe(torch)
@@ -842,6 +870,9 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": meth_bytes,
                      "design_bytes_per_launch": des_bytes,
                      "design_frac": round(des_bytes / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "method_steps_bytes_per_launch": fused.get(dom),
+                     "method_steps_frac": (round(fused[dom] / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                                           if dom in fused else None),
                      "us_per_launch": round(dom_ms * 1e3, 2)},
         "copy_probe_gbs": round(copy_gbs, 1),
         "kernels": kernels,

@@ -54,7 +54,7 @@ static const char* const kKernelNames[K_NUM_KERNELS] = {
     "samu_controller_bwd", "samu_params", "rglru_chunk_summary", "rglru_replay",
     "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha", "samu_decode",
     "baseline_sequential", "baseline_associative", "gate_projection", "gate_projection_dx",
-    "gate_projection_dw", "gate_projection_reduce", "samu_forward_scan"};
+    "gate_projection_dw", "gate_projection_reduce", "samu_forward_scan", "samu_backward_scan", "clear"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 
@@ -169,22 +169,34 @@ static SamuFwdWs samu_fwd_ws_layout(void* base, const Chunking& ch, int M, size_
     return w;
 }
 
+// The grouped path keeps its reverse summaries and carries in LDS and needs
+// only the single-pass backward's hand-off words and one (d nu, d theta) row
+// per group; the three-kernel prefix keeps summaries, carries and one row
+// per chunk.
 struct SamuBwdWs {
     float *rsumm, *rchunk, *rgsum, *carry, *tok_part, *mode_part, *g_part;
+    void* pub;
+    size_t pub_bytes;
     int n_tiles, n_blk;
 };
 static SamuBwdWs samu_bwd_ws_layout(void* base, const Chunking& ch, int D, int M, size_t* bytes) {
     Carver cv(base);
-    SamuBwdWs w;
+    SamuBwdWs w{};
     const size_t BCM = (size_t)ch.B * ch.C * M;
     w.n_tiles = samu_bwd_tiles(M);
     w.n_blk = (int)ceil_div((int64_t)ch.B * ch.L, samu_ctl_tok_per_blk());
-    w.rsumm = cv.take<float>(BCM * 2);
-    w.rchunk = cv.take<float>((size_t)ch.B * ch.C * 4);
-    w.rgsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
-    w.carry = samu_fused(ch) ? nullptr : cv.take<float>(BCM * 2);  // the grouped path forms carries in LDS
+    const bool fused = samu_fused(ch);
+    if (fused) {
+        w.pub_bytes = samu_gscan_pub_bytes(ch, M);
+        w.pub = cv.take<uint64_t>(w.pub_bytes / sizeof(uint64_t));
+    } else {
+        w.rsumm = cv.take<float>(BCM * 2);
+        w.rchunk = cv.take<float>((size_t)ch.B * ch.C * 4);
+        w.rgsum = cv.take<float>((size_t)ch.B * ch.NG * M * 6);
+        w.carry = cv.take<float>(BCM * 2);
+    }
     w.tok_part = cv.take<float>((size_t)ch.B * w.n_tiles * ch.L * 2);
-    w.mode_part = cv.take<float>(BCM * 2);
+    w.mode_part = cv.take<float>((size_t)ch.B * (fused ? ch.NG : ch.C) * M * 2);
     w.g_part = cv.take<float>((size_t)w.n_blk * samu_param_columns(D) * 2);
     if (bytes) *bytes = cv.off;
     return w;
@@ -420,17 +432,11 @@ scan_status samu_scan_bwd(int B, int L, int D, int K, int G, const void* x_sel, 
     SamuBwdWs ws = samu_bwd_ws_layout(workspace, ch, D, M, nullptr);
     const int f32 = grad_dtype == SCAN_F32;
     if (samu_fused(ch)) {
-        LRS_TRY(launch_samu_gsummary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, sv.crec, ws.rgsum, s),
-                "samu reverse summary");
-        const float* gcarry = dz_final;
-        if (ch.NG > 1) {
-            float* gentry = ws.rgsum + (size_t)ch.B * ch.NG * M * 4;
-            LRS_TRY(launch_group_scan(2, ch, M, ws.rgsum, dz_final, gentry, s), "samu reverse group scan");
-            gcarry = gentry;
-        }
-        LRS_TRY(launch_samu_gbwd_replay(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, ws.rsumm, sv.crec, gcarry, dy,
-                                        db, f32, dz0, ws.tok_part, ws.n_tiles, ws.mode_part, s),
-                "samu backward replay");
+        // the hand-off words cleared, then reverse summaries, group carries
+        // and the backward replay in one launch
+        LRS_TRY(launch_samu_gbscan(p, ch, sv.ctl, sv.mtab, sv.entries, sv.mid, sv.crec, dz_final, ws.pub,
+                                   ws.pub_bytes, dy, db, f32, dz0, ws.tok_part, ws.n_tiles, ws.mode_part, s),
+                "samu backward scan");
     } else {
         LRS_TRY(launch_samu_summary(p, ch, sv.ctl, sv.mtab, dy, true, ws.rsumm, ws.rchunk, s),
                 "samu reverse summary");

@@ -217,6 +217,165 @@ struct TokenCtl { float E, C, S, d; };
 struct ChunkCtl { float G, cD, sD, pad; };
 
 
+// ------------------------------------------------ group hand-off words ---
+// The single-pass scans hand the state between groups of chunks through
+// 64-bit words: (1 << 32 | float bits), written and read with relaxed
+// device-scope atomics.  The area starts zeroed, so a word is valid exactly
+// when its high half is 1; a word is never torn, so a reader that sees every
+// word it needs valid holds consistent values, and no fence is needed
+// between words.  Per (group, mode) two words: the affine part B of the
+// group's map U (a group inside a segment) or the state leaving the group
+// (a segment's last group).  The transition part A of U is not published:
+// a reader forms it from the chunk records exactly as the group itself does.
+constexpr int SCAN_SPIN_MAX = 1 << 14;
+constexpr int SCAN_PUB_WORDS = 2;
+
+// Word `i` of a group for one lane: `grp` is the group's (wave-uniform) first
+// word, `off` the lane's byte offset (mode * 8) and `Mb` = M * 8, so the
+// address is a uniform base plus a 32-bit lane offset.
+__device__ __forceinline__ uint64_t* pub_word(const uint64_t* grp, int i, uint32_t Mb, uint32_t off) {
+    return reinterpret_cast<uint64_t*>(const_cast<char*>(reinterpret_cast<const char*>(grp)) +
+                                       (size_t)i * Mb + off);
+}
+__device__ __forceinline__ uint64_t pub_load(const uint64_t* grp, int i, uint32_t Mb, uint32_t off) {
+    return __hip_atomic_load(pub_word(grp, i, Mb, off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void pub_store(uint64_t* grp, int i, uint32_t Mb, uint32_t off, float v) {
+    __hip_atomic_store(pub_word(grp, i, Mb, off), (uint64_t(1) << 32) | (uint64_t)__float_as_uint(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool pub_ok(uint64_t w) { return (uint32_t)(w >> 32) == 1u; }
+__device__ __forceinline__ float pub_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// The two words of an earlier group for this lane's mode, once both are
+// published.
+__device__ __forceinline__ float2 wait_pair(const uint64_t* grp, uint32_t Mb, uint32_t off) {
+    float2 v = make_float2(0.f, 0.f);
+    bool ok = false;
+    for (int it = 0; it < SCAN_SPIN_MAX; ++it) {
+        if (!ok) {
+            // the lane offset afresh each poll: addresses kept across the
+            // loop would cost two registers each
+            const uint32_t o = opaque_v(off);
+            const uint64_t w0 = pub_load(grp, 0, Mb, o), w1 = pub_load(grp, 1, Mb, o);
+            if (pub_ok(w0) && pub_ok(w1)) {
+                v = make_float2(pub_val(w0), pub_val(w1));
+                ok = true;
+            }
+        }
+        if (__all(ok)) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return v;
+}
+
+// Where the chunks of a group come from: chunk records [C] of the row, the
+// mode's chunk phasors (e^{i K theta} and, for the last chunk, e^{i K_last
+// theta}) and kappa; processing order pc maps to chunk pc (forward) or
+// C - 1 - pc (REV, the adjoint).
+struct GroupChunks {
+    const float4* rec;
+    float4 ph_full, ph_last;
+    float kappa;
+    int C;
+};
+
+// The transition part of group j's map U_j for this lane's mode: the product
+// of its chunks' transitions in processing order, formed with the same
+// operations as the group's own table (chunk_transition, then cmul).
+template <bool REV>
+__device__ __forceinline__ cf group_transition(const GroupChunks& gc, int G, int j) {
+    cf ua = {1.f, 0.f};
+    for (int i = 0; i < G; ++i) {
+        const int pc = j * G + i;
+        const int c = REV ? gc.C - 1 - pc : pc;
+        const cf a = chunk_transition<REV>(gc.kappa, c == gc.C - 1 ? gc.ph_last : gc.ph_full, gc.rec[c]);
+        ua = cmul(a, ua);
+    }
+    return ua;
+}
+
+// The state entering group q (processing order) of one batch row, for this
+// lane's mode `mc`; every wave of the workgroup calls it (it holds two
+// workgroup barriers).  comp [G][64]: the (A, B) map of each of the group's
+// chunks in processing order (wave w's at w); look [G][64]: scratch.
+// seed: the state before the first group ([M] complex, NULL = 0); pub: the
+// row's [NG][SCAN_PUB_WORDS][M] words.
+//
+// Fixed order of evaluation.  The groups form segments of G consecutive
+// groups.  The last group of a segment publishes the state leaving it (its
+// chunks' maps applied in order to the state entering it); every other group
+// publishes the B part of U_q = S_{G-1} o ... o S_0.  Group q takes the state
+// leaving the previous segment (the seed for the first) and applies the U of
+// the segment's groups before it, oldest first: at most G - 1 maps and one
+// state, read by G waves at once.  Which words a group reads and the order it
+// applies them in depend only on q and G, never on timing, so the result is
+// bitwise the same on every run.  The only serial dependence across
+// workgroups is the chain of segment states, one link per G groups.
+//
+// Progress.  Workgroups are dispatched in grid order (mode tiles fastest,
+// then groups), and a workgroup only waits for words of lower-numbered
+// groups of its own row and mode tile, which were dispatched before it and
+// never wait for it, so every wait ends.  Each wait is nevertheless bounded
+// (SCAN_SPIN_MAX polls).
+template <bool REV>
+__device__ __forceinline__ float4 group_handoff(const float4* comp, float4* look, int G, int w, int lane, int q,
+                                                int NG, int M, int mc, bool active, const float2* seed,
+                                                uint64_t* pub, const GroupChunks& gc) {
+    constexpr int GL = 64;
+    const uint32_t Mb = (uint32_t)M * 8u, moff = (uint32_t)mc * 8u;
+    uint64_t* mine = pub + (size_t)q * SCAN_PUB_WORDS * M;  // wave-uniform
+    const int nprev = q % G;                          // earlier groups of this segment
+    const bool seg_last = nprev == G - 1 || q == NG - 1;
+    if (w == 0 && active && q + 1 < NG && !seg_last) {
+        // the B part of U_q = S_{G-1} o ... o S_0 (the right operand first),
+        // published at once
+        cf ub = {0.f, 0.f};
+        for (int j = 0; j < G; ++j) {  // all G chunks: a group short of G chunks is the last one
+            const float4 f = comp[j * GL + lane];
+            ub = cfma({f.x, f.y}, ub, {f.z, f.w});
+        }
+        pub_store(mine, 0, Mb, moff, ub.re);
+        pub_store(mine, 1, Mb, moff, ub.im);
+    }
+    // wave w < nprev reads U of group q-1-w, wave nprev the state entering
+    // the segment
+    if (w < nprev) {
+        const int j = q - 1 - w;
+        const cf ua = group_transition<REV>(gc, G, j);
+        const float2 ub = wait_pair(pub + (size_t)j * SCAN_PUB_WORDS * M, Mb, moff);
+        look[w * GL + lane] = make_float4(ua.re, ua.im, ub.x, ub.y);
+    } else if (w == nprev) {
+        float2 zs = make_float2(0.f, 0.f);
+        if (q - nprev > 0) zs = wait_pair(pub + (size_t)(q - nprev - 1) * SCAN_PUB_WORDS * M, Mb, moff);
+        else if (seed) zs = seed[mc];
+        look[w * GL + lane] = make_float4(zs.x, zs.y, 0.f, 0.f);
+    }
+    __syncthreads();
+    if (w == 0) {
+        const float4 zs = look[nprev * GL + lane];
+        cf z = {zs.x, zs.y};
+        for (int v = nprev - 1; v >= 0; --v) {  // oldest first
+            const float4 f = look[v * GL + lane];
+            z = cfma({f.x, f.y}, z, {f.z, f.w});
+        }
+        if (active && q + 1 < NG && seg_last) {
+            // the state leaving the group, for the next segment: this
+            // group's chunks applied in order, as in the chain
+            cf zo = z;
+            for (int j = 0; j < G; ++j) {
+                const float4 f = comp[j * GL + lane];
+                zo = cfma({f.x, f.y}, zo, {f.z, f.w});
+            }
+            pub_store(mine, 0, Mb, moff, zo.re);
+            pub_store(mine, 1, Mb, moff, zo.im);
+        }
+        look[lane] = make_float4(z.re, z.im, 0.f, 0.f);
+    }
+    __syncthreads();
+    return look[lane];
+}
+
 // ------------------------------------------------------ wave reductions ---
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

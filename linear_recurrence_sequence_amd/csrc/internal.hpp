@@ -38,6 +38,8 @@ enum KernelId {
     K_GATE_PROJ_DW,
     K_GATE_PROJ_REDUCE,
     K_SAMU_FWD_SCAN,
+    K_SAMU_BWD_SCAN,
+    K_CLEAR,
     K_NUM_KERNELS
 };
 
@@ -85,12 +87,6 @@ struct PrefixSummaries {
 hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const PrefixSummaries& sm,
                          float* gsum, const float* init, float* entries, hipStream_t s);
 
-// The scan over group summaries alone (the middle launch of launch_prefix):
-// gsum [B, NG, W] U_g (ELEM-complex affine maps) -> gentry [B, NG, W], the
-// state entering each group (processing order).
-hipError_t launch_group_scan(int elem, const Chunking& ch, int W, const float* gsum, const float* init,
-                             float* gentry, hipStream_t s);
-
 // ---------------------------------------------------------------- SAMU ---
 struct SamuParams {
     int B, L, D, M;
@@ -132,33 +128,28 @@ hipError_t launch_samu_summary(const SamuParams& p, const Chunking& ch, const fl
 hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const float* ctl,
                               const float* mtab, const float* entries, float* mid, void* y, int y_f32,
                               float* z_final, hipStream_t s);
-// Grouped path without the compose and expand launches: a workgroup owns one
-// group of ch.G <= SAMU_GROUP_MAX consecutive chunks (processing order) and
-// 64 modes, one wave per chunk.
+// Grouped path (single-pass scans): a workgroup owns one group of
+// ch.G <= SAMU_GROUP_MAX consecutive chunks (processing order) and 64 modes,
+// one wave per chunk; groups hand states to each other through
+// samu_gscan_pub_bytes() of tagged words that must be zero at launch.
 //   gscan:    the whole forward after the controller in one launch (chunk
-//             summaries, U_g, the state entering the group from the groups
-//             before it, the replay, which also writes the entry states
-//             [B, C, M] the backward reads); pub: samu_gscan_pub_bytes() of
-//             hand-off words, cleared to zero by the controller launch before
-//             it (its `clear` argument);
-//   gsummary: the reverse summaries of dy (B parts, with the chunk records
-//             the controller wrote, read only) plus the reverse U_g of every
-//             group composed in LDS -> gsum [B, NG, M] (A, B) pairs;
-//   gbwd_replay: carries formed in LDS from the carry entering the group,
-//             then the backward replay (groups aligned from the last chunk).
+//             summaries, the state entering the group from the groups before
+//             it, the replay, which also writes the entry states [B, C, M]
+//             the backward reads); its words are cleared by the controller
+//             launch before it (the controller's `clear` argument);
 constexpr int SAMU_GROUP_MAX = 16;
 size_t samu_gscan_pub_bytes(const Chunking& ch, int M);
 hipError_t launch_samu_gscan(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
                              const float* chunk_rec, void* pub, float* entries, float* mid, void* y, int y_f32,
                              float* z_final, hipStream_t s);
-hipError_t launch_samu_gsummary(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
-                                const void* drive, bool reverse, float* summ, const float* chunk_rec, float* gsum,
-                                hipStream_t s);
-hipError_t launch_samu_gbwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
-                                   const float* entries, const float* mid, const float* rsumm,
-                                   const float* rchunk, const float* gcarry, const void* dy, void* db,
-                                   int db_f32, float* dz0, float* tok_part, int n_tiles, float* mode_part,
-                                   hipStream_t s);
+//   gbscan:   the whole adjoint scan in one launch (reverse summaries, the
+//             carry entering each group from the groups after it in time, the
+//             backward replay); it clears its words with a small launch of
+//             its own first.  mode_part: [B, NG, M] per-group (d nu, d theta)
+hipError_t launch_samu_gbscan(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                              const float* entries, const float* mid, const float* chunk_rec, const float* dz_final,
+                              void* pub, size_t pub_bytes, const void* dy, void* db, int db_f32, float* dz0,
+                              float* tok_part, int n_tiles, float* mode_part, hipStream_t s);
 // carry_in: [B, C, M] cotangent arriving after each chunk's last token;
 // mode_part: [B, C, M] per-chunk (d nu, d theta) partials (gbwd_replay:
 // [B, NG, M] per-group sums)

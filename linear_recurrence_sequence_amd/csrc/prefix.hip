@@ -227,20 +227,6 @@ void run_prefix(const Chunking& ch, int W, Sum sm, float* gsum, const float* ini
 
 }  // namespace
 
-hipError_t launch_group_scan(int elem, const Chunking& ch, int W, const float* gsum, const float* init,
-                             float* gentry, hipStream_t s) {
-    int slots = 1;
-    while (slots < ch.NG && slots < SCAN_THREADS / 8) slots <<= 1;
-    const int MT = SCAN_THREADS / slots;
-    const dim3 sgrid((unsigned)ceil_div(W, MT), ch.B);
-    if (elem == 2)
-        LRS_LAUNCH(K_PREFIX_OUTER, (prefix_group_scan_kernel<2>), sgrid, dim3(SCAN_THREADS), 0, s, ch.NG, W, MT,
-                   gsum, init, gentry);
-    else
-        LRS_LAUNCH(K_PREFIX_OUTER, (prefix_group_scan_kernel<1>), sgrid, dim3(SCAN_THREADS), 0, s, ch.NG, W, MT,
-                   gsum, init, gentry);
-    return hipGetLastError();
-}
 
 hipError_t launch_prefix(int elem, bool reverse, const Chunking& ch, int W, const PrefixSummaries& sm,
                          float* gsum, const float* init, float* entries, hipStream_t s) {

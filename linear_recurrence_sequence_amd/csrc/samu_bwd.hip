@@ -52,7 +52,7 @@ constexpr int BWD_THREADS = 256;
 // Past a partial chunk's end (token i >= kc) a load is skipped (CLAMP false:
 // the word reads as zero) or re-reads token kc - 1 (CLAMP true: no branch;
 // the word is never used).
-template <int K, int H, bool FULL, bool CLAMP>
+template <int K, int H, bool FULL, bool CLAMP, bool GW = true>
 __device__ __forceinline__ void bwd_issue(cf (&ck)[K / H], uint32_t (&bw)[K], uint32_t (&gw)[K], int kc,
                                           size_t row0, int M, int mm, size_t bc,
                                           const float2* __restrict__ entries, const float2* __restrict__ mid,
@@ -75,7 +75,7 @@ __device__ __forceinline__ void bwd_issue(cf (&ck)[K / H], uint32_t (&bw)[K], ui
             if (FULL || CLAMP) bw[i] = (drive + row0 + (size_t)(FULL ? i : min(i, kc - 1)) * M)[mm];
             else bw[i] = i < kc ? (drive + row0 + (size_t)i * M)[mm] : 0u;
         }
-        if (h != NH - 1) continue;  // earlier sub-chunks: requested when they start
+        if (!GW || h != NH - 1) continue;  // earlier sub-chunks: requested when they start
 #pragma unroll
         for (int j = H - 1; j >= 0; --j) {
             const int i = h * H + j;
@@ -247,37 +247,43 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(LRS
     }
 }
 
-// Grouped backward replay: a workgroup owns one group of G chunks in the
-// adjoint's processing order (chunk C - 1 - (q G + w) for wave w) and 64
-// modes.  Each wave rebuilds its chunk's conjugate reverse summary (the
-// compressed B part and the chunk record the reverse summary kernel wrote)
-// into the group's LDS table; after the workgroup's one barrier, wave w forms
-// the cotangent arriving after its chunk by applying the group's earlier
-// summaries (processing order) to the cotangent entering the group, then runs
-// the adjoint of its chunk with wave-local LDS traffic only.
 constexpr int GB_LANES = 64;
 
+// Single-pass grouped backward: the reverse summaries, the carry entering
+// each group and the backward replay in one launch.  A workgroup owns one
+// group of G chunks in the adjoint's processing order (wave w on chunk
+// C - 1 - (q G + w)) and 64 modes.  Each wave reads its chunk's cotangent
+// words once for the conjugate reverse summary (and keeps the last
+// sub-chunk's words for the replay) and puts the chunk's map into the
+// group's LDS table; the carry entering the group comes from the groups after
+// it in time through group_handoff (the fixed-order chain of common.hpp,
+// seeded with dz_final); wave w then applies the group's earlier maps to it
+// to get the cotangent arriving after its chunk, and runs the adjoint of its
+// chunk (bwd_body) with wave-local LDS traffic only.  The reverse summaries
+// and group carries never go to memory as tensors.
 template <int K, int H, bool F32, bool ALLACT>
-__device__ __forceinline__ void gbwd_body(float4* gdyn, int G, int L, int M, int C, int n_tiles, int per_group,
-                                          const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
-                                          const float4* __restrict__ mtab, const float2* __restrict__ entries,
-                                          const float2* __restrict__ mid, const float2* __restrict__ rsumm,
-                                          const float4* __restrict__ rchunk, const float2* __restrict__ gcarry,
-                                          const uint32_t* __restrict__ dy, void* __restrict__ db,
-                                          float2* __restrict__ dz0, float* __restrict__ tok_part,
-                                          float2* __restrict__ mode_part) {
+__device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, int C, int n_tiles,
+                                            const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
+                                            const float4* __restrict__ mtab, const float2* __restrict__ entries,
+                                            const float2* __restrict__ mid, const float4* __restrict__ chunk_rec,
+                                            const float2* __restrict__ dz_final, uint64_t* __restrict__ pub,
+                                            const uint32_t* __restrict__ dy, void* __restrict__ db,
+                                            float2* __restrict__ dz0, float* __restrict__ tok_part,
+                                            float2* __restrict__ mode_part) {
     constexpr int NH = K / H;
     constexpr int ROW = 64 * (2 * H + 1);  // floats of one wave's transpose rows
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     // LDS: [G][64] entry states, [G][K] token controls, [G][ROW] transpose
-    // rows; the group's summary table [G][64] float4 overlays the rows (it is
-    // read only before the second barrier, the rows only after it)
+    // rows; the group's summary table and the hand-off scratch ([G][64]
+    // float4 each) overlay the rows (read only before the last barrier ahead
+    // of the replay, the rows only after it)
     float2* stash = reinterpret_cast<float2*>(gdyn) + w * GB_LANES + lane;
     TokenCtl* sctl = reinterpret_cast<TokenCtl*>(reinterpret_cast<float2*>(gdyn) + G * GB_LANES) + w * K;
     float* rows = reinterpret_cast<float*>(reinterpret_cast<TokenCtl*>(reinterpret_cast<float2*>(gdyn) + G * GB_LANES) +
                                            G * K);
     float* lds_w = rows + w * ROW;
     float4* comp = reinterpret_cast<float4*>(rows);
+    float4* look = comp + G * GB_LANES;
     const int q = blockIdx.y, b = blockIdx.z, NG = gridDim.y;
     const int pc = q * G + w;
     const bool valid = pc < C;  // wave-uniform
@@ -291,29 +297,51 @@ __device__ __forceinline__ void gbwd_body(float4* gdyn, int G, int L, int M, int
     const size_t row0 = ((size_t)b * L + s) * M;  // wave-uniform
     const size_t bc = (size_t)b * C + c;
 
-    // requests: token controls, mode constants, this chunk's reverse summary,
-    // the cotangent entering the group, then the replay's own words
+    // requests: token controls, mode constants, the chunk record, every
+    // cotangent word of the chunk (last token first, the order the reverse
+    // summary takes them in; past a partial chunk's end they read as 0),
+    // then the replay's states and drive words
     float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lane < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + lane];
     const ModeConst k = load_mode(mtab, mm);
     const float4 ph = mtab[MODE_REC * mm + (c == C - 1 ? 3 : 2)];
-    const float4 rec = rchunk[bc];
-    const float2 bp = rsumm[bc * M + mm];
-    float2 g0 = make_float2(0.f, 0.f);
-    if (gcarry) g0 = per_group ? gcarry[((size_t)b * NG + q) * M + mm] : gcarry[(size_t)b * M + mm];
-    cf ck[NH];
-    uint32_t bw[K], gw[K];
-    bwd_issue<K, H, false, true>(ck, bw, gw, kc, row0, M, mm, bc, entries, mid, drive, dy);
-    if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
+    const float4 rec = chunk_rec[bc];
+    uint32_t gw[K];
     {
-        const cf a = chunk_transition<true>(k.kappa, ph, rec);
-        comp[w * GB_LANES + lane] = make_float4(a.re, a.im, bp.x, bp.y);
+        const ChunkRows cr(dy + row0, kc, M);
+#pragma unroll
+        for (int j = 0; j < K; ++j) gw[K - 1 - j] = cr.load(K - 1 - j, mm);
     }
+    cf ck[NH];
+    uint32_t bw[K];
+    bwd_issue<K, H, false, true, false>(ck, bw, gw, kc, row0, M, mm, bc, entries, mid, drive, dy);
+    if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
+    wave_lds_sync();
+    // the chunk's conjugate reverse summary: carry -> conj(lambda_t) (dy_t + carry)
+    cf A = {1.f, 0.f}, Bv = {0.f, 0.f};
+    if (valid) {
+        const int kq = opaque(kc);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int i = K - 1 - j;
+            if (i < kq) {
+                const TokenCtl t = sctl[i];
+                const cf lam = mode_lambda(k, t.E, t.C, t.S);
+                Bv = cmulc(lam, {Bv.re + bf16_lo(gw[i]), Bv.im + bf16_hi(gw[i])});
+            }
+        }
+        A = chunk_transition<true>(k.kappa, ph, rec);
+    }
+    comp[w * GB_LANES + lane] = make_float4(A.re, A.im, Bv.re, Bv.im);
     if (NH > 1) *stash = make_float2(ck[0].re, ck[0].im);
     __syncthreads();
-    // the cotangent arriving after this chunk: the group's earlier summaries
-    // (processing order) applied to the cotangent entering the group
-    cf carry = {g0.x, g0.y};
+    // the cotangent entering the group, then the one arriving after this
+    // chunk: the group's earlier summaries (processing order) applied to it
+    const GroupChunks gc{chunk_rec + (size_t)b * C, mtab[MODE_REC * mm + 2], mtab[MODE_REC * mm + 3], k.kappa, C};
+    const float4 gin = group_handoff<true>(comp, look, G, w, lane, q, NG, M, mm, active,
+                                           dz_final ? dz_final + (size_t)b * M : nullptr,
+                                           pub + (size_t)b * NG * SCAN_PUB_WORDS * M, gc);
+    cf carry = {gin.x, gin.y};
     if (valid) {
         for (int j = 0; j < w; ++j) {
             const float4 f = comp[j * GB_LANES + lane];
@@ -323,6 +351,8 @@ __device__ __forceinline__ void gbwd_body(float4* gdyn, int G, int L, int M, int
     __syncthreads();  // the summary table's LDS becomes the transpose rows
     float acc_nu = 0.f, acc_th = 0.f;
     if (valid) {
+        // the last sub-chunk's cotangent words are still held from the
+        // summary; bwd_body requests the earlier sub-chunks' as they start
         bwd_body<K, H, F32, false, true, true, (NH > 1)>(lds_w, sctl, k, active, lane, tile, n_tiles, L, M, b, s,
                                                          kc, row0, mm, dy, db, tok_part, ck, bw, gw, carry, acc_nu,
                                                          acc_th, stash);
@@ -347,20 +377,27 @@ __device__ __forceinline__ void gbwd_body(float4* gdyn, int G, int L, int M, int
 
 template <int K, int H, bool F32>
 __global__ __launch_bounds__(GB_LANES * SAMU_GROUP_MAX) __attribute__((amdgpu_waves_per_eu(4, 8))) void
-samu_gbwd_replay_kernel(int L, int M, int C, int G, int n_tiles, int per_group, const TokenCtl* __restrict__ ctl,
-                        const uint32_t* __restrict__ drive, const float4* __restrict__ mtab,
-                        const float2* __restrict__ entries, const float2* __restrict__ mid,
-                        const float2* __restrict__ rsumm, const float4* __restrict__ rchunk,
-                        const float2* __restrict__ gcarry, const uint32_t* __restrict__ dy, void* __restrict__ db,
-                        float2* __restrict__ dz0, float* __restrict__ tok_part, float2* __restrict__ mode_part) {
+samu_gbscan_kernel(int L, int M, int C, int G, int n_tiles, const TokenCtl* __restrict__ ctl,
+                   const uint32_t* __restrict__ drive, const float4* __restrict__ mtab,
+                   const float2* __restrict__ entries, const float2* __restrict__ mid,
+                   const float4* __restrict__ chunk_rec, const float2* __restrict__ dz_final,
+                   uint64_t* __restrict__ pub, const uint32_t* __restrict__ dy, void* __restrict__ db,
+                   float2* __restrict__ dz0, float* __restrict__ tok_part, float2* __restrict__ mode_part) {
     static_assert(K % H == 0 && 64 % (2 * H) == 0, "sub-chunk shape");
     extern __shared__ float4 gdyn[];
     if ((int)(blockIdx.x + 1) * GB_LANES <= M)  // uniform over the workgroup
-        gbwd_body<K, H, F32, true>(gdyn, G, L, M, C, n_tiles, per_group, ctl, drive, mtab, entries, mid, rsumm,
-                                   rchunk, gcarry, dy, db, dz0, tok_part, mode_part);
+        gbscan_body<K, H, F32, true>(gdyn, G, L, M, C, n_tiles, ctl, drive, mtab, entries, mid, chunk_rec, dz_final,
+                                     pub, dy, db, dz0, tok_part, mode_part);
     else
-        gbwd_body<K, H, F32, false>(gdyn, G, L, M, C, n_tiles, per_group, ctl, drive, mtab, entries, mid, rsumm,
-                                    rchunk, gcarry, dy, db, dz0, tok_part, mode_part);
+        gbscan_body<K, H, F32, false>(gdyn, G, L, M, C, n_tiles, ctl, drive, mtab, entries, mid, chunk_rec,
+                                      dz_final, pub, dy, db, dz0, tok_part, mode_part);
+}
+
+// Zeroes n 16-byte words (the single-pass backward's hand-off area, before
+// the pass).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint4* __restrict__ p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // -------------------------------------------------- controller backward ---
@@ -756,32 +793,36 @@ hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const
     return hipGetLastError();
 }
 
-hipError_t launch_samu_gbwd_replay(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
-                                   const float* entries, const float* mid, const float* rsumm,
-                                   const float* rchunk, const float* gcarry, const void* dy, void* db,
-                                   int db_f32, float* dz0, float* tok_part, int n_tiles, float* mode_part,
-                                   hipStream_t s) {
+
+hipError_t launch_samu_gbscan(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
+                              const float* entries, const float* mid, const float* chunk_rec, const float* dz_final,
+                              void* pub, size_t pub_bytes, const void* dy, void* db, int db_f32, float* dz0,
+                              float* tok_part, int n_tiles, float* mode_part, hipStream_t s) {
+    {
+        const size_t n16 = pub_bytes / 16;
+        const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div((int64_t)n16, 256), 2048));
+        LRS_LAUNCH(K_CLEAR, clear_words_kernel, dim3(blocks), dim3(256), 0, s, (uint4*)pub, n16);
+    }
     const dim3 grid((unsigned)ceil_div(p.M, GB_LANES), ch.NG, ch.B);
     const dim3 block(GB_LANES * ch.G);
     const int H = ch.K == 32 ? SAMU_BWD_SUB : 16;
     // entry-state stash, token controls, transpose rows (the summary table
-    // overlays the rows, which are larger)
+    // and the hand-off scratch overlay the rows, which are larger)
     const size_t lds = (size_t)ch.G * GB_LANES * sizeof(float2) + (size_t)ch.G * ch.K * sizeof(TokenCtl) +
                        (size_t)ch.G * 64 * (2 * H + 1) * sizeof(float);
-    const int per_group = ch.NG > 1;
-#define GBWD_CASE(KK, HH, FF)                                                                               \
-    LRS_LAUNCH(K_SAMU_BWD_REPLAY, (samu_gbwd_replay_kernel<KK, HH, FF>), grid, block, lds, s, p.L, p.M,   \
-               ch.C, ch.G, n_tiles, per_group, (const TokenCtl*)ctl, (const uint32_t*)p.b,               \
-               (const float4*)mtab, (const float2*)entries, (const float2*)mid, (const float2*)rsumm,     \
-               (const float4*)rchunk, (const float2*)gcarry, (const uint32_t*)dy, db, (float2*)dz0,      \
-               tok_part, (float2*)mode_part)
+#define GBSCAN_CASE(KK, HH, FF)                                                                            \
+    LRS_LAUNCH(K_SAMU_BWD_SCAN, (samu_gbscan_kernel<KK, HH, FF>), grid, block, lds, s, p.L, p.M, ch.C, ch.G, \
+               n_tiles, (const TokenCtl*)ctl, (const uint32_t*)p.b, (const float4*)mtab,                 \
+               (const float2*)entries, (const float2*)mid, (const float4*)chunk_rec,                     \
+               (const float2*)dz_final, (uint64_t*)pub, (const uint32_t*)dy, db, (float2*)dz0, tok_part, \
+               (float2*)mode_part)
     constexpr int H32 = SAMU_BWD_SUB, H16 = SAMU_BWD_SUB < 16 ? SAMU_BWD_SUB : 16;
     if (ch.K == 32) {
-        if (db_f32) GBWD_CASE(32, H32, true); else GBWD_CASE(32, H32, false);
+        if (db_f32) GBSCAN_CASE(32, H32, true); else GBSCAN_CASE(32, H32, false);
     } else {
-        if (db_f32) GBWD_CASE(16, H16, true); else GBWD_CASE(16, H16, false);
+        if (db_f32) GBSCAN_CASE(16, H16, true); else GBSCAN_CASE(16, H16, false);
     }
-#undef GBWD_CASE
+#undef GBSCAN_CASE
     return hipGetLastError();
 }
 

@@ -484,156 +484,9 @@ __device__ __forceinline__ void load_chunk_clamped(Words<1> (&w)[K], const uint3
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int K, bool REV, bool ALLACT>
-__device__ __forceinline__ void gsummary_body(float4* gdyn, int G, int L, int M, int C,
-                                              const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
-                                              const float4* __restrict__ mtab, float* __restrict__ summ,
-                                              const float4* __restrict__ chunk_rec, float4* __restrict__ gsum) {
-    float4* comp = gdyn;
-    TokenCtl* sctl = reinterpret_cast<TokenCtl*>(gdyn + G * GRP_LANES);
-    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int q = blockIdx.y, b = blockIdx.z, NG = gridDim.y;
-    const int pc = q * G + w;
-    const bool valid = pc < C;  // wave-uniform
-    const int pcc = min(pc, C - 1);
-    const int c = REV ? C - 1 - pcc : pcc;
-    const int m = blockIdx.x * GRP_LANES + lane;
-    const bool active = ALLACT || m < M;
-    const int mc = active ? m : M - 1;
-    const int s = c * K;
-    const int kc = min(K, L - s);
-    sctl += w * K;
-
-    float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + lane];
-    ModeConst k[1];
-    k[0] = load_mode(mtab, mc);
-    const float4 ph = mtab[MODE_REC * mc + (c == C - 1 ? 3 : 2)];
-    const float4 rec = chunk_rec[(size_t)b * C + c];  // (G_c, cos D_c, sin D_c), from the controller
-    Words<1> wd[K];
-    load_chunk_clamped<K, REV>(wd, drive + ((size_t)b * L + s) * M, M, mc, kc);
-    if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
-    wave_lds_sync();
-    cf A = {1.f, 0.f}, Bv[1] = {{0.f, 0.f}};
-    if (valid) {
-        const int kq = opaque(kc);
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-            const int i = REV ? K - 1 - j : j;
-            if (i < kq) summary_step<1, REV>(k, Bv, sctl[i], wd[i]);
-        }
-        if (active) reinterpret_cast<float2*>(summ)[((size_t)b * C + c) * M + m] = make_float2(Bv[0].re, Bv[0].im);
-        A = chunk_transition<REV>(k[0].kappa, ph, rec);
-    }
-    group_put(comp, w, lane, A, Bv[0]);
-    __syncthreads();
-    if (w == 0 && active) {
-        // U_g = S_{n-1} o ... o S_0 in processing order (the right operand first)
-        const int n = min(G, C - q * G);
-        cf ua = {1.f, 0.f}, ub = {0.f, 0.f};
-        for (int j = 0; j < n; ++j) {
-            const float4 f = comp[j * GRP_LANES + lane];
-            const cf fa = {f.x, f.y}, fb = {f.z, f.w};
-            ub = cfma(fa, ub, fb);
-            ua = cmul(fa, ua);
-        }
-        gsum[((size_t)b * NG + q) * M + m] = make_float4(ua.re, ua.im, ub.re, ub.im);
-    }
-}
-
-template <int K, bool REV>
-__global__ __launch_bounds__(GRP_LANES * SAMU_GROUP_MAX) __attribute__((amdgpu_waves_per_eu(4, 8))) void
-samu_gsummary_kernel(int L, int M, int C, int G, const TokenCtl* __restrict__ ctl,
-                     const uint32_t* __restrict__ drive, const float4* __restrict__ mtab, float* __restrict__ summ,
-                     const float4* __restrict__ chunk_rec, float4* __restrict__ gsum) {
-    extern __shared__ float4 gdyn[];
-    if ((int)(blockIdx.x + 1) * GRP_LANES <= M)  // uniform over the workgroup
-        gsummary_body<K, REV, true>(gdyn, G, L, M, C, ctl, drive, mtab, summ, chunk_rec, gsum);
-    else
-        gsummary_body<K, REV, false>(gdyn, G, L, M, C, ctl, drive, mtab, summ, chunk_rec, gsum);
-}
-
-// ----------------------------------------- single-pass grouped forward ---
-// The whole scan after the controller in one launch: each workgroup (one
-// group of G chunks x 64 modes, as above) reads its drive words once, forms
-// its chunks' summaries and U_q in LDS, learns the state entering its group
-// from the groups before it, and replays its chunks from the words still in
-// registers.  Chunk summaries, group summaries and group entry states never
-// go to memory as tensors, and b is read once instead of twice.
-//
-// Fixed order of evaluation.  The groups form segments of G consecutive
-// groups.  The last group of a segment publishes the state leaving it (its
-// chunks' maps applied in order to the state entering it); every other group
-// publishes its U_q = (A_q, B_q).  Group q takes the state leaving the
-// previous segment (z0 for the first) and applies the published U of the
-// segment's groups before it, oldest first: at most G - 1 maps and one
-// state, read by G waves at once.  Which words a group reads and the order it
-// applies them in depend only on q and G, never on timing, so the result is
-// bitwise the same on every run.  The only serial dependence across
-// workgroups is the chain of segment states, one link per G groups.
-//
-// Hand-off.  Each published value is its own 64-bit word (1 << 32 | float
-// bits), written and read with relaxed device-scope atomics; the controller
-// clears the area to zero before every forward, so a word is valid exactly
-// when its high half is 1.  A word is never torn, so a reader that sees
-// every word it needs valid holds consistent values, and no fence is needed
-// between words.
-//
-// Progress.  Workgroups are dispatched in grid order (mode tiles fastest,
-// then groups), and a workgroup only waits for words of lower-numbered
-// groups of its own row and mode tile, which were dispatched before it and
-// never wait for it, so every wait ends.  Each wait is nevertheless bounded
-// (SCAN_SPIN_MAX polls).
-constexpr int SCAN_SPIN_MAX = 1 << 14;
-constexpr int SCAN_PUB_WORDS = 6;  // A.re, A.im, B.re, B.im of U_q, then the leaving state
-
-// Word `i` of a group for one lane: `grp` is the group's (wave-uniform) first
-// word, `off` the lane's byte offset (mode * 8) and `Mb` = M * 8, so the
-// address is a uniform base plus a 32-bit lane offset.
-__device__ __forceinline__ uint64_t* pub_word(const uint64_t* grp, int i, uint32_t Mb, uint32_t off) {
-    return reinterpret_cast<uint64_t*>(const_cast<char*>(reinterpret_cast<const char*>(grp)) +
-                                       (size_t)i * Mb + off);
-}
-__device__ __forceinline__ uint64_t pub_load(const uint64_t* grp, int i, uint32_t Mb, uint32_t off) {
-    return __hip_atomic_load(pub_word(grp, i, Mb, off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void pub_store(uint64_t* grp, int i, uint32_t Mb, uint32_t off, float v) {
-    __hip_atomic_store(pub_word(grp, i, Mb, off), (uint64_t(1) << 32) | (uint64_t)__float_as_uint(v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ bool pub_ok(uint64_t w) { return (uint32_t)(w >> 32) == 1u; }
-__device__ __forceinline__ float pub_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
-
-// Words [i0, i0 + N) of an earlier group for this lane's mode, once all are
-// published: U as (A.re, A.im, B.re, B.im) for i0 = 0, N = 4, or the leaving
-// state as (z.re, z.im, 0, 0) for i0 = 4, N = 2.
-template <int N>
-__device__ __forceinline__ float4 wait_words(const uint64_t* grp, int i0, uint32_t Mb, uint32_t off) {
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    bool ok = false;
-    for (int it = 0; it < SCAN_SPIN_MAX; ++it) {
-        if (!ok) {
-            // the lane offset afresh each poll: addresses kept across the
-            // loop would cost two registers each
-            const uint32_t o = opaque_v(off);
-            uint64_t wv[N];
-#pragma unroll
-            for (int i = 0; i < N; ++i) wv[i] = pub_load(grp, i0 + i, Mb, o);
-            bool all = true;
-#pragma unroll
-            for (int i = 0; i < N; ++i) all = all && pub_ok(wv[i]);
-            if (all) {
-#pragma unroll
-                for (int i = 0; i < N; ++i) v[i] = pub_val(wv[i]);
-                ok = true;
-            }
-        }
-        if (__all(ok)) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
-
+// The state entering each group comes from group_handoff (common.hpp): a
+// fixed-order chain over segments of G groups, handed between workgroups
+// through tagged words that the controller clears before every forward.
 template <int K, bool F32, bool ALLACT>
 __device__ __forceinline__ void gscan_body(float4* gdyn, int G, int L, int M, int C,
                                            const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
@@ -681,59 +534,10 @@ __device__ __forceinline__ void gscan_body(float4* gdyn, int G, int L, int M, in
     group_put(comp, w, lane, A, Bv[0]);
     __syncthreads();
 
-    const uint32_t Mb = (uint32_t)M * 8u, moff = (uint32_t)mc * 8u;
-    uint64_t* mine = pub + ((size_t)b * NG + q) * SCAN_PUB_WORDS * M;  // wave-uniform
-    const int nprev = q % G;                          // earlier groups of this segment
-    const bool seg_last = nprev == G - 1 || q == NG - 1;
-    if (w == 0 && active && q + 1 < NG && !seg_last) {
-        // U_q = S_{n-1} o ... o S_0 (the right operand first), published at once
-        cf ua = {1.f, 0.f}, ub = {0.f, 0.f};
-        for (int j = 0; j < G; ++j) {  // all G chunks: a group short of G chunks is the last one
-            const float4 f = comp[j * GRP_LANES + lane];
-            ub = cfma({f.x, f.y}, ub, {f.z, f.w});
-            ua = cmul({f.x, f.y}, ua);
-        }
-        pub_store(mine, 0, Mb, moff, ua.re);
-        pub_store(mine, 1, Mb, moff, ua.im);
-        pub_store(mine, 2, Mb, moff, ub.re);
-        pub_store(mine, 3, Mb, moff, ub.im);
-    }
-    // wave w < nprev reads U of group q-1-w, wave nprev the state entering
-    // the segment
-    if (w < nprev) {
-        look[w * GRP_LANES + lane] =
-            wait_words<4>(pub + ((size_t)b * NG + q - 1 - w) * SCAN_PUB_WORDS * M, 0, Mb, moff);
-    } else if (w == nprev) {
-        float4 zs = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (q - nprev > 0)
-            zs = wait_words<2>(pub + ((size_t)b * NG + q - nprev - 1) * SCAN_PUB_WORDS * M, 4, Mb, moff);
-        else if (z0)
-            zs = make_float4(z0[(size_t)b * M + mc].x, z0[(size_t)b * M + mc].y, 0.f, 0.f);
-        look[w * GRP_LANES + lane] = zs;
-    }
-    __syncthreads();
-    if (w == 0) {
-        const float4 zs = look[nprev * GRP_LANES + lane];
-        cf z = {zs.x, zs.y};
-        for (int v = nprev - 1; v >= 0; --v) {  // oldest first
-            const float4 f = look[v * GRP_LANES + lane];
-            z = cfma({f.x, f.y}, z, {f.z, f.w});
-        }
-        if (active && q + 1 < NG && seg_last) {
-            // the state leaving the group, for the next segment: this
-            // group's chunks applied in order, as in the chain
-            cf zo = z;
-            for (int j = 0; j < G; ++j) {
-                const float4 f = comp[j * GRP_LANES + lane];
-                zo = cfma({f.x, f.y}, zo, {f.z, f.w});
-            }
-            pub_store(mine, 4, Mb, moff, zo.re);
-            pub_store(mine, 5, Mb, moff, zo.im);
-        }
-        look[lane] = make_float4(z.re, z.im, 0.f, 0.f);
-    }
-    __syncthreads();
-    const float4 gin = look[lane];
+    const GroupChunks gc{chunk_rec + (size_t)b * C, mtab[MODE_REC * mc + 2], mtab[MODE_REC * mc + 3], k[0].kappa, C};
+    const float4 gin = group_handoff<false>(comp, look, G, w, lane, q, NG, M, mc, active,
+                                            z0 ? z0 + (size_t)b * M : nullptr,
+                                            pub + (size_t)b * NG * SCAN_PUB_WORDS * M, gc);
     if (!valid) return;
     // the mode constants again (a fresh load, not registers held across the
     // hand-off)
@@ -835,25 +639,6 @@ hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const flo
 
 static size_t samu_group_lds_bytes(int G, int K) { return (size_t)G * GRP_LANES * sizeof(float4) + (size_t)G * K * sizeof(TokenCtl); }
 
-hipError_t launch_samu_gsummary(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
-                                const void* drive, bool reverse, float* summ, const float* chunk_rec, float* gsum,
-                                hipStream_t s) {
-    const dim3 grid((unsigned)ceil_div(p.M, GRP_LANES), ch.NG, ch.B);
-    const dim3 block(GRP_LANES * ch.G);
-    const size_t lds = samu_group_lds_bytes(ch.G, ch.K);
-    const int id = reverse ? K_SAMU_REV_SUMMARY : K_SAMU_SUMMARY;
-#define GSUM_CASE(KK, RR)                                                                                  \
-    LRS_LAUNCH(id, (samu_gsummary_kernel<KK, RR>), grid, block, lds, s, p.L, p.M, ch.C, ch.G,            \
-               (const TokenCtl*)ctl, (const uint32_t*)drive, (const float4*)mtab, summ,                    \
-               (const float4*)chunk_rec, (float4*)gsum)
-    if (ch.K == 32) {
-        if (reverse) GSUM_CASE(32, true); else GSUM_CASE(32, false);
-    } else {
-        if (reverse) GSUM_CASE(16, true); else GSUM_CASE(16, false);
-    }
-#undef GSUM_CASE
-    return hipGetLastError();
-}
 
 
 }  // namespace lrs

@@ -86,7 +86,7 @@ int main() {
             EXPECT(samu_scan_fwd(B, L, D, K, G, P(X), P(Bd), F(W1), F(W2), F(A1), F(A2), F(NU), F(TH), nullptr,
                                  P(Y), dt, nullptr, P(SV), P(WS), samu_scan_workspace_bytes(B, L, D, K, G, 0),
                                  nullptr) == SCAN_ERR_DEVICE);
-    EXPECT(samu_scan_fwd_noalloc(4, 131072, 2048, 32, 0, P(X), P(Bd), F(W1), F(W2), F(A1), F(A2), F(NU), F(TH),
+    EXPECT(samu_scan_fwd_noalloc(16, 131072, 2048, 32, 0, P(X), P(Bd), F(W1), F(W2), F(A1), F(A2), F(NU), F(TH),
                                  nullptr, P(Y), 0, nullptr, P(SV), nullptr) == SCAN_ERR_WORKSPACE);
     for (int G : {0, 1, 17})
         EXPECT(samu_scan_bwd(B, L, D, K, G, P(X), P(Bd), F(W1), F(W2), F(A1), F(A2), F(NU), F(TH), P(SV),

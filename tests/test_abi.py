@@ -80,10 +80,10 @@ def test_saved_and_workspace_sizes():
     need = B * L * (4 + 4 + 8 + 16) + M * 64 + B * C * M * 8 + B * C * M * 8 + B * C * 16
     assert need <= sv < need + 9 * 256
     # forward workspace, grouped path (G <= 16): the single-pass forward's
-    # hand-off words, six 8-byte words per (group, mode)
+    # hand-off words, two 8-byte words per (group, mode)
     G = 4
     NG = C // G
-    need = B * NG * M * 48
+    need = B * NG * M * 16
     assert need <= scan.samu_scan_workspace_bytes(B, L, D, K, G, False) < need + 256
     # three-kernel prefix (G > 16): compressed chunk summaries (8 B per mode
     # plus a 16 B record per chunk), group summaries (16 B per mode) and group
@@ -248,7 +248,7 @@ def test_noalloc_forward_rejects_before_enqueue():
     p = [f(0x100000), f(0x200000), f(0x300000), f(0x300100), f(0x300200), f(0x300210), f(0x300300),
          f(0x300400)]
     # a forward workspace above the 32 MiB static scratch
-    assert L.samu_scan_fwd_noalloc(4, 131072, 2048, 32, 0, *p, None, f(0x400000), 0, None, f(0x500000),
+    assert L.samu_scan_fwd_noalloc(16, 131072, 2048, 32, 0, *p, None, f(0x400000), 0, None, f(0x500000),
                                    None) == -4
     assert b"static scratch" in L.scan_last_error()
     # an unsupported shape is named by the forward's own check

@@ -74,7 +74,7 @@ def test_noalloc_forward_matches_allocating_forward():
 
 
 def test_noalloc_rejects_shapes_beyond_its_scratch():
-    B, L, D, K = 4, 131072, 2048, 32       # forward workspace well above 32 MiB
+    B, L, D, K = 16, 131072, 2048, 32      # forward workspace well above 32 MiB
     need = scan.samu_scan_workspace_bytes(B, L, D, K, 0, False)
     assert need > (32 << 20)
     x = torch.empty(16, dtype=torch.uint8, device="cuda")
