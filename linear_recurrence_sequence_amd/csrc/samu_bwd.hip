@@ -306,15 +306,20 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
     const ModeConst k = load_mode(mtab, mm);
     const float4 ph = mtab[MODE_REC * mm + (c == C - 1 ? 3 : 2)];
     const float4 rec = chunk_rec[bc];
-    uint32_t gw[K];
-    {
+    // the replay's requests as the grouped replay makes them (its states, all
+    // drive words, the last sub-chunk's cotangent words), then the earlier
+    // sub-chunks' cotangent words, which only the summary uses here (the
+    // replay requests them again as their sub-chunk starts)
+    cf ck[NH];
+    uint32_t bw[K], gw[K];
+    bwd_issue<K, H, false, true>(ck, bw, gw, kc, row0, M, mm, bc, entries, mid, drive, dy);
+    constexpr int KE = K - H;  // tokens of the earlier sub-chunks
+    uint32_t ge[KE > 0 ? KE : 1];
+    if (KE > 0) {
         const ChunkRows cr(dy + row0, kc, M);
 #pragma unroll
-        for (int j = 0; j < K; ++j) gw[K - 1 - j] = cr.load(K - 1 - j, mm);
+        for (int j = 0; j < KE; ++j) ge[KE - 1 - j] = cr.load(KE - 1 - j, mm);
     }
-    cf ck[NH];
-    uint32_t bw[K];
-    bwd_issue<K, H, false, true, false>(ck, bw, gw, kc, row0, M, mm, bc, entries, mid, drive, dy);
     if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
     wave_lds_sync();
     // the chunk's conjugate reverse summary: carry -> conj(lambda_t) (dy_t + carry)
@@ -327,7 +332,8 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
             if (i < kq) {
                 const TokenCtl t = sctl[i];
                 const cf lam = mode_lambda(k, t.E, t.C, t.S);
-                Bv = cmulc(lam, {Bv.re + bf16_lo(gw[i]), Bv.im + bf16_hi(gw[i])});
+                const uint32_t x = i >= KE ? gw[i] : ge[i < KE ? i : 0];
+                Bv = cmulc(lam, {Bv.re + bf16_lo(x), Bv.im + bf16_hi(x)});
             }
         }
         A = chunk_transition<true>(k.kappa, ph, rec);
