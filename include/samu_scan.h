@@ -26,15 +26,18 @@
  *   - Gradients overwrite their buffers.  Outputs must not overlap inputs
  *     (SCAN_ERR_ALIAS).
  *   - Results are bitwise deterministic for the same inputs, (K, G), device
- *     and library build: every reduction has a fixed order; no atomics.
+ *     and library build: every reduction has a fixed order and nothing is
+ *     accumulated atomically.  (The SAMU single-pass scans hand states
+ *     between workgroups through atomic loads and stores of whole words, in
+ *     an order of evaluation fixed by the group index alone.)
  *   - K (chunk length) is 16 or 32.  G (chunks per group of the two-level
  *     prefix) is >= 1, or 0 for the library's choice.
- *       SAMU: G = 0 means groups of 8 chunks.  Any G <= 16 runs the grouped
- *       path (one workgroup per group of chunks: the group's composition U_g
- *       and the state entering each chunk are formed on chip, with one scan
- *       over the groups between the summary and replay launches); G > 16
- *       runs the three-launch prefix (compose U_g, scan over groups, chunk
- *       entries).
+ *       SAMU: G = 0 means groups of 8 chunks.  Any G <= 16 runs the
+ *       single-pass scans (one workgroup per group of chunks forms the
+ *       chunk summaries, takes the state entering its group from the
+ *       earlier groups and replays, in one launch per direction); G > 16
+ *       runs separate summary, three-launch prefix (compose U_g, scan over
+ *       groups, chunk entries) and replay launches.
  *       RG-LRU: G = 0 means the serial prefix when ceil(L/K) <= 128, else
  *       groups of max(16, ceil(ceil(L/K) / 128)) chunks.
  *     G >= ceil(L/K) gives a single group (the serial chunk-to-chunk

@@ -1,7 +1,8 @@
 // noalloc.hip -- samu_scan_fwd for callers that cannot allocate device memory
 // (code under stream capture, tight serving loops): the forward workspace
-// (compressed chunk summaries, group summaries, group entry states) lives in
-// one file-scope device array instead of a caller buffer.
+// (the single-pass forward's hand-off words, or for groups longer than 16
+// chunks the three-launch prefix's summaries and group states) lives in one
+// file-scope device array instead of a caller buffer.
 //
 // Host code never passes the array's name to a kernel or a copy: on the host
 // that name is only a stand-in for the symbol.  Its device address is looked

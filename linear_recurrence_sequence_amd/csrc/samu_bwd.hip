@@ -16,8 +16,9 @@
 // With gamma = conj(lambda_t) g_t conj(z_{t-1}) = g_t conj(lambda_t z_{t-1}):
 //   d nu_m = -sum E_t Re gamma,  d theta_m = sum Im gamma,
 //   c-bar_t = -E_t sum_m nu_m Re gamma,  d-bar_t = sum_m Im gamma.
-// No atomics anywhere: every sum has a fixed order, so results are bitwise
-// reproducible run to run.
+// No atomic accumulation: every sum has a fixed order (the single-pass scan
+// hands whole words between workgroups in an order fixed by the group
+// index), so results are bitwise reproducible run to run.
 #include "common.hpp"
 
 namespace lrs {

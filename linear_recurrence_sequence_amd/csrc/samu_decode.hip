@@ -12,10 +12,13 @@
 //   z' = lambda z + b,  y = z'.
 //
 // Grid (ceil(M / 256), B): each workgroup forms the two dot products (and,
-// without a prepared table, the two direction norms) of its batch row --
-// every mode block repeats this small reduction, which measured faster than
-// one larger workgroup per row at B = 1..256 -- then 256 lanes advance one
-// mode each.  Sums run in a fixed order, so a step is bitwise reproducible.
+// without a prepared table, the two direction norms) of its batch row, 16
+// bytes of the row per thread and step, then 256 lanes advance one mode
+// each.  Every mode block repeats the row's small reduction, which measured
+// faster than one larger workgroup per row, and faster than several rows per
+// workgroup sharing the direction loads (the rows then run one after another
+// in each workgroup).  Sums run in a fixed order, so a step is bitwise
+// reproducible.
 #include "common.hpp"
 
 namespace lrs {
@@ -29,24 +32,29 @@ constexpr int DEC_WAVES = DEC_THREADS / 64;
 // reduction and no amplitude tanh per step).
 template <bool F32, bool TAB>
 __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
-    int D, int M, const uint32_t* __restrict__ x_sel, const uint32_t* __restrict__ drive,
+    int B, int D, int M, const uint32_t* __restrict__ x_sel, const uint32_t* __restrict__ drive,
     const float* __restrict__ w_phi, const float* __restrict__ w_r, const float* __restrict__ a_phi,
     const float* __restrict__ a_r, const float* __restrict__ nu, const float* __restrict__ theta,
     const float4* __restrict__ table, const float2* z_in, float2* z_out, void* __restrict__ y) {
-    __shared__ float red[4][DEC_WAVES];
+    constexpr int R = 1;  // batch rows per workgroup
+    __shared__ float red[2 * R + 2][DEC_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.y;
+    const int b0 = blockIdx.y * R;
     const int W = D / 2;  // selector words per row
-    const uint32_t* xr = x_sel + (size_t)b * W;
 
-    // this lane's mode: its inputs are requested first and its constant
-    // phasor is formed (or loaded) while the selector reduction is in flight
+    // this lane's mode in each row: its inputs are requested first and its
+    // constant phasor is formed (or loaded) while the reduction is in flight
     const int m = blockIdx.x * DEC_THREADS + tid;
     const bool act = m < M;
     const int mc = act ? m : M - 1;
-    const size_t i = (size_t)b * M + mc;
-    const float2 z0 = z_in ? z_in[i] : make_float2(0.f, 0.f);
-    const uint32_t bw = drive[i];
+    float2 zr[R];
+    uint32_t bw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const size_t i = (size_t)min(b0 + r, B - 1) * M + mc;
+        zr[r] = z_in ? z_in[i] : make_float2(0.f, 0.f);
+        bw[r] = drive[i];
+    }
     ModeConst k;
     float4 inv = make_float4(0.f, 0.f, 0.f, 0.f);
     float nu_m = 0.f, th_m = 0.f;
@@ -58,67 +66,109 @@ __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
         th_m = theta[mc];
     }
 
-    float sp = 0.f, sr = 0.f, np = 0.f, nr = 0.f;
-#pragma unroll 4
-    for (int j = tid; j < W; j += DEC_THREADS) {
-        const uint32_t xw = xr[j];
-        const float2 wp = reinterpret_cast<const float2*>(w_phi)[j];
-        const float2 wr = reinterpret_cast<const float2*>(w_r)[j];
-        const float x0 = bf16_lo(xw), x1 = bf16_hi(xw);
-        sp = fmaf(x1, wp.y, fmaf(x0, wp.x, sp));
-        sr = fmaf(x1, wr.y, fmaf(x0, wr.x, sr));
+    // dot products over 8 selector values (16 bytes) per thread and step;
+    // each direction chunk is loaded once for the R rows
+    float sp[R], sr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) { sp[r] = 0.f; sr[r] = 0.f; }
+    float np = 0.f, nr = 0.f;
+    const int W4 = W >> 2;  // 16-byte selector pieces per row (D % 8 == 0)
+    for (int j = tid; j < W4; j += DEC_THREADS) {
+        uint4 xv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            xv[r] = reinterpret_cast<const uint4*>(x_sel + (size_t)min(b0 + r, B - 1) * W)[j];
+        const float4 p0 = reinterpret_cast<const float4*>(w_phi)[2 * j];
+        const float4 p1 = reinterpret_cast<const float4*>(w_phi)[2 * j + 1];
+        const float4 q0 = reinterpret_cast<const float4*>(w_r)[2 * j];
+        const float4 q1 = reinterpret_cast<const float4*>(w_r)[2 * j + 1];
+        const float wp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        const float wr[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t xw[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sp[r] = fmaf(bf16_lo(xw[e]), wp[2 * e], sp[r]);
+                sp[r] = fmaf(bf16_hi(xw[e]), wp[2 * e + 1], sp[r]);
+                sr[r] = fmaf(bf16_lo(xw[e]), wr[2 * e], sr[r]);
+                sr[r] = fmaf(bf16_hi(xw[e]), wr[2 * e + 1], sr[r]);
+            }
+        }
         if (!TAB) {
-            np = fmaf(wp.y, wp.y, fmaf(wp.x, wp.x, np));
-            nr = fmaf(wr.y, wr.y, fmaf(wr.x, wr.x, nr));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                np = fmaf(wp[e], wp[e], np);
+                nr = fmaf(wr[e], wr[e], nr);
+            }
         }
     }
     if (tid == 0) {  // the constant 1 of x~ and the bias slot of each direction
         const float bp = w_phi[D], br = w_r[D];
-        sp += bp;
-        sr += br;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            sp[r] += bp;
+            sr[r] += br;
+        }
         np = fmaf(bp, bp, np);
         nr = fmaf(br, br, nr);
     }
     if (!TAB) k = mode_const(nu_m, th_m);
-    sp = wave_sum(sp);
-    sr = wave_sum(sr);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        sp[r] = wave_sum(sp[r]);
+        sr[r] = wave_sum(sr[r]);
+    }
     if (!TAB) {
         np = wave_sum(np);
         nr = wave_sum(nr);
     }
     if (lane == 0) {
-        red[0][wave] = sp;
-        red[1][wave] = sr;
-        red[2][wave] = np;
-        red[3][wave] = nr;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            red[2 * r][wave] = sp[r];
+            red[2 * r + 1][wave] = sr[r];
+        }
+        red[2 * R][wave] = np;
+        red[2 * R + 1][wave] = nr;
     }
     __syncthreads();
-    float Sp = 0.f, Sr = 0.f, Np = 0.f, Nr = 0.f;
+    float Np = 0.f, Nr = 0.f;
+    if (!TAB) {
 #pragma unroll
-    for (int w = 0; w < DEC_WAVES; ++w) {
-        Sp += red[0][w];
-        Sr += red[1][w];
-        if (!TAB) {
-            Np += red[2][w];
-            Nr += red[3][w];
+        for (int w = 0; w < DEC_WAVES; ++w) {
+            Np += red[2 * R][w];
+            Nr += red[2 * R + 1][w];
         }
     }
-    const float p = tanhf(TAB ? Sp * inv.x : Sp / sqrtf(Np));
-    const float r = tanhf(TAB ? Sr * inv.y : Sr / sqrtf(Nr));
-    const float q = r / (1.0f + r * r);
     const float sM = sqrtf((float)M);
-    const float d = (TAB ? inv.z : tanhf(a_phi[0]) / sM) * p;
-    const float c = (TAB ? inv.w : tanhf(a_r[0]) / sM) * q;
-    const float E = expf(c);
-    float S, Cd;
-    sincosf(d, &S, &Cd);
-
+    const float amp_p = TAB ? inv.z : tanhf(a_phi[0]) / sM;
+    const float amp_r = TAB ? inv.w : tanhf(a_r[0]) / sM;
     if (!act) return;
-    const cf lam = mode_lambda(k, E, Cd, S);
-    const cf z = cfma(lam, {z0.x, z0.y}, {bf16_lo(bw), bf16_hi(bw)});
-    z_out[i] = make_float2(z.re, z.im);
-    if (F32) reinterpret_cast<float2*>(y)[i] = make_float2(z.re, z.im);
-    else reinterpret_cast<uint32_t*>(y)[i] = pack_bf16x2(z.re, z.im);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (b0 + r >= B) break;  // uniform over the workgroup
+        float Sp = 0.f, Sr = 0.f;
+#pragma unroll
+        for (int w = 0; w < DEC_WAVES; ++w) {
+            Sp += red[2 * r][w];
+            Sr += red[2 * r + 1][w];
+        }
+        const float p = tanhf(TAB ? Sp * inv.x : Sp / sqrtf(Np));
+        const float rr = tanhf(TAB ? Sr * inv.y : Sr / sqrtf(Nr));
+        const float q = rr / (1.0f + rr * rr);
+        const float d = amp_p * p;
+        const float c = amp_r * q;
+        const float E = expf(c);
+        float S, Cd;
+        sincosf(d, &S, &Cd);
+        const cf lam = mode_lambda(k, E, Cd, S);
+        const cf z = cfma(lam, {zr[r].x, zr[r].y}, {bf16_lo(bw[r]), bf16_hi(bw[r])});
+        const size_t i = (size_t)(b0 + r) * M + mc;
+        z_out[i] = make_float2(z.re, z.im);
+        if (F32) reinterpret_cast<float2*>(y)[i] = make_float2(z.re, z.im);
+        else reinterpret_cast<uint32_t*>(y)[i] = pack_bf16x2(z.re, z.im);
+    }
 }
 
 // The table of samu_decode_kernel<.., true>: the per-mode constant records
@@ -184,7 +234,7 @@ hipError_t launch_samu_decode(int B, int D, const void* x_sel, const void* b, co
     const int M = D / 2;
     const dim3 grid((unsigned)ceil_div(M, DEC_THREADS), (unsigned)B);
 #define DEC_CASE(FF, TT)                                                                                    \
-    LRS_LAUNCH(K_SAMU_DECODE, (samu_decode_kernel<FF, TT>), grid, dim3(DEC_THREADS), 0, s, D, M,          \
+    LRS_LAUNCH(K_SAMU_DECODE, (samu_decode_kernel<FF, TT>), grid, dim3(DEC_THREADS), 0, s, B, D, M,       \
                (const uint32_t*)x_sel, (const uint32_t*)b, w_phi, w_r, a_phi, a_r, nu, theta,              \
                (const float4*)table, (const float2*)z_in, (float2*)z_out, y)
     if (table) {

@@ -191,11 +191,15 @@ def test_samu_metric_shape_full_parity():
 
 
 # The pages' other full-size F+B workloads: long sequences at D=1024 with
-# 64-chunk groups and a zero initial state; wide states at L=32768 with a
-# nonzero initial state and its gradient.
+# the pages' 64-chunk groups (three-launch prefix) and with the default
+# grouping the benchmark times (single-pass scans, 256 and 512 groups handed
+# on in a chain), zero and nonzero initial states; wide states at L=32768
+# with a nonzero initial state and its gradient.
 FULL_CASES = [
     ("long_b1_l65536_d1024", 1, 65536, 1024, 32, 64, None, 2001),
     ("long_b1_l131072_d1024", 1, 131072, 1024, 32, 64, None, 2002),
+    ("long_b1_l65536_d1024_default_groups", 1, 65536, 1024, 32, 0, None, 2003),
+    ("long_b1_l131072_d1024_default_groups", 1, 131072, 1024, 32, 0, 0.1, 2004),
     ("wide_b1_l32768_d1024", 1, 32768, 1024, 32, 0, 0.1, 3000),
     ("wide_b1_l32768_d1536", 1, 32768, 1536, 32, 0, 0.1, 3001),
     ("wide_b1_l32768_d2560", 1, 32768, 2560, 32, 0, 0.1, 3003),
