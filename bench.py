@@ -723,7 +723,8 @@ def main():
         layer_ms, _ = timed.graph(layer_step, args.steps, 1)
         _, lprof = timed(layer_step, args.steps, 1, True)
         BLD = B * L * D
-        pbytes = {"gate_projection": 6 * BLD, "gate_projection_dx": 8 * BLD, "gate_projection_dw": 6 * BLD}
+        pbytes = {"gate_projection": 6 * BLD, "gate_projection_dx": 8 * BLD, "gate_projection_dw": 6 * BLD,
+                  "gate_projection_adjoint": 10 * BLD}
         proj = {}
         for n, (t, c) in lprof.items():
             if n.startswith("gate_projection"):

@@ -54,7 +54,8 @@ static const char* const kKernelNames[K_NUM_KERNELS] = {
     "samu_controller_bwd", "samu_params", "rglru_chunk_summary", "rglru_replay",
     "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha", "samu_decode",
     "baseline_sequential", "baseline_associative", "gate_projection", "gate_projection_dx",
-    "gate_projection_dw", "gate_projection_reduce", "samu_forward_scan", "samu_backward_scan", "clear"};
+    "gate_projection_dw", "gate_projection_reduce", "samu_forward_scan", "samu_backward_scan", "clear",
+    "gate_projection_adjoint"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 

@@ -53,6 +53,9 @@ constexpr int FPAD = 4;   // FP32 elements of LDS row padding
 #ifndef LRS_GP_DW_RANGE
 #define LRS_GP_DW_RANGE 2048    // tokens per dW partial sum
 #endif
+#ifndef LRS_GP_ADJ_FUSED
+#define LRS_GP_ADJ_FUSED 1      // BF16 adjoint as one pass (dx and dW from shared tiles)
+#endif
 
 template <int MT>
 struct Geo {
@@ -746,6 +749,265 @@ __global__ __launch_bounds__(64 * dw_waves<MT>()) void gate_proj_dw_kernel(
     }
 }
 
+// ------------------------------------------- adjoint in one pass (BF16)
+// grid (16 blocks, ranges of LRS_GP_DW_RANGE tokens).  dx and dW need the
+// same cotangent tiles, so one workgroup streams x, dl^x, dl^a and dx_in
+// through LDS once and splits its waves by product: waves [0, NWX) form
+// dx (the dx kernel's layout: W_g^T fragments in registers, cotangent rows
+// as B), waves [NWX, NWX + NWW) form the dW and db partials of the range
+// (the dW kernel's layout: transposing LDS reads, accumulators in
+// registers).  The two roles run separate copies of one tile loop, so the W
+// fragments of one and the accumulators of the other never hold registers
+// at the same time; both copies pass the same barriers in the same order.
+// Tiles sit in the dW kernel's LDS layout (row stride an odd multiple of 16
+// elements); rows past the range are zero, which dW needs and dx never
+// stores.  The LDS holds two tiles: tile i + 1 is written while tile i is
+// multiplied, so that write needs no barrier of its own.
+template <int MT>
+constexpr int adj_waves() {
+    return dx_waves<MT>() + dw_waves<MT>();
+}
+// the matrix-core adjoint in one pass: BF16 cotangents and up to 8 tiles per
+// block (wider blocks would not fit both roles' registers at four waves per
+// SIMD)
+template <int MT>
+constexpr bool adj_fused() {
+    return MT <= 8 && adj_waves<MT>() <= 16;
+}
+#ifndef LRS_GP_ADJ_DBUF
+#define LRS_GP_ADJ_DBUF 1       // two LDS tiles (the next tile is written during the products)
+#endif
+#ifndef LRS_GP_ADJ_DIRECT
+#define LRS_GP_ADJ_DIRECT 0     // dx written by the lanes that form it (measured slower than staged rows)
+#endif
+template <int MT>
+constexpr size_t adj_lds_bytes() {
+    constexpr int Db = 16 * MT;
+    constexpr size_t tiles = (size_t)(LRS_GP_ADJ_DBUF ? 2 : 1) * 4 * TT * dw_row<MT>() * 2;  // x, dl^x, dl^a, dx
+    constexpr size_t wts = (size_t)2 * Db * (Db + XPAD) * 2;                                 // W_x^T, W_a^T
+    return tiles > wts ? tiles : wts;
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * adj_waves<MT>()) void gate_proj_adj_kernel(
+    int BL, int D, int range, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_x,
+    const uint16_t* __restrict__ w_a, const uint16_t* __restrict__ dlx, const uint16_t* __restrict__ dla,
+    const uint16_t* dx_in, uint16_t* dx_out, float* __restrict__ dw_part, float* __restrict__ db_part) {
+    using G = Geo<MT>;
+    constexpr int Db = G::Db, NWX = dx_waves<MT>(), NWW = dw_waves<MT>(), NT = 64 * (NWX + NWW);
+    constexpr int T = TT, RS = dw_row<MT>(), RW = Db + XPAD, R = dw_rows<MT>();
+    constexpr int WPP = NWX / G::P, TGW = (T / 16) / WPP;  // dx: waves per pair, token groups per wave
+    constexpr int CPR = Db / 8, NCH = T * CPR, S = (NCH + NT - 1) / NT;  // 16-byte chunks per plane
+    constexpr bool DBUF = LRS_GP_ADJ_DBUF != 0, DIRECT = LRS_GP_ADJ_DIRECT != 0;
+    constexpr int TILE = 4 * T * RS;  // elements of one tile's four planes
+    static_assert(TGW >= 1 && 64 * (NWX + NWW) <= 1024, "adjoint workgroup shape");
+    extern __shared__ uint16_t gp_lds[];  // per tile: x [T][RS], dl^x, dl^a [2][T][RS], dx rows [T][RS]
+    const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int blk = blockIdx.x, r = blockIdx.y;
+    const size_t tr0 = (size_t)r * range, tr1 = min((size_t)BL, tr0 + range);
+    const int ntile = (int)((tr1 - tr0 + T - 1) / T);
+
+    // W_x^T and W_a^T of the block, for the dx waves' fragments
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+        stage_transposed_bf16(gp_lds + gg * Db * RW, RW, (gg ? w_a : w_x) + (size_t)blk * Db * Db, Db, Db, Db, NT);
+    __syncthreads();
+
+    // Tile loads, shared by both roles: unconditional (rows past the range
+    // re-read its last row, tiles past it its last tile); a row mask zeroes
+    // those rows when the tile is written to LDS.  Addresses are a uniform
+    // tile base plus a 32-bit lane offset in bytes.
+    struct Regs {
+        v4u v[4][S];  // x, dl^x, dl^a, dx_in
+        uint32_t ok;  // bit s: the token row of chunk s is in the range
+    };
+    const char* const src[4] = {reinterpret_cast<const char*>(x), reinterpret_cast<const char*>(dlx),
+                                reinterpret_cast<const char*>(dla), reinterpret_cast<const char*>(dx_in)};
+    auto load = [&](Regs& b, int i) {
+        const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * T;
+        const int last = (int)(tr1 - 1 - t0);  // the range's last row, counted from t0
+        b.ok = 0;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int c = NCH % NT == 0 ? threadIdx.x + s * NT : min((int)threadIdx.x + s * NT, NCH - 1);
+            const int row = c / CPR, ch = c - row * CPR;
+            b.ok |= (i < ntile && row <= last) ? 1u << s : 0u;
+            const uint32_t off = (uint32_t)((min(row, last) * D + blk * Db + 8 * ch) * 2);
+#pragma unroll
+            for (int pl = 0; pl < 4; ++pl) b.v[pl][s] = ld16(src[pl] + t0 * D * 2 + off);
+        }
+    };
+    auto tile_of = [&](int i) { return gp_lds + (DBUF ? (i & 1) * TILE : 0); };
+    auto store = [&](const Regs& b, uint16_t* tl) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int c = threadIdx.x + s * NT;
+            if (NCH % NT != 0 && c >= NCH) continue;
+            const int row = c / CPR, ch = c - row * CPR;
+            const bool ok = (b.ok >> s) & 1u;
+#pragma unroll
+            for (int pl = 0; pl < 4; ++pl) st16(tl + (pl * T + row) * RS + 8 * ch, ok ? b.v[pl][s] : zero4());
+        }
+    };
+    // the staged dx rows of tile i, written out whole (when not DIRECT)
+    auto flush = [&](int i, const uint16_t* tl) {
+        const size_t t0 = tr0 + (size_t)i * T;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int c = threadIdx.x + s * NT;
+            if (NCH % NT != 0 && c >= NCH) continue;
+            const int row = c / CPR, ch = c - row * CPR;
+            if (t0 + row < tr1)
+                out_store<u32x4_t>(reinterpret_cast<char*>(dx_out) + t0 * D * 2 +
+                                       (uint32_t)((row * D + blk * Db + 8 * ch) * 2),
+                                   __builtin_bit_cast(u32x4_t, ld16(tl + (3 * T + row) * RS + 8 * ch)));
+        }
+    };
+    // The tile loop of both roles.  With DBUF, tile i + 1 goes to the other
+    // LDS tile while tile i is multiplied (that tile was last read before the
+    // previous barrier); otherwise a barrier keeps them apart.
+    auto run = [&](auto&& compute) {
+        Regs rr;
+        load(rr, 0);
+        sched_fence();
+        __syncthreads();  // every dx wave holds its fragments: the tiles may overwrite the weights
+        if (DBUF) {
+            store(rr, tile_of(0));
+            load(rr, 1);
+            sched_fence();
+            __syncthreads();
+        }
+        for (int i = 0; i < ntile; ++i) {
+            if (DBUF) {
+                store(rr, tile_of(i + 1));
+                load(rr, i + 2);
+            } else {
+                store(rr, tile_of(i));
+                load(rr, i + 1);
+                sched_fence();
+                __syncthreads();
+            }
+            sched_fence();
+            compute(i, tile_of(i));
+            sched_fence();
+            __syncthreads();
+            if (!DIRECT) {
+                flush(i, tile_of(i));
+                __syncthreads();  // the rows are read before a later tile overwrites them
+            }
+        }
+    };
+
+    if (wave < NWX) {
+        // ---- dx: A = W_g^T rows (registers), B = cotangent rows
+        const int p = wave / WPP, tgb = (wave - p * WPP) * TGW;
+        const int c0 = 32 * p + 8 * grp;
+        const bool cv = c0 + 8 <= Db;
+        v4u wf[2][2][G::KS];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = pair_chan(p, col, h);
+#pragma unroll
+                for (int ks = 0; ks < G::KS; ++ks) {
+                    const int o0 = 32 * ks + 8 * grp;
+                    wf[gg][h][ks] = (k < Db && o0 < Db) ? ld16(gp_lds + (gg * Db + k) * RW + o0) : zero4();
+                }
+            }
+        run([&](int i, uint16_t* tl) {
+            const uint16_t* const sl = tl + T * RS;
+            uint16_t* const sio = tl + 3 * T * RS;
+            const size_t t0 = tr0 + (size_t)i * T;
+#pragma unroll
+            for (int q = 0; q < TGW; ++q) {
+                const int tok = (tgb + q) * 16 + col;
+                uint16_t* const sdx = sio + tok * RS + min(c0, Db - 8);
+                const v4u in0 = ld16(sdx);
+                v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+                for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+                    for (int ks = 0; ks < G::KS; ++ks) {
+                        const bool half = G::ODD && ks == G::KS - 1;
+                        const int o0 = 32 * ks + 8 * grp - ((half && grp >= 2) ? 16 : 0);
+                        v4u bf = ld16(sl + (gg * T + tok) * RS + o0);
+                        if (half && grp >= 2) bf = zero4();
+                        a0 = mfma(wf[gg][0][ks], bf, a0);
+                        a1 = mfma(wf[gg][1][ks], bf, a1);
+                    }
+                const v4u r0{pack_bf16x2(bf16_lo(in0.x) + a0[0], bf16_hi(in0.x) + a0[1]),
+                             pack_bf16x2(bf16_lo(in0.y) + a0[2], bf16_hi(in0.y) + a0[3]),
+                             pack_bf16x2(bf16_lo(in0.z) + a1[0], bf16_hi(in0.z) + a1[1]),
+                             pack_bf16x2(bf16_lo(in0.w) + a1[2], bf16_hi(in0.w) + a1[3])};
+                if (DIRECT) {
+                    if (cv && t0 + tok < tr1)
+                        out_store<u32x4_t>(reinterpret_cast<char*>(dx_out) + t0 * D * 2 +
+                                               (uint32_t)((tok * D + blk * Db + c0) * 2),
+                                           __builtin_bit_cast(u32x4_t, r0));
+                } else if (cv) {
+                    st16(sdx, r0);
+                }
+            }
+        });
+    } else {
+        // ---- dW, db: partial sums over the range, tokens as the reduction index
+        const int dv = wave - NWX;
+        v4f acc[R][MT + 1];
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int n = 0; n <= MT; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
+        run([&](int, uint16_t* tl) {
+            const uint16_t* const sx = tl;
+            const uint16_t* const sl = tl + T * RS;
+#pragma unroll
+            for (int kt = 0; kt < T; kt += 32) {
+                const int toff = (kt + 8 * grp + (col >> 2)) * RS + 4 * (col & 3);  // this lane's read address
+                v4u af[R];
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int row = dv * R + j;  // gate row / MT, tile row % MT
+                    const int rc = row < 2 * MT ? row : 0;
+                    const int gg = rc / MT, mo = rc - gg * MT;
+                    af[j] = tr_frag(sl + gg * T * RS + toff + mo * 16, RS);
+                }
+                // one B fragment at a time (the accumulators leave no room
+                // to request them all at once)
+#pragma unroll
+                for (int n = 0; n <= MT; ++n) {
+                    const uint32_t one = col == 0 ? 0x3f803f80u : 0u;  // the bias tile's column (1, 0, ..., 0)
+                    const v4u bf = n < MT ? tr_frag(sx + toff + n * 16, RS) : v4u{one, one, one, one};
+#pragma unroll
+                    for (int j = 0; j < R; ++j) {
+                        if (2 * MT % NWW != 0 && dv * R + j >= 2 * MT) continue;
+                        acc[j][n] = mfma(af[j], bf, acc[j][n]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        });
+        // D[o][k]: lane holds o = mo 16 + 4 grp + e, k = n 16 + col
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int row = dv * R + j;
+            if (row >= 2 * MT) continue;
+            const int gg = row / MT, mo = row - gg * MT;
+            float* dst = dw_part + ((((size_t)r * 2 + gg) * 16 + blk) * Db + mo * 16 + 4 * grp) * Db + col;
+#pragma unroll
+            for (int n = 0; n < MT; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(size_t)e * Db + n * 16] = acc[j][n][e];
+            if (col == 0) {
+                float* db = db_part + ((size_t)r * 2 + gg) * D + (size_t)blk * Db + mo * 16 + 4 * grp;
+                *reinterpret_cast<float4*>(db) =
+                    make_float4(acc[j][MT][0], acc[j][MT][1], acc[j][MT][2], acc[j][MT][3]);
+            }
+        }
+    }
+}
+
 // Sum of the range partials in range order (FP64): dw [2][16][Db][Db], db [2][D].
 // The loads of eight ranges are issued ahead of their additions.
 __global__ __launch_bounds__(256) void gate_proj_reduce_kernel(int n_ranges, int nw, int D,
@@ -802,6 +1064,15 @@ hipError_t bwd_mt(int BL, int D, const void* x, const void* w_x, const void* w_a
                   const void* dx_in, void* dx_out, float* dw_part, float* db_part, hipStream_t s) {
     constexpr size_t lds_dx = dx_lds_bytes<MT, F32>(), lds_dw = dw_lds_bytes<MT, F32>();
     hipError_t e;
+    if constexpr (!F32 && LRS_GP_ADJ_FUSED && adj_fused<MT>()) {
+        constexpr size_t lds = adj_lds_bytes<MT>();
+        if ((e = allow_lds(gate_proj_adj_kernel<MT>, lds)) != hipSuccess) return e;
+        LRS_LAUNCH(K_GATE_PROJ_ADJ, gate_proj_adj_kernel<MT>, dim3(16, (unsigned)gate_proj_ranges(BL)),
+                   dim3(64 * adj_waves<MT>()), lds, s, BL, D, LRS_GP_DW_RANGE, (const uint16_t*)x,
+                   (const uint16_t*)w_x, (const uint16_t*)w_a, (const uint16_t*)dlx, (const uint16_t*)dla,
+                   (const uint16_t*)dx_in, (uint16_t*)dx_out, dw_part, db_part);
+        return hipGetLastError();
+    }
     if ((e = allow_lds(gate_proj_dx_kernel<MT, F32>, lds_dx)) != hipSuccess) return e;
     if ((e = allow_lds(gate_proj_dw_kernel<MT, F32>, lds_dw)) != hipSuccess) return e;
     const int range = stream_range(BL);

@@ -40,6 +40,7 @@ enum KernelId {
     K_SAMU_FWD_SCAN,
     K_SAMU_BWD_SCAN,
     K_CLEAR,
+    K_GATE_PROJ_ADJ,
     K_NUM_KERNELS
 };
 

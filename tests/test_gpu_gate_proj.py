@@ -199,3 +199,38 @@ def test_projection_odd_tiles_and_modes(D, mode):
     say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
     for k, v in errs.items():
         assert v <= TOL_OUT, (k, v)
+
+
+@pytest.mark.parametrize("D", [256, 512, 2048, 2560])
+def test_projection_adjoint_bf16_ranges(D):
+    """BF16 cotangents over several 2048-token dW ranges with a ragged last
+    range and tile (B=3, L=1500: 4500 tokens), at the block widths the odd
+    widths test leaves out (1, 2, 8 and 10 tiles of 16 channels; up to 8 the
+    adjoint runs as one pass, dx and dW from shared tiles): dx within half a
+    BF16 ulp of the exact sum plus FP32 accumulation slack, dW and db at
+    1e-5 against the FP64 oracle; accumulating in place gives the same bits."""
+    from linear_recurrence_sequence_amd import scan
+    B, L = 3, 1500
+    say(f"[gate proj] adjoint B={B} L={L} D={D} bf16 cotangents, several ranges")
+    x = inputs.rglru_inputs(B, L, D, 910 + D)["x"]
+    prm = inputs.rglru_proj_inputs(D, 911 + D)
+    ct = inputs.proj_cotangents(B, L, D, 912 + D, bf16=True)
+    d = {k: dev_tensor(v) for k, v in {"x": x, **prm, **ct}.items()}
+    p = scan.rglru_gate_proj_bwd(d["x"], d["w_x"], d["w_a"], d["dlx"], d["dla"], d["dx"])
+    dx2 = d["dx"].clone()
+    q = scan.rglru_gate_proj_bwd(d["x"], d["w_x"], d["w_a"], d["dlx"], d["dla"], dx2, dx_out=dx2)
+    torch.cuda.synchronize()
+    for k in p:
+        assert torch.equal(p[k], q[k]), k
+    dx, dw_x, db_x = oracle.rglru_gate_proj_bwd(x, prm["w_x"], ct["dlx"], ct["dx"])
+    dx, dw_a, db_a = oracle.rglru_gate_proj_bwd(x, prm["w_a"], ct["dla"], dx)
+    mx, _, _ = oracle.rglru_gate_proj_bwd(np.abs(oracle.widen(x)), np.abs(oracle.widen(prm["w_x"])),
+                                          np.abs(oracle.widen(ct["dlx"])), np.abs(oracle.widen(ct["dx"])))
+    mag, _, _ = oracle.rglru_gate_proj_bwd(np.abs(oracle.widen(x)), np.abs(oracle.widen(prm["w_a"])),
+                                           np.abs(oracle.widen(ct["dla"])), mx)
+    _check_bf16_output("dx", p["dx"], dx, mag)
+    errs = {"dw_x": rel_l2(to_f64(p["dw_x"]), dw_x), "db_x": rel_l2(to_f64(p["db_x"]), db_x),
+            "dw_a": rel_l2(to_f64(p["dw_a"]), dw_a), "db_a": rel_l2(to_f64(p["db_a"]), db_a)}
+    say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v <= TOL_OUT, (k, v)
