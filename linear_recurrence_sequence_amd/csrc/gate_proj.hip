@@ -759,10 +759,15 @@ __global__ __launch_bounds__(64 * dw_waves<MT>()) void gate_proj_dw_kernel(
 // registers).  The two roles run separate copies of one tile loop, so the W
 // fragments of one and the accumulators of the other never hold registers
 // at the same time; both copies pass the same barriers in the same order.
-// Tiles sit in the dW kernel's LDS layout (row stride an odd multiple of 16
-// elements); rows past the range are zero, which dW needs and dx never
-// stores.  The LDS holds two tiles: tile i + 1 is written while tile i is
-// multiplied, so that write needs no barrier of its own.
+// The x plane keeps the dW kernel's LDS row stride and the cotangent and dx
+// planes the dx kernel's, so each product's reads stay free of bank
+// conflicts.  Rows past the range read as zero (range-checked buffer
+// loads), which dW needs and dx never stores.  The LDS holds two tiles:
+// tile i + 1 is written while tile i is multiplied, so that write needs no
+// barrier of its own.  Measured at B=1, L=32768, D=2048: 145 us against
+// 101 + 93 us for the dx and dW kernels.  Two tiles in flight (the dx waves
+// requesting every tile), the separate row strides and 1024- or 4096-token
+// ranges each left it within a microsecond or made it slower.
 template <int MT>
 constexpr int adj_waves() {
     return dx_waves<MT>() + dw_waves<MT>();
@@ -783,7 +788,7 @@ constexpr bool adj_fused() {
 template <int MT>
 constexpr size_t adj_lds_bytes() {
     constexpr int Db = 16 * MT;
-    constexpr size_t tiles = (size_t)(LRS_GP_ADJ_DBUF ? 2 : 1) * 4 * TT * dw_row<MT>() * 2;  // x, dl^x, dl^a, dx
+    constexpr size_t tiles = (size_t)(LRS_GP_ADJ_DBUF ? 2 : 1) * TT * (dw_row<MT>() + 3 * (Db + XPAD)) * 2;
     constexpr size_t wts = (size_t)2 * Db * (Db + XPAD) * 2;                                 // W_x^T, W_a^T
     return tiles > wts ? tiles : wts;
 }
@@ -795,49 +800,55 @@ __global__ __launch_bounds__(64 * adj_waves<MT>()) void gate_proj_adj_kernel(
     const uint16_t* dx_in, uint16_t* dx_out, float* __restrict__ dw_part, float* __restrict__ db_part) {
     using G = Geo<MT>;
     constexpr int Db = G::Db, NWX = dx_waves<MT>(), NWW = dw_waves<MT>(), NT = 64 * (NWX + NWW);
-    constexpr int T = TT, RS = dw_row<MT>(), RW = Db + XPAD, R = dw_rows<MT>();
+    // row strides: x as in the dW kernel (rows on disjoint banks for the
+    // transposing reads), the cotangent and dx planes as in the dx kernel
+    // (sixteen consecutive rows on disjoint banks for the 16-byte row reads)
+    constexpr int T = TT, RX = dw_row<MT>(), RL = Db + XPAD, RW = Db + XPAD, R = dw_rows<MT>();
     constexpr int WPP = NWX / G::P, TGW = (T / 16) / WPP;  // dx: waves per pair, token groups per wave
     constexpr int CPR = Db / 8, NCH = T * CPR, S = (NCH + NT - 1) / NT;  // 16-byte chunks per plane
     constexpr bool DBUF = LRS_GP_ADJ_DBUF != 0, DIRECT = LRS_GP_ADJ_DIRECT != 0;
-    constexpr int TILE = 4 * T * RS;  // elements of one tile's four planes
+    constexpr int TILE = T * (RX + 3 * RL);  // elements of one tile's four planes
+    constexpr int PL1 = T * RX, PL3 = T * (RX + 2 * RL);  // plane offsets: dl^x (dl^a follows), dx rows
     static_assert(TGW >= 1 && 64 * (NWX + NWW) <= 1024, "adjoint workgroup shape");
-    extern __shared__ uint16_t gp_lds[];  // per tile: x [T][RS], dl^x, dl^a [2][T][RS], dx rows [T][RS]
+    extern __shared__ uint16_t gp_lds[];  // per tile: x [T][RX], dl^x, dl^a [2][T][RL], dx rows [T][RL]
     const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int blk = blockIdx.x, r = blockIdx.y;
     const size_t tr0 = (size_t)r * range, tr1 = min((size_t)BL, tr0 + range);
     const int ntile = (int)((tr1 - tr0 + T - 1) / T);
 
+    // Tile loads, shared by both roles, through one buffer descriptor per
+    // plane whose range is the workgroup's token rows: a row past the range
+    // (a ragged last tile, the tiles the pipeline requests past the end)
+    // reads as zero and costs no memory access -- the zero rows dW needs and
+    // dx never stores.  The offset of a 16-byte chunk is a 32-bit lane value.
+    struct Regs {
+        v4u v[4][S];  // x, dl^x, dl^a, dx_in
+    };
+    const int rbytes = (int)((tr1 - tr0) * D * 2);  // at most range * 2560 * 2 bytes
+    const char* const src[4] = {reinterpret_cast<const char*>(x), reinterpret_cast<const char*>(dlx),
+                                reinterpret_cast<const char*>(dla), reinterpret_cast<const char*>(dx_in)};
+    __amdgpu_buffer_rsrc_t rsrc[4];
+#pragma unroll
+    for (int pl = 0; pl < 4; ++pl)
+        rsrc[pl] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src[pl] + tr0 * D * 2), (short)0, rbytes,
+                                                     0x00020000);
+    auto load = [&](Regs& b, int i) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int c = NCH % NT == 0 ? threadIdx.x + s * NT : min((int)threadIdx.x + s * NT, NCH - 1);
+            const int row = c / CPR, ch = c - row * CPR;
+            const uint32_t off = (uint32_t)(((i * T + row) * D + blk * Db + 8 * ch) * 2);
+#pragma unroll
+            for (int pl = 0; pl < 4; ++pl) b.v[pl][s] = __builtin_amdgcn_raw_buffer_load_b128(rsrc[pl], off, 0, 0);
+        }
+    };
     // W_x^T and W_a^T of the block, for the dx waves' fragments
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg)
         stage_transposed_bf16(gp_lds + gg * Db * RW, RW, (gg ? w_a : w_x) + (size_t)blk * Db * Db, Db, Db, Db, NT);
     __syncthreads();
 
-    // Tile loads, shared by both roles: unconditional (rows past the range
-    // re-read its last row, tiles past it its last tile); a row mask zeroes
-    // those rows when the tile is written to LDS.  Addresses are a uniform
-    // tile base plus a 32-bit lane offset in bytes.
-    struct Regs {
-        v4u v[4][S];  // x, dl^x, dl^a, dx_in
-        uint32_t ok;  // bit s: the token row of chunk s is in the range
-    };
-    const char* const src[4] = {reinterpret_cast<const char*>(x), reinterpret_cast<const char*>(dlx),
-                                reinterpret_cast<const char*>(dla), reinterpret_cast<const char*>(dx_in)};
-    auto load = [&](Regs& b, int i) {
-        const size_t t0 = tr0 + (size_t)min(i, ntile - 1) * T;
-        const int last = (int)(tr1 - 1 - t0);  // the range's last row, counted from t0
-        b.ok = 0;
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const int c = NCH % NT == 0 ? threadIdx.x + s * NT : min((int)threadIdx.x + s * NT, NCH - 1);
-            const int row = c / CPR, ch = c - row * CPR;
-            b.ok |= (i < ntile && row <= last) ? 1u << s : 0u;
-            const uint32_t off = (uint32_t)((min(row, last) * D + blk * Db + 8 * ch) * 2);
-#pragma unroll
-            for (int pl = 0; pl < 4; ++pl) b.v[pl][s] = ld16(src[pl] + t0 * D * 2 + off);
-        }
-    };
     auto tile_of = [&](int i) { return gp_lds + (DBUF ? (i & 1) * TILE : 0); };
     auto store = [&](const Regs& b, uint16_t* tl) {
 #pragma unroll
@@ -845,9 +856,8 @@ __global__ __launch_bounds__(64 * adj_waves<MT>()) void gate_proj_adj_kernel(
             const int c = threadIdx.x + s * NT;
             if (NCH % NT != 0 && c >= NCH) continue;
             const int row = c / CPR, ch = c - row * CPR;
-            const bool ok = (b.ok >> s) & 1u;
 #pragma unroll
-            for (int pl = 0; pl < 4; ++pl) st16(tl + (pl * T + row) * RS + 8 * ch, ok ? b.v[pl][s] : zero4());
+            for (int pl = 0; pl < 4; ++pl) st16(tl + (pl ? PL1 + ((pl - 1) * T + row) * RL : row * RX) + 8 * ch, b.v[pl][s]);
         }
     };
     // the staged dx rows of tile i, written out whole (when not DIRECT)
@@ -861,7 +871,7 @@ __global__ __launch_bounds__(64 * adj_waves<MT>()) void gate_proj_adj_kernel(
             if (t0 + row < tr1)
                 out_store<u32x4_t>(reinterpret_cast<char*>(dx_out) + t0 * D * 2 +
                                        (uint32_t)((row * D + blk * Db + 8 * ch) * 2),
-                                   __builtin_bit_cast(u32x4_t, ld16(tl + (3 * T + row) * RS + 8 * ch)));
+                                   __builtin_bit_cast(u32x4_t, ld16(tl + PL3 + row * RL + 8 * ch)));
         }
     };
     // The tile loop of both roles.  With DBUF, tile i + 1 goes to the other
@@ -917,13 +927,13 @@ __global__ __launch_bounds__(64 * adj_waves<MT>()) void gate_proj_adj_kernel(
                 }
             }
         run([&](int i, uint16_t* tl) {
-            const uint16_t* const sl = tl + T * RS;
-            uint16_t* const sio = tl + 3 * T * RS;
+            const uint16_t* const sl = tl + PL1;
+            uint16_t* const sio = tl + PL3;
             const size_t t0 = tr0 + (size_t)i * T;
 #pragma unroll
             for (int q = 0; q < TGW; ++q) {
                 const int tok = (tgb + q) * 16 + col;
-                uint16_t* const sdx = sio + tok * RS + min(c0, Db - 8);
+                uint16_t* const sdx = sio + tok * RL + min(c0, Db - 8);
                 const v4u in0 = ld16(sdx);
                 v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
@@ -932,7 +942,7 @@ __global__ __launch_bounds__(64 * adj_waves<MT>()) void gate_proj_adj_kernel(
                     for (int ks = 0; ks < G::KS; ++ks) {
                         const bool half = G::ODD && ks == G::KS - 1;
                         const int o0 = 32 * ks + 8 * grp - ((half && grp >= 2) ? 16 : 0);
-                        v4u bf = ld16(sl + (gg * T + tok) * RS + o0);
+                        v4u bf = ld16(sl + (gg * T + tok) * RL + o0);
                         if (half && grp >= 2) bf = zero4();
                         a0 = mfma(wf[gg][0][ks], bf, a0);
                         a1 = mfma(wf[gg][1][ks], bf, a1);
@@ -961,24 +971,25 @@ __global__ __launch_bounds__(64 * adj_waves<MT>()) void gate_proj_adj_kernel(
             for (int n = 0; n <= MT; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
         run([&](int, uint16_t* tl) {
             const uint16_t* const sx = tl;
-            const uint16_t* const sl = tl + T * RS;
+            const uint16_t* const sl = tl + PL1;
 #pragma unroll
             for (int kt = 0; kt < T; kt += 32) {
-                const int toff = (kt + 8 * grp + (col >> 2)) * RS + 4 * (col & 3);  // this lane's read address
+                const int trow = kt + 8 * grp + (col >> 2);  // this lane's read addresses
+                const int tx = trow * RX + 4 * (col & 3), tlo = trow * RL + 4 * (col & 3);
                 v4u af[R];
 #pragma unroll
                 for (int j = 0; j < R; ++j) {
                     const int row = dv * R + j;  // gate row / MT, tile row % MT
                     const int rc = row < 2 * MT ? row : 0;
                     const int gg = rc / MT, mo = rc - gg * MT;
-                    af[j] = tr_frag(sl + gg * T * RS + toff + mo * 16, RS);
+                    af[j] = tr_frag(sl + gg * T * RL + tlo + mo * 16, RL);
                 }
                 // one B fragment at a time (the accumulators leave no room
                 // to request them all at once)
 #pragma unroll
                 for (int n = 0; n <= MT; ++n) {
                     const uint32_t one = col == 0 ? 0x3f803f80u : 0u;  // the bias tile's column (1, 0, ..., 0)
-                    const v4u bf = n < MT ? tr_frag(sx + toff + n * 16, RS) : v4u{one, one, one, one};
+                    const v4u bf = n < MT ? tr_frag(sx + tx + n * 16, RX) : v4u{one, one, one, one};
 #pragma unroll
                     for (int j = 0; j < R; ++j) {
                         if (2 * MT % NWW != 0 && dv * R + j >= 2 * MT) continue;
