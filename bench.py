@@ -54,14 +54,15 @@ def log(*a):
 
 
 def effective_groups(L, K, G, min_group=8, samu=None):
-    """Chunks per group the library uses for G (0 = its choice: SAMU groups
-    of 8 chunks, one workgroup each; RG-LRU serial up to 128 chunks, else
-    about 128 groups of >= min_group chunks)."""
+    """Chunks per group the library uses for G (0 = its choice: groups of 8
+    chunks, one workgroup each, for SAMU and for RG-LRU at K=16; RG-LRU at
+    K=32 serial up to 128 chunks, else about 128 groups of >= min_group
+    chunks)."""
     C = -(-L // K)
     if samu is None:
         samu = min_group == 8
     if G == 0:
-        if samu:
+        if samu or K == 16:
             G = 8
         else:
             G = C if C <= 128 else max(min_group, -(-C // 128))
@@ -168,7 +169,7 @@ def samu_kernel_bytes(B, L, D, K, G, unfused=False):
     return tab
 
 
-def rglru_kernel_bytes(B, L, D, K, G, resets):
+def rglru_kernel_bytes(B, L, D, K, G, resets, unfused=False):
     """(method, design) bytes per launch of each RG-LRU kernel (the real
     scan keeps full FP32 (A, B) summaries, so both agree but for the
     per-token reset flags)."""
@@ -186,7 +187,37 @@ def rglru_kernel_bytes(B, L, D, K, G, resets):
         "prefix_group_scan": 8 * B * NG * D + 4 * B * D + 4 * B * NG * D,
         "prefix_chunk_entries": 4 * B * NG * D + 8 * BCD + 4 * BCD,
     }
-    return {k: (v, v) for k, v in tab.items()}
+    tab = {k: (v, v) for k, v in tab.items()}
+    G_ = effective_groups(L, K, G, 16)
+    if K == 16 and G_ <= 16 and not unfused:
+        # the single-pass path: x, l^x, l^a (and dy) read once per direction;
+        # the design adds the hand-off (16 B per (group, channel) published,
+        # about (G - 1) / 2 maps and one state read per group) and writes one
+        # alpha row per group
+        NGD = B * NG * D
+        handoff = 16 * NGD + (8 * (G_ - 1) + 8) * NGD
+        for k in ("rglru_chunk_summary", "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay",
+                  "prefix_group_compose", "prefix_group_scan", "prefix_chunk_entries"):
+            tab.pop(k, None)
+        fwd = 6 * BLD + 4 * D + rs + 2 * BLD + 4 * BCD + 4 * B * D
+        bwd = 8 * BLD + 4 * D + rs + 4 * BCD + 6 * BLD + 4 * B * D
+        tab.update({
+            "rglru_forward_scan": (fwd, fwd + handoff),
+            "rglru_backward_scan": (bwd + 4 * BCD, bwd + 4 * NGD + handoff),
+            "rglru_alpha": (4 * BCD + 4 * D, 4 * NGD + 4 * D),
+            "clear": (0, 16 * NGD),
+        })
+    return tab
+
+
+def rglru_fused_step_bytes(B, L, D, K, G, resets):
+    """The bytes of the method's separate steps (summary, prefix, replay)
+    each RG-LRU single-pass kernel does the work of."""
+    full = rglru_kernel_bytes(B, L, D, K, G, resets, unfused=True)
+    return {"rglru_forward_scan": full["rglru_chunk_summary"][0] + full["prefix_group_scan"][0]
+            + full["rglru_replay"][0],
+            "rglru_backward_scan": full["rglru_reverse_summary"][0] + full["prefix_group_scan"][0]
+            + full["rglru_bwd_replay"][0]}
 
 
 def sources_digest(paths):
@@ -489,7 +520,7 @@ def kernel_rates(prof, steps, table, fused=None):
 # kernels that stream the [B, L, D] tensors
 STREAM_KERNELS = ("samu_controller", "samu_chunk_summary", "samu_replay", "samu_forward_scan", "samu_reverse_summary",
                   "samu_bwd_replay", "samu_backward_scan", "samu_controller_bwd", "rglru_chunk_summary", "rglru_replay",
-                  "rglru_reverse_summary", "rglru_bwd_replay")
+                  "rglru_reverse_summary", "rglru_bwd_replay", "rglru_forward_scan", "rglru_backward_scan")
 
 
 def run_case(timer, kind, step, B, L, D, K, G, steps, warmup, resets=False, repeats=3):
@@ -506,7 +537,8 @@ def run_case(timer, kind, step, B, L, D, K, G, steps, warmup, resets=False, repe
     _, prof = timer(step, steps, 1, True)
     floor = (FLOOR_SAMU if kind == "samu" else FLOOR_RGLRU) * B * L * D
     table = samu_kernel_bytes(B, L, D, K, G) if kind == "samu" else rglru_kernel_bytes(B, L, D, K, G, resets)
-    ks = kernel_rates(prof, steps, table, fused_step_bytes(B, L, D, K, G) if kind == "samu" else None)
+    ks = kernel_rates(prof, steps, table, fused_step_bytes(B, L, D, K, G) if kind == "samu"
+                      else rglru_fused_step_bytes(B, L, D, K, G, resets))
     row = {"B": B, "L": L, "D": D, "K": K,
            "G": effective_groups(L, K, G, 8 if kind == "samu" else 16),
            "ms_per_step": round(ms, 4), "ms_runs": [round(t, 4) for t in gruns],
@@ -686,7 +718,7 @@ def main():
         best = None
         rd = None
         for RK in (16, 32):
-            for RG in (0, 8, 16, 32, 64):
+            for RG in (0, 4, 8, 16, 32, 64):
                 step, rb = rglru_case(torch, scan, inputs, B, L, D, RK, RG, 3003, 0.1, d=rd)
                 rd = rb["d"]
                 t = timed.graph(step, args.steps, args.warmup)[0]

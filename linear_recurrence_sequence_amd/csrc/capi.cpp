@@ -55,7 +55,7 @@ static const char* const kKernelNames[K_NUM_KERNELS] = {
     "rglru_reverse_summary", "rglru_bwd_replay", "rglru_alpha", "samu_decode",
     "baseline_sequential", "baseline_associative", "gate_projection", "gate_projection_dx",
     "gate_projection_dw", "gate_projection_reduce", "samu_forward_scan", "samu_backward_scan", "clear",
-    "gate_projection_adjoint"};
+    "gate_projection_adjoint", "rglru_forward_scan", "rglru_backward_scan"};
 
 const char* kernel_name(int id) { return (id >= 0 && id < K_NUM_KERNELS) ? kKernelNames[id] : "?"; }
 
@@ -122,6 +122,10 @@ static bool chunking(int B, int L, int K, int G, int min_group, Chunking* ch, in
 
 static constexpr int kSamuMinGroup = 8;      // see chunking()
 static constexpr int kRglruMinGroup = 16;
+// RG-LRU with K = 16 and G == 0: groups of kRglruGroup chunks on the
+// single-pass path (rglru_fused); K = 32 and longer groups take the
+// three-kernel prefix.
+static constexpr int kRglruGroup = 8;
 // SAMU with G == 0: groups of kSamuGroup chunks on the grouped path (one
 // workgroup per group; see launch_samu_gscan), which any G up to
 // SAMU_GROUP_MAX takes; longer groups take the three-kernel prefix.
@@ -214,19 +218,30 @@ static RgSaved rg_saved_layout(void* base, const Chunking& ch, int D, size_t* by
     return s;
 }
 
+// The single-pass path (rglru_fused) needs only its hand-off words and, in
+// the backward, one alpha row per group; the three-kernel prefix keeps chunk
+// summaries, group summaries, carries and one alpha row per chunk.
 struct RgWs {
     float *summ, *gsum, *carry, *alpha_part;
+    void* pub;
+    size_t pub_bytes;
+    int alpha_rows;
 };
 static RgWs rg_ws_layout(void* base, const Chunking& ch, int D, bool backward, size_t* bytes) {
     Carver cv(base);
     RgWs w{};
     const size_t BCD = (size_t)ch.B * ch.C * D;
-    w.summ = cv.take<float>(BCD * 2);
-    w.gsum = cv.take<float>((size_t)ch.B * ch.NG * D * 3);
-    if (backward) {
-        w.carry = cv.take<float>(BCD);
-        w.alpha_part = cv.take<float>(BCD);
+    if (rglru_fused(ch)) {
+        w.pub_bytes = rglru_pub_bytes(ch, D);
+        w.pub = cv.take<uint64_t>(w.pub_bytes / sizeof(uint64_t));
+        w.alpha_rows = ch.B * ch.NG;
+    } else {
+        w.summ = cv.take<float>(BCD * 2);
+        w.gsum = cv.take<float>((size_t)ch.B * ch.NG * D * 3);
+        if (backward) w.carry = cv.take<float>(BCD);
+        w.alpha_rows = ch.B * ch.C;
     }
+    if (backward) w.alpha_part = cv.take<float>((size_t)w.alpha_rows * D);
     if (bytes) *bytes = cv.off;
     return w;
 }
@@ -287,7 +302,7 @@ static bool samu_shape(int B, int L, int D, int K, int G, Chunking* ch) {
 
 static bool rglru_shape(int B, int L, int D, int K, int G, Chunking* ch) {
     if (D < 2 || D % 2 != 0) return false;
-    return chunking(B, L, K, G, kRglruMinGroup, ch);
+    return chunking(B, L, K, G, kRglruMinGroup, ch, K == 16 ? kRglruGroup : 0);
 }
 
 static std::string shape_text(int B, int L, int D, int K, int G) {
@@ -747,6 +762,11 @@ scan_status rglru_scan_fwd(int B, int L, int D, int K, int G, const void* x, con
     RglruParams p{B, L, D, x, lx, la, alpha, reset, h0};
     RgSaved sv = rg_saved_layout(saved, ch, D, nullptr);
     RgWs ws = rg_ws_layout(workspace, ch, D, false, nullptr);
+    if (rglru_fused(ch)) {
+        LRS_TRY(launch_rglru_gscan(p, ch, ws.pub, ws.pub_bytes, sv.entries, y, y_dtype == SCAN_F32, h_final, s),
+                "rglru forward scan");
+        return SCAN_OK;
+    }
     LRS_TRY(launch_rglru_summary(p, ch, ws.summ, s), "rglru chunk summary");
     LRS_TRY(launch_prefix(1, false, ch, D, PrefixSummaries{ws.summ, nullptr, nullptr, nullptr}, ws.gsum, h0,
                           sv.entries, s),
@@ -790,13 +810,20 @@ scan_status rglru_scan_bwd(int B, int L, int D, int K, int G, const void* x, con
     RgSaved sv = rg_saved_layout(const_cast<void*>(saved), ch, D, nullptr);
     RgWs ws = rg_ws_layout(workspace, ch, D, true, nullptr);
     const int f32 = grad_dtype == SCAN_F32;
+    if (rglru_fused(ch)) {
+        LRS_TRY(launch_rglru_gbscan(p, ch, sv.entries, dh_final, ws.pub, ws.pub_bytes, dy, dx, dlx, dla, f32, dh0,
+                                    ws.alpha_part, s),
+                "rglru backward scan");
+        LRS_TRY(launch_rglru_alpha_reduce(p, ws.alpha_rows, ws.alpha_part, dalpha, s), "rglru alpha reduction");
+        return SCAN_OK;
+    }
     LRS_TRY(launch_rglru_rev_summary(p, ch, dy, ws.summ, s), "rglru reverse summary");
     LRS_TRY(launch_prefix(1, true, ch, D, PrefixSummaries{ws.summ, nullptr, nullptr, nullptr}, ws.gsum,
                           dh_final, ws.carry, s),
             "rglru reverse prefix");
     LRS_TRY(launch_rglru_bwd_replay(p, ch, sv.entries, ws.carry, dy, dx, dlx, dla, f32, dh0, ws.alpha_part, s),
             "rglru backward replay");
-    LRS_TRY(launch_rglru_alpha_reduce(p, ch, ws.alpha_part, dalpha, s), "rglru alpha reduction");
+    LRS_TRY(launch_rglru_alpha_reduce(p, ws.alpha_rows, ws.alpha_part, dalpha, s), "rglru alpha reduction");
     return SCAN_OK;
 }
 

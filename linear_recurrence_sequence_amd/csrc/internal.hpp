@@ -41,6 +41,8 @@ enum KernelId {
     K_SAMU_BWD_SCAN,
     K_CLEAR,
     K_GATE_PROJ_ADJ,
+    K_RGLRU_FWD_SCAN,
+    K_RGLRU_BWD_SCAN,
     K_NUM_KERNELS
 };
 
@@ -203,9 +205,28 @@ hipError_t launch_rglru_bwd_replay(const RglruParams& p, const Chunking& ch,
                                    const float* entries, const float* carry_in, const void* dy,
                                    void* dx, void* dlx, void* dla, int g_f32, float* dh0,
                                    float* alpha_part, hipStream_t s);
-// alpha_part: [B*C, D] per-chunk partials
-hipError_t launch_rglru_alpha_reduce(const RglruParams& p, const Chunking& ch, const float* alpha_part,
-                                     float* dalpha, hipStream_t s);
+// alpha_part: [rows, D] partials (B*C per-chunk rows, or B*NG per-group rows
+// on the single-pass path)
+hipError_t launch_rglru_alpha_reduce(const RglruParams& p, int rows, const float* alpha_part, float* dalpha,
+                                     hipStream_t s);
+// Single-pass grouped scans (K = 16, ch.G <= RG_GROUP_MAX): one workgroup per
+// group of consecutive chunks and 64 channel pairs, one wave per chunk; the
+// groups hand states to each other through rglru_pub_bytes() of tagged
+// words, cleared by the launcher first.
+//   gscan:  the whole forward (summaries, hand-off, replay; writes the entry
+//           states [B, C, D] the backward reads);
+//   gbscan: the whole adjoint scan (reverse summaries, hand-off, backward
+//           replay); alpha_part: [B, NG, D] per-group partial sums.
+constexpr int RG_GROUP_MAX = 16;
+bool rglru_fused(const Chunking& ch);
+size_t rglru_pub_bytes(const Chunking& ch, int D);
+hipError_t launch_rglru_gscan(const RglruParams& p, const Chunking& ch, void* pub, size_t pub_bytes,
+                              float* entries, void* y, int y_f32, float* h_final, hipStream_t s);
+hipError_t launch_rglru_gbscan(const RglruParams& p, const Chunking& ch, const float* entries,
+                               const float* dh_final, void* pub, size_t pub_bytes, const void* dy, void* dx,
+                               void* dlx, void* dla, int g_f32, float* dh0, float* alpha_part, hipStream_t s);
+// zeroes `bytes` (a multiple of 16) at p: hand-off words before a single-pass scan
+hipError_t launch_clear_words(void* p, size_t bytes, hipStream_t s);
 
 // ------------------------------------------------------ comparison scans ---
 // variant 0: per-channel sequential scan; 1: associative (recursive pairwise)

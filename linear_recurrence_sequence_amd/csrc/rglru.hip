@@ -224,6 +224,201 @@ __global__ __launch_bounds__(RG_THREADS) void rglru_replay_kernel(RgIn in, int C
         reinterpret_cast<float2*>(h_final)[(size_t)b * in.W + lw] = make_float2(h[0], h[1]);
 }
 
+// ------------------------------------------------- single-pass grouped scans
+// One launch per direction on the grouped path (G <= RG_GROUP_MAX): a
+// workgroup owns one group of G consecutive chunks (processing order) and 64
+// lanes of channel pairs; wave w handles chunk w of the group.  Each wave
+// reads its chunk's words once, forms the chunk's map (A, B) per channel
+// for the group's LDS table, takes the state entering the group from the
+// groups before it (rg_group_handoff) and runs the chunk from the state
+// entering it.
+constexpr int RG_GL = 64;  // lanes (channel pairs) per workgroup
+
+// Hand-off words, per (group, lane): the group's map (A0, B0, A1, B1) for a
+// group inside a segment, or the state (h0, h1) leaving a segment's last
+// group; each value is its own tagged 64-bit word (pub_store / pub_load of
+// common.hpp).  Unlike the complex scan, the transition part of a group's
+// map depends on every token's gate, so it travels with the affine part.
+constexpr int RG_PUB_WORDS = 4;
+
+// The first N words of an earlier group for this lane, once all are
+// published (bounded wait, as wait_pair).
+template <int N>
+__device__ __forceinline__ void wait_words(const uint64_t* grp, uint32_t Wb, uint32_t off, float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = 0.f;
+    bool ok = false;
+    for (int it = 0; it < SCAN_SPIN_MAX; ++it) {
+        if (!ok) {
+            const uint32_t o = opaque_v(off);
+            uint64_t wd[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) wd[i] = pub_load(grp, i, Wb, o);
+            bool all = true;
+#pragma unroll
+            for (int i = 0; i < N; ++i) all = all && pub_ok(wd[i]);
+            if (all) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) v[i] = pub_val(wd[i]);
+                ok = true;
+            }
+        }
+        if (__all(ok)) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// The state entering group q (processing order) for this lane's two
+// channels; the fixed-order segment chain of group_handoff (common.hpp)
+// with real maps h -> A h + B per channel.  comp [G][64]: (A0, B0, A1, B1) of
+// each of the group's chunks in processing order; look [G][64]: scratch;
+// seed: the row's state before the first group (float2 per lane, NULL = 0);
+// pub: the row's [NG][RG_PUB_WORDS][W] words; lw: the lane's word (clamped
+// into the row, so that a lane past the row reads a published word).
+__device__ __forceinline__ float2 rg_group_handoff(const float4* comp, float4* look, int G, int w, int lane, int q,
+                                                   int NG, int W, int lw, bool active, const float2* seed,
+                                                   uint64_t* pub) {
+    const uint32_t Wb = (uint32_t)W * 8u, off = (uint32_t)lw * 8u;
+    uint64_t* mine = pub + (size_t)q * RG_PUB_WORDS * W;  // wave-uniform
+    const int nprev = q % G;
+    const bool seg_last = nprev == G - 1 || q == NG - 1;
+    if (w == 0 && active && q + 1 < NG && !seg_last) {
+        // U_q = S_{G-1} o ... o S_0, composed in chunk order, published at once
+        float a0 = 1.f, b0 = 0.f, a1 = 1.f, b1 = 0.f;
+        for (int j = 0; j < G; ++j) {
+            const float4 f = comp[j * RG_GL + lane];
+            b0 = fmaf(f.x, b0, f.y);
+            a0 *= f.x;
+            b1 = fmaf(f.z, b1, f.w);
+            a1 *= f.z;
+        }
+        pub_store(mine, 0, Wb, off, a0);
+        pub_store(mine, 1, Wb, off, b0);
+        pub_store(mine, 2, Wb, off, a1);
+        pub_store(mine, 3, Wb, off, b1);
+    }
+    if (w < nprev) {
+        float v[4];
+        wait_words<4>(pub + (size_t)(q - 1 - w) * RG_PUB_WORDS * W, Wb, off, v);
+        look[w * RG_GL + lane] = make_float4(v[0], v[1], v[2], v[3]);
+    } else if (w == nprev) {
+        float2 hs = make_float2(0.f, 0.f);
+        if (q - nprev > 0) {
+            float v[2];
+            wait_words<2>(pub + (size_t)(q - nprev - 1) * RG_PUB_WORDS * W, Wb, off, v);
+            hs = make_float2(v[0], v[1]);
+        } else if (seed) {
+            hs = seed[lw];
+        }
+        look[w * RG_GL + lane] = make_float4(hs.x, hs.y, 0.f, 0.f);
+    }
+    __syncthreads();
+    if (w == 0) {
+        const float4 hs = look[nprev * RG_GL + lane];
+        float h0 = hs.x, h1 = hs.y;
+        for (int v = nprev - 1; v >= 0; --v) {  // oldest first
+            const float4 f = look[v * RG_GL + lane];
+            h0 = fmaf(f.x, h0, f.y);
+            h1 = fmaf(f.z, h1, f.w);
+        }
+        if (active && q + 1 < NG && seg_last) {
+            float o0 = h0, o1 = h1;
+            for (int j = 0; j < G; ++j) {
+                const float4 f = comp[j * RG_GL + lane];
+                o0 = fmaf(f.x, o0, f.y);
+                o1 = fmaf(f.z, o1, f.w);
+            }
+            pub_store(mine, 0, Wb, off, o0);
+            pub_store(mine, 1, Wb, off, o1);
+        }
+        look[lane] = make_float4(h0, h1, 0.f, 0.f);
+    }
+    __syncthreads();
+    const float4 r = look[lane];
+    return make_float2(r.x, r.y);
+}
+
+// Forward: every gate of the chunk is formed once; the chunk's retention
+// and drive per token (a_t, x_t g^x_t m_t) stay in registers from the
+// summary to the replay.
+template <int K, bool F32>
+__global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gscan_kernel(
+    int L, int W, int C, int G, const uint32_t* __restrict__ x, const uint32_t* __restrict__ lx,
+    const uint32_t* __restrict__ la, const unsigned char* __restrict__ reset, const float* __restrict__ alpha,
+    const float2* __restrict__ h0, uint64_t* __restrict__ pub, float2* __restrict__ entries, void* __restrict__ y,
+    float2* __restrict__ h_final) {
+    extern __shared__ float4 rg_lds[];  // comp [G][64], look [G][64]
+    float4* const comp = rg_lds;
+    float4* const look = rg_lds + G * RG_GL;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = blockIdx.y, b = blockIdx.z, NG = gridDim.y;
+    const int c = q * G + w;
+    const bool valid = c < C;  // wave-uniform
+    const int lw0 = blockIdx.x * RG_GL + lane;
+    const bool active = lw0 < W;
+    const int lw = active ? lw0 : W - 1;
+    const size_t tok0 = (size_t)b * L + (size_t)min(c, C - 1) * K;
+    const int kc = valid ? min(K, L - c * K) : 0;
+    const uint32_t rm = reset_mask<K>(reset, tok0, kc);
+    const ChanConst k[2] = {chan_const(alpha[2 * lw]), chan_const(alpha[2 * lw + 1])};
+    // the chunk's words (rows past its end read as 0 and are never used)
+    uint32_t xs[K], lxs[K], las[K];
+    {
+        const ChunkRows rx(x + tok0 * W, kc, W), rl(lx + tok0 * W, kc, W), ra(la + tok0 * W, kc, W);
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            xs[i] = rx.load(i, lw);
+            lxs[i] = rl.load(i, lw);
+            las[i] = ra.load(i, lw);
+        }
+    }
+    float av[K][2], bv[K][2];
+    float A[2] = {1.f, 1.f}, Bs[2] = {0.f, 0.f};
+    const int kq = opaque(kc);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        if (i < kq) {
+            const bool rs = bit(rm, i);
+            const float xv[2] = {bf16_lo(xs[i]), bf16_hi(xs[i])};
+            const float lxv[2] = {bf16_lo(lxs[i]), bf16_hi(lxs[i])};
+            const float lav[2] = {bf16_lo(las[i]), bf16_hi(las[i])};
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const Gate g = gates(k[v], lxv[v], lav[v], rs);
+                av[i][v] = g.a;
+                bv[i][v] = xv[v] * g.gx * g.m;
+                A[v] *= g.a;
+                Bs[v] = fmaf(g.a, Bs[v], bv[i][v]);
+            }
+        }
+    }
+    comp[w * RG_GL + lane] = make_float4(A[0], Bs[0], A[1], Bs[1]);
+    __syncthreads();
+    const float2 hin = rg_group_handoff(comp, look, G, w, lane, q, NG, W, lw, active,
+                                        h0 ? h0 + (size_t)b * W : nullptr, pub + (size_t)b * NG * RG_PUB_WORDS * W);
+    if (!valid) return;  // no barrier follows
+    float h[2] = {hin.x, hin.y};
+    for (int j = 0; j < w; ++j) {
+        const float4 f = comp[j * RG_GL + lane];
+        h[0] = fmaf(f.x, h[0], f.y);
+        h[1] = fmaf(f.z, h[1], f.w);
+    }
+    if (active) entries[((size_t)b * C + c) * W + lw] = make_float2(h[0], h[1]);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        if (i < kq) {
+            h[0] = fmaf(av[i][0], h[0], bv[i][0]);
+            h[1] = fmaf(av[i][1], h[1], bv[i][1]);
+            if (active) {
+                const size_t row = (tok0 + i) * (size_t)W;  // wave-uniform
+                if (F32) out_f32x2(reinterpret_cast<float2*>(y) + row + lw, h[0], h[1]);
+                else out_u32(reinterpret_cast<uint32_t*>(y) + row + lw, pack_bf16x2(h[0], h[1]));
+            }
+        }
+    }
+    if (h_final && active && c == C - 1) h_final[(size_t)b * W + lw] = make_float2(h[0], h[1]);
+}
+
 // -------------------------------------------------------- reverse summary
 // carry -> a_t (dy_t + carry), composed from the last token of the chunk to
 // the first: (A, B) with carry_before = A carry_after + B.
@@ -285,22 +480,16 @@ struct RgBwdOut {
     void* dla;
 };
 
+// The adjoint over H tokens whose words are held in registers, from the
+// state h_in entering them; `active` = the lane's outputs are stored.
 template <int H, bool F32, bool FULL>
-__device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
-                                           size_t tok0, int lw, int kq, uint32_t rm,
-                                           const float (&h_in)[2], float (&carry)[2], float (&acc)[2],
-                                           float2* hist) {
-    uint32_t xs[H], lxs[H], las[H], gws[H];
+__device__ __forceinline__ void rg_bwd_words(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
+                                             size_t tok0, int lw, int kq, uint32_t rm, bool active,
+                                             const uint32_t (&xs)[H], const uint32_t (&lxs)[H],
+                                             const uint32_t (&las)[H], const uint32_t (&gws)[H],
+                                             const float (&h_in)[2], float (&carry)[2], float (&acc)[2],
+                                             float2* hist) {
     float h[2] = {h_in[0], h_in[1]};
-#pragma unroll
-    for (int i = 0; i < H; ++i) {
-        if (FULL || i < kq) {
-            xs[i] = word(in.x, tok0, i, in.W, lw);
-            lxs[i] = word(in.lx, tok0, i, in.W, lw);
-            las[i] = word(in.la, tok0, i, in.W, lw);
-            gws[i] = word(o.dy, tok0, i, in.W, lw);
-        }
-    }
 #pragma unroll
     for (int i = 0; i < H; ++i) {
         if (FULL || i < kq) {
@@ -350,17 +539,35 @@ __device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[
                 carry[v] = gt.a * g;
             }
             const size_t row = (tok0 + i) * (size_t)in.W;
-            if (F32) {
+            if (F32 && active) {
                 out_f32x2(reinterpret_cast<float2*>(o.dx) + row + lw, ox[0], ox[1]);
                 out_f32x2(reinterpret_cast<float2*>(o.dlx) + row + lw, olx[0], olx[1]);
                 out_f32x2(reinterpret_cast<float2*>(o.dla) + row + lw, ola[0], ola[1]);
-            } else {
+            } else if (active) {
                 out_u32(reinterpret_cast<uint32_t*>(o.dx) + row + lw, pack_bf16x2(ox[0], ox[1]));
                 out_u32(reinterpret_cast<uint32_t*>(o.dlx) + row + lw, pack_bf16x2(olx[0], olx[1]));
                 out_u32(reinterpret_cast<uint32_t*>(o.dla) + row + lw, pack_bf16x2(ola[0], ola[1]));
             }
         }
     }
+}
+
+template <int H, bool F32, bool FULL>
+__device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
+                                           size_t tok0, int lw, int kq, uint32_t rm,
+                                           const float (&h_in)[2], float (&carry)[2], float (&acc)[2],
+                                           float2* hist) {
+    uint32_t xs[H], lxs[H], las[H], gws[H];
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        if (FULL || i < kq) {
+            xs[i] = word(in.x, tok0, i, in.W, lw);
+            lxs[i] = word(in.lx, tok0, i, in.W, lw);
+            las[i] = word(in.la, tok0, i, in.W, lw);
+            gws[i] = word(o.dy, tok0, i, in.W, lw);
+        }
+    }
+    rg_bwd_words<H, F32, FULL>(in, k, o, tok0, lw, kq, rm, true, xs, lxs, las, gws, h_in, carry, acc, hist);
 }
 
 // state after `n` tokens (n <= H, guarded when not FULL) from h
@@ -434,6 +641,103 @@ __global__ __launch_bounds__(RG_THREADS) __attribute__((amdgpu_waves_per_eu(LRS_
     else rg_bwd_chunk<K, H, F32, false>(in, k, o, tok0, lw, kc, rm, h0, carry, acc, hist);
     reinterpret_cast<float2*>(alpha_part)[cw] = make_float2(acc[0] * k[0].dsp8, acc[1] * k[1].dsp8);
     if (dh0 && c == 0) reinterpret_cast<float2*>(dh0)[(size_t)b * in.W + lw] = make_float2(carry[0], carry[1]);
+}
+
+// Single-pass backward: wave w of group q takes chunk C - 1 - (q G + w)
+// (processing order runs backward in time).  Its words (x, l^x, l^a, dy) are
+// read once: the conjugate-free reverse summary carry -> a_t (dy_t + carry)
+// forms the chunk's map for the group's table, the carry arriving after the
+// chunk comes from the hand-off and the group's later chunks, and the
+// backward replay of rg_bwd_words runs from the saved entry state with the
+// same words.  The lanes' h histories overlay the table once the carries are
+// formed; the alpha partials of the group's chunks are added in processing
+// order into one row per group.
+template <int K, bool F32>
+__global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
+    int L, int W, int C, int G, const uint32_t* __restrict__ x, const uint32_t* __restrict__ lx,
+    const uint32_t* __restrict__ la, const unsigned char* __restrict__ reset, const float* __restrict__ alpha,
+    const float2* __restrict__ entries, const float2* __restrict__ dh_final, uint64_t* __restrict__ pub,
+    const uint32_t* __restrict__ dy, void* __restrict__ dx, void* __restrict__ dlx, void* __restrict__ dla,
+    float2* __restrict__ dh0, float2* __restrict__ alpha_part) {
+    extern __shared__ float4 rg_lds[];  // comp [G][64] and look [G][64], later hist [G][K][64] float2
+    float4* const comp = rg_lds;
+    float4* const look = rg_lds + G * RG_GL;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    float2* const hist = reinterpret_cast<float2*>(rg_lds) + (size_t)w * K * RG_GL + lane;
+    const int q = blockIdx.y, b = blockIdx.z, NG = gridDim.y;
+    const int pc = q * G + w;
+    const bool valid = pc < C;  // wave-uniform
+    const int c = C - 1 - min(pc, C - 1);
+    const int lw0 = blockIdx.x * RG_GL + lane;
+    const bool active = lw0 < W;
+    const int lw = active ? lw0 : W - 1;
+    const size_t tok0 = (size_t)b * L + (size_t)c * K;
+    const int kc = valid ? min(K, L - c * K) : 0;
+    const uint32_t rm = reset_mask<K>(reset, tok0, kc);
+    const ChanConst k[2] = {chan_const(alpha[2 * lw]), chan_const(alpha[2 * lw + 1])};
+    const float2 e = entries[((size_t)b * C + c) * W + lw];
+    uint32_t xs[K], lxs[K], las[K], gws[K];
+    {
+        const ChunkRows rx(x + tok0 * W, kc, W), rl(lx + tok0 * W, kc, W), ra(la + tok0 * W, kc, W),
+            rg(dy + tok0 * W, kc, W);
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            xs[i] = rx.load(i, lw);
+            lxs[i] = rl.load(i, lw);
+            las[i] = ra.load(i, lw);
+            gws[i] = rg.load(i, lw);
+        }
+    }
+    const int kq = opaque(kc);
+    float A[2] = {1.f, 1.f}, Bv[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = K - 1; i >= 0; --i) {
+        if (i < kq) {
+            const bool rs = bit(rm, i);
+            const float lav[2] = {bf16_lo(las[i]), bf16_hi(las[i])};
+            const float gv[2] = {bf16_lo(gws[i]), bf16_hi(gws[i])};
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const float a = retention(k[v], lav[v], rs);
+                A[v] *= a;
+                Bv[v] = a * (Bv[v] + gv[v]);
+            }
+        }
+    }
+    comp[w * RG_GL + lane] = make_float4(A[0], Bv[0], A[1], Bv[1]);
+    __syncthreads();
+    const float2 cin = rg_group_handoff(comp, look, G, w, lane, q, NG, W, lw, active,
+                                        dh_final ? dh_final + (size_t)b * W : nullptr,
+                                        pub + (size_t)b * NG * RG_PUB_WORDS * W);
+    float carry[2] = {cin.x, cin.y};
+    for (int j = 0; j < w; ++j) {
+        const float4 f = comp[j * RG_GL + lane];
+        carry[0] = fmaf(f.x, carry[0], f.y);
+        carry[1] = fmaf(f.z, carry[1], f.w);
+    }
+    __syncthreads();  // the table's LDS becomes the h histories
+    float acc[2] = {0.f, 0.f};
+    if (valid) {
+        const RgIn in{L, W, x, lx, la, reset};
+        const RgBwdOut o{dy, dx, dlx, dla};
+        const float h_in[2] = {e.x, e.y};
+        rg_bwd_words<K, F32, false>(in, k, o, tok0, lw, kq, rm, active, xs, lxs, las, gws, h_in, carry, acc, hist);
+        if (dh0 && active && c == 0) dh0[(size_t)b * W + lw] = make_float2(carry[0], carry[1]);
+    }
+    // the alpha partials of the group's chunks, in processing order, through
+    // each wave's own history slots (free once its replay is done)
+    hist[0] = make_float2(acc[0] * k[0].dsp8, acc[1] * k[1].dsp8);
+    __syncthreads();
+    if (w == 0 && active) {
+        const int n = min(G, C - q * G);
+        float s0 = 0.f, s1 = 0.f;
+        for (int j = 0; j < n; ++j) {
+            const float2 v = reinterpret_cast<const float2*>(rg_lds)[(size_t)j * K * RG_GL + lane];
+            s0 += v.x;
+            s1 += v.y;
+        }
+        alpha_part[((size_t)b * NG + q) * W + lw] = make_float2(s0, s1);
+    }
 }
 
 // ------------------------------------------------------ alpha reduction
@@ -541,10 +845,59 @@ hipError_t launch_rglru_bwd_replay(const RglruParams& p, const Chunking& ch, con
     return hipGetLastError();
 }
 
-hipError_t launch_rglru_alpha_reduce(const RglruParams& p, const Chunking& ch, const float* alpha_part,
-                                     float* dalpha, hipStream_t s) {
+hipError_t launch_rglru_alpha_reduce(const RglruParams& p, int rows, const float* alpha_part, float* dalpha,
+                                     hipStream_t s) {
     LRS_LAUNCH(K_RGLRU_ALPHA, rglru_alpha_kernel, dim3((unsigned)ceil_div(p.D, AR_COLS)), dim3(AR_THREADS), 0, s,
-               ch.B * ch.C, p.D, alpha_part, dalpha);
+               rows, p.D, alpha_part, dalpha);
+    return hipGetLastError();
+}
+
+bool rglru_fused(const Chunking& ch) { return ch.K == 16 && ch.G <= RG_GROUP_MAX; }
+
+size_t rglru_pub_bytes(const Chunking& ch, int D) {
+    return (size_t)ch.B * ch.NG * RG_PUB_WORDS * (size_t)(D / 2) * sizeof(uint64_t);
+}
+
+hipError_t launch_rglru_gscan(const RglruParams& p, const Chunking& ch, void* pub, size_t pub_bytes,
+                              float* entries, void* y, int y_f32, float* h_final, hipStream_t s) {
+    if (ch.NG > 1) {
+        const hipError_t e = launch_clear_words(pub, pub_bytes, s);
+        if (e != hipSuccess) return e;
+    }
+    const int W = p.D / 2;
+    const dim3 grid((unsigned)ceil_div(W, RG_GL), ch.NG, ch.B);
+    const dim3 block(RG_GL * ch.G);
+    const size_t lds = (size_t)2 * ch.G * RG_GL * sizeof(float4);
+#define RG_GSCAN(FF)                                                                                           \
+    LRS_LAUNCH(K_RGLRU_FWD_SCAN, (rglru_gscan_kernel<16, FF>), grid, block, lds, s, p.L, W, ch.C, ch.G,          \
+               (const uint32_t*)p.x, (const uint32_t*)p.lx, (const uint32_t*)p.la, p.reset, p.alpha,            \
+               (const float2*)p.h0, (uint64_t*)pub, (float2*)entries, y, (float2*)h_final)
+    if (y_f32) RG_GSCAN(true);
+    else RG_GSCAN(false);
+#undef RG_GSCAN
+    return hipGetLastError();
+}
+
+hipError_t launch_rglru_gbscan(const RglruParams& p, const Chunking& ch, const float* entries,
+                               const float* dh_final, void* pub, size_t pub_bytes, const void* dy, void* dx,
+                               void* dlx, void* dla, int g_f32, float* dh0, float* alpha_part, hipStream_t s) {
+    if (ch.NG > 1) {
+        const hipError_t e = launch_clear_words(pub, pub_bytes, s);
+        if (e != hipSuccess) return e;
+    }
+    const int W = p.D / 2;
+    const dim3 grid((unsigned)ceil_div(W, RG_GL), ch.NG, ch.B);
+    const dim3 block(RG_GL * ch.G);
+    // the map table and hand-off scratch, overlaid by the h histories
+    const size_t lds = std::max((size_t)2 * ch.G * RG_GL * sizeof(float4), (size_t)ch.G * 16 * RG_GL * sizeof(float2));
+#define RG_GBSCAN(FF)                                                                                          \
+    LRS_LAUNCH(K_RGLRU_BWD_SCAN, (rglru_gbscan_kernel<16, FF>), grid, block, lds, s, p.L, W, ch.C, ch.G,         \
+               (const uint32_t*)p.x, (const uint32_t*)p.lx, (const uint32_t*)p.la, p.reset, p.alpha,            \
+               (const float2*)entries, (const float2*)dh_final, (uint64_t*)pub, (const uint32_t*)dy, dx, dlx,   \
+               dla, (float2*)dh0, (float2*)alpha_part)
+    if (g_f32) RG_GBSCAN(true);
+    else RG_GBSCAN(false);
+#undef RG_GBSCAN
     return hipGetLastError();
 }
 

@@ -801,14 +801,20 @@ hipError_t launch_samu_bwd_replay(const SamuParams& p, const Chunking& ch, const
 }
 
 
+hipError_t launch_clear_words(void* p, size_t bytes, hipStream_t s) {
+    const size_t n16 = bytes / 16;
+    const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div((int64_t)n16, 256), 2048));
+    LRS_LAUNCH(K_CLEAR, clear_words_kernel, dim3(blocks), dim3(256), 0, s, (uint4*)p, n16);
+    return hipGetLastError();
+}
+
 hipError_t launch_samu_gbscan(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
                               const float* entries, const float* mid, const float* chunk_rec, const float* dz_final,
                               void* pub, size_t pub_bytes, const void* dy, void* db, int db_f32, float* dz0,
                               float* tok_part, int n_tiles, float* mode_part, hipStream_t s) {
     {
-        const size_t n16 = pub_bytes / 16;
-        const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div((int64_t)n16, 256), 2048));
-        LRS_LAUNCH(K_CLEAR, clear_words_kernel, dim3(blocks), dim3(256), 0, s, (uint4*)pub, n16);
+        const hipError_t e = launch_clear_words(pub, pub_bytes, s);
+        if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)ceil_div(p.M, GB_LANES), ch.NG, ch.B);
     const dim3 block(GB_LANES * ch.G);

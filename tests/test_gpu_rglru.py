@@ -21,6 +21,13 @@ CASES = [
     ("shorter_than_chunk", 1, 5, 10, 16, 0, 0.0, 0.1),
     ("serial_prefix", 2, 500, 130, 16, 1000, 0.02, None),
     ("resets_everywhere", 1, 40, 8, 16, 1, 1.0, 0.1),
+    # single-pass scans (K=16, groups of at most 16 chunks): segments of
+    # groups chained over three segments, a ragged last chunk and a lane
+    # tile with one channel pair; the largest group; and the three-launch
+    # prefix just past it
+    ("segments_chain", 2, 2600, 130, 16, 8, 1.0 / 128, 0.1),
+    ("groups_of_16", 1, 3000, 256, 16, 16, 0.0, 0.1),
+    ("three_launch_groups", 1, 3000, 256, 16, 17, 0.01, 0.1),
 ]
 
 
