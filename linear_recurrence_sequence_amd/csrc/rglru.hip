@@ -480,15 +480,16 @@ struct RgBwdOut {
     void* dla;
 };
 
-// The adjoint over H tokens whose words are held in registers, from the
-// state h_in entering them; `active` = the lane's outputs are stored.
-template <int H, bool F32, bool FULL>
-__device__ __forceinline__ void rg_bwd_words(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
-                                             size_t tok0, int lw, int kq, uint32_t rm, bool active,
-                                             const uint32_t (&xs)[H], const uint32_t (&lxs)[H],
-                                             const uint32_t (&las)[H], const uint32_t (&gws)[H],
-                                             const float (&h_in)[2], float (&carry)[2], float (&acc)[2],
-                                             float2* hist) {
+// The forward recompute over H tokens whose words are held in registers,
+// from the state h_in entering them: h_{t-1} of every token goes to the
+// lane's LDS history.  SUMM: also the chunk's adjoint map carry_before =
+// A carry_after + B with zero carry-in, formed in token order from the same
+// retentions: A = prod a_t, B = sum_t (a_0 ... a_t) dy_t.
+template <int H, bool FULL, bool SUMM>
+__device__ __forceinline__ void rg_bwd_forward(const ChanConst (&k)[2], int kq, uint32_t rm, const uint32_t (&xs)[H],
+                                               const uint32_t (&lxs)[H], const uint32_t (&las)[H],
+                                               const uint32_t (&gws)[H], const float (&h_in)[2], float2* hist,
+                                               float (&A)[2], float (&Bv)[2]) {
     float h[2] = {h_in[0], h_in[1]};
 #pragma unroll
     for (int i = 0; i < H; ++i) {
@@ -497,15 +498,30 @@ __device__ __forceinline__ void rg_bwd_words(const RgIn& in, const ChanConst (&k
             const float xv[2] = {bf16_lo(xs[i]), bf16_hi(xs[i])};
             const float lxv[2] = {bf16_lo(lxs[i]), bf16_hi(lxs[i])};
             const float lav[2] = {bf16_lo(las[i]), bf16_hi(las[i])};
+            const float gv[2] = {bf16_lo(gws[i]), bf16_hi(gws[i])};
             hist[i * 64] = make_float2(h[0], h[1]);
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
                 const Gate g = gates(k[v], lxv[v], lav[v], rs);
                 h[v] = fmaf(g.a, h[v], xv[v] * g.gx * g.m);
+                if (SUMM) {
+                    A[v] *= g.a;
+                    Bv[v] = fmaf(A[v], gv[v], Bv[v]);
+                }
             }
         }
     }
-    asm volatile("" ::: "memory");  // read the history back from LDS, not from registers
+}
+
+// The adjoint over H tokens in reverse, from the cotangent `carry` arriving
+// after them, with h_{t-1} from the LDS history; `active` = the lane's
+// outputs are stored.
+template <int H, bool F32, bool FULL>
+__device__ __forceinline__ void rg_bwd_reverse(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
+                                               size_t tok0, int lw, int kq, uint32_t rm, bool active,
+                                               const uint32_t (&xs)[H], const uint32_t (&lxs)[H],
+                                               const uint32_t (&las)[H], const uint32_t (&gws)[H],
+                                               float (&carry)[2], float (&acc)[2], const float2* hist) {
 #pragma unroll
     for (int i = H - 1; i >= 0; --i) {
         if (FULL || i < kq) {
@@ -552,6 +568,19 @@ __device__ __forceinline__ void rg_bwd_words(const RgIn& in, const ChanConst (&k
     }
 }
 
+
+template <int H, bool F32, bool FULL>
+__device__ __forceinline__ void rg_bwd_words(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
+                                             size_t tok0, int lw, int kq, uint32_t rm, const uint32_t (&xs)[H],
+                                             const uint32_t (&lxs)[H], const uint32_t (&las)[H],
+                                             const uint32_t (&gws)[H], const float (&h_in)[2], float (&carry)[2],
+                                             float (&acc)[2], float2* hist) {
+    float A[2], Bv[2];
+    rg_bwd_forward<H, FULL, false>(k, kq, rm, xs, lxs, las, gws, h_in, hist, A, Bv);
+    asm volatile("" ::: "memory");  // read the history back from LDS, not from registers
+    rg_bwd_reverse<H, F32, FULL>(in, k, o, tok0, lw, kq, rm, true, xs, lxs, las, gws, carry, acc, hist);
+}
+
 template <int H, bool F32, bool FULL>
 __device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
                                            size_t tok0, int lw, int kq, uint32_t rm,
@@ -567,7 +596,7 @@ __device__ __forceinline__ void rg_bwd_sub(const RgIn& in, const ChanConst (&k)[
             gws[i] = word(o.dy, tok0, i, in.W, lw);
         }
     }
-    rg_bwd_words<H, F32, FULL>(in, k, o, tok0, lw, kq, rm, true, xs, lxs, las, gws, h_in, carry, acc, hist);
+    rg_bwd_words<H, F32, FULL>(in, k, o, tok0, lw, kq, rm, xs, lxs, las, gws, h_in, carry, acc, hist);
 }
 
 // state after `n` tokens (n <= H, guarded when not FULL) from h
@@ -645,13 +674,13 @@ __global__ __launch_bounds__(RG_THREADS) __attribute__((amdgpu_waves_per_eu(LRS_
 
 // Single-pass backward: wave w of group q takes chunk C - 1 - (q G + w)
 // (processing order runs backward in time).  Its words (x, l^x, l^a, dy) are
-// read once: the conjugate-free reverse summary carry -> a_t (dy_t + carry)
-// forms the chunk's map for the group's table, the carry arriving after the
-// chunk comes from the hand-off and the group's later chunks, and the
-// backward replay of rg_bwd_words runs from the saved entry state with the
-// same words.  The lanes' h histories overlay the table once the carries are
-// formed; the alpha partials of the group's chunks are added in processing
-// order into one row per group.
+// read once.  Before the hand-off, the forward recompute runs from the
+// chunk's saved entry state (h_{t-1} into the lane's LDS history) and, from
+// the same retentions, forms the chunk's adjoint map for the group's table;
+// the carry arriving after the chunk then comes from the hand-off and the
+// group's later chunks, and the reverse pass (gates evaluated again) runs
+// from it.  The alpha partials of the group's chunks are added in
+// processing order into one row per group.
 template <int K, bool F32>
 __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
     int L, int W, int C, int G, const uint32_t* __restrict__ x, const uint32_t* __restrict__ lx,
@@ -659,11 +688,11 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
     const float2* __restrict__ entries, const float2* __restrict__ dh_final, uint64_t* __restrict__ pub,
     const uint32_t* __restrict__ dy, void* __restrict__ dx, void* __restrict__ dlx, void* __restrict__ dla,
     float2* __restrict__ dh0, float2* __restrict__ alpha_part) {
-    extern __shared__ float4 rg_lds[];  // comp [G][64] and look [G][64], later hist [G][K][64] float2
+    extern __shared__ float4 rg_lds[];  // comp [G][64], look [G][64], hist [G][K][64] float2
     float4* const comp = rg_lds;
     float4* const look = rg_lds + G * RG_GL;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    float2* const hist = reinterpret_cast<float2*>(rg_lds) + (size_t)w * K * RG_GL + lane;
+    float2* const hist = reinterpret_cast<float2*>(rg_lds + 2 * G * RG_GL) + (size_t)w * K * RG_GL + lane;
     const int q = blockIdx.y, b = blockIdx.z, NG = gridDim.y;
     const int pc = q * G + w;
     const bool valid = pc < C;  // wave-uniform
@@ -690,19 +719,9 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
     }
     const int kq = opaque(kc);
     float A[2] = {1.f, 1.f}, Bv[2] = {0.f, 0.f};
-#pragma unroll
-    for (int i = K - 1; i >= 0; --i) {
-        if (i < kq) {
-            const bool rs = bit(rm, i);
-            const float lav[2] = {bf16_lo(las[i]), bf16_hi(las[i])};
-            const float gv[2] = {bf16_lo(gws[i]), bf16_hi(gws[i])};
-#pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                const float a = retention(k[v], lav[v], rs);
-                A[v] *= a;
-                Bv[v] = a * (Bv[v] + gv[v]);
-            }
-        }
+    {
+        const float h_in[2] = {e.x, e.y};
+        rg_bwd_forward<K, false, true>(k, kq, rm, xs, lxs, las, gws, h_in, hist, A, Bv);
     }
     comp[w * RG_GL + lane] = make_float4(A[0], Bv[0], A[1], Bv[1]);
     __syncthreads();
@@ -715,24 +734,23 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
         carry[0] = fmaf(f.x, carry[0], f.y);
         carry[1] = fmaf(f.z, carry[1], f.w);
     }
-    __syncthreads();  // the table's LDS becomes the h histories
     float acc[2] = {0.f, 0.f};
     if (valid) {
         const RgIn in{L, W, x, lx, la, reset};
         const RgBwdOut o{dy, dx, dlx, dla};
-        const float h_in[2] = {e.x, e.y};
-        rg_bwd_words<K, F32, false>(in, k, o, tok0, lw, kq, rm, active, xs, lxs, las, gws, h_in, carry, acc, hist);
+        rg_bwd_reverse<K, F32, false>(in, k, o, tok0, lw, kq, rm, active, xs, lxs, las, gws, carry, acc, hist);
         if (dh0 && active && c == 0) dh0[(size_t)b * W + lw] = make_float2(carry[0], carry[1]);
     }
     // the alpha partials of the group's chunks, in processing order, through
-    // each wave's own history slots (free once its replay is done)
+    // each wave's own history slots (free once its reverse pass is done)
     hist[0] = make_float2(acc[0] * k[0].dsp8, acc[1] * k[1].dsp8);
     __syncthreads();
     if (w == 0 && active) {
+        const float2* part = reinterpret_cast<const float2*>(rg_lds + 2 * G * RG_GL) + lane;
         const int n = min(G, C - q * G);
         float s0 = 0.f, s1 = 0.f;
         for (int j = 0; j < n; ++j) {
-            const float2 v = reinterpret_cast<const float2*>(rg_lds)[(size_t)j * K * RG_GL + lane];
+            const float2 v = part[(size_t)j * K * RG_GL];
             s0 += v.x;
             s1 += v.y;
         }
@@ -888,8 +906,8 @@ hipError_t launch_rglru_gbscan(const RglruParams& p, const Chunking& ch, const f
     const int W = p.D / 2;
     const dim3 grid((unsigned)ceil_div(W, RG_GL), ch.NG, ch.B);
     const dim3 block(RG_GL * ch.G);
-    // the map table and hand-off scratch, overlaid by the h histories
-    const size_t lds = std::max((size_t)2 * ch.G * RG_GL * sizeof(float4), (size_t)ch.G * 16 * RG_GL * sizeof(float2));
+    // the map table, the hand-off scratch and the h histories
+    const size_t lds = (size_t)2 * ch.G * RG_GL * sizeof(float4) + (size_t)ch.G * 16 * RG_GL * sizeof(float2);
 #define RG_GBSCAN(FF)                                                                                          \
     LRS_LAUNCH(K_RGLRU_BWD_SCAN, (rglru_gbscan_kernel<16, FF>), grid, block, lds, s, p.L, W, ch.C, ch.G,         \
                (const uint32_t*)p.x, (const uint32_t*)p.lx, (const uint32_t*)p.la, p.reset, p.alpha,            \
