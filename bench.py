@@ -191,11 +191,11 @@ def rglru_kernel_bytes(B, L, D, K, G, resets, unfused=False):
     G_ = effective_groups(L, K, G, 16)
     if K == 16 and G_ <= 16 and not unfused:
         # the single-pass path: x, l^x, l^a (and dy) read once per direction;
-        # the design adds the hand-off (16 B per (group, channel) published,
-        # about (G - 1) / 2 maps and one state read per group) and writes one
-        # alpha row per group
+        # the design adds the hand-off (one 8 B word per (group, channel)
+        # published, about (G - 1) / 2 maps and one state read per group) and
+        # writes one alpha row per group
         NGD = B * NG * D
-        handoff = 16 * NGD + (8 * (G_ - 1) + 8) * NGD
+        handoff = 8 * NGD + (4 * (G_ - 1) + 8) * NGD
         for k in ("rglru_chunk_summary", "rglru_replay", "rglru_reverse_summary", "rglru_bwd_replay",
                   "prefix_group_compose", "prefix_group_scan", "prefix_chunk_entries"):
             tab.pop(k, None)
@@ -205,7 +205,7 @@ def rglru_kernel_bytes(B, L, D, K, G, resets, unfused=False):
             "rglru_forward_scan": (fwd, fwd + handoff),
             "rglru_backward_scan": (bwd + 4 * BCD, bwd + 4 * NGD + handoff),
             "rglru_alpha": (4 * BCD + 4 * D, 4 * NGD + 4 * D),
-            "clear": (0, 16 * NGD),
+            "clear": (0, 8 * NGD),
         })
     return tab
 

@@ -234,38 +234,46 @@ __global__ __launch_bounds__(RG_THREADS) void rglru_replay_kernel(RgIn in, int C
 // entering it.
 constexpr int RG_GL = 64;  // lanes (channel pairs) per workgroup
 
-// Hand-off words, per (group, lane): the group's map (A0, B0, A1, B1) for a
-// group inside a segment, or the state (h0, h1) leaving a segment's last
-// group; each value is its own tagged 64-bit word (pub_store / pub_load of
-// common.hpp).  Unlike the complex scan, the transition part of a group's
-// map depends on every token's gate, so it travels with the affine part.
-constexpr int RG_PUB_WORDS = 4;
+// Hand-off words, per (group, lane), one per channel: the group's map for a
+// group inside a segment, or the state leaving a segment's last group.  A
+// map (A, B) is one word, B in the high half and -A in the low half: A is a
+// product of retentions, never negative, so the low half of a published map
+// has its sign bit set and a zeroed word reads as unpublished.  A state is
+// a tagged word as in the complex scan ((1 << 32) | float bits, pub_store of
+// common.hpp).  A 64-bit word is never torn, so no fence is needed.  Unlike
+// the complex scan, the transition part of a group's map depends on every
+// token's gate, so it travels with the affine part.
+constexpr int RG_PUB_WORDS = 2;
 
-// The first N words of an earlier group for this lane, once all are
-// published (bounded wait, as wait_pair).
-template <int N>
-__device__ __forceinline__ void wait_words(const uint64_t* grp, uint32_t Wb, uint32_t off, float (&v)[N]) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = 0.f;
+__device__ __forceinline__ void pub_store_map(uint64_t* grp, int i, uint32_t Wb, uint32_t off, float a, float b) {
+    __hip_atomic_store(pub_word(grp, i, Wb, off),
+                       ((uint64_t)__float_as_uint(b) << 32) | (uint64_t)__float_as_uint(-a), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool map_ok(uint64_t w) { return ((uint32_t)w >> 31) != 0u; }
+
+// The two words of an earlier group for this lane, once both are published
+// (MAP: maps, else states; bounded wait, as wait_pair).  v = (A0, B0, A1, B1)
+// for maps, (h0, h1, 0, 0) for states.
+template <bool MAP>
+__device__ __forceinline__ float4 wait_group(const uint64_t* grp, uint32_t Wb, uint32_t off) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     bool ok = false;
     for (int it = 0; it < SCAN_SPIN_MAX; ++it) {
         if (!ok) {
             const uint32_t o = opaque_v(off);
-            uint64_t wd[N];
-#pragma unroll
-            for (int i = 0; i < N; ++i) wd[i] = pub_load(grp, i, Wb, o);
-            bool all = true;
-#pragma unroll
-            for (int i = 0; i < N; ++i) all = all && pub_ok(wd[i]);
-            if (all) {
-#pragma unroll
-                for (int i = 0; i < N; ++i) v[i] = pub_val(wd[i]);
+            const uint64_t w0 = pub_load(grp, 0, Wb, o), w1 = pub_load(grp, 1, Wb, o);
+            if (MAP ? (map_ok(w0) && map_ok(w1)) : (pub_ok(w0) && pub_ok(w1))) {
+                v = MAP ? make_float4(-__uint_as_float((uint32_t)w0), __uint_as_float((uint32_t)(w0 >> 32)),
+                                      -__uint_as_float((uint32_t)w1), __uint_as_float((uint32_t)(w1 >> 32)))
+                        : make_float4(pub_val(w0), pub_val(w1), 0.f, 0.f);
                 ok = true;
             }
         }
         if (__all(ok)) break;
         __builtin_amdgcn_s_sleep(1);
     }
+    return v;
 }
 
 // The state entering group q (processing order) for this lane's two
@@ -292,25 +300,20 @@ __device__ __forceinline__ float2 rg_group_handoff(const float4* comp, float4* l
             b1 = fmaf(f.z, b1, f.w);
             a1 *= f.z;
         }
-        pub_store(mine, 0, Wb, off, a0);
-        pub_store(mine, 1, Wb, off, b0);
-        pub_store(mine, 2, Wb, off, a1);
-        pub_store(mine, 3, Wb, off, b1);
+        pub_store_map(mine, 0, Wb, off, a0, b0);
+        pub_store_map(mine, 1, Wb, off, a1, b1);
     }
     if (w < nprev) {
-        float v[4];
-        wait_words<4>(pub + (size_t)(q - 1 - w) * RG_PUB_WORDS * W, Wb, off, v);
-        look[w * RG_GL + lane] = make_float4(v[0], v[1], v[2], v[3]);
+        look[w * RG_GL + lane] = wait_group<true>(pub + (size_t)(q - 1 - w) * RG_PUB_WORDS * W, Wb, off);
     } else if (w == nprev) {
-        float2 hs = make_float2(0.f, 0.f);
+        float4 hs = make_float4(0.f, 0.f, 0.f, 0.f);
         if (q - nprev > 0) {
-            float v[2];
-            wait_words<2>(pub + (size_t)(q - nprev - 1) * RG_PUB_WORDS * W, Wb, off, v);
-            hs = make_float2(v[0], v[1]);
+            hs = wait_group<false>(pub + (size_t)(q - nprev - 1) * RG_PUB_WORDS * W, Wb, off);
         } else if (seed) {
-            hs = seed[lw];
+            const float2 h = seed[lw];
+            hs = make_float4(h.x, h.y, 0.f, 0.f);
         }
-        look[w * RG_GL + lane] = make_float4(hs.x, hs.y, 0.f, 0.f);
+        look[w * RG_GL + lane] = hs;
     }
     __syncthreads();
     if (w == 0) {
