@@ -74,14 +74,16 @@ struct Gate {
     float r;        // rsq(1 - a0^2) (infinite-free)
 };
 
-// Gates of one channel at one token; rs = segment start.
-__device__ __forceinline__ Gate gates(const ChanConst& k, float lx, float la, bool rs) {
+// Gates of one channel at one token; rs = segment start.  KNOWN: the
+// retention a0 was formed earlier from the same inputs and is passed in.
+template <bool KNOWN = false>
+__device__ __forceinline__ Gate gates(const ChanConst& k, float lx, float la, bool rs, float a0 = 0.f) {
     Gate g;
     const float px = 1.0f + neg_exp(lx), pa = 1.0f + neg_exp(la);
     const float q = __builtin_amdgcn_rcpf(px * pa);
     g.gx = q * pa;
     g.ga = q * px;
-    g.a0 = __builtin_amdgcn_exp2f(k.k8 * g.ga);
+    g.a0 = KNOWN ? a0 : __builtin_amdgcn_exp2f(k.k8 * g.ga);
     // 1 - a^2 >= 0 exactly (a <= 1), so the FMA result is >= 0; the floor only
     // keeps rsq finite at a = 1, where u rsq(u) is then 0 as it must be
     const float u = fmaxf(fmaf(-g.a0, g.a0, 1.0f), 1e-30f);
@@ -488,11 +490,12 @@ struct RgBwdOut {
 // lane's LDS history.  SUMM: also the chunk's adjoint map carry_before =
 // A carry_after + B with zero carry-in, formed in token order from the same
 // retentions: A = prod a_t, B = sum_t (a_0 ... a_t) dy_t.
-template <int H, bool FULL, bool SUMM>
+// KEEP: every token's retention a0 is kept in a0s for the reverse pass.
+template <int H, bool FULL, bool SUMM, bool KEEP = false>
 __device__ __forceinline__ void rg_bwd_forward(const ChanConst (&k)[2], int kq, uint32_t rm, const uint32_t (&xs)[H],
                                                const uint32_t (&lxs)[H], const uint32_t (&las)[H],
                                                const uint32_t (&gws)[H], const float (&h_in)[2], float2* hist,
-                                               float (&A)[2], float (&Bv)[2]) {
+                                               float (&A)[2], float (&Bv)[2], float (&a0s)[H][2]) {
     float h[2] = {h_in[0], h_in[1]};
 #pragma unroll
     for (int i = 0; i < H; ++i) {
@@ -506,6 +509,7 @@ __device__ __forceinline__ void rg_bwd_forward(const ChanConst (&k)[2], int kq, 
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
                 const Gate g = gates(k[v], lxv[v], lav[v], rs);
+                if (KEEP) a0s[i][v] = g.a0;
                 h[v] = fmaf(g.a, h[v], xv[v] * g.gx * g.m);
                 if (SUMM) {
                     A[v] *= g.a;
@@ -518,13 +522,14 @@ __device__ __forceinline__ void rg_bwd_forward(const ChanConst (&k)[2], int kq, 
 
 // The adjoint over H tokens in reverse, from the cotangent `carry` arriving
 // after them, with h_{t-1} from the LDS history; `active` = the lane's
-// outputs are stored.
-template <int H, bool F32, bool FULL>
+// outputs are stored; KEEP: the retentions come from the forward pass.
+template <int H, bool F32, bool FULL, bool KEEP = false>
 __device__ __forceinline__ void rg_bwd_reverse(const RgIn& in, const ChanConst (&k)[2], const RgBwdOut& o,
                                                size_t tok0, int lw, int kq, uint32_t rm, bool active,
                                                const uint32_t (&xs)[H], const uint32_t (&lxs)[H],
                                                const uint32_t (&las)[H], const uint32_t (&gws)[H],
-                                               float (&carry)[2], float (&acc)[2], const float2* hist) {
+                                               float (&carry)[2], float (&acc)[2], const float2* hist,
+                                               const float (&a0s)[H][2]) {
 #pragma unroll
     for (int i = H - 1; i >= 0; --i) {
         if (FULL || i < kq) {
@@ -542,7 +547,7 @@ __device__ __forceinline__ void rg_bwd_reverse(const RgIn& in, const ChanConst (
             float ox[2], olx[2], ola[2];
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
-                const Gate gt = gates(k[v], lxv[v], lav[v], rs);
+                const Gate gt = gates<KEEP>(k[v], lxv[v], lav[v], rs, a0s[i][v]);
                 const float g = gv[v] + carry[v];
                 const float xg = xv[v] * gt.gx;
                 ox[v] = g * gt.gx * gt.m;
@@ -578,10 +583,10 @@ __device__ __forceinline__ void rg_bwd_words(const RgIn& in, const ChanConst (&k
                                              const uint32_t (&lxs)[H], const uint32_t (&las)[H],
                                              const uint32_t (&gws)[H], const float (&h_in)[2], float (&carry)[2],
                                              float (&acc)[2], float2* hist) {
-    float A[2], Bv[2];
-    rg_bwd_forward<H, FULL, false>(k, kq, rm, xs, lxs, las, gws, h_in, hist, A, Bv);
+    float A[2], Bv[2], a0s[H][2];
+    rg_bwd_forward<H, FULL, false>(k, kq, rm, xs, lxs, las, gws, h_in, hist, A, Bv, a0s);
     asm volatile("" ::: "memory");  // read the history back from LDS, not from registers
-    rg_bwd_reverse<H, F32, FULL>(in, k, o, tok0, lw, kq, rm, true, xs, lxs, las, gws, carry, acc, hist);
+    rg_bwd_reverse<H, F32, FULL>(in, k, o, tok0, lw, kq, rm, true, xs, lxs, las, gws, carry, acc, hist, a0s);
 }
 
 template <int H, bool F32, bool FULL>
@@ -675,6 +680,14 @@ __global__ __launch_bounds__(RG_THREADS) __attribute__((amdgpu_waves_per_eu(LRS_
     if (dh0 && c == 0) reinterpret_cast<float2*>(dh0)[(size_t)b * in.W + lw] = make_float2(carry[0], carry[1]);
 }
 
+// The single-pass backward keeps each token's retention from the forward
+// recompute to the reverse pass (one special function fewer per channel
+// and token in the reverse pass, 32 more registers).
+#ifndef LRS_RG_GB_KEEP
+#define LRS_RG_GB_KEEP 1
+#endif
+constexpr bool RG_GB_KEEP = LRS_RG_GB_KEEP != 0;
+
 // Single-pass backward: wave w of group q takes chunk C - 1 - (q G + w)
 // (processing order runs backward in time).  Its words (x, l^x, l^a, dy) are
 // read once.  Before the hand-off, the forward recompute runs from the
@@ -721,10 +734,10 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
         }
     }
     const int kq = opaque(kc);
-    float A[2] = {1.f, 1.f}, Bv[2] = {0.f, 0.f};
+    float A[2] = {1.f, 1.f}, Bv[2] = {0.f, 0.f}, a0s[K][2];
     {
         const float h_in[2] = {e.x, e.y};
-        rg_bwd_forward<K, false, true>(k, kq, rm, xs, lxs, las, gws, h_in, hist, A, Bv);
+        rg_bwd_forward<K, false, true, RG_GB_KEEP>(k, kq, rm, xs, lxs, las, gws, h_in, hist, A, Bv, a0s);
     }
     comp[w * RG_GL + lane] = make_float4(A[0], Bv[0], A[1], Bv[1]);
     __syncthreads();
@@ -741,7 +754,8 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
     if (valid) {
         const RgIn in{L, W, x, lx, la, reset};
         const RgBwdOut o{dy, dx, dlx, dla};
-        rg_bwd_reverse<K, F32, false>(in, k, o, tok0, lw, kq, rm, active, xs, lxs, las, gws, carry, acc, hist);
+        rg_bwd_reverse<K, F32, false, RG_GB_KEEP>(in, k, o, tok0, lw, kq, rm, active, xs, lxs, las, gws, carry,
+                                                  acc, hist, a0s);
         if (dh0 && active && c == 0) dh0[(size_t)b * W + lw] = make_float2(carry[0], carry[1]);
     }
     // the alpha partials of the group's chunks, in processing order, through
