@@ -226,6 +226,12 @@ scan_status samu_scan_decode_prepare(int D, const float* w_phi, const float* w_r
  *   g^x = sigmoid(l^x), g^a = sigmoid(l^a), a_t = exp(-8 g^a softplus(alpha)),
  *   b_t = x_t g^x sqrt(max(1 - a_t^2, 0)),  h_t = a_t h_{t-1} + b_t,  y_t = h_t;
  *   at a segment start (reset[b, t] != 0): a_t = 0 and the multiplier is 1.
+ * K and G as for SAMU; G = 0 picks groups of 8 chunks at K = 16 and the
+ * pages' long groups at K = 32.  At K = 16 with G <= 16 each direction is
+ * one single-pass launch (after a small one that clears its hand-off words),
+ * as for SAMU; otherwise the three-launch prefix runs.  Either way nothing
+ * is accumulated atomically and results are bitwise reproducible for the
+ * same inputs, K, G and device.
  * ====================================================================== */
 
 size_t rglru_scan_saved_bytes(int B, int L, int D, int K);
@@ -277,7 +283,8 @@ scan_status rglru_gate_proj_fwd(int B, int L, int D, const void* x,
                                 void* lx, void* la, void* stream);
 
 /* Adjoint of the projections for the logit cotangents dlx, dla (as written
- * by rglru_scan_bwd, of grad_dtype):
+ * by rglru_scan_bwd, of grad_dtype); with BF16 cotangents and D <= 2048 one
+ * pass over the tensors forms dx and the weight partials together:
  *   dx_out = dx_in + per block W_x^T dlx + W_a^T dla   ([B, L, D], grad_dtype;
  *            dx_out may equal dx_in, must not overlap it otherwise),
  *   dw = sum_t dl x^T per block (f32 [16, D/16, D/16]), db = sum_t dl (f32 [D]).

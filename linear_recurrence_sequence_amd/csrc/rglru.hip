@@ -13,11 +13,13 @@
 //   square-root derivative is truncated (capped at 1000 here).
 //
 // Layout: lanes run over channel pairs (one 32-bit word of each BF16 tensor
-// per lane and token, so a wave reads 256 contiguous bytes of a row); a
-// workgroup owns one chunk of one batch row and 512 channels.  Every chunk
-// but a ragged last one is loaded branch-free from a uniform row base plus
-// a 32-bit lane offset; the last one takes a guarded instance of the same
-// code.
+// per lane and token, so a wave reads 256 contiguous bytes of a row).  On
+// the single-pass path (K = 16, groups of up to 16 chunks) a workgroup owns
+// one group of chunks, one wave per chunk, and 64 channel pairs, and the
+// groups hand states to each other; on the three-launch path a workgroup
+// owns one chunk of one batch row and 512 channels, every chunk but a
+// ragged last one loaded branch-free from a uniform row base plus a 32-bit
+// lane offset, the last one by a guarded instance of the same code.
 //
 // Special functions per channel and token: both sigmoids share one
 // reciprocal, 1/((1+e^-lx)(1+e^-la)), and one reciprocal square root gives
