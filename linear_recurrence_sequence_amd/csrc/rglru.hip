@@ -552,15 +552,19 @@ __device__ __forceinline__ void rg_bwd_reverse(const RgIn& in, const ChanConst (
                 const Gate gt = gates<KEEP>(k[v], lxv[v], lav[v], rs, a0s[i][v]);
                 const float g = gv[v] + carry[v];
                 const float xg = xv[v] * gt.gx;
-                ox[v] = g * gt.gx * gt.m;
-                olx[v] = g * xg * gt.m * (1.0f - gt.gx);
+                // dx = g g^x m; dl^x = g m x g^x (1 - g^x), with x g^x (1 - g^x)
+                // = xg - xg g^x
+                const float gm = g * gt.m;
+                ox[v] = gm * gt.gx;
+                olx[v] = gm * fmaf(-xg, gt.gx, xg);
                 // d h / d a = h_{t-1} + x g^x dm/da, dm/da = -a / sqrt(u) (capped);
                 // zero at a segment start, where a and m are constants
                 const float dm_da = -gt.a0 * fminf(gt.r, RG_RSQ_CAP);
                 const float abar = rs ? 0.0f : g * fmaf(xg, dm_da, hpv[v]);
                 // d a / d l^a = a (-8 sp) g^a (1 - g^a); d a / d alpha = a g^a (-8 sigmoid(alpha))
-                const float ag = abar * gt.a0 * gt.ga;
-                ola[v] = ag * k[v].sp8 * (1.0f - gt.ga);
+                const float ag = abar * (gt.a0 * gt.ga);
+                const float ags = ag * k[v].sp8;
+                ola[v] = fmaf(-ags, gt.ga, ags);
                 acc[v] += ag;
                 carry[v] = gt.a * g;
             }
