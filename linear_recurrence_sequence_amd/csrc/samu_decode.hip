@@ -11,14 +11,15 @@
 //   lambda_m = exp(-nu_m e^c) [(cos th_m cos d - sin th_m sin d) + i (...)],
 //   z' = lambda z + b,  y = z'.
 //
-// Grid (ceil(M / 256), B): each workgroup forms the two dot products (and,
-// without a prepared table, the two direction norms) of its batch row, 16
-// bytes of the row per thread and step, then 256 lanes advance one mode
-// each.  Every mode block repeats the row's small reduction, which measured
-// faster than one larger workgroup per row, and faster than several rows per
-// workgroup sharing the direction loads (the rows then run one after another
-// in each workgroup).  Sums run in a fixed order, so a step is bitwise
-// reproducible.
+// Grid (ceil(M / NT), B) with NT = 256 threads (512 from 128 rows up): each
+// workgroup forms the two dot products (and, without a prepared table, the
+// two direction norms) of its batch row, 16 bytes of the row per thread and
+// step, then NT lanes advance one mode each.  Every mode block repeats the
+// row's small reduction, which measured faster than one workgroup per row
+// (1024 threads), and faster than several rows per workgroup sharing the
+// direction loads (the rows then run one after another in each workgroup).
+// Sums run in a fixed order for a given batch size and width, so a step is
+// bitwise reproducible.
 #include "common.hpp"
 
 namespace lrs {
@@ -30,21 +31,22 @@ constexpr int DEC_WAVES = DEC_THREADS / 64;
 // TAB: the mode constants, 1/||w|| and tanh(a)/sqrt(M) come from a table
 // written once by samu_decode_prepare_kernel (no FP64 phasor, no norm
 // reduction and no amplitude tanh per step).
-template <bool F32, bool TAB>
-__global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
+template <bool F32, bool TAB, int NT>
+__global__ __launch_bounds__(NT) void samu_decode_kernel(
     int B, int D, int M, const uint32_t* __restrict__ x_sel, const uint32_t* __restrict__ drive,
     const float* __restrict__ w_phi, const float* __restrict__ w_r, const float* __restrict__ a_phi,
     const float* __restrict__ a_r, const float* __restrict__ nu, const float* __restrict__ theta,
     const float4* __restrict__ table, const float2* z_in, float2* z_out, void* __restrict__ y) {
     constexpr int R = 1;  // batch rows per workgroup
-    __shared__ float red[2 * R + 2][DEC_WAVES];
+    constexpr int NW = NT / 64;
+    __shared__ float red[2 * R + 2][NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b0 = blockIdx.y * R;
     const int W = D / 2;  // selector words per row
 
     // this lane's mode in each row: its inputs are requested first and its
     // constant phasor is formed (or loaded) while the reduction is in flight
-    const int m = blockIdx.x * DEC_THREADS + tid;
+    const int m = blockIdx.x * NT + tid;
     const bool act = m < M;
     const int mc = act ? m : M - 1;
     float2 zr[R];
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
     for (int r = 0; r < R; ++r) { sp[r] = 0.f; sr[r] = 0.f; }
     float np = 0.f, nr = 0.f;
     const int W4 = W >> 2;  // 16-byte selector pieces per row (D % 8 == 0)
-    for (int j = tid; j < W4; j += DEC_THREADS) {
+    for (int j = tid; j < W4; j += NT) {
         uint4 xv[R];
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
     float Np = 0.f, Nr = 0.f;
     if (!TAB) {
 #pragma unroll
-        for (int w = 0; w < DEC_WAVES; ++w) {
+        for (int w = 0; w < NW; ++w) {
             Np += red[2 * R][w];
             Nr += red[2 * R + 1][w];
         }
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(DEC_THREADS) void samu_decode_kernel(
         if (b0 + r >= B) break;  // uniform over the workgroup
         float Sp = 0.f, Sr = 0.f;
 #pragma unroll
-        for (int w = 0; w < DEC_WAVES; ++w) {
+        for (int w = 0; w < NW; ++w) {
             Sp += red[2 * r][w];
             Sr += red[2 * r + 1][w];
         }
@@ -232,16 +234,23 @@ hipError_t launch_samu_decode(int B, int D, const void* x_sel, const void* b, co
                               const float* theta, const float* table, const float* z_in, float* z_out, void* y,
                               int y_f32, hipStream_t s) {
     const int M = D / 2;
-    const dim3 grid((unsigned)ceil_div(M, DEC_THREADS), (unsigned)B);
-#define DEC_CASE(FF, TT)                                                                                    \
-    LRS_LAUNCH(K_SAMU_DECODE, (samu_decode_kernel<FF, TT>), grid, dim3(DEC_THREADS), 0, s, B, D, M,       \
+    // 512-thread workgroups from 128 rows up (half as many workgroups, each
+    // row's reduction shared by 512 modes): measured faster at B = 256 (4.0
+    // against 4.4 us per step from a graph), slower below 128 rows
+    const int NT = B >= 128 ? 512 : DEC_THREADS;
+    const dim3 grid((unsigned)ceil_div(M, NT), (unsigned)B);
+#define DEC_CASE(FF, TT, N)                                                                                 \
+    LRS_LAUNCH(K_SAMU_DECODE, (samu_decode_kernel<FF, TT, N>), grid, dim3(N), 0, s, B, D, M,               \
                (const uint32_t*)x_sel, (const uint32_t*)b, w_phi, w_r, a_phi, a_r, nu, theta,              \
                (const float4*)table, (const float2*)z_in, (float2*)z_out, y)
+#define DEC_SIZES(FF, TT) \
+    if (NT == 512) DEC_CASE(FF, TT, 512); else DEC_CASE(FF, TT, DEC_THREADS);
     if (table) {
-        if (y_f32) DEC_CASE(true, true); else DEC_CASE(false, true);
+        if (y_f32) { DEC_SIZES(true, true) } else { DEC_SIZES(false, true) }
     } else {
-        if (y_f32) DEC_CASE(true, false); else DEC_CASE(false, false);
+        if (y_f32) { DEC_SIZES(true, false) } else { DEC_SIZES(false, false) }
     }
+#undef DEC_SIZES
 #undef DEC_CASE
     return hipGetLastError();
 }
