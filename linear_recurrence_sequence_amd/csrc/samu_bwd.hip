@@ -98,18 +98,23 @@ __device__ __forceinline__ void bwd_issue(cf (&ck)[K / H], uint32_t (&bw)[K], ui
 // code for full and partial chunks alike -- loads past a partial chunk's end
 // re-read its last token and every use is guarded by the token count.
 // STASH: the first sub-chunk's state is read from ck0_lds, so ck[0] need not
-// stay in a register through the later sub-chunks.
-template <int K, int H, bool F32, bool FULL, bool WSYNC, bool CLAMP = false, bool STASH = false>
+// stay in a register through the later sub-chunks.  RH: tokens per partial-
+// sum transpose (the rows hold RH tokens).  DYS: the cotangent words of the
+// earlier sub-chunks come from the lane's LDS slots dy_lds[i * 64] (written
+// by the caller) instead of a second read from memory.
+template <int K, int H, bool F32, bool FULL, bool WSYNC, bool CLAMP = false, bool STASH = false, int RH = H,
+          bool DYS = false>
 __device__ __forceinline__ void bwd_body(float* lds_w, const TokenCtl* sctl, const ModeConst& k, bool active,
                                          int lane, int tile, int n_tiles, int L, int M, int b, int s, int kc,
                                          size_t row0, int mm, const uint32_t* __restrict__ dy, void* __restrict__ db,
                                          float* __restrict__ tok_part, const cf (&ck)[K / H], const uint32_t (&bw)[K],
                                          uint32_t (&gw)[K], cf& carry, float& acc_nu, float& acc_th,
-                                         const float2* ck0_lds = nullptr) {
+                                         const float2* ck0_lds = nullptr, const uint32_t* dy_lds = nullptr) {
     constexpr int NH = K / H;
     static_assert(NH == 1 || (H == SAMU_BWD_SUB && NH - 1 == samu_mid_states(K)),
                   "sub-chunks must match the forward's mid states");
-    constexpr int NV = 2 * H;
+    static_assert(H % RH == 0 && 64 % (2 * RH) == 0, "transpose blocks");
+    constexpr int NV = 2 * RH;
     constexpr int PAD = NV + 1;
     const int kq = opaque(kc);
     float* row = &lds_w[lane * PAD];
@@ -121,7 +126,8 @@ __device__ __forceinline__ void bwd_body(float* lds_w, const TokenCtl* sctl, con
 #pragma unroll
             for (int j = H - 1; j >= 0; --j) {
                 const int i = i0 + j;
-                if (CLAMP) gw[i] = (dy + row0 + (size_t)min(i, kc - 1) * M)[mm];
+                if (DYS) gw[i] = dy_lds[i * 64];
+                else if (CLAMP) gw[i] = (dy + row0 + (size_t)min(i, kc - 1) * M)[mm];
                 else gw[i] = (FULL || i < kc) ? (dy + row0 + (size_t)i * M)[mm] : 0u;
             }
         }
@@ -163,27 +169,29 @@ __device__ __forceinline__ void bwd_body(float* lds_w, const TokenCtl* sctl, con
                 carry = cmulc(lam[j], gg);
             }
             if (!active) { pr = 0.f; pi = 0.f; }
-            row[2 * j] = pr;
-            row[2 * j + 1] = pi;
-        }
-        if (WSYNC) wave_lds_sync(); else __syncthreads();
-        // column col (token col/2, component col%2) summed over the wave's
-        // 64 modes: 64/NV lanes per column, NV rows each, then a butterfly
-        {
-            const int col = lane % NV, grp = lane / NV;
-            const float* src = &lds_w[grp * NV * PAD + col];
-            float acc = 0.f;
+            row[2 * (j % RH)] = pr;
+            row[2 * (j % RH) + 1] = pi;
+            if (j % RH != 0) continue;
+            if (WSYNC) wave_lds_sync(); else __syncthreads();
+            // column col (token j + col/2, component col%2) summed over the
+            // wave's 64 modes: 64/NV lanes per column, NV rows each, then a
+            // butterfly
+            {
+                const int col = lane % NV, grp = lane / NV;
+                const float* src = &lds_w[grp * NV * PAD + col];
+                float acc = 0.f;
 #pragma unroll
-            for (int r = 0; r < NV; ++r) acc += src[r * PAD];
+                for (int r = 0; r < NV; ++r) acc += src[r * PAD];
 #pragma unroll
-            for (int o = NV; o < 64; o <<= 1) acc += __shfl_xor(acc, o);
-            const int t = i0 + (col >> 1);
-            if (grp == 0 && t < kc && tile < n_tiles) {
-                if ((col & 1) == 0) acc *= -sctl[t].E;
-                tok_part[(((size_t)b * n_tiles + tile) * L + s + i0) * 2 + col] = acc;
+                for (int o = NV; o < 64; o <<= 1) acc += __shfl_xor(acc, o);
+                const int t = i0 + j + (col >> 1);
+                if (grp == 0 && t < kc && tile < n_tiles) {
+                    if ((col & 1) == 0) acc *= -sctl[t].E;
+                    tok_part[(((size_t)b * n_tiles + tile) * L + s + i0 + j) * 2 + col] = acc;
+                }
             }
+            if (WSYNC) wave_lds_sync(); else __syncthreads();
         }
-        if (WSYNC) wave_lds_sync(); else __syncthreads();
     }
 }
 
@@ -249,6 +257,10 @@ __global__ __launch_bounds__(BWD_THREADS) __attribute__((amdgpu_waves_per_eu(LRS
 }
 
 constexpr int GB_LANES = 64;
+// Tokens per partial-sum transpose in the single-pass backward: 8 when the
+// chunk has earlier sub-chunks, whose cotangent words then take the LDS the
+// smaller rows leave free, else the sub-chunk.
+__host__ __device__ constexpr inline int gb_row_tokens(int K, int H) { return K > H ? 8 : H; }
 
 // Single-pass grouped backward: the reverse summaries, the carry entering
 // each group and the backward replay in one launch.  A workgroup owns one
@@ -272,16 +284,21 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
                                             float2* __restrict__ dz0, float* __restrict__ tok_part,
                                             float2* __restrict__ mode_part) {
     constexpr int NH = K / H;
-    constexpr int ROW = 64 * (2 * H + 1);  // floats of one wave's transpose rows
+    constexpr int KE = K - H;  // tokens of the earlier sub-chunks
+    constexpr int RH = gb_row_tokens(K, H);
+    constexpr int ROW = 64 * (2 * RH + 1);  // floats of one wave's transpose rows
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    // LDS: [G][64] entry states, [G][K] token controls, [G][ROW] transpose
-    // rows; the group's summary table and the hand-off scratch ([G][64]
-    // float4 each) overlay the rows (read only before the last barrier ahead
-    // of the replay, the rows only after it)
+    // LDS: [G][64] entry states, [G][K] token controls, [G][KE][64] the
+    // earlier sub-chunks' cotangent words, [G][ROW] transpose rows; the
+    // group's summary table and the hand-off scratch ([G][64] float4 each)
+    // overlay the rows (read only before the last barrier ahead of the
+    // replay, the rows only after it)
     float2* stash = reinterpret_cast<float2*>(gdyn) + w * GB_LANES + lane;
     TokenCtl* sctl = reinterpret_cast<TokenCtl*>(reinterpret_cast<float2*>(gdyn) + G * GB_LANES) + w * K;
-    float* rows = reinterpret_cast<float*>(reinterpret_cast<TokenCtl*>(reinterpret_cast<float2*>(gdyn) + G * GB_LANES) +
-                                           G * K);
+    uint32_t* dys = reinterpret_cast<uint32_t*>(reinterpret_cast<TokenCtl*>(reinterpret_cast<float2*>(gdyn) +
+                                                                             G * GB_LANES) + G * K);
+    float* rows = reinterpret_cast<float*>(dys + G * KE * 64);
+    uint32_t* dy_w = dys + w * KE * 64 + lane;
     float* lds_w = rows + w * ROW;
     float4* comp = reinterpret_cast<float4*>(rows);
     float4* look = comp + G * GB_LANES;
@@ -314,7 +331,6 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
     cf ck[NH];
     uint32_t bw[K], gw[K];
     bwd_issue<K, H, false, true>(ck, bw, gw, kc, row0, M, mm, bc, entries, mid, drive, dy);
-    constexpr int KE = K - H;  // tokens of the earlier sub-chunks
     uint32_t ge[KE > 0 ? KE : 1];
     if (KE > 0) {
         const ChunkRows cr(dy + row0, kc, M);
@@ -339,6 +355,9 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
         }
         A = chunk_transition<true>(k.kappa, ph, rec);
     }
+    // the earlier sub-chunks' words wait in LDS for the replay
+#pragma unroll
+    for (int i = 0; i < KE; ++i) dy_w[i * 64] = ge[i];
     comp[w * GB_LANES + lane] = make_float4(A.re, A.im, Bv.re, Bv.im);
     if (NH > 1) *stash = make_float2(ck[0].re, ck[0].im);
     __syncthreads();
@@ -359,10 +378,10 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
     float acc_nu = 0.f, acc_th = 0.f;
     if (valid) {
         // the last sub-chunk's cotangent words are still held from the
-        // summary; bwd_body requests the earlier sub-chunks' as they start
-        bwd_body<K, H, F32, false, true, true, (NH > 1)>(lds_w, sctl, k, active, lane, tile, n_tiles, L, M, b, s,
-                                                         kc, row0, mm, dy, db, tok_part, ck, bw, gw, carry, acc_nu,
-                                                         acc_th, stash);
+        // summary, the earlier sub-chunks' wait in LDS
+        bwd_body<K, H, F32, false, true, true, (NH > 1), RH, (KE > 0)>(
+            lds_w, sctl, k, active, lane, tile, n_tiles, L, M, b, s, kc, row0, mm, dy, db, tok_part, ck, bw, gw,
+            carry, acc_nu, acc_th, stash, dy_w);
         if (active && dz0 && c == 0) dz0[(size_t)b * M + m] = make_float2(carry.re, carry.im);
     }
     // the (d nu, d theta) partials of the group's chunks, added in processing
@@ -819,10 +838,12 @@ hipError_t launch_samu_gbscan(const SamuParams& p, const Chunking& ch, const flo
     const dim3 grid((unsigned)ceil_div(p.M, GB_LANES), ch.NG, ch.B);
     const dim3 block(GB_LANES * ch.G);
     const int H = ch.K == 32 ? SAMU_BWD_SUB : 16;
-    // entry-state stash, token controls, transpose rows (the summary table
-    // and the hand-off scratch overlay the rows, which are larger)
+    // entry-state stash, token controls, the earlier sub-chunks' cotangent
+    // words, transpose rows (the summary table and the hand-off scratch
+    // overlay the rows, which are larger)
     const size_t lds = (size_t)ch.G * GB_LANES * sizeof(float2) + (size_t)ch.G * ch.K * sizeof(TokenCtl) +
-                       (size_t)ch.G * 64 * (2 * H + 1) * sizeof(float);
+                       (size_t)ch.G * (ch.K - H) * 64 * sizeof(uint32_t) +
+                       (size_t)ch.G * 64 * (2 * gb_row_tokens(ch.K, H) + 1) * sizeof(float);
 #define GBSCAN_CASE(KK, HH, FF)                                                                            \
     LRS_LAUNCH(K_SAMU_BWD_SCAN, (samu_gbscan_kernel<KK, HH, FF>), grid, block, lds, s, p.L, p.M, ch.C, ch.G, \
                n_tiles, (const TokenCtl*)ctl, (const uint32_t*)p.b, (const float4*)mtab,                 \
