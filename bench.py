@@ -143,14 +143,12 @@ def samu_kernel_bytes(B, L, D, K, G, unfused=False):
                                   + 8 * BCM + handoff),
             # dy read once (the reverse summary and the replay), b, the entry
             # states, db, the per-tile controller partials and the (d nu,
-            # d theta) partials; the design re-reads the first half of every
-            # chunk's dy (held neither in registers nor in LDS across the
-            # hand-off), reads the mid-chunk states, the records and the
-            # mode table, writes one (d nu, d theta) row per group, and the
-            # hand-off
+            # d theta) partials; the design reads the mid-chunk states, the
+            # records and the mode table, writes one (d nu, d theta) row per
+            # group, and the hand-off
             "samu_backward_scan": (2 * BLD + 2 * BLD + 2 * BLD + 12 * BL + 8 * M + 8 * BCM
                                    + 8 * B * n_tiles * L + 8 * BCM,
-                                   2 * BLD + BLD + 2 * BLD + 2 * BLD + 16 * BL + 64 * M + 16 * BC + 8 * BCM
+                                   2 * BLD + 2 * BLD + 2 * BLD + 16 * BL + 64 * M + 16 * BC + 8 * BCM
                                    + 8 * BMID + 8 * B * n_tiles * L + 8 * NGM + handoff),
             "clear": (0, 16 * NGM),
         })

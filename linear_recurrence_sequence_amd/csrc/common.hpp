@@ -180,6 +180,10 @@ struct ChunkRows {
     __device__ uint32_t load(int i, int m) const {
         return __builtin_amdgcn_raw_buffer_load_b32(rsrc, (i * M + m) * 4, 0, 0);
     }
+    // the same with the non-temporal hint, for words nothing reads again
+    __device__ uint32_t load_nt(int i, int m) const {
+        return __builtin_amdgcn_raw_buffer_load_b32(rsrc, (i * M + m) * 4, 0, 2);
+    }
 };
 
 // Orders LDS traffic among the lanes of one wave (a region no other wave

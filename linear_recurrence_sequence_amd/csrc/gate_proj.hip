@@ -833,6 +833,8 @@ __global__ __launch_bounds__(64 * adj_waves<MT>()) void gate_proj_adj_kernel(
     for (int pl = 0; pl < 4; ++pl)
         rsrc[pl] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src[pl] + tr0 * D * 2), (short)0, rbytes,
                                                      0x00020000);
+    // every word is read once, by the step's last reader of it: cache policy
+    // 2 (non-temporal) keeps the planes out of the memory-side cache
     auto load = [&](Regs& b, int i) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
@@ -840,7 +842,7 @@ __global__ __launch_bounds__(64 * adj_waves<MT>()) void gate_proj_adj_kernel(
             const int row = c / CPR, ch = c - row * CPR;
             const uint32_t off = (uint32_t)(((i * T + row) * D + blk * Db + 8 * ch) * 2);
 #pragma unroll
-            for (int pl = 0; pl < 4; ++pl) b.v[pl][s] = __builtin_amdgcn_raw_buffer_load_b128(rsrc[pl], off, 0, 0);
+            for (int pl = 0; pl < 4; ++pl) b.v[pl][s] = __builtin_amdgcn_raw_buffer_load_b128(rsrc[pl], off, 0, 2);
         }
     };
     // W_x^T and W_a^T of the block, for the dx waves' fragments

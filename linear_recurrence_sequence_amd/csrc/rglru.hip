@@ -729,14 +729,16 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
     const float2 e = entries[((size_t)b * C + c) * W + lw];
     uint32_t xs[K], lxs[K], las[K], gws[K];
     {
+        // the pass's only read of these words, and the step's last: the
+        // non-temporal hint keeps them out of the memory-side cache
         const ChunkRows rx(x + tok0 * W, kc, W), rl(lx + tok0 * W, kc, W), ra(la + tok0 * W, kc, W),
             rg(dy + tok0 * W, kc, W);
 #pragma unroll
         for (int i = 0; i < K; ++i) {
-            xs[i] = rx.load(i, lw);
-            lxs[i] = rl.load(i, lw);
-            las[i] = ra.load(i, lw);
-            gws[i] = rg.load(i, lw);
+            xs[i] = rx.load_nt(i, lw);
+            lxs[i] = rl.load_nt(i, lw);
+            las[i] = ra.load_nt(i, lw);
+            gws[i] = rg.load_nt(i, lw);
         }
     }
     const int kq = opaque(kc);

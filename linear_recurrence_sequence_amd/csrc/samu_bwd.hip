@@ -52,7 +52,8 @@ constexpr int BWD_THREADS = 256;
 // waves per SIMD, which costs more than the latency the early request hides.
 // Past a partial chunk's end (token i >= kc) a load is skipped (CLAMP false:
 // the word reads as zero) or re-reads token kc - 1 (CLAMP true: no branch;
-// the word is never used).
+// the word is never used).  The CLAMP form serves the single-pass backward,
+// which reads each word once, so its loads carry the non-temporal hint.
 template <int K, int H, bool FULL, bool CLAMP, bool GW = true>
 __device__ __forceinline__ void bwd_issue(cf (&ck)[K / H], uint32_t (&bw)[K], uint32_t (&gw)[K], int kc,
                                           size_t row0, int M, int mm, size_t bc,
@@ -73,14 +74,16 @@ __device__ __forceinline__ void bwd_issue(cf (&ck)[K / H], uint32_t (&bw)[K], ui
 #pragma unroll
         for (int j = 0; j < H; ++j) {
             const int i = h * H + j;
-            if (FULL || CLAMP) bw[i] = (drive + row0 + (size_t)(FULL ? i : min(i, kc - 1)) * M)[mm];
+            if (CLAMP) bw[i] = __builtin_nontemporal_load(&(drive + row0 + (size_t)min(i, kc - 1) * M)[mm]);
+            else if (FULL) bw[i] = (drive + row0 + (size_t)i * M)[mm];
             else bw[i] = i < kc ? (drive + row0 + (size_t)i * M)[mm] : 0u;
         }
         if (!GW || h != NH - 1) continue;  // earlier sub-chunks: requested when they start
 #pragma unroll
         for (int j = H - 1; j >= 0; --j) {
             const int i = h * H + j;
-            if (FULL || CLAMP) gw[i] = (dy + row0 + (size_t)(FULL ? i : min(i, kc - 1)) * M)[mm];
+            if (CLAMP) gw[i] = __builtin_nontemporal_load(&(dy + row0 + (size_t)min(i, kc - 1) * M)[mm]);
+            else if (FULL) gw[i] = (dy + row0 + (size_t)i * M)[mm];
             else gw[i] = i < kc ? (dy + row0 + (size_t)i * M)[mm] : 0u;
         }
     }
@@ -318,7 +321,9 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
     // requests: token controls, mode constants, the chunk record, every
     // cotangent word of the chunk (last token first, the order the reverse
     // summary takes them in; past a partial chunk's end they read as 0),
-    // then the replay's states and drive words
+    // then the replay's states and drive words.  The drive and cotangent
+    // words are read once here and by no later kernel of the step, so they
+    // carry the non-temporal hint.
     float4 tn = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lane < kc) tn = reinterpret_cast<const float4*>(ctl)[(size_t)b * L + s + lane];
     const ModeConst k = load_mode(mtab, mm);
@@ -335,7 +340,7 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
     if (KE > 0) {
         const ChunkRows cr(dy + row0, kc, M);
 #pragma unroll
-        for (int j = 0; j < KE; ++j) ge[KE - 1 - j] = cr.load(KE - 1 - j, mm);
+        for (int j = 0; j < KE; ++j) ge[KE - 1 - j] = cr.load_nt(KE - 1 - j, mm);
     }
     if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
     wave_lds_sync();
@@ -458,12 +463,15 @@ __device__ __forceinline__ int clamp_tok(int tok0, int i, int BL) {
 // Tokens are clamped into the tensor, so every load is issued unconditionally
 // (a guarded load becomes a branch, after which waiting for any earlier
 // request turns into waiting for all of them); the consumer skips the rest.
+// This is the step's last read of x_sel, so the loads carry the non-temporal
+// hint.
 __device__ __forceinline__ void ctl_load_batch(uint4 (&xv)[CTL_TOKB], const uint4* __restrict__ x_sel, int tok0,
                                                int BL, int D8, int j8) {
 #pragma unroll
     for (int t = 0; t < CTL_TOKB; ++t) {
         const uint4* row = x_sel + (size_t)clamp_tok(tok0, t, BL) * D8;  // wave-uniform
-        xv[t] = row[j8];
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(&row[j8]));
+        xv[t] = make_uint4(v.x, v.y, v.z, v.w);
     }
 }
 
