@@ -441,13 +441,19 @@ def samu_case(torch, scan, inputs, B, L, D, K, G, seed, z0_std):
                dw_r=torch.empty(D + 1, **f32), da_phi=torch.empty(1, **f32),
                da_r=torch.empty(1, **f32), dnu=torch.empty(M, **f32), dtheta=torch.empty(M, **f32))
 
-    def step():
+    def fwd():
         scan.samu_scan_fwd(d["x_sel"], d["b"], d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"],
                            d["theta"], d["z0"], K=K, G=G, y=y, z_final=zf, saved=saved, workspace=ws_f)
+
+    def bwd():
         scan.samu_scan_bwd(d["x_sel"], d["b"], d["w_phi"], d["w_r"], d["a_phi"], d["a_r"], d["nu"],
                            d["theta"], saved, d["dy"], None, K=K, G=G, out=out, workspace=ws_b)
 
-    return step, dict(d=d, y=y, zf=zf, saved=saved, ws_f=ws_f, ws_b=ws_b, out=out)
+    def step():
+        fwd()
+        bwd()
+
+    return step, dict(d=d, y=y, zf=zf, saved=saved, ws_f=ws_f, ws_b=ws_b, out=out, fwd=fwd, bwd=bwd)
 
 
 def rglru_case(torch, scan, inputs, B, L, D, K, G, seed, h0_std, reset_p=0.0, d=None):
@@ -677,6 +683,24 @@ def main():
     launches_per_step = sum(c for _, c in prof.values()) / args.steps
     for name, (tot, cnt) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
         log(f"    {name:24s} {tot / cnt * 1e3:9.2f} us/launch  x{cnt // args.steps}/step")
+    # the same kernels with the memory-side cache emptied before each pass (a
+    # 1 GiB read ahead of the forward and of the backward): no stream one pass
+    # reads is then still cached from the other pass or from the step before,
+    # as in a network where other layers run between a layer's passes
+    flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+
+    def cold_step():
+        flush.sum()
+        sb["fwd"]()
+        flush.sum()
+        sb["bwd"]()
+
+    _, prof_cold = timed(cold_step, args.steps, 1, True)
+    del flush
+    kern_us = sum(t for t, _ in prof.values()) / args.steps * 1e3
+    kern_us_cold = sum(t for t, _ in prof_cold.values()) / args.steps * 1e3
+    log(f"[bench] SAMU F+B kernels {kern_us:.1f} us/step, {kern_us_cold:.1f} us/step with the cache emptied "
+        f"before each pass")
 
     ms, graph_runs, graph_equal = ms_eager, None, None
     if not args.no_graph:
@@ -887,6 +911,8 @@ def main():
                    "initial_state": "N(0, 0.1^2) with gradient"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "ms_per_step_with_kernel_events": round(ms_ev, 4),
+        "kernel_us_per_step": round(kern_us, 1),
+        "kernel_us_per_step_cold_passes": round(kern_us_cold, 1),
         "launches_per_step": launches_per_step,
         "token_channels_per_s": round(B * L * D / (ms * 1e-3), 1),
         "workspace_bytes": {"saved": scan.samu_scan_saved_bytes(B, L, D, K),
