@@ -186,6 +186,26 @@ struct ChunkRows {
     }
 };
 
+// Stores into one chunk's rows of a [B, L, M] tensor of `eb`-byte elements
+// (4: a packed BF16 pair, 8: an FP32 pair) through a raw buffer descriptor:
+// the token's row offset goes into the scalar offset and the lane's into the
+// vector offset, so a store needs no per-token address arithmetic in vector
+// registers.  The stores carry the output streams' cache policy.
+struct ChunkOut {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int stride;  // bytes per token row
+    __device__ ChunkOut(void* chunk_row0, int kc, int M, int eb)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(chunk_row0, (short)0, kc * M * eb, 0x00020000)),
+          stride(M * eb) {}
+    __device__ void u32(int i, uint32_t voff, uint32_t v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(v, rsrc, voff, i * stride, LRS_STREAM_NT ? 2 : 0);
+    }
+    __device__ void f32x2(int i, uint32_t voff, float a, float b) const {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(a), __float_as_uint(b)}, rsrc, voff,
+                                              i * stride, LRS_STREAM_NT ? 2 : 0);
+    }
+};
+
 // Orders LDS traffic among the lanes of one wave (a region no other wave
 // touches): the wave's LDS instructions execute in program order, so only
 // the compiler has to be kept from moving accesses across this point.

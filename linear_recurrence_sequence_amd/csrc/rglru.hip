@@ -411,15 +411,16 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gscan_kernel(
         h[1] = fmaf(f.z, h[1], f.w);
     }
     if (active) entries[((size_t)b * C + c) * W + lw] = make_float2(h[0], h[1]);
+    const ChunkOut yo(reinterpret_cast<char*>(y) + tok0 * (size_t)W * (F32 ? 8 : 4), K, W, F32 ? 8 : 4);
+    const uint32_t yoff = (uint32_t)lw * (F32 ? 8u : 4u);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         if (i < kq) {
             h[0] = fmaf(av[i][0], h[0], bv[i][0]);
             h[1] = fmaf(av[i][1], h[1], bv[i][1]);
             if (active) {
-                const size_t row = (tok0 + i) * (size_t)W;  // wave-uniform
-                if (F32) out_f32x2(reinterpret_cast<float2*>(y) + row + lw, h[0], h[1]);
-                else out_u32(reinterpret_cast<uint32_t*>(y) + row + lw, pack_bf16x2(h[0], h[1]));
+                if (F32) yo.f32x2(i, yoff, h[0], h[1]);
+                else yo.u32(i, yoff, pack_bf16x2(h[0], h[1]));
             }
         }
     }

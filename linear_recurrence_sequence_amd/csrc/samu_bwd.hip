@@ -104,9 +104,10 @@ __device__ __forceinline__ void bwd_issue(cf (&ck)[K / H], uint32_t (&bw)[K], ui
 // stay in a register through the later sub-chunks.  RH: tokens per partial-
 // sum transpose (the rows hold RH tokens).  DYS: the cotangent words of the
 // earlier sub-chunks come from the lane's LDS slots dy_lds[i * 64] (written
-// by the caller) instead of a second read from memory.
+// by the caller) instead of a second read from memory.  BST: db goes out
+// through a buffer descriptor over the chunk's rows (ChunkOut).
 template <int K, int H, bool F32, bool FULL, bool WSYNC, bool CLAMP = false, bool STASH = false, int RH = H,
-          bool DYS = false>
+          bool DYS = false, bool BST = false>
 __device__ __forceinline__ void bwd_body(float* lds_w, const TokenCtl* sctl, const ModeConst& k, bool active,
                                          int lane, int tile, int n_tiles, int L, int M, int b, int s, int kc,
                                          size_t row0, int mm, const uint32_t* __restrict__ dy, void* __restrict__ db,
@@ -121,6 +122,8 @@ __device__ __forceinline__ void bwd_body(float* lds_w, const TokenCtl* sctl, con
     constexpr int PAD = NV + 1;
     const int kq = opaque(kc);
     float* row = &lds_w[lane * PAD];
+    const ChunkOut dbo(reinterpret_cast<char*>(db) + row0 * (F32 ? 8 : 4), kc, M, F32 ? 8 : 4);
+    const uint32_t dboff = (uint32_t)mm * (F32 ? 8u : 4u);
 #pragma unroll
     for (int h = NH - 1; h >= 0; --h) {
         const int i0 = h * H;
@@ -159,8 +162,14 @@ __device__ __forceinline__ void bwd_body(float* lds_w, const TokenCtl* sctl, con
                 const float E = sctl[i0 + j].E;
                 const cf gg = {bf16_lo(gw[i0 + j]) + carry.re, bf16_hi(gw[i0 + j]) + carry.im};
                 if (active) {
-                    if (F32) out_f32x2(reinterpret_cast<float2*>(db) + rowj + mm, gg.re, gg.im);
-                    else out_u32(reinterpret_cast<uint32_t*>(db) + rowj + mm, pack_bf16x2(gg.re, gg.im));
+                    if (BST) {
+                        if (F32) dbo.f32x2(i0 + j, dboff, gg.re, gg.im);
+                        else dbo.u32(i0 + j, dboff, pack_bf16x2(gg.re, gg.im));
+                    } else if (F32) {
+                        out_f32x2(reinterpret_cast<float2*>(db) + rowj + mm, gg.re, gg.im);
+                    } else {
+                        out_u32(reinterpret_cast<uint32_t*>(db) + rowj + mm, pack_bf16x2(gg.re, gg.im));
+                    }
                 }
                 // gamma = g conj(w)
                 const float gre = fmaf(gg.re, wz[j].re, gg.im * wz[j].im);
@@ -344,6 +353,9 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
     }
     if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
     wave_lds_sync();
+    // the controls through one vector-register base kept for the whole chunk
+    // (an LDS read needs its address in a vector register)
+    const TokenCtl* sv = sctl + opaque_v(0u);
     // the chunk's conjugate reverse summary: carry -> conj(lambda_t) (dy_t + carry)
     cf A = {1.f, 0.f}, Bv = {0.f, 0.f};
     if (valid) {
@@ -352,7 +364,7 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
         for (int j = 0; j < K; ++j) {
             const int i = K - 1 - j;
             if (i < kq) {
-                const TokenCtl t = sctl[i];
+                const TokenCtl t = sv[i];
                 const cf lam = mode_lambda(k, t.E, t.C, t.S);
                 const uint32_t x = i >= KE ? gw[i] : ge[i < KE ? i : 0];
                 Bv = cmulc(lam, {Bv.re + bf16_lo(x), Bv.im + bf16_hi(x)});
@@ -384,8 +396,8 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
     if (valid) {
         // the last sub-chunk's cotangent words are still held from the
         // summary, the earlier sub-chunks' wait in LDS
-        bwd_body<K, H, F32, false, true, true, (NH > 1), RH, (KE > 0)>(
-            lds_w, sctl, k, active, lane, tile, n_tiles, L, M, b, s, kc, row0, mm, dy, db, tok_part, ck, bw, gw,
+        bwd_body<K, H, F32, false, true, true, (NH > 1), RH, (KE > 0), !F32>(
+            lds_w, sv, k, active, lane, tile, n_tiles, L, M, b, s, kc, row0, mm, dy, db, tok_part, ck, bw, gw,
             carry, acc_nu, acc_th, stash, dy_w);
         if (active && dz0 && c == 0) dz0[(size_t)b * M + m] = make_float2(carry.re, carry.im);
     }

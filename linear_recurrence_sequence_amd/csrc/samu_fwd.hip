@@ -524,11 +524,14 @@ __device__ __forceinline__ void gscan_body(float4* gdyn, int G, int L, int M, in
     if (lane < kc) reinterpret_cast<float4*>(sctl)[lane] = tn;
     wave_lds_sync();
     const int kq = opaque(kc);
+    // the controls through one vector-register base kept for the whole
+    // chunk (an LDS read needs its address in a vector register)
+    const TokenCtl* sv = sctl + opaque_v(0u);
     cf A = {1.f, 0.f}, Bv[1] = {{0.f, 0.f}};
     if (valid) {
 #pragma unroll
         for (int i = 0; i < K; ++i)
-            if (i < kq) summary_step<1, false>(k, Bv, sctl[i], wd[i]);
+            if (i < kq) summary_step<1, false>(k, Bv, sv[i], wd[i]);
         A = chunk_transition<false>(k[0].kappa, ph, rec);
     }
     group_put(comp, w, lane, A, Bv[0]);
@@ -549,15 +552,19 @@ __device__ __forceinline__ void gscan_body(float4* gdyn, int G, int L, int M, in
         z = cfma({f.x, f.y}, z, {f.z, f.w});
     }
     if (active) entries[((size_t)b * C + c) * M + m] = make_float2(z.re, z.im);
+    const ChunkOut yo(reinterpret_cast<char*>(y) + row0 * (F32 ? 8 : 4), kc, M, F32 ? 8 : 4);
+    const uint32_t yoff = (uint32_t)mc * (F32 ? 8u : 4u);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         if (i < kq) {
-            const TokenCtl t = sctl[i];
+            const TokenCtl t = sv[i];
             // the word again, not the summary's unpacked pair kept live since
             const uint32_t xw = opaque_v(wd[i].w[0]);
             z = cfma(mode_lambda(k2, t.E, t.C, t.S), z, {bf16_lo(xw), bf16_hi(xw)});
-            const cf zz[1] = {z};
-            if (active) store_states<1, F32>(y, row0 + (size_t)i * M, mc, zz);
+            if (active) {
+                if (F32) yo.f32x2(i, yoff, z.re, z.im);
+                else yo.u32(i, yoff, pack_bf16x2(z.re, z.im));
+            }
             if (NMID > 0 && (i + 1) % SAMU_BWD_SUB == 0 && i + 1 < K && active)
                 reinterpret_cast<float2*>(mid)[(((size_t)b * C + c) * NMID + (i + 1) / SAMU_BWD_SUB - 1) * M + mc] =
                     make_float2(z.re, z.im);
