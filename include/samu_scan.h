@@ -357,6 +357,22 @@ const char* scan_profile_kernel_name(int id);
  * NULL), then forgets the records.  Returns SCAN_OK or SCAN_ERR_DEVICE. */
 scan_status scan_profile_collect(double* total_ms, int* launches);
 
+/* ======================================================================
+ * Hand-off wait limit of the single-pass scans (SAMU forward and backward;
+ * RG-LRU forward and backward at K=16 with groups of at most 16 chunks).
+ * A workgroup of these scans waits for words that earlier workgroups of the
+ * same launch publish; every such wait is bounded by a number of polls.  A
+ * wait that expires yields NaN, which reaches every output downstream of
+ * it, instead of a plausible wrong value.  The default (16384 polls) is far
+ * above what a wait takes while the publishing workgroup runs; the limit
+ * exists so that tests can force the expiry path.
+ * Sets the limit for launches enqueued from now on (polls >= 0; a negative
+ * value restores the default) and returns the previous limit.  Process-wide;
+ * launches already captured into a graph keep the limit they were enqueued
+ * with.
+ * ====================================================================== */
+int scan_set_handoff_poll_limit(int polls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -22,6 +23,10 @@ static scan_status fail(scan_status st, const std::string& msg) {
 }
 
 scan_status set_last_error(scan_status st, const char* msg) { return fail(st, msg); }
+
+// ------------------------------------------------- hand-off wait limit ---
+std::atomic<int> g_handoff_polls{HANDOFF_POLLS_DEFAULT};
+int handoff_poll_limit() { return g_handoff_polls.load(std::memory_order_relaxed); }
 
 // ----------------------------------------------------------- profiler ---
 namespace {
@@ -828,6 +833,11 @@ scan_status rglru_scan_bwd(int B, int L, int D, int K, int G, const void* x, con
 }
 
 // ------------------------------------------------------------ profiler ---
+int scan_set_handoff_poll_limit(int polls) {
+    const int v = polls < 0 ? lrs::HANDOFF_POLLS_DEFAULT : polls;
+    return lrs::g_handoff_polls.exchange(v);
+}
+
 void scan_profile_enable(int on) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof_on = on != 0;

@@ -251,7 +251,6 @@ struct ChunkCtl { float G, cD, sD, pad; };
 // group's map U (a group inside a segment) or the state leaving the group
 // (a segment's last group).  The transition part A of U is not published:
 // a reader forms it from the chunk records exactly as the group itself does.
-constexpr int SCAN_SPIN_MAX = 1 << 14;
 constexpr int SCAN_PUB_WORDS = 2;
 
 // Word `i` of a group for one lane: `grp` is the group's (wave-uniform) first
@@ -273,10 +272,10 @@ __device__ __forceinline__ float pub_val(uint64_t w) { return __uint_as_float((u
 
 // The two words of an earlier group for this lane's mode, once both are
 // published.
-__device__ __forceinline__ float2 wait_pair(const uint64_t* grp, uint32_t Mb, uint32_t off) {
-    float2 v = make_float2(0.f, 0.f);
+__device__ __forceinline__ float2 wait_pair(const uint64_t* grp, uint32_t Mb, uint32_t off, int polls) {
+    float2 v = make_float2(__builtin_nanf(""), __builtin_nanf(""));  // kept if the wait expires
     bool ok = false;
-    for (int it = 0; it < SCAN_SPIN_MAX; ++it) {
+    for (int it = 0; it < polls; ++it) {
         if (!ok) {
             // the lane offset afresh each poll: addresses kept across the
             // loop would cost two registers each
@@ -341,11 +340,12 @@ __device__ __forceinline__ cf group_transition(const GroupChunks& gc, int G, int
 // then groups), and a workgroup only waits for words of lower-numbered
 // groups of its own row and mode tile, which were dispatched before it and
 // never wait for it, so every wait ends.  Each wait is nevertheless bounded
-// (SCAN_SPIN_MAX polls).
+// (`polls` polls); a wait that expires yields NaN, which then reaches every
+// output downstream of it.
 template <bool REV>
 __device__ __forceinline__ float4 group_handoff(const float4* comp, float4* look, int G, int w, int lane, int q,
                                                 int NG, int M, int mc, bool active, const float2* seed,
-                                                uint64_t* pub, const GroupChunks& gc) {
+                                                uint64_t* pub, const GroupChunks& gc, int polls) {
     constexpr int GL = 64;
     const uint32_t Mb = (uint32_t)M * 8u, moff = (uint32_t)mc * 8u;
     uint64_t* mine = pub + (size_t)q * SCAN_PUB_WORDS * M;  // wave-uniform
@@ -367,11 +367,11 @@ __device__ __forceinline__ float4 group_handoff(const float4* comp, float4* look
     if (w < nprev) {
         const int j = q - 1 - w;
         const cf ua = group_transition<REV>(gc, G, j);
-        const float2 ub = wait_pair(pub + (size_t)j * SCAN_PUB_WORDS * M, Mb, moff);
+        const float2 ub = wait_pair(pub + (size_t)j * SCAN_PUB_WORDS * M, Mb, moff, polls);
         look[w * GL + lane] = make_float4(ua.re, ua.im, ub.x, ub.y);
     } else if (w == nprev) {
         float2 zs = make_float2(0.f, 0.f);
-        if (q - nprev > 0) zs = wait_pair(pub + (size_t)(q - nprev - 1) * SCAN_PUB_WORDS * M, Mb, moff);
+        if (q - nprev > 0) zs = wait_pair(pub + (size_t)(q - nprev - 1) * SCAN_PUB_WORDS * M, Mb, moff, polls);
         else if (seed) zs = seed[mc];
         look[w * GL + lane] = make_float4(zs.x, zs.y, 0.f, 0.f);
     }

@@ -141,6 +141,13 @@ hipError_t launch_samu_replay(const SamuParams& p, const Chunking& ch, const flo
 //             the backward reads); its words are cleared by the controller
 //             launch before it (the controller's `clear` argument);
 constexpr int SAMU_GROUP_MAX = 16;
+// Polls a single-pass scan's wait for another workgroup's hand-off words
+// makes before it gives up (the words then read as NaN, so an expired wait
+// shows in the outputs instead of passing as a wrong value).  The default
+// is far above what a wait takes when the producer runs; the setter exists
+// so that tests can force the expiry path.
+constexpr int HANDOFF_POLLS_DEFAULT = 1 << 14;
+int handoff_poll_limit();
 size_t samu_gscan_pub_bytes(const Chunking& ch, int M);
 hipError_t launch_samu_gscan(const SamuParams& p, const Chunking& ch, const float* ctl, const float* mtab,
                              const float* chunk_rec, void* pub, float* entries, float* mid, void* y, int y_f32,

@@ -260,10 +260,11 @@ __device__ __forceinline__ bool map_ok(uint64_t w) { return ((uint32_t)w >> 31) 
 // (MAP: maps, else states; bounded wait, as wait_pair).  v = (A0, B0, A1, B1)
 // for maps, (h0, h1, 0, 0) for states.
 template <bool MAP>
-__device__ __forceinline__ float4 wait_group(const uint64_t* grp, uint32_t Wb, uint32_t off) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+__device__ __forceinline__ float4 wait_group(const uint64_t* grp, uint32_t Wb, uint32_t off, int polls) {
+    const float nan = __builtin_nanf("");
+    float4 v = make_float4(nan, nan, nan, nan);  // kept if the wait expires
     bool ok = false;
-    for (int it = 0; it < SCAN_SPIN_MAX; ++it) {
+    for (int it = 0; it < polls; ++it) {
         if (!ok) {
             const uint32_t o = opaque_v(off);
             const uint64_t w0 = pub_load(grp, 0, Wb, o), w1 = pub_load(grp, 1, Wb, o);
@@ -289,7 +290,7 @@ __device__ __forceinline__ float4 wait_group(const uint64_t* grp, uint32_t Wb, u
 // into the row, so that a lane past the row reads a published word).
 __device__ __forceinline__ float2 rg_group_handoff(const float4* comp, float4* look, int G, int w, int lane, int q,
                                                    int NG, int W, int lw, bool active, const float2* seed,
-                                                   uint64_t* pub) {
+                                                   uint64_t* pub, int polls) {
     const uint32_t Wb = (uint32_t)W * 8u, off = (uint32_t)lw * 8u;
     uint64_t* mine = pub + (size_t)q * RG_PUB_WORDS * W;  // wave-uniform
     const int nprev = q % G;
@@ -308,11 +309,11 @@ __device__ __forceinline__ float2 rg_group_handoff(const float4* comp, float4* l
         pub_store_map(mine, 1, Wb, off, a1, b1);
     }
     if (w < nprev) {
-        look[w * RG_GL + lane] = wait_group<true>(pub + (size_t)(q - 1 - w) * RG_PUB_WORDS * W, Wb, off);
+        look[w * RG_GL + lane] = wait_group<true>(pub + (size_t)(q - 1 - w) * RG_PUB_WORDS * W, Wb, off, polls);
     } else if (w == nprev) {
         float4 hs = make_float4(0.f, 0.f, 0.f, 0.f);
         if (q - nprev > 0) {
-            hs = wait_group<false>(pub + (size_t)(q - nprev - 1) * RG_PUB_WORDS * W, Wb, off);
+            hs = wait_group<false>(pub + (size_t)(q - nprev - 1) * RG_PUB_WORDS * W, Wb, off, polls);
         } else if (seed) {
             const float2 h = seed[lw];
             hs = make_float4(h.x, h.y, 0.f, 0.f);
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gscan_kernel(
     int L, int W, int C, int G, const uint32_t* __restrict__ x, const uint32_t* __restrict__ lx,
     const uint32_t* __restrict__ la, const unsigned char* __restrict__ reset, const float* __restrict__ alpha,
     const float2* __restrict__ h0, uint64_t* __restrict__ pub, float2* __restrict__ entries, void* __restrict__ y,
-    float2* __restrict__ h_final) {
+    float2* __restrict__ h_final, int polls) {
     extern __shared__ float4 rg_lds[];  // comp [G][64], look [G][64]
     float4* const comp = rg_lds;
     float4* const look = rg_lds + G * RG_GL;
@@ -402,7 +403,8 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gscan_kernel(
     comp[w * RG_GL + lane] = make_float4(A[0], Bs[0], A[1], Bs[1]);
     __syncthreads();
     const float2 hin = rg_group_handoff(comp, look, G, w, lane, q, NG, W, lw, active,
-                                        h0 ? h0 + (size_t)b * W : nullptr, pub + (size_t)b * NG * RG_PUB_WORDS * W);
+                                        h0 ? h0 + (size_t)b * W : nullptr, pub + (size_t)b * NG * RG_PUB_WORDS * W,
+                                        polls);
     if (!valid) return;  // no barrier follows
     float h[2] = {hin.x, hin.y};
     for (int j = 0; j < w; ++j) {
@@ -710,7 +712,7 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
     const uint32_t* __restrict__ la, const unsigned char* __restrict__ reset, const float* __restrict__ alpha,
     const float2* __restrict__ entries, const float2* __restrict__ dh_final, uint64_t* __restrict__ pub,
     const uint32_t* __restrict__ dy, void* __restrict__ dx, void* __restrict__ dlx, void* __restrict__ dla,
-    float2* __restrict__ dh0, float2* __restrict__ alpha_part) {
+    float2* __restrict__ dh0, float2* __restrict__ alpha_part, int polls) {
     extern __shared__ float4 rg_lds[];  // comp [G][64], look [G][64], hist [G][K][64] float2
     float4* const comp = rg_lds;
     float4* const look = rg_lds + G * RG_GL;
@@ -752,7 +754,7 @@ __global__ __launch_bounds__(RG_GL * RG_GROUP_MAX) void rglru_gbscan_kernel(
     __syncthreads();
     const float2 cin = rg_group_handoff(comp, look, G, w, lane, q, NG, W, lw, active,
                                         dh_final ? dh_final + (size_t)b * W : nullptr,
-                                        pub + (size_t)b * NG * RG_PUB_WORDS * W);
+                                        pub + (size_t)b * NG * RG_PUB_WORDS * W, polls);
     float carry[2] = {cin.x, cin.y};
     for (int j = 0; j < w; ++j) {
         const float4 f = comp[j * RG_GL + lane];
@@ -915,7 +917,7 @@ hipError_t launch_rglru_gscan(const RglruParams& p, const Chunking& ch, void* pu
 #define RG_GSCAN(FF)                                                                                           \
     LRS_LAUNCH(K_RGLRU_FWD_SCAN, (rglru_gscan_kernel<16, FF>), grid, block, lds, s, p.L, W, ch.C, ch.G,          \
                (const uint32_t*)p.x, (const uint32_t*)p.lx, (const uint32_t*)p.la, p.reset, p.alpha,            \
-               (const float2*)p.h0, (uint64_t*)pub, (float2*)entries, y, (float2*)h_final)
+               (const float2*)p.h0, (uint64_t*)pub, (float2*)entries, y, (float2*)h_final, handoff_poll_limit())
     if (y_f32) RG_GSCAN(true);
     else RG_GSCAN(false);
 #undef RG_GSCAN
@@ -938,7 +940,7 @@ hipError_t launch_rglru_gbscan(const RglruParams& p, const Chunking& ch, const f
     LRS_LAUNCH(K_RGLRU_BWD_SCAN, (rglru_gbscan_kernel<16, FF>), grid, block, lds, s, p.L, W, ch.C, ch.G,         \
                (const uint32_t*)p.x, (const uint32_t*)p.lx, (const uint32_t*)p.la, p.reset, p.alpha,            \
                (const float2*)entries, (const float2*)dh_final, (uint64_t*)pub, (const uint32_t*)dy, dx, dlx,   \
-               dla, (float2*)dh0, (float2*)alpha_part)
+               dla, (float2*)dh0, (float2*)alpha_part, handoff_poll_limit())
     if (g_f32) RG_GBSCAN(true);
     else RG_GBSCAN(false);
 #undef RG_GBSCAN

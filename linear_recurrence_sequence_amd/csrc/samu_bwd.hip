@@ -294,7 +294,7 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
                                             const float2* __restrict__ dz_final, uint64_t* __restrict__ pub,
                                             const uint32_t* __restrict__ dy, void* __restrict__ db,
                                             float2* __restrict__ dz0, float* __restrict__ tok_part,
-                                            float2* __restrict__ mode_part) {
+                                            float2* __restrict__ mode_part, int polls) {
     constexpr int NH = K / H;
     constexpr int KE = K - H;  // tokens of the earlier sub-chunks
     constexpr int RH = gb_row_tokens(K, H);
@@ -383,7 +383,7 @@ __device__ __forceinline__ void gbscan_body(float4* gdyn, int G, int L, int M, i
     const GroupChunks gc{chunk_rec + (size_t)b * C, mtab[MODE_REC * mm + 2], mtab[MODE_REC * mm + 3], k.kappa, C};
     const float4 gin = group_handoff<true>(comp, look, G, w, lane, q, NG, M, mm, active,
                                            dz_final ? dz_final + (size_t)b * M : nullptr,
-                                           pub + (size_t)b * NG * SCAN_PUB_WORDS * M, gc);
+                                           pub + (size_t)b * NG * SCAN_PUB_WORDS * M, gc, polls);
     cf carry = {gin.x, gin.y};
     if (valid) {
         for (int j = 0; j < w; ++j) {
@@ -425,15 +425,16 @@ samu_gbscan_kernel(int L, int M, int C, int G, int n_tiles, const TokenCtl* __re
                    const float2* __restrict__ entries, const float2* __restrict__ mid,
                    const float4* __restrict__ chunk_rec, const float2* __restrict__ dz_final,
                    uint64_t* __restrict__ pub, const uint32_t* __restrict__ dy, void* __restrict__ db,
-                   float2* __restrict__ dz0, float* __restrict__ tok_part, float2* __restrict__ mode_part) {
+                   float2* __restrict__ dz0, float* __restrict__ tok_part, float2* __restrict__ mode_part,
+                   int polls) {
     static_assert(K % H == 0 && 64 % (2 * H) == 0, "sub-chunk shape");
     extern __shared__ float4 gdyn[];
     if ((int)(blockIdx.x + 1) * GB_LANES <= M)  // uniform over the workgroup
         gbscan_body<K, H, F32, true>(gdyn, G, L, M, C, n_tiles, ctl, drive, mtab, entries, mid, chunk_rec, dz_final,
-                                     pub, dy, db, dz0, tok_part, mode_part);
+                                     pub, dy, db, dz0, tok_part, mode_part, polls);
     else
         gbscan_body<K, H, F32, false>(gdyn, G, L, M, C, n_tiles, ctl, drive, mtab, entries, mid, chunk_rec,
-                                      dz_final, pub, dy, db, dz0, tok_part, mode_part);
+                                      dz_final, pub, dy, db, dz0, tok_part, mode_part, polls);
 }
 
 // Zeroes n 16-byte words (the single-pass backward's hand-off area, before
@@ -869,7 +870,7 @@ hipError_t launch_samu_gbscan(const SamuParams& p, const Chunking& ch, const flo
                n_tiles, (const TokenCtl*)ctl, (const uint32_t*)p.b, (const float4*)mtab,                 \
                (const float2*)entries, (const float2*)mid, (const float4*)chunk_rec,                     \
                (const float2*)dz_final, (uint64_t*)pub, (const uint32_t*)dy, db, (float2*)dz0, tok_part, \
-               (float2*)mode_part)
+               (float2*)mode_part, handoff_poll_limit())
     constexpr int H32 = SAMU_BWD_SUB, H16 = SAMU_BWD_SUB < 16 ? SAMU_BWD_SUB : 16;
     if (ch.K == 32) {
         if (db_f32) GBSCAN_CASE(32, H32, true); else GBSCAN_CASE(32, H32, false);

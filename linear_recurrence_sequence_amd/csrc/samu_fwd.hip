@@ -493,7 +493,7 @@ __device__ __forceinline__ void gscan_body(float4* gdyn, int G, int L, int M, in
                                            const float4* __restrict__ mtab, const float4* __restrict__ chunk_rec,
                                            const float2* __restrict__ z0, uint64_t* __restrict__ pub,
                                            float2* __restrict__ entries, float* __restrict__ mid,
-                                           void* __restrict__ y, float* __restrict__ z_final) {
+                                           void* __restrict__ y, float* __restrict__ z_final, int polls) {
     constexpr int NMID = samu_mid_states(K);
     float4* comp = gdyn;                   // [G][64] (A_c, B_c) of the group's chunks
     float4* look = gdyn + G * GRP_LANES;   // [G][64] what each wave read of the earlier groups
@@ -540,7 +540,7 @@ __device__ __forceinline__ void gscan_body(float4* gdyn, int G, int L, int M, in
     const GroupChunks gc{chunk_rec + (size_t)b * C, mtab[MODE_REC * mc + 2], mtab[MODE_REC * mc + 3], k[0].kappa, C};
     const float4 gin = group_handoff<false>(comp, look, G, w, lane, q, NG, M, mc, active,
                                             z0 ? z0 + (size_t)b * M : nullptr,
-                                            pub + (size_t)b * NG * SCAN_PUB_WORDS * M, gc);
+                                            pub + (size_t)b * NG * SCAN_PUB_WORDS * M, gc, polls);
     if (!valid) return;
     // the mode constants again (a fresh load, not registers held across the
     // hand-off)
@@ -579,12 +579,14 @@ __global__ __launch_bounds__(GRP_LANES * SAMU_GROUP_MAX) __attribute__((amdgpu_w
 samu_gscan_kernel(int L, int M, int C, int G, const TokenCtl* __restrict__ ctl, const uint32_t* __restrict__ drive,
                   const float4* __restrict__ mtab, const float4* __restrict__ chunk_rec,
                   const float2* __restrict__ z0, uint64_t* __restrict__ pub, float2* __restrict__ entries,
-                  float* __restrict__ mid, void* __restrict__ y, float* __restrict__ z_final) {
+                  float* __restrict__ mid, void* __restrict__ y, float* __restrict__ z_final, int polls) {
     extern __shared__ float4 gdyn[];
     if ((int)(blockIdx.x + 1) * GRP_LANES <= M)  // uniform over the workgroup
-        gscan_body<K, F32, true>(gdyn, G, L, M, C, ctl, drive, mtab, chunk_rec, z0, pub, entries, mid, y, z_final);
+        gscan_body<K, F32, true>(gdyn, G, L, M, C, ctl, drive, mtab, chunk_rec, z0, pub, entries, mid, y, z_final,
+                                 polls);
     else
-        gscan_body<K, F32, false>(gdyn, G, L, M, C, ctl, drive, mtab, chunk_rec, z0, pub, entries, mid, y, z_final);
+        gscan_body<K, F32, false>(gdyn, G, L, M, C, ctl, drive, mtab, chunk_rec, z0, pub, entries, mid, y, z_final,
+                                  polls);
 }
 
 inline int mode_block(int M, int VM) {
@@ -664,7 +666,7 @@ hipError_t launch_samu_gscan(const SamuParams& p, const Chunking& ch, const floa
 #define GSCAN_CASE(KK, FF)                                                                                     \
     LRS_LAUNCH(K_SAMU_FWD_SCAN, (samu_gscan_kernel<KK, FF>), grid, block, lds, s, p.L, p.M, ch.C, ch.G,       \
                (const TokenCtl*)ctl, (const uint32_t*)p.b, (const float4*)mtab, (const float4*)chunk_rec,      \
-               (const float2*)p.z0, (uint64_t*)pub, (float2*)entries, mid, y, z_final)
+               (const float2*)p.z0, (uint64_t*)pub, (float2*)entries, mid, y, z_final, handoff_poll_limit())
     if (ch.K == 32) {
         if (y_f32) GSCAN_CASE(32, true); else GSCAN_CASE(32, false);
     } else {

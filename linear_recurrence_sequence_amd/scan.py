@@ -78,6 +78,8 @@ def lib():
     L.rglru_scan_bwd.restype = i
     L.scan_profile_enable.argtypes = [i]
     L.scan_profile_enable.restype = None
+    L.scan_set_handoff_poll_limit.argtypes = [i]
+    L.scan_set_handoff_poll_limit.restype = i
     L.scan_profile_kernel_count.restype = i
     L.scan_profile_kernel_name.argtypes = [i]
     L.scan_profile_kernel_name.restype = ctypes.c_char_p
@@ -513,6 +515,13 @@ def rglru_scan_bwd(x, lx, la, alpha, reset, saved, dy, dh_final=None, *, K=16, G
 
 
 # --------------------------------------------------------------- profiler ---
+def scan_set_handoff_poll_limit(polls):
+    """Polls a single-pass scan's hand-off wait makes before it gives up
+    (its words then read as NaN); negative restores the default.  Returns
+    the previous limit."""
+    return int(lib().scan_set_handoff_poll_limit(int(polls)))
+
+
 def scan_profile_enable(on=True):
     lib().scan_profile_enable(int(bool(on)))
 

@@ -55,6 +55,18 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, n), f"{n} declared in samu_scan.h but not exported"
 
 
+def test_handoff_poll_limit_round_trip():
+    # host state only: the limit the next single-pass launches take
+    from linear_recurrence_sequence_amd import scan
+    prev = scan.scan_set_handoff_poll_limit(7)
+    try:
+        assert scan.scan_set_handoff_poll_limit(0) == 7
+        assert scan.scan_set_handoff_poll_limit(-5) == 0
+        assert scan.scan_set_handoff_poll_limit(-1) == 16384
+    finally:
+        scan.scan_set_handoff_poll_limit(prev)
+
+
 def test_prefix_scratch_matches_pages_table():
     from linear_recurrence_sequence_amd import scan
     gold = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_tables.json")))
