@@ -8,6 +8,8 @@
   the results must equal those of ordinary allocations bit for bit.
 * Determinism under load: the same forward+backward while another stream
   keeps the device busy gives bitwise the same results as on a quiet device.
+* Concurrency: single-pass scans of independent calls on several streams at
+  once give bitwise the results of the same calls run one at a time.
 """
 import numpy as np
 import pytest
@@ -150,3 +152,35 @@ def test_deterministic_with_another_stream_busy():
         torch.cuda.synchronize()
         _equal(busy_s, quiet_s)
         _equal(busy_r, quiet_r)
+
+
+def test_single_pass_scans_concurrent_on_three_streams():
+    """Two SAMU and one RG-LRU forward+backward, each with its own outputs
+    and workspaces, enqueued on three streams at once, so the workgroups of
+    their single-pass launches share the device: bitwise equal to the same
+    calls run one at a time.  A workgroup of these launches waits only for
+    earlier workgroups of its own launch, which were dispatched before it,
+    so sharing the device delays the waits but cannot stall them."""
+    B, L, D = 2, 16384, 1024
+    s1 = {k: dev_tensor(v) for k, v in inputs.samu_inputs(B, L, D, 6400, z0_std=0.1, dz_final_std=0.1).items()}
+    s2 = {k: dev_tensor(v) for k, v in inputs.samu_inputs(B, L, D, 6401, z0_std=0.1).items()}
+    rr = {k: dev_tensor(v) for k, v in inputs.rglru_inputs(B, L, D, 6402, reset_p=1.0 / 512, h0_std=0.1,
+                                                          dh_final_std=0.1).items()}
+    say(f"[hygiene] concurrent streams B={B} L={L} D={D}: one at a time")
+    ref1 = _samu_run(s1, B, L, D, 32, 0, torch.bfloat16)
+    ref2 = _samu_run(s2, B, L, D, 32, 0, torch.bfloat16)
+    refr = _rglru_run(rr, B, L, D, 16, 0, torch.bfloat16)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for rep in range(3):
+        say(f"[hygiene] concurrent streams: round {rep}")
+        with torch.cuda.stream(streams[0]):
+            got1 = _samu_run(s1, B, L, D, 32, 0, torch.bfloat16)
+        with torch.cuda.stream(streams[1]):
+            got2 = _samu_run(s2, B, L, D, 32, 0, torch.bfloat16)
+        with torch.cuda.stream(streams[2]):
+            gotr = _rglru_run(rr, B, L, D, 16, 0, torch.bfloat16)
+        torch.cuda.synchronize()
+        _equal(got1, ref1)
+        _equal(got2, ref2)
+        _equal(gotr, refr)
