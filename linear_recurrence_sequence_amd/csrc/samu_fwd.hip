@@ -53,7 +53,6 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     float* __restrict__ p_out, float* __restrict__ r_out, float2* __restrict__ u_out,
     TokenCtl* __restrict__ ctl, float4* __restrict__ mtab, float* __restrict__ inv_norm,
     float4* __restrict__ crec, uint4* __restrict__ clear, size_t n_clear) {
-    __shared__ float red[2][CTL_WAVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     const int D8 = D >> 3;  // 16-byte words per row
@@ -66,6 +65,9 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     float ap[CTL_TOK], ar[CTL_TOK];
 #pragma unroll
     for (int q = 0; q < CTL_TOK; ++q) { ap[q] = 0.f; ar[q] = 0.f; }
+    // squared direction norms from the weights the dot products load anyway
+    // (every wave covers all D columns, so each wave forms the whole norm)
+    float sp = 0.f, sr = 0.f;
     // CTL_SLAB column slabs of 512 selector columns per iteration, all their
     // loads issued before the arithmetic
     for (int j0 = lane; j0 < D8; j0 += 64 * CTL_SLAB) {
@@ -88,6 +90,11 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
             const float4 wr1 = reinterpret_cast<const float4*>(w_r)[2 * j + 1];
             const float wp[8] = {wp0.x, wp0.y, wp0.z, wp0.w, wp1.x, wp1.y, wp1.z, wp1.w};
             const float wr[8] = {wr0.x, wr0.y, wr0.z, wr0.w, wr1.x, wr1.y, wr1.z, wr1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sp = fmaf(wp[e], wp[e], sp);
+                sr = fmaf(wr[e], wr[e], sr);
+            }
 #pragma unroll
             for (int q = 0; q < CTL_TOK; ++q) {
                 const uint32_t xw[4] = {xv[sl][q].x, xv[sl][q].y, xv[sl][q].z, xv[sl][q].w};
@@ -114,19 +121,9 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
     // rather than delaying its first request.
     for (int m = blockIdx.x * CTL_THREADS + tid; m < M; m += gridDim.x * CTL_THREADS)
         store_mode(mtab, m, mode_const(nu[m], theta[m]), chunk_phase(theta[m], K), chunk_phase(theta[m], K_last));
-    // direction norms over all D+1 entries
-    float sp = 0.f, sr = 0.f;
-    for (int j = tid; j <= D; j += CTL_THREADS) {
-        sp = fmaf(w_phi[j], w_phi[j], sp);
-        sr = fmaf(w_r[j], w_r[j], sr);
-    }
-    sp = wave_sum(sp);
-    sr = wave_sum(sr);
-    if (lane == 0) { red[0][wave] = sp; red[1][wave] = sr; }
-    __syncthreads();
-    float np = 0.f, nr = 0.f;
-#pragma unroll
-    for (int i = 0; i < CTL_WAVES; ++i) { np += red[0][i]; nr += red[1][i]; }
+    // direction norms over all D+1 entries: the wave's sum over columns
+    // 0..D-1, then the bias entry
+    const float np = fmaf(w_phi[D], w_phi[D], wave_sum(sp)), nr = fmaf(w_r[D], w_r[D], wave_sum(sr));
     const float inv_phi = 1.0f / sqrtf(np), inv_r = 1.0f / sqrtf(nr);
     if (inv_norm && blockIdx.x == 0) {
         // for the backward: 1/||w|| as used here (controller backward), and
