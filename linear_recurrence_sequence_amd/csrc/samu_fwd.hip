@@ -116,9 +116,9 @@ __global__ __launch_bounds__(CTL_THREADS) void samu_controller_kernel(
         if (lane == q) { up = sp_q; ur = sr_q; }
     }
 
-    // The dot products above use the raw directions, so the norms (small,
-    // cache-resident reads) come after the selector stream has been consumed
-    // rather than delaying its first request.
+    // The dot products above use the raw directions; the mode table comes
+    // after the selector stream has been consumed rather than delaying its
+    // first request.
     for (int m = blockIdx.x * CTL_THREADS + tid; m < M; m += gridDim.x * CTL_THREADS)
         store_mode(mtab, m, mode_const(nu[m], theta[m]), chunk_phase(theta[m], K), chunk_phase(theta[m], K_last));
     // direction norms over all D+1 entries: the wave's sum over columns
