@@ -203,6 +203,9 @@ FULL_CASES = [
     ("wide_b1_l32768_d1024", 1, 32768, 1024, 32, 0, 0.1, 3000),
     ("wide_b1_l32768_d1536", 1, 32768, 1536, 32, 0, 0.1, 3001),
     ("wide_b1_l32768_d2560", 1, 32768, 2560, 32, 0, 0.1, 3003),
+    # several batch rows, each with its own chain of 32 groups, at the
+    # packed-sequence workload's shape
+    ("rows_b4_l8192_d2560", 4, 8192, 2560, 32, 0, 0.1, 3004),
 ]
 
 
