@@ -75,7 +75,8 @@ const char* scan_last_error(void);
 
 /* ======================================================================
  * SAMU mixer scan (page "SAMU 与 RG-LRU 的 H800 训练性能对比", section 05).
- * D real state channels = M = D/2 complex modes; D must be a multiple of 8.
+ * D real state channels = M = D/2 complex modes; D must be a multiple of 8,
+ * at most 1048576 (every call taking D rejects a wider state).
  *
  * Forward, per batch row and token t = 1..L:
  *   x~_t = [x_sel_t; 1], w^ = w / ||w||_2 (norm over all D+1 entries),
@@ -222,7 +223,7 @@ scan_status samu_scan_decode_prepare(int D, const float* w_phi, const float* w_r
 /* ======================================================================
  * RG-LRU scan (page "SAMU 与 RG-LRU 的 H800 训练性能对比", section 04; reset
  * semantics also page "Griffin 第 4、5 节 H800 对照协议", "RG-LRU 的固定方程").
- * D real channels, D even.
+ * D real channels, D even, at most 1048576.
  *   g^x = sigmoid(l^x), g^a = sigmoid(l^a), a_t = exp(-8 g^a softplus(alpha)),
  *   b_t = x_t g^x sqrt(max(1 - a_t^2, 0)),  h_t = a_t h_{t-1} + b_t,  y_t = h_t;
  *   at a segment start (reset[b, t] != 0): a_t = 0 and the multiplier is 1.

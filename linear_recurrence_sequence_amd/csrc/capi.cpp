@@ -300,13 +300,18 @@ static scan_status device_status(hipError_t e, const char* where) {
         if (_st != SCAN_OK) return _st;                         \
     } while (0)
 
+// Widest state accepted: keeps every chunk's rows (at most 32 tokens of
+// 8-byte elements) far inside the 32-bit byte ranges of the kernels' buffer
+// descriptors and offsets.
+static constexpr int kMaxD = 1 << 20;
+
 static bool samu_shape(int B, int L, int D, int K, int G, Chunking* ch) {
-    if (D < 8 || D % 8 != 0) return false;
+    if (D < 8 || D % 8 != 0 || D > kMaxD) return false;
     return chunking(B, L, K, G, kSamuMinGroup, ch, kSamuGroup);
 }
 
 static bool rglru_shape(int B, int L, int D, int K, int G, Chunking* ch) {
-    if (D < 2 || D % 2 != 0) return false;
+    if (D < 2 || D % 2 != 0 || D > kMaxD) return false;
     return chunking(B, L, K, G, kRglruMinGroup, ch, K == 16 ? kRglruGroup : 0);
 }
 
@@ -357,8 +362,8 @@ scan_status samu_scan_fwd(int B, int L, int D, int K, int G, const void* x_sel, 
     Chunking ch;
     if (!samu_shape(B, L, D, K, G, &ch))
         return fail(SCAN_ERR_SHAPE, "samu_scan_fwd: unsupported shape " + shape_text(B, L, D, K, G) +
-                                        " (need B, L >= 1, D >= 8 a multiple of 8, K in {16, 32}, G >= 0,"
-                                        " ceil(L/K) <= 65535)");
+                                        " (need B, L >= 1, 8 <= D <= 1048576 a multiple of 8, K in {16, 32},"
+                                        " G >= 0, ceil(L/K) <= 65535)");
     if (y_dtype != SCAN_BF16 && y_dtype != SCAN_F32)
         return fail(SCAN_ERR_SHAPE, "samu_scan_fwd: y_dtype must be SCAN_BF16 or SCAN_F32");
     scan_status st = check_ptrs({{x_sel, 0, "x_sel"}, {b, 0, "b"}, {w_phi, 0, "w_phi"}, {w_r, 0, "w_r"},
@@ -498,6 +503,7 @@ static SamuBaseWs samu_base_layout(void* base, int B, int L, int M, int variant,
 static bool base_shape(int variant, int B, int L, int D, bool samu) {
     if (variant != SCAN_BASELINE_SEQUENTIAL && variant != SCAN_BASELINE_ASSOCIATIVE) return false;
     if (B < 1 || B > 65535 || L < 1 || (int64_t)B * L > 0x7fffffff) return false;
+    if (D > kMaxD) return false;
     return samu ? (D >= 8 && D % 8 == 0) : (D >= 2 && D % 2 == 0);
 }
 
@@ -661,16 +667,16 @@ scan_status rglru_gate_proj_bwd(int B, int L, int D, const void* x, const void* 
 
 // ------------------------------------------------------- SAMU decode ---
 size_t samu_scan_decode_table_bytes(int D) {
-    if (D < 8 || D % 8 != 0) return 0;
+    if (D < 8 || D % 8 != 0 || D > kMaxD) return 0;
     return samu_decode_table_floats(D / 2) * sizeof(float);
 }
 
 scan_status samu_scan_decode_prepare(int D, const float* w_phi, const float* w_r, const float* a_phi,
                                      const float* a_r, const float* nu, const float* theta, void* table,
                                      void* stream) {
-    if (D < 8 || D % 8 != 0)
+    if (D < 8 || D % 8 != 0 || D > kMaxD)
         return fail(SCAN_ERR_SHAPE, "samu_scan_decode_prepare: unsupported D=" + std::to_string(D) +
-                                        " (need D >= 8 a multiple of 8)");
+                                        " (need 8 <= D <= 1048576 a multiple of 8)");
     scan_status st = check_ptrs({{w_phi, 0, "w_phi"}, {w_r, 0, "w_r"}, {a_phi, 0, "a_phi"}, {a_r, 0, "a_r"},
                                  {nu, 0, "nu"}, {theta, 0, "theta"}, {table, 0, "table"}},
                                 {});
@@ -691,10 +697,10 @@ scan_status samu_scan_decode(int B, int D, const void* x_sel, const void* b, con
                              const float* w_r, const float* a_phi, const float* a_r, const float* nu,
                              const float* theta, const void* table, const float* z_in, float* z_out, void* y,
                              int y_dtype, void* stream) {
-    if (B < 1 || B > 65535 || D < 8 || D % 8 != 0)
+    if (B < 1 || B > 65535 || D < 8 || D % 8 != 0 || D > kMaxD)
         return fail(SCAN_ERR_SHAPE, "samu_scan_decode: unsupported shape B=" + std::to_string(B) +
                                         " D=" + std::to_string(D) +
-                                        " (need 1 <= B <= 65535, D >= 8 a multiple of 8)");
+                                        " (need 1 <= B <= 65535, 8 <= D <= 1048576 a multiple of 8)");
     if (y_dtype != SCAN_BF16 && y_dtype != SCAN_F32)
         return fail(SCAN_ERR_SHAPE, "samu_scan_decode: y_dtype must be SCAN_BF16 or SCAN_F32");
     scan_status st = check_ptrs({{x_sel, 0, "x_sel"}, {b, 0, "b"}, {w_phi, 0, "w_phi"}, {w_r, 0, "w_r"},
@@ -743,7 +749,7 @@ scan_status rglru_scan_fwd(int B, int L, int D, int K, int G, const void* x, con
     Chunking ch;
     if (!rglru_shape(B, L, D, K, G, &ch))
         return fail(SCAN_ERR_SHAPE, "rglru_scan_fwd: unsupported shape " + shape_text(B, L, D, K, G) +
-                                        " (need B, L >= 1, D >= 2 even, K in {16, 32}, G >= 0,"
+                                        " (need B, L >= 1, 2 <= D <= 1048576 even, K in {16, 32}, G >= 0,"
                                         " ceil(L/K) <= 65535)");
     if (y_dtype != SCAN_BF16 && y_dtype != SCAN_F32)
         return fail(SCAN_ERR_SHAPE, "rglru_scan_fwd: y_dtype must be SCAN_BF16 or SCAN_F32");

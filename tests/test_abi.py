@@ -111,6 +111,13 @@ def test_saved_and_workspace_sizes():
     assert scan.samu_scan_workspace_bytes(B, L, D, 24, 0, False) == 0        # K
     assert scan.rglru_scan_saved_bytes(4, 8192, 2560, 16) >= 4 * 512 * 2560 * 4
     assert scan.rglru_scan_workspace_bytes(1, 10, 3, 16, 0, False) == 0     # D odd
+    # the widest state accepted (every chunk's rows stay inside 32-bit byte
+    # ranges): 2^20 channels
+    assert scan.samu_scan_workspace_bytes(1, 64, 1 << 20, K, 0, False) > 0
+    assert scan.samu_scan_workspace_bytes(1, 64, (1 << 20) + 8, K, 0, False) == 0
+    assert scan.rglru_scan_workspace_bytes(1, 64, 1 << 20, 16, 0, False) > 0
+    assert scan.rglru_scan_workspace_bytes(1, 64, (1 << 20) + 2, 16, 0, False) == 0
+    assert scan.lib().samu_scan_decode_table_bytes((1 << 20) + 8) == 0
 
 
 def _fake(addr):
@@ -137,7 +144,8 @@ def _call_samu_fwd(a):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(D=12), -2), (dict(D=0), -2), (dict(K=8), -2), (dict(L=0), -2), (dict(B=0), -2),
+    (dict(D=12), -2), (dict(D=0), -2), (dict(D=(1 << 20) + 8), -2), (dict(K=8), -2), (dict(L=0), -2),
+    (dict(B=0), -2),
     (dict(G=-1), -2), (dict(L=32 * 65536), -2), (dict(y_dtype=3), -2),
     (dict(x_sel=None), -1), (dict(saved=None), -1), (dict(nu=None), -1),
     (dict(b=0x200004), -3), (dict(z0=0x700008), -3),

@@ -23,9 +23,10 @@ def _params(d):
 
 
 @pytest.mark.parametrize("table", [False, True], ids=["per_step_constants", "prepared_table"])
-# an odd batch with a mode count that leaves the last 256-mode workgroup partial
+# an odd batch with a mode count that leaves the last 256-mode workgroup partial,
+# and the widest state the library accepts (2^20 channels)
 @pytest.mark.parametrize("B,D,std", [(3, 64, 0.5), (1, 2048, 0.1), (256, 2048, 0.1), (5, 1032, None),
-                                     (67, 1032, 0.5)])
+                                     (67, 1032, 0.5), (2, 1 << 20, 0.1)])
 def test_decode_step_matches_oracle(B, D, std, table):
     from linear_recurrence_sequence_amd import scan
     inp = inputs.samu_inputs(B, 1, D, 500 + D + B, z0_std=std, with_dy=False)

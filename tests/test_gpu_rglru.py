@@ -16,6 +16,8 @@ TOL_OUT, TOL_GRAD = 1e-5, 1e-4
 # (name, B, L, D, K, G, reset_p, state_std)
 CASES = [
     ("packed_small", 4, 600, 256, 16, 0, 1.0 / 64, 0.1),
+    # the widest state the library accepts (2^20 channels), a partial last chunk
+    ("widest_state", 1, 80, 1 << 20, 16, 0, 1.0 / 64, 0.1),
     ("ragged_groups", 2, 77, 6, 16, 2, 0.1, 0.1),
     ("k32_groups", 1, 1000, 64, 32, 4, 0.0, 0.1),
     ("shorter_than_chunk", 1, 5, 10, 16, 0, 0.0, 0.1),

@@ -206,6 +206,9 @@ FULL_CASES = [
     # several batch rows, each with its own chain of 32 groups, at the
     # packed-sequence workload's shape
     ("rows_b4_l8192_d2560", 4, 8192, 2560, 32, 0, 0.1, 3004),
+    # the widest state the library accepts (2^20 channels, 8192 mode tiles),
+    # three chunks with a partial last one
+    ("widest_state_b1_l80", 1, 80, 1 << 20, 32, 0, 0.1, 3005),
 ]
 
 
