@@ -279,3 +279,34 @@ def test_samu_signed_and_large_amplitudes(amp, D):
     assert errs["y"] <= TOL_OUT and errs["z_final"] <= TOL_OUT
     for k in ("dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta", "dz0", "da_phi", "da_r"):
         assert errs[k] <= TOL_GRAD, (k, errs[k])
+
+
+def test_samu_degenerate_spectrum():
+    """Degenerate spectra: modes that never decay (nu = 0, so |lambda| = 1
+    and the state keeps every drive), modes that forget at once (nu = 20,
+    lambda ~ 2e-9), real transitions (theta = 0 or pi) and a quarter turn,
+    mixed with ordinary modes, over a ragged length and the default
+    single-pass grouping: both output modes against the oracle."""
+    B, L, D, K = 2, 1500, 64, 32
+    M = D // 2
+    inp = inputs.samu_inputs(B, L, D, 8900, z0_std=0.1, dz_final_std=0.1)
+    nu, theta = inp["nu"].copy(), inp["theta"].copy()
+    nu[0:8] = 0.0
+    nu[8:12] = 20.0
+    nu[12:16] = 1e-4
+    theta[0:16] = np.tile(np.array([0.0, np.pi, np.pi / 2, -np.pi / 2], np.float32), 4)
+    inp["nu"], inp["theta"] = nu.astype(np.float32), theta.astype(np.float32)
+    say(f"[samu parity] degenerate spectrum: B={B} L={L} D={D} (M={M})")
+    rf, rg = _oracle(inp)
+    y, zf, g = _gpu(inp, K, 0, torch.float32)
+    errs = {"y": rel_l2(to_f64(y), rf["y"]), "z_final": rel_l2(to_f64(zf), rf["z_final"])}
+    for k in ("dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta", "dz0"):
+        errs[k] = rel_l2(to_f64(g[k]), rg[k])
+    say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["y"] <= TOL_OUT and errs["z_final"] <= TOL_OUT
+    for k in ("dx_sel", "db", "dw_phi", "dw_r", "dnu", "dtheta", "dz0"):
+        assert errs[k] <= TOL_GRAD, (k, errs[k])
+    yb, zfb, gb = _gpu(inp, K, 0, torch.bfloat16)
+    assert torch.equal(yb, y.to(torch.bfloat16))
+    assert torch.equal(gb["db"], g["db"].to(torch.bfloat16))
+    assert torch.equal(gb["dx_sel"], g["dx_sel"].to(torch.bfloat16))
